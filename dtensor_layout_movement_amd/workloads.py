@@ -1,0 +1,160 @@
+"""Seeded synthetic reshard workloads.
+
+This module only describes inputs: global shapes, dtypes, source and
+destination layouts, and seeded value generators.  It holds none of the
+reshard's arithmetic (no shard boxes, no intersections): code that needs a
+rank's box asks either the product library or, in tests, the oracle, and hands
+the boxes to ``cut``.
+
+Workloads (all synthetic; the pages publish no dataset and no per-tensor
+numbers, only an 8x8 example and multi-node refit latencies):
+
+* ``worked_example_8x8`` -- the pages' example: an 8x8 matrix row-sharded over
+  two training GPUs and column-sharded over four inference GPUs, so that every
+  destination receives one 4x2 block from each source (techfeed.io write-up,
+  "reformulation" section; news.bpdata.com write-up, "the approach" section).
+  Values 0..63, exact in bf16.
+* ``ffn_up_14336x4096`` -- one feed-forward up-projection (the FFN projections
+  carry about 95% of the refit payload: techfeed.io, "results" section):
+  TP4 row split -> DP2 x TP2 column split.
+* ``moe_experts_64x2048x7168`` -- an MoE expert stack: EP8 x TP2 -> DP2 x TP8.
+* ``uneven_5000x3001`` -- odd fp32 shape with a nested split of one dim into
+  ragged chunks -> seven row shards.
+* ``ffn_refit_32_layers`` -- 32 layers x (gate, up, down) moved by one fused
+  launch: 4 pipeline stages x TP2 -> DP2 x TP4.
+
+Values: bf16 tensors are N(0, 0.02) drawn in fp32 and rounded to nearest-even;
+fp32 tensors are U[-1, 1); "raw" fills every byte uniformly at random (NaN
+payloads, infinities, signed zeros and subnormals included).  Tensor t of a
+workload under seed s draws from ``torch.Generator().manual_seed(1000*s + t)``.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+from typing import Sequence
+
+import torch
+
+R = -1  # Replicate placement code (Shard(k) is k)
+
+
+@dataclass(frozen=True)
+class TensorSpec:
+    name: str
+    shape: tuple
+    dtype: torch.dtype
+    src_mesh: tuple
+    src_placements: tuple
+    dst_mesh: tuple
+    dst_placements: tuple
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    tensors: tuple
+    values: str  # "arange" | "normal" | "uniform"
+    description: str
+
+    @property
+    def global_bytes(self) -> int:
+        return sum(_numel(t.shape) * _esize(t.dtype) for t in self.tensors)
+
+
+def _numel(shape) -> int:
+    n = 1
+    for s in shape:
+        n *= s
+    return n
+
+
+def _esize(dtype: torch.dtype) -> int:
+    return torch.empty((), dtype=dtype).element_size()
+
+
+def worked_example_8x8() -> Workload:
+    t = TensorSpec("w", (8, 8), torch.bfloat16, (2,), (0,), (4,), (1,))
+    return Workload("worked_example_8x8", (t,), "arange",
+                    "8x8 bf16 0..63, (2,)[S0] -> (4,)[S1]")
+
+
+def ffn_up(rows: int = 14336, cols: int = 4096) -> Workload:
+    t = TensorSpec("up_proj", (rows, cols), torch.bfloat16, (4,), (0,), (2, 2), (R, 1))
+    return Workload(f"ffn_up_{rows}x{cols}", (t,), "normal",
+                    f"{rows}x{cols} bf16 N(0,0.02), (4,)[S0] -> (2,2)[R,S1]")
+
+
+def moe_experts(experts: int = 64, hidden: int = 2048, ffn: int = 7168) -> Workload:
+    t = TensorSpec("experts", (experts, hidden, ffn), torch.bfloat16, (8, 2), (0, 1), (2, 8), (R, 2))
+    return Workload(f"moe_experts_{experts}x{hidden}x{ffn}", (t,), "normal",
+                    f"[{experts},{hidden},{ffn}] bf16 N(0,0.02), (8,2)[S0,S1] -> (2,8)[R,S2]")
+
+
+def uneven(rows: int = 5000, cols: int = 3001) -> Workload:
+    t = TensorSpec("uneven", (rows, cols), torch.float32, (3, 2), (1, 1), (7,), (0,))
+    return Workload(f"uneven_{rows}x{cols}", (t,), "uniform",
+                    f"{rows}x{cols} fp32 U[-1,1), (3,2)[S1,S1] -> (7,)[S0]")
+
+
+def ffn_refit(layers: int = 32, hidden: int = 4096, ffn: int = 14336, stages: int = 4) -> Workload:
+    """Per layer gate [ffn, hidden], up [ffn, hidden], down [hidden, ffn].  Each
+    tensor lives on its pipeline stage's 2-rank mesh; tensors are ordered
+    layer-major (gate, up, down)."""
+    ts = []
+    for layer in range(layers):
+        for name in ("gate", "up", "down"):
+            if name == "down":
+                shape, sp, dp = (hidden, ffn), (1,), (R, 1)
+            else:
+                shape, sp, dp = (ffn, hidden), (0,), (R, 0)
+            ts.append(TensorSpec(f"layer{layer}.{name}", shape, torch.bfloat16, (2,), sp, (2, 4), dp))
+    return Workload(f"ffn_refit_{layers}_layers", tuple(ts), "normal",
+                    f"{layers} layers x (gate {ffn}x{hidden}, up {ffn}x{hidden}, down {hidden}x{ffn}) "
+                    f"bf16, PP{stages} x (2,)[S0|S1] -> (2,4)[R,S0|S1], one fused launch")
+
+
+def stage_of_layer(layer: int, layers: int = 32, stages: int = 4) -> int:
+    """Pipeline stage holding `layer` (contiguous blocks of layers per stage)."""
+    return layer * stages // layers
+
+
+WORKLOADS = {
+    "worked_example_8x8": worked_example_8x8,
+    "ffn_up_14336x4096": ffn_up,
+    "moe_experts_64x2048x7168": moe_experts,
+    "uneven_5000x3001": uneven,
+    "ffn_refit_32_layers": ffn_refit,
+}
+
+
+def generator(seed: int, tensor_index: int) -> torch.Generator:
+    return torch.Generator().manual_seed(1000 * seed + tensor_index)
+
+
+def make_global(spec: TensorSpec, values: str, seed: int, tensor_index: int = 0) -> torch.Tensor:
+    """The seeded global tensor (CPU, contiguous) of one workload tensor."""
+    g = generator(seed, tensor_index)
+    if values == "arange":
+        return torch.arange(_numel(spec.shape), dtype=torch.float32).reshape(spec.shape).to(spec.dtype)
+    if values == "normal":
+        return (torch.randn(spec.shape, generator=g, dtype=torch.float32) * 0.02).to(spec.dtype)
+    if values == "uniform":
+        return (torch.rand(spec.shape, generator=g, dtype=torch.float32) * 2 - 1).to(spec.dtype)
+    if values == "raw":
+        nbytes = _numel(spec.shape) * _esize(spec.dtype)
+        raw = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
+        return raw.view(spec.dtype).reshape(spec.shape)
+    raise ValueError(f"unknown value kind {values!r}")
+
+
+def cut(global_tensor: torch.Tensor, boxes: Sequence) -> list:
+    """Contiguous copies of ``global_tensor[lo:hi, ...]`` for each ``(lo, hi)`` box;
+    None for empty boxes."""
+    out = []
+    for lo, hi in boxes:
+        if any(h <= l for l, h in zip(lo, hi)):
+            out.append(None)
+            continue
+        idx = tuple(slice(l, h) for l, h in zip(lo, hi))
+        out.append(global_tensor[idx].contiguous())
+    return out

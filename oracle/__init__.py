@@ -1,0 +1,133 @@
+"""CPU oracle for the DTensor reshard -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product library
+(``dtensor_layout_movement_amd``) never imports, links or calls it, and it
+imports nothing from the product.
+
+The arithmetic lives in ``oracle.cpp`` (plain C++17 built with g++): the
+gather-then-slice scheme that the reshard write-ups give as the usual refit path
+(techfeed.io, "core problem" section; news.bpdata.com, "why is weight refit a
+problem" section): rebuild the global tensor from the source shards, then cut
+every destination shard out of it.  This module only marshals arguments.
+
+Placements are ints: ``-1`` is Replicate, ``k >= 0`` is Shard(k).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+from typing import Sequence
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "oracle.cpp")
+_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+_lib = None
+
+OK = 0
+BAD_LAYOUT = 1
+REPLICA_MISMATCH = 2
+COVERAGE_MISMATCH = 3
+NO_MEMORY = 4
+NULL_BUFFER = 5
+
+_I64P = ctypes.POINTER(ctypes.c_int64)
+_I32P = ctypes.POINTER(ctypes.c_int32)
+
+
+def build(out_path: str = _LIB_PATH, source: str = _SRC) -> str:
+    """Compile the oracle with g++ into ``out_path`` and return that path."""
+    cmd = ["g++", "-std=c++17", "-O2", "-Wall", "-fPIC", "-shared", "-pthread",
+           source, "-o", out_path]
+    subprocess.run(cmd, check=True)
+    return out_path
+
+
+def load(path: str = _LIB_PATH) -> ctypes.CDLL:
+    """Load (building first if absent) the oracle library."""
+    global _lib
+    if path == _LIB_PATH and _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        build(path)
+    lib = ctypes.CDLL(path)
+    lib.oracle_num_ranks.argtypes = [ctypes.c_int, _I64P, ctypes.c_int, _I64P, _I32P, _I64P]
+    lib.oracle_shard_box.argtypes = [ctypes.c_int, _I64P, ctypes.c_int, _I64P, _I32P,
+                                     ctypes.c_int64, _I64P, _I64P]
+    lib.oracle_reshard.argtypes = [ctypes.c_int, _I64P, ctypes.c_int64,
+                                   ctypes.c_int, _I64P, _I32P, ctypes.POINTER(ctypes.c_void_p),
+                                   ctypes.c_int, _I64P, _I32P, ctypes.POINTER(ctypes.c_void_p),
+                                   ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+    for f in (lib.oracle_num_ranks, lib.oracle_shard_box, lib.oracle_reshard):
+        f.restype = ctypes.c_int
+    if path == _LIB_PATH:
+        _lib = lib
+    return lib
+
+
+def _i64(xs: Sequence[int]):
+    return (ctypes.c_int64 * max(1, len(xs)))(*xs)
+
+
+def _i32(xs: Sequence[int]):
+    return (ctypes.c_int32 * max(1, len(xs)))(*xs)
+
+
+class OracleError(RuntimeError):
+    def __init__(self, code: int):
+        names = {1: "bad layout", 2: "replica mismatch", 3: "coverage mismatch",
+                 4: "out of memory", 5: "NULL buffer for a non-empty shard"}
+        super().__init__(f"oracle error {code}: {names.get(code, '?')}")
+        self.code = code
+
+
+def num_ranks(shape, mesh, placements, lib=None) -> int:
+    lib = lib or load()
+    out = ctypes.c_int64(0)
+    rc = lib.oracle_num_ranks(len(shape), _i64(shape), len(mesh), _i64(mesh),
+                              _i32(placements), ctypes.byref(out))
+    if rc:
+        raise OracleError(rc)
+    return out.value
+
+
+def shard_box(shape, mesh, placements, rank, lib=None):
+    """Return ``(lo, hi)`` lists: the half-open box that ``rank`` holds."""
+    lib = lib or load()
+    lo = (ctypes.c_int64 * len(shape))()
+    hi = (ctypes.c_int64 * len(shape))()
+    rc = lib.oracle_shard_box(len(shape), _i64(shape), len(mesh), _i64(mesh),
+                              _i32(placements), rank, lo, hi)
+    if rc:
+        raise OracleError(rc)
+    return list(lo), list(hi)
+
+
+def _addr(buf) -> int | None:
+    if buf is None:
+        return None
+    if hasattr(buf, "data_ptr"):           # torch CPU tensor
+        if buf.device.type != "cpu" or not buf.is_contiguous():
+            raise ValueError("oracle buffers must be contiguous CPU tensors")
+        return buf.data_ptr() if buf.numel() else None
+    iface = buf.__array_interface__        # numpy array
+    return iface["data"][0] if buf.size else None
+
+
+def reshard(shape, elem_size, src_mesh, src_pl, src_bufs, dst_mesh, dst_pl, dst_bufs,
+            global_out=None, check: bool = True, threads: int = 1, lib=None) -> None:
+    """Gather-then-slice: fill every ``dst_bufs[d]`` from ``src_bufs``.
+
+    Buffers are contiguous CPU tensors / numpy arrays (or None for empty shards),
+    one per rank in row-major mesh order.  Raises OracleError on a failed check.
+    """
+    lib = lib or load()
+    srcs = (ctypes.c_void_p * max(1, len(src_bufs)))(*[_addr(b) for b in src_bufs])
+    dsts = (ctypes.c_void_p * max(1, len(dst_bufs)))(*[_addr(b) for b in dst_bufs])
+    rc = lib.oracle_reshard(len(shape), _i64(shape), elem_size,
+                            len(src_mesh), _i64(src_mesh), _i32(src_pl), srcs,
+                            len(dst_mesh), _i64(dst_mesh), _i32(dst_pl), dsts,
+                            _addr(global_out), int(check), int(threads))
+    if rc:
+        raise OracleError(rc)

@@ -1,0 +1,293 @@
+/*
+ * CPU oracle for the DTensor-to-DTensor reshard.  TEST INFRASTRUCTURE ONLY:
+ * the tests, the smoke check and the CPU-baseline leg of the benchmark may load
+ * it; the product library never does.  It shares no code, header or constant
+ * with the GPU path.
+ *
+ * What it computes ("gather, then keep your slice"):
+ *   The reshard pages describe the usual refit path as: all-gather every full
+ *   parameter from the training shards, broadcast it, and let every inference
+ *   GPU keep only its own shard ("Accelerating RL Weight Refit with the Reshard
+ *   Collective" write-ups: techfeed.io, "core problem" section; news.bpdata.com,
+ *   "why is weight refit a problem" section).  Reshard must reach exactly the
+ *   same destination bytes while moving only the overlaps.  This file runs that
+ *   baseline scheme on the host:
+ *     1. X[box(src, s)] = src_shard[s] for every source rank s (the gather);
+ *     2. dst_shard[d]   = X[box(dst, d)] for every destination rank d (the slice).
+ *
+ * Layout model (DTensor: global shape + device mesh + placements; techfeed.io,
+ * "reformulation" section; news.bpdata.com, "the approach" section):
+ *   - a placement is Replicate (code -1) or Shard(k) (code k >= 0);
+ *   - ranks are numbered row-major over mesh coordinates;
+ *   - Shard uses torch.chunk ceil-splitting: chunk = ceil(n / mesh_size), so
+ *     trailing ranks may get a short or empty piece;
+ *   - several mesh dims sharding the same tensor dim nest left to right, each
+ *     splitting the interval left by the previous one;
+ *   - a local shard is stored contiguous row-major with the box's extents.
+ *   The pages say only "sharded"; the split rule and the nesting order are the
+ *   readings this project takes (they match PyTorch DTensor's own rule).
+ *
+ * Checks made while gathering: a replicated source rank must hold bytes equal
+ * to what an earlier replica already put into X, and at the end every global
+ * element must have been covered exactly R_src times, R_src being the product
+ * of the mesh sizes of the source's Replicate dims.
+ *
+ * Built with g++ (plain C++17, std::thread); no HIP.
+ */
+#include <atomic>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <thread>
+#include <vector>
+
+namespace {
+
+constexpr int kMaxDims = 8;
+constexpr int32_t kReplicate = -1;
+
+enum OracleStatus {
+  ORACLE_OK = 0,
+  ORACLE_BAD_LAYOUT = 1,
+  ORACLE_REPLICA_MISMATCH = 2,
+  ORACLE_COVERAGE_MISMATCH = 3,
+  ORACLE_NO_MEMORY = 4,
+  ORACLE_NULL_BUFFER = 5,
+};
+
+struct Layout {
+  int ndim;
+  const int64_t* shape;
+  int mesh_ndim;
+  const int64_t* mesh;
+  const int32_t* placements;
+};
+
+bool layout_ok(const Layout& L) {
+  if (L.ndim < 1 || L.ndim > kMaxDims) return false;
+  if (L.mesh_ndim < 1 || L.mesh_ndim > kMaxDims) return false;
+  for (int k = 0; k < L.ndim; ++k)
+    if (L.shape[k] < 0) return false;
+  for (int m = 0; m < L.mesh_ndim; ++m) {
+    if (L.mesh[m] < 1) return false;
+    int32_t p = L.placements[m];
+    if (p != kReplicate && (p < 0 || p >= L.ndim)) return false;
+  }
+  return true;
+}
+
+int64_t num_ranks(const Layout& L) {
+  int64_t n = 1;
+  for (int m = 0; m < L.mesh_ndim; ++m) n *= L.mesh[m];
+  return n;
+}
+
+/* Box [lo, hi) of `rank` under layout L. */
+void box_of(const Layout& L, int64_t rank, int64_t* lo, int64_t* hi) {
+  int64_t coord[kMaxDims];
+  int64_t r = rank;
+  for (int m = L.mesh_ndim - 1; m >= 0; --m) {  // row-major mesh order
+    coord[m] = r % L.mesh[m];
+    r /= L.mesh[m];
+  }
+  for (int k = 0; k < L.ndim; ++k) {
+    lo[k] = 0;
+    hi[k] = L.shape[k];
+  }
+  for (int m = 0; m < L.mesh_ndim; ++m) {  // nest left to right
+    int32_t p = L.placements[m];
+    if (p == kReplicate) continue;
+    int64_t n = hi[p] - lo[p];
+    int64_t chunk = (n + L.mesh[m] - 1) / L.mesh[m];  // ceil(n / mesh size)
+    int64_t a = lo[p] + coord[m] * chunk;
+    int64_t b = a + chunk;
+    int64_t end = hi[p];
+    lo[p] = a < end ? a : end;
+    hi[p] = b < end ? b : end;
+  }
+}
+
+bool box_empty(int ndim, const int64_t* lo, const int64_t* hi) {
+  for (int k = 0; k < ndim; ++k)
+    if (hi[k] <= lo[k]) return true;
+  return false;
+}
+
+/* Run fn(row_begin, row_end) over [0, rows) split into `threads` contiguous parts. */
+template <class Fn>
+void parallel_rows(int64_t rows, int threads, Fn fn) {
+  if (threads <= 1 || rows < 2 * (int64_t)threads) {
+    fn((int64_t)0, rows);
+    return;
+  }
+  std::vector<std::thread> pool;
+  int64_t per = (rows + threads - 1) / threads;
+  for (int t = 0; t < threads; ++t) {
+    int64_t a = t * per, b = a + per < rows ? a + per : rows;
+    if (a >= b) break;
+    pool.emplace_back(fn, a, b);
+  }
+  for (auto& th : pool) th.join();
+}
+
+/*
+ * Offset, in elements, of the first element of row `row` of a box inside the
+ * global row-major tensor.  A "row" is one run along the last dim; rows are
+ * numbered row-major over the box's other dims.
+ */
+int64_t global_row_offset(int ndim, const int64_t* shape, const int64_t* lo,
+                          const int64_t* ext, int64_t row) {
+  int64_t off = 0, stride = shape[ndim - 1];
+  off += lo[ndim - 1];
+  for (int k = ndim - 2; k >= 0; --k) {
+    int64_t i = row % ext[k];
+    row /= ext[k];
+    off += (lo[k] + i) * stride;
+    stride *= shape[k];
+  }
+  return off;
+}
+
+}  // namespace
+
+extern "C" {
+
+int oracle_num_ranks(int ndim, const int64_t* shape, int mesh_ndim, const int64_t* mesh,
+                     const int32_t* placements, int64_t* out) {
+  Layout L{ndim, shape, mesh_ndim, mesh, placements};
+  if (!layout_ok(L)) return ORACLE_BAD_LAYOUT;
+  *out = num_ranks(L);
+  return ORACLE_OK;
+}
+
+int oracle_shard_box(int ndim, const int64_t* shape, int mesh_ndim, const int64_t* mesh,
+                     const int32_t* placements, int64_t rank, int64_t* lo, int64_t* hi) {
+  Layout L{ndim, shape, mesh_ndim, mesh, placements};
+  if (!layout_ok(L) || rank < 0 || rank >= num_ranks(L)) return ORACLE_BAD_LAYOUT;
+  box_of(L, rank, lo, hi);
+  return ORACLE_OK;
+}
+
+/*
+ * Gather-then-slice reshard of one tensor.
+ *   elem_size        bytes per element (the copy is bytewise; no conversion)
+ *   src_bufs[s]      source shard of rank s (contiguous row-major box); may be
+ *                    NULL only when that box is empty
+ *   dst_bufs[d]      destination shard of rank d, written by this call
+ *   global_out       optional caller buffer of prod(shape)*elem_size bytes that
+ *                    receives X; NULL lets the oracle allocate its own
+ *   check            nonzero: replica-consistency and coverage checks
+ *   threads          host threads used for each box copy (>= 1)
+ * Returns 0, or an OracleStatus code.
+ */
+int oracle_reshard(int ndim, const int64_t* shape, int64_t elem_size,
+                   int src_mesh_ndim, const int64_t* src_mesh, const int32_t* src_pl,
+                   const void* const* src_bufs,
+                   int dst_mesh_ndim, const int64_t* dst_mesh, const int32_t* dst_pl,
+                   void* const* dst_bufs,
+                   void* global_out, int check, int threads) {
+  Layout S{ndim, shape, src_mesh_ndim, src_mesh, src_pl};
+  Layout D{ndim, shape, dst_mesh_ndim, dst_mesh, dst_pl};
+  if (!layout_ok(S) || !layout_ok(D) || elem_size < 1) return ORACLE_BAD_LAYOUT;
+  if (threads < 1) threads = 1;
+
+  int64_t numel = 1;
+  for (int k = 0; k < ndim; ++k) numel *= shape[k];
+  const size_t es = (size_t)elem_size;
+
+  int64_t r_src = 1;  // expected coverage of every element by the sources
+  for (int m = 0; m < S.mesh_ndim; ++m)
+    if (S.placements[m] == kReplicate) r_src *= S.mesh[m];
+  if (check && r_src > 254) check = 0;  // uint8 counters; such meshes skip the count
+
+  unsigned char* X = (unsigned char*)global_out;
+  bool own_x = false;
+  if (X == nullptr && numel > 0) {
+    X = (unsigned char*)std::malloc((size_t)numel * es);
+    if (!X) return ORACLE_NO_MEMORY;
+    own_x = true;
+  }
+  unsigned char* count = nullptr;
+  if (check && numel > 0) {
+    count = (unsigned char*)std::calloc((size_t)numel, 1);
+    if (!count) {
+      if (own_x) std::free(X);
+      return ORACLE_NO_MEMORY;
+    }
+  }
+  int status = ORACLE_OK;
+
+  // 1. Gather: X[box(src, s)] = src_shard[s].
+  for (int64_t s = 0; s < num_ranks(S) && status == ORACLE_OK; ++s) {
+    int64_t lo[kMaxDims], hi[kMaxDims], ext[kMaxDims];
+    box_of(S, s, lo, hi);
+    if (box_empty(ndim, lo, hi)) continue;
+    if (src_bufs[s] == nullptr) {
+      status = ORACLE_NULL_BUFFER;
+      break;
+    }
+    int64_t rows = 1;
+    for (int k = 0; k < ndim; ++k) ext[k] = hi[k] - lo[k];
+    for (int k = 0; k < ndim - 1; ++k) rows *= ext[k];
+    const int64_t run = ext[ndim - 1];
+    const unsigned char* shard = (const unsigned char*)src_bufs[s];
+    std::atomic<int> mismatch{0};
+    parallel_rows(rows, threads, [&](int64_t a, int64_t b) {
+      for (int64_t row = a; row < b; ++row) {
+        int64_t g = global_row_offset(ndim, shape, lo, ext, row);
+        const unsigned char* from = shard + (size_t)(row * run) * es;
+        unsigned char* to = X + (size_t)g * es;
+        if (!check) {
+          std::memcpy(to, from, (size_t)run * es);
+          continue;
+        }
+        for (int64_t j = 0; j < run; ++j) {
+          if (count[g + j] == 0) {
+            std::memcpy(to + j * es, from + j * es, es);
+          } else if (std::memcmp(to + j * es, from + j * es, es) != 0) {
+            mismatch.store(1);
+          }
+          count[g + j] += 1;
+        }
+      }
+    });
+    if (mismatch.load()) status = ORACLE_REPLICA_MISMATCH;
+  }
+
+  // Every element must be covered exactly R_src times.
+  if (status == ORACLE_OK && check) {
+    for (int64_t i = 0; i < numel; ++i)
+      if (count[i] != (unsigned char)r_src) {
+        status = ORACLE_COVERAGE_MISMATCH;
+        break;
+      }
+  }
+
+  // 2. Slice: dst_shard[d] = X[box(dst, d)].
+  for (int64_t d = 0; d < num_ranks(D) && status == ORACLE_OK; ++d) {
+    int64_t lo[kMaxDims], hi[kMaxDims], ext[kMaxDims];
+    box_of(D, d, lo, hi);
+    if (box_empty(ndim, lo, hi)) continue;
+    if (dst_bufs[d] == nullptr) {
+      status = ORACLE_NULL_BUFFER;
+      break;
+    }
+    int64_t rows = 1;
+    for (int k = 0; k < ndim; ++k) ext[k] = hi[k] - lo[k];
+    for (int k = 0; k < ndim - 1; ++k) rows *= ext[k];
+    const int64_t run = ext[ndim - 1];
+    unsigned char* shard = (unsigned char*)dst_bufs[d];
+    parallel_rows(rows, threads, [&](int64_t a, int64_t b) {
+      for (int64_t row = a; row < b; ++row) {
+        int64_t g = global_row_offset(ndim, shape, lo, ext, row);
+        std::memcpy(shard + (size_t)(row * run) * es, X + (size_t)g * es, (size_t)run * es);
+      }
+    });
+  }
+
+  std::free(count);
+  if (own_x) std::free(X);
+  return status;
+}
+
+}  // extern "C"

@@ -1,0 +1,109 @@
+"""The CPU oracle against its pins (CPU only), and proof that the pins catch
+plausible mistakes: each mutant below plants one mistake in a copy of
+oracle.cpp, and at least one pin must fail against it."""
+import os
+import subprocess
+import sys
+
+import pytest
+import torch
+
+import oracle
+import oracle_pins as P
+from dtensor_layout_movement_amd import workloads as W
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+
+
+def test_pin_worked_example(oracle_lib):
+    P.pin_worked_example(oracle_lib)
+
+
+def test_pin_box_vs_dtensor(oracle_lib):
+    P.pin_box_vs_dtensor(oracle_lib)
+
+
+def test_pin_box_vs_chunk(oracle_lib):
+    P.pin_box_vs_chunk(oracle_lib)
+
+
+def test_pin_end_to_end_chunk(oracle_lib):
+    P.pin_end_to_end_chunk(oracle_lib)
+
+
+def test_pin_gather_and_checks(oracle_lib):
+    P.pin_gather(oracle_lib)
+
+
+def test_pin_raw_bits(oracle_lib):
+    P.pin_raw_bits(oracle_lib)
+
+
+def test_nested_split_reading(oracle_lib):
+    # Nested Shard on one dim splits the interval left by the outer mesh dim
+    # (DTensor's rule), which differs from a flat 6-way split at rank (0, 1).
+    shape, mesh, pl = (5000, 3001), (3, 2), (1, 1)
+    cols = [oracle.shard_box(shape, mesh, pl, r, lib=oracle_lib) for r in range(6)]
+    assert [(lo[1], hi[1]) for lo, hi in cols] == [
+        (0, 501), (501, 1001), (1001, 1502), (1502, 2002), (2002, 2502), (2502, 3001)]
+
+
+def test_threads_give_same_bytes(oracle_lib):
+    spec = W.moe_experts(16, 64, 448).tensors[0]
+    g = W.make_global(spec, "normal", seed=1)
+    one, _ = P.run_oracle(oracle_lib, spec, g, threads=1)
+    many, _ = P.run_oracle(oracle_lib, spec, g, threads=8)
+    for a, b in zip(one, many):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+@pytest.mark.parametrize("spec_fn", [W.ffn_up, W.uneven])
+def test_full_size_slices(oracle_lib, spec_fn):
+    """Full-size configs: every destination shard equals the generated global
+    sliced by PyTorch DTensor's boxes (no oracle arithmetic on that side)."""
+    wl = spec_fn()
+    spec = wl.tensors[0]
+    g = W.make_global(spec, wl.values, seed=0)
+    dsts, _ = P.run_oracle(oracle_lib, spec, g, threads=4)
+    for d, got in enumerate(dsts):
+        off, ext = P.dtensor_box(spec.shape, spec.dst_mesh, spec.dst_placements, d)
+        idx = tuple(slice(o, o + e) for o, e in zip(off, ext))
+        assert torch.equal(got.view(torch.uint8), g[idx].contiguous().view(torch.uint8))
+
+
+# Each mutant plants one plausible mistake in the oracle's source.
+MUTANTS = {
+    "floor_split": ("int64_t chunk = (n + L.mesh[m] - 1) / L.mesh[m];",
+                    "int64_t chunk = n / L.mesh[m] + (n % L.mesh[m] != 0 && coord[m] == 0);"),
+    "column_major_mesh": ("for (int m = L.mesh_ndim - 1; m >= 0; --m) {  // row-major mesh order",
+                          "for (int m = 0; m < L.mesh_ndim; ++m) {"),
+    "flat_nesting": ("int64_t a = lo[p] + coord[m] * chunk;", "int64_t a = coord[m] * chunk;"),
+    "stride_from_box": ("    stride *= shape[k];", "    stride *= ext[k];"),
+    "dropped_column_offset": ("  off += lo[ndim - 1];", "  off += 0;"),
+    "swapped_row_index": ("    int64_t i = row % ext[k];\n    row /= ext[k];",
+                          "    int64_t i = row / ext[k] % ext[k];\n    row %= ext[k];"),
+    "short_run": ("std::memcpy(shard + (size_t)(row * run) * es, X + (size_t)g * es, (size_t)run * es);",
+                  "std::memcpy(shard + (size_t)(row * run) * es, X + (size_t)g * es, (size_t)(run - (run > 1)) * es);"),
+    "coverage_all_dims": ("if (S.placements[m] == kReplicate) r_src *= S.mesh[m];",
+                          "r_src *= S.mesh[m];"),
+    "no_replica_compare": ("} else if (std::memcmp(to + j * es, from + j * es, es) != 0) {",
+                           "} else if (false) {"),
+    "replicate_splits": ("if (p == kReplicate) continue;\n    int64_t n",
+                         "if (p == kReplicate) p = 0;\n    int64_t n"),
+}
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_mutant(name, tmp_path):
+    src = open(os.path.join(ROOT, "oracle", "oracle.cpp")).read()
+    find, repl = MUTANTS[name]
+    assert src.count(find) == 1, f"mutation anchor for {name} not found exactly once"
+    mutant = tmp_path / "oracle_mutant.cpp"
+    mutant.write_text(src.replace(find, repl))
+    lib = oracle.build(str(tmp_path / "liboracle_mutant.so"), str(mutant))
+    # run the pins in a child process: a mutant may also crash, which counts as caught
+    env = dict(os.environ, PYTHONPATH=os.pathsep.join([ROOT, HERE]))
+    res = subprocess.run([sys.executable, os.path.join(HERE, "oracle_pins.py"), lib],
+                         capture_output=True, text=True, env=env, timeout=600)
+    assert res.returncode != 0, f"no pin caught mutant {name}:\n{res.stdout}\n{res.stderr}"
