@@ -1,0 +1,297 @@
+"""Benchmark of the reshard execute on one MI355X.
+
+A step is one reshard_execute of the workload's plan: one fused launch that
+reads every source byte once and writes every destination shard.  The plan
+(boxes, replica groups, intersections, replica choice, descriptors) is built
+once per layout pair and reused for every refit; its host time is reported
+separately as ``plan_us``.
+
+Inputs are resident in HBM before timing starts.  To keep every step cold in
+the 256 MB Infinity Cache, steps rotate over several independent sets of
+source and destination buffers whose total size is at least 2 GB.
+
+Prints one JSON line.  ``value`` = algorithmic bytes (global bytes read once +
+every destination shard written once) per second over the timed steps;
+``roofline.achieved`` = the same bytes over the kernel's mean launch duration
+from per-launch HIP events on the launch stream.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, decimal GB/s
+METRIC = "reshard execute GB/s (bytes read+written) and % of MI355X HBM peak; plan time us"
+DEFAULT_WORKLOAD = "ffn_up_14336x4096"
+KERNEL_SOURCE = os.path.join(ROOT, "dtensor_layout_movement_amd", "csrc", "reshard.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_NAME = "reshard_copy_kernel"
+
+
+def kernel_source_sha() -> str:
+    with open(KERNEL_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def layout_str(mesh, placements) -> str:
+    pl = ",".join("R" if p < 0 else f"S{p}" for p in placements)
+    return f"({','.join(str(m) for m in mesh)})[{pl}]"
+
+
+def traffic_from_profile(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or None
+    if there is none or the kernel source changed since it was taken."""
+    path = os.path.join(PROFILES, f"{KERNEL_NAME}_{workload}_counters.txt")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and not line.startswith("#"):
+            k, v = line.strip().split("=", 1)
+            vals[k.strip()] = v.strip()
+    if vals.get("kernel_source_sha256_16") != kernel_source_sha():
+        return None
+    try:
+        return int(vals["fetch_bytes_per_launch"]) + int(vals["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def build_plan(R, wl):
+    srcs, dsts = [], []
+    for t in wl.tensors:
+        code = R.dtype_code(t.dtype)
+        srcs.append(R.reshard_layout_create(t.shape, code, t.src_mesh, t.src_placements))
+        dsts.append(R.reshard_layout_create(t.shape, code, t.dst_mesh, t.dst_placements))
+    plan = R.reshard_plan_create_batched(srcs, dsts)
+    return plan, srcs, dsts
+
+
+def plan_timing(R, wl, reps: int) -> dict:
+    host, wall = [], []
+    for _ in range(reps):
+        t0 = time.perf_counter()
+        plan, srcs, dsts = build_plan(R, wl)
+        wall.append((time.perf_counter() - t0) * 1e6)
+        host.append(R.reshard_plan_stats(plan)["plan_host_us"])
+        R.reshard_plan_destroy(plan)
+        for h in srcs + dsts:
+            R.reshard_layout_destroy(h)
+    return {"host_median": round(statistics.median(host), 2),
+            "with_layouts_and_binding_median": round(statistics.median(wall), 2), "reps": reps}
+
+
+def alloc_set(torch, R, wl, lay_src, lay_dst, dev, seed):
+    """One set of source shards (seeded values) and destination shards."""
+    from dtensor_layout_movement_amd import workloads as W
+    src_bufs, dst_bufs = [], []
+    for t, spec in enumerate(wl.tensors):
+        nd = len(spec.shape)
+        sboxes, dboxes = [], []
+        for r in range(R.reshard_layout_num_ranks(lay_src[t])):
+            off, ext = R.reshard_layout_shard_box(lay_src[t], r, nd)
+            sboxes.append((off, [o + e for o, e in zip(off, ext)]))
+        for r in range(R.reshard_layout_num_ranks(lay_dst[t])):
+            off, ext = R.reshard_layout_shard_box(lay_dst[t], r, nd)
+            dboxes.append((off, [o + e for o, e in zip(off, ext)]))
+        g = W.make_global(spec, wl.values, seed, t, device=dev)
+        src_bufs += W.cut(g, sboxes)
+        del g
+        for lo, hi in dboxes:
+            shape = [max(0, h - l) for l, h in zip(lo, hi)]
+            dst_bufs.append(torch.empty(shape, dtype=spec.dtype, device=dev) if all(shape) else None)
+    sp = R.pointer_array([b.data_ptr() if b is not None else 0 for b in src_bufs])
+    dp = R.pointer_array([b.data_ptr() if b is not None else 0 for b in dst_bufs])
+    return src_bufs, dst_bufs, sp, dp
+
+
+def cpu_baseline(wl, budget_s: float) -> dict:
+    """The oracle (gather-then-slice) timed on this host's cores on the same workload."""
+    import torch
+    import oracle
+    from dtensor_layout_movement_amd import workloads as W
+    cores = len(os.sched_getaffinity(0))
+    total_bytes, secs, reps = 0, 0.0, 0
+    algo = 0
+    prepared = []
+    for t, spec in enumerate(wl.tensors):
+        n = 1
+        for m in spec.src_mesh:
+            n *= m
+        boxes = [oracle.shard_box(list(spec.shape), list(spec.src_mesh), list(spec.src_placements), r)
+                 for r in range(n)]
+        nd = 1
+        for m in spec.dst_mesh:
+            nd *= m
+        dboxes = [oracle.shard_box(list(spec.shape), list(spec.dst_mesh), list(spec.dst_placements), r)
+                  for r in range(nd)]
+        prepared.append((spec, boxes, dboxes))
+        if len(prepared) >= 3:  # a bounded sample of a many-tensor workload
+            break
+    while reps < 1 or (secs < budget_s and reps < 50):
+        for t, (spec, boxes, dboxes) in enumerate(prepared):
+            g = W.make_global(spec, wl.values, 0, t)
+            srcs = W.cut(g, boxes)
+            dsts = [torch.empty([max(0, h - l) for l, h in zip(lo, hi)], dtype=spec.dtype)
+                    for lo, hi in dboxes]
+            es = g.element_size()
+            t0 = time.perf_counter()
+            oracle.reshard(list(spec.shape), es, list(spec.src_mesh), list(spec.src_placements), srcs,
+                           list(spec.dst_mesh), list(spec.dst_placements),
+                           [d if d.numel() else None for d in dsts], threads=cores)
+            secs += time.perf_counter() - t0
+            algo += g.numel() * es + sum(d.numel() for d in dsts) * es
+        reps += 1
+    names = ", ".join(p[0].name for p in prepared)
+    return {"value": round(algo / secs / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": f"{reps} x gather-then-slice of [{names}] from {wl.name} (replica and coverage "
+                      f"checks on), {secs:.2f} s timed, GB/s over the reshard's algorithmic bytes"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--min-footprint-gb", type=float, default=2.0)
+    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--plan-reps", type=int, default=200)
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the reshard's source and destination ranks are "
+              "simulated as separate buffers in one MI355X's HBM; there is no multi-GPU path "
+              "in this build.", file=sys.stderr)
+        return 2
+
+    import torch
+    import dtensor_layout_movement_amd as R
+    from dtensor_layout_movement_amd import workloads as W
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    wl = W.WORKLOADS[args.workload]()
+
+    plan, lay_src, lay_dst = build_plan(R, wl)
+    stream = torch.cuda.current_stream()
+    R.reshard_plan_upload(plan, stream.cuda_stream)
+    st = R.reshard_plan_stats(plan)
+    algo_bytes = st["bytes_read"] + st["bytes_written"]
+    n_sets = max(1, min(16, int(-(-args.min_footprint_gb * 1e9 // algo_bytes))))
+    sets = [alloc_set(torch, R, wl, lay_src, lay_dst, dev, seed=s) for s in range(n_sets)]
+    torch.cuda.synchronize()
+
+    for i in range(args.warmup):
+        _, _, sp, dp = sets[i % n_sets]
+        R.reshard_execute(plan, sp, dp, stream.cuda_stream)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev_s = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    ev_e = [torch.cuda.Event(enable_timing=True) for _ in range(K)]
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(K):
+        _, _, sp, dp = sets[i % n_sets]
+        ev_s[i].record(stream)
+        R.reshard_execute(plan, sp, dp, stream.cuda_stream)
+        ev_e[i].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = t_begin.elapsed_time(t_end)
+    launch_ms = [a.elapsed_time(b) for a, b in zip(ev_s, ev_e)]
+    ms_per_step = total_ms / K
+    kernel_ms = statistics.mean(launch_ms)
+    value = algo_bytes / (ms_per_step * 1e-3) / 1e9
+    achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
+
+    # context: a plain device copy moving the same number of bytes (read + write)
+    half = algo_bytes // 2
+    a = torch.empty(half, dtype=torch.uint8, device=dev)
+    b = torch.empty(half, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        b.copy_(a)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(20):
+        b.copy_(a)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * half / (c0.elapsed_time(c1) / 20 * 1e-3) / 1e9
+    del a, b
+
+    plan_us = plan_timing(R, wl, args.plan_reps if algo_bytes < 2e10 else max(5, args.plan_reps // 20))
+    traffic = traffic_from_profile(wl.name)
+    spec0 = wl.tensors[0]
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": str(spec0.dtype).replace("torch.", "").replace("bfloat16", "bf16").replace("float32", "f32"),
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "tensors": len(wl.tensors),
+            "global_shape": list(spec0.shape) if len(wl.tensors) == 1 else None,
+            "src_layout": layout_str(spec0.src_mesh, spec0.src_placements),
+            "dst_layout": layout_str(spec0.dst_mesh, spec0.dst_placements),
+            "bytes_read": st["bytes_read"],
+            "bytes_written": st["bytes_written"],
+            "pieces": st["n_pieces"],
+            "descriptors": st["n_descriptors"],
+            "grid_workgroups": st["n_workgroups"],
+            "buffer_sets_rotated": n_sets,
+            "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        },
+        "plan_us": plan_us,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 2),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": KERNEL_NAME,
+            "kernel_mean_us": round(kernel_ms * 1e3, 3),
+            "kernel_median_us": round(statistics.median(launch_ms) * 1e3, 3),
+        },
+        "copy_reference_gbps": round(copy_gbps, 1),
+        "wall_s": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+    print(json.dumps(out), flush=True)
+
+    R.reshard_plan_destroy(plan)
+    for h in lay_src + lay_dst:
+        R.reshard_layout_destroy(h)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

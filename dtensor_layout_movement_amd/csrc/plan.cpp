@@ -1,0 +1,462 @@
+// Host planner: layouts -> boxes -> replica groups -> overlaps -> descriptors.
+// Plain C++17; the device side lives in reshard.hip.
+#include "plan.h"
+
+#include <algorithm>
+#include <chrono>
+#include <cstring>
+#include <map>
+#include <unordered_map>
+
+namespace rs {
+
+namespace {
+
+int64_t elem_size_of(int dtype) {
+  switch (dtype) {
+    case RESHARD_DTYPE_U8:
+    case RESHARD_DTYPE_I8:
+    case RESHARD_DTYPE_BOOL:
+    case RESHARD_DTYPE_FP8_E4M3:
+    case RESHARD_DTYPE_FP8_E5M2:
+      return 1;
+    case RESHARD_DTYPE_BF16:
+    case RESHARD_DTYPE_F16:
+    case RESHARD_DTYPE_I16:
+      return 2;
+    case RESHARD_DTYPE_F32:
+    case RESHARD_DTYPE_I32:
+      return 4;
+    case RESHARD_DTYPE_F64:
+    case RESHARD_DTYPE_I64:
+      return 8;
+    default:
+      return 0;
+  }
+}
+
+std::vector<int64_t> box_key(int ndim, const Box& b) {
+  std::vector<int64_t> k(2 * ndim);
+  for (int d = 0; d < ndim; ++d) {
+    k[2 * d] = b.lo[d];
+    k[2 * d + 1] = b.hi[d];
+  }
+  return k;
+}
+
+// Groups the non-empty boxes of one tensor's layout by equality.  Groups come
+// out ordered by their lowest rank.
+void group_ranks(const Layout& L, int64_t tensor, std::vector<Group>* groups) {
+  std::map<std::vector<int64_t>, size_t> seen;
+  for (int64_t r = 0; r < L.nranks; ++r) {
+    Box b;
+    shard_box(L, r, &b);
+    if (box_empty(L.ndim, b)) continue;
+    auto key = box_key(L.ndim, b);
+    auto it = seen.find(key);
+    if (it == seen.end()) {
+      seen.emplace(std::move(key), groups->size());
+      groups->push_back(Group{tensor, b, {r}});
+    } else {
+      (*groups)[it->second].ranks.push_back(r);
+    }
+  }
+}
+
+// Unique source boxes of one tensor seen as a grid.  Along each tensor dim the
+// distinct non-empty source intervals are disjoint and cover the dim, and every
+// combination of them is some rank's box (each tensor dim's interval depends
+// only on the coordinates of the mesh dims that shard it).
+struct SourceGrid {
+  int ndim = 0;
+  std::vector<std::vector<std::pair<int64_t, int64_t>>> iv;  // per dim, sorted by lo
+  std::vector<int64_t> cell_stride;
+  std::unordered_map<int64_t, int64_t> cell_to_group;
+};
+
+int64_t interval_index(const std::vector<std::pair<int64_t, int64_t>>& v, int64_t lo) {
+  auto it = std::lower_bound(v.begin(), v.end(), std::make_pair(lo, INT64_MIN));
+  return int64_t(it - v.begin());
+}
+
+SourceGrid make_grid(int ndim, const std::vector<Group>& groups, size_t g_begin, size_t g_end) {
+  SourceGrid G;
+  G.ndim = ndim;
+  G.iv.resize(ndim);
+  for (int d = 0; d < ndim; ++d) {
+    auto& v = G.iv[d];
+    for (size_t g = g_begin; g < g_end; ++g) v.emplace_back(groups[g].box.lo[d], groups[g].box.hi[d]);
+    std::sort(v.begin(), v.end());
+    v.erase(std::unique(v.begin(), v.end()), v.end());
+  }
+  G.cell_stride.assign(ndim, 1);
+  for (int d = ndim - 2; d >= 0; --d) G.cell_stride[d] = G.cell_stride[d + 1] * int64_t(G.iv[d + 1].size());
+  for (size_t g = g_begin; g < g_end; ++g) {
+    int64_t cell = 0;
+    for (int d = 0; d < ndim; ++d) cell += interval_index(G.iv[d], groups[g].box.lo[d]) * G.cell_stride[d];
+    G.cell_to_group.emplace(cell, int64_t(g));
+  }
+  return G;
+}
+
+struct Dim {
+  int64_t e;   // extent
+  int64_t ss;  // source stride, bytes
+  int64_t sd;  // destination stride, bytes
+};
+
+uint32_t unit_for(int64_t bits) {
+  uint32_t u = 16;
+  while (u > 1 && (bits & int64_t(u - 1))) u >>= 1;
+  return u;
+}
+
+// Emits descriptors for a run of `run_bytes` contiguous bytes repeated over the
+// outer dims (inner -> outer order), splitting where the kernel's 31-bit item
+// indexing or its three outer dims would be exceeded.
+void emit(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_begin, uint32_t fanout,
+          int64_t src_off, int64_t dst_off, int64_t run_bytes, std::vector<Dim> outer) {
+  if (outer.size() > 3) {  // peel the outermost dim into separate descriptors
+    Dim top = outer.back();
+    outer.pop_back();
+    for (int64_t i = 0; i < top.e; ++i)
+      emit(P, piece, src_ptr, ref_begin, fanout, src_off + i * top.ss, dst_off + i * top.sd,
+           run_bytes, outer);
+    return;
+  }
+  int64_t bits = src_off | dst_off | run_bytes;
+  for (const Dim& d : outer) bits |= d.ss | d.sd;
+  const uint32_t unit = unit_for(bits);
+  const uint64_t run_units = uint64_t(run_bytes) / unit;
+  uint64_t rows = 1;
+  for (const Dim& d : outer) rows *= uint64_t(d.e);
+
+  if (run_units > kMaxItems) {  // split every row into column chunks
+    const int64_t chunk_units = int64_t(1) << 30;
+    for (int64_t c = 0; c < int64_t(run_units); c += chunk_units) {
+      int64_t n = std::min<int64_t>(chunk_units, int64_t(run_units) - c);
+      emit(P, piece, src_ptr, ref_begin, fanout, src_off + c * unit, dst_off + c * unit, n * unit, outer);
+    }
+    return;
+  }
+  if (rows * run_units > kMaxItems) {  // halve the outermost dim with extent > 1
+    for (int k = int(outer.size()) - 1; k >= 0; --k) {
+      if (outer[k].e < 2) continue;
+      std::vector<Dim> a = outer, b = outer;
+      int64_t h = outer[k].e / 2;
+      a[k].e = h;
+      b[k].e = outer[k].e - h;
+      emit(P, piece, src_ptr, ref_begin, fanout, src_off, dst_off, run_bytes, a);
+      emit(P, piece, src_ptr, ref_begin, fanout, src_off + h * outer[k].ss, dst_off + h * outer[k].sd,
+           run_bytes, b);
+      return;
+    }
+  }
+
+  reshard_descriptor_t D;
+  std::memset(&D, 0, sizeof(D));
+  D.src_offset = src_off;
+  D.dst_offset = dst_off;
+  // descriptor order: extent[0] outermost, extent[2] the fastest outer dim;
+  // `outer` is listed inner -> outer, so outer[j] goes to slot 2 - j.
+  for (int j = 0; j < 3; ++j) {
+    const int slot = 2 - j;
+    if (j < int(outer.size())) {
+      D.extent[slot] = uint32_t(outer[j].e);
+      D.src_stride[slot] = outer[j].ss;
+      D.dst_stride[slot] = outer[j].sd;
+    } else {
+      D.extent[slot] = 1;
+    }
+  }
+  D.run_units = uint32_t(run_units);
+  D.unit = unit;
+  D.src_ptr = src_ptr;
+  D.dst_ref_begin = ref_begin;
+  D.fanout = fanout;
+  magic_u31(D.run_units, &D.magic[0][0], &D.magic[0][1]);
+  magic_u31(D.extent[2], &D.magic[1][0], &D.magic[1][1]);
+  magic_u31(D.extent[1], &D.magic[2][0], &D.magic[2][1]);
+  D.piece = piece;
+  P->descs.push_back(D);
+  P->desc_cost.push_back(uint64_t(rows * run_units * unit) * (1 + fanout));
+}
+
+// Turns one overlap into descriptors: local offsets in the source and
+// destination shards, then adjacent dims are merged wherever both sides are
+// contiguous across them, and size-1 dims are dropped.
+void describe_piece(HostPlan* P, uint32_t piece_idx, uint32_t src_ptr, uint32_t ref_begin,
+                    uint32_t fanout, const Box& piece, const Box& sbox, const Box& dbox, int ndim,
+                    int64_t es) {
+  int64_t s_stride[kMaxDims], d_stride[kMaxDims];
+  int64_t ss = es, sd = es;
+  for (int k = ndim - 1; k >= 0; --k) {
+    s_stride[k] = ss;
+    d_stride[k] = sd;
+    ss *= sbox.hi[k] - sbox.lo[k];
+    sd *= dbox.hi[k] - dbox.lo[k];
+  }
+  int64_t src_off = 0, dst_off = 0;
+  for (int k = 0; k < ndim; ++k) {
+    src_off += (piece.lo[k] - sbox.lo[k]) * s_stride[k];
+    dst_off += (piece.lo[k] - dbox.lo[k]) * d_stride[k];
+  }
+  // Fold dims from the innermost outwards into the contiguous run while both
+  // sides stay contiguous; the rest become outer dims.
+  bool in_run = true;
+  int64_t run_bytes = es;
+  std::vector<Dim> outer;  // inner -> outer
+  for (int k = ndim - 1; k >= 0; --k) {
+    int64_t e = piece.hi[k] - piece.lo[k];
+    if (e == 1) continue;
+    if (in_run && s_stride[k] == run_bytes && d_stride[k] == run_bytes) {
+      run_bytes *= e;
+      continue;
+    }
+    in_run = false;
+    if (!outer.empty() && s_stride[k] == outer.back().e * outer.back().ss &&
+        d_stride[k] == outer.back().e * outer.back().sd) {
+      outer.back().e *= e;
+      continue;
+    }
+    outer.push_back(Dim{e, s_stride[k], d_stride[k]});
+  }
+  emit(P, piece_idx, src_ptr, ref_begin, fanout, src_off, dst_off, run_bytes, outer);
+}
+
+}  // namespace
+
+void magic_u31(uint32_t d, uint32_t* m, uint32_t* s) {
+  uint32_t l = 0;
+  while ((uint64_t(1) << l) < d) ++l;  // l = ceil(log2 d)
+  uint64_t mm = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+  *m = uint32_t(mm);
+  *s = l;
+}
+
+bool make_layout(int ndim, const int64_t* shape, int dtype, int mesh_ndim, const int64_t* mesh,
+                 const int32_t* placements, Layout* out, std::string* err) {
+  if (ndim < 1 || ndim > kMaxDims) {
+    *err = "ndim must be in [1, " + std::to_string(kMaxDims) + "]";
+    return false;
+  }
+  if (mesh_ndim < 1 || mesh_ndim > kMaxMeshDims) {
+    *err = "mesh_ndim must be in [1, " + std::to_string(kMaxMeshDims) + "]";
+    return false;
+  }
+  if (!shape || !mesh || !placements) {
+    *err = "NULL shape, mesh or placements";
+    return false;
+  }
+  Layout L;
+  L.ndim = ndim;
+  L.dtype = dtype;
+  L.elem_size = elem_size_of(dtype);
+  if (L.elem_size == 0) {
+    *err = "unknown dtype " + std::to_string(dtype);
+    return false;
+  }
+  for (int k = 0; k < ndim; ++k) {
+    if (shape[k] < 0 || shape[k] > (int64_t(1) << 40)) {
+      *err = "global_shape[" + std::to_string(k) + "] out of range";
+      return false;
+    }
+    L.shape[k] = shape[k];
+  }
+  L.mesh_ndim = mesh_ndim;
+  L.nranks = 1;
+  for (int m = 0; m < mesh_ndim; ++m) {
+    if (mesh[m] < 1 || mesh[m] > (int64_t(1) << 20)) {
+      *err = "mesh_shape[" + std::to_string(m) + "] must be in [1, 2^20]";
+      return false;
+    }
+    if (placements[m] != RESHARD_REPLICATE && (placements[m] < 0 || placements[m] >= ndim)) {
+      *err = "placements[" + std::to_string(m) + "] must be RESHARD_REPLICATE or a tensor dim";
+      return false;
+    }
+    L.mesh[m] = mesh[m];
+    L.place[m] = placements[m];
+    L.nranks *= mesh[m];
+    if (L.nranks > (int64_t(1) << 24)) {
+      *err = "mesh has more than 2^24 ranks";
+      return false;
+    }
+  }
+  *out = L;
+  return true;
+}
+
+void shard_box(const Layout& L, int64_t rank, Box* out) {
+  int64_t coord[kMaxMeshDims];
+  for (int m = L.mesh_ndim - 1; m >= 0; --m) {
+    coord[m] = rank % L.mesh[m];
+    rank /= L.mesh[m];
+  }
+  for (int k = 0; k < L.ndim; ++k) {
+    out->lo[k] = 0;
+    out->hi[k] = L.shape[k];
+  }
+  for (int m = 0; m < L.mesh_ndim; ++m) {
+    if (L.place[m] == RESHARD_REPLICATE) continue;
+    const int k = L.place[m];
+    const int64_t lo = out->lo[k], hi = out->hi[k];
+    const int64_t chunk = (hi - lo + L.mesh[m] - 1) / L.mesh[m];
+    out->lo[k] = std::min(hi, lo + coord[m] * chunk);
+    out->hi[k] = std::min(hi, lo + (coord[m] + 1) * chunk);
+  }
+}
+
+bool box_empty(int ndim, const Box& b) {
+  for (int k = 0; k < ndim; ++k)
+    if (b.hi[k] <= b.lo[k]) return true;
+  return false;
+}
+
+int64_t box_numel(int ndim, const Box& b) {
+  int64_t n = 1;
+  for (int k = 0; k < ndim; ++k) n *= std::max<int64_t>(0, b.hi[k] - b.lo[k]);
+  return n;
+}
+
+reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const* dst, HostPlan* P,
+                            std::string* err) {
+  auto t0 = std::chrono::steady_clock::now();
+  if (n < 1) {
+    *err = "a plan needs at least one tensor";
+    return RESHARD_ERR_INVALID_ARGUMENT;
+  }
+  P->n_tensors = n;
+  for (int t = 0; t < n; ++t) {
+    if (!src[t] || !dst[t]) {
+      *err = "NULL layout for tensor " + std::to_string(t);
+      return RESHARD_ERR_INVALID_ARGUMENT;
+    }
+    const Layout& S = *src[t];
+    const Layout& D = *dst[t];
+    if (S.ndim != D.ndim || S.elem_size != D.elem_size || S.dtype != D.dtype ||
+        !std::equal(S.shape, S.shape + S.ndim, D.shape)) {
+      *err = "tensor " + std::to_string(t) + ": source and destination differ in global shape or dtype";
+      return RESHARD_ERR_LAYOUT_MISMATCH;
+    }
+    P->src.push_back(S);
+    P->dst.push_back(D);
+    P->src_base.push_back(P->n_src_ptrs);
+    P->dst_base.push_back(P->n_dst_ptrs);
+    P->n_src_ptrs += S.nranks;
+    P->n_dst_ptrs += D.nranks;
+  }
+  if (P->n_src_ptrs + P->n_dst_ptrs > (int64_t(1) << 31)) {
+    *err = "too many ranks in the plan";
+    return RESHARD_ERR_INVALID_ARGUMENT;
+  }
+  P->src_needed.assign(P->n_src_ptrs, 0);
+  P->dst_needed.assign(P->n_dst_ptrs, 0);
+
+  std::vector<int64_t> load(P->n_src_ptrs, 0);  // bytes read from each source slot
+  for (int t = 0; t < n; ++t) {
+    const Layout& S = P->src[t];
+    const Layout& D = P->dst[t];
+    const int nd = S.ndim;
+    const int64_t es = S.elem_size;
+    int64_t numel = 1;
+    for (int k = 0; k < nd; ++k) numel *= S.shape[k];
+    P->global_bytes += numel * es;
+
+    const size_t sg0 = P->src_groups.size();
+    group_ranks(S, t, &P->src_groups);
+    const size_t sg1 = P->src_groups.size();
+    const size_t dg0 = P->dst_groups.size();
+    group_ranks(D, t, &P->dst_groups);
+    const size_t dg1 = P->dst_groups.size();
+    for (size_t g = sg0; g < sg1; ++g)
+      for (int64_t r : P->src_groups[g].ranks) P->src_needed[P->src_base[t] + r] = 1;
+    for (size_t g = dg0; g < dg1; ++g)
+      for (int64_t r : P->dst_groups[g].ranks) P->dst_needed[P->dst_base[t] + r] = 1;
+    if (sg0 == sg1) continue;  // empty tensor
+
+    SourceGrid grid = make_grid(nd, P->src_groups, sg0, sg1);
+    for (size_t g = dg0; g < dg1; ++g) {
+      const Group& dgrp = P->dst_groups[g];
+      // per dim, the range of source intervals that overlap this destination box
+      int64_t first[kMaxDims], last[kMaxDims], idx[kMaxDims];
+      for (int k = 0; k < nd; ++k) {
+        const auto& v = grid.iv[k];
+        auto lo_it = std::upper_bound(v.begin(), v.end(), std::make_pair(dgrp.box.lo[k], INT64_MAX));
+        first[k] = std::max<int64_t>(0, int64_t(lo_it - v.begin()) - 1);
+        last[k] = first[k];
+        while (last[k] + 1 < int64_t(v.size()) && v[last[k] + 1].first < dgrp.box.hi[k]) ++last[k];
+        idx[k] = first[k];
+      }
+      for (;;) {  // every cell in the product of those ranges
+        int64_t cell = 0;
+        Box box;
+        bool empty = false;
+        for (int k = 0; k < nd; ++k) {
+          cell += idx[k] * grid.cell_stride[k];
+          box.lo[k] = std::max(dgrp.box.lo[k], grid.iv[k][idx[k]].first);
+          box.hi[k] = std::min(dgrp.box.hi[k], grid.iv[k][idx[k]].second);
+          if (box.hi[k] <= box.lo[k]) empty = true;
+        }
+        if (!empty) {
+          auto it = grid.cell_to_group.find(cell);
+          if (it == grid.cell_to_group.end()) {
+            *err = "internal: source grid cell without a rank";
+            return RESHARD_ERR_INVALID_ARGUMENT;
+          }
+          const Group& sgrp = P->src_groups[it->second];
+          // least-loaded replica of this source box; ties go to the lowest rank
+          int64_t best = sgrp.ranks[0];
+          for (int64_t r : sgrp.ranks)
+            if (load[P->src_base[t] + r] < load[P->src_base[t] + best]) best = r;
+          const int64_t bytes = box_numel(nd, box) * es;
+          load[P->src_base[t] + best] += bytes;
+          Piece pc{t, best, it->second, int64_t(g), box, bytes};
+          const uint32_t piece_idx = uint32_t(P->pieces.size());
+          P->pieces.push_back(pc);
+          const uint32_t ref_begin = uint32_t(P->refs.size());
+          for (int64_t r : dgrp.ranks) P->refs.push_back(uint32_t(P->dst_base[t] + r));
+          const uint32_t fanout = uint32_t(dgrp.ranks.size());
+          describe_piece(P, piece_idx, uint32_t(P->src_base[t] + best), ref_begin, fanout, box,
+                         sgrp.box, dgrp.box, nd, es);
+          P->bytes_read += bytes;
+          P->bytes_written += bytes * fanout;
+          P->n_dst_writes += fanout;
+        }
+        int k = nd - 1;
+        while (k >= 0 && idx[k] == last[k]) {
+          idx[k] = first[k];
+          --k;
+        }
+        if (k < 0) break;
+        ++idx[k];
+      }
+    }
+  }
+  auto t1 = std::chrono::steady_clock::now();
+  P->plan_host_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
+  return RESHARD_OK;
+}
+
+std::vector<WgStart> partition(const HostPlan& P, uint32_t n_wg) {
+  std::vector<WgStart> out(size_t(n_wg) + 1);
+  const size_t nd = P.descs.size();
+  std::vector<uint64_t> cum(nd + 1, 0);
+  for (size_t i = 0; i < nd; ++i) cum[i + 1] = cum[i] + P.desc_cost[i];
+  const uint64_t total = cum[nd];
+  size_t d = 0;
+  for (uint32_t w = 0; w <= n_wg; ++w) {
+    // boundary w at traffic w * total / n_wg (128-bit safe: total < 2^50, n_wg < 2^14)
+    const uint64_t c = (w == n_wg) ? total : uint64_t((unsigned __int128)total * w / n_wg);
+    while (d < nd && cum[d + 1] <= c) ++d;
+    if (d >= nd) {
+      out[w] = WgStart{uint32_t(nd), 0};
+      continue;
+    }
+    const reshard_descriptor_t& D = P.descs[d];
+    const uint64_t per_item = uint64_t(D.unit) * (1 + D.fanout);
+    out[w] = WgStart{uint32_t(d), uint32_t((c - cum[d]) / per_item)};
+  }
+  return out;
+}
+
+}  // namespace rs

@@ -1,0 +1,105 @@
+// Host planner of the reshard library: plain C++17, no HIP.
+//
+// From two DTensor layouts (global shape + device mesh + placements) it finds
+// every overlap between a source shard and a destination shard and turns each
+// overlap into copy descriptors for the fused gfx950 copy kernel.  The pages
+// that describe the Reshard collective fix the principle -- compute the exact
+// intersections of source and destination shards, then move only those
+// (news.bpdata.com write-up, "the Reshard collective" section; techfeed.io
+// write-up, "reformulation" section and its 8x8 example) -- and the
+// send-once-then-replicate treatment of destination replicas (techfeed.io,
+// "NVIDIA's NVLink implementation" section).
+#pragma once
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "reshard.h"
+
+namespace rs {
+
+constexpr int kMaxDims = RESHARD_MAX_NDIM;
+constexpr int kMaxMeshDims = RESHARD_MAX_MESH_NDIM;
+
+struct Layout {
+  int ndim = 0;
+  int64_t shape[kMaxDims] = {};
+  int dtype = 0;
+  int64_t elem_size = 0;
+  int mesh_ndim = 0;
+  int64_t mesh[kMaxMeshDims] = {};
+  int32_t place[kMaxMeshDims] = {};
+  int64_t nranks = 0;
+};
+
+struct Box {
+  int64_t lo[kMaxDims];
+  int64_t hi[kMaxDims];
+};
+
+// Validates and fills a layout; returns false with a message on bad input.
+bool make_layout(int ndim, const int64_t* shape, int dtype, int mesh_ndim, const int64_t* mesh,
+                 const int32_t* placements, Layout* out, std::string* err);
+
+// Box of `rank` (row-major mesh coordinates, nested ceil-chunk splitting).
+void shard_box(const Layout& L, int64_t rank, Box* out);
+bool box_empty(int ndim, const Box& b);
+int64_t box_numel(int ndim, const Box& b);
+
+// A set of ranks of one tensor that hold the same non-empty box.
+struct Group {
+  int64_t tensor;
+  Box box;
+  std::vector<int64_t> ranks;  // ascending
+};
+
+// One overlap of a unique source box and a unique destination box.
+struct Piece {
+  int64_t tensor;
+  int64_t src_rank;   // replica chosen to read from
+  int64_t src_group;  // index into HostPlan::src_groups
+  int64_t dst_group;  // index into HostPlan::dst_groups
+  Box box;            // global coordinates
+  int64_t bytes;
+};
+
+// Start of one workgroup's share of the copy: descriptor index and item index.
+struct WgStart {
+  uint32_t desc;
+  uint32_t item;
+};
+
+struct HostPlan {
+  int n_tensors = 0;
+  std::vector<Layout> src, dst;
+  std::vector<int64_t> src_base, dst_base;  // first pointer-array slot of each tensor
+  int64_t n_src_ptrs = 0, n_dst_ptrs = 0;
+  std::vector<uint8_t> src_needed, dst_needed;  // 1 if that pointer slot holds a non-empty shard
+  std::vector<Group> src_groups, dst_groups;
+  std::vector<Piece> pieces;
+  std::vector<reshard_descriptor_t> descs;
+  std::vector<uint32_t> refs;       // fan-out: destination pointer slots (0-based in dst_ptrs)
+  std::vector<uint64_t> desc_cost;  // bytes read + written by each descriptor
+  int64_t global_bytes = 0, bytes_read = 0, bytes_written = 0, n_dst_writes = 0;
+  double plan_host_us = 0.0;
+};
+
+// Builds the host plan of n tensors.  Returns RESHARD_OK or an error code with
+// a message in *err.
+reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const* dst,
+                            HostPlan* out, std::string* err);
+
+// Splits the plan's copy traffic into `n_wg` equal shares at item granularity
+// and returns n_wg + 1 starts (the last one is {n_desc, 0}).
+std::vector<WgStart> partition(const HostPlan& plan, uint32_t n_wg);
+
+// Division by an invariant 32-bit divisor d >= 1 for numerators below 2^31:
+// q = (mulhi(n, m) + n) >> s.  Granlund & Montgomery, "Division by invariant
+// integers using multiplication" (PLDI 1994), round-up multiplier.
+void magic_u31(uint32_t d, uint32_t* m, uint32_t* s);
+
+// Largest item count a descriptor may hold (items are indexed in 31 bits).
+constexpr uint64_t kMaxItems = (uint64_t(1) << 31) - 1;
+
+}  // namespace rs

@@ -1,0 +1,510 @@
+// C ABI of the reshard library and its gfx950 copy kernel.
+//
+// Execute = one launch of reshard_copy_kernel.  The plan's descriptor table
+// sits in device memory; each workgroup owns an equal share of the plan's
+// traffic (bytes read + bytes written) and walks the descriptors that share
+// covers.  A descriptor copies rows of contiguous items (1-16 bytes each):
+// every item is loaded once and stored to each destination replica (the
+// single-GPU form of "send each contribution once, replicate locally":
+// techfeed.io write-up, "NVIDIA's NVLink implementation" section).  Data only
+// moves through integer registers, so the copy is bit-exact for every dtype.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstring>
+#include <mutex>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "plan.h"
+#include "reshard.h"
+
+struct reshard_layout_s {
+  rs::Layout L;
+};
+
+namespace {
+
+constexpr int kBlock = 256;            // threads per workgroup (4 wave64s)
+constexpr int kKargPtrs = 120;         // pointer slots passed in kernel arguments
+constexpr int kSlots = 8;              // device pointer-table slots for bigger plans
+constexpr int kMaxWgPerCu = 8;         // cap on resident workgroups per CU used for the grid
+constexpr uint64_t kMinTrafficPerWg = 64 * 1024;  // no workgroup gets less than this
+
+struct KargPtrs {
+  const void* p[kKargPtrs];
+};
+
+thread_local std::string g_err;
+
+reshard_status_t fail(reshard_status_t s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+reshard_status_t hip_fail(hipError_t e, const char* what) {
+  return fail(e == hipErrorOutOfMemory ? RESHARD_ERR_OUT_OF_MEMORY : RESHARD_ERR_HIP,
+              std::string(what) + ": " + hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- device code
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// q = n / d for n < 2^31 with the planner's round-up multiplier (m, s).
+__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t s) {
+  return (__umulhi(n, m) + n) >> s;
+}
+
+struct ItemOffsets {
+  uint64_t src, dst;
+};
+
+// Byte offsets (relative to the shard pointers) of item f of descriptor D.
+__device__ __forceinline__ ItemOffsets item_offsets(const reshard_descriptor_t& D, uint32_t f) {
+  const uint32_t row = div_magic(f, D.magic[0][0], D.magic[0][1]);
+  const uint32_t col = f - row * D.run_units;
+  const uint32_t t = div_magic(row, D.magic[1][0], D.magic[1][1]);
+  const uint32_t i2 = row - t * D.extent[2];
+  const uint32_t i0 = div_magic(t, D.magic[2][0], D.magic[2][1]);
+  const uint32_t i1 = t - i0 * D.extent[1];
+  const uint64_t c = uint64_t(col) * D.unit;
+  ItemOffsets o;
+  o.src = uint64_t(D.src_offset) + uint64_t(i0) * uint64_t(D.src_stride[0]) +
+          uint64_t(i1) * uint64_t(D.src_stride[1]) + uint64_t(i2) * uint64_t(D.src_stride[2]) + c;
+  o.dst = uint64_t(D.dst_offset) + uint64_t(i0) * uint64_t(D.dst_stride[0]) +
+          uint64_t(i1) * uint64_t(D.dst_stride[1]) + uint64_t(i2) * uint64_t(D.dst_stride[2]) + c;
+  return o;
+}
+
+
+__device__ __forceinline__ uintptr_t shard_ptr(const void* const* table, const KargPtrs& karg,
+                                               uint32_t i) {
+  return table ? reinterpret_cast<uintptr_t>(table[i]) : reinterpret_cast<uintptr_t>(karg.p[i]);
+}
+
+template <typename V>
+__device__ __forceinline__ V load_item(const uint8_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
+}
+
+template <typename V>
+__device__ __forceinline__ void store_item(uint8_t* p, V v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
+}
+
+// Items [lo, hi) of D with V-sized accesses: U items per thread in flight, all
+// loads issued before the stores; each loaded item is stored to every replica.
+template <typename V, int U>
+__device__ __forceinline__ void copy_span(const reshard_descriptor_t& D, const uint8_t* src,
+                                          const uint32_t* __restrict__ refs,
+                                          const void* const* table, const KargPtrs& karg,
+                                          uint32_t lo, uint32_t hi) {
+  for (uint32_t base = lo; base < hi; base += uint32_t(kBlock * U)) {
+    V v[U];
+    uint64_t doff[U];
+    bool ok[U];
+#pragma unroll
+    for (int k = 0; k < U; ++k) {
+      const uint32_t f = base + uint32_t(k * kBlock) + threadIdx.x;
+      ok[k] = f < hi;
+      const ItemOffsets o = item_offsets(D, ok[k] ? f : lo);
+      doff[k] = o.dst;
+      if (ok[k]) v[k] = load_item<V>(src + o.src);
+    }
+    for (uint32_t r = 0; r < D.fanout; ++r) {
+      uint8_t* dst = reinterpret_cast<uint8_t*>(shard_ptr(table, karg, refs[D.dst_ref_begin + r]));
+#pragma unroll
+      for (int k = 0; k < U; ++k)
+        if (ok[k]) store_item<V>(dst + doff[k], v[k]);
+    }
+  }
+}
+
+// Same traffic bytewise, for shard pointers not aligned to the descriptor's unit.
+__device__ void copy_span_bytes(const reshard_descriptor_t& D, const uint8_t* src,
+                                const uint32_t* __restrict__ refs, const void* const* table,
+                                const KargPtrs& karg, uint32_t lo, uint32_t hi) {
+  for (uint32_t f = lo + threadIdx.x; f < hi; f += kBlock) {
+    const ItemOffsets o = item_offsets(D, f);
+    for (uint32_t r = 0; r < D.fanout; ++r) {
+      uint8_t* dst = reinterpret_cast<uint8_t*>(shard_ptr(table, karg, refs[D.dst_ref_begin + r]));
+      for (uint32_t b = 0; b < D.unit; ++b) dst[o.dst + b] = src[o.src + b];
+    }
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
+    const reshard_descriptor_t* __restrict__ descs, uint32_t n_desc,
+    const uint32_t* __restrict__ refs, const rs::WgStart* __restrict__ starts,
+    const void* const* __restrict__ table, KargPtrs karg) {
+  const rs::WgStart a = starts[blockIdx.x];
+  const rs::WgStart b = starts[blockIdx.x + 1];
+  for (uint32_t d = a.desc; d < n_desc && d <= b.desc; ++d) {
+    const reshard_descriptor_t& D = descs[d];
+    const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.run_units;
+    const uint32_t lo = (d == a.desc) ? a.item : 0u;
+    const uint32_t hi = (d == b.desc) ? b.item : items;
+    if (lo >= hi) continue;
+    const uint8_t* src = reinterpret_cast<const uint8_t*>(shard_ptr(table, karg, D.src_ptr));
+    uintptr_t bits = reinterpret_cast<uintptr_t>(src);
+    for (uint32_t r = 0; r < D.fanout; ++r) bits |= shard_ptr(table, karg, refs[D.dst_ref_begin + r]);
+    if (bits & (D.unit - 1)) {
+      copy_span_bytes(D, src, refs, table, karg, lo, hi);
+      continue;
+    }
+    switch (D.unit) {
+      case 16: copy_span<u32x4, 4>(D, src, refs, table, karg, lo, hi); break;
+      case 8: copy_span<u32x2, 4>(D, src, refs, table, karg, lo, hi); break;
+      case 4: copy_span<uint32_t, 4>(D, src, refs, table, karg, lo, hi); break;
+      case 2: copy_span<uint16_t, 4>(D, src, refs, table, karg, lo, hi); break;
+      default: copy_span<uint8_t, 4>(D, src, refs, table, karg, lo, hi); break;
+    }
+  }
+}
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+}  // namespace
+
+// ------------------------------------------------------------------ host side
+
+struct reshard_plan_s {
+  rs::HostPlan host;
+  std::mutex mu;
+  bool uploaded = false;
+  int device = -1;
+  uint32_t n_wg = 0;
+  void* table = nullptr;  // device: descriptors | refs (absolute pointer slots) | starts
+  const reshard_descriptor_t* d_descs = nullptr;
+  const uint32_t* d_refs = nullptr;
+  const rs::WgStart* d_starts = nullptr;
+  // pointer-table slots, used when the pointers do not fit in kernel arguments
+  int64_t n_ptrs = 0;
+  void* d_slots = nullptr;
+  void** h_slots = nullptr;  // pinned host staging, kSlots * n_ptrs entries
+  hipEvent_t ev[kSlots] = {};
+  bool ev_live[kSlots] = {};
+  int next_slot = 0;
+  int last_slot = -1;
+};
+
+namespace {
+
+reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (p->uploaded) {
+    if (dev != p->device)
+      return fail(RESHARD_ERR_DEVICE_MISMATCH, "plan was uploaded to device " +
+                                                   std::to_string(p->device) + ", current device is " +
+                                                   std::to_string(dev));
+    return RESHARD_OK;
+  }
+  const rs::HostPlan& H = p->host;
+  uint32_t n_wg = 0;
+  if (!H.descs.empty()) {
+    int cus = 0, occ = 0;
+    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reshard_copy_kernel, kBlock, 0);
+    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
+    occ = std::max(1, std::min(occ, kMaxWgPerCu));
+    uint64_t traffic = 0;
+    for (uint64_t c : H.desc_cost) traffic += c;
+    const uint64_t want = std::max<uint64_t>(1, (traffic + kMinTrafficPerWg - 1) / kMinTrafficPerWg);
+    n_wg = uint32_t(std::min<uint64_t>(uint64_t(cus) * uint64_t(occ), want));
+  }
+  const std::vector<rs::WgStart> starts = rs::partition(H, n_wg);
+  const size_t desc_bytes = H.descs.size() * sizeof(reshard_descriptor_t);
+  const size_t refs_off = align_up(desc_bytes, 256);
+  const size_t starts_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);
+  const size_t total = starts_off + starts.size() * sizeof(rs::WgStart);
+  std::vector<uint8_t> img(total, 0);
+  if (desc_bytes) std::memcpy(img.data(), H.descs.data(), desc_bytes);
+  uint32_t* r = reinterpret_cast<uint32_t*>(img.data() + refs_off);
+  for (size_t i = 0; i < H.refs.size(); ++i) r[i] = uint32_t(H.n_src_ptrs) + H.refs[i];
+  std::memcpy(img.data() + starts_off, starts.data(), starts.size() * sizeof(rs::WgStart));
+
+  void* table = nullptr;
+  e = hipMalloc(&table, total);
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc(descriptor table)");
+  e = hipMemcpyAsync(table, img.data(), total, hipMemcpyHostToDevice, stream);
+  if (e == hipSuccess) e = hipStreamSynchronize(stream);
+  if (e != hipSuccess) {
+    (void)hipFree(table);
+    return hip_fail(e, "descriptor table upload");
+  }
+  p->n_ptrs = H.n_src_ptrs + H.n_dst_ptrs;
+  if (p->n_ptrs > kKargPtrs) {
+    const size_t bytes = size_t(kSlots) * size_t(p->n_ptrs) * sizeof(void*);
+    e = hipMalloc(&p->d_slots, bytes);
+    if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&p->h_slots), bytes, hipHostMallocDefault);
+    for (int s = 0; s < kSlots && e == hipSuccess; ++s)
+      e = hipEventCreateWithFlags(&p->ev[s], hipEventDisableTiming);
+    if (e != hipSuccess) {
+      (void)hipFree(table);
+      return hip_fail(e, "pointer-table slots");
+    }
+  }
+  p->table = table;
+  p->d_descs = reinterpret_cast<const reshard_descriptor_t*>(table);
+  p->d_refs = reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + refs_off);
+  p->d_starts = reinterpret_cast<const rs::WgStart*>(static_cast<uint8_t*>(table) + starts_off);
+  p->n_wg = n_wg;
+  p->device = dev;
+  p->uploaded = true;
+  return RESHARD_OK;
+}
+
+reshard_status_t make_plan(int n, const reshard_layout_t* src, const reshard_layout_t* dst,
+                           reshard_plan_t* out) {
+  if (!out) return fail(RESHARD_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (n < 1 || !src || !dst) return fail(RESHARD_ERR_INVALID_ARGUMENT, "need n >= 1 layouts");
+  std::vector<const rs::Layout*> s(n), d(n);
+  for (int t = 0; t < n; ++t) {
+    if (!src[t] || !dst[t]) return fail(RESHARD_ERR_INVALID_ARGUMENT, "NULL layout");
+    s[t] = &src[t]->L;
+    d[t] = &dst[t]->L;
+  }
+  reshard_plan_s* p = new (std::nothrow) reshard_plan_s();
+  if (!p) return fail(RESHARD_ERR_OUT_OF_MEMORY, "plan allocation");
+  std::string err;
+  reshard_status_t st;
+  try {
+    st = rs::build_plan(n, s.data(), d.data(), &p->host, &err);
+  } catch (const std::bad_alloc&) {
+    st = RESHARD_ERR_OUT_OF_MEMORY;
+    err = "host memory exhausted while planning";
+  }
+  if (st != RESHARD_OK) {
+    delete p;
+    return fail(st, err);
+  }
+  *out = p;
+  return RESHARD_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t reshard_dtype_size(int dtype) {
+  rs::Layout L;
+  std::string err;
+  const int64_t one = 1;
+  const int32_t rep = RESHARD_REPLICATE;
+  if (!rs::make_layout(1, &one, dtype, 1, &one, &rep, &L, &err)) return 0;
+  return L.elem_size;
+}
+
+reshard_status_t reshard_layout_create(int ndim, const int64_t* global_shape, int dtype,
+                                       int mesh_ndim, const int64_t* mesh_shape,
+                                       const int32_t* placements, reshard_layout_t* out) {
+  if (!out) return fail(RESHARD_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  rs::Layout L;
+  std::string err;
+  if (!rs::make_layout(ndim, global_shape, dtype, mesh_ndim, mesh_shape, placements, &L, &err))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, err);
+  reshard_layout_s* h = new (std::nothrow) reshard_layout_s{L};
+  if (!h) return fail(RESHARD_ERR_OUT_OF_MEMORY, "layout allocation");
+  *out = h;
+  return RESHARD_OK;
+}
+
+void reshard_layout_destroy(reshard_layout_t layout) { delete layout; }
+
+reshard_status_t reshard_layout_num_ranks(reshard_layout_t layout, int64_t* out) {
+  if (!layout || !out) return fail(RESHARD_ERR_INVALID_ARGUMENT, "NULL argument");
+  *out = layout->L.nranks;
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_layout_shard_box(reshard_layout_t layout, int64_t rank, int64_t* offset,
+                                          int64_t* extent) {
+  if (!layout || !offset || !extent) return fail(RESHARD_ERR_INVALID_ARGUMENT, "NULL argument");
+  if (rank < 0 || rank >= layout->L.nranks)
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "rank out of range");
+  rs::Box b;
+  rs::shard_box(layout->L, rank, &b);
+  for (int k = 0; k < layout->L.ndim; ++k) {
+    offset[k] = b.lo[k];
+    extent[k] = b.hi[k] - b.lo[k];
+  }
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_plan_create(reshard_layout_t src, reshard_layout_t dst, reshard_plan_t* out) {
+  return make_plan(1, &src, &dst, out);
+}
+
+reshard_status_t reshard_plan_create_batched(int n, const reshard_layout_t* src,
+                                             const reshard_layout_t* dst, reshard_plan_t* out) {
+  return make_plan(n, src, dst, out);
+}
+
+reshard_status_t reshard_plan_upload(reshard_plan_t plan, void* stream) {
+  if (!plan) return fail(RESHARD_ERR_INVALID_ARGUMENT, "plan is NULL");
+  std::lock_guard<std::mutex> lock(plan->mu);
+  return upload_locked(plan, static_cast<hipStream_t>(stream));
+}
+
+reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptrs,
+                                 void* const* dst_ptrs, void* stream_arg) {
+  if (!plan) return fail(RESHARD_ERR_INVALID_ARGUMENT, "plan is NULL");
+  const rs::HostPlan& H = plan->host;
+  if ((H.n_src_ptrs && !src_ptrs) || (H.n_dst_ptrs && !dst_ptrs))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "pointer array is NULL");
+  for (int64_t i = 0; i < H.n_src_ptrs; ++i)
+    if (H.src_needed[i] && !src_ptrs[i])
+      return fail(RESHARD_ERR_NULL_SHARD, "src_ptrs[" + std::to_string(i) + "] is NULL but its shard is not empty");
+  for (int64_t i = 0; i < H.n_dst_ptrs; ++i)
+    if (H.dst_needed[i] && !dst_ptrs[i])
+      return fail(RESHARD_ERR_NULL_SHARD, "dst_ptrs[" + std::to_string(i) + "] is NULL but its shard is not empty");
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_arg);
+  std::lock_guard<std::mutex> lock(plan->mu);
+  reshard_status_t st = upload_locked(plan, stream);
+  if (st != RESHARD_OK) return st;
+  if (H.descs.empty()) return RESHARD_OK;
+
+  KargPtrs karg;
+  std::memset(&karg, 0, sizeof(karg));
+  const void* const* table = nullptr;
+  int slot = -1;
+  hipError_t e;
+  if (plan->n_ptrs <= kKargPtrs) {
+    for (int64_t i = 0; i < H.n_src_ptrs; ++i) karg.p[i] = src_ptrs[i];
+    for (int64_t i = 0; i < H.n_dst_ptrs; ++i) karg.p[H.n_src_ptrs + i] = dst_ptrs[i];
+  } else {
+    const size_t n = size_t(plan->n_ptrs);
+    auto same = [&](int s) {
+      void** h = plan->h_slots + size_t(s) * n;
+      for (int64_t i = 0; i < H.n_src_ptrs; ++i)
+        if (h[i] != src_ptrs[i]) return false;
+      for (int64_t i = 0; i < H.n_dst_ptrs; ++i)
+        if (h[H.n_src_ptrs + i] != dst_ptrs[i]) return false;
+      return true;
+    };
+    if (plan->last_slot >= 0 && same(plan->last_slot)) {
+      slot = plan->last_slot;  // already on the device; no copy
+    } else {
+      slot = plan->next_slot;
+      plan->next_slot = (plan->next_slot + 1) % kSlots;
+      if (plan->ev_live[slot]) {  // the slot's last user must be done with it
+        e = hipEventSynchronize(plan->ev[slot]);
+        if (e != hipSuccess) return hip_fail(e, "hipEventSynchronize(pointer slot)");
+      }
+      void** h = plan->h_slots + size_t(slot) * n;
+      for (int64_t i = 0; i < H.n_src_ptrs; ++i) h[i] = const_cast<void*>(src_ptrs[i]);
+      for (int64_t i = 0; i < H.n_dst_ptrs; ++i) h[H.n_src_ptrs + i] = dst_ptrs[i];
+      void* d = static_cast<void**>(plan->d_slots) + size_t(slot) * n;
+      e = hipMemcpyAsync(d, h, n * sizeof(void*), hipMemcpyHostToDevice, stream);
+      if (e != hipSuccess) {
+        plan->last_slot = -1;
+        return hip_fail(e, "pointer-table copy");
+      }
+      plan->last_slot = slot;
+    }
+    table = reinterpret_cast<const void* const*>(static_cast<void**>(plan->d_slots) + size_t(slot) * n);
+  }
+  hipLaunchKernelGGL(reshard_copy_kernel, dim3(plan->n_wg), dim3(kBlock), 0, stream, plan->d_descs,
+                     uint32_t(H.descs.size()), plan->d_refs, plan->d_starts, table, karg);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "reshard_copy_kernel launch");
+  if (slot >= 0) {
+    e = hipEventRecord(plan->ev[slot], stream);
+    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(pointer slot)");
+    plan->ev_live[slot] = true;
+  }
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_plan_stats(reshard_plan_t plan, reshard_plan_stats_t* out) {
+  if (!plan || !out) return fail(RESHARD_ERR_INVALID_ARGUMENT, "NULL argument");
+  const rs::HostPlan& H = plan->host;
+  std::memset(out, 0, sizeof(*out));
+  out->n_tensors = H.n_tensors;
+  out->n_src_ptrs = H.n_src_ptrs;
+  out->n_dst_ptrs = H.n_dst_ptrs;
+  out->n_pieces = int64_t(H.pieces.size());
+  out->n_dst_writes = H.n_dst_writes;
+  out->global_bytes = H.global_bytes;
+  out->bytes_read = H.bytes_read;
+  out->bytes_written = H.bytes_written;
+  out->n_descriptors = int64_t(H.descs.size());
+  out->table_bytes = int64_t(H.descs.size() * sizeof(reshard_descriptor_t) + H.refs.size() * 4);
+  out->n_workgroups = plan->n_wg;
+  out->plan_host_us = H.plan_host_us;
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_plan_pieces(reshard_plan_t plan, int64_t capacity, reshard_piece_t* out,
+                                     int64_t* n_total) {
+  if (!plan || !n_total || capacity < 0 || (capacity > 0 && !out))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "bad argument");
+  const rs::HostPlan& H = plan->host;
+  *n_total = int64_t(H.pieces.size());
+  for (int64_t i = 0; i < std::min<int64_t>(capacity, *n_total); ++i) {
+    const rs::Piece& pc = H.pieces[i];
+    reshard_piece_t& o = out[i];
+    std::memset(&o, 0, sizeof(o));
+    o.tensor = pc.tensor;
+    o.src_rank = pc.src_rank;
+    o.src_group = pc.src_group;
+    o.dst_group = pc.dst_group;
+    o.fanout = int64_t(H.dst_groups[pc.dst_group].ranks.size());
+    const int nd = H.src[pc.tensor].ndim;
+    for (int k = 0; k < nd; ++k) {
+      o.lo[k] = pc.box.lo[k];
+      o.hi[k] = pc.box.hi[k];
+    }
+  }
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_plan_piece_fanout(reshard_plan_t plan, int64_t index, int64_t capacity,
+                                           int64_t* ranks, int64_t* n_total) {
+  if (!plan || !n_total || capacity < 0 || (capacity > 0 && !ranks))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "bad argument");
+  const rs::HostPlan& H = plan->host;
+  if (index < 0 || index >= int64_t(H.pieces.size()))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "piece index out of range");
+  const auto& rk = H.dst_groups[H.pieces[index].dst_group].ranks;
+  *n_total = int64_t(rk.size());
+  for (int64_t i = 0; i < std::min<int64_t>(capacity, *n_total); ++i) ranks[i] = rk[i];
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_plan_descriptors(reshard_plan_t plan, int64_t capacity,
+                                          reshard_descriptor_t* out, int64_t* n_desc,
+                                          int64_t ref_capacity, uint32_t* refs, int64_t* n_refs) {
+  if (!plan || !n_desc || !n_refs || capacity < 0 || ref_capacity < 0 ||
+      (capacity > 0 && !out) || (ref_capacity > 0 && !refs))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "bad argument");
+  const rs::HostPlan& H = plan->host;
+  *n_desc = int64_t(H.descs.size());
+  *n_refs = int64_t(H.refs.size());
+  for (int64_t i = 0; i < std::min<int64_t>(capacity, *n_desc); ++i) out[i] = H.descs[i];
+  for (int64_t i = 0; i < std::min<int64_t>(ref_capacity, *n_refs); ++i) refs[i] = H.refs[i];
+  return RESHARD_OK;
+}
+
+void reshard_plan_destroy(reshard_plan_t plan) {
+  if (!plan) return;
+  if (plan->table) (void)hipFree(plan->table);
+  if (plan->d_slots) (void)hipFree(plan->d_slots);
+  if (plan->h_slots) (void)hipHostFree(plan->h_slots);
+  for (int s = 0; s < kSlots; ++s)
+    if (plan->ev[s]) (void)hipEventDestroy(plan->ev[s]);
+  delete plan;
+}
+
+const char* reshard_last_error(void) { return g_err.c_str(); }
+
+}  // extern "C"

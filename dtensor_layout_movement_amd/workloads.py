@@ -127,22 +127,27 @@ WORKLOADS = {
 }
 
 
-def generator(seed: int, tensor_index: int) -> torch.Generator:
-    return torch.Generator().manual_seed(1000 * seed + tensor_index)
+def generator(seed: int, tensor_index: int, device="cpu") -> torch.Generator:
+    return torch.Generator(device=device).manual_seed(1000 * seed + tensor_index)
 
 
-def make_global(spec: TensorSpec, values: str, seed: int, tensor_index: int = 0) -> torch.Tensor:
-    """The seeded global tensor (CPU, contiguous) of one workload tensor."""
-    g = generator(seed, tensor_index)
+def make_global(spec: TensorSpec, values: str, seed: int, tensor_index: int = 0,
+                device="cpu") -> torch.Tensor:
+    """The seeded global tensor (contiguous) of one workload tensor.  The CPU and
+    GPU generators are different streams: a given (seed, device) is reproducible."""
+    g = generator(seed, tensor_index, device)
     if values == "arange":
-        return torch.arange(_numel(spec.shape), dtype=torch.float32).reshape(spec.shape).to(spec.dtype)
+        n = _numel(spec.shape)
+        return torch.arange(n, dtype=torch.float32, device=device).reshape(spec.shape).to(spec.dtype)
     if values == "normal":
-        return (torch.randn(spec.shape, generator=g, dtype=torch.float32) * 0.02).to(spec.dtype)
+        x = torch.randn(spec.shape, generator=g, dtype=torch.float32, device=device)
+        return (x * 0.02).to(spec.dtype)
     if values == "uniform":
-        return (torch.rand(spec.shape, generator=g, dtype=torch.float32) * 2 - 1).to(spec.dtype)
+        x = torch.rand(spec.shape, generator=g, dtype=torch.float32, device=device)
+        return (x * 2 - 1).to(spec.dtype)
     if values == "raw":
         nbytes = _numel(spec.shape) * _esize(spec.dtype)
-        raw = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g)
+        raw = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g, device=device)
         return raw.view(spec.dtype).reshape(spec.shape)
     raise ValueError(f"unknown value kind {values!r}")
 

@@ -1,0 +1,234 @@
+/*
+ * reshard.h -- C ABI of the MI355X (gfx950) DTensor-to-DTensor reshard library.
+ *
+ * The operation.  A tensor of a given global shape is spread over a device mesh
+ * by per-mesh-dim placements (Shard(k) or Replicate): the DTensor description of
+ * a layout (techfeed.io write-up, "reformulation as DTensor-to-DTensor
+ * transfer" section; news.bpdata.com write-up, "the approach: refit as a
+ * DTensor-to-DTensor reshard" section).  A reshard takes the shards of a source
+ * layout and produces the shards of a destination layout.  It first computes
+ * the exact intersection of every source shard with every destination shard
+ * and then moves only those overlaps (news.bpdata.com, "the Reshard
+ * collective" section; the 8x8 example in which each of four column shards
+ * receives one 4x2 block from each of two row shards, techfeed.io,
+ * "reformulation" section).  Each overlap is read once and written to every
+ * destination replica that needs it (send once, replicate locally:
+ * techfeed.io, "NVIDIA's NVLink implementation" section).
+ *
+ * One process, one GPU.  Every source rank and destination rank is a separate
+ * shard buffer in the HBM of the GPU that is current when the plan is first
+ * executed.  The library computes the plan on the host, keeps a copy-descriptor
+ * table in device memory, and runs one fused copy kernel per execute.
+ *
+ * Layout semantics (readings the library fixes where the pages are silent):
+ *   - placement codes: RESHARD_REPLICATE (-1) or k >= 0 for Shard(k);
+ *   - ranks are numbered row-major over mesh coordinates;
+ *   - Shard(k) splits like torch.chunk: chunk = ceil(n / mesh_size); trailing
+ *     ranks may hold a short or an empty (zero-size) shard;
+ *   - several mesh dims that shard the same tensor dim nest left to right;
+ *   - each local shard is a contiguous row-major buffer whose shape is the
+ *     extent of its box (reshard_layout_shard_box).
+ * The copy is bytewise: bf16/fp32 NaN payloads, -0.0 and subnormals arrive
+ * unchanged.  Source and destination dtypes must match.
+ *
+ * Errors.  Every call returns a reshard_status_t and never throws; on failure
+ * reshard_last_error() gives a message for the calling thread.
+ */
+#ifndef RESHARD_H_
+#define RESHARD_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RESHARD_MAX_NDIM 8       /* tensor dims supported */
+#define RESHARD_MAX_MESH_NDIM 8  /* mesh dims supported */
+#define RESHARD_REPLICATE (-1)   /* placement code for Replicate */
+
+typedef enum reshard_status {
+  RESHARD_OK = 0,
+  RESHARD_ERR_INVALID_ARGUMENT = 1, /* bad shape, mesh, placement, dtype, rank or NULL out-pointer */
+  RESHARD_ERR_LAYOUT_MISMATCH = 2,  /* source and destination disagree on global shape or dtype */
+  RESHARD_ERR_NULL_SHARD = 3,       /* NULL pointer passed for a non-empty shard */
+  RESHARD_ERR_OUT_OF_MEMORY = 4,    /* host or device allocation failed */
+  RESHARD_ERR_HIP = 5,              /* a HIP runtime call failed (no device, launch error, ...) */
+  RESHARD_ERR_DEVICE_MISMATCH = 6,  /* executed on a device other than the plan's */
+} reshard_status_t;
+
+/* Element types.  Only the element size matters to the copy. */
+typedef enum reshard_dtype {
+  RESHARD_DTYPE_U8 = 0,
+  RESHARD_DTYPE_I8 = 1,
+  RESHARD_DTYPE_BOOL = 2,
+  RESHARD_DTYPE_FP8_E4M3 = 3,
+  RESHARD_DTYPE_FP8_E5M2 = 4,
+  RESHARD_DTYPE_BF16 = 5,
+  RESHARD_DTYPE_F16 = 6,
+  RESHARD_DTYPE_I16 = 7,
+  RESHARD_DTYPE_F32 = 8,
+  RESHARD_DTYPE_I32 = 9,
+  RESHARD_DTYPE_F64 = 10,
+  RESHARD_DTYPE_I64 = 11,
+} reshard_dtype_t;
+
+typedef struct reshard_layout_s* reshard_layout_t; /* immutable after create */
+typedef struct reshard_plan_s* reshard_plan_t;     /* immutable plan + its device table */
+
+/* Plan statistics; all byte counts are for one execute. */
+typedef struct reshard_plan_stats {
+  int64_t n_tensors;      /* tensors in the plan (1 unless batched) */
+  int64_t n_src_ptrs;     /* length of the src_ptrs array reshard_execute expects */
+  int64_t n_dst_ptrs;     /* length of the dst_ptrs array reshard_execute expects */
+  int64_t n_pieces;       /* source box x unique destination box overlaps */
+  int64_t n_dst_writes;   /* sum over pieces of their destination fan-out */
+  int64_t global_bytes;   /* sum over tensors of the global tensor's bytes (G) */
+  int64_t bytes_read;     /* bytes the kernel reads  (= G: each element once) */
+  int64_t bytes_written;  /* bytes the kernel writes (= sum of destination shard bytes) */
+  int64_t n_descriptors;  /* device copy descriptors after dim merging / splitting */
+  int64_t table_bytes;    /* size of the device-resident descriptor table */
+  int64_t n_workgroups;   /* grid of one execute launch (0 until first upload) */
+  double plan_host_us;    /* host time spent planning in reshard_plan_create* */
+} reshard_plan_stats_t;
+
+/* One planned overlap, in global coordinates (inspection API). */
+typedef struct reshard_piece {
+  int64_t tensor;                 /* tensor index inside the plan */
+  int64_t src_rank;               /* source rank read (after replica choice) */
+  int64_t src_group;              /* index of the unique source box it belongs to */
+  int64_t dst_group;              /* index of the unique destination box it feeds */
+  int64_t fanout;                 /* destination ranks written (replicas of dst_group) */
+  int64_t lo[RESHARD_MAX_NDIM];   /* box [lo, hi) of the overlap, global coordinates */
+  int64_t hi[RESHARD_MAX_NDIM];
+} reshard_piece_t;
+
+/*
+ * Device copy descriptor (the table the kernel reads; inspection API).
+ * The descriptor copies rows of `run_units` items of `unit` bytes.  Rows are
+ * indexed by up to three outer dims (extent[0] outermost); a row's first byte is
+ *   base + offset + i0*stride[0] + i1*stride[1] + i2*stride[2]
+ * on each side, base being the shard pointer.  Items in a row are contiguous.
+ */
+typedef struct reshard_descriptor {
+  int64_t src_offset;       /* byte offset of the first item in the source shard */
+  int64_t dst_offset;       /* byte offset of the first item in each destination shard */
+  int64_t src_stride[3];    /* bytes, outer dims; unused dims have extent 1 */
+  int64_t dst_stride[3];
+  uint32_t extent[3];       /* outer extents; product = rows */
+  uint32_t run_units;       /* items per row */
+  uint32_t unit;            /* item size in bytes: 1, 2, 4, 8 or 16 */
+  uint32_t src_ptr;         /* index into the execute's source pointer array */
+  uint32_t dst_ref_begin;   /* first entry of this descriptor's fan-out list */
+  uint32_t fanout;          /* destination pointers written */
+  uint32_t magic[3][2];     /* division constants for run_units, extent[2], extent[1] */
+  uint32_t piece;           /* index of the planned piece it copies (or part of) */
+  uint32_t reserved;
+} reshard_descriptor_t;
+
+/* Bytes per element of `dtype`, or 0 if unknown. */
+int64_t reshard_dtype_size(int dtype);
+
+/*
+ * Describe a layout.  global_shape[ndim] (extents >= 0, 1 <= ndim <= 8),
+ * mesh_shape[mesh_ndim] (sizes >= 1, 1 <= mesh_ndim <= 8), placements[mesh_ndim]
+ * (RESHARD_REPLICATE or a tensor dim).  Arrays are copied; *out receives a new
+ * handle owned by the caller (free with reshard_layout_destroy).
+ * Errors: RESHARD_ERR_INVALID_ARGUMENT.
+ */
+reshard_status_t reshard_layout_create(int ndim, const int64_t* global_shape, int dtype,
+                                       int mesh_ndim, const int64_t* mesh_shape,
+                                       const int32_t* placements, reshard_layout_t* out);
+void reshard_layout_destroy(reshard_layout_t layout); /* NULL is a no-op */
+
+/* Number of ranks (product of the mesh shape). */
+reshard_status_t reshard_layout_num_ranks(reshard_layout_t layout, int64_t* out);
+
+/*
+ * Box held by `rank`: offset[ndim] (global start) and extent[ndim] (local shape,
+ * may contain zeros for an empty shard).  Errors: RESHARD_ERR_INVALID_ARGUMENT.
+ */
+reshard_status_t reshard_layout_shard_box(reshard_layout_t layout, int64_t rank,
+                                          int64_t* offset, int64_t* extent);
+
+/*
+ * Plan the reshard of one tensor from layout src to layout dst (same global
+ * shape and dtype).  Host-only: intersects every source box with every unique
+ * destination box, picks one source replica per overlap (least-loaded first),
+ * merges contiguous dims and builds the descriptor table.  The layouts may be
+ * destroyed afterwards.  The device table is uploaded by reshard_plan_upload or
+ * by the first reshard_execute.
+ * Errors: RESHARD_ERR_INVALID_ARGUMENT, RESHARD_ERR_LAYOUT_MISMATCH,
+ * RESHARD_ERR_OUT_OF_MEMORY.
+ */
+reshard_status_t reshard_plan_create(reshard_layout_t src, reshard_layout_t dst,
+                                     reshard_plan_t* out);
+
+/*
+ * Plan n tensors that are moved together by one fused kernel launch per execute.
+ * Pointer arrays of reshard_execute are then concatenated tensor-major: tensor
+ * 0's ranks first, each tensor's ranks in row-major mesh order.
+ */
+reshard_status_t reshard_plan_create_batched(int n, const reshard_layout_t* src,
+                                             const reshard_layout_t* dst, reshard_plan_t* out);
+
+/*
+ * Upload the descriptor table to the current HIP device (once; later calls are
+ * no-ops) using `stream` (a hipStream_t; NULL = default stream).  Synchronises
+ * with the upload before returning.
+ * Errors: RESHARD_ERR_HIP, RESHARD_ERR_OUT_OF_MEMORY, RESHARD_ERR_DEVICE_MISMATCH.
+ */
+reshard_status_t reshard_plan_upload(reshard_plan_t plan, void* stream);
+
+/*
+ * Run the reshard on `stream` (hipStream_t, NULL = default stream); asynchronous.
+ *   src_ptrs[n_src_ptrs]  device pointers to the source shards (read only)
+ *   dst_ptrs[n_dst_ptrs]  device pointers to the destination shards (written)
+ * Pointers are borrowed: keep the buffers alive until the stream has passed the
+ * work.  NULL is allowed only for empty shards.  Sources and destinations must
+ * not overlap.  One kernel launch moves every piece of every tensor; when the
+ * pointer arrays exceed the kernel-argument capacity they are first copied to a
+ * plan-owned device slot with one asynchronous host-to-device copy.  Device
+ * faults surface at the caller's next synchronisation, as with any HIP launch.
+ * Calls on several streams may overlap.
+ * Errors: RESHARD_ERR_INVALID_ARGUMENT, RESHARD_ERR_NULL_SHARD, RESHARD_ERR_HIP,
+ * RESHARD_ERR_DEVICE_MISMATCH, RESHARD_ERR_OUT_OF_MEMORY.
+ */
+reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptrs,
+                                 void* const* dst_ptrs, void* stream);
+
+reshard_status_t reshard_plan_stats(reshard_plan_t plan, reshard_plan_stats_t* out);
+
+/*
+ * Inspection: copy up to `capacity` pieces into out[] and the total count into
+ * *n_total (out may be NULL when capacity is 0).
+ */
+reshard_status_t reshard_plan_pieces(reshard_plan_t plan, int64_t capacity,
+                                     reshard_piece_t* out, int64_t* n_total);
+
+/* Destination ranks (within the piece's tensor) that piece `index` is written to. */
+reshard_status_t reshard_plan_piece_fanout(reshard_plan_t plan, int64_t index, int64_t capacity,
+                                           int64_t* ranks, int64_t* n_total);
+
+/*
+ * Inspection: copy the descriptor table (up to `capacity` entries) and the
+ * fan-out reference list (indices into the destination pointer array; up to
+ * `ref_capacity` entries).  Totals go to *n_desc and *n_refs.
+ */
+reshard_status_t reshard_plan_descriptors(reshard_plan_t plan, int64_t capacity,
+                                          reshard_descriptor_t* out, int64_t* n_desc,
+                                          int64_t ref_capacity, uint32_t* refs,
+                                          int64_t* n_refs);
+
+/* Free the plan and its device memory.  No execute using it may be in flight.  NULL is a no-op. */
+void reshard_plan_destroy(reshard_plan_t plan);
+
+/* Message of the calling thread's last failed call ("" if none).  Valid until its next call. */
+const char* reshard_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RESHARD_H_ */

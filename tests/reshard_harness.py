@@ -1,0 +1,181 @@
+"""Test-side helpers around the reshard library: plans for workload specs, and
+two host-side *interpreters* of a plan that exist only in the tests:
+
+* ``apply_pieces``      -- applies the planned overlaps (global boxes) with torch
+  slicing, checking the planner's intersections and replica choice;
+* ``run_descriptors``   -- walks the device descriptor table byte by byte the way
+  the kernel reads it (rows, strides, unit, fan-out), checking dim merging,
+  splitting and offsets.
+
+Neither is reachable from the product library, which has no CPU copy path.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import dtensor_layout_movement_amd as R
+import oracle
+from dtensor_layout_movement_amd import workloads as W
+
+
+class Plan:
+    """A plan for a list of TensorSpecs plus its layouts (freed on close)."""
+
+    def __init__(self, specs):
+        self.specs = list(specs)
+        self.src_layouts, self.dst_layouts = [], []
+        for t in self.specs:
+            code = R.dtype_code(t.dtype)
+            self.src_layouts.append(R.reshard_layout_create(t.shape, code, t.src_mesh, t.src_placements))
+            self.dst_layouts.append(R.reshard_layout_create(t.shape, code, t.dst_mesh, t.dst_placements))
+        self.handle = R.reshard_plan_create_batched(self.src_layouts, self.dst_layouts)
+
+    def src_boxes(self, t):
+        return lib_boxes(self.src_layouts[t], self.specs[t].shape)
+
+    def dst_boxes(self, t):
+        return lib_boxes(self.dst_layouts[t], self.specs[t].shape)
+
+    def stats(self):
+        return R.reshard_plan_stats(self.handle)
+
+    def close(self):
+        if self.handle:
+            R.reshard_plan_destroy(self.handle)
+            self.handle = None
+        for lay in self.src_layouts + self.dst_layouts:
+            R.reshard_layout_destroy(lay)
+        self.src_layouts, self.dst_layouts = [], []
+
+    def __enter__(self):
+        return self
+
+    def __exit__(self, *exc):
+        self.close()
+
+
+def lib_boxes(layout, shape):
+    n = R.reshard_layout_num_ranks(layout)
+    out = []
+    for r in range(n):
+        off, ext = R.reshard_layout_shard_box(layout, r, len(shape))
+        out.append(([o for o in off], [o + e for o, e in zip(off, ext)]))
+    return out
+
+
+def oracle_boxes(shape, mesh, placements):
+    n = 1
+    for m in mesh:
+        n *= m
+    return [oracle.shard_box(list(shape), list(mesh), list(placements), r) for r in range(n)]
+
+
+def assert_boxes_agree(plan: Plan):
+    """The library's boxes must equal the oracle's before any buffer is sized."""
+    for t, spec in enumerate(plan.specs):
+        assert plan.src_boxes(t) == oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements), spec
+        assert plan.dst_boxes(t) == oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements), spec
+
+
+def box_shape(box):
+    lo, hi = box
+    return [max(0, h - l) for l, h in zip(lo, hi)]
+
+
+def oracle_dsts(spec, srcs, threads=1):
+    """Destination shards by the oracle (gather-then-slice) from given sources."""
+    boxes = oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements)
+    dsts = [torch.empty(box_shape(b), dtype=spec.dtype) for b in boxes]
+    oracle.reshard(list(spec.shape), torch.empty((), dtype=spec.dtype).element_size(),
+                   list(spec.src_mesh), list(spec.src_placements),
+                   [s if s is not None and s.numel() else None for s in srcs],
+                   list(spec.dst_mesh), list(spec.dst_placements),
+                   [d if d.numel() else None for d in dsts], threads=threads)
+    return dsts
+
+
+def sources_for(spec, values, seed, t=0):
+    """Seeded global tensor and its source shards cut with the oracle's boxes."""
+    g = W.make_global(spec, values, seed, t)
+    return g, W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
+
+
+def apply_pieces(plan: Plan, srcs_per_tensor, fill=None):
+    """Destination shards built by copying every planned piece on the host."""
+    out = []
+    for t, spec in enumerate(plan.specs):
+        boxes = plan.dst_boxes(t)
+        out.append([torch.full(box_shape(b), 0, dtype=spec.dtype) if fill is None else
+                    torch.full(box_shape(b), fill, dtype=spec.dtype) for b in boxes])
+    sboxes = [plan.src_boxes(t) for t in range(len(plan.specs))]
+    dboxes = [plan.dst_boxes(t) for t in range(len(plan.specs))]
+    for i, pc in enumerate(R.reshard_plan_pieces(plan.handle)):
+        t = pc["tensor"]
+        nd = len(plan.specs[t].shape)
+        lo, hi = pc["lo"][:nd], pc["hi"][:nd]
+        slo = sboxes[t][pc["src_rank"]][0]
+        src = srcs_per_tensor[t][pc["src_rank"]]
+        s_idx = tuple(slice(l - o, h - o) for l, h, o in zip(lo, hi, slo))
+        for d in R.reshard_plan_piece_fanout(plan.handle, i):
+            dlo = dboxes[t][d][0]
+            d_idx = tuple(slice(l - o, h - o) for l, h, o in zip(lo, hi, dlo))
+            out[t][d][d_idx] = src[s_idx]
+    return out
+
+
+def run_descriptors(plan: Plan, srcs_flat, dsts_flat):
+    """Execute the descriptor table on host byte arrays exactly as the kernel
+    addresses memory.  srcs_flat/dsts_flat: uint8 numpy arrays (or None), in
+    the pointer-array order of reshard_execute."""
+    descs, refs = R.reshard_plan_descriptors(plan.handle)
+    for D in descs:
+        e0, e1, e2 = D["extent"]
+        ru, u = D["run_units"], D["unit"]
+        i0, i1, i2, col = np.meshgrid(np.arange(e0), np.arange(e1), np.arange(e2), np.arange(ru),
+                                      indexing="ij")
+        so = (D["src_offset"] + i0 * D["src_stride"][0] + i1 * D["src_stride"][1]
+              + i2 * D["src_stride"][2] + col * u).reshape(-1)
+        do = (D["dst_offset"] + i0 * D["dst_stride"][0] + i1 * D["dst_stride"][1]
+              + i2 * D["dst_stride"][2] + col * u).reshape(-1)
+        so = (so[:, None] + np.arange(u)[None, :]).reshape(-1)
+        do = (do[:, None] + np.arange(u)[None, :]).reshape(-1)
+        src = srcs_flat[D["src_ptr"]]
+        data = src[so]
+        for r in range(D["fanout"]):
+            dst = dsts_flat[refs[D["dst_ref_begin"] + r]]
+            dst[do] = data
+
+
+def shard_bytes(plan: Plan):
+    """Bytes of every shard, in the src / dst pointer-array order of execute."""
+    sb, db = [], []
+    for t, spec in enumerate(plan.specs):
+        es = spec.dtype.itemsize
+        sb += [int(np.prod(box_shape(b))) * es for b in plan.src_boxes(t)]
+        db += [int(np.prod(box_shape(b))) * es for b in plan.dst_boxes(t)]
+    return sb, db
+
+
+def assert_descriptors_in_bounds(plan: Plan):
+    """Every byte a descriptor touches lies inside its shards (checked before
+    any launch)."""
+    sb, db = shard_bytes(plan)
+    descs, refs = R.reshard_plan_descriptors(plan.handle)
+    for D in descs:
+        ext = D["extent"]
+        assert D["run_units"] >= 1 and all(e >= 1 for e in ext)
+        assert ext[0] * ext[1] * ext[2] * D["run_units"] < 2 ** 31
+        span = D["run_units"] * D["unit"]
+        s_last = D["src_offset"] + sum((e - 1) * st for e, st in zip(ext, D["src_stride"])) + span
+        d_last = D["dst_offset"] + sum((e - 1) * st for e, st in zip(ext, D["dst_stride"])) + span
+        assert D["src_offset"] >= 0 and D["dst_offset"] >= 0
+        assert all(st >= 0 for st in D["src_stride"] + D["dst_stride"])
+        assert s_last <= sb[D["src_ptr"]], D
+        for r in range(D["fanout"]):
+            assert d_last <= db[refs[D["dst_ref_begin"] + r]], D
+
+
+def magic_div(n, m, s):
+    """The kernel's quotient formula for n < 2^31."""
+    return ((n * m >> 32) + n) >> s

@@ -1,0 +1,177 @@
+"""GPU parity: the fused gfx950 copy kernel, called through the C ABI, against
+the CPU oracle, bit for bit, on guarded shard buffers.  Full-size workloads run
+in the same launch configuration as the benchmark (the plan's own grid)."""
+import numpy as np
+import pytest
+import torch
+
+import dtensor_layout_movement_amd as R
+import oracle_pins as P
+from dtensor_layout_movement_amd import workloads as W
+from gpu_harness import GuardedShards, run_parity, shard_nbytes
+from reshard_harness import Plan, assert_boxes_agree, assert_descriptors_in_bounds, oracle_boxes
+from test_planner import small_specs
+
+pytestmark = pytest.mark.gpu
+
+T = W.TensorSpec
+RR = W.R
+
+
+@pytest.fixture(scope="module", autouse=True)
+def gpu():
+    if not torch.cuda.is_available():
+        pytest.fail("GPU tests need a visible MI355X")
+    torch.cuda.set_device(0)
+    yield
+    torch.cuda.synchronize()
+
+
+def test_worked_example_golden():
+    """The pages' 8x8 example on the GPU against the golden fixture."""
+    wl = W.worked_example_8x8()
+    spec = wl.tensors[0]
+    gold = P.read_golden()
+    with Plan([spec]) as plan:
+        assert_boxes_agree(plan)
+        g = W.make_global(spec, "arange", 0)
+        srcs = W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
+        src_d = [s.cuda() for s in srcs]
+        dst_d = [torch.full((8, 2), -1.0, dtype=torch.bfloat16, device="cuda") for _ in range(4)]
+        R.reshard_execute(plan.handle, [t.data_ptr() for t in src_d], [t.data_ptr() for t in dst_d],
+                          torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        for c, d in enumerate(dst_d):
+            got = d.cpu().float().numpy().astype(np.int64)
+            assert np.array_equal(got, gold[("dst", c)])
+
+
+SMALL_FULL = ["worked_example_8x8", "ffn_up_14336x4096", "moe_experts_64x2048x7168", "uneven_5000x3001"]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+@pytest.mark.parametrize("name", SMALL_FULL)
+def test_workload_parity_full_size(name, seed):
+    wl = W.WORKLOADS[name]()
+    run_parity(wl.tensors, wl.values, seed)
+
+
+@pytest.mark.parametrize("name", SMALL_FULL)
+def test_workload_parity_raw_bits(name):
+    """Random bytes (NaN payloads, infinities, -0.0, subnormals) arrive unchanged."""
+    wl = W.WORKLOADS[name]()
+    run_parity(wl.tensors, "raw", 7)
+
+
+@pytest.mark.parametrize("values", ["normal", "raw"])
+def test_ffn_refit_32_layers_one_launch(values):
+    """All 96 tensors of the 32-layer refit in one fused launch (pointer table
+    too large for kernel arguments: uploaded into a device slot)."""
+    wl = W.ffn_refit()
+    st = run_parity(wl.tensors, values, 0, threads=16)
+    assert st["n_tensors"] == 96 and st["n_pieces"] == 384
+
+
+@pytest.mark.parametrize("spec", small_specs(), ids=lambda s: s.name)
+def test_small_layouts(spec):
+    run_parity([spec], "raw", 3)
+
+
+@pytest.mark.parametrize("misalign", [1, 2, 4, 8])
+def test_misaligned_shard_pointers(misalign):
+    """Shard pointers off the 16-byte grid take the bytewise path; results and
+    guard bands must be unaffected."""
+    specs = [W.uneven(50, 31).tensors[0], W.ffn_up(112, 64).tensors[0]]
+    for spec in specs:
+        run_parity([spec], "raw", 4, misalign=misalign)
+
+
+def test_batched_mixed_dtypes():
+    specs = list(W.ffn_refit(2, 64, 224).tensors) + [W.uneven(77, 53).tensors[0]] + \
+        [s for s in small_specs() if s.name in ("u8_odd", "i64", "five_d", "rep_src")]
+    run_parity(specs, "raw", 5)
+
+
+def test_pointer_slot_ring():
+    """More pointers than kernel arguments hold: each execute with a new pointer
+    set goes through the slot ring (wrapping it), repeats reuse the slot."""
+    specs = list(W.ffn_refit(16, 64, 96).tensors)  # 48 tensors x 10 ranks = 480 pointers
+    with Plan(specs) as plan:
+        assert_boxes_agree(plan)
+        assert_descriptors_in_bounds(plan)
+        srcs_all, want_all = [], []
+        src_sets = []
+        for t, spec in enumerate(specs):
+            g = W.make_global(spec, "raw", 9, t)
+            sb = oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements)
+            srcs = W.cut(g, sb)
+            srcs_all.append(srcs)
+            from reshard_harness import oracle_dsts
+            want_all.append(oracle_dsts(spec, srcs))
+            gs = GuardedShards(shard_nbytes(sb, spec.dtype), "cuda")
+            for i, s in enumerate(srcs):
+                gs.region(i).copy_(s.reshape(-1).view(torch.uint8).cuda())
+            src_sets.append(gs)
+        src_ptrs = [p for s in src_sets for p in s.ptrs]
+        stream = torch.cuda.current_stream().cuda_stream
+        rounds = []
+        for k in range(11):  # 11 distinct destination sets > 8 slots
+            dsts = [GuardedShards(shard_nbytes(oracle_boxes(s.shape, s.dst_mesh, s.dst_placements),
+                                               s.dtype), "cuda") for s in specs]
+            dst_ptrs = [p for d in dsts for p in d.ptrs]
+            R.reshard_execute(plan.handle, src_ptrs, dst_ptrs, stream)
+            if k == 3:  # the same pointers again: slot reuse without a copy
+                R.reshard_execute(plan.handle, src_ptrs, dst_ptrs, stream)
+            rounds.append(dsts)
+        torch.cuda.synchronize()
+        for dsts in rounds:
+            for t, spec in enumerate(specs):
+                for i, w in enumerate(want_all[t]):
+                    assert torch.equal(dsts[t].region(i).cpu(), w.reshape(-1).view(torch.uint8))
+                    assert dsts[t].guards_intact(i)
+
+
+def test_two_streams_concurrently():
+    spec = W.ffn_up(1024, 512).tensors[0]
+    with Plan([spec]) as plan:
+        assert_boxes_agree(plan)
+        g = W.make_global(spec, "raw", 11)
+        sb = oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements)
+        db = oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements)
+        srcs = W.cut(g, sb)
+        from reshard_harness import oracle_dsts
+        want = oracle_dsts(spec, srcs)
+        src = GuardedShards(shard_nbytes(sb, spec.dtype), "cuda")
+        for i, s in enumerate(srcs):
+            src.region(i).copy_(s.reshape(-1).view(torch.uint8).cuda())
+        torch.cuda.synchronize()
+        outs = []
+        streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+        for st in streams:
+            d = GuardedShards(shard_nbytes(db, spec.dtype), "cuda")
+            torch.cuda.synchronize()
+            with torch.cuda.stream(st):
+                for _ in range(3):
+                    R.reshard_execute(plan.handle, src.ptrs, d.ptrs, st.cuda_stream)
+            outs.append(d)
+        torch.cuda.synchronize()
+        for d in outs:
+            for i, w in enumerate(want):
+                assert torch.equal(d.region(i).cpu(), w.reshape(-1).view(torch.uint8))
+                assert d.guards_intact(i)
+
+
+def test_empty_plan_launches_nothing():
+    spec = T("zero", (0, 6), torch.float32, (2,), (0,), (3,), (1,))
+    with Plan([spec]) as plan:
+        R.reshard_execute(plan.handle, [0, 0], [0, 0, 0], torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        assert plan.stats()["n_workgroups"] == 0
+
+
+def test_upload_and_stats_after_execute():
+    with Plan(W.ffn_up().tensors) as plan:
+        R.reshard_plan_upload(plan.handle, torch.cuda.current_stream().cuda_stream)
+        st = plan.stats()
+        assert 1 <= st["n_workgroups"] <= 256 * 8
+        R.reshard_plan_upload(plan.handle, None)  # second upload is a no-op
