@@ -432,31 +432,20 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
       }
     }
   }
+  // tiles: each descriptor gets ceil(items / tile_items(unit)) consecutive tiles
+  P->tile_begin.assign(1, 0);
+  for (const reshard_descriptor_t& D : P->descs) {
+    const uint64_t items = uint64_t(D.extent[0]) * D.extent[1] * D.extent[2] * D.run_units;
+    P->n_tiles += (items + tile_items(D.unit) - 1) / tile_items(D.unit);
+    if (P->n_tiles >= (uint64_t(1) << 31)) {
+      *err = "plan needs more than 2^31 tiles";
+      return RESHARD_ERR_INVALID_ARGUMENT;
+    }
+    P->tile_begin.push_back(uint32_t(P->n_tiles));
+  }
   auto t1 = std::chrono::steady_clock::now();
   P->plan_host_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
   return RESHARD_OK;
-}
-
-std::vector<WgStart> partition(const HostPlan& P, uint32_t n_wg) {
-  std::vector<WgStart> out(size_t(n_wg) + 1);
-  const size_t nd = P.descs.size();
-  std::vector<uint64_t> cum(nd + 1, 0);
-  for (size_t i = 0; i < nd; ++i) cum[i + 1] = cum[i] + P.desc_cost[i];
-  const uint64_t total = cum[nd];
-  size_t d = 0;
-  for (uint32_t w = 0; w <= n_wg; ++w) {
-    // boundary w at traffic w * total / n_wg (128-bit safe: total < 2^50, n_wg < 2^14)
-    const uint64_t c = (w == n_wg) ? total : uint64_t((unsigned __int128)total * w / n_wg);
-    while (d < nd && cum[d + 1] <= c) ++d;
-    if (d >= nd) {
-      out[w] = WgStart{uint32_t(nd), 0};
-      continue;
-    }
-    const reshard_descriptor_t& D = P.descs[d];
-    const uint64_t per_item = uint64_t(D.unit) * (1 + D.fanout);
-    out[w] = WgStart{uint32_t(d), uint32_t((c - cum[d]) / per_item)};
-  }
-  return out;
 }
 
 }  // namespace rs

@@ -64,11 +64,12 @@ struct Piece {
   int64_t bytes;
 };
 
-// Start of one workgroup's share of the copy: descriptor index and item index.
-struct WgStart {
-  uint32_t desc;
-  uint32_t item;
-};
+// Tiling.  One workgroup of kTileThreads threads copies one tile of one
+// descriptor: tile_items(unit) consecutive items, i.e. 4 KiB of source bytes for
+// 16-byte items (fewer bytes for narrow items, which take 4 items per thread).
+constexpr uint32_t kTileThreads = 256;
+constexpr uint32_t tile_items_per_thread(uint32_t unit) { return unit >= 16 ? 1u : unit == 8 ? 2u : 4u; }
+constexpr uint32_t tile_items(uint32_t unit) { return kTileThreads * tile_items_per_thread(unit); }
 
 struct HostPlan {
   int n_tensors = 0;
@@ -81,6 +82,8 @@ struct HostPlan {
   std::vector<reshard_descriptor_t> descs;
   std::vector<uint32_t> refs;       // fan-out: destination pointer slots (0-based in dst_ptrs)
   std::vector<uint64_t> desc_cost;  // bytes read + written by each descriptor
+  std::vector<uint32_t> tile_begin; // first tile of each descriptor; n_desc + 1 entries
+  uint64_t n_tiles = 0;
   int64_t global_bytes = 0, bytes_read = 0, bytes_written = 0, n_dst_writes = 0;
   double plan_host_us = 0.0;
 };
@@ -89,10 +92,6 @@ struct HostPlan {
 // a message in *err.
 reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const* dst,
                             HostPlan* out, std::string* err);
-
-// Splits the plan's copy traffic into `n_wg` equal shares at item granularity
-// and returns n_wg + 1 starts (the last one is {n_desc, 0}).
-std::vector<WgStart> partition(const HostPlan& plan, uint32_t n_wg);
 
 // Division by an invariant 32-bit divisor d >= 1 for numerators below 2^31:
 // q = (mulhi(n, m) + n) >> s.  Granlund & Montgomery, "Division by invariant

@@ -1,13 +1,15 @@
 // C ABI of the reshard library and its gfx950 copy kernel.
 //
 // Execute = one launch of reshard_copy_kernel.  The plan's descriptor table
-// sits in device memory; each workgroup owns an equal share of the plan's
-// traffic (bytes read + bytes written) and walks the descriptors that share
-// covers.  A descriptor copies rows of contiguous items (1-16 bytes each):
-// every item is loaded once and stored to each destination replica (the
-// single-GPU form of "send each contribution once, replicate locally":
-// techfeed.io write-up, "NVIDIA's NVLink implementation" section).  Data only
-// moves through integer registers, so the copy is bit-exact for every dtype.
+// sits in device memory together with the first tile of every descriptor.  One
+// workgroup copies one tile (4 KiB of source for 16-byte items): it finds its
+// descriptor by a binary search over the tile prefix, then every thread loads
+// its item(s) once and stores them to each destination replica (the single-GPU
+// form of "send each contribution once, replicate locally": techfeed.io
+// write-up, "NVIDIA's NVLink implementation" section).  Many small workgroups
+// let the dispatcher balance the load; consecutive tiles are kept on one XCD so
+// that rows straddling tile edges merge in that XCD's L2.  Data only moves
+// through integer registers, so the copy is bit-exact for every dtype.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -26,11 +28,10 @@ struct reshard_layout_s {
 
 namespace {
 
-constexpr int kBlock = 256;            // threads per workgroup (4 wave64s)
+constexpr int kBlock = int(rs::kTileThreads);  // threads per workgroup (4 wave64s)
+constexpr uint32_t kXcds = 8;          // MI355X: workgroups go round-robin over 8 XCDs
 constexpr int kKargPtrs = 120;         // pointer slots passed in kernel arguments
 constexpr int kSlots = 8;              // device pointer-table slots for bigger plans
-constexpr int kMaxWgPerCu = 8;         // cap on resident workgroups per CU used for the grid
-constexpr uint64_t kMinTrafficPerWg = 64 * 1024;  // no workgroup gets less than this
 
 struct KargPtrs {
   const void* p[kKargPtrs];
@@ -95,36 +96,35 @@ __device__ __forceinline__ void store_item(uint8_t* p, V v) {
   __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
 }
 
-// Items [lo, hi) of D with V-sized accesses: U items per thread in flight, all
-// loads issued before the stores; each loaded item is stored to every replica.
+// Items [lo, hi) of D (at most kBlock * U of them) with V-sized accesses: all
+// loads are issued before the stores; each loaded item is stored to every
+// destination replica.
 template <typename V, int U>
-__device__ __forceinline__ void copy_span(const reshard_descriptor_t& D, const uint8_t* src,
+__device__ __forceinline__ void copy_tile(const reshard_descriptor_t& D, const uint8_t* src,
                                           const uint32_t* __restrict__ refs,
                                           const void* const* table, const KargPtrs& karg,
                                           uint32_t lo, uint32_t hi) {
-  for (uint32_t base = lo; base < hi; base += uint32_t(kBlock * U)) {
-    V v[U];
-    uint64_t doff[U];
-    bool ok[U];
+  V v[U];
+  uint64_t doff[U];
+  bool ok[U];
 #pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const uint32_t f = base + uint32_t(k * kBlock) + threadIdx.x;
-      ok[k] = f < hi;
-      const ItemOffsets o = item_offsets(D, ok[k] ? f : lo);
-      doff[k] = o.dst;
-      if (ok[k]) v[k] = load_item<V>(src + o.src);
-    }
-    for (uint32_t r = 0; r < D.fanout; ++r) {
-      uint8_t* dst = reinterpret_cast<uint8_t*>(shard_ptr(table, karg, refs[D.dst_ref_begin + r]));
+  for (int k = 0; k < U; ++k) {
+    const uint32_t f = lo + uint32_t(k * kBlock) + threadIdx.x;
+    ok[k] = f < hi;
+    const ItemOffsets o = item_offsets(D, ok[k] ? f : lo);
+    doff[k] = o.dst;
+    if (ok[k]) v[k] = load_item<V>(src + o.src);
+  }
+  for (uint32_t r = 0; r < D.fanout; ++r) {
+    uint8_t* dst = reinterpret_cast<uint8_t*>(shard_ptr(table, karg, refs[D.dst_ref_begin + r]));
 #pragma unroll
-      for (int k = 0; k < U; ++k)
-        if (ok[k]) store_item<V>(dst + doff[k], v[k]);
-    }
+    for (int k = 0; k < U; ++k)
+      if (ok[k]) store_item<V>(dst + doff[k], v[k]);
   }
 }
 
 // Same traffic bytewise, for shard pointers not aligned to the descriptor's unit.
-__device__ void copy_span_bytes(const reshard_descriptor_t& D, const uint8_t* src,
+__device__ void copy_tile_bytes(const reshard_descriptor_t& D, const uint8_t* src,
                                 const uint32_t* __restrict__ refs, const void* const* table,
                                 const KargPtrs& karg, uint32_t lo, uint32_t hi) {
   for (uint32_t f = lo + threadIdx.x; f < hi; f += kBlock) {
@@ -138,30 +138,33 @@ __device__ void copy_span_bytes(const reshard_descriptor_t& D, const uint8_t* sr
 
 __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     const reshard_descriptor_t* __restrict__ descs, uint32_t n_desc,
-    const uint32_t* __restrict__ refs, const rs::WgStart* __restrict__ starts,
-    const void* const* __restrict__ table, KargPtrs karg) {
-  const rs::WgStart a = starts[blockIdx.x];
-  const rs::WgStart b = starts[blockIdx.x + 1];
-  for (uint32_t d = a.desc; d < n_desc && d <= b.desc; ++d) {
-    const reshard_descriptor_t& D = descs[d];
-    const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.run_units;
-    const uint32_t lo = (d == a.desc) ? a.item : 0u;
-    const uint32_t hi = (d == b.desc) ? b.item : items;
-    if (lo >= hi) continue;
-    const uint8_t* src = reinterpret_cast<const uint8_t*>(shard_ptr(table, karg, D.src_ptr));
-    uintptr_t bits = reinterpret_cast<uintptr_t>(src);
-    for (uint32_t r = 0; r < D.fanout; ++r) bits |= shard_ptr(table, karg, refs[D.dst_ref_begin + r]);
-    if (bits & (D.unit - 1)) {
-      copy_span_bytes(D, src, refs, table, karg, lo, hi);
-      continue;
-    }
-    switch (D.unit) {
-      case 16: copy_span<u32x4, 4>(D, src, refs, table, karg, lo, hi); break;
-      case 8: copy_span<u32x2, 4>(D, src, refs, table, karg, lo, hi); break;
-      case 4: copy_span<uint32_t, 4>(D, src, refs, table, karg, lo, hi); break;
-      case 2: copy_span<uint16_t, 4>(D, src, refs, table, karg, lo, hi); break;
-      default: copy_span<uint8_t, 4>(D, src, refs, table, karg, lo, hi); break;
-    }
+    const uint32_t* __restrict__ tile_begin, const uint32_t* __restrict__ refs,
+    const void* const* __restrict__ table, KargPtrs karg, uint32_t n_tiles, uint32_t per_xcd) {
+  // consecutive tiles on one XCD: block b runs on XCD b % kXcds
+  const uint32_t t = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  if (t >= n_tiles) return;
+  uint32_t lo = 0, hi = n_desc;  // last descriptor whose first tile is <= t
+  while (hi - lo > 1) {
+    const uint32_t mid = (lo + hi) >> 1;
+    if (tile_begin[mid] <= t) lo = mid; else hi = mid;
+  }
+  const reshard_descriptor_t& D = descs[lo];
+  const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.run_units;
+  const uint32_t first = (t - tile_begin[lo]) * rs::tile_items(D.unit);
+  const uint32_t last = min(first + rs::tile_items(D.unit), items);
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(shard_ptr(table, karg, D.src_ptr));
+  uintptr_t bits = reinterpret_cast<uintptr_t>(src);
+  for (uint32_t r = 0; r < D.fanout; ++r) bits |= shard_ptr(table, karg, refs[D.dst_ref_begin + r]);
+  if (bits & (D.unit - 1)) {
+    copy_tile_bytes(D, src, refs, table, karg, first, last);
+    return;
+  }
+  switch (D.unit) {
+    case 16: copy_tile<u32x4, rs::tile_items_per_thread(16)>(D, src, refs, table, karg, first, last); break;
+    case 8: copy_tile<u32x2, rs::tile_items_per_thread(8)>(D, src, refs, table, karg, first, last); break;
+    case 4: copy_tile<uint32_t, rs::tile_items_per_thread(4)>(D, src, refs, table, karg, first, last); break;
+    case 2: copy_tile<uint16_t, rs::tile_items_per_thread(2)>(D, src, refs, table, karg, first, last); break;
+    default: copy_tile<uint8_t, rs::tile_items_per_thread(1)>(D, src, refs, table, karg, first, last); break;
   }
 }
 
@@ -176,11 +179,12 @@ struct reshard_plan_s {
   std::mutex mu;
   bool uploaded = false;
   int device = -1;
-  uint32_t n_wg = 0;
-  void* table = nullptr;  // device: descriptors | refs (absolute pointer slots) | starts
+  uint32_t n_wg = 0;       // grid of one launch (tiles rounded up to a multiple of kXcds)
+  uint32_t per_xcd = 0;    // tiles per XCD
+  void* table = nullptr;  // device: descriptors | refs (absolute pointer slots) | tile_begin
   const reshard_descriptor_t* d_descs = nullptr;
   const uint32_t* d_refs = nullptr;
-  const rs::WgStart* d_starts = nullptr;
+  const uint32_t* d_tile_begin = nullptr;
   // pointer-table slots, used when the pointers do not fit in kernel arguments
   int64_t n_ptrs = 0;
   void* d_slots = nullptr;
@@ -205,29 +209,16 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
     return RESHARD_OK;
   }
   const rs::HostPlan& H = p->host;
-  uint32_t n_wg = 0;
-  if (!H.descs.empty()) {
-    int cus = 0, occ = 0;
-    e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
-    if (e != hipSuccess) return hip_fail(e, "hipDeviceGetAttribute");
-    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reshard_copy_kernel, kBlock, 0);
-    if (e != hipSuccess) return hip_fail(e, "hipOccupancyMaxActiveBlocksPerMultiprocessor");
-    occ = std::max(1, std::min(occ, kMaxWgPerCu));
-    uint64_t traffic = 0;
-    for (uint64_t c : H.desc_cost) traffic += c;
-    const uint64_t want = std::max<uint64_t>(1, (traffic + kMinTrafficPerWg - 1) / kMinTrafficPerWg);
-    n_wg = uint32_t(std::min<uint64_t>(uint64_t(cus) * uint64_t(occ), want));
-  }
-  const std::vector<rs::WgStart> starts = rs::partition(H, n_wg);
+  const uint32_t per_xcd = uint32_t((H.n_tiles + kXcds - 1) / kXcds);
   const size_t desc_bytes = H.descs.size() * sizeof(reshard_descriptor_t);
   const size_t refs_off = align_up(desc_bytes, 256);
-  const size_t starts_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);
-  const size_t total = starts_off + starts.size() * sizeof(rs::WgStart);
+  const size_t tiles_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);
+  const size_t total = tiles_off + H.tile_begin.size() * sizeof(uint32_t);
   std::vector<uint8_t> img(total, 0);
   if (desc_bytes) std::memcpy(img.data(), H.descs.data(), desc_bytes);
   uint32_t* r = reinterpret_cast<uint32_t*>(img.data() + refs_off);
   for (size_t i = 0; i < H.refs.size(); ++i) r[i] = uint32_t(H.n_src_ptrs) + H.refs[i];
-  std::memcpy(img.data() + starts_off, starts.data(), starts.size() * sizeof(rs::WgStart));
+  std::memcpy(img.data() + tiles_off, H.tile_begin.data(), H.tile_begin.size() * sizeof(uint32_t));
 
   void* table = nullptr;
   e = hipMalloc(&table, total);
@@ -247,14 +238,22 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
       e = hipEventCreateWithFlags(&p->ev[s], hipEventDisableTiming);
     if (e != hipSuccess) {
       (void)hipFree(table);
+      if (p->d_slots) (void)hipFree(p->d_slots);
+      if (p->h_slots) (void)hipHostFree(p->h_slots);
+      for (int s = 0; s < kSlots; ++s)
+        if (p->ev[s]) (void)hipEventDestroy(p->ev[s]);
+      p->d_slots = nullptr;
+      p->h_slots = nullptr;
+      for (int s = 0; s < kSlots; ++s) p->ev[s] = nullptr;
       return hip_fail(e, "pointer-table slots");
     }
   }
   p->table = table;
   p->d_descs = reinterpret_cast<const reshard_descriptor_t*>(table);
   p->d_refs = reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + refs_off);
-  p->d_starts = reinterpret_cast<const rs::WgStart*>(static_cast<uint8_t*>(table) + starts_off);
-  p->n_wg = n_wg;
+  p->d_tile_begin = reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + tiles_off);
+  p->per_xcd = per_xcd;
+  p->n_wg = per_xcd * kXcds;
   p->device = dev;
   p->uploaded = true;
   return RESHARD_OK;
@@ -414,7 +413,8 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
     table = reinterpret_cast<const void* const*>(static_cast<void**>(plan->d_slots) + size_t(slot) * n);
   }
   hipLaunchKernelGGL(reshard_copy_kernel, dim3(plan->n_wg), dim3(kBlock), 0, stream, plan->d_descs,
-                     uint32_t(H.descs.size()), plan->d_refs, plan->d_starts, table, karg);
+                     uint32_t(H.descs.size()), plan->d_tile_begin, plan->d_refs, table, karg,
+                     uint32_t(H.n_tiles), plan->per_xcd);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "reshard_copy_kernel launch");
   if (slot >= 0) {

@@ -89,7 +89,7 @@ typedef struct reshard_plan_stats {
   int64_t bytes_written;  /* bytes the kernel writes (= sum of destination shard bytes) */
   int64_t n_descriptors;  /* device copy descriptors after dim merging / splitting */
   int64_t table_bytes;    /* size of the device-resident descriptor table */
-  int64_t n_workgroups;   /* grid of one execute launch (0 until first upload) */
+  int64_t n_workgroups;   /* grid of one execute launch: one workgroup per tile (0 until upload) */
   double plan_host_us;    /* host time spent planning in reshard_plan_create* */
 } reshard_plan_stats_t;
 
