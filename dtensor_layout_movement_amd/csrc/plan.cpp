@@ -124,22 +124,22 @@ void emit(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_begin, uin
            run_bytes, outer);
     return;
   }
-  int64_t bits = src_off | dst_off | run_bytes;
-  for (const Dim& d : outer) bits |= d.ss | d.sd;
-  const uint32_t unit = unit_for(bits);
-  const uint64_t run_units = uint64_t(run_bytes) / unit;
-  uint64_t rows = 1;
-  for (const Dim& d : outer) rows *= uint64_t(d.e);
-
-  if (run_units > kMaxItems) {  // split every row into column chunks
-    const int64_t chunk_units = int64_t(1) << 30;
-    for (int64_t c = 0; c < int64_t(run_units); c += chunk_units) {
-      int64_t n = std::min<int64_t>(chunk_units, int64_t(run_units) - c);
-      emit(P, piece, src_ptr, ref_begin, fanout, src_off + c * unit, dst_off + c * unit, n * unit, outer);
+  if (run_bytes > kMaxRunBytes) {  // split every row into column ranges
+    for (int64_t c = 0; c < run_bytes; c += kMaxRunBytes) {
+      const int64_t n = std::min<int64_t>(kMaxRunBytes, run_bytes - c);
+      emit(P, piece, src_ptr, ref_begin, fanout, src_off + c, dst_off + c, n, outer);
     }
     return;
   }
-  if (rows * run_units > kMaxItems) {  // halve the outermost dim with extent > 1
+  int64_t bits = src_off | dst_off | run_bytes;
+  for (const Dim& d : outer) bits |= d.ss | d.sd;
+  const uint32_t unit = unit_for(bits);
+  const bool chunked = unit < 16 && run_bytes >= kChunkedMinRun;
+  const uint64_t row_items = chunked ? uint64_t(run_bytes + 30) / 16 : uint64_t(run_bytes) / unit;
+  uint64_t rows = 1;
+  for (const Dim& d : outer) rows *= uint64_t(d.e);
+
+  if (rows * row_items > kMaxItems) {  // halve the outermost dim with extent > 1
     for (int k = int(outer.size()) - 1; k >= 0; --k) {
       if (outer[k].e < 2) continue;
       std::vector<Dim> a = outer, b = outer;
@@ -169,17 +169,19 @@ void emit(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_begin, uin
       D.extent[slot] = 1;
     }
   }
-  D.run_units = uint32_t(run_units);
-  D.unit = unit;
+  D.run_bytes = uint32_t(run_bytes);
+  D.row_items = uint32_t(row_items);
+  D.unit = uint16_t(unit);
+  D.mode = chunked ? RESHARD_DESC_DST_CHUNKS : RESHARD_DESC_ITEMS;
   D.src_ptr = src_ptr;
   D.dst_ref_begin = ref_begin;
   D.fanout = fanout;
-  magic_u31(D.run_units, &D.magic[0][0], &D.magic[0][1]);
+  magic_u31(D.row_items, &D.magic[0][0], &D.magic[0][1]);
   magic_u31(D.extent[2], &D.magic[1][0], &D.magic[1][1]);
   magic_u31(D.extent[1], &D.magic[2][0], &D.magic[2][1]);
   D.piece = piece;
   P->descs.push_back(D);
-  P->desc_cost.push_back(uint64_t(rows * run_units * unit) * (1 + fanout));
+  P->desc_cost.push_back(rows * uint64_t(run_bytes) * (1 + fanout));
 }
 
 // Turns one overlap into descriptors: local offsets in the source and
@@ -432,11 +434,11 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
       }
     }
   }
-  // tiles: each descriptor gets ceil(items / tile_items(unit)) consecutive tiles
+  // tiles: each descriptor gets ceil(items / kTileItems) consecutive tiles
   P->tile_begin.assign(1, 0);
   for (const reshard_descriptor_t& D : P->descs) {
-    const uint64_t items = uint64_t(D.extent[0]) * D.extent[1] * D.extent[2] * D.run_units;
-    P->n_tiles += (items + tile_items(D.unit) - 1) / tile_items(D.unit);
+    const uint64_t items = uint64_t(D.extent[0]) * D.extent[1] * D.extent[2] * D.row_items;
+    P->n_tiles += (items + kTileItems - 1) / kTileItems;
     if (P->n_tiles >= (uint64_t(1) << 31)) {
       *err = "plan needs more than 2^31 tiles";
       return RESHARD_ERR_INVALID_ARGUMENT;

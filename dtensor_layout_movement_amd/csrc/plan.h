@@ -65,11 +65,17 @@ struct Piece {
 };
 
 // Tiling.  One workgroup of kTileThreads threads copies one tile of one
-// descriptor: tile_items(unit) consecutive items, i.e. 4 KiB of source bytes for
-// 16-byte items (fewer bytes for narrow items, which take 4 items per thread).
+// descriptor: kTileItems consecutive items, two per thread (8 KiB of source for
+// 16-byte items and 16-byte destination chunks).
 constexpr uint32_t kTileThreads = 256;
-constexpr uint32_t tile_items_per_thread(uint32_t unit) { return unit >= 16 ? 1u : unit == 8 ? 2u : 4u; }
-constexpr uint32_t tile_items(uint32_t unit) { return kTileThreads * tile_items_per_thread(unit); }
+constexpr uint32_t kItemsPerThread = 2;
+constexpr uint32_t kTileItems = kTileThreads * kItemsPerThread;
+
+// Rows at least this long whose alignment is below 16 bytes are copied as
+// destination-aligned 16-byte chunks; shorter ones item by item.
+constexpr int64_t kChunkedMinRun = 128;
+// Longest row a descriptor holds (longer rows are split into column ranges).
+constexpr int64_t kMaxRunBytes = int64_t(1) << 30;
 
 struct HostPlan {
   int n_tensors = 0;

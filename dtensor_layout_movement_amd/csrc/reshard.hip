@@ -2,7 +2,7 @@
 //
 // Execute = one launch of reshard_copy_kernel.  The plan's descriptor table
 // sits in device memory together with the first tile of every descriptor.  One
-// workgroup copies one tile (4 KiB of source for 16-byte items): it finds its
+// workgroup copies one tile (8 KiB of source for 16-byte items): it finds its
 // descriptor by a binary search over the tile prefix, then every thread loads
 // its item(s) once and stores them to each destination replica (the single-GPU
 // form of "send each contribution once, replicate locally": techfeed.io
@@ -59,31 +59,25 @@ __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t s
   return (__umulhi(n, m) + n) >> s;
 }
 
-struct ItemOffsets {
-  uint64_t src, dst;
+// Row origin offsets (relative to the shard pointers) and item index of item f.
+struct ItemPos {
+  uint64_t src, dst;  // byte offsets of the row origin
+  uint32_t col;       // item index inside the row
 };
 
-// Byte offsets (relative to the shard pointers) of item f of descriptor D.
-__device__ __forceinline__ ItemOffsets item_offsets(const reshard_descriptor_t& D, uint32_t f) {
+__device__ __forceinline__ ItemPos item_pos(const reshard_descriptor_t& D, uint32_t f) {
   const uint32_t row = div_magic(f, D.magic[0][0], D.magic[0][1]);
-  const uint32_t col = f - row * D.run_units;
   const uint32_t t = div_magic(row, D.magic[1][0], D.magic[1][1]);
   const uint32_t i2 = row - t * D.extent[2];
   const uint32_t i0 = div_magic(t, D.magic[2][0], D.magic[2][1]);
   const uint32_t i1 = t - i0 * D.extent[1];
-  const uint64_t c = uint64_t(col) * D.unit;
-  ItemOffsets o;
+  ItemPos o;
+  o.col = f - row * D.row_items;
   o.src = uint64_t(D.src_offset) + uint64_t(i0) * uint64_t(D.src_stride[0]) +
-          uint64_t(i1) * uint64_t(D.src_stride[1]) + uint64_t(i2) * uint64_t(D.src_stride[2]) + c;
+          uint64_t(i1) * uint64_t(D.src_stride[1]) + uint64_t(i2) * uint64_t(D.src_stride[2]);
   o.dst = uint64_t(D.dst_offset) + uint64_t(i0) * uint64_t(D.dst_stride[0]) +
-          uint64_t(i1) * uint64_t(D.dst_stride[1]) + uint64_t(i2) * uint64_t(D.dst_stride[2]) + c;
+          uint64_t(i1) * uint64_t(D.dst_stride[1]) + uint64_t(i2) * uint64_t(D.dst_stride[2]);
   return o;
-}
-
-
-__device__ __forceinline__ uintptr_t shard_ptr(const void* const* table, const KargPtrs& karg,
-                                               uint32_t i) {
-  return table ? reinterpret_cast<uintptr_t>(table[i]) : reinterpret_cast<uintptr_t>(karg.p[i]);
 }
 
 template <typename V>
@@ -96,14 +90,41 @@ __device__ __forceinline__ void store_item(uint8_t* p, V v) {
   __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
 }
 
-// Items [lo, hi) of D (at most kBlock * U of them) with V-sized accesses: all
-// loads are issued before the stores; each loaded item is stored to every
-// destination replica.
-template <typename V, int U>
-__device__ __forceinline__ void copy_tile(const reshard_descriptor_t& D, const uint8_t* src,
-                                          const uint32_t* __restrict__ refs,
-                                          const void* const* table, const KargPtrs& karg,
-                                          uint32_t lo, uint32_t hi) {
+// Global-memory (address space 1) pointer from an address computed as an
+// integer, so that accesses compile to global_* rather than flat_* instructions.
+template <typename T>
+using global_ptr = __attribute__((address_space(1))) T*;
+template <typename T>
+__device__ __forceinline__ global_ptr<T> as_global(uintptr_t a) {
+  return reinterpret_cast<global_ptr<T>>(a);
+}
+
+// 16 bytes from any byte address (gfx950 global loads need no alignment).
+typedef uint32_t u32x4_u __attribute__((ext_vector_type(4), aligned(1)));
+__device__ __forceinline__ u32x4 load_16_unaligned(uintptr_t a) {
+  return __builtin_nontemporal_load(as_global<const u32x4_u>(a));
+}
+
+// Shard pointers of one descriptor.  kKarg: the pointer array sits in the kernel
+// arguments; otherwise in a device table.  Either way every lookup is a scalar
+// load from a known address space.
+template <bool kKarg>
+struct Shards {
+  const void* const* table;
+  const KargPtrs* karg;
+  const uint32_t* refs;  // this descriptor's fan-out list
+  __device__ __forceinline__ uintptr_t ptr(uint32_t i) const {
+    if constexpr (kKarg) return reinterpret_cast<uintptr_t>(karg->p[i]);
+    else return reinterpret_cast<uintptr_t>(table[i]);
+  }
+  __device__ __forceinline__ uintptr_t dst(uint32_t r) const { return ptr(refs[r]); }
+};
+
+// ITEMS mode: items [lo, hi) (at most kBlock * U of them) with V-sized accesses.
+// All loads are issued before the stores; each item is stored to every replica.
+template <typename V, int U, class Sh>
+__device__ __forceinline__ void copy_items(const reshard_descriptor_t& D, const uint8_t* src,
+                                           const Sh& sh, uint32_t lo, uint32_t hi) {
   V v[U];
   uint64_t doff[U];
   bool ok[U];
@@ -111,35 +132,124 @@ __device__ __forceinline__ void copy_tile(const reshard_descriptor_t& D, const u
   for (int k = 0; k < U; ++k) {
     const uint32_t f = lo + uint32_t(k * kBlock) + threadIdx.x;
     ok[k] = f < hi;
-    const ItemOffsets o = item_offsets(D, ok[k] ? f : lo);
-    doff[k] = o.dst;
-    if (ok[k]) v[k] = load_item<V>(src + o.src);
+    const ItemPos o = item_pos(D, ok[k] ? f : lo);
+    const uint64_t c = uint64_t(o.col) * sizeof(V);
+    doff[k] = o.dst + c;
+    if (ok[k]) v[k] = load_item<V>(src + o.src + c);
   }
   for (uint32_t r = 0; r < D.fanout; ++r) {
-    uint8_t* dst = reinterpret_cast<uint8_t*>(shard_ptr(table, karg, refs[D.dst_ref_begin + r]));
+    uint8_t* dst = reinterpret_cast<uint8_t*>(sh.dst(r));
 #pragma unroll
     for (int k = 0; k < U; ++k)
       if (ok[k]) store_item<V>(dst + doff[k], v[k]);
   }
 }
 
-// Same traffic bytewise, for shard pointers not aligned to the descriptor's unit.
-__device__ void copy_tile_bytes(const reshard_descriptor_t& D, const uint8_t* src,
-                                const uint32_t* __restrict__ refs, const void* const* table,
-                                const KargPtrs& karg, uint32_t lo, uint32_t hi) {
+// Byte range [lo, hi) of the destination row starting at `row` (absolute address
+// of replica 0) that chunk `col` covers: the row's part of the col-th 16-byte
+// aligned block it touches.
+__device__ __forceinline__ void chunk_range(uintptr_t row, uint32_t run, uint32_t col,
+                                            uintptr_t* lo, uintptr_t* hi) {
+  const uintptr_t block = (row & ~uintptr_t(15)) + uintptr_t(col) * 16;
+  *lo = block > row ? block : row;
+  *hi = block + 16 < row + run ? block + 16 : row + run;
+  if (*hi < *lo) *hi = *lo;  // a block past the row's end: empty
+}
+
+// Partial chunk: the n < 16 bytes at s go to d_r = d + shift_r for every
+// replica.  n, s and d are multiples of sizeof(E); all loads are issued before
+// any store so that they overlap.
+template <typename E, class Sh>
+__device__ __forceinline__ void copy_partial(uintptr_t s, uintptr_t d, uint32_t n, const Sh& sh,
+                                             uint32_t fanout, uintptr_t d0) {
+  constexpr int kMax = 16 / int(sizeof(E));
+  E e[kMax];
+#pragma unroll
+  for (int i = 0; i < kMax; ++i)
+    if (uint32_t(i) * sizeof(E) < n) e[i] = *as_global<const E>(s + i * sizeof(E));
+  for (uint32_t r = 0; r < fanout; ++r) {
+    const uintptr_t dr = d + (sh.dst(r) - d0);
+#pragma unroll
+    for (int i = 0; i < kMax; ++i)
+      if (uint32_t(i) * sizeof(E) < n) *as_global<E>(dr + i * sizeof(E)) = e[i];
+  }
+}
+
+// DST_CHUNKS mode: chunks [lo, hi).  A full chunk is one unaligned 16-byte load
+// and one aligned 16-byte store per replica.  The partial chunks at the two ends
+// of a row are copied afterwards in pieces of the row's alignment.  Replicas
+// share replica 0's 16-byte phase.
+template <int U, class Sh>
+__device__ __forceinline__ void copy_chunks(const reshard_descriptor_t& D, uint32_t unit,
+                                            const uint8_t* src, const Sh& sh, uint32_t lo, uint32_t hi) {
+  const uintptr_t d0 = sh.dst(0);
+  u32x4 v[U];
+  uintptr_t clo[U], chi[U];   // covered destination bytes, replica-0 addresses
+  uintptr_t sdelta[U];        // source address minus destination address for this row
+  bool full[U];
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const uint32_t f = lo + uint32_t(k * kBlock) + threadIdx.x;
+    const ItemPos o = item_pos(D, f < hi ? f : lo);
+    const uintptr_t row = d0 + o.dst;
+    chunk_range(row, D.run_bytes, o.col, &clo[k], &chi[k]);
+    if (f >= hi) chi[k] = clo[k];
+    sdelta[k] = reinterpret_cast<uintptr_t>(src) + o.src - row;
+    full[k] = chi[k] - clo[k] == 16;
+    if (full[k]) v[k] = load_16_unaligned(clo[k] + sdelta[k]);
+  }
+  for (uint32_t r = 0; r < D.fanout; ++r) {
+    const uintptr_t shift = sh.dst(r) - d0;
+#pragma unroll
+    for (int k = 0; k < U; ++k)
+      if (full[k]) __builtin_nontemporal_store(v[k], as_global<u32x4>(clo[k] + shift));
+  }
+#pragma unroll
+  for (int k = 0; k < U; ++k) {
+    const uint32_t n = uint32_t(chi[k] - clo[k]);
+    if (full[k] || n == 0) continue;
+    const uintptr_t s = clo[k] + sdelta[k];
+    if (unit >= 4) copy_partial<uint32_t>(s, clo[k], n, sh, D.fanout, d0);
+    else if (unit == 2) copy_partial<uint16_t>(s, clo[k], n, sh, D.fanout, d0);
+    else copy_partial<uint8_t>(s, clo[k], n, sh, D.fanout, d0);
+  }
+}
+
+// Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
+// aligned to the descriptor's unit, or replicas differ in 16-byte phase.
+template <class Sh>
+__device__ void copy_bytes(const reshard_descriptor_t& D, uint32_t unit, uint32_t mode,
+                           const uint8_t* src, const Sh& sh, uint32_t lo, uint32_t hi) {
+  const uintptr_t d0 = sh.dst(0);
   for (uint32_t f = lo + threadIdx.x; f < hi; f += kBlock) {
-    const ItemOffsets o = item_offsets(D, f);
+    const ItemPos o = item_pos(D, f);
+    uintptr_t a, b;
+    if (mode == RESHARD_DESC_DST_CHUNKS) {
+      chunk_range(d0 + o.dst, D.run_bytes, o.col, &a, &b);
+      a -= d0;
+      b -= d0;
+    } else {
+      a = o.dst + uint64_t(o.col) * unit;
+      b = a + unit;
+    }
+    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src) + o.src;
     for (uint32_t r = 0; r < D.fanout; ++r) {
-      uint8_t* dst = reinterpret_cast<uint8_t*>(shard_ptr(table, karg, refs[D.dst_ref_begin + r]));
-      for (uint32_t b = 0; b < D.unit; ++b) dst[o.dst + b] = src[o.src + b];
+      const uintptr_t dr = sh.dst(r);
+      for (uintptr_t x = a; x < b; ++x)  // same place in the row on both sides
+        *as_global<uint8_t>(dr + x) = *as_global<const uint8_t>(s0 + (x - o.dst));
     }
   }
 }
 
+// Bits of the kernel's `flags` argument.
+constexpr uint32_t kAllAligned16 = 1;  // every shard pointer of this execute is 16-byte aligned
+
+template <bool kKarg>
 __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     const reshard_descriptor_t* __restrict__ descs, uint32_t n_desc,
     const uint32_t* __restrict__ tile_begin, const uint32_t* __restrict__ refs,
-    const void* const* __restrict__ table, KargPtrs karg, uint32_t n_tiles, uint32_t per_xcd) {
+    const void* const* __restrict__ table, KargPtrs karg, uint32_t n_tiles, uint32_t per_xcd,
+    uint32_t flags) {
   // consecutive tiles on one XCD: block b runs on XCD b % kXcds
   const uint32_t t = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
   if (t >= n_tiles) return;
@@ -149,22 +259,39 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     if (tile_begin[mid] <= t) lo = mid; else hi = mid;
   }
   const reshard_descriptor_t& D = descs[lo];
-  const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.run_units;
-  const uint32_t first = (t - tile_begin[lo]) * rs::tile_items(D.unit);
-  const uint32_t last = min(first + rs::tile_items(D.unit), items);
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(shard_ptr(table, karg, D.src_ptr));
-  uintptr_t bits = reinterpret_cast<uintptr_t>(src);
-  for (uint32_t r = 0; r < D.fanout; ++r) bits |= shard_ptr(table, karg, refs[D.dst_ref_begin + r]);
-  if (bits & (D.unit - 1)) {
-    copy_tile_bytes(D, src, refs, table, karg, first, last);
+  uint32_t unit_mode;  // the two 16-bit fields as one scalar word
+  __builtin_memcpy(&unit_mode, &D.unit, sizeof(unit_mode));
+  const uint32_t unit = unit_mode & 0xffffu, mode = unit_mode >> 16;
+  const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;
+  const uint32_t first = (t - tile_begin[lo]) * rs::kTileItems;
+  const uint32_t last = min(first + rs::kTileItems, items);
+  const Shards<kKarg> sh{table, &karg, refs + D.dst_ref_begin};
+  const uint8_t* src = reinterpret_cast<const uint8_t*>(sh.ptr(D.src_ptr));
+  if (!(flags & kAllAligned16)) {
+    // alignment every access width relies on: the unit for ITEMS; for
+    // DST_CHUNKS, replicas in the same 16-byte phase as replica 0
+    const uintptr_t d0 = sh.dst(0);
+    uintptr_t bits = reinterpret_cast<uintptr_t>(src) | d0, phase = 0;
+    for (uint32_t r = 1; r < D.fanout; ++r) {
+      bits |= sh.dst(r);
+      phase |= sh.dst(r) - d0;
+    }
+    const bool ok = mode == RESHARD_DESC_DST_CHUNKS ? (phase & 15) == 0 : (bits & (unit - 1)) == 0;
+    if (!ok) {
+      copy_bytes(D, unit, mode, src, sh, first, last);
+      return;
+    }
+  }
+  if (mode == RESHARD_DESC_DST_CHUNKS) {
+    copy_chunks<rs::kItemsPerThread>(D, unit, src, sh, first, last);
     return;
   }
-  switch (D.unit) {
-    case 16: copy_tile<u32x4, rs::tile_items_per_thread(16)>(D, src, refs, table, karg, first, last); break;
-    case 8: copy_tile<u32x2, rs::tile_items_per_thread(8)>(D, src, refs, table, karg, first, last); break;
-    case 4: copy_tile<uint32_t, rs::tile_items_per_thread(4)>(D, src, refs, table, karg, first, last); break;
-    case 2: copy_tile<uint16_t, rs::tile_items_per_thread(2)>(D, src, refs, table, karg, first, last); break;
-    default: copy_tile<uint8_t, rs::tile_items_per_thread(1)>(D, src, refs, table, karg, first, last); break;
+  switch (unit) {
+    case 16: copy_items<u32x4, rs::kItemsPerThread>(D, src, sh, first, last); break;
+    case 8: copy_items<u32x2, rs::kItemsPerThread>(D, src, sh, first, last); break;
+    case 4: copy_items<uint32_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
+    case 2: copy_items<uint16_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
+    default: copy_items<uint8_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
   }
 }
 
@@ -377,6 +504,10 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
   const void* const* table = nullptr;
   int slot = -1;
   hipError_t e;
+  uintptr_t ptr_bits = 0;  // low bits of every pointer, for the all-aligned fast path
+  for (int64_t i = 0; i < H.n_src_ptrs; ++i) ptr_bits |= reinterpret_cast<uintptr_t>(src_ptrs[i]);
+  for (int64_t i = 0; i < H.n_dst_ptrs; ++i) ptr_bits |= reinterpret_cast<uintptr_t>(dst_ptrs[i]);
+  const uint32_t flags = (ptr_bits & 15) == 0 ? kAllAligned16 : 0;
   if (plan->n_ptrs <= kKargPtrs) {
     for (int64_t i = 0; i < H.n_src_ptrs; ++i) karg.p[i] = src_ptrs[i];
     for (int64_t i = 0; i < H.n_dst_ptrs; ++i) karg.p[H.n_src_ptrs + i] = dst_ptrs[i];
@@ -412,9 +543,14 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
     }
     table = reinterpret_cast<const void* const*>(static_cast<void**>(plan->d_slots) + size_t(slot) * n);
   }
-  hipLaunchKernelGGL(reshard_copy_kernel, dim3(plan->n_wg), dim3(kBlock), 0, stream, plan->d_descs,
-                     uint32_t(H.descs.size()), plan->d_tile_begin, plan->d_refs, table, karg,
-                     uint32_t(H.n_tiles), plan->per_xcd);
+  if (table)
+    hipLaunchKernelGGL(reshard_copy_kernel<false>, dim3(plan->n_wg), dim3(kBlock), 0, stream,
+                       plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin, plan->d_refs,
+                       table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
+  else
+    hipLaunchKernelGGL(reshard_copy_kernel<true>, dim3(plan->n_wg), dim3(kBlock), 0, stream,
+                       plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin, plan->d_refs,
+                       table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "reshard_copy_kernel launch");
   if (slot >= 0) {

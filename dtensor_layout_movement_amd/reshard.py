@@ -35,6 +35,9 @@ DTYPE_BF16, DTYPE_F16, DTYPE_I16 = 5, 6, 7
 DTYPE_F32, DTYPE_I32 = 8, 9
 DTYPE_F64, DTYPE_I64 = 10, 11
 
+DESC_ITEMS = 0       # rows of items of `unit` bytes
+DESC_DST_CHUNKS = 1  # rows cut into destination-aligned 16-byte chunks
+
 EXPORTED = (
     "reshard_dtype_size", "reshard_layout_create", "reshard_layout_destroy",
     "reshard_layout_num_ranks", "reshard_layout_shard_box", "reshard_plan_create",
@@ -67,11 +70,11 @@ class Piece(ctypes.Structure):
 class Descriptor(ctypes.Structure):
     _fields_ = [("src_offset", ctypes.c_int64), ("dst_offset", ctypes.c_int64),
                 ("src_stride", ctypes.c_int64 * 3), ("dst_stride", ctypes.c_int64 * 3),
-                ("extent", ctypes.c_uint32 * 3), ("run_units", ctypes.c_uint32),
-                ("unit", ctypes.c_uint32), ("src_ptr", ctypes.c_uint32),
-                ("dst_ref_begin", ctypes.c_uint32), ("fanout", ctypes.c_uint32),
-                ("magic", (ctypes.c_uint32 * 2) * 3), ("piece", ctypes.c_uint32),
-                ("reserved", ctypes.c_uint32)]
+                ("extent", ctypes.c_uint32 * 3), ("run_bytes", ctypes.c_uint32),
+                ("row_items", ctypes.c_uint32), ("unit", ctypes.c_uint16), ("mode", ctypes.c_uint16),
+                ("src_ptr", ctypes.c_uint32), ("dst_ref_begin", ctypes.c_uint32),
+                ("fanout", ctypes.c_uint32), ("magic", (ctypes.c_uint32 * 2) * 3),
+                ("piece", ctypes.c_uint32)]
 
 
 assert ctypes.sizeof(Descriptor) == 128
@@ -252,7 +255,8 @@ def reshard_plan_descriptors(plan: int):
         out.append({
             "src_offset": d.src_offset, "dst_offset": d.dst_offset,
             "src_stride": list(d.src_stride), "dst_stride": list(d.dst_stride),
-            "extent": list(d.extent), "run_units": d.run_units, "unit": d.unit,
+            "extent": list(d.extent), "run_bytes": d.run_bytes, "row_items": d.row_items,
+            "unit": d.unit, "mode": d.mode,
             "src_ptr": d.src_ptr, "dst_ref_begin": d.dst_ref_begin, "fanout": d.fanout,
             "magic": [list(m) for m in d.magic], "piece": d.piece,
         })

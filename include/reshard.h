@@ -104,27 +104,39 @@ typedef struct reshard_piece {
   int64_t hi[RESHARD_MAX_NDIM];
 } reshard_piece_t;
 
+/* Descriptor modes. */
+#define RESHARD_DESC_ITEMS 0      /* rows of items of `unit` bytes (unit = 16, or short rows) */
+#define RESHARD_DESC_DST_CHUNKS 1 /* rows cut into 16-byte chunks aligned to the destination */
+
 /*
  * Device copy descriptor (the table the kernel reads; inspection API).
- * The descriptor copies rows of `run_units` items of `unit` bytes.  Rows are
- * indexed by up to three outer dims (extent[0] outermost); a row's first byte is
+ * A descriptor copies rows of `run_bytes` contiguous bytes.  Rows are indexed by
+ * up to three outer dims (extent[0] outermost); a row's first byte is
  *   base + offset + i0*stride[0] + i1*stride[1] + i2*stride[2]
- * on each side, base being the shard pointer.  Items in a row are contiguous.
+ * on each side, base being the shard pointer.  The kernel indexes `row_items`
+ * items per row:
+ *   RESHARD_DESC_ITEMS       item c is bytes [c*unit, (c+1)*unit) of the row;
+ *                            row_items = run_bytes / unit.
+ *   RESHARD_DESC_DST_CHUNKS  item c is the part of the row inside the c-th 16-byte
+ *                            aligned destination block the row touches (empty,
+ *                            partial or full); row_items = ceil((run_bytes+15)/16);
+ *                            `unit` is the row's natural alignment (1..8 bytes).
  */
 typedef struct reshard_descriptor {
-  int64_t src_offset;       /* byte offset of the first item in the source shard */
-  int64_t dst_offset;       /* byte offset of the first item in each destination shard */
+  int64_t src_offset;       /* byte offset of the row origin in the source shard */
+  int64_t dst_offset;       /* byte offset of the row origin in each destination shard */
   int64_t src_stride[3];    /* bytes, outer dims; unused dims have extent 1 */
   int64_t dst_stride[3];
   uint32_t extent[3];       /* outer extents; product = rows */
-  uint32_t run_units;       /* items per row */
-  uint32_t unit;            /* item size in bytes: 1, 2, 4, 8 or 16 */
+  uint32_t run_bytes;       /* contiguous bytes per row, both sides */
+  uint32_t row_items;       /* items the kernel indexes per row (see the modes) */
+  uint16_t unit;            /* item size (ITEMS) or natural alignment (DST_CHUNKS) */
+  uint16_t mode;            /* RESHARD_DESC_ITEMS or RESHARD_DESC_DST_CHUNKS */
   uint32_t src_ptr;         /* index into the execute's source pointer array */
   uint32_t dst_ref_begin;   /* first entry of this descriptor's fan-out list */
   uint32_t fanout;          /* destination pointers written */
-  uint32_t magic[3][2];     /* division constants for run_units, extent[2], extent[1] */
+  uint32_t magic[3][2];     /* division constants for row_items, extent[2], extent[1] */
   uint32_t piece;           /* index of the planned piece it copies (or part of) */
-  uint32_t reserved;
 } reshard_descriptor_t;
 
 /* Bytes per element of `dtype`, or 0 if unknown. */

@@ -124,27 +124,49 @@ def apply_pieces(plan: Plan, srcs_per_tensor, fill=None):
     return out
 
 
+def _ranges(starts, lengths):
+    """Concatenation of the integer ranges [starts[i], starts[i] + lengths[i])."""
+    lengths = np.asarray(lengths, dtype=np.int64)
+    total = int(lengths.sum())
+    if total == 0:
+        return np.zeros(0, dtype=np.int64)
+    offs = np.repeat(np.cumsum(lengths) - lengths, lengths)
+    return np.repeat(np.asarray(starts, dtype=np.int64), lengths) + (np.arange(total) - offs)
+
+
 def run_descriptors(plan: Plan, srcs_flat, dsts_flat):
     """Execute the descriptor table on host byte arrays exactly as the kernel
-    addresses memory.  srcs_flat/dsts_flat: uint8 numpy arrays (or None), in
-    the pointer-array order of reshard_execute."""
+    addresses memory (shard bases taken as 16-byte aligned).  srcs_flat /
+    dsts_flat: uint8 numpy arrays (or None), in the pointer-array order of
+    reshard_execute.  For DST_CHUNKS descriptors it also checks that the chunks
+    of every row tile the row exactly."""
     descs, refs = R.reshard_plan_descriptors(plan.handle)
     for D in descs:
         e0, e1, e2 = D["extent"]
-        ru, u = D["run_units"], D["unit"]
-        i0, i1, i2, col = np.meshgrid(np.arange(e0), np.arange(e1), np.arange(e2), np.arange(ru),
-                                      indexing="ij")
+        i0, i1, i2 = np.meshgrid(np.arange(e0), np.arange(e1), np.arange(e2), indexing="ij")
         so = (D["src_offset"] + i0 * D["src_stride"][0] + i1 * D["src_stride"][1]
-              + i2 * D["src_stride"][2] + col * u).reshape(-1)
+              + i2 * D["src_stride"][2]).reshape(-1)
         do = (D["dst_offset"] + i0 * D["dst_stride"][0] + i1 * D["dst_stride"][1]
-              + i2 * D["dst_stride"][2] + col * u).reshape(-1)
-        so = (so[:, None] + np.arange(u)[None, :]).reshape(-1)
-        do = (do[:, None] + np.arange(u)[None, :]).reshape(-1)
-        src = srcs_flat[D["src_ptr"]]
-        data = src[so]
+              + i2 * D["dst_stride"][2]).reshape(-1)
+        L, n = D["run_bytes"], D["row_items"]
+        c = np.arange(n, dtype=np.int64)
+        if D["mode"] == R.DESC_ITEMS:
+            assert n * D["unit"] == L
+            lo = do[:, None] + c[None, :] * D["unit"]
+            hi = lo + D["unit"]
+        else:
+            assert D["mode"] == R.DESC_DST_CHUNKS and n == (L + 30) // 16
+            block = (do[:, None] & ~15) + 16 * c[None, :]
+            lo = np.maximum(block, do[:, None])
+            hi = np.maximum(np.minimum(block + 16, do[:, None] + L), lo)
+            assert ((hi - lo).sum(axis=1) == L).all()          # every byte of every row, once
+        lengths = (hi - lo).reshape(-1)
+        dst_idx = _ranges(lo.reshape(-1), lengths)
+        shift = np.repeat(np.repeat(so - do, n), lengths)       # same place in the row
+        src_idx = dst_idx + shift
+        data = srcs_flat[D["src_ptr"]][src_idx]
         for r in range(D["fanout"]):
-            dst = dsts_flat[refs[D["dst_ref_begin"] + r]]
-            dst[do] = data
+            dsts_flat[refs[D["dst_ref_begin"] + r]][dst_idx] = data
 
 
 def shard_bytes(plan: Plan):
@@ -164,9 +186,9 @@ def assert_descriptors_in_bounds(plan: Plan):
     descs, refs = R.reshard_plan_descriptors(plan.handle)
     for D in descs:
         ext = D["extent"]
-        assert D["run_units"] >= 1 and all(e >= 1 for e in ext)
-        assert ext[0] * ext[1] * ext[2] * D["run_units"] < 2 ** 31
-        span = D["run_units"] * D["unit"]
+        assert D["run_bytes"] >= 1 and D["row_items"] >= 1 and all(e >= 1 for e in ext)
+        assert ext[0] * ext[1] * ext[2] * D["row_items"] < 2 ** 31
+        span = D["run_bytes"]
         s_last = D["src_offset"] + sum((e - 1) * st for e, st in zip(ext, D["src_stride"])) + span
         d_last = D["dst_offset"] + sum((e - 1) * st for e, st in zip(ext, D["dst_stride"])) + span
         assert D["src_offset"] >= 0 and D["dst_offset"] >= 0

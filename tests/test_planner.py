@@ -48,6 +48,9 @@ def small_specs():
         T("nested", (9, 4, 10), torch.bfloat16, (2, 3), (0, 0), (2, 2, 2), (2, 0, 2)),
         T("one_elem", (1,), torch.float32, (3,), (0,), (2,), (RR,)),
         T("peel_outer", (3, 5, 5, 5, 6), torch.float32, (2, 2, 2), (1, 2, 3), (2,), (4,)),
+        T("chunked_bf16", (37, 301), torch.bfloat16, (3,), (1,), (2, 2), (RR, 0)),
+        T("chunked_u8", (9, 1000), torch.uint8, (3,), (1,), (2,), (0,)),
+        T("chunked_f64", (11, 45), torch.float64, (2,), (1,), (3,), (0,)),
     ]
     return specs
 
@@ -224,12 +227,12 @@ def test_dim_merging():
         descs, _ = R.reshard_plan_descriptors(plan.handle)
         gate = descs[0]  # gate piece: rows of a row split -> one contiguous run
         assert gate["extent"] == [1, 1, 1] and gate["unit"] == 16
-        assert gate["run_units"] * 16 == 3584 * 4096 * 2
-        down = [d for d in descs if d["run_units"] * d["unit"] == 3584 * 2]
+        assert gate["run_bytes"] == 3584 * 4096 * 2 and gate["mode"] == R.DESC_ITEMS
+        down = [d for d in descs if d["run_bytes"] == 3584 * 2]
         assert down and all(d["extent"][2] == 4096 for d in down)
     with Plan(W.moe_experts().tensors) as plan:
         d = R.reshard_plan_descriptors(plan.handle)[0][0]
-        assert d["extent"][1:] == [8, 1024] and d["run_units"] * d["unit"] == 1792
+        assert d["extent"][1:] == [8, 1024] and d["run_bytes"] == 1792 and d["unit"] == 16
 
 
 def test_big_tensor_is_split_within_31_bit_items():
@@ -242,10 +245,10 @@ def test_big_tensor_is_split_within_31_bit_items():
         pieces = R.reshard_plan_pieces(plan.handle)
         assert len(descs) > len(pieces)
         for d in descs:
-            items = d["extent"][0] * d["extent"][1] * d["extent"][2] * d["run_units"]
-            assert items < 2 ** 31
+            items = d["extent"][0] * d["extent"][1] * d["extent"][2] * d["row_items"]
+            assert items < 2 ** 31 and d["run_bytes"] <= 2 ** 30
         for i, pc in enumerate(pieces):
-            mine = sorted((d["src_offset"], d["run_units"] * d["unit"]) for d in descs if d["piece"] == i)
+            mine = sorted((d["src_offset"], d["run_bytes"]) for d in descs if d["piece"] == i)
             size = pc["hi"][0] - pc["lo"][0]
             pos = mine[0][0]
             for off, length in mine:
@@ -260,7 +263,7 @@ def test_magic_constants_exact():
         descs, _ = R.reshard_plan_descriptors(plan.handle)
     divisors = {}
     for d in descs:
-        divisors[d["run_units"]] = tuple(d["magic"][0])
+        divisors[d["row_items"]] = tuple(d["magic"][0])
         divisors[d["extent"][2]] = tuple(d["magic"][1])
         divisors[d["extent"][1]] = tuple(d["magic"][2])
     assert len(divisors) > 5
@@ -268,6 +271,17 @@ def test_magic_constants_exact():
         ns = [0, 1, dv - 1, dv, dv + 1, 2 ** 31 - 1, 2 ** 31 - 2] + [rng.randrange(2 ** 31) for _ in range(2000)]
         for n in ns:
             assert magic_div(n, m, s) == n // dv, (dv, n)
+
+
+def test_descriptor_modes():
+    """16-byte aligned rows copy as 16-byte items; long misaligned rows as
+    destination-aligned 16-byte chunks; short misaligned rows item by item."""
+    def modes(wl):
+        with Plan(wl.tensors) as plan:
+            return {(d["mode"], d["unit"]) for d in R.reshard_plan_descriptors(plan.handle)[0]}
+    assert modes(W.ffn_up()) == {(R.DESC_ITEMS, 16)}
+    assert modes(W.uneven()) == {(R.DESC_DST_CHUNKS, 4)}       # 12004-byte destination rows
+    assert modes(W.worked_example_8x8()) == {(R.DESC_ITEMS, 4)}  # 4-byte rows
 
 
 def test_outer_dims_beyond_three_are_peeled():
