@@ -65,10 +65,10 @@ struct Piece {
 };
 
 // Tiling.  One workgroup of kTileThreads threads copies one tile of one
-// descriptor: kTileItems consecutive items, two per thread (8 KiB of source for
+// descriptor: kTileItems consecutive items, one per thread (4 KiB of source for
 // 16-byte items and 16-byte destination chunks).
 constexpr uint32_t kTileThreads = 256;
-constexpr uint32_t kItemsPerThread = 2;
+constexpr uint32_t kItemsPerThread = 1;
 constexpr uint32_t kTileItems = kTileThreads * kItemsPerThread;
 
 // Rows at least this long whose alignment is below 16 bytes are copied as

@@ -2,13 +2,13 @@
 //
 // Execute = one launch of reshard_copy_kernel.  The plan's descriptor table
 // sits in device memory together with the first tile of every descriptor.  One
-// workgroup copies one tile (8 KiB of source for 16-byte items): it finds its
+// workgroup copies one tile (4 KiB of source for 16-byte items): it finds its
 // descriptor by a binary search over the tile prefix, then every thread loads
 // its item(s) once and stores them to each destination replica (the single-GPU
 // form of "send each contribution once, replicate locally": techfeed.io
 // write-up, "NVIDIA's NVLink implementation" section).  Many small workgroups
-// let the dispatcher balance the load; consecutive tiles are kept on one XCD so
-// that rows straddling tile edges merge in that XCD's L2.  Data only moves
+// let the dispatcher balance the load; groups of consecutive tiles are kept on
+// one XCD so that rows straddling tile edges merge in that XCD's L2.  Data only moves
 // through integer registers, so the copy is bit-exact for every dtype.
 #include <hip/hip_runtime.h>
 
@@ -30,6 +30,7 @@ namespace {
 
 constexpr int kBlock = int(rs::kTileThreads);  // threads per workgroup (4 wave64s)
 constexpr uint32_t kXcds = 8;          // MI355X: workgroups go round-robin over 8 XCDs
+constexpr uint32_t kXcdGroup = 64;     // consecutive tiles one XCD takes at a time
 constexpr int kKargPtrs = 120;         // pointer slots passed in kernel arguments
 constexpr int kSlots = 8;              // device pointer-table slots for bigger plans
 
@@ -156,62 +157,86 @@ __device__ __forceinline__ void chunk_range(uintptr_t row, uint32_t run, uint32_
   if (*hi < *lo) *hi = *lo;  // a block past the row's end: empty
 }
 
-// Partial chunk: the n < 16 bytes at s go to d_r = d + shift_r for every
-// replica.  n, s and d are multiples of sizeof(E); all loads are issued before
-// any store so that they overlap.
-template <typename E, class Sh>
-__device__ __forceinline__ void copy_partial(uintptr_t s, uintptr_t d, uint32_t n, const Sh& sh,
-                                             uint32_t fanout, uintptr_t d0) {
-  constexpr int kMax = 16 / int(sizeof(E));
-  E e[kMax];
-#pragma unroll
-  for (int i = 0; i < kMax; ++i)
-    if (uint32_t(i) * sizeof(E) < n) e[i] = *as_global<const E>(s + i * sizeof(E));
-  for (uint32_t r = 0; r < fanout; ++r) {
-    const uintptr_t dr = d + (sh.dst(r) - d0);
-#pragma unroll
-    for (int i = 0; i < kMax; ++i)
-      if (uint32_t(i) * sizeof(E) < n) *as_global<E>(dr + i * sizeof(E)) = e[i];
+typedef uint64_t u64_u __attribute__((aligned(1)));
+typedef uint32_t u32_u __attribute__((aligned(1)));
+typedef uint16_t u16_u __attribute__((aligned(1)));
+
+// v >> (8 * s) as a 128-bit little-endian value, 1 <= s <= 15.
+__device__ __forceinline__ u32x4 shift_right_bytes(u32x4 v, uint32_t s) {
+  uint64_t lo = (uint64_t(v.y) << 32) | v.x, hi = (uint64_t(v.w) << 32) | v.z;
+  const uint32_t b = 8 * s;
+  if (b >= 64) {
+    lo = hi >> (b - 64);
+    hi = 0;
+  } else {
+    lo = (lo >> b) | (hi << (64 - b));
+    hi >>= b;
   }
+  return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
 }
 
-// DST_CHUNKS mode: chunks [lo, hi).  A full chunk is one unaligned 16-byte load
-// and one aligned 16-byte store per replica.  The partial chunks at the two ends
-// of a row are copied afterwards in pieces of the row's alignment.  Replicas
-// share replica 0's 16-byte phase.
+// The first n < 16 bytes of v to address d, with at most four stores.
+__device__ __forceinline__ void store_head_bytes(uintptr_t d, u32x4 v, uint32_t n) {
+  uint64_t lo = (uint64_t(v.y) << 32) | v.x;
+  const uint64_t hi = (uint64_t(v.w) << 32) | v.z;
+  if (n & 8) {
+    *as_global<u64_u>(d) = lo;
+    d += 8;
+    lo = hi;
+  }
+  if (n & 4) {
+    *as_global<u32_u>(d) = uint32_t(lo);
+    d += 4;
+    lo >>= 32;
+  }
+  if (n & 2) {
+    *as_global<u16_u>(d) = uint16_t(lo);
+    d += 2;
+    lo >>= 16;
+  }
+  if (n & 1) *as_global<uint8_t>(d) = uint8_t(lo);
+}
+
+// DST_CHUNKS mode: chunks [lo, hi).  Every non-empty chunk is one 16-byte load
+// that stays inside its source row: at the chunk's own bytes for a full chunk,
+// at the row start for the head chunk and at the row end minus 16 for the tail
+// chunk (rows are at least kChunkedMinRun bytes).  A full chunk is then one
+// aligned 16-byte store per replica; a partial one (fewer than 16 bytes) at most
+// four.  All loads are issued before any store.  Replicas share replica 0's
+// 16-byte phase.
 template <int U, class Sh>
-__device__ __forceinline__ void copy_chunks(const reshard_descriptor_t& D, uint32_t unit,
-                                            const uint8_t* src, const Sh& sh, uint32_t lo, uint32_t hi) {
+__device__ __forceinline__ void copy_chunks(const reshard_descriptor_t& D, const uint8_t* src,
+                                            const Sh& sh, uint32_t lo, uint32_t hi) {
   const uintptr_t d0 = sh.dst(0);
+  const uint32_t run = D.run_bytes;
   u32x4 v[U];
-  uintptr_t clo[U], chi[U];   // covered destination bytes, replica-0 addresses
-  uintptr_t sdelta[U];        // source address minus destination address for this row
-  bool full[U];
+  uintptr_t clo[U];  // first covered destination byte, replica-0 address
+  uint32_t n[U];     // covered bytes: 16 (full), 1..15 (partial) or 0
+  uint32_t skip[U];  // leading bytes of the load that precede the chunk (tail chunk only)
 #pragma unroll
   for (int k = 0; k < U; ++k) {
     const uint32_t f = lo + uint32_t(k * kBlock) + threadIdx.x;
     const ItemPos o = item_pos(D, f < hi ? f : lo);
     const uintptr_t row = d0 + o.dst;
-    chunk_range(row, D.run_bytes, o.col, &clo[k], &chi[k]);
-    if (f >= hi) chi[k] = clo[k];
-    sdelta[k] = reinterpret_cast<uintptr_t>(src) + o.src - row;
-    full[k] = chi[k] - clo[k] == 16;
-    if (full[k]) v[k] = load_16_unaligned(clo[k] + sdelta[k]);
+    uintptr_t chi;
+    chunk_range(row, run, o.col, &clo[k], &chi);
+    n[k] = f < hi ? uint32_t(chi - clo[k]) : 0u;
+    const uint32_t off = uint32_t(clo[k] - row);            // chunk's first byte within the row
+    const uint32_t load_off = off < run - 16 ? off : run - 16;
+    skip[k] = off - load_off;
+    if (n[k] != 0) v[k] = load_16_unaligned(reinterpret_cast<uintptr_t>(src) + o.src + load_off);
   }
+#pragma unroll
+  for (int k = 0; k < U; ++k)
+    if (n[k] != 0 && skip[k] != 0) v[k] = shift_right_bytes(v[k], skip[k]);
   for (uint32_t r = 0; r < D.fanout; ++r) {
     const uintptr_t shift = sh.dst(r) - d0;
 #pragma unroll
-    for (int k = 0; k < U; ++k)
-      if (full[k]) __builtin_nontemporal_store(v[k], as_global<u32x4>(clo[k] + shift));
-  }
-#pragma unroll
-  for (int k = 0; k < U; ++k) {
-    const uint32_t n = uint32_t(chi[k] - clo[k]);
-    if (full[k] || n == 0) continue;
-    const uintptr_t s = clo[k] + sdelta[k];
-    if (unit >= 4) copy_partial<uint32_t>(s, clo[k], n, sh, D.fanout, d0);
-    else if (unit == 2) copy_partial<uint16_t>(s, clo[k], n, sh, D.fanout, d0);
-    else copy_partial<uint8_t>(s, clo[k], n, sh, D.fanout, d0);
+    for (int k = 0; k < U; ++k) {
+      const uintptr_t d = clo[k] + shift;
+      if (n[k] == 16) __builtin_nontemporal_store(v[k], as_global<u32x4>(d));
+      else if (n[k] != 0) store_head_bytes(d, v[k], n[k]);
+    }
   }
 }
 
@@ -250,8 +275,11 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     const uint32_t* __restrict__ tile_begin, const uint32_t* __restrict__ refs,
     const void* const* __restrict__ table, KargPtrs karg, uint32_t n_tiles, uint32_t per_xcd,
     uint32_t flags) {
-  // consecutive tiles on one XCD: block b runs on XCD b % kXcds
-  const uint32_t t = (blockIdx.x % kXcds) * per_xcd + blockIdx.x / kXcds;
+  // Block b runs on XCD b % kXcds.  Each XCD takes groups of kXcdGroup
+  // consecutive tiles, the XCDs side by side: nearby tiles share an XCD's L2
+  // while all XCDs stream through the same region of memory.
+  const uint32_t kx = blockIdx.x / kXcds;
+  const uint32_t t = ((kx / kXcdGroup) * kXcds + blockIdx.x % kXcds) * kXcdGroup + kx % kXcdGroup;
   if (t >= n_tiles) return;
   uint32_t lo = 0, hi = n_desc;  // last descriptor whose first tile is <= t
   while (hi - lo > 1) {
@@ -283,7 +311,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     }
   }
   if (mode == RESHARD_DESC_DST_CHUNKS) {
-    copy_chunks<rs::kItemsPerThread>(D, unit, src, sh, first, last);
+    copy_chunks<rs::kItemsPerThread>(D, src, sh, first, last);
     return;
   }
   switch (unit) {
@@ -306,8 +334,8 @@ struct reshard_plan_s {
   std::mutex mu;
   bool uploaded = false;
   int device = -1;
-  uint32_t n_wg = 0;       // grid of one launch (tiles rounded up to a multiple of kXcds)
-  uint32_t per_xcd = 0;    // tiles per XCD
+  uint32_t n_wg = 0;       // grid of one launch: kXcds * per_xcd blocks (surplus ones exit)
+  uint32_t per_xcd = 0;    // blocks per XCD, a multiple of kXcdGroup
   void* table = nullptr;  // device: descriptors | refs (absolute pointer slots) | tile_begin
   const reshard_descriptor_t* d_descs = nullptr;
   const uint32_t* d_refs = nullptr;
@@ -336,7 +364,9 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
     return RESHARD_OK;
   }
   const rs::HostPlan& H = p->host;
-  const uint32_t per_xcd = uint32_t((H.n_tiles + kXcds - 1) / kXcds);
+  // blocks per XCD, a whole number of tile groups
+  const uint64_t per_xcd_min = (H.n_tiles + kXcds - 1) / kXcds;
+  const uint32_t per_xcd = uint32_t((per_xcd_min + kXcdGroup - 1) / kXcdGroup * kXcdGroup);
   const size_t desc_bytes = H.descs.size() * sizeof(reshard_descriptor_t);
   const size_t refs_off = align_up(desc_bytes, 256);
   const size_t tiles_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);

@@ -173,6 +173,7 @@ def test_upload_and_stats_after_execute():
     with Plan(W.ffn_up().tensors) as plan:
         R.reshard_plan_upload(plan.handle, torch.cuda.current_stream().cuda_stream)
         st = plan.stats()
-        tiles = -(-117440512 // 8192)  # one workgroup per 8 KiB source tile
-        assert st["n_workgroups"] == -(-tiles // 8) * 8
+        tiles = -(-117440512 // 4096)  # one workgroup per 4 KiB source tile
+        per_xcd = -(-(-(-tiles // 8)) // 64) * 64  # whole groups of 64 tiles per XCD
+        assert st["n_workgroups"] == 8 * per_xcd
         R.reshard_plan_upload(plan.handle, None)  # second upload is a no-op
