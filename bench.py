@@ -33,14 +33,19 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, decimal GB/s
 METRIC = "reshard execute GB/s (bytes read+written) and % of MI355X HBM peak; plan time us"
 DEFAULT_WORKLOAD = "ffn_up_14336x4096"
-KERNEL_SOURCE = os.path.join(ROOT, "dtensor_layout_movement_amd", "csrc", "reshard.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "dtensor_layout_movement_amd", "csrc", f)
+                  for f in ("reshard.hip", "plan.h", "plan.cpp")]
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_NAME = "reshard_copy_kernel"
 
 
 def kernel_source_sha() -> str:
-    with open(KERNEL_SOURCE, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the sources that fix what the copy kernel reads and writes."""
+    h = hashlib.sha256()
+    for path in KERNEL_SOURCES:
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def layout_str(mesh, placements) -> str:
