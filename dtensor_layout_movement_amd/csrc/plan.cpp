@@ -226,6 +226,185 @@ void describe_piece(HostPlan* P, uint32_t piece_idx, uint32_t src_ptr, uint32_t 
   emit(P, piece_idx, src_ptr, ref_begin, fanout, src_off, dst_off, run_bytes, outer);
 }
 
+// Copy descriptors of every piece of one tensor, in piece order.
+void emit_pieces(HostPlan* P, int t, size_t pc0, size_t pc1) {
+  const int nd = P->src[t].ndim;
+  const int64_t es = P->src[t].elem_size;
+  for (size_t i = pc0; i < pc1; ++i) {
+    const Piece& pc = P->pieces[i];
+    const Group& sgrp = P->src_groups[pc.src_group];
+    const Group& dgrp = P->dst_groups[pc.dst_group];
+    const uint32_t ref_begin = uint32_t(P->refs.size());
+    for (int64_t r : dgrp.ranks) P->refs.push_back(uint32_t(P->dst_base[t] + r));
+    describe_piece(P, uint32_t(i), uint32_t(P->src_base[t] + pc.src_rank), ref_begin,
+                   uint32_t(dgrp.ranks.size()), pc.box, sgrp.box, dgrp.box, nd, es);
+  }
+}
+
+// 2-d view of a tensor for windows: rows = dims 0..nd-2 flattened, columns =
+// the last dim.  Valid when no box splits dims 1..nd-2.
+struct View2d {
+  int64_t row_mult = 1;  // flattened rows per unit of dim 0
+  int64_t cols = 1;
+};
+
+bool view_2d(const HostPlan& P, int t, size_t pc0, size_t pc1, View2d* v) {
+  const Layout& S = P.src[t];
+  const int nd = S.ndim;
+  if (nd < 2) return false;
+  v->cols = S.shape[nd - 1];
+  v->row_mult = 1;
+  for (int k = 1; k < nd - 1; ++k) v->row_mult *= S.shape[k];
+  for (size_t i = pc0; i < pc1; ++i) {
+    const Box* boxes[2] = {&P.src_groups[P.pieces[i].src_group].box, &P.dst_groups[P.pieces[i].dst_group].box};
+    for (const Box* b : boxes)
+      for (int k = 1; k < nd - 1; ++k)
+        if (b->lo[k] != 0 || b->hi[k] != S.shape[k]) return false;
+  }
+  return true;
+}
+
+// Window bands of one tensor.  Rows are cut wherever a source or destination
+// box starts or ends; each band lists the pieces that cover it as source
+// segments (merged where one shard continues across pieces) and the
+// destination boxes that cover it as destination segments.
+bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
+  const int nd = P->src[t].ndim;
+  const int64_t es = P->src[t].elem_size;
+  const int64_t width = v.cols * es;
+  const int64_t pitch = (width + 15) / 16 * 16;
+  if (width <= 0 || pitch > int64_t(kWindowBytes)) return false;
+  const int64_t rows_per_tile = int64_t(kWindowBytes) / pitch;
+  auto rlo = [&](const Box& b) { return b.lo[0] * v.row_mult; };
+  auto rhi = [&](const Box& b) { return b.hi[0] * v.row_mult; };
+  std::vector<int64_t> cuts;
+  for (size_t i = pc0; i < pc1; ++i) {
+    cuts.push_back(rlo(P->pieces[i].box));
+    cuts.push_back(rhi(P->pieces[i].box));
+  }
+  std::sort(cuts.begin(), cuts.end());
+  cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+  struct Pending {
+    reshard_descriptor_t d;
+    std::vector<reshard_segment_t> src, dst;
+    std::vector<std::vector<uint32_t>> dst_refs;
+  };
+  std::vector<Pending> bands;
+  for (size_t c = 0; c + 1 < cuts.size(); ++c) {
+    const int64_t ra = cuts[c], rb = cuts[c + 1];
+    Pending b;
+    std::vector<int64_t> dst_seen;
+    int64_t bits = width;
+    for (size_t i = pc0; i < pc1; ++i) {
+      const Piece& pc = P->pieces[i];
+      if (rlo(pc.box) > ra || rhi(pc.box) < rb) continue;
+      const Box& sb = P->src_groups[pc.src_group].box;
+      const int64_t s_cols = sb.hi[nd - 1] - sb.lo[nd - 1];
+      reshard_segment_t s;
+      s.offset = ((ra - rlo(sb)) * s_cols + (pc.box.lo[nd - 1] - sb.lo[nd - 1])) * es;
+      s.row_stride = s_cols * es;
+      s.col = uint32_t(pc.box.lo[nd - 1] * es);
+      s.width = uint32_t((pc.box.hi[nd - 1] - pc.box.lo[nd - 1]) * es);
+      s.ptr = uint32_t(P->src_base[t] + pc.src_rank);
+      s.fanout = 0;
+      b.src.push_back(s);
+      if (std::find(dst_seen.begin(), dst_seen.end(), pc.dst_group) == dst_seen.end()) {
+        dst_seen.push_back(pc.dst_group);
+        const Group& dg = P->dst_groups[pc.dst_group];
+        const int64_t d_cols = dg.box.hi[nd - 1] - dg.box.lo[nd - 1];
+        reshard_segment_t d;
+        d.offset = (ra - rlo(dg.box)) * d_cols * es;
+        d.row_stride = d_cols * es;
+        d.col = uint32_t(dg.box.lo[nd - 1] * es);
+        d.width = uint32_t(d_cols * es);
+        d.ptr = 0;
+        d.fanout = uint32_t(dg.ranks.size());
+        b.dst.push_back(d);
+        std::vector<uint32_t> refs;
+        for (int64_t r : dg.ranks) refs.push_back(uint32_t(P->dst_base[t] + r));
+        b.dst_refs.push_back(refs);
+      }
+    }
+    // sources in column order; merge neighbours that continue in the same shard
+    std::sort(b.src.begin(), b.src.end(),
+              [](const reshard_segment_t& x, const reshard_segment_t& y) { return x.col < y.col; });
+    std::vector<reshard_segment_t> merged;
+    for (const reshard_segment_t& s : b.src) {
+      if (!merged.empty()) {
+        reshard_segment_t& m = merged.back();
+        if (m.ptr == s.ptr && m.row_stride == s.row_stride && m.col + m.width == s.col &&
+            m.offset + int64_t(m.width) == s.offset) {
+          m.width += s.width;
+          continue;
+        }
+      }
+      merged.push_back(s);
+    }
+    b.src = merged;
+    if (b.src.size() > kWindowMaxSegs || b.dst.size() > kWindowMaxSegs) return false;
+    for (const auto& s : b.src) bits |= s.offset | s.row_stride | s.col | s.width;
+    for (const auto& d : b.dst) bits |= d.offset | d.row_stride | d.col | d.width;
+    std::memset(&b.d, 0, sizeof(b.d));
+    b.d.mode = RESHARD_DESC_WINDOW;
+    b.d.unit = uint16_t(unit_for(bits));
+    b.d.run_bytes = uint32_t(width);
+    b.d.row_items = uint32_t(pitch);
+    b.d.extent[0] = uint32_t(rb - ra);
+    b.d.extent[1] = uint32_t(rows_per_tile);
+    b.d.extent[2] = 1;
+    b.d.piece = uint32_t(pc0);
+    if (rb - ra > int64_t(kMaxItems)) return false;
+    bands.push_back(std::move(b));
+  }
+  for (Pending& b : bands) {
+    b.d.src_ptr = uint32_t(P->segs.size());
+    b.d.dst_ref_begin = uint32_t(b.src.size());
+    b.d.fanout = uint32_t(b.dst.size());
+    for (const auto& s : b.src) P->segs.push_back(s);
+    for (size_t k = 0; k < b.dst.size(); ++k) {
+      reshard_segment_t d = b.dst[k];
+      d.ptr = uint32_t(P->refs.size());
+      for (uint32_t r : b.dst_refs[k]) P->refs.push_back(r);
+      P->segs.push_back(d);
+    }
+    P->descs.push_back(b.d);
+    P->desc_cost.push_back(uint64_t(b.d.extent[0]) * uint64_t(width));
+  }
+  return true;
+}
+
+// Descriptors of one tensor: windows when some piece has narrow rows and the
+// tensor has a 2-d view that fits, per-piece descriptors otherwise.
+void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1) {
+  if (pc0 == pc1) return;
+  const size_t d0 = P->descs.size(), r0 = P->refs.size();
+  emit_pieces(P, t, pc0, pc1);
+  bool narrow = false;
+  for (size_t i = d0; i < P->descs.size(); ++i) {
+    const reshard_descriptor_t& D = P->descs[i];
+    const uint64_t rows = uint64_t(D.extent[0]) * D.extent[1] * D.extent[2];
+    if (rows > 1 && int64_t(D.run_bytes) < kWindowMaxRun) narrow = true;
+  }
+  View2d v;
+  if (!narrow || !view_2d(*P, t, pc0, pc1, &v)) return;
+  const size_t s0 = P->segs.size();
+  std::vector<reshard_descriptor_t> saved(P->descs.begin() + d0, P->descs.end());
+  std::vector<uint64_t> saved_cost(P->desc_cost.begin() + d0, P->desc_cost.end());
+  std::vector<uint32_t> saved_refs(P->refs.begin() + r0, P->refs.end());
+  P->descs.resize(d0);
+  P->desc_cost.resize(d0);
+  P->refs.resize(r0);
+  if (!emit_windows(P, t, pc0, pc1, v)) {  // keep the per-piece descriptors
+    P->descs.resize(d0);
+    P->desc_cost.resize(d0);
+    P->refs.resize(r0);
+    P->segs.resize(s0);
+    P->descs.insert(P->descs.end(), saved.begin(), saved.end());
+    P->desc_cost.insert(P->desc_cost.end(), saved_cost.begin(), saved_cost.end());
+    P->refs.insert(P->refs.end(), saved_refs.begin(), saved_refs.end());
+  }
+}
+
 }  // namespace
 
 void magic_u31(uint32_t d, uint32_t* m, uint32_t* s) {
@@ -377,6 +556,7 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
     if (sg0 == sg1) continue;  // empty tensor
 
     SourceGrid grid = make_grid(nd, P->src_groups, sg0, sg1);
+    const size_t pc0 = P->pieces.size();
     for (size_t g = dg0; g < dg1; ++g) {
       const Group& dgrp = P->dst_groups[g];
       // per dim, the range of source intervals that overlap this destination box
@@ -412,14 +592,8 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
             if (load[P->src_base[t] + r] < load[P->src_base[t] + best]) best = r;
           const int64_t bytes = box_numel(nd, box) * es;
           load[P->src_base[t] + best] += bytes;
-          Piece pc{t, best, it->second, int64_t(g), box, bytes};
-          const uint32_t piece_idx = uint32_t(P->pieces.size());
-          P->pieces.push_back(pc);
-          const uint32_t ref_begin = uint32_t(P->refs.size());
-          for (int64_t r : dgrp.ranks) P->refs.push_back(uint32_t(P->dst_base[t] + r));
-          const uint32_t fanout = uint32_t(dgrp.ranks.size());
-          describe_piece(P, piece_idx, uint32_t(P->src_base[t] + best), ref_begin, fanout, box,
-                         sgrp.box, dgrp.box, nd, es);
+          P->pieces.push_back(Piece{t, best, it->second, int64_t(g), box, bytes});
+          const int64_t fanout = int64_t(dgrp.ranks.size());
           P->bytes_read += bytes;
           P->bytes_written += bytes * fanout;
           P->n_dst_writes += fanout;
@@ -433,12 +607,12 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
         ++idx[k];
       }
     }
+    emit_tensor(P, t, pc0, P->pieces.size());
   }
-  // tiles: each descriptor gets ceil(items / kTileItems) consecutive tiles
+  // tiles: each descriptor gets desc_tiles() consecutive tiles
   P->tile_begin.assign(1, 0);
   for (const reshard_descriptor_t& D : P->descs) {
-    const uint64_t items = uint64_t(D.extent[0]) * D.extent[1] * D.extent[2] * D.row_items;
-    P->n_tiles += (items + kTileItems - 1) / kTileItems;
+    P->n_tiles += desc_tiles(D);
     if (P->n_tiles >= (uint64_t(1) << 31)) {
       *err = "plan needs more than 2^31 tiles";
       return RESHARD_ERR_INVALID_ARGUMENT;

@@ -77,6 +77,21 @@ constexpr int64_t kChunkedMinRun = 128;
 // Longest row a descriptor holds (longer rows are split into column ranges).
 constexpr int64_t kMaxRunBytes = int64_t(1) << 30;
 
+// LDS window of a RESHARD_DESC_WINDOW tile, and the most segments one band may
+// have on each side.  A tensor's pieces go through windows when rows are at most
+// kWindowBytes wide, only the first and the last tensor dims are split, and some
+// piece has rows shorter than kWindowMaxRun bytes (narrow column runs).
+constexpr uint32_t kWindowBytes = 16384;
+constexpr uint32_t kWindowMaxSegs = 64;
+constexpr int64_t kWindowMaxRun = 128;
+
+// Tiles of one descriptor.
+inline uint64_t desc_tiles(const reshard_descriptor_t& D) {
+  if (D.mode == RESHARD_DESC_WINDOW) return (uint64_t(D.extent[0]) + D.extent[1] - 1) / D.extent[1];
+  const uint64_t items = uint64_t(D.extent[0]) * D.extent[1] * D.extent[2] * D.row_items;
+  return (items + kTileItems - 1) / kTileItems;
+}
+
 struct HostPlan {
   int n_tensors = 0;
   std::vector<Layout> src, dst;
@@ -87,6 +102,7 @@ struct HostPlan {
   std::vector<Piece> pieces;
   std::vector<reshard_descriptor_t> descs;
   std::vector<uint32_t> refs;       // fan-out: destination pointer slots (0-based in dst_ptrs)
+  std::vector<reshard_segment_t> segs;  // segments of RESHARD_DESC_WINDOW descriptors
   std::vector<uint64_t> desc_cost;  // bytes read + written by each descriptor
   std::vector<uint32_t> tile_begin; // first tile of each descriptor; n_desc + 1 entries
   uint64_t n_tiles = 0;

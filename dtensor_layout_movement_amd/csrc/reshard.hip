@@ -240,6 +240,250 @@ __device__ __forceinline__ void copy_chunks(const reshard_descriptor_t& D, const
   }
 }
 
+// ---------------------------------------------------------------- windows
+//
+// A RESHARD_DESC_WINDOW tile moves rows [r0, r0 + hr) of a band through an LDS
+// window (row r at r * pitch).  Phase 1 reads every source segment into the
+// window, phase 2 writes every destination segment from it to each replica.
+// Global accesses are 16-byte chunks aligned to the global address; the LDS side
+// takes whatever alignment that leaves.  A segment whose rows are packed in its
+// shard (row stride == width) is handled as one contiguous run, so narrow column
+// runs still move in 16-byte global accesses.
+
+typedef uint32_t u32x4_u1 __attribute__((ext_vector_type(4), aligned(1)));
+
+__device__ __forceinline__ u32x4 shift_left_bytes(u32x4 v, uint32_t s) {  // s in [0, 15]
+  if (s == 0) return v;
+  uint64_t lo = (uint64_t(v.y) << 32) | v.x, hi = (uint64_t(v.w) << 32) | v.z;
+  const uint32_t b = 8 * s;
+  if (b >= 64) {
+    hi = lo << (b - 64);
+    lo = 0;
+  } else {
+    hi = (hi << b) | (lo >> (64 - b));
+    lo <<= b;
+  }
+  return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
+}
+
+// Bytes [0, n) of v (n <= 16) into LDS at p, with at most four writes.
+__device__ __forceinline__ void lds_put(uint8_t* p, u32x4 v, uint32_t n) {
+  if (n == 16) {
+    *reinterpret_cast<u32x4_u1*>(p) = v;
+    return;
+  }
+  uint64_t lo = (uint64_t(v.y) << 32) | v.x;
+  const uint64_t hi = (uint64_t(v.w) << 32) | v.z;
+  if (n & 8) {
+    *reinterpret_cast<u64_u*>(p) = lo;
+    p += 8;
+    lo = hi;
+  }
+  if (n & 4) {
+    *reinterpret_cast<u32_u*>(p) = uint32_t(lo);
+    p += 4;
+    lo >>= 32;
+  }
+  if (n & 2) {
+    *reinterpret_cast<u16_u*>(p) = uint16_t(lo);
+    p += 2;
+    lo >>= 16;
+  }
+  if (n & 1) *p = uint8_t(lo);
+}
+
+// n <= 16 bytes from LDS at p into bytes [0, n) of the result.
+__device__ __forceinline__ u32x4 lds_get(const uint8_t* p, uint32_t n) {
+  if (n == 16) return *reinterpret_cast<const u32x4_u1*>(p);
+  uint64_t lo = 0, hi = 0;
+  uint32_t at = 0;  // bytes gathered so far
+  if (n & 8) {
+    lo = *reinterpret_cast<const u64_u*>(p);
+    at = 8;
+  }
+  if (n & 4) {
+    const uint64_t x = *reinterpret_cast<const u32_u*>(p + at);
+    if (at < 8) lo |= x << (8 * at); else hi |= x;
+    at += 4;
+  }
+  if (n & 2) {
+    const uint64_t x = *reinterpret_cast<const u16_u*>(p + at);
+    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
+    at += 2;
+  }
+  if (n & 1) {
+    const uint64_t x = p[at];
+    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
+  }
+  return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
+}
+
+// The len <= 16 bytes at global address lo of a run [base, base + n): bytes
+// [0, len) of the result.  Reads stay inside the run: one 16-byte load when the
+// run is at least 16 bytes long, else pieces of `unit` bytes.
+__device__ __forceinline__ u32x4 load_in_run(uintptr_t base, uint32_t n, uintptr_t lo, uint32_t len,
+                                             uint32_t unit) {
+  if (n >= 16) {
+    const uint32_t off = uint32_t(lo - base);
+    const uint32_t at = off < n - 16 ? off : n - 16;
+    u32x4 v = load_16_unaligned(base + at);
+    return off > at ? shift_right_bytes(v, off - at) : v;
+  }
+  uint64_t w[2] = {0, 0};
+  for (uint32_t b = 0; b < len; b += unit) {
+    uint64_t x;
+    if (unit >= 8) x = *as_global<const u64_u>(lo + b);
+    else if (unit == 4) x = *as_global<const u32_u>(lo + b);
+    else if (unit == 2) x = *as_global<const u16_u>(lo + b);
+    else x = *as_global<const uint8_t>(lo + b);
+    w[b / 8] |= x << (8 * (b % 8));
+  }
+  return u32x4{uint32_t(w[0]), uint32_t(w[0] >> 32), uint32_t(w[1]), uint32_t(w[1] >> 32)};
+}
+
+// Bytes [0, len) of v to global address d (len < 16: at most four stores).
+__device__ __forceinline__ void store_chunk(uintptr_t d, u32x4 v, uint32_t len) {
+  if (len == 16) *as_global<u32x4_u>(d) = v;
+  else store_head_bytes(d, v, len);
+}
+
+// Where chunk j of a segment's tile lies.  Packed segments: one run of hr*w
+// bytes at g.  Otherwise row r of the tile starts at g + r*stride and has
+// chunks_per_row chunk slots.
+struct SegChunk {
+  uintptr_t lo;      // first global byte (replica-0 address for destinations)
+  uint32_t len;      // bytes, 0 if the slot is empty
+  uint32_t run_off;  // packed: offset of lo in the run; else offset of lo in its row
+  uint32_t row;      // row of lo inside the tile
+  uintptr_t base;    // start of the run (packed) or of the row
+  uint32_t n;        // bytes of the run (packed) or of the row
+};
+
+__device__ __forceinline__ SegChunk seg_chunk(uintptr_t g, uint64_t stride, uint32_t w, uint32_t hr,
+                                              bool packed, uint32_t chunks_per_row, uint32_t j) {
+  SegChunk c;
+  if (packed) {
+    c.base = g;
+    c.n = hr * w;
+    c.row = 0;
+  } else {
+    c.row = j / chunks_per_row;
+    j -= c.row * chunks_per_row;
+    c.base = g + c.row * stride;
+    c.n = w;
+  }
+  const uintptr_t block = (c.base & ~uintptr_t(15)) + uintptr_t(j) * 16;
+  const uintptr_t lo = block > c.base ? block : c.base;
+  const uintptr_t end = c.base + c.n;
+  const uintptr_t hi = block + 16 < end ? block + 16 : end;
+  c.lo = lo;
+  c.len = hi > lo ? uint32_t(hi - lo) : 0u;
+  c.run_off = uint32_t(lo - c.base);
+  return c;
+}
+
+__device__ __forceinline__ uint32_t seg_chunks(uintptr_t g, uint32_t w, uint32_t hr, bool packed,
+                                               uint32_t* chunks_per_row) {
+  *chunks_per_row = (w + 30) / 16;
+  if (packed) return uint32_t(((g & 15) + uint64_t(hr) * w + 15) / 16);
+  return hr * *chunks_per_row;
+}
+
+// LDS address of byte `off` of a packed run (rows of w bytes, window column col).
+__device__ __forceinline__ uint8_t* run_lds(uint8_t* lds, uint32_t pitch, uint32_t col, uint32_t w,
+                                           uint32_t off) {
+  const uint32_t r = off / w;
+  return lds + r * pitch + col + (off - r * w);
+}
+
+constexpr int kWindowBatch = 4;  // chunks per thread with loads in flight together
+
+template <class Sh>
+__device__ void window_tile(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
+                            const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile,
+                            uint8_t* lds) {
+  const uint32_t rows = D.extent[0], per_tile = D.extent[1], pitch = D.row_items;
+  const uint32_t r0 = tile * per_tile;
+  const uint32_t hr = min(per_tile, rows - r0);
+  const uint32_t unit = D.unit;
+  const reshard_segment_t* src_segs = segs + D.src_ptr;
+  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+
+  // phase 1: source segments -> window
+  for (uint32_t s = 0; s < D.dst_ref_begin; ++s) {
+    const reshard_segment_t S = src_segs[s];
+    const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+    const bool packed = uint64_t(S.row_stride) == S.width;
+    uint32_t cpr;
+    const uint32_t n = seg_chunks(g, S.width, hr, packed, &cpr);
+    for (uint32_t base = 0; base < n; base += kBlock * kWindowBatch) {
+      u32x4 v[kWindowBatch];
+      SegChunk c[kWindowBatch];
+#pragma unroll
+      for (int k = 0; k < kWindowBatch; ++k) {
+        const uint32_t j = base + uint32_t(k * kBlock) + threadIdx.x;
+        c[k] = seg_chunk(g, uint64_t(S.row_stride), S.width, hr, packed, cpr, j < n ? j : 0);
+        if (j >= n) c[k].len = 0;
+        if (c[k].len) v[k] = load_in_run(c[k].base, c[k].n, c[k].lo, c[k].len, unit);
+      }
+#pragma unroll
+      for (int k = 0; k < kWindowBatch; ++k) {
+        if (!c[k].len) continue;
+        if (!packed) {
+          lds_put(lds + c[k].row * pitch + S.col + c[k].run_off, v[k], c[k].len);
+          continue;
+        }
+        // a packed chunk may cover several window rows
+        uint32_t off = c[k].run_off, left = c[k].len;
+        u32x4 x = v[k];
+        while (left) {
+          const uint32_t in_row = S.width - off % S.width;
+          const uint32_t take = left < in_row ? left : in_row;
+          lds_put(run_lds(lds, pitch, S.col, S.width, off), x, take);
+          left -= take;
+          off += take;
+          if (left) x = shift_right_bytes(x, take);
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  // phase 2: window -> destination segments, every replica
+  for (uint32_t s = 0; s < D.fanout; ++s) {
+    const reshard_segment_t S = dst_segs[s];
+    const uint64_t row_off = uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+    const uintptr_t g = sh.ptr(refs[S.ptr]) + row_off;
+    const bool packed = uint64_t(S.row_stride) == S.width;
+    uint32_t cpr;
+    const uint32_t n = seg_chunks(g, S.width, hr, packed, &cpr);
+    for (uint32_t j = threadIdx.x; j < n; j += kBlock) {
+      const SegChunk c = seg_chunk(g, uint64_t(S.row_stride), S.width, hr, packed, cpr, j);
+      if (!c.len) continue;
+      u32x4 v;
+      if (!packed) {
+        v = lds_get(lds + c.row * pitch + S.col + c.run_off, c.len);
+      } else {
+        uint32_t off = c.run_off, got = 0;
+        v = u32x4{0, 0, 0, 0};
+        while (got < c.len) {
+          const uint32_t in_row = S.width - off % S.width;
+          const uint32_t take = c.len - got < in_row ? c.len - got : in_row;
+          const u32x4 part = lds_get(run_lds(lds, pitch, S.col, S.width, off), take);
+          const u32x4 sh_part = shift_left_bytes(part, got);
+          v = u32x4{v.x | sh_part.x, v.y | sh_part.y, v.z | sh_part.z, v.w | sh_part.w};
+          got += take;
+          off += take;
+        }
+      }
+      for (uint32_t r = 0; r < S.fanout; ++r) {
+        const uintptr_t d = sh.ptr(refs[S.ptr + r]) + row_off + (c.lo - g);
+        store_chunk(d, v, c.len);
+      }
+    }
+  }
+}
+
 // Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
 // aligned to the descriptor's unit, or replicas differ in 16-byte phase.
 template <class Sh>
@@ -273,8 +517,9 @@ template <bool kKarg>
 __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     const reshard_descriptor_t* __restrict__ descs, uint32_t n_desc,
     const uint32_t* __restrict__ tile_begin, const uint32_t* __restrict__ refs,
-    const void* const* __restrict__ table, KargPtrs karg, uint32_t n_tiles, uint32_t per_xcd,
-    uint32_t flags) {
+    const reshard_segment_t* __restrict__ segs, const void* const* __restrict__ table, KargPtrs karg,
+    uint32_t n_tiles, uint32_t per_xcd, uint32_t flags) {
+  __shared__ __attribute__((aligned(16))) uint8_t window[rs::kWindowBytes];
   // Block b runs on XCD b % kXcds.  Each XCD takes groups of kXcdGroup
   // consecutive tiles, the XCDs side by side: nearby tiles share an XCD's L2
   // while all XCDs stream through the same region of memory.
@@ -290,6 +535,11 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   uint32_t unit_mode;  // the two 16-bit fields as one scalar word
   __builtin_memcpy(&unit_mode, &D.unit, sizeof(unit_mode));
   const uint32_t unit = unit_mode & 0xffffu, mode = unit_mode >> 16;
+  if (mode == RESHARD_DESC_WINDOW) {  // any alignment: global chunks follow the addresses
+    const Shards<kKarg> wsh{table, &karg, refs};
+    window_tile(D, segs, refs, wsh, t - tile_begin[lo], window);
+    return;
+  }
   const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;
   const uint32_t first = (t - tile_begin[lo]) * rs::kTileItems;
   const uint32_t last = min(first + rs::kTileItems, items);
@@ -340,6 +590,7 @@ struct reshard_plan_s {
   const reshard_descriptor_t* d_descs = nullptr;
   const uint32_t* d_refs = nullptr;
   const uint32_t* d_tile_begin = nullptr;
+  const reshard_segment_t* d_segs = nullptr;
   // pointer-table slots, used when the pointers do not fit in kernel arguments
   int64_t n_ptrs = 0;
   void* d_slots = nullptr;
@@ -370,12 +621,16 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   const size_t desc_bytes = H.descs.size() * sizeof(reshard_descriptor_t);
   const size_t refs_off = align_up(desc_bytes, 256);
   const size_t tiles_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);
-  const size_t total = tiles_off + H.tile_begin.size() * sizeof(uint32_t);
+  const size_t segs_off = align_up(tiles_off + H.tile_begin.size() * sizeof(uint32_t), 256);
+  const size_t total = segs_off + H.segs.size() * sizeof(reshard_segment_t);
   std::vector<uint8_t> img(total, 0);
   if (desc_bytes) std::memcpy(img.data(), H.descs.data(), desc_bytes);
   uint32_t* r = reinterpret_cast<uint32_t*>(img.data() + refs_off);
   for (size_t i = 0; i < H.refs.size(); ++i) r[i] = uint32_t(H.n_src_ptrs) + H.refs[i];
   std::memcpy(img.data() + tiles_off, H.tile_begin.data(), H.tile_begin.size() * sizeof(uint32_t));
+  // window segments: source pointer indices become absolute pointer slots
+  reshard_segment_t* sg = reinterpret_cast<reshard_segment_t*>(img.data() + segs_off);
+  for (size_t i = 0; i < H.segs.size(); ++i) sg[i] = H.segs[i];
 
   void* table = nullptr;
   e = hipMalloc(&table, total);
@@ -409,6 +664,7 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   p->d_descs = reinterpret_cast<const reshard_descriptor_t*>(table);
   p->d_refs = reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + refs_off);
   p->d_tile_begin = reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + tiles_off);
+  p->d_segs = reinterpret_cast<const reshard_segment_t*>(static_cast<uint8_t*>(table) + segs_off);
   p->per_xcd = per_xcd;
   p->n_wg = per_xcd * kXcds;
   p->device = dev;
@@ -576,11 +832,11 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
   if (table)
     hipLaunchKernelGGL(reshard_copy_kernel<false>, dim3(plan->n_wg), dim3(kBlock), 0, stream,
                        plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin, plan->d_refs,
-                       table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
+                       plan->d_segs, table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
   else
     hipLaunchKernelGGL(reshard_copy_kernel<true>, dim3(plan->n_wg), dim3(kBlock), 0, stream,
                        plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin, plan->d_refs,
-                       table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
+                       plan->d_segs, table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "reshard_copy_kernel launch");
   if (slot >= 0) {
@@ -604,7 +860,8 @@ reshard_status_t reshard_plan_stats(reshard_plan_t plan, reshard_plan_stats_t* o
   out->bytes_read = H.bytes_read;
   out->bytes_written = H.bytes_written;
   out->n_descriptors = int64_t(H.descs.size());
-  out->table_bytes = int64_t(H.descs.size() * sizeof(reshard_descriptor_t) + H.refs.size() * 4);
+  out->table_bytes = int64_t(H.descs.size() * sizeof(reshard_descriptor_t) + H.refs.size() * 4 +
+                             H.tile_begin.size() * 4 + H.segs.size() * sizeof(reshard_segment_t));
   out->n_workgroups = plan->n_wg;
   out->plan_host_us = H.plan_host_us;
   return RESHARD_OK;
@@ -658,6 +915,16 @@ reshard_status_t reshard_plan_descriptors(reshard_plan_t plan, int64_t capacity,
   *n_refs = int64_t(H.refs.size());
   for (int64_t i = 0; i < std::min<int64_t>(capacity, *n_desc); ++i) out[i] = H.descs[i];
   for (int64_t i = 0; i < std::min<int64_t>(ref_capacity, *n_refs); ++i) refs[i] = H.refs[i];
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_plan_segments(reshard_plan_t plan, int64_t capacity, reshard_segment_t* out,
+                                       int64_t* n_total) {
+  if (!plan || !n_total || capacity < 0 || (capacity > 0 && !out))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "bad argument");
+  const rs::HostPlan& H = plan->host;
+  *n_total = int64_t(H.segs.size());
+  for (int64_t i = 0; i < std::min<int64_t>(capacity, *n_total); ++i) out[i] = H.segs[i];
   return RESHARD_OK;
 }
 

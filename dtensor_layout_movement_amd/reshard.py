@@ -37,13 +37,15 @@ DTYPE_F64, DTYPE_I64 = 10, 11
 
 DESC_ITEMS = 0       # rows of items of `unit` bytes
 DESC_DST_CHUNKS = 1  # rows cut into destination-aligned 16-byte chunks
+DESC_WINDOW = 2      # a band of rows staged through an LDS window
 
 EXPORTED = (
     "reshard_dtype_size", "reshard_layout_create", "reshard_layout_destroy",
     "reshard_layout_num_ranks", "reshard_layout_shard_box", "reshard_plan_create",
     "reshard_plan_create_batched", "reshard_plan_upload", "reshard_execute",
     "reshard_plan_stats", "reshard_plan_pieces", "reshard_plan_piece_fanout",
-    "reshard_plan_descriptors", "reshard_plan_destroy", "reshard_last_error",
+    "reshard_plan_descriptors", "reshard_plan_segments", "reshard_plan_destroy",
+    "reshard_last_error",
 )
 
 
@@ -78,6 +80,14 @@ class Descriptor(ctypes.Structure):
 
 
 assert ctypes.sizeof(Descriptor) == 128
+
+
+class Segment(ctypes.Structure):
+    _fields_ = [("offset", ctypes.c_int64), ("row_stride", ctypes.c_int64), ("col", ctypes.c_uint32),
+                ("width", ctypes.c_uint32), ("ptr", ctypes.c_uint32), ("fanout", ctypes.c_uint32)]
+
+
+assert ctypes.sizeof(Segment) == 32
 
 _lib = None
 _VP = ctypes.c_void_p
@@ -116,6 +126,7 @@ def _load() -> ctypes.CDLL:
         "reshard_plan_piece_fanout": (st, [_VP, _I64, _I64, _I64P, _I64P]),
         "reshard_plan_descriptors": (st, [_VP, _I64, ctypes.POINTER(Descriptor), _I64P, _I64,
                                           ctypes.POINTER(ctypes.c_uint32), _I64P]),
+        "reshard_plan_segments": (st, [_VP, _I64, ctypes.POINTER(Segment), _I64P]),
         "reshard_plan_destroy": (None, [_VP]),
         "reshard_last_error": (ctypes.c_char_p, []),
     }
@@ -261,6 +272,16 @@ def reshard_plan_descriptors(plan: int):
             "magic": [list(m) for m in d.magic], "piece": d.piece,
         })
     return out, list(refs[:nr.value])
+
+
+def reshard_plan_segments(plan: int) -> list[dict]:
+    """Segments of the plan's window descriptors (see reshard_segment_t)."""
+    n = ctypes.c_int64()
+    _check(_load().reshard_plan_segments(plan, 0, None, ctypes.byref(n)))
+    arr = (Segment * max(1, n.value))()
+    _check(_load().reshard_plan_segments(plan, n.value, arr, ctypes.byref(n)))
+    return [{"offset": x.offset, "row_stride": x.row_stride, "col": x.col, "width": x.width,
+             "ptr": x.ptr, "fanout": x.fanout} for x in arr[:n.value]]
 
 
 def reshard_plan_destroy(plan: int) -> None:

@@ -118,12 +118,22 @@ def stage_of_layer(layer: int, layers: int = 32, stages: int = 4) -> int:
     return layer * stages // layers
 
 
+def narrow_columns(rows: int = 1 << 22) -> Workload:
+    """The worked example's layouts on a tall matrix: 8 bf16 columns, rows split
+    over two sources, columns over four destinations, so every destination row is
+    a 2-element (4-byte) slice of a 16-byte source row."""
+    t = TensorSpec("narrow", (rows, 8), torch.bfloat16, (2,), (0,), (4,), (1,))
+    return Workload(f"narrow_columns_{rows}x8", (t,), "normal",
+                    f"{rows}x8 bf16 N(0,0.02), (2,)[S0] -> (4,)[S1]: 2-element column slices")
+
+
 WORKLOADS = {
     "worked_example_8x8": worked_example_8x8,
     "ffn_up_14336x4096": ffn_up,
     "moe_experts_64x2048x7168": moe_experts,
     "uneven_5000x3001": uneven,
     "ffn_refit_32_layers": ffn_refit,
+    "narrow_columns_4194304x8": narrow_columns,
 }
 
 

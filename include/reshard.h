@@ -107,6 +107,7 @@ typedef struct reshard_piece {
 /* Descriptor modes. */
 #define RESHARD_DESC_ITEMS 0      /* rows of items of `unit` bytes (unit = 16, or short rows) */
 #define RESHARD_DESC_DST_CHUNKS 1 /* rows cut into 16-byte chunks aligned to the destination */
+#define RESHARD_DESC_WINDOW 2     /* a band of rows staged through LDS (see below) */
 
 /*
  * Device copy descriptor (the table the kernel reads; inspection API).
@@ -121,6 +122,14 @@ typedef struct reshard_piece {
  *                            aligned destination block the row touches (empty,
  *                            partial or full); row_items = ceil((run_bytes+15)/16);
  *                            `unit` is the row's natural alignment (1..8 bytes).
+ *   RESHARD_DESC_WINDOW      a band of `extent[0]` rows of a 2-d view of one
+ *                            tensor (rows x inner dim), `run_bytes` wide, moved
+ *                            `extent[1]` rows per tile through an LDS window of
+ *                            pitch `row_items`.  Its segments are
+ *                            segments[src_ptr .. src_ptr + dst_ref_begin) (sources,
+ *                            read into the window) followed by `fanout` destination
+ *                            segments (written from it); offsets and strides are
+ *                            ignored.  Used for narrow or misaligned pieces.
  */
 typedef struct reshard_descriptor {
   int64_t src_offset;       /* byte offset of the row origin in the source shard */
@@ -138,6 +147,22 @@ typedef struct reshard_descriptor {
   uint32_t magic[3][2];     /* division constants for row_items, extent[2], extent[1] */
   uint32_t piece;           /* index of the planned piece it copies (or part of) */
 } reshard_descriptor_t;
+
+/*
+ * One segment of a RESHARD_DESC_WINDOW band (inspection API): rows of `width`
+ * bytes at window column `col`; row r of the band is at byte
+ * offset + r * row_stride of its shard.  A source segment (fanout 0) reads shard
+ * `ptr` of the source pointer array; a destination segment writes the `fanout`
+ * destination shards listed in the fan-out list from entry `ptr`.
+ */
+typedef struct reshard_segment {
+  int64_t offset;      /* byte offset of the band's first row in the shard */
+  int64_t row_stride;  /* bytes between consecutive rows in the shard */
+  uint32_t col;        /* first byte column inside the window */
+  uint32_t width;      /* bytes per row */
+  uint32_t ptr;        /* source pointer index, or first fan-out entry */
+  uint32_t fanout;     /* 0 for a source segment, else destination replicas */
+} reshard_segment_t;
 
 /* Bytes per element of `dtype`, or 0 if unknown. */
 int64_t reshard_dtype_size(int dtype);
@@ -232,6 +257,10 @@ reshard_status_t reshard_plan_descriptors(reshard_plan_t plan, int64_t capacity,
                                           reshard_descriptor_t* out, int64_t* n_desc,
                                           int64_t ref_capacity, uint32_t* refs,
                                           int64_t* n_refs);
+
+/* Inspection: copy up to `capacity` window segments; the total goes to *n_total. */
+reshard_status_t reshard_plan_segments(reshard_plan_t plan, int64_t capacity,
+                                       reshard_segment_t* out, int64_t* n_total);
 
 /* Free the plan and its device memory.  No execute using it may be in flight.  NULL is a no-op. */
 void reshard_plan_destroy(reshard_plan_t plan);

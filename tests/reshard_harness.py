@@ -141,7 +141,11 @@ def run_descriptors(plan: Plan, srcs_flat, dsts_flat):
     reshard_execute.  For DST_CHUNKS descriptors it also checks that the chunks
     of every row tile the row exactly."""
     descs, refs = R.reshard_plan_descriptors(plan.handle)
+    segs = R.reshard_plan_segments(plan.handle)
     for D in descs:
+        if D["mode"] == R.DESC_WINDOW:
+            _run_window(D, segs, refs, srcs_flat, dsts_flat)
+            continue
         e0, e1, e2 = D["extent"]
         i0, i1, i2 = np.meshgrid(np.arange(e0), np.arange(e1), np.arange(e2), indexing="ij")
         so = (D["src_offset"] + i0 * D["src_stride"][0] + i1 * D["src_stride"][1]
@@ -169,6 +173,30 @@ def run_descriptors(plan: Plan, srcs_flat, dsts_flat):
             dsts_flat[refs[D["dst_ref_begin"] + r]][dst_idx] = data
 
 
+def _run_window(D, segs, refs, srcs_flat, dsts_flat):
+    """A window band row by row: sources into a window row, window row out to
+    every destination replica.  Also checks that the sources and the
+    destinations each tile the window row exactly."""
+    rows, width = D["extent"][0], D["run_bytes"]
+    window = np.zeros((rows, width), dtype=np.uint8)
+    srcs = segs[D["src_ptr"]:D["src_ptr"] + D["dst_ref_begin"]]
+    dsts = segs[D["src_ptr"] + D["dst_ref_begin"]:D["src_ptr"] + D["dst_ref_begin"] + D["fanout"]]
+    for side in (srcs, dsts):
+        cover = np.zeros(width, dtype=np.int32)
+        for sg in side:
+            cover[sg["col"]:sg["col"] + sg["width"]] += 1
+        assert (cover == 1).all()
+    r = np.arange(rows, dtype=np.int64)[:, None]
+    for sg in srcs:
+        assert sg["fanout"] == 0
+        idx = sg["offset"] + r * sg["row_stride"] + np.arange(sg["width"])[None, :]
+        window[:, sg["col"]:sg["col"] + sg["width"]] = srcs_flat[sg["ptr"]][idx]
+    for sg in dsts:
+        idx = sg["offset"] + r * sg["row_stride"] + np.arange(sg["width"])[None, :]
+        for k in range(sg["fanout"]):
+            dsts_flat[refs[sg["ptr"] + k]][idx] = window[:, sg["col"]:sg["col"] + sg["width"]]
+
+
 def shard_bytes(plan: Plan):
     """Bytes of every shard, in the src / dst pointer-array order of execute."""
     sb, db = [], []
@@ -184,8 +212,23 @@ def assert_descriptors_in_bounds(plan: Plan):
     any launch)."""
     sb, db = shard_bytes(plan)
     descs, refs = R.reshard_plan_descriptors(plan.handle)
+    segs = R.reshard_plan_segments(plan.handle)
     for D in descs:
         ext = D["extent"]
+        if D["mode"] == R.DESC_WINDOW:
+            rows, per_tile, pitch, width = ext[0], ext[1], D["row_items"], D["run_bytes"]
+            assert rows >= 1 and per_tile >= 1 and pitch % 16 == 0 and pitch >= width
+            assert per_tile * pitch <= 16384
+            first = D["src_ptr"]
+            for i, sg in enumerate(segs[first:first + D["dst_ref_begin"] + D["fanout"]]):
+                assert sg["col"] + sg["width"] <= width and sg["offset"] >= 0 and sg["row_stride"] >= 0
+                last = sg["offset"] + (rows - 1) * sg["row_stride"] + sg["width"]
+                if i < D["dst_ref_begin"]:
+                    assert last <= sb[sg["ptr"]], sg
+                else:
+                    for k in range(sg["fanout"]):
+                        assert last <= db[refs[sg["ptr"] + k]], sg
+            continue
         assert D["run_bytes"] >= 1 and D["row_items"] >= 1 and all(e >= 1 for e in ext)
         assert ext[0] * ext[1] * ext[2] * D["row_items"] < 2 ** 31
         span = D["run_bytes"]

@@ -46,7 +46,8 @@ def test_worked_example_golden():
             assert np.array_equal(got, gold[("dst", c)])
 
 
-SMALL_FULL = ["worked_example_8x8", "ffn_up_14336x4096", "moe_experts_64x2048x7168", "uneven_5000x3001"]
+SMALL_FULL = ["worked_example_8x8", "ffn_up_14336x4096", "moe_experts_64x2048x7168", "uneven_5000x3001",
+              "narrow_columns_4194304x8"]
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])

@@ -51,6 +51,11 @@ def small_specs():
         T("chunked_bf16", (37, 301), torch.bfloat16, (3,), (1,), (2, 2), (RR, 0)),
         T("chunked_u8", (9, 1000), torch.uint8, (3,), (1,), (2,), (0,)),
         T("chunked_f64", (11, 45), torch.float64, (2,), (1,), (3,), (0,)),
+        T("narrow_scatter", (4099, 8), torch.bfloat16, (2,), (0,), (4,), (1,)),
+        T("narrow_gather", (4099, 8), torch.bfloat16, (4,), (1,), (2,), (0,)),
+        T("narrow_fp8_3d", (6, 7, 24), torch.uint8, (2, 3), (0, 2), (4,), (2,)),
+        T("narrow_rep", (301, 12), torch.float32, (3,), (1,), (2, 3), (RR, 1)),
+        T("wide_window", (37, 4001), torch.bfloat16, (3,), (1,), (5,), (0,)),
     ]
     return specs
 
@@ -199,7 +204,7 @@ def test_worked_example_plan():
 
 def test_piece_counts_of_workloads():
     counts = {"worked_example_8x8": 8, "ffn_up_14336x4096": 8, "moe_experts_64x2048x7168": 128,
-              "uneven_5000x3001": 42, "ffn_refit_32_layers": 384}
+              "uneven_5000x3001": 42, "ffn_refit_32_layers": 384, "narrow_columns_4194304x8": 8}
     for wl in full_workload_plans():
         with Plan(wl.tensors) as plan:
             assert plan.stats()["n_pieces"] == counts[wl.name]
@@ -263,6 +268,8 @@ def test_magic_constants_exact():
         descs, _ = R.reshard_plan_descriptors(plan.handle)
     divisors = {}
     for d in descs:
+        if d["mode"] == R.DESC_WINDOW:  # windows divide nothing
+            continue
         divisors[d["row_items"]] = tuple(d["magic"][0])
         divisors[d["extent"][2]] = tuple(d["magic"][1])
         divisors[d["extent"][1]] = tuple(d["magic"][2])
@@ -281,7 +288,24 @@ def test_descriptor_modes():
             return {(d["mode"], d["unit"]) for d in R.reshard_plan_descriptors(plan.handle)[0]}
     assert modes(W.ffn_up()) == {(R.DESC_ITEMS, 16)}
     assert modes(W.uneven()) == {(R.DESC_DST_CHUNKS, 4)}       # 12004-byte destination rows
-    assert modes(W.worked_example_8x8()) == {(R.DESC_ITEMS, 4)}  # 4-byte rows
+    assert {m for m, _ in modes(W.worked_example_8x8())} == {R.DESC_WINDOW}  # 4-byte rows
+
+
+def test_window_segments_worked_example():
+    """The pages' example as one window band per source shard: one source segment
+    (the whole 16-byte rows, merged across the four pieces) and four destination
+    segments of 4-byte rows."""
+    with Plan(W.worked_example_8x8().tensors) as plan:
+        descs, _ = R.reshard_plan_descriptors(plan.handle)
+        segs = R.reshard_plan_segments(plan.handle)
+        assert [d["mode"] for d in descs] == [R.DESC_WINDOW, R.DESC_WINDOW]
+        for d in descs:
+            assert d["extent"][0] == 4 and d["run_bytes"] == 16
+            assert d["dst_ref_begin"] == 1 and d["fanout"] == 4
+            src = segs[d["src_ptr"]]
+            assert src["width"] == 16 and src["row_stride"] == 16
+            dsts = segs[d["src_ptr"] + 1:d["src_ptr"] + 5]
+            assert [x["col"] for x in dsts] == [0, 4, 8, 12] and all(x["width"] == 4 for x in dsts)
 
 
 def test_outer_dims_beyond_three_are_peeled():
