@@ -10,6 +10,11 @@ Inputs are resident in HBM before timing starts.  To keep every step cold in
 the 256 MB Infinity Cache, steps rotate over several independent sets of
 source and destination buffers whose total size is at least 2 GB.
 
+After the timed region (and outside it) the same inputs are also moved by the
+pages' baseline scheme, gather-then-slice, built from two plans of the same
+library (sources -> one global buffer -> destinations); its step time and the
+reshard's speed-up over it are reported as ``gather_then_slice_gpu``.
+
 Prints one JSON line.  ``value`` = algorithmic bytes (global bytes read once +
 every destination shard written once) per second over the timed steps;
 ``roofline.achieved`` = the same bytes over the kernel's mean launch duration:
@@ -120,6 +125,47 @@ def alloc_set(torch, R, wl, lay_src, lay_dst, dev, seed):
     return src_bufs, dst_bufs, sp, dp
 
 
+def gather_then_slice(torch, R, wl, lay_src, lay_dst, sets, stream, steps: int, reshard_ms: float) -> dict:
+    """The pages' baseline scheme on the same GPU, built from two plans of the same
+    library: every source shard into one global buffer (gather), then every
+    destination shard out of it (slice).  It moves twice the reshard's bytes."""
+    g_lay, plans_g, plans_s = [], None, None
+    for t, spec in enumerate(wl.tensors):
+        g_lay.append(R.reshard_layout_create(spec.shape, R.dtype_code(spec.dtype), (1,), (R.REPLICATE,)))
+    plans_g = R.reshard_plan_create_batched(lay_src, g_lay)
+    plans_s = R.reshard_plan_create_batched(g_lay, lay_dst)
+    R.reshard_plan_upload(plans_g, stream.cuda_stream)
+    R.reshard_plan_upload(plans_s, stream.cuda_stream)
+    n_sets = len(sets)
+    globals_ = [[torch.empty(spec.shape, dtype=spec.dtype, device="cuda") for spec in wl.tensors]
+                for _ in range(n_sets)]
+    gp = [R.pointer_array([g.data_ptr() for g in gl]) for gl in globals_]
+    for i in range(3):
+        _, _, sp, dp = sets[i % n_sets]
+        R.reshard_execute(plans_g, sp, gp[i % n_sets], stream.cuda_stream)
+        R.reshard_execute(plans_s, gp[i % n_sets], dp, stream.cuda_stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for i in range(steps):
+        _, _, sp, dp = sets[i % n_sets]
+        R.reshard_execute(plans_g, sp, gp[i % n_sets], stream.cuda_stream)
+        R.reshard_execute(plans_s, gp[i % n_sets], dp, stream.cuda_stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    st_g, st_s = R.reshard_plan_stats(plans_g), R.reshard_plan_stats(plans_s)
+    traffic = st_g["bytes_read"] + st_g["bytes_written"] + st_s["bytes_read"] + st_s["bytes_written"]
+    R.reshard_plan_destroy(plans_g)
+    R.reshard_plan_destroy(plans_s)
+    for h in g_lay:
+        R.reshard_layout_destroy(h)
+    del globals_
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(ms, 5), "bytes_moved": traffic, "steps": steps,
+            "reshard_speedup": round(ms / reshard_ms, 3)}
+
+
 def cpu_baseline(wl, budget_s: float) -> dict:
     """The oracle (gather-then-slice) timed on this host's cores on the same workload."""
     import torch
@@ -172,6 +218,8 @@ def main() -> int:
     ap.add_argument("--min-footprint-gb", type=float, default=2.0)
     ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-comparator", action="store_true",
+                    help="skip the gather-then-slice comparator run on the GPU")
     ap.add_argument("--plan-reps", type=int, default=200)
     args = ap.parse_args()
 
@@ -239,6 +287,10 @@ def main() -> int:
     copy_gbps = 2 * half / (c0.elapsed_time(c1) / 20 * 1e-3) / 1e9
     del a, b
 
+    comparator = None
+    if not args.no_comparator:
+        comparator = gather_then_slice(torch, R, wl, lay_src, lay_dst, sets, stream,
+                                       max(5, K // 4), ms_per_step)
     plan_us = plan_timing(R, wl, args.plan_reps if algo_bytes < 2e10 else max(5, args.plan_reps // 20))
     traffic = traffic_from_profile(wl.name)
     spec0 = wl.tensors[0]
@@ -281,6 +333,7 @@ def main() -> int:
             "kernel_mean_us": round(kernel_ms * 1e3, 3),
         },
         "copy_reference_gbps": round(copy_gbps, 1),
+        "gather_then_slice_gpu": comparator,
         "wall_s": round(wall, 4),
     }
     if not args.no_cpu_baseline:

@@ -178,3 +178,31 @@ def test_upload_and_stats_after_execute():
         per_xcd = -(-(-(-tiles // 8)) // 64) * 64  # whole groups of 64 tiles per XCD
         assert st["n_workgroups"] == 8 * per_xcd
         R.reshard_plan_upload(plan.handle, None)  # second upload is a no-op
+
+
+def test_gather_then_slice_two_plans_match_oracle():
+    """The comparator the benchmark times (sources -> one global buffer ->
+    destinations, two plans of the same library) produces the oracle's bytes."""
+    from reshard_harness import oracle_dsts
+    for spec in (W.uneven(301, 257).tensors[0], W.ffn_up(448, 320).tensors[0]):
+        code = R.dtype_code(spec.dtype)
+        with Plan([spec]) as plan:
+            g_lay = R.reshard_layout_create(spec.shape, code, (1,), (R.REPLICATE,))
+            p_g = R.reshard_plan_create(plan.src_layouts[0], g_lay)
+            p_s = R.reshard_plan_create(g_lay, plan.dst_layouts[0])
+            g = W.make_global(spec, "raw", 12)
+            srcs = W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
+            want = oracle_dsts(spec, srcs)
+            src_d = [s.cuda() for s in srcs]
+            glob = torch.empty(spec.shape, dtype=spec.dtype, device="cuda")
+            dst_d = [torch.empty_like(w, device="cuda") for w in want]
+            stream = torch.cuda.current_stream().cuda_stream
+            R.reshard_execute(p_g, [t.data_ptr() for t in src_d], [glob.data_ptr()], stream)
+            R.reshard_execute(p_s, [glob.data_ptr()], [t.data_ptr() for t in dst_d], stream)
+            torch.cuda.synchronize()
+            assert torch.equal(glob.cpu().view(torch.uint8), g.view(torch.uint8))
+            for got, w in zip(dst_d, want):
+                assert torch.equal(got.cpu().view(torch.uint8), w.view(torch.uint8))
+            R.reshard_plan_destroy(p_g)
+            R.reshard_plan_destroy(p_s)
+            R.reshard_layout_destroy(g_lay)
