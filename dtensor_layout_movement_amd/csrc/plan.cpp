@@ -35,31 +35,43 @@ int64_t elem_size_of(int dtype) {
   }
 }
 
-std::vector<int64_t> box_key(int ndim, const Box& b) {
-  std::vector<int64_t> k(2 * ndim);
-  for (int d = 0; d < ndim; ++d) {
-    k[2 * d] = b.lo[d];
-    k[2 * d + 1] = b.hi[d];
-  }
-  return k;
+bool same_box(int ndim, const Box& a, const Box& b) {
+  for (int k = 0; k < ndim; ++k)
+    if (a.lo[k] != b.lo[k] || a.hi[k] != b.hi[k]) return false;
+  return true;
 }
 
 // Groups the non-empty boxes of one tensor's layout by equality.  Groups come
-// out ordered by their lowest rank.
+// out ordered by their lowest rank.  Ranks that share a box differ only in the
+// coordinates of Replicate mesh dims (and of mesh dims whose chunks are empty),
+// so a rank is compared with the groups already formed, most recent first.
 void group_ranks(const Layout& L, int64_t tensor, std::vector<Group>* groups) {
-  std::map<std::vector<int64_t>, size_t> seen;
+  const size_t first = groups->size();
+  std::map<std::vector<int64_t>, size_t> index;  // used only for big meshes
+  const bool use_index = L.nranks > 256;
   for (int64_t r = 0; r < L.nranks; ++r) {
     Box b;
     shard_box(L, r, &b);
     if (box_empty(L.ndim, b)) continue;
-    auto key = box_key(L.ndim, b);
-    auto it = seen.find(key);
-    if (it == seen.end()) {
-      seen.emplace(std::move(key), groups->size());
-      groups->push_back(Group{tensor, b, {r}});
+    size_t found = SIZE_MAX;
+    if (use_index) {
+      std::vector<int64_t> key(2 * L.ndim);
+      for (int k = 0; k < L.ndim; ++k) {
+        key[2 * k] = b.lo[k];
+        key[2 * k + 1] = b.hi[k];
+      }
+      auto it = index.find(key);
+      if (it != index.end()) found = it->second;
+      else index.emplace(std::move(key), groups->size());
     } else {
-      (*groups)[it->second].ranks.push_back(r);
+      for (size_t g = groups->size(); g-- > first;)
+        if (same_box(L.ndim, (*groups)[g].box, b)) {
+          found = g;
+          break;
+        }
     }
+    if (found == SIZE_MAX) groups->push_back(Group{tensor, b, {r}});
+    else (*groups)[found].ranks.push_back(r);
   }
 }
 
@@ -71,7 +83,13 @@ struct SourceGrid {
   int ndim = 0;
   std::vector<std::vector<std::pair<int64_t, int64_t>>> iv;  // per dim, sorted by lo
   std::vector<int64_t> cell_stride;
-  std::unordered_map<int64_t, int64_t> cell_to_group;
+  std::vector<int64_t> dense;                      // cell -> group, when the grid is small
+  std::unordered_map<int64_t, int64_t> sparse;     // cell -> group otherwise
+  int64_t group_of(int64_t cell) const {
+    if (!dense.empty()) return dense[size_t(cell)];
+    auto it = sparse.find(cell);
+    return it == sparse.end() ? -1 : it->second;
+  }
 };
 
 int64_t interval_index(const std::vector<std::pair<int64_t, int64_t>>& v, int64_t lo) {
@@ -91,10 +109,13 @@ SourceGrid make_grid(int ndim, const std::vector<Group>& groups, size_t g_begin,
   }
   G.cell_stride.assign(ndim, 1);
   for (int d = ndim - 2; d >= 0; --d) G.cell_stride[d] = G.cell_stride[d + 1] * int64_t(G.iv[d + 1].size());
+  const int64_t cells = G.cell_stride[0] * int64_t(G.iv[0].size());
+  if (cells <= (int64_t(1) << 20)) G.dense.assign(size_t(cells), -1);
   for (size_t g = g_begin; g < g_end; ++g) {
     int64_t cell = 0;
     for (int d = 0; d < ndim; ++d) cell += interval_index(G.iv[d], groups[g].box.lo[d]) * G.cell_stride[d];
-    G.cell_to_group.emplace(cell, int64_t(g));
+    if (!G.dense.empty()) G.dense[size_t(cell)] = int64_t(g);
+    else G.sparse.emplace(cell, int64_t(g));
   }
   return G;
 }
@@ -103,6 +124,21 @@ struct Dim {
   int64_t e;   // extent
   int64_t ss;  // source stride, bytes
   int64_t sd;  // destination stride, bytes
+};
+
+// Outer dims of a run, inner -> outer (at most one per tensor dim).
+struct Dims {
+  Dim d[kMaxDims];
+  int n = 0;
+  size_t size() const { return size_t(n); }
+  bool empty() const { return n == 0; }
+  Dim& operator[](size_t i) { return d[i]; }
+  const Dim& operator[](size_t i) const { return d[i]; }
+  Dim& back() { return d[n - 1]; }
+  void push_back(const Dim& x) { d[n++] = x; }
+  void pop_back() { --n; }
+  const Dim* begin() const { return d; }
+  const Dim* end() const { return d + n; }
 };
 
 uint32_t unit_for(int64_t bits) {
@@ -115,7 +151,7 @@ uint32_t unit_for(int64_t bits) {
 // outer dims (inner -> outer order), splitting where the kernel's 31-bit item
 // indexing or its three outer dims would be exceeded.
 void emit(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_begin, uint32_t fanout,
-          int64_t src_off, int64_t dst_off, int64_t run_bytes, std::vector<Dim> outer) {
+          int64_t src_off, int64_t dst_off, int64_t run_bytes, Dims outer) {
   if (outer.size() > 3) {  // peel the outermost dim into separate descriptors
     Dim top = outer.back();
     outer.pop_back();
@@ -142,7 +178,7 @@ void emit(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_begin, uin
   if (rows * row_items > kMaxItems) {  // halve the outermost dim with extent > 1
     for (int k = int(outer.size()) - 1; k >= 0; --k) {
       if (outer[k].e < 2) continue;
-      std::vector<Dim> a = outer, b = outer;
+      Dims a = outer, b = outer;
       int64_t h = outer[k].e / 2;
       a[k].e = h;
       b[k].e = outer[k].e - h;
@@ -207,7 +243,7 @@ void describe_piece(HostPlan* P, uint32_t piece_idx, uint32_t src_ptr, uint32_t 
   // sides stay contiguous; the rest become outer dims.
   bool in_run = true;
   int64_t run_bytes = es;
-  std::vector<Dim> outer;  // inner -> outer
+  Dims outer;  // inner -> outer
   for (int k = ndim - 1; k >= 0; --k) {
     int64_t e = piece.hi[k] - piece.lo[k];
     if (e == 1) continue;
@@ -580,19 +616,19 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
           if (box.hi[k] <= box.lo[k]) empty = true;
         }
         if (!empty) {
-          auto it = grid.cell_to_group.find(cell);
-          if (it == grid.cell_to_group.end()) {
+          const int64_t sg = grid.group_of(cell);
+          if (sg < 0) {
             *err = "internal: source grid cell without a rank";
             return RESHARD_ERR_INVALID_ARGUMENT;
           }
-          const Group& sgrp = P->src_groups[it->second];
+          const Group& sgrp = P->src_groups[sg];
           // least-loaded replica of this source box; ties go to the lowest rank
           int64_t best = sgrp.ranks[0];
           for (int64_t r : sgrp.ranks)
             if (load[P->src_base[t] + r] < load[P->src_base[t] + best]) best = r;
           const int64_t bytes = box_numel(nd, box) * es;
           load[P->src_base[t] + best] += bytes;
-          P->pieces.push_back(Piece{t, best, it->second, int64_t(g), box, bytes});
+          P->pieces.push_back(Piece{t, best, sg, int64_t(g), box, bytes});
           const int64_t fanout = int64_t(dgrp.ranks.size());
           P->bytes_read += bytes;
           P->bytes_written += bytes * fanout;

@@ -522,9 +522,11 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   __shared__ __attribute__((aligned(16))) uint8_t window[rs::kWindowBytes];
   // Block b runs on XCD b % kXcds.  Each XCD takes groups of kXcdGroup
   // consecutive tiles, the XCDs side by side: nearby tiles share an XCD's L2
-  // while all XCDs stream through the same region of memory.
+  // while all XCDs stream through the same region of memory.  Plans smaller
+  // than one round of groups (per_xcd == 0) use block b for tile b.
   const uint32_t kx = blockIdx.x / kXcds;
-  const uint32_t t = ((kx / kXcdGroup) * kXcds + blockIdx.x % kXcds) * kXcdGroup + kx % kXcdGroup;
+  const uint32_t t = per_xcd == 0 ? blockIdx.x
+                                  : ((kx / kXcdGroup) * kXcds + blockIdx.x % kXcds) * kXcdGroup + kx % kXcdGroup;
   if (t >= n_tiles) return;
   uint32_t lo = 0, hi = n_desc;  // last descriptor whose first tile is <= t
   while (hi - lo > 1) {
@@ -585,7 +587,7 @@ struct reshard_plan_s {
   bool uploaded = false;
   int device = -1;
   uint32_t n_wg = 0;       // grid of one launch: kXcds * per_xcd blocks (surplus ones exit)
-  uint32_t per_xcd = 0;    // blocks per XCD, a multiple of kXcdGroup
+  uint32_t per_xcd = 0;    // blocks per XCD, a multiple of kXcdGroup (0: one block per tile)
   void* table = nullptr;  // device: descriptors | refs (absolute pointer slots) | tile_begin
   const reshard_descriptor_t* d_descs = nullptr;
   const uint32_t* d_refs = nullptr;
@@ -615,9 +617,11 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
     return RESHARD_OK;
   }
   const rs::HostPlan& H = p->host;
-  // blocks per XCD, a whole number of tile groups
+  // blocks per XCD, a whole number of tile groups; 0: too few tiles to group
   const uint64_t per_xcd_min = (H.n_tiles + kXcds - 1) / kXcds;
-  const uint32_t per_xcd = uint32_t((per_xcd_min + kXcdGroup - 1) / kXcdGroup * kXcdGroup);
+  const uint32_t per_xcd =
+      H.n_tiles < uint64_t(kXcds) * kXcdGroup ? 0u
+                                              : uint32_t((per_xcd_min + kXcdGroup - 1) / kXcdGroup * kXcdGroup);
   const size_t desc_bytes = H.descs.size() * sizeof(reshard_descriptor_t);
   const size_t refs_off = align_up(desc_bytes, 256);
   const size_t tiles_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);
@@ -666,7 +670,7 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   p->d_tile_begin = reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + tiles_off);
   p->d_segs = reinterpret_cast<const reshard_segment_t*>(static_cast<uint8_t*>(table) + segs_off);
   p->per_xcd = per_xcd;
-  p->n_wg = per_xcd * kXcds;
+  p->n_wg = per_xcd ? per_xcd * kXcds : uint32_t(H.n_tiles);
   p->device = dev;
   p->uploaded = true;
   return RESHARD_OK;

@@ -113,6 +113,28 @@ def ffn_refit(layers: int = 32, hidden: int = 4096, ffn: int = 14336, stages: in
                     f"bf16, PP{stages} x (2,)[S0|S1] -> (2,4)[R,S0|S1], one fused launch")
 
 
+def dense_layer_refit(layers: int = 32, hidden: int = 4096, kv: int = 1024, ffn: int = 14336,
+                      stages: int = 4) -> Workload:
+    """Every weight of `layers` dense transformer layers in one fused launch:
+    q [hidden, hidden], k and v [kv, hidden] (grouped-query attention), o
+    [hidden, hidden], gate/up [ffn, hidden], down [hidden, ffn], and two norm
+    vectors [hidden].  Training side: a pipeline stage's 2-rank mesh, matrices
+    split on their output dim (row) except o and down, split on the input dim;
+    the norm vectors replicated on both ranks.  Inference side: (2, 4) = DP2 x
+    TP4 with the same split dims; the norm vectors replicated on all 8 ranks."""
+    ts = []
+    for layer in range(layers):
+        for name, shape, d in (("q", (hidden, hidden), 0), ("k", (kv, hidden), 0), ("v", (kv, hidden), 0),
+                               ("o", (hidden, hidden), 1), ("gate", (ffn, hidden), 0),
+                               ("up", (ffn, hidden), 0), ("down", (hidden, ffn), 1)):
+            ts.append(TensorSpec(f"layer{layer}.{name}", shape, torch.bfloat16, (2,), (d,), (2, 4), (R, d)))
+        for name in ("input_norm", "post_norm"):
+            ts.append(TensorSpec(f"layer{layer}.{name}", (hidden,), torch.bfloat16, (2,), (R,), (2, 4), (R, R)))
+    return Workload(f"dense_layer_refit_{layers}_layers", tuple(ts), "normal",
+                    f"{layers} layers x (q, k, v, o, gate, up, down, 2 norms) bf16, PP{stages} x (2,) -> (2,4), "
+                    f"one fused launch")
+
+
 def stage_of_layer(layer: int, layers: int = 32, stages: int = 4) -> int:
     """Pipeline stage holding `layer` (contiguous blocks of layers per stage)."""
     return layer * stages // layers
@@ -134,6 +156,7 @@ WORKLOADS = {
     "uneven_5000x3001": uneven,
     "ffn_refit_32_layers": ffn_refit,
     "narrow_columns_4194304x8": narrow_columns,
+    "dense_layer_refit_32_layers": dense_layer_refit,
 }
 
 

@@ -73,6 +73,15 @@ def test_ffn_refit_32_layers_one_launch(values):
     assert st["n_tensors"] == 96 and st["n_pieces"] == 384
 
 
+def test_dense_layer_refit_32_layers_one_launch():
+    """Every weight of 32 dense layers (attention, FFN, replicated norm vectors
+    read from one of two source replicas and written to 8 destinations) in one
+    fused launch."""
+    wl = W.dense_layer_refit()
+    st = run_parity(wl.tensors, "raw", 0, threads=16)
+    assert st["n_tensors"] == 32 * 9
+
+
 @pytest.mark.parametrize("spec", small_specs(), ids=lambda s: s.name)
 def test_small_layouts(spec):
     run_parity([spec], "raw", 3)
@@ -177,6 +186,9 @@ def test_upload_and_stats_after_execute():
         tiles = -(-117440512 // 4096)  # one workgroup per 4 KiB source tile
         per_xcd = -(-(-(-tiles // 8)) // 64) * 64  # whole groups of 64 tiles per XCD
         assert st["n_workgroups"] == 8 * per_xcd
+    with Plan(W.worked_example_8x8().tensors) as plan:  # fewer tiles than one group round
+        R.reshard_plan_upload(plan.handle, torch.cuda.current_stream().cuda_stream)
+        assert plan.stats()["n_workgroups"] == 2
         R.reshard_plan_upload(plan.handle, None)  # second upload is a no-op
 
 

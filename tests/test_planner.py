@@ -204,7 +204,8 @@ def test_worked_example_plan():
 
 def test_piece_counts_of_workloads():
     counts = {"worked_example_8x8": 8, "ffn_up_14336x4096": 8, "moe_experts_64x2048x7168": 128,
-              "uneven_5000x3001": 42, "ffn_refit_32_layers": 384, "narrow_columns_4194304x8": 8}
+              "uneven_5000x3001": 42, "ffn_refit_32_layers": 384, "narrow_columns_4194304x8": 8,
+              "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1)}
     for wl in full_workload_plans():
         with Plan(wl.tensors) as plan:
             assert plan.stats()["n_pieces"] == counts[wl.name]
