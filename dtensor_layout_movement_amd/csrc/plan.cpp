@@ -217,7 +217,6 @@ void emit(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_begin, uin
   magic_u31(D.extent[1], &D.magic[2][0], &D.magic[2][1]);
   D.piece = piece;
   P->descs.push_back(D);
-  P->desc_cost.push_back(rows * uint64_t(run_bytes) * (1 + fanout));
 }
 
 // Turns one overlap into descriptors: local offsets in the source and
@@ -404,7 +403,6 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
       P->segs.push_back(d);
     }
     P->descs.push_back(b.d);
-    P->desc_cost.push_back(uint64_t(b.d.extent[0]) * uint64_t(width));
   }
   return true;
 }
@@ -425,18 +423,14 @@ void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1) {
   if (!narrow || !view_2d(*P, t, pc0, pc1, &v)) return;
   const size_t s0 = P->segs.size();
   std::vector<reshard_descriptor_t> saved(P->descs.begin() + d0, P->descs.end());
-  std::vector<uint64_t> saved_cost(P->desc_cost.begin() + d0, P->desc_cost.end());
   std::vector<uint32_t> saved_refs(P->refs.begin() + r0, P->refs.end());
   P->descs.resize(d0);
-  P->desc_cost.resize(d0);
   P->refs.resize(r0);
   if (!emit_windows(P, t, pc0, pc1, v)) {  // keep the per-piece descriptors
     P->descs.resize(d0);
-    P->desc_cost.resize(d0);
     P->refs.resize(r0);
     P->segs.resize(s0);
     P->descs.insert(P->descs.end(), saved.begin(), saved.end());
-    P->desc_cost.insert(P->desc_cost.end(), saved_cost.begin(), saved_cost.end());
     P->refs.insert(P->refs.end(), saved_refs.begin(), saved_refs.end());
   }
 }

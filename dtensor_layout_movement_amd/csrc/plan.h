@@ -103,7 +103,6 @@ struct HostPlan {
   std::vector<reshard_descriptor_t> descs;
   std::vector<uint32_t> refs;       // fan-out: destination pointer slots (0-based in dst_ptrs)
   std::vector<reshard_segment_t> segs;  // segments of RESHARD_DESC_WINDOW descriptors
-  std::vector<uint64_t> desc_cost;  // bytes read + written by each descriptor
   std::vector<uint32_t> tile_begin; // first tile of each descriptor; n_desc + 1 entries
   uint64_t n_tiles = 0;
   int64_t global_bytes = 0, bytes_read = 0, bytes_written = 0, n_dst_writes = 0;

@@ -218,3 +218,54 @@ def test_gather_then_slice_two_plans_match_oracle():
             R.reshard_plan_destroy(p_g)
             R.reshard_plan_destroy(p_s)
             R.reshard_layout_destroy(g_lay)
+
+
+@pytest.mark.parametrize("layers", [1, 16], ids=["kernel_arg_pointers", "slot_ring_pointers"])
+def test_execute_from_many_threads(layers):
+    """One plan executed concurrently from several host threads, each on its own
+    stream with its own destination buffers; with more pointers than kernel
+    arguments hold, every call goes through the shared slot ring."""
+    import threading
+    from reshard_harness import oracle_dsts
+    specs = list(W.ffn_refit(layers, 64, 96).tensors)
+    with Plan(specs) as plan:
+        assert_boxes_agree(plan)
+        assert_descriptors_in_bounds(plan)
+        want, src_sets = [], []
+        for t, spec in enumerate(specs):
+            g = W.make_global(spec, "raw", 21, t)
+            sb = oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements)
+            srcs = W.cut(g, sb)
+            want.append(oracle_dsts(spec, srcs))
+            gs = GuardedShards(shard_nbytes(sb, spec.dtype), "cuda")
+            for i, s in enumerate(srcs):
+                gs.region(i).copy_(s.reshape(-1).view(torch.uint8).cuda())
+            src_sets.append(gs)
+        src_ptrs = [p for s in src_sets for p in s.ptrs]
+        outs = [[GuardedShards(shard_nbytes(oracle_boxes(s.shape, s.dst_mesh, s.dst_placements), s.dtype),
+                               "cuda") for s in specs] for _ in range(4)]
+        torch.cuda.synchronize()
+        errors = []
+
+        def work(k):
+            try:
+                st = torch.cuda.Stream()
+                dst_ptrs = [p for d in outs[k] for p in d.ptrs]
+                with torch.cuda.stream(st):
+                    for _ in range(5):
+                        R.reshard_execute(plan.handle, src_ptrs, dst_ptrs, st.cuda_stream)
+                st.synchronize()
+            except Exception as e:  # noqa: BLE001
+                errors.append(e)
+        threads = [threading.Thread(target=work, args=(k,)) for k in range(4)]
+        for th in threads:
+            th.start()
+        for th in threads:
+            th.join()
+        torch.cuda.synchronize()
+        assert not errors, errors
+        for dsts in outs:
+            for t in range(len(specs)):
+                for i, w in enumerate(want[t]):
+                    assert torch.equal(dsts[t].region(i).cpu(), w.reshape(-1).view(torch.uint8))
+                    assert dsts[t].guards_intact(i)

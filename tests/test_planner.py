@@ -390,3 +390,44 @@ def test_plan_stats_fields():
         assert st["n_dst_writes"] == 16 and st["n_descriptors"] == 8
         assert st["n_workgroups"] == 0  # not uploaded: no device touched
         assert st["plan_host_us"] > 0
+
+
+def test_plans_from_many_threads():
+    """Planning is host-only and re-entrant: plans built concurrently from
+    several threads equal the one built alone."""
+    import threading
+    wl = W.dense_layer_refit(4, 256, 64, 512)
+    with Plan(wl.tensors) as ref_plan:
+        ref = R.reshard_plan_descriptors(ref_plan.handle)
+    results, errors = [], []
+
+    def work():
+        try:
+            for _ in range(5):
+                with Plan(wl.tensors) as p:
+                    results.append(R.reshard_plan_descriptors(p.handle))
+        except Exception as e:  # noqa: BLE001
+            errors.append(e)
+    threads = [threading.Thread(target=work) for _ in range(6)]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    assert not errors and len(results) == 30
+    assert all(r == ref for r in results)
+
+
+def test_device_calls_fail_cleanly_without_a_gpu():
+    """With no visible GPU, upload and execute return RESHARD_ERR_HIP (no crash);
+    planning and inspection keep working."""
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is visible")
+    with Plan(W.ffn_up(64, 32).tensors) as plan:
+        with pytest.raises(R.ReshardError) as e:
+            R.reshard_plan_upload(plan.handle, None)
+        assert e.value.status == R.ERR_HIP
+        with pytest.raises(R.ReshardError) as e:
+            R.reshard_execute(plan.handle, [0x1000] * 4, [0x2000] * 4, None)
+        assert e.value.status == R.ERR_HIP
+        assert plan.stats()["n_pieces"] == 8
