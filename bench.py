@@ -15,6 +15,10 @@ pages' baseline scheme, gather-then-slice, built from two plans of the same
 library (sources -> one global buffer -> destinations); its step time and the
 reshard's speed-up over it are reported as ``gather_then_slice_gpu``.
 
+The two-stage transport of the pages (each destination box delivered once,
+split over its replicas, then assembled by every replica; pipelined over
+tensor chunks on two streams) is timed the same way as ``two_stage_gpu``.
+
 Prints one JSON line.  ``value`` = algorithmic bytes (global bytes read once +
 every destination shard written once) per second over the timed steps;
 ``roofline.achieved`` = the same bytes over the kernel's mean launch duration:
@@ -97,8 +101,18 @@ def plan_timing(R, wl, reps: int) -> dict:
         R.reshard_plan_destroy(plan)
         for h in srcs + dsts:
             R.reshard_layout_destroy(h)
+    up = []
+    for _ in range(max(3, reps // 10)):
+        plan, srcs, dsts = build_plan(R, wl)
+        t0 = time.perf_counter()
+        R.reshard_plan_upload(plan, None)
+        up.append((time.perf_counter() - t0) * 1e6)
+        R.reshard_plan_destroy(plan)
+        for h in srcs + dsts:
+            R.reshard_layout_destroy(h)
     return {"host_median": round(statistics.median(host), 2),
-            "with_layouts_and_binding_median": round(statistics.median(wall), 2), "reps": reps}
+            "with_layouts_and_binding_median": round(statistics.median(wall), 2),
+            "upload_median": round(statistics.median(up), 2), "reps": reps}
 
 
 def alloc_set(torch, R, wl, lay_src, lay_dst, dev, seed):
@@ -166,13 +180,46 @@ def gather_then_slice(torch, R, wl, lay_src, lay_dst, sets, stream, steps: int, 
             "reshard_speedup": round(ms / reshard_ms, 3)}
 
 
-def cpu_baseline(wl, budget_s: float) -> dict:
+def two_stage(torch, wl, sets_boxes, steps: int, reshard_ms: float, chunks: int = 4) -> dict:
+    """The pages' two-stage transport emulated on the same GPU: each destination
+    box delivered once, split over its replicas, then assembled by every
+    replica; pipelined over tensor chunks on two streams."""
+    from dtensor_layout_movement_amd.two_stage import TwoStagePlan
+    ts = TwoStagePlan(wl.tensors, chunks=chunks)
+    try:
+        staging = [[torch.empty(sh, dtype=spec.dtype, device="cuda") if all(sh) else None
+                    for sh in shapes] for spec, shapes in zip(wl.tensors, ts.staging_shapes())]
+        stag_ptrs = [[x.data_ptr() if x is not None else 0 for x in row] for row in staging]
+        arrays = [ts.pointer_arrays(sp, stag_ptrs, dp) for sp, dp in sets_boxes]
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        events = [torch.cuda.Event() for _ in range(chunks)]
+        torch.cuda.synchronize()
+        for i in range(3):
+            ts.execute(arrays[i % len(arrays)], a, b, events)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(a)
+        for i in range(steps):
+            b.wait_stream(a)
+            a.wait_stream(b)
+            ts.execute(arrays[i % len(arrays)], a, b, events)
+        a.wait_stream(b)
+        e1.record(a)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        return {"ms_per_step": round(ms, 5), "bytes_moved": ts.bytes_moved(), "steps": steps,
+                "chunks": len(ts.stage1), "reshard_speedup": round(ms / reshard_ms, 3)}
+    finally:
+        ts.close()
+
+
+def cpu_baseline(wl, budget_s: float, cores: int | None = None) -> dict:
     """The oracle (gather-then-slice) timed on this host's cores on the same workload."""
     import torch
     import oracle
     from dtensor_layout_movement_amd import workloads as W
-    cores = len(os.sched_getaffinity(0))
-    total_bytes, secs, reps = 0, 0.0, 0
+    cores = cores or len(os.sched_getaffinity(0))
+    secs, reps = 0.0, 0
     algo = 0
     prepared = []
     for t, spec in enumerate(wl.tensors):
@@ -272,6 +319,28 @@ def main() -> int:
     value = algo_bytes / (ms_per_step * 1e-3) / 1e9
     achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
 
+    # outside the timed region: per-launch event distribution, and warm steps on
+    # one buffer set (inputs partly cache-resident)
+    n_dist = min(50, K)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_dist)]
+    for i in range(n_dist):
+        _, _, sp, dp = sets[i % n_sets]
+        ev[i][0].record(stream)
+        R.reshard_execute(plan, sp, dp, stream.cuda_stream)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    per_launch = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    _, _, sp0, dp0 = sets[0]
+    for _ in range(3):
+        R.reshard_execute(plan, sp0, dp0, stream.cuda_stream)
+    w0, w1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0.record(stream)
+    for _ in range(n_dist):
+        R.reshard_execute(plan, sp0, dp0, stream.cuda_stream)
+    w1.record(stream)
+    torch.cuda.synchronize()
+    warm_ms = w0.elapsed_time(w1) / n_dist
+
     # context: a plain device copy moving the same number of bytes (read + write)
     half = algo_bytes // 2
     a = torch.empty(half, dtype=torch.uint8, device=dev)
@@ -291,6 +360,19 @@ def main() -> int:
     if not args.no_comparator:
         comparator = gather_then_slice(torch, R, wl, lay_src, lay_dst, sets, stream,
                                        max(5, K // 4), ms_per_step)
+    two = None
+    if not args.no_comparator:
+        per_tensor = []
+        for src_bufs, dst_bufs, _, _ in sets:
+            sp, dp, i_s, i_d = [], [], 0, 0
+            for t in range(len(wl.tensors)):
+                ns, nd = R.reshard_layout_num_ranks(lay_src[t]), R.reshard_layout_num_ranks(lay_dst[t])
+                sp.append([b.data_ptr() if b is not None else 0 for b in src_bufs[i_s:i_s + ns]])
+                dp.append([b.data_ptr() if b is not None else 0 for b in dst_bufs[i_d:i_d + nd]])
+                i_s += ns
+                i_d += nd
+            per_tensor.append((sp, dp))
+        two = two_stage(torch, wl, per_tensor, max(5, K // 4), ms_per_step)
     plan_us = plan_timing(R, wl, args.plan_reps if algo_bytes < 2e10 else max(5, args.plan_reps // 20))
     traffic = traffic_from_profile(wl.name)
     spec0 = wl.tensors[0]
@@ -332,12 +414,19 @@ def main() -> int:
             "kernel": KERNEL_NAME,
             "kernel_mean_us": round(kernel_ms * 1e3, 3),
         },
+        "launch_us_cold": {"p10": round(per_launch[len(per_launch) // 10], 2),
+                           "p50": round(per_launch[len(per_launch) // 2], 2),
+                           "p90": round(per_launch[(9 * len(per_launch)) // 10], 2), "n": n_dist},
+        "warm_same_buffers_gbps": round(algo_bytes / (warm_ms * 1e-3) / 1e9, 1),
         "copy_reference_gbps": round(copy_gbps, 1),
         "gather_then_slice_gpu": comparator,
+        "two_stage_gpu": two,
         "wall_s": round(wall, 4),
     }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
+        one = cpu_baseline(wl, min(5.0, args.cpu_budget_s), cores=1)
+        out["cpu_baseline"]["single_core_value"] = one["value"]
     print(json.dumps(out), flush=True)
 
     R.reshard_plan_destroy(plan)

@@ -269,3 +269,37 @@ def test_execute_from_many_threads(layers):
                 for i, w in enumerate(want[t]):
                     assert torch.equal(dsts[t].region(i).cpu(), w.reshape(-1).view(torch.uint8))
                     assert dsts[t].guards_intact(i)
+
+
+@pytest.mark.parametrize("chunks", [1, 4])
+def test_two_stage_send_once_then_exchange(chunks):
+    """The two-stage transport (each box delivered once, split over its replicas,
+    then assembled by every replica; pipelined over tensor chunks on two
+    streams) reaches the oracle's bytes."""
+    from dtensor_layout_movement_amd.two_stage import TwoStagePlan
+    from reshard_harness import oracle_dsts
+    specs = list(W.ffn_refit(3, 64, 224).tensors) + [W.ffn_up(448, 320).tensors[0], W.uneven(301, 257).tensors[0]]
+    ts = TwoStagePlan(specs, chunks=chunks)
+    try:
+        srcs_d, dsts_d, stag_d, wants = [], [], [], []
+        for t, spec in enumerate(specs):
+            g = W.make_global(spec, "raw", 31, t)
+            srcs = W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
+            wants.append(oracle_dsts(spec, srcs))
+            srcs_d.append([s.cuda() if s is not None else None for s in srcs])
+            dsts_d.append([torch.full_like(w, 0, device="cuda") for w in wants[-1]])
+        for t, shapes in enumerate(ts.staging_shapes()):
+            stag_d.append([torch.empty(sh, dtype=specs[t].dtype, device="cuda") if all(sh) else None
+                           for sh in shapes])
+        ptr = lambda lst: [[x.data_ptr() if x is not None and x.numel() else 0 for x in row] for row in lst]
+        arrays = ts.pointer_arrays(ptr(srcs_d), ptr(stag_d), ptr(dsts_d))
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        torch.cuda.synchronize()
+        events = [torch.cuda.Event() for _ in arrays]
+        ts.execute(arrays, a, b, events)
+        torch.cuda.synchronize()
+        for t in range(len(specs)):
+            for got, w in zip(dsts_d[t], wants[t]):
+                assert torch.equal(got.cpu().view(torch.uint8), w.view(torch.uint8)), specs[t].name
+    finally:
+        ts.close()

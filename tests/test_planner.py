@@ -431,3 +431,28 @@ def test_device_calls_fail_cleanly_without_a_gpu():
             R.reshard_execute(plan.handle, [0x1000] * 4, [0x2000] * 4, None)
         assert e.value.status == R.ERR_HIP
         assert plan.stats()["n_pieces"] == 8
+
+
+@pytest.mark.parametrize("wl", full_workload_plans() + [W.dense_layer_refit(2, 256, 64, 512)],
+                         ids=lambda w: w.name)
+def test_two_stage_layout_slices_tile_each_box(wl):
+    """Stage 1 of the two-stage transport gives every destination replica one
+    slice of its box; the slices of a box's replicas tile it exactly (checked
+    with the oracle's box function)."""
+    import oracle
+    from dtensor_layout_movement_amd.two_stage import stage1_layout
+    for spec in wl.tensors[:9]:
+        mesh1, pl1, rank_map = stage1_layout(spec.dst_mesh, spec.dst_placements)
+        n1 = int(np.prod(mesh1))
+        covered = {}
+        for r1 in range(n1):
+            lo, hi = oracle.shard_box(list(spec.shape), list(mesh1), list(pl1), r1)
+            dlo, dhi = oracle.shard_box(list(spec.shape), list(spec.dst_mesh), list(spec.dst_placements),
+                                        rank_map[r1])
+            assert all(a <= l and h <= b for l, h, a, b in zip(lo, hi, dlo, dhi) if h > l)
+            vol = int(np.prod([max(0, h - l) for l, h in zip(lo, hi)]))
+            key = (tuple(dlo), tuple(dhi))
+            covered[key] = covered.get(key, 0) + vol
+        for (dlo, dhi), vol in covered.items():
+            assert vol == int(np.prod([max(0, h - l) for l, h in zip(dlo, dhi)]))
+        assert sorted(rank_map) == list(range(int(np.prod(spec.dst_mesh))))
