@@ -17,7 +17,9 @@ reshard's speed-up over it are reported as ``gather_then_slice_gpu``.
 
 The two-stage transport of the pages (each destination box delivered once,
 split over its replicas, then assembled by every replica; pipelined over
-tensor chunks on two streams) is timed the same way as ``two_stage_gpu``.
+tensor chunks on two streams) is timed the same way as ``two_stage_gpu``, and
+the pages' hybrid refit (FFN projections by the reshard, other weights by
+gather-then-slice) as ``hybrid_gpu`` where the workload has both kinds.
 
 Prints one JSON line.  ``value`` = algorithmic bytes (global bytes read once +
 every destination shard written once) per second over the timed steps;
@@ -213,6 +215,38 @@ def two_stage(torch, wl, sets_boxes, steps: int, reshard_ms: float, chunks: int 
         ts.close()
 
 
+def hybrid(torch, wl, sets_boxes, stream, steps: int, reshard_ms: float):
+    """The pages' hybrid refit on the same GPU: FFN projections by the reshard,
+    the other weights by gather-then-slice, one stream.  None when the routing
+    does not split the workload."""
+    from dtensor_layout_movement_amd.hybrid import HybridPlan
+    hp = HybridPlan(wl.tensors)
+    try:
+        if not hp.direct or not hp.gather:
+            return None
+        n_sets = len(sets_boxes)
+        glob = [[torch.empty(sh, dtype=wl.tensors[t].dtype, device="cuda")
+                 for t, sh in zip(hp.gather, hp.global_shapes())] for _ in range(n_sets)]
+        arrays = [hp.pointer_arrays(sp, dp, [g.data_ptr() for g in glob[i]])
+                  for i, (sp, dp) in enumerate(sets_boxes)]
+        for i in range(3):
+            hp.execute(arrays[i % n_sets], stream.cuda_stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            hp.execute(arrays[i % n_sets], stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        return {"ms_per_step": round(ms, 5), "bytes_moved": hp.bytes_moved(), "steps": steps,
+                "reshard_tensors": len(hp.direct), "gather_tensors": len(hp.gather),
+                "reshard_share_of_bytes": round(hp.reshard_share(), 4),
+                "reshard_speedup": round(ms / reshard_ms, 3)}
+    finally:
+        hp.close()
+
+
 def cpu_baseline(wl, budget_s: float, cores: int | None = None) -> dict:
     """The oracle (gather-then-slice) timed on this host's cores on the same workload."""
     import torch
@@ -360,7 +394,7 @@ def main() -> int:
     if not args.no_comparator:
         comparator = gather_then_slice(torch, R, wl, lay_src, lay_dst, sets, stream,
                                        max(5, K // 4), ms_per_step)
-    two = None
+    two = mixed = None
     if not args.no_comparator:
         per_tensor = []
         for src_bufs, dst_bufs, _, _ in sets:
@@ -373,6 +407,7 @@ def main() -> int:
                 i_d += nd
             per_tensor.append((sp, dp))
         two = two_stage(torch, wl, per_tensor, max(5, K // 4), ms_per_step)
+        mixed = hybrid(torch, wl, per_tensor, stream, max(5, K // 4), ms_per_step)
     plan_us = plan_timing(R, wl, args.plan_reps if algo_bytes < 2e10 else max(5, args.plan_reps // 20))
     traffic = traffic_from_profile(wl.name)
     spec0 = wl.tensors[0]
@@ -421,6 +456,7 @@ def main() -> int:
         "copy_reference_gbps": round(copy_gbps, 1),
         "gather_then_slice_gpu": comparator,
         "two_stage_gpu": two,
+        "hybrid_gpu": mixed,
         "wall_s": round(wall, 4),
     }
     if not args.no_cpu_baseline:

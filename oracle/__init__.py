@@ -59,7 +59,9 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
                                    ctypes.c_int, _I64P, _I32P, ctypes.POINTER(ctypes.c_void_p),
                                    ctypes.c_int, _I64P, _I32P, ctypes.POINTER(ctypes.c_void_p),
                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
-    for f in (lib.oracle_num_ranks, lib.oracle_shard_box, lib.oracle_reshard):
+    lib.oracle_convert.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
+                                   ctypes.c_int64, ctypes.c_int]
+    for f in (lib.oracle_num_ranks, lib.oracle_shard_box, lib.oracle_reshard, lib.oracle_convert):
         f.restype = ctypes.c_int
     if path == _LIB_PATH:
         _lib = lib
@@ -131,3 +133,25 @@ def reshard(shape, elem_size, src_mesh, src_pl, src_bufs, dst_mesh, dst_pl, dst_
                             _addr(global_out), int(check), int(threads))
     if rc:
         raise OracleError(rc)
+
+
+# Float formats of oracle_convert, by name.
+FORMATS = {"f32": 0, "bf16": 1, "f16": 2}
+
+
+def convert(values, from_fmt: str, to_fmt: str, threads: int = 1, lib=None):
+    """Convert a contiguous CPU torch tensor of `from_fmt` elements to `to_fmt`
+    ("f32", "bf16", "f16"): round to nearest, ties to even; NaN keeps its sign
+    and leading payload bits and becomes quiet.  Returns a new tensor."""
+    import torch
+    lib = lib or load()
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+    if values.dtype != dt[from_fmt] or not values.is_contiguous() or values.device.type != "cpu":
+        raise ValueError("convert needs a contiguous CPU tensor of the source format")
+    out = torch.empty(values.shape, dtype=dt[to_fmt])
+    if values.numel():
+        rc = lib.oracle_convert(FORMATS[from_fmt], FORMATS[to_fmt], values.data_ptr(), out.data_ptr(),
+                                values.numel(), int(threads))
+        if rc:
+            raise OracleError(rc)
+    return out

@@ -32,9 +32,13 @@
  * element must have been covered exactly R_src times, R_src being the product
  * of the mesh sizes of the source's Replicate dims.
  *
+ * Element conversion (oracle_convert) serves a reshard whose destination dtype
+ * differs from the source's; see the comment above that function.
+ *
  * Built with g++ (plain C++17, std::thread); no HIP.
  */
 #include <atomic>
+#include <cmath>
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
@@ -146,6 +150,105 @@ int64_t global_row_offset(int ndim, const int64_t* shape, const int64_t* lo,
     stride *= shape[k];
   }
   return off;
+}
+
+/*
+ * Floating-point formats for oracle_convert.  The reshard pages mention that
+ * the refit has precision modes and say nothing more (news.bpdata.com and
+ * techfeed.io write-ups of the NVIDIA blog, closing remarks on the refit guide).
+ * The reading taken here: a destination may hold a different float format than
+ * the source; widening keeps the value; narrowing rounds to nearest, ties to
+ * even, with overflow to infinity (IEEE 754 default rounding).
+ *
+ * Each format is (total bits, fraction bits, exponent bias).  A finite value is
+ * decoded to a double (exact for all three formats), rounded to the target's
+ * precision and exponent range by a plain floor-and-compare, and encoded.  NaN
+ * has no value to round; the convention used for it is: sign kept, the leading
+ * fraction bits kept (shifted to the target's width), quiet bit set.
+ */
+struct Format {
+  int bits;  // 32 or 16
+  int frac;  // fraction (stored mantissa) bits
+  int bias;
+};
+
+constexpr Format kFormats[3] = {
+    {32, 23, 127},  // 0: IEEE binary32
+    {16, 7, 127},   // 1: bfloat16
+    {16, 10, 15},   // 2: IEEE binary16
+};
+
+int exp_bits(const Format& f) { return f.bits - 1 - f.frac; }
+uint32_t exp_all_ones(const Format& f) { return (1u << exp_bits(f)) - 1; }
+
+double max_finite(const Format& f) {
+  const int emax = int(exp_all_ones(f)) - 1 - f.bias;
+  return std::ldexp(2.0 - std::ldexp(1.0, -f.frac), emax);
+}
+
+/* Value of a finite bit pattern. */
+double decode(const Format& f, uint32_t bits) {
+  const bool neg = (bits >> (f.bits - 1)) & 1;
+  const uint32_t e = (bits >> f.frac) & exp_all_ones(f);
+  const uint32_t m = bits & ((1u << f.frac) - 1);
+  double v;
+  if (e == 0) v = std::ldexp(double(m), 1 - f.bias - f.frac);  // subnormal or zero
+  else v = std::ldexp(double((1u << f.frac) + m), int(e) - f.bias - f.frac);
+  return neg ? -v : v;
+}
+
+/* x rounded to the nearest value of format f (ties to even); beyond the largest
+   finite value after rounding: infinity.  x is finite. */
+double round_to(const Format& f, double x) {
+  if (x == 0) return x;
+  const double a = std::fabs(x);
+  int e;
+  std::frexp(a, &e);        // a = m * 2^e with m in [0.5, 1): a's exponent is e - 1
+  int E = e - 1;
+  if (E < 1 - f.bias) E = 1 - f.bias;   // subnormal range: fixed spacing
+  const int q = E - f.frac;             // weight of the last kept bit is 2^q
+  const double s = std::ldexp(a, -q);   // exact
+  double r = std::floor(s);
+  const double d = s - r;
+  if (d > 0.5 || (d == 0.5 && std::fmod(r, 2.0) != 0)) r += 1;
+  double y = std::ldexp(r, q);
+  if (y > max_finite(f)) y = INFINITY;
+  return x < 0 ? -y : y;
+}
+
+/* Bit pattern of y, which is a value of format f (or an infinity). */
+uint32_t encode(const Format& f, double y) {
+  const uint32_t sign = std::signbit(y) ? 1u << (f.bits - 1) : 0u;
+  const double a = std::fabs(y);
+  if (std::isinf(a)) return sign | (exp_all_ones(f) << f.frac);
+  if (a == 0) return sign;
+  int e;
+  std::frexp(a, &e);
+  const int E = e - 1;
+  if (E < 1 - f.bias)  // subnormal: the fraction counts units of 2^(1 - bias - frac)
+    return sign | uint32_t(std::ldexp(a, f.bias - 1 + f.frac));
+  const uint32_t m = uint32_t(std::ldexp(a, f.frac - E)) - (1u << f.frac);
+  return sign | (uint32_t(E + f.bias) << f.frac) | m;
+}
+
+bool is_nan(const Format& f, uint32_t bits) {
+  return ((bits >> f.frac) & exp_all_ones(f)) == exp_all_ones(f) && (bits & ((1u << f.frac) - 1)) != 0;
+}
+
+uint32_t convert_one(const Format& from, const Format& to, uint32_t bits) {
+  if (is_nan(from, bits)) {
+    const uint32_t sign = (bits >> (from.bits - 1)) & 1;
+    uint32_t m = bits & ((1u << from.frac) - 1);
+    m = to.frac >= from.frac ? m << (to.frac - from.frac) : m >> (from.frac - to.frac);
+    m |= 1u << (to.frac - 1);  // quiet
+    return (sign << (to.bits - 1)) | (exp_all_ones(to) << to.frac) | m;
+  }
+  const uint32_t e = (bits >> from.frac) & exp_all_ones(from);
+  if (e == exp_all_ones(from)) {  // infinity
+    const uint32_t sign = (bits >> (from.bits - 1)) & 1;
+    return (sign << (to.bits - 1)) | (exp_all_ones(to) << to.frac);
+  }
+  return encode(to, round_to(to, decode(from, bits)));
 }
 
 }  // namespace
@@ -288,6 +391,37 @@ int oracle_reshard(int ndim, const int64_t* shape, int64_t elem_size,
   std::free(count);
   if (own_x) std::free(X);
   return status;
+}
+
+/*
+ * Converts n elements from format `from` to format `to` (0 = binary32,
+ * 1 = bfloat16, 2 = binary16; elements are stored little-endian in 4 or 2
+ * bytes).  Used after the gather-then-slice for a reshard whose destination
+ * dtype differs from the source's.  Returns 0, or ORACLE_BAD_LAYOUT for an
+ * unknown format.
+ */
+int oracle_convert(int from, int to, const void* in, void* out, int64_t n, int threads) {
+  if (from < 0 || from > 2 || to < 0 || to > 2 || n < 0) return ORACLE_BAD_LAYOUT;
+  const Format& F = kFormats[from];
+  const Format& T = kFormats[to];
+  parallel_rows(n, threads < 1 ? 1 : threads, [&](int64_t a, int64_t b) {
+    for (int64_t i = a; i < b; ++i) {
+      uint32_t x;
+      if (F.bits == 32) std::memcpy(&x, (const unsigned char*)in + 4 * i, 4);
+      else {
+        uint16_t h;
+        std::memcpy(&h, (const unsigned char*)in + 2 * i, 2);
+        x = h;
+      }
+      const uint32_t y = convert_one(F, T, x);
+      if (T.bits == 32) std::memcpy((unsigned char*)out + 4 * i, &y, 4);
+      else {
+        const uint16_t h = uint16_t(y);
+        std::memcpy((unsigned char*)out + 2 * i, &h, 2);
+      }
+    }
+  });
+  return ORACLE_OK;
 }
 
 }  // extern "C"

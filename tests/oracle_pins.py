@@ -17,6 +17,12 @@ a mismatch.  What pins what:
 * ``pin_gather``           -- the rebuilt global equals the generated one, and
   replica / coverage / layout checks fire on bad input.
 * ``pin_raw_bits``         -- bytes (NaN payloads, -0.0, subnormals) survive.
+* ``pin_convert_library``  -- float conversion against numpy's float16 and
+  torch's bfloat16 casts (both IEEE round to nearest, ties to even) on random
+  bit patterns and on every tie point between adjacent target values (and one
+  f32 step either side); widening over all 65536 patterns of each 16-bit format.
+* ``pin_convert_closed``   -- float conversion on hand-derived values: ties to
+  even, the overflow threshold, subnormals, signed zero, NaN convention.
 """
 from __future__ import annotations
 
@@ -253,7 +259,116 @@ def pin_raw_bits(lib):
             assert d.view(torch.uint8).numpy().tobytes() == want.view(torch.uint8).numpy().tobytes()
 
 
-ALL_PINS = (pin_worked_example, pin_box_vs_dtensor, pin_box_vs_chunk, pin_end_to_end_chunk,
+# ----------------------------------------------------------------- conversion
+
+def _from_bits(bits):  # int32 tensor -> f32 tensor with exactly those bits
+    return bits.to(torch.int32).view(torch.float32)
+
+
+def convert_cases(rng, fmt):
+    """Non-NaN f32 inputs probing narrowing to `fmt` ("bf16" or "f16")."""
+    rand = rng.integers(0, 1 << 32, size=1 << 18, dtype=np.uint64).astype(np.uint32).view(np.int32)
+    if fmt == "bf16":
+        # ties sit at bit 15 of the f32 pattern: (k << 16) | 0x8000, and one step either side
+        k = np.arange(0, 0x7f80, dtype=np.int64)
+        ties = (k << 16) | 0x8000
+    else:
+        # every tie between adjacent f16 values, taken from their f32 midpoints
+        h = np.arange(0, 0x7c00, dtype=np.uint16)
+        v = h.view(np.float16).astype(np.float64)
+        nxt = (h + 1).view(np.float16).astype(np.float64)
+        mid = ((v + nxt) / 2).astype(np.float32)          # exact: 12 significant bits
+        ties = mid.view(np.int32).astype(np.int64)
+    pos = np.concatenate([ties - 1, ties, ties + 1]).astype(np.int64)
+    pos = pos[(pos >= 0) & (pos < 0x7f800000)]
+    signed = np.concatenate([pos, pos | (1 << 31)]).astype(np.uint32).view(np.int32)
+    bits = np.concatenate([rand, signed])
+    x = bits.view(np.float32)
+    return torch.from_numpy(bits[~np.isnan(x)].copy())
+
+
+def pin_convert_library(lib, seed=3):
+    rng = np.random.default_rng(seed)
+    # f32 -> f16 against numpy
+    bits = convert_cases(rng, "f16")
+    x = _from_bits(bits)
+    got = oracle.convert(x, "f32", "f16", lib=lib).view(torch.int16).numpy()
+    with np.errstate(over="ignore"):
+        want = x.numpy().astype(np.float16).view(np.int16)
+    bad = np.nonzero(got != want)[0]
+    assert bad.size == 0, f"f32->f16 differs from numpy at {bad.size} inputs, e.g. {hex(int(bits[bad[0]]) & 0xffffffff)}"
+    # f32 -> bf16 against torch
+    bits = convert_cases(rng, "bf16")
+    x = _from_bits(bits)
+    got = oracle.convert(x, "f32", "bf16", lib=lib).view(torch.int16)
+    want = x.to(torch.bfloat16).view(torch.int16)
+    bad = torch.nonzero(got != want)
+    assert bad.numel() == 0, f"f32->bf16 differs from torch at {bad.numel()} inputs"
+    # widening, every pattern; NaN compared as NaN with its sign
+    allp = torch.arange(-(1 << 15), 1 << 15, dtype=torch.int32).to(torch.int16)
+    for fmt, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
+        h = allp.view(tdt)
+        got = oracle.convert(h.contiguous(), fmt, "f32", lib=lib)
+        want = h.to(torch.float32) if fmt == "bf16" else torch.from_numpy(h.numpy().astype(np.float32))             if False else torch.from_numpy(allp.numpy().view(np.float16).astype(np.float32))
+        nan = torch.isnan(want)
+        assert torch.equal(torch.isnan(got), nan), f"{fmt}->f32 NaN-ness"
+        assert torch.equal(got[~nan].view(torch.int32), want[~nan].view(torch.int32)), f"{fmt}->f32 values"
+        assert torch.equal(torch.signbit(got[nan]), torch.signbit(want[nan])), f"{fmt}->f32 NaN sign"
+    # NaN in narrowing: NaN out, sign kept
+    nans = torch.tensor([0x7f800001, 0x7fc00000, 0x7fffffff, 0xff800001 - (1 << 32), 0x7f802000],
+                        dtype=torch.int64).to(torch.int32)
+    for fmt in ("bf16", "f16"):
+        out = oracle.convert(_from_bits(nans), "f32", fmt, lib=lib).view(torch.int16).numpy().astype(np.uint16)
+        expo = 0x7F80 if fmt == "bf16" else 0x7C00      # exponent field all ones, fraction nonzero
+        assert all((int(v) & expo) == expo and (int(v) & 0x7FFF & ~expo) for v in out), f"f32->{fmt}: NaN lost"
+        assert [(int(v) >> 15) & 1 for v in out] == [(int(b) >> 31) & 1 for b in nans.tolist()], f"f32->{fmt}: NaN sign"
+
+
+def pin_convert_closed(lib):
+    """Values derived by hand from the formats (f16: 10 fraction bits, bias 15;
+    bf16: 7 fraction bits, bias 127)."""
+    f16 = [  # (f32 input, expected binary16 bits)
+        (1.0, 0x3C00), (-2.0, 0xC000), (65504.0, 0x7BFF),
+        (65519.99609375, 0x7BFF),            # just below the overflow tie
+        (65520.0, 0x7C00),                   # tie between 65504 and 2^16: to even -> infinity
+        (2.0 ** -14, 0x0400),                # smallest normal
+        (2.0 ** -24, 0x0001),                # smallest subnormal
+        (2.0 ** -25, 0x0000),                # tie between 0 and 2^-24: to even -> 0
+        (1.5 * 2.0 ** -25, 0x0001), (3 * 2.0 ** -25, 0x0002),   # 1.5 ulp tie -> 2 (even)
+        (1 + 2.0 ** -11, 0x3C00), (1 + 3 * 2.0 ** -11, 0x3C02),  # ties to even
+        (-0.0, 0x8000), (float("inf"), 0x7C00), (float("-inf"), 0xFC00),
+        ((2 - 2.0 ** -10) * 2.0 ** -15, 0x0400),  # 1023.5 subnormal units: tie, to even -> smallest normal
+        (2.0 ** -15 + 2.0 ** -25, 0x0200),        # 512.5 units: tie, to even -> 512
+    ]
+    bf16 = [
+        (1.0, 0x3F80), (1 + 2.0 ** -8, 0x3F80), (1 + 3 * 2.0 ** -8, 0x3F82),
+        (65504.0, 0x4780), (2.0 ** -133, 0x0001), (2.0 ** -134, 0x0000),
+        (3 * 2.0 ** -134, 0x0002), (-0.0, 0x8000), (float("inf"), 0x7F80),
+    ]
+    for fmt, table in (("f16", f16), ("bf16", bf16)):
+        x = torch.tensor([v for v, _ in table], dtype=torch.float32)
+        got = oracle.convert(x, "f32", fmt, lib=lib).view(torch.int16).numpy().astype(np.uint16)
+        want = np.array([b for _, b in table], dtype=np.uint16)
+        bad = np.nonzero(got != want)[0]
+        assert bad.size == 0, f"f32->{fmt}: {[(table[i][0], hex(got[i]), hex(want[i])) for i in bad]}"
+    # bf16 overflow: the tie between the largest bf16 and 2^128 goes to infinity
+    # (largest bf16 has an odd last bit); the largest f32 too
+    x = _from_bits(torch.tensor([0x7F7F8000, 0x7F7F7FFF, 0x7F7FFFFF], dtype=torch.int32))
+    got = oracle.convert(x, "f32", "bf16", lib=lib).view(torch.int16).numpy().astype(np.uint16)
+    assert got.tolist() == [0x7F80, 0x7F7F, 0x7F80], [hex(v) for v in got]
+    # NaN convention: sign kept, leading payload bits kept, quiet bit set
+    x = _from_bits(torch.tensor([0x7F800001, 0xFFA12345 - (1 << 32)], dtype=torch.int64).to(torch.int32))
+    got = oracle.convert(x, "f32", "bf16", lib=lib).view(torch.int16).numpy().astype(np.uint16)
+    assert got.tolist() == [0x7FC0, 0xFFE1], [hex(v) for v in got]
+    got = oracle.convert(x, "f32", "f16", lib=lib).view(torch.int16).numpy().astype(np.uint16)
+    assert got.tolist() == [0x7E00, 0xFE00 | (0x212345 >> 13)], [hex(v) for v in got]
+    h = torch.tensor([0x7C01, 0xFD55 - (1 << 16)], dtype=torch.int32).to(torch.int16).view(torch.float16)
+    got = oracle.convert(h.contiguous(), "f16", "f32", lib=lib).view(torch.int32).numpy().astype(np.uint32)
+    assert got.tolist() == [0x7FC02000, 0xFFC00000 | (0x155 << 13)], [hex(v) for v in got]
+
+
+ALL_PINS = (pin_convert_library, pin_convert_closed,
+            pin_worked_example, pin_box_vs_dtensor, pin_box_vs_chunk, pin_end_to_end_chunk,
             pin_gather, pin_raw_bits)
 
 

@@ -303,3 +303,32 @@ def test_two_stage_send_once_then_exchange(chunks):
                 assert torch.equal(got.cpu().view(torch.uint8), w.view(torch.uint8)), specs[t].name
     finally:
         ts.close()
+
+
+def test_hybrid_routing_matches_oracle():
+    """FFN projections by the reshard, the other weights by gather-then-slice,
+    all on one stream: every destination shard equals the oracle's."""
+    from dtensor_layout_movement_amd.hybrid import HybridPlan
+    from reshard_harness import oracle_dsts
+    specs = W.dense_layer_refit(2, 256, 64, 512).tensors
+    hp = HybridPlan(specs)
+    try:
+        srcs_d, dsts_d, wants = [], [], []
+        for t, spec in enumerate(specs):
+            g = W.make_global(spec, "raw", 41, t)
+            srcs = W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
+            wants.append(oracle_dsts(spec, srcs))
+            srcs_d.append([s.cuda() if s is not None else None for s in srcs])
+            dsts_d.append([torch.zeros_like(w, device="cuda") for w in wants[-1]])
+        glob = [torch.empty(sh, dtype=specs[t].dtype, device="cuda")
+                for t, sh in zip(hp.gather, hp.global_shapes())]
+        ptr = lambda lst: [[x.data_ptr() if x is not None and x.numel() else 0 for x in row] for row in lst]
+        arrays = hp.pointer_arrays(ptr(srcs_d), ptr(dsts_d), [g.data_ptr() for g in glob])
+        stream = torch.cuda.current_stream()
+        hp.execute(arrays, stream.cuda_stream)
+        torch.cuda.synchronize()
+        for t in range(len(specs)):
+            for got, w in zip(dsts_d[t], wants[t]):
+                assert torch.equal(got.cpu().view(torch.uint8), w.view(torch.uint8)), specs[t].name
+    finally:
+        hp.close()

@@ -40,6 +40,23 @@ def test_pin_raw_bits(oracle_lib):
     P.pin_raw_bits(oracle_lib)
 
 
+def test_pin_convert_library(oracle_lib):
+    P.pin_convert_library(oracle_lib)
+
+
+def test_pin_convert_closed(oracle_lib):
+    P.pin_convert_closed(oracle_lib)
+
+
+def test_convert_threads_and_errors(oracle_lib):
+    x = torch.randn(100_003, dtype=torch.float32)
+    a = oracle.convert(x, "f32", "bf16", threads=1, lib=oracle_lib)
+    b = oracle.convert(x, "f32", "bf16", threads=8, lib=oracle_lib)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    assert oracle_lib.oracle_convert(0, 3, None, None, 0, 1) == oracle.BAD_LAYOUT
+    assert oracle.convert(torch.empty(0), "f32", "f16", lib=oracle_lib).numel() == 0
+
+
 def test_nested_split_reading(oracle_lib):
     # Nested Shard on one dim splits the interval left by the outer mesh dim
     # (DTensor's rule), which differs from a flat 6-way split at rank (0, 1).
@@ -91,6 +108,15 @@ MUTANTS = {
                            "} else if (false) {"),
     "replicate_splits": ("if (p == kReplicate) continue;\n    int64_t n",
                          "if (p == kReplicate) p = 0;\n    int64_t n"),
+    # float conversion
+    "round_toward_zero": ("if (d > 0.5 || (d == 0.5 && std::fmod(r, 2.0) != 0)) r += 1;", "if (false) r += 1;"),
+    "ties_away_from_zero": ("(d == 0.5 && std::fmod(r, 2.0) != 0)", "(d == 0.5)"),
+    "no_subnormal_spacing": ("  if (E < 1 - f.bias) E = 1 - f.bias;   // subnormal range: fixed spacing", "  (void)0;"),
+    "no_overflow_to_inf": ("  if (y > max_finite(f)) y = INFINITY;", "  (void)0;"),
+    "f16_bias_16": ("    {16, 10, 15},   // 2: IEEE binary16", "    {16, 10, 16},   // 2: IEEE binary16"),
+    "nan_not_quiet": ("    m |= 1u << (to.frac - 1);  // quiet", "    m |= 0;"),
+    "nan_sign_dropped": ("return (sign << (to.bits - 1)) | (exp_all_ones(to) << to.frac) | m;",
+                         "return (exp_all_ones(to) << to.frac) | m;"),
 }
 
 

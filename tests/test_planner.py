@@ -456,3 +456,31 @@ def test_two_stage_layout_slices_tile_each_box(wl):
         for (dlo, dhi), vol in covered.items():
             assert vol == int(np.prod([max(0, h - l) for l, h in zip(dlo, dhi)]))
         assert sorted(rank_map) == list(range(int(np.prod(spec.dst_mesh))))
+
+
+def test_hybrid_routing_bytes():
+    """Hybrid refit: FFN projections by the reshard (G(1+R) bytes each), the
+    rest by gather-then-slice (source reads + one full write, then a full read
+    per destination box plus every destination write)."""
+    from dtensor_layout_movement_amd.hybrid import HybridPlan
+    wl = W.dense_layer_refit(2, 256, 64, 512)
+    hp = HybridPlan(wl.tensors)
+    try:
+        names = [wl.tensors[t].name.split(".")[1] for t in hp.direct]
+        assert sorted(set(names)) == ["down", "gate", "up"] and len(hp.direct) == 6
+        assert len(hp.gather) == 12
+        want = 0
+        for t, spec in enumerate(wl.tensors):
+            g = int(np.prod(spec.shape)) * 2
+            if t in hp.direct:
+                want += g * (1 + 2)                # read once, written to both replicas
+            else:
+                unique = 1 if len(spec.shape) == 1 else 4
+                r = 8 // unique
+                want += 2 * g + g + g * r          # gather: read + write G; slice: read G, write G*R
+        assert hp.bytes_moved() == want
+        ffn = sum(int(np.prod(wl.tensors[t].shape)) for t in hp.direct)
+        allb = sum(int(np.prod(s.shape)) for s in wl.tensors)
+        assert abs(hp.reshard_share() - ffn / allb) < 1e-12
+    finally:
+        hp.close()
