@@ -59,6 +59,11 @@ def kernel_source_sha() -> str:
     return h.hexdigest()[:16]
 
 
+def dtype_name(dt) -> str:
+    return {"bfloat16": "bf16", "float32": "f32", "float16": "f16", "float64": "f64",
+            "uint8": "u8"}.get(str(dt).replace("torch.", ""), str(dt).replace("torch.", ""))
+
+
 def layout_str(mesh, placements) -> str:
     pl = ",".join("R" if p < 0 else f"S{p}" for p in placements)
     return f"({','.join(str(m) for m in mesh)})[{pl}]"
@@ -86,9 +91,8 @@ def traffic_from_profile(workload: str):
 def build_plan(R, wl):
     srcs, dsts = [], []
     for t in wl.tensors:
-        code = R.dtype_code(t.dtype)
-        srcs.append(R.reshard_layout_create(t.shape, code, t.src_mesh, t.src_placements))
-        dsts.append(R.reshard_layout_create(t.shape, code, t.dst_mesh, t.dst_placements))
+        srcs.append(R.reshard_layout_create(t.shape, R.dtype_code(t.dtype), t.src_mesh, t.src_placements))
+        dsts.append(R.reshard_layout_create(t.shape, R.dtype_code(t.out_dtype), t.dst_mesh, t.dst_placements))
     plan = R.reshard_plan_create_batched(srcs, dsts)
     return plan, srcs, dsts
 
@@ -135,7 +139,7 @@ def alloc_set(torch, R, wl, lay_src, lay_dst, dev, seed):
         del g
         for lo, hi in dboxes:
             shape = [max(0, h - l) for l, h in zip(lo, hi)]
-            dst_bufs.append(torch.empty(shape, dtype=spec.dtype, device=dev) if all(shape) else None)
+            dst_bufs.append(torch.empty(shape, dtype=spec.out_dtype, device=dev) if all(shape) else None)
     sp = R.pointer_array([b.data_ptr() if b is not None else 0 for b in src_bufs])
     dp = R.pointer_array([b.data_ptr() if b is not None else 0 for b in dst_bufs])
     return src_bufs, dst_bufs, sp, dp
@@ -189,7 +193,7 @@ def two_stage(torch, wl, sets_boxes, steps: int, reshard_ms: float, chunks: int 
     from dtensor_layout_movement_amd.two_stage import TwoStagePlan
     ts = TwoStagePlan(wl.tensors, chunks=chunks)
     try:
-        staging = [[torch.empty(sh, dtype=spec.dtype, device="cuda") if all(sh) else None
+        staging = [[torch.empty(sh, dtype=spec.out_dtype, device="cuda") if all(sh) else None
                     for sh in shapes] for spec, shapes in zip(wl.tensors, ts.staging_shapes())]
         stag_ptrs = [[x.data_ptr() if x is not None else 0 for x in row] for row in staging]
         arrays = [ts.pointer_arrays(sp, stag_ptrs, dp) for sp, dp in sets_boxes]
@@ -422,7 +426,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": str(spec0.dtype).replace("torch.", "").replace("bfloat16", "bf16").replace("float32", "f32"),
+        "dtype": dtype_name(spec0.dtype) + ("" if spec0.out_dtype == spec0.dtype else "->" + dtype_name(spec0.out_dtype)),
         "data": "synthetic",
         "config": {
             "workload": wl.name,

@@ -35,6 +35,19 @@ int64_t elem_size_of(int dtype) {
   }
 }
 
+}  // namespace
+
+int conversion_of(int src_dtype, int dst_dtype) {
+  if (src_dtype == dst_dtype) return 0;
+  if (src_dtype == RESHARD_DTYPE_F32 && dst_dtype == RESHARD_DTYPE_BF16) return RESHARD_CONVERT_F32_BF16;
+  if (src_dtype == RESHARD_DTYPE_F32 && dst_dtype == RESHARD_DTYPE_F16) return RESHARD_CONVERT_F32_F16;
+  if (src_dtype == RESHARD_DTYPE_BF16 && dst_dtype == RESHARD_DTYPE_F32) return RESHARD_CONVERT_BF16_F32;
+  if (src_dtype == RESHARD_DTYPE_F16 && dst_dtype == RESHARD_DTYPE_F32) return RESHARD_CONVERT_F16_F32;
+  return -1;
+}
+
+namespace {
+
 bool same_box(int ndim, const Box& a, const Box& b) {
   for (int k = 0; k < ndim; ++k)
     if (a.lo[k] != b.lo[k] || a.hi[k] != b.hi[k]) return false;
@@ -219,14 +232,80 @@ void emit(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_begin, uin
   P->descs.push_back(D);
 }
 
+// RESHARD_DESC_CONVERT descriptors for rows of `run` elements (outer dims
+// inner -> outer, byte strides of each side), split like emit() does.
+void emit_convert(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_begin, uint32_t fanout,
+                  int64_t src_off, int64_t dst_off, int64_t run, Dims outer, int conv, int64_t es_s,
+                  int64_t es_d) {
+  if (outer.size() > 3) {
+    Dim top = outer.back();
+    outer.pop_back();
+    for (int64_t i = 0; i < top.e; ++i)
+      emit_convert(P, piece, src_ptr, ref_begin, fanout, src_off + i * top.ss, dst_off + i * top.sd,
+                   run, outer, conv, es_s, es_d);
+    return;
+  }
+  const int64_t max_run = kMaxRunBytes / 4;  // elements: every row stays under kMaxRunBytes per side
+  if (run > max_run) {
+    for (int64_t c = 0; c < run; c += max_run)
+      emit_convert(P, piece, src_ptr, ref_begin, fanout, src_off + c * es_s, dst_off + c * es_d,
+                   std::min<int64_t>(max_run, run - c), outer, conv, es_s, es_d);
+    return;
+  }
+  const uint64_t row_items = uint64_t(run + kConvertElems - 1) / kConvertElems;
+  uint64_t rows = 1;
+  for (const Dim& d : outer) rows *= uint64_t(d.e);
+  if (rows * row_items > kMaxItems) {  // halve the outermost dim with extent > 1
+    for (int k = int(outer.size()) - 1; k >= 0; --k) {
+      if (outer[k].e < 2) continue;
+      Dims a = outer, b = outer;
+      const int64_t h = outer[k].e / 2;
+      a[k].e = h;
+      b[k].e = outer[k].e - h;
+      emit_convert(P, piece, src_ptr, ref_begin, fanout, src_off, dst_off, run, a, conv, es_s, es_d);
+      emit_convert(P, piece, src_ptr, ref_begin, fanout, src_off + h * outer[k].ss,
+                   dst_off + h * outer[k].sd, run, b, conv, es_s, es_d);
+      return;
+    }
+  }
+  reshard_descriptor_t D;
+  std::memset(&D, 0, sizeof(D));
+  D.src_offset = src_off;
+  D.dst_offset = dst_off;
+  for (int j = 0; j < 3; ++j) {
+    const int slot = 2 - j;
+    if (j < int(outer.size())) {
+      D.extent[slot] = uint32_t(outer[j].e);
+      D.src_stride[slot] = outer[j].ss;
+      D.dst_stride[slot] = outer[j].sd;
+    } else {
+      D.extent[slot] = 1;
+    }
+  }
+  D.run_bytes = uint32_t(run);
+  D.row_items = uint32_t(row_items);
+  D.unit = uint16_t(conv);
+  D.mode = RESHARD_DESC_CONVERT;
+  D.src_ptr = src_ptr;
+  D.dst_ref_begin = ref_begin;
+  D.fanout = fanout;
+  magic_u31(D.row_items, &D.magic[0][0], &D.magic[0][1]);
+  magic_u31(D.extent[2], &D.magic[1][0], &D.magic[1][1]);
+  magic_u31(D.extent[1], &D.magic[2][0], &D.magic[2][1]);
+  D.piece = piece;
+  P->descs.push_back(D);
+}
+
 // Turns one overlap into descriptors: local offsets in the source and
 // destination shards, then adjacent dims are merged wherever both sides are
-// contiguous across them, and size-1 dims are dropped.
+// contiguous across them, and size-1 dims are dropped.  Merging works in
+// elements; strides become bytes of each side's dtype (they differ only for a
+// converting reshard, conv != 0).
 void describe_piece(HostPlan* P, uint32_t piece_idx, uint32_t src_ptr, uint32_t ref_begin,
                     uint32_t fanout, const Box& piece, const Box& sbox, const Box& dbox, int ndim,
-                    int64_t es) {
-  int64_t s_stride[kMaxDims], d_stride[kMaxDims];
-  int64_t ss = es, sd = es;
+                    int64_t es_s, int64_t es_d, int conv) {
+  int64_t s_stride[kMaxDims], d_stride[kMaxDims];  // elements
+  int64_t ss = 1, sd = 1;
   for (int k = ndim - 1; k >= 0; --k) {
     s_stride[k] = ss;
     d_stride[k] = sd;
@@ -241,13 +320,13 @@ void describe_piece(HostPlan* P, uint32_t piece_idx, uint32_t src_ptr, uint32_t 
   // Fold dims from the innermost outwards into the contiguous run while both
   // sides stay contiguous; the rest become outer dims.
   bool in_run = true;
-  int64_t run_bytes = es;
-  Dims outer;  // inner -> outer
+  int64_t run = 1;  // elements
+  Dims outer;       // inner -> outer
   for (int k = ndim - 1; k >= 0; --k) {
     int64_t e = piece.hi[k] - piece.lo[k];
     if (e == 1) continue;
-    if (in_run && s_stride[k] == run_bytes && d_stride[k] == run_bytes) {
-      run_bytes *= e;
+    if (in_run && s_stride[k] == run && d_stride[k] == run) {
+      run *= e;
       continue;
     }
     in_run = false;
@@ -258,13 +337,22 @@ void describe_piece(HostPlan* P, uint32_t piece_idx, uint32_t src_ptr, uint32_t 
     }
     outer.push_back(Dim{e, s_stride[k], d_stride[k]});
   }
-  emit(P, piece_idx, src_ptr, ref_begin, fanout, src_off, dst_off, run_bytes, outer);
+  for (int j = 0; j < outer.n; ++j) {
+    outer[j].ss *= es_s;
+    outer[j].sd *= es_d;
+  }
+  if (conv == 0)
+    emit(P, piece_idx, src_ptr, ref_begin, fanout, src_off * es_s, dst_off * es_d, run * es_s, outer);
+  else
+    emit_convert(P, piece_idx, src_ptr, ref_begin, fanout, src_off * es_s, dst_off * es_d, run, outer,
+                 conv, es_s, es_d);
 }
 
 // Copy descriptors of every piece of one tensor, in piece order.
 void emit_pieces(HostPlan* P, int t, size_t pc0, size_t pc1) {
   const int nd = P->src[t].ndim;
-  const int64_t es = P->src[t].elem_size;
+  const int64_t es_s = P->src[t].elem_size, es_d = P->dst[t].elem_size;
+  const int conv = P->conv[t];
   for (size_t i = pc0; i < pc1; ++i) {
     const Piece& pc = P->pieces[i];
     const Group& sgrp = P->src_groups[pc.src_group];
@@ -272,7 +360,7 @@ void emit_pieces(HostPlan* P, int t, size_t pc0, size_t pc1) {
     const uint32_t ref_begin = uint32_t(P->refs.size());
     for (int64_t r : dgrp.ranks) P->refs.push_back(uint32_t(P->dst_base[t] + r));
     describe_piece(P, uint32_t(i), uint32_t(P->src_base[t] + pc.src_rank), ref_begin,
-                   uint32_t(dgrp.ranks.size()), pc.box, sgrp.box, dgrp.box, nd, es);
+                   uint32_t(dgrp.ranks.size()), pc.box, sgrp.box, dgrp.box, nd, es_s, es_d, conv);
   }
 }
 
@@ -413,6 +501,7 @@ void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1) {
   if (pc0 == pc1) return;
   const size_t d0 = P->descs.size(), r0 = P->refs.size();
   emit_pieces(P, t, pc0, pc1);
+  if (P->conv[t] != 0) return;  // converting rows always go element-group by element-group
   bool narrow = false;
   for (size_t i = d0; i < P->descs.size(); ++i) {
     const reshard_descriptor_t& D = P->descs[i];
@@ -544,11 +633,17 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
     }
     const Layout& S = *src[t];
     const Layout& D = *dst[t];
-    if (S.ndim != D.ndim || S.elem_size != D.elem_size || S.dtype != D.dtype ||
-        !std::equal(S.shape, S.shape + S.ndim, D.shape)) {
-      *err = "tensor " + std::to_string(t) + ": source and destination differ in global shape or dtype";
+    if (S.ndim != D.ndim || !std::equal(S.shape, S.shape + S.ndim, D.shape)) {
+      *err = "tensor " + std::to_string(t) + ": source and destination differ in global shape";
       return RESHARD_ERR_LAYOUT_MISMATCH;
     }
+    const int conv = conversion_of(S.dtype, D.dtype);
+    if (conv < 0) {
+      *err = "tensor " + std::to_string(t) + ": no conversion from dtype " + std::to_string(S.dtype) +
+             " to dtype " + std::to_string(D.dtype);
+      return RESHARD_ERR_LAYOUT_MISMATCH;
+    }
+    P->conv.push_back(conv);
     P->src.push_back(S);
     P->dst.push_back(D);
     P->src_base.push_back(P->n_src_ptrs);
@@ -625,7 +720,7 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
           P->pieces.push_back(Piece{t, best, sg, int64_t(g), box, bytes});
           const int64_t fanout = int64_t(dgrp.ranks.size());
           P->bytes_read += bytes;
-          P->bytes_written += bytes * fanout;
+          P->bytes_written += box_numel(nd, box) * D.elem_size * fanout;
           P->n_dst_writes += fanout;
         }
         int k = nd - 1;

@@ -38,6 +38,10 @@ struct Box {
   int64_t hi[kMaxDims];
 };
 
+// Conversion code (RESHARD_CONVERT_*) from src_dtype to dst_dtype: 0 when the
+// dtypes are equal, -1 when the pair is not supported.
+int conversion_of(int src_dtype, int dst_dtype);
+
 // Validates and fills a layout; returns false with a message on bad input.
 bool make_layout(int ndim, const int64_t* shape, int dtype, int mesh_ndim, const int64_t* mesh,
                  const int32_t* placements, Layout* out, std::string* err);
@@ -85,6 +89,9 @@ constexpr uint32_t kWindowBytes = 16384;
 constexpr uint32_t kWindowMaxSegs = 64;
 constexpr int64_t kWindowMaxRun = 128;
 
+// Elements per item of a RESHARD_DESC_CONVERT row.
+constexpr uint32_t kConvertElems = RESHARD_CONVERT_ELEMS;
+
 // Tiles of one descriptor.
 inline uint64_t desc_tiles(const reshard_descriptor_t& D) {
   if (D.mode == RESHARD_DESC_WINDOW) return (uint64_t(D.extent[0]) + D.extent[1] - 1) / D.extent[1];
@@ -95,6 +102,7 @@ inline uint64_t desc_tiles(const reshard_descriptor_t& D) {
 struct HostPlan {
   int n_tensors = 0;
   std::vector<Layout> src, dst;
+  std::vector<int> conv;                     // per tensor: RESHARD_CONVERT_* or 0
   std::vector<int64_t> src_base, dst_base;  // first pointer-array slot of each tensor
   int64_t n_src_ptrs = 0, n_dst_ptrs = 0;
   std::vector<uint8_t> src_needed, dst_needed;  // 1 if that pointer slot holds a non-empty shard

@@ -513,6 +513,119 @@ __device__ void copy_bytes(const reshard_descriptor_t& D, uint32_t unit, uint32_
 // Bits of the kernel's `flags` argument.
 constexpr uint32_t kAllAligned16 = 1;  // every shard pointer of this execute is 16-byte aligned
 
+// ---------------------------------------------------------------- conversion
+//
+// Float conversions of a RESHARD_DESC_CONVERT descriptor, on bit patterns with
+// integer operations only (no dependence on the hardware's rounding mode).
+// Narrowing rounds to nearest, ties to even: adding 2^(k-1) - 1 plus the last
+// kept bit and dropping the k low bits rounds the magnitude that way, and a
+// carry out of the fraction lands in the exponent, up to infinity.  A NaN keeps
+// its sign and leading payload bits and gets the quiet bit.
+
+__device__ __forceinline__ uint32_t f32_to_bf16(uint32_t u) {
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
+  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ uint32_t f32_to_f16(uint32_t u) {
+  const uint32_t sign = (u >> 16) & 0x8000u, a = u & 0x7fffffffu;
+  if (a > 0x7f800000u) return sign | 0x7e00u | ((a >> 13) & 0x3ffu);
+  if (a >= 0x477ff000u) return sign | 0x7c00u;  // rounds past 65504: infinity
+  if (a >= 0x38800000u)                         // normal binary16 (>= 2^-14): rebias 127 -> 15
+    return sign | (((a + 0xfffu + ((a >> 13) & 1u)) >> 13) - (112u << 10));
+  // below 2^-14: a multiple of 2^-24 (subnormal), rounded to nearest even
+  const uint32_t e = a >> 23;
+  if (e < 102) return sign;  // below 2^-25: rounds to zero
+  const uint32_t m = (a & 0x7fffffu) | 0x800000u, sh = 126u - e;  // value = m * 2^(e - 150)
+  const uint32_t q = m >> sh, rem = m & ((1u << sh) - 1u), half = 1u << (sh - 1u);
+  return sign | (q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u));
+}
+
+__device__ __forceinline__ uint32_t bf16_to_f32(uint32_t h) {
+  const uint32_t u = h << 16;
+  return (u & 0x7fffffffu) > 0x7f800000u ? u | 0x00400000u : u;
+}
+
+__device__ __forceinline__ uint32_t f16_to_f32(uint32_t h) {
+  const uint32_t sign = (h & 0x8000u) << 16, e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
+  if (e == 0x1fu) return sign | 0x7f800000u | (m << 13) | (m ? 0x00400000u : 0u);
+  if (e != 0) return sign | ((e + 112u) << 23) | (m << 13);
+  if (m == 0) return sign;
+  const uint32_t p = 31u - __clz(m);  // subnormal m * 2^-24: leading bit at p < 10
+  return sign | ((p + 103u) << 23) | ((m << (23u - p)) & 0x7fffffu);
+}
+
+template <int kConv>
+__device__ __forceinline__ uint32_t convert_elem(uint32_t x) {
+  if constexpr (kConv == RESHARD_CONVERT_F32_BF16) return f32_to_bf16(x);
+  else if constexpr (kConv == RESHARD_CONVERT_F32_F16) return f32_to_f16(x);
+  else if constexpr (kConv == RESHARD_CONVERT_BF16_F32) return bf16_to_f32(x);
+  else return f16_to_f32(x);
+}
+
+// CONVERT mode: item f is up to 8 elements of a row.  A full item whose source
+// and destination are 16-byte aligned moves as 16-byte accesses (32 bytes of
+// fp32 in, 16 of 16-bit out, or the reverse); anything else element by element.
+template <int kConv, class Sh>
+__device__ __forceinline__ void convert_items(const reshard_descriptor_t& D, const uint8_t* src,
+                                              const Sh& sh, uint32_t lo, uint32_t hi, bool aligned) {
+  constexpr bool kNarrow = kConv == RESHARD_CONVERT_F32_BF16 || kConv == RESHARD_CONVERT_F32_F16;
+  constexpr uint32_t kEs = kNarrow ? 4 : 2, kEd = kNarrow ? 2 : 4;
+  const uint32_t f = lo + threadIdx.x;
+  if (f >= hi) return;
+  const ItemPos o = item_pos(D, f);
+  const uint32_t e0 = o.col * rs::kConvertElems;
+  const uint32_t n = min(rs::kConvertElems, D.run_bytes - e0);
+  const uintptr_t s = reinterpret_cast<uintptr_t>(src) + o.src + uint64_t(e0) * kEs;
+  const uint64_t doff = o.dst + uint64_t(e0) * kEd;
+  if (aligned && n == rs::kConvertElems && ((s | doff) & 15) == 0) {
+    uint32_t x[8];
+    if constexpr (kNarrow) {
+      const u32x4 a = __builtin_nontemporal_load(as_global<const u32x4>(s));
+      const u32x4 b = __builtin_nontemporal_load(as_global<const u32x4>(s + 16));
+      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+    } else {
+      const u32x4 a = __builtin_nontemporal_load(as_global<const u32x4>(s));
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = w[k] & 0xffffu;
+        x[2 * k + 1] = w[k] >> 16;
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = convert_elem<kConv>(x[k]);
+    for (uint32_t r = 0; r < D.fanout; ++r) {
+      const uintptr_t d = sh.dst(r) + doff;
+      if constexpr (kNarrow) {
+        const u32x4 v{x[0] | (x[1] << 16), x[2] | (x[3] << 16), x[4] | (x[5] << 16), x[6] | (x[7] << 16)};
+        __builtin_nontemporal_store(v, as_global<u32x4>(d));
+      } else {
+        __builtin_nontemporal_store(u32x4{x[0], x[1], x[2], x[3]}, as_global<u32x4>(d));
+        __builtin_nontemporal_store(u32x4{x[4], x[5], x[6], x[7]}, as_global<u32x4>(d + 16));
+      }
+    }
+    return;
+  }
+  uint32_t x[8];
+#pragma unroll
+  for (uint32_t k = 0; k < 8; ++k) {
+    if (k >= n) break;
+    if constexpr (kNarrow) x[k] = convert_elem<kConv>(*as_global<const u32_u>(s + 4 * k));
+    else x[k] = convert_elem<kConv>(*as_global<const u16_u>(s + 2 * k));
+  }
+  for (uint32_t r = 0; r < D.fanout; ++r) {
+    const uintptr_t d = sh.dst(r) + doff;
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) {
+      if (k >= n) break;
+      if constexpr (kNarrow) *as_global<u16_u>(d + 2 * k) = uint16_t(x[k]);
+      else *as_global<u32_u>(d + 4 * k) = x[k];
+    }
+  }
+}
+
 template <bool kKarg>
 __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     const reshard_descriptor_t* __restrict__ descs, uint32_t n_desc,
@@ -547,6 +660,16 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t last = min(first + rs::kTileItems, items);
   const Shards<kKarg> sh{table, &karg, refs + D.dst_ref_begin};
   const uint8_t* src = reinterpret_cast<const uint8_t*>(sh.ptr(D.src_ptr));
+  if (mode == RESHARD_DESC_CONVERT) {  // checks its own alignment per item
+    const bool aligned = (flags & kAllAligned16) != 0;
+    switch (unit) {
+      case RESHARD_CONVERT_F32_BF16: convert_items<RESHARD_CONVERT_F32_BF16>(D, src, sh, first, last, aligned); break;
+      case RESHARD_CONVERT_F32_F16: convert_items<RESHARD_CONVERT_F32_F16>(D, src, sh, first, last, aligned); break;
+      case RESHARD_CONVERT_BF16_F32: convert_items<RESHARD_CONVERT_BF16_F32>(D, src, sh, first, last, aligned); break;
+      default: convert_items<RESHARD_CONVERT_F16_F32>(D, src, sh, first, last, aligned); break;
+    }
+    return;
+  }
   if (!(flags & kAllAligned16)) {
     // alignment every access width relies on: the unit for ITEMS; for
     // DST_CHUNKS, replicas in the same 16-byte phase as replica 0

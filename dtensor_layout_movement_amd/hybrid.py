@@ -37,8 +37,9 @@ class HybridPlan:
         src, dst, glob = {}, {}, {}
         for t, spec in enumerate(self.specs):
             code = R.dtype_code(spec.dtype)
+            out = R.dtype_code(getattr(spec, "out_dtype", spec.dtype))
             src[t] = R.reshard_layout_create(spec.shape, code, spec.src_mesh, spec.src_placements)
-            dst[t] = R.reshard_layout_create(spec.shape, code, spec.dst_mesh, spec.dst_placements)
+            dst[t] = R.reshard_layout_create(spec.shape, out, spec.dst_mesh, spec.dst_placements)
             self._layouts += [src[t], dst[t]]
             if t in self.gather:
                 glob[t] = R.reshard_layout_create(spec.shape, code, (1,), (R.REPLICATE,))

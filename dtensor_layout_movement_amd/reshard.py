@@ -38,6 +38,13 @@ DTYPE_F64, DTYPE_I64 = 10, 11
 DESC_ITEMS = 0       # rows of items of `unit` bytes
 DESC_DST_CHUNKS = 1  # rows cut into destination-aligned 16-byte chunks
 DESC_WINDOW = 2      # a band of rows staged through an LDS window
+DESC_CONVERT = 3     # rows of elements converted to another float format (run in elements)
+
+# conversions: the `unit` of a DESC_CONVERT descriptor
+CONVERT_F32_BF16 = 1
+CONVERT_F32_F16 = 2
+CONVERT_BF16_F32 = 3
+CONVERT_F16_F32 = 4
 
 EXPORTED = (
     "reshard_dtype_size", "reshard_layout_create", "reshard_layout_destroy",

@@ -76,10 +76,11 @@ class TwoStagePlan:
         self.src_l, self.mid_l, self.dst_l, self.mid_map = [], [], [], []
         for spec in self.specs:
             code = R.dtype_code(spec.dtype)
+            out = R.dtype_code(getattr(spec, "out_dtype", spec.dtype))  # a conversion happens in stage 1
             m1, p1, rank_map = stage1_layout(spec.dst_mesh, spec.dst_placements)
             s = R.reshard_layout_create(spec.shape, code, spec.src_mesh, spec.src_placements)
-            m = R.reshard_layout_create(spec.shape, code, m1, p1)
-            d = R.reshard_layout_create(spec.shape, code, spec.dst_mesh, spec.dst_placements)
+            m = R.reshard_layout_create(spec.shape, out, m1, p1)
+            d = R.reshard_layout_create(spec.shape, out, spec.dst_mesh, spec.dst_placements)
             self._layouts += [s, m, d]
             self.src_l.append(s)
             self.mid_l.append(m)

@@ -47,6 +47,12 @@ class TensorSpec:
     src_placements: tuple
     dst_mesh: tuple
     dst_placements: tuple
+    dst_dtype: torch.dtype | None = None  # another float format: a converting reshard
+
+    @property
+    def out_dtype(self) -> torch.dtype:
+        """Element type of the destination shards."""
+        return self.dst_dtype if self.dst_dtype is not None else self.dtype
 
 
 @dataclass(frozen=True)
@@ -135,6 +141,15 @@ def dense_layer_refit(layers: int = 32, hidden: int = 4096, kv: int = 1024, ffn:
                     f"one fused launch")
 
 
+def ffn_up_f32_to_bf16(rows: int = 14336, cols: int = 4096) -> Workload:
+    """The ffn_up layouts with a precision change on the way: fp32 training
+    weights, TP4 over rows, to bf16 inference weights, DP2 x TP2 over columns
+    (each element converted once per destination replica)."""
+    t = TensorSpec("up_proj", (rows, cols), torch.float32, (4,), (0,), (2, 2), (R, 1), torch.bfloat16)
+    return Workload(f"ffn_up_f32_to_bf16_{rows}x{cols}", (t,), "normal",
+                    f"{rows}x{cols} fp32 N(0,0.02) (4,)[S0] -> bf16 (2,2)[R,S1]")
+
+
 def stage_of_layer(layer: int, layers: int = 32, stages: int = 4) -> int:
     """Pipeline stage holding `layer` (contiguous blocks of layers per stage)."""
     return layer * stages // layers
@@ -156,6 +171,7 @@ WORKLOADS = {
     "uneven_5000x3001": uneven,
     "ffn_refit_32_layers": ffn_refit,
     "narrow_columns_4194304x8": narrow_columns,
+    "ffn_up_f32_to_bf16_14336x4096": ffn_up_f32_to_bf16,
     "dense_layer_refit_32_layers": dense_layer_refit,
 }
 

@@ -29,7 +29,18 @@
  *   - each local shard is a contiguous row-major buffer whose shape is the
  *     extent of its box (reshard_layout_shard_box).
  * The copy is bytewise: bf16/fp32 NaN payloads, -0.0 and subnormals arrive
- * unchanged.  Source and destination dtypes must match.
+ * unchanged.  Source and destination dtypes match, or the pair is one of the
+ * float conversions below.
+ *
+ * Converting reshard.  The pages mention that the refit supports precision
+ * modes and say nothing more (the news.bpdata.com and techfeed.io write-ups,
+ * closing remarks on the refit guide).  The reading taken: a destination layout
+ * may hold another float format than the source (say fp32 training weights,
+ * bf16 inference weights).  Supported pairs: F32 -> BF16, F32 -> F16 (round to
+ * nearest, ties to even, overflow to infinity) and BF16 -> F32, F16 -> F32
+ * (exact).  A NaN stays a NaN with its sign and leading payload bits and with
+ * the quiet bit set.  Conversion happens in the copy kernel, element by element,
+ * once per destination element; everything else is as for a plain reshard.
  *
  * Errors.  Every call returns a reshard_status_t and never throws; on failure
  * reshard_last_error() gives a message for the calling thread.
@@ -51,14 +62,15 @@ extern "C" {
 typedef enum reshard_status {
   RESHARD_OK = 0,
   RESHARD_ERR_INVALID_ARGUMENT = 1, /* bad shape, mesh, placement, dtype, rank or NULL out-pointer */
-  RESHARD_ERR_LAYOUT_MISMATCH = 2,  /* source and destination disagree on global shape or dtype */
+  RESHARD_ERR_LAYOUT_MISMATCH = 2,  /* source and destination disagree on global shape, or on dtype
+                                       outside the supported conversions */
   RESHARD_ERR_NULL_SHARD = 3,       /* NULL pointer passed for a non-empty shard */
   RESHARD_ERR_OUT_OF_MEMORY = 4,    /* host or device allocation failed */
   RESHARD_ERR_HIP = 5,              /* a HIP runtime call failed (no device, launch error, ...) */
   RESHARD_ERR_DEVICE_MISMATCH = 6,  /* executed on a device other than the plan's */
 } reshard_status_t;
 
-/* Element types.  Only the element size matters to the copy. */
+/* Element types.  Only the element size matters to a copy without conversion. */
 typedef enum reshard_dtype {
   RESHARD_DTYPE_U8 = 0,
   RESHARD_DTYPE_I8 = 1,
@@ -84,9 +96,10 @@ typedef struct reshard_plan_stats {
   int64_t n_dst_ptrs;     /* length of the dst_ptrs array reshard_execute expects */
   int64_t n_pieces;       /* source box x unique destination box overlaps */
   int64_t n_dst_writes;   /* sum over pieces of their destination fan-out */
-  int64_t global_bytes;   /* sum over tensors of the global tensor's bytes (G) */
+  int64_t global_bytes;   /* sum over tensors of the global tensor's bytes in the source dtype (G) */
   int64_t bytes_read;     /* bytes the kernel reads  (= G: each element once) */
-  int64_t bytes_written;  /* bytes the kernel writes (= sum of destination shard bytes) */
+  int64_t bytes_written;  /* bytes the kernel writes (= sum of destination shard bytes, in the
+                             destination dtype) */
   int64_t n_descriptors;  /* device copy descriptors after dim merging / splitting */
   int64_t table_bytes;    /* size of the device-resident descriptor table */
   int64_t n_workgroups;   /* grid of one execute launch: one workgroup per tile (0 until upload) */
@@ -108,6 +121,14 @@ typedef struct reshard_piece {
 #define RESHARD_DESC_ITEMS 0      /* rows of items of `unit` bytes (unit = 16, or short rows) */
 #define RESHARD_DESC_DST_CHUNKS 1 /* rows cut into 16-byte chunks aligned to the destination */
 #define RESHARD_DESC_WINDOW 2     /* a band of rows staged through LDS (see below) */
+#define RESHARD_DESC_CONVERT 3    /* rows of elements converted to another float format */
+
+/* Conversions (the `unit` field of a RESHARD_DESC_CONVERT descriptor). */
+#define RESHARD_CONVERT_F32_BF16 1
+#define RESHARD_CONVERT_F32_F16 2
+#define RESHARD_CONVERT_BF16_F32 3
+#define RESHARD_CONVERT_F16_F32 4
+#define RESHARD_CONVERT_ELEMS 8   /* elements per item of a RESHARD_DESC_CONVERT row */
 
 /*
  * Device copy descriptor (the table the kernel reads; inspection API).
@@ -130,6 +151,11 @@ typedef struct reshard_piece {
  *                            read into the window) followed by `fanout` destination
  *                            segments (written from it); offsets and strides are
  *                            ignored.  Used for narrow or misaligned pieces.
+ *   RESHARD_DESC_CONVERT     rows of `run_bytes` ELEMENTS (not bytes) converted by
+ *                            conversion `unit`; item c is elements
+ *                            [c*8, min(c*8+8, run)) of the row; row_items =
+ *                            ceil(run / 8).  Offsets and strides are in bytes of
+ *                            each side's own dtype.
  */
 typedef struct reshard_descriptor {
   int64_t src_offset;       /* byte offset of the row origin in the source shard */
@@ -137,10 +163,11 @@ typedef struct reshard_descriptor {
   int64_t src_stride[3];    /* bytes, outer dims; unused dims have extent 1 */
   int64_t dst_stride[3];
   uint32_t extent[3];       /* outer extents; product = rows */
-  uint32_t run_bytes;       /* contiguous bytes per row, both sides */
+  uint32_t run_bytes;       /* contiguous bytes per row, both sides (CONVERT: elements) */
   uint32_t row_items;       /* items the kernel indexes per row (see the modes) */
-  uint16_t unit;            /* item size (ITEMS) or natural alignment (DST_CHUNKS) */
-  uint16_t mode;            /* RESHARD_DESC_ITEMS or RESHARD_DESC_DST_CHUNKS */
+  uint16_t unit;            /* item size (ITEMS), natural alignment (DST_CHUNKS, WINDOW) or
+                               conversion (CONVERT) */
+  uint16_t mode;            /* RESHARD_DESC_* */
   uint32_t src_ptr;         /* index into the execute's source pointer array */
   uint32_t dst_ref_begin;   /* first entry of this descriptor's fan-out list */
   uint32_t fanout;          /* destination pointers written */
@@ -191,7 +218,7 @@ reshard_status_t reshard_layout_shard_box(reshard_layout_t layout, int64_t rank,
 
 /*
  * Plan the reshard of one tensor from layout src to layout dst (same global
- * shape and dtype).  Host-only: intersects every source box with every unique
+ * shape; same dtype or a supported conversion).  Host-only: intersects every source box with every unique
  * destination box, picks one source replica per overlap (least-loaded first),
  * merges contiguous dims and builds the descriptor table.  The layouts may be
  * destroyed afterwards.  The device table is uploaded by reshard_plan_upload or

@@ -55,9 +55,16 @@ def shard_nbytes(boxes, dtype):
     return out
 
 
-def run_parity(specs, values, seed, misalign=0, device="cuda", threads=8, executes=1):
+def run_parity(specs, values, seed, misalign=0, device="cuda", threads=8, executes=1, globals_=None):
     """Plan, fill guarded sources, execute through the C ABI, and compare every
-    destination shard bit for bit with the oracle.  Returns the plan stats."""
+    destination shard bit for bit with the oracle.  Returns the plan stats.
+    globals_: optional list of CPU global tensors (one per spec) used instead of
+    the seeded generator."""
+    def make(t, spec, dev):
+        if globals_ is not None:
+            return globals_[t].to(dev)
+        return W.make_global(spec, values, seed, t, device=dev)
+
     dev = torch.device(device)
     with Plan(specs) as plan:
         assert_boxes_agree(plan)
@@ -67,13 +74,13 @@ def run_parity(specs, values, seed, misalign=0, device="cuda", threads=8, execut
             sboxes = oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements)
             dboxes = oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements)
             srcs = GuardedShards(shard_nbytes(sboxes, spec.dtype), dev, misalign)
-            g = W.make_global(spec, values, seed, t, device=dev)
+            g = make(t, spec, dev)
             for i, piece in enumerate(W.cut(g, sboxes)):
                 if piece is not None:
                     srcs.region(i).copy_(piece.reshape(-1).view(torch.uint8))
             del g
             src_sets.append(srcs)
-            dst_sets.append(GuardedShards(shard_nbytes(dboxes, spec.dtype), dev, misalign))
+            dst_sets.append(GuardedShards(shard_nbytes(dboxes, spec.out_dtype), dev, misalign))
         src_ptrs = [p for s in src_sets for p in s.ptrs]
         dst_ptrs = [p for d in dst_sets for p in d.ptrs]
         print(f"[parity] {specs[0].name}{'+' if len(specs) > 1 else ''} values={values} seed={seed} "
@@ -82,7 +89,7 @@ def run_parity(specs, values, seed, misalign=0, device="cuda", threads=8, execut
             R.reshard_execute(plan.handle, src_ptrs, dst_ptrs, torch.cuda.current_stream().cuda_stream)
         torch.cuda.synchronize()
         for t, spec in enumerate(plan.specs):
-            g = W.make_global(spec, values, seed, t, device=dev).cpu()
+            g = make(t, spec, dev).cpu()
             srcs_cpu = W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
             del g
             want = oracle_dsts(spec, srcs_cpu, threads=threads)

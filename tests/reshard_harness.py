@@ -26,9 +26,10 @@ class Plan:
         self.specs = list(specs)
         self.src_layouts, self.dst_layouts = [], []
         for t in self.specs:
-            code = R.dtype_code(t.dtype)
-            self.src_layouts.append(R.reshard_layout_create(t.shape, code, t.src_mesh, t.src_placements))
-            self.dst_layouts.append(R.reshard_layout_create(t.shape, code, t.dst_mesh, t.dst_placements))
+            self.src_layouts.append(R.reshard_layout_create(t.shape, R.dtype_code(t.dtype), t.src_mesh,
+                                                            t.src_placements))
+            self.dst_layouts.append(R.reshard_layout_create(t.shape, R.dtype_code(t.out_dtype), t.dst_mesh,
+                                                            t.dst_placements))
         self.handle = R.reshard_plan_create_batched(self.src_layouts, self.dst_layouts)
 
     def src_boxes(self, t):
@@ -83,8 +84,12 @@ def box_shape(box):
     return [max(0, h - l) for l, h in zip(lo, hi)]
 
 
+FMT = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+
+
 def oracle_dsts(spec, srcs, threads=1):
-    """Destination shards by the oracle (gather-then-slice) from given sources."""
+    """Destination shards by the oracle (gather-then-slice) from given sources;
+    for a converting spec, each shard is then converted by the oracle."""
     boxes = oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements)
     dsts = [torch.empty(box_shape(b), dtype=spec.dtype) for b in boxes]
     oracle.reshard(list(spec.shape), torch.empty((), dtype=spec.dtype).element_size(),
@@ -92,6 +97,8 @@ def oracle_dsts(spec, srcs, threads=1):
                    [s if s is not None and s.numel() else None for s in srcs],
                    list(spec.dst_mesh), list(spec.dst_placements),
                    [d if d.numel() else None for d in dsts], threads=threads)
+    if spec.out_dtype != spec.dtype:
+        dsts = [oracle.convert(d, FMT[spec.dtype], FMT[spec.out_dtype], threads=threads) for d in dsts]
     return dsts
 
 
@@ -106,8 +113,8 @@ def apply_pieces(plan: Plan, srcs_per_tensor, fill=None):
     out = []
     for t, spec in enumerate(plan.specs):
         boxes = plan.dst_boxes(t)
-        out.append([torch.full(box_shape(b), 0, dtype=spec.dtype) if fill is None else
-                    torch.full(box_shape(b), fill, dtype=spec.dtype) for b in boxes])
+        out.append([torch.full(box_shape(b), 0 if fill is None else fill, dtype=spec.out_dtype)
+                    for b in boxes])
     sboxes = [plan.src_boxes(t) for t in range(len(plan.specs))]
     dboxes = [plan.dst_boxes(t) for t in range(len(plan.specs))]
     for i, pc in enumerate(R.reshard_plan_pieces(plan.handle)):
@@ -117,10 +124,14 @@ def apply_pieces(plan: Plan, srcs_per_tensor, fill=None):
         slo = sboxes[t][pc["src_rank"]][0]
         src = srcs_per_tensor[t][pc["src_rank"]]
         s_idx = tuple(slice(l - o, h - o) for l, h, o in zip(lo, hi, slo))
+        part = src[s_idx]
+        spec = plan.specs[t]
+        if spec.out_dtype != spec.dtype:
+            part = oracle.convert(part.contiguous(), FMT[spec.dtype], FMT[spec.out_dtype])
         for d in R.reshard_plan_piece_fanout(plan.handle, i):
             dlo = dboxes[t][d][0]
             d_idx = tuple(slice(l - o, h - o) for l, h, o in zip(lo, hi, dlo))
-            out[t][d][d_idx] = src[s_idx]
+            out[t][d][d_idx] = part
     return out
 
 
@@ -145,6 +156,9 @@ def run_descriptors(plan: Plan, srcs_flat, dsts_flat):
     for D in descs:
         if D["mode"] == R.DESC_WINDOW:
             _run_window(D, segs, refs, srcs_flat, dsts_flat)
+            continue
+        if D["mode"] == R.DESC_CONVERT:
+            _run_convert(D, refs, srcs_flat, dsts_flat)
             continue
         e0, e1, e2 = D["extent"]
         i0, i1, i2 = np.meshgrid(np.arange(e0), np.arange(e1), np.arange(e2), indexing="ij")
@@ -171,6 +185,38 @@ def run_descriptors(plan: Plan, srcs_flat, dsts_flat):
         data = srcs_flat[D["src_ptr"]][src_idx]
         for r in range(D["fanout"]):
             dsts_flat[refs[D["dst_ref_begin"] + r]][dst_idx] = data
+
+
+CONVERSIONS = {R.CONVERT_F32_BF16: ("f32", "bf16", 4, 2), R.CONVERT_F32_F16: ("f32", "f16", 4, 2),
+               R.CONVERT_BF16_F32: ("bf16", "f32", 2, 4), R.CONVERT_F16_F32: ("f16", "f32", 2, 4)}
+_TORCH = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def _run_convert(D, refs, srcs_flat, dsts_flat):
+    """A CONVERT descriptor element by element: items of 8 elements tile each
+    row of `run` elements; elements are converted by the oracle."""
+    fs, fd, es, ed = CONVERSIONS[D["unit"]]
+    run, n = D["run_bytes"], D["row_items"]
+    assert n == (run + 7) // 8
+    e0, e1, e2 = D["extent"]
+    i0, i1, i2 = np.meshgrid(np.arange(e0), np.arange(e1), np.arange(e2), indexing="ij")
+    so = (D["src_offset"] + i0 * D["src_stride"][0] + i1 * D["src_stride"][1]
+          + i2 * D["src_stride"][2]).reshape(-1)
+    do = (D["dst_offset"] + i0 * D["dst_stride"][0] + i1 * D["dst_stride"][1]
+          + i2 * D["dst_stride"][2]).reshape(-1)
+    # element k of item c is element c*8 + k of the row (k < 8, inside the row)
+    el = np.arange(n * 8, dtype=np.int64)
+    el = el[el < run]
+    s_byte = (so[:, None] + el[None, :] * es).reshape(-1)
+    d_byte = (do[:, None] + el[None, :] * ed).reshape(-1)
+    src = srcs_flat[D["src_ptr"]]
+    vals = np.stack([src[s_byte + b] for b in range(es)], axis=1).reshape(-1)
+    conv = oracle.convert(torch.from_numpy(vals.copy()).view(_TORCH[fs]), fs, fd)
+    out = conv.view(torch.uint8).numpy().reshape(-1, ed)
+    for r in range(D["fanout"]):
+        dst = dsts_flat[refs[D["dst_ref_begin"] + r]]
+        for b in range(ed):
+            dst[d_byte + b] = out[:, b]
 
 
 def _run_window(D, segs, refs, srcs_flat, dsts_flat):
@@ -201,9 +247,8 @@ def shard_bytes(plan: Plan):
     """Bytes of every shard, in the src / dst pointer-array order of execute."""
     sb, db = [], []
     for t, spec in enumerate(plan.specs):
-        es = spec.dtype.itemsize
-        sb += [int(np.prod(box_shape(b))) * es for b in plan.src_boxes(t)]
-        db += [int(np.prod(box_shape(b))) * es for b in plan.dst_boxes(t)]
+        sb += [int(np.prod(box_shape(b))) * spec.dtype.itemsize for b in plan.src_boxes(t)]
+        db += [int(np.prod(box_shape(b))) * spec.out_dtype.itemsize for b in plan.dst_boxes(t)]
     return sb, db
 
 
@@ -231,9 +276,12 @@ def assert_descriptors_in_bounds(plan: Plan):
             continue
         assert D["run_bytes"] >= 1 and D["row_items"] >= 1 and all(e >= 1 for e in ext)
         assert ext[0] * ext[1] * ext[2] * D["row_items"] < 2 ** 31
-        span = D["run_bytes"]
-        s_last = D["src_offset"] + sum((e - 1) * st for e, st in zip(ext, D["src_stride"])) + span
-        d_last = D["dst_offset"] + sum((e - 1) * st for e, st in zip(ext, D["dst_stride"])) + span
+        s_span = d_span = D["run_bytes"]
+        if D["mode"] == R.DESC_CONVERT:
+            _, _, es, ed = CONVERSIONS[D["unit"]]
+            s_span, d_span = D["run_bytes"] * es, D["run_bytes"] * ed
+        s_last = D["src_offset"] + sum((e - 1) * st for e, st in zip(ext, D["src_stride"])) + s_span
+        d_last = D["dst_offset"] + sum((e - 1) * st for e, st in zip(ext, D["dst_stride"])) + d_span
         assert D["src_offset"] >= 0 and D["dst_offset"] >= 0
         assert all(st >= 0 for st in D["src_stride"] + D["dst_stride"])
         assert s_last <= sb[D["src_ptr"]], D

@@ -47,7 +47,7 @@ def test_worked_example_golden():
 
 
 SMALL_FULL = ["worked_example_8x8", "ffn_up_14336x4096", "moe_experts_64x2048x7168", "uneven_5000x3001",
-              "narrow_columns_4194304x8"]
+              "narrow_columns_4194304x8", "ffn_up_f32_to_bf16_14336x4096"]
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -91,15 +91,52 @@ def test_small_layouts(spec):
 def test_misaligned_shard_pointers(misalign):
     """Shard pointers off the 16-byte grid take the bytewise path; results and
     guard bands must be unaffected."""
-    specs = [W.uneven(50, 31).tensors[0], W.ffn_up(112, 64).tensors[0]]
+    specs = [W.uneven(50, 31).tensors[0], W.ffn_up(112, 64).tensors[0]] + \
+        [s for s in small_specs() if s.name in ("conv_f32_bf16", "conv_bf16_f32_ragged")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 
 
 def test_batched_mixed_dtypes():
     specs = list(W.ffn_refit(2, 64, 224).tensors) + [W.uneven(77, 53).tensors[0]] + \
-        [s for s in small_specs() if s.name in ("u8_odd", "i64", "five_d", "rep_src")]
+        [s for s in small_specs() if s.name in ("u8_odd", "i64", "five_d", "rep_src", "conv_f32_f16_ragged",
+                                                "conv_f16_f32_nested")]
     run_parity(specs, "raw", 5)
+
+
+def _narrowing_patterns():
+    """f32 bit patterns: every upper half with lower halves at and around each
+    place a bf16 or f16 rounding decision (normal or subnormal) is taken."""
+    lows = [0x0000, 0x0001, 0x0FFF, 0x1000, 0x1001, 0x1FFF, 0x2000, 0x2001, 0x3000, 0x3FFF, 0x4000,
+            0x4001, 0x5000, 0x6000, 0x7000, 0x7FFF, 0x8000, 0x8001, 0x9000, 0xA000, 0xBFFF, 0xC000,
+            0xC001, 0xE000, 0xF000, 0xFFFE, 0xFFFF, 0x0800, 0x1800, 0x2800, 0x5555, 0xAAAA]
+    hi = torch.arange(1 << 16, dtype=torch.int64) << 16
+    bits = (hi[:, None] | torch.tensor(lows, dtype=torch.int64)[None, :]).reshape(-1)
+    return bits.to(torch.int32).view(torch.float32)   # wraps to the signed pattern, same bits
+
+
+@pytest.mark.parametrize("layout", ["ragged", "aligned"])
+@pytest.mark.parametrize("conv", ["f32_bf16", "f32_f16", "bf16_f32", "f16_f32"])
+def test_conversion_bit_patterns(conv, layout):
+    """Every rounding case of the formats through the kernel's conversion:
+    all 2^16 upper halves of an f32 with 32 lower halves around each rounding
+    point (ties, one below, one above; normal and subnormal targets, overflow,
+    NaN payloads), or all 2^16 patterns of a 16-bit format, each four times.
+    'ragged': (2,)[S0] -> (3,)[S0], shard rows off the 16-byte grid (element
+    path at the edges); 'aligned': (2,)[S0] -> (2,)[S0] (16-byte path)."""
+    src_dt, dst_dt = {"f32_bf16": (torch.float32, torch.bfloat16), "f32_f16": (torch.float32, torch.float16),
+                      "bf16_f32": (torch.bfloat16, torch.float32), "f16_f32": (torch.float16, torch.float32)}[conv]
+    if src_dt == torch.float32:
+        g = _narrowing_patterns()
+    else:
+        g = torch.arange(1 << 16, dtype=torch.int32).to(torch.int16).view(src_dt).repeat(4)
+    n = g.numel()
+    if layout == "ragged":
+        spec = W.TensorSpec(f"bits_{conv}", (n - 3,), src_dt, (2,), (0,), (3,), (0,), dst_dt)
+        g = g[:n - 3].contiguous()
+    else:
+        spec = W.TensorSpec(f"bits_{conv}", (n,), src_dt, (2,), (0,), (2,), (0,), dst_dt)
+    run_parity([spec], "given", 0, globals_=[g])
 
 
 def test_pointer_slot_ring():

@@ -56,6 +56,16 @@ def small_specs():
         T("narrow_fp8_3d", (6, 7, 24), torch.uint8, (2, 3), (0, 2), (4,), (2,)),
         T("narrow_rep", (301, 12), torch.float32, (3,), (1,), (2, 3), (RR, 1)),
         T("wide_window", (37, 4001), torch.bfloat16, (3,), (1,), (5,), (0,)),
+        # converting reshards: ragged rows (not a multiple of 8 elements), fan-out,
+        # nesting, peeled outer dims, empty shards
+        T("conv_f32_bf16", (112, 64), torch.float32, (4,), (0,), (2, 2), (RR, 1), torch.bfloat16),
+        T("conv_f32_f16_ragged", (37, 29), torch.float32, (2, 2), (RR, 0), (3,), (1,), torch.float16),
+        T("conv_bf16_f32_ragged", (50, 31), torch.bfloat16, (3,), (1,), (2, 2), (0, RR), torch.float32),
+        T("conv_f16_f32_nested", (9, 4, 10), torch.float16, (2, 3), (0, 0), (2, 2, 2), (2, 0, 2),
+          torch.float32),
+        T("conv_peel", (3, 5, 5, 5, 6), torch.float32, (2, 2, 2), (1, 2, 3), (2,), (4,), torch.bfloat16),
+        T("conv_empty", (5, 3), torch.float32, (4,), (0,), (2,), (1,), torch.float16),
+        T("conv_narrow", (4099, 8), torch.float32, (2,), (0,), (4,), (1,), torch.bfloat16),
     ]
     return specs
 
@@ -76,7 +86,7 @@ def test_pieces_and_descriptors_match_oracle(spec):
         # byte-level walk of the device table
         sflat = [None if s is None else s.contiguous().view(torch.uint8).reshape(-1).numpy()
                  for s in srcs]
-        dflat = [np.full(int(np.prod(box_shape(b))) * g.element_size(), 0xA5, dtype=np.uint8)
+        dflat = [np.full(int(np.prod(box_shape(b))) * spec.out_dtype.itemsize, 0xA5, dtype=np.uint8)
                  for b in plan.dst_boxes(0)]
         run_descriptors(plan, sflat, dflat)
         for d, (a, b) in enumerate(zip(dflat, want)):
@@ -144,7 +154,7 @@ def test_invariants_full_size(wl):
         pieces = R.reshard_plan_pieces(plan.handle)
         dst_bytes = 0
         for t, spec in enumerate(wl.tensors):
-            es = spec.dtype.itemsize
+            es = spec.out_dtype.itemsize
             for b in plan.dst_boxes(t):
                 dst_bytes += int(np.prod(box_shape(b))) * es
         # I2, I3: write bytes = destination bytes, read bytes = global bytes (no 2x inflation)
@@ -204,7 +214,7 @@ def test_worked_example_plan():
 
 def test_piece_counts_of_workloads():
     counts = {"worked_example_8x8": 8, "ffn_up_14336x4096": 8, "moe_experts_64x2048x7168": 128,
-              "uneven_5000x3001": 42, "ffn_refit_32_layers": 384, "narrow_columns_4194304x8": 8,
+              "uneven_5000x3001": 42, "ffn_refit_32_layers": 384, "narrow_columns_4194304x8": 8, "ffn_up_f32_to_bf16_14336x4096": 8,
               "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1)}
     for wl in full_workload_plans():
         with Plan(wl.tensors) as plan:
@@ -342,11 +352,21 @@ def test_errors():
         R.reshard_layout_create(tuple([2] * 9), R.DTYPE_F32, (2,), (0,))  # ndim 9
     a = R.reshard_layout_create((4, 4), R.DTYPE_F32, (2,), (0,))
     b = R.reshard_layout_create((4, 5), R.DTYPE_F32, (2,), (0,))
-    c = R.reshard_layout_create((4, 4), R.DTYPE_BF16, (2,), (0,))
-    for other in (b, c):
+    c = R.reshard_layout_create((4, 4), R.DTYPE_I32, (2,), (0,))     # same size, no conversion
+    c2 = R.reshard_layout_create((4, 4), R.DTYPE_F64, (2,), (0,))    # no f32 -> f64 conversion
+    bf = R.reshard_layout_create((4, 4), R.DTYPE_BF16, (2,), (0,))
+    hf = R.reshard_layout_create((4, 4), R.DTYPE_F16, (2,), (0,))
+    for other in (b, c, c2):
         with pytest.raises(R.ReshardError) as e:
             R.reshard_plan_create(a, other)
         assert e.value.status == R.ERR_LAYOUT_MISMATCH
+    with pytest.raises(R.ReshardError) as e:
+        R.reshard_plan_create(bf, hf)  # bf16 -> f16 is not a supported conversion
+    assert e.value.status == R.ERR_LAYOUT_MISMATCH
+    for x, y in ((a, bf), (a, hf), (bf, a), (hf, a)):  # the supported conversions plan
+        R.reshard_plan_destroy(R.reshard_plan_create(x, y))
+    for h in (c2, bf, hf):
+        R.reshard_layout_destroy(h)
     with pytest.raises(R.ReshardError):
         R.reshard_layout_shard_box(a, 2, 2)  # rank out of range
     plan = R.reshard_plan_create(a, a)
