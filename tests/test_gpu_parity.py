@@ -10,7 +10,7 @@ import oracle_pins as P
 from dtensor_layout_movement_amd import workloads as W
 from gpu_harness import GuardedShards, run_parity, shard_nbytes
 from reshard_harness import Plan, assert_boxes_agree, assert_descriptors_in_bounds, oracle_boxes
-from test_planner import small_specs
+from test_planner import random_specs, small_specs
 
 pytestmark = pytest.mark.gpu
 
@@ -369,3 +369,12 @@ def test_hybrid_routing_matches_oracle():
                 assert torch.equal(got.cpu().view(torch.uint8), w.view(torch.uint8)), specs[t].name
     finally:
         hp.close()
+
+
+@pytest.mark.parametrize("batch", range(5))
+def test_random_layouts_batched(batch):
+    """Seeded random layout pairs of moderate size (1-4 dims, up to three mesh
+    dims, nested / replicated / empty shards, several dtypes and conversions),
+    six per fused launch."""
+    specs = random_specs(100 + batch, 6)
+    run_parity(specs, "raw", batch)

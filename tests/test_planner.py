@@ -141,6 +141,49 @@ def test_brute_force_random_layout_pairs():
         n += 1
 
 
+def random_specs(seed, count, max_numel=400_000):
+    """Seeded random layout pairs of moderate size: 1-4 dims, meshes of up to
+    three dims, any placements (nested, replicated, empty shards), several
+    dtypes and the supported conversions."""
+    rng = random.Random(seed)
+    caps = {1: 200_000, 2: 1500, 3: 120, 4: 40}
+    out = []
+    while len(out) < count:
+        nd = rng.randint(1, 4)
+        shape = tuple(rng.choice([rng.randint(1, 7), rng.randint(1, caps[nd])]) for _ in range(nd))
+        if int(np.prod(shape)) > max_numel:
+            continue
+        def layout():
+            md = rng.randint(1, 3)
+            mesh = tuple(rng.randint(1, 5) for _ in range(md))
+            if int(np.prod(mesh)) > 32:
+                mesh = mesh[:1]
+            return mesh, tuple(rng.choice([RR] + list(range(nd))) for _ in range(len(mesh)))
+        (sm, sp), (dm, dp) = layout(), layout()
+        pair = rng.choice([(torch.uint8, None), (torch.bfloat16, None), (torch.float32, None),
+                           (torch.float64, None), (torch.int16, None), (torch.float32, torch.bfloat16),
+                           (torch.float32, torch.float16), (torch.bfloat16, torch.float32),
+                           (torch.float16, torch.float32)])
+        out.append(T(f"rand{seed}_{len(out)}", shape, pair[0], sm, sp, dm, dp, pair[1]))
+    return out
+
+
+def test_random_moderate_layouts_descriptor_walk():
+    """40 seeded random layout pairs of moderate size: planned pieces and the
+    byte-level walk of the descriptor table both equal the oracle."""
+    for spec in random_specs(11, 40):
+        with Plan([spec]) as plan:
+            assert_boxes_agree(plan)
+            assert_descriptors_in_bounds(plan)
+            _, srcs = sources_for(spec, "raw", seed=5)
+            want = oracle_dsts(spec, srcs)
+            sflat = [None if s is None else s.contiguous().view(torch.uint8).reshape(-1).numpy() for s in srcs]
+            dflat = [np.zeros(b.numel() * b.element_size(), dtype=np.uint8) for b in want]
+            run_descriptors(plan, sflat, dflat)
+            for a, b in zip(dflat, want):
+                assert a.tobytes() == b.view(torch.uint8).reshape(-1).numpy().tobytes(), spec
+
+
 def full_workload_plans():
     return [mk() for mk in W.WORKLOADS.values()]
 
