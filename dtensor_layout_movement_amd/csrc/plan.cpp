@@ -397,7 +397,8 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
   const int64_t width = v.cols * es;
   const int64_t pitch = (width + 15) / 16 * 16;
   if (width <= 0 || pitch > int64_t(kWindowBytes)) return false;
-  const int64_t rows_per_tile = int64_t(kWindowBytes) / pitch;
+  const int64_t rows_per_tile = width <= kRowModeBytes ? int64_t(kTileThreads) * kRowsPerLane
+                                                      : int64_t(kWindowBytes) / pitch;
   auto rlo = [&](const Box& b) { return b.lo[0] * v.row_mult; };
   auto rhi = [&](const Box& b) { return b.hi[0] * v.row_mult; };
   std::vector<int64_t> cuts;

@@ -88,6 +88,10 @@ constexpr int64_t kMaxRunBytes = int64_t(1) << 30;
 constexpr uint32_t kWindowBytes = 16384;
 constexpr uint32_t kWindowMaxSegs = 64;
 constexpr int64_t kWindowMaxRun = 128;
+// Bands at most kRowModeBytes wide skip LDS: each lane assembles whole rows in a
+// 16-byte register, kRowsPerLane rows per lane and tile.
+constexpr int64_t kRowModeBytes = 16;
+constexpr uint32_t kRowsPerLane = 4;
 
 // Elements per item of a RESHARD_DESC_CONVERT row.
 constexpr uint32_t kConvertElems = RESHARD_CONVERT_ELEMS;

@@ -484,6 +484,79 @@ __device__ void window_tile(const reshard_descriptor_t& D, const reshard_segment
   }
 }
 
+// n <= 16 bytes from global address a into bytes [0, n) of the result (any
+// alignment: gfx950 global accesses need none).
+__device__ __forceinline__ u32x4 load_bytes(uintptr_t a, uint32_t n) {
+  if (n == 16) return load_16_unaligned(a);
+  uint64_t lo = 0, hi = 0;
+  uint32_t at = 0;
+  if (n & 8) {
+    lo = *as_global<const u64_u>(a);
+    at = 8;
+  }
+  if (n & 4) {
+    const uint64_t x = *as_global<const u32_u>(a + at);
+    if (at < 8) lo |= x << (8 * at); else hi |= x;
+    at += 4;
+  }
+  if (n & 2) {
+    const uint64_t x = *as_global<const u16_u>(a + at);
+    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
+    at += 2;
+  }
+  if (n & 1) {
+    const uint64_t x = *as_global<const uint8_t>(a + at);
+    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
+  }
+  return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
+}
+
+// A window band at most 16 bytes wide, without LDS: each lane owns rows
+// r = k * kBlock + lane of the tile, builds each row in one 16-byte register
+// from every source segment (shifted to its column), then writes each
+// destination segment's bytes of it to every replica.  Consecutive lanes touch
+// consecutive rows, so packed segments give contiguous wave accesses.
+template <class Sh>
+__device__ void window_rows(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
+                            const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
+  constexpr int kRows = int(rs::kRowsPerLane);
+  const uint32_t rows = D.extent[0], per_tile = D.extent[1];
+  const uint32_t r0 = tile * per_tile;
+  const uint32_t hr = min(per_tile, rows - r0);
+  const reshard_segment_t* src_segs = segs + D.src_ptr;
+  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+  u32x4 v[kRows];
+#pragma unroll
+  for (int k = 0; k < kRows; ++k) v[k] = u32x4{0, 0, 0, 0};
+  for (uint32_t s = 0; s < D.dst_ref_begin; ++s) {
+    const reshard_segment_t S = src_segs[s];
+    const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
+      if (r < hr) {
+        const u32x4 x = shift_left_bytes(load_bytes(g + uint64_t(r) * uint64_t(S.row_stride), S.width), S.col);
+        v[k] = u32x4{v[k].x | x.x, v[k].y | x.y, v[k].z | x.z, v[k].w | x.w};
+      }
+    }
+  }
+  for (uint32_t s = 0; s < D.fanout; ++s) {
+    const reshard_segment_t S = dst_segs[s];
+    const uint64_t row_off = uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+    u32x4 x[kRows];
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) x[k] = S.col == 0 ? v[k] : shift_right_bytes(v[k], S.col);
+    for (uint32_t f = 0; f < S.fanout; ++f) {
+      const uintptr_t g = sh.ptr(refs[S.ptr + f]) + row_off;
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+        const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
+        if (r < hr) store_chunk(g + uint64_t(r) * uint64_t(S.row_stride), x[k], S.width);
+      }
+    }
+  }
+}
+
 // Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
 // aligned to the descriptor's unit, or replicas differ in 16-byte phase.
 template <class Sh>
@@ -652,7 +725,8 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t unit = unit_mode & 0xffffu, mode = unit_mode >> 16;
   if (mode == RESHARD_DESC_WINDOW) {  // any alignment: global chunks follow the addresses
     const Shards<kKarg> wsh{table, &karg, refs};
-    window_tile(D, segs, refs, wsh, t - tile_begin[lo], window);
+    if (D.run_bytes <= uint32_t(rs::kRowModeBytes)) window_rows(D, segs, refs, wsh, t - tile_begin[lo]);
+    else window_tile(D, segs, refs, wsh, t - tile_begin[lo], window);
     return;
   }
   const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;

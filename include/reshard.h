@@ -151,6 +151,9 @@ typedef struct reshard_piece {
  *                            read into the window) followed by `fanout` destination
  *                            segments (written from it); offsets and strides are
  *                            ignored.  Used for narrow or misaligned pieces.
+ *                            A band at most 16 bytes wide skips LDS: one lane
+ *                            per row assembles the row in registers; then
+ *                            `extent[1]` = 1024 rows per tile.
  *   RESHARD_DESC_CONVERT     rows of `run_bytes` ELEMENTS (not bytes) converted by
  *                            conversion `unit`; item c is elements
  *                            [c*8, min(c*8+8, run)) of the row; row_items =

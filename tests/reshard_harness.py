@@ -263,7 +263,7 @@ def assert_descriptors_in_bounds(plan: Plan):
         if D["mode"] == R.DESC_WINDOW:
             rows, per_tile, pitch, width = ext[0], ext[1], D["row_items"], D["run_bytes"]
             assert rows >= 1 and per_tile >= 1 and pitch % 16 == 0 and pitch >= width
-            assert per_tile * pitch <= 16384
+            assert per_tile * pitch <= 16384 or (width <= 16 and per_tile % 256 == 0)  # LDS window, or row mode
             first = D["src_ptr"]
             for i, sg in enumerate(segs[first:first + D["dst_ref_begin"] + D["fanout"]]):
                 assert sg["col"] + sg["width"] <= width and sg["offset"] >= 0 and sg["row_stride"] >= 0
