@@ -485,17 +485,17 @@ __device__ void window_tile(const reshard_descriptor_t& D, const reshard_segment
 }
 
 // n <= 16 bytes from global address a into bytes [0, n) of the result (any
-// alignment: gfx950 global accesses need none).
+// alignment: gfx950 global accesses need none).  Streaming (non-temporal).
 __device__ __forceinline__ u32x4 load_bytes(uintptr_t a, uint32_t n) {
   if (n == 16) return load_16_unaligned(a);
   uint64_t lo = 0, hi = 0;
   uint32_t at = 0;
   if (n & 8) {
-    lo = *as_global<const u64_u>(a);
+    lo = __builtin_nontemporal_load(as_global<const u64_u>(a));
     at = 8;
   }
   if (n & 4) {
-    const uint64_t x = *as_global<const u32_u>(a + at);
+    const uint64_t x = __builtin_nontemporal_load(as_global<const u32_u>(a + at));
     if (at < 8) lo |= x << (8 * at); else hi |= x;
     at += 4;
   }
@@ -509,6 +509,15 @@ __device__ __forceinline__ u32x4 load_bytes(uintptr_t a, uint32_t n) {
     if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
   }
   return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
+}
+
+// Bytes [0, n) of v (n <= 16) to global address d, streaming stores for the
+// whole-word widths, at most four stores otherwise.
+__device__ __forceinline__ void store_bytes(uintptr_t d, u32x4 v, uint32_t n) {
+  if (n == 16) __builtin_nontemporal_store(v, as_global<u32x4_u>(d));
+  else if (n == 8) __builtin_nontemporal_store((uint64_t(v.y) << 32) | v.x, as_global<u64_u>(d));
+  else if (n == 4) __builtin_nontemporal_store(v.x, as_global<u32_u>(d));
+  else store_head_bytes(d, v, n);
 }
 
 // A window band at most 16 bytes wide, without LDS: each lane owns rows
@@ -551,7 +560,7 @@ __device__ void window_rows(const reshard_descriptor_t& D, const reshard_segment
 #pragma unroll
       for (int k = 0; k < kRows; ++k) {
         const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
-        if (r < hr) store_chunk(g + uint64_t(r) * uint64_t(S.row_stride), x[k], S.width);
+        if (r < hr) store_bytes(g + uint64_t(r) * uint64_t(S.row_stride), x[k], S.width);
       }
     }
   }
