@@ -991,6 +991,22 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
 
   hipStream_t stream = static_cast<hipStream_t>(stream_arg);
   std::lock_guard<std::mutex> lock(plan->mu);
+  // Under stream capture only the launch itself may be recorded: the table
+  // upload synchronises and the pointer-slot ring copies from host memory that
+  // later calls rewrite, so neither may end up in a graph.
+  hipStreamCaptureStatus capture = hipStreamCaptureStatusNone;
+  if (stream) {
+    const hipError_t ce = hipStreamIsCapturing(stream, &capture);
+    if (ce != hipSuccess) return hip_fail(ce, "hipStreamIsCapturing");
+  }
+  if (capture != hipStreamCaptureStatusNone) {
+    if (!plan->uploaded)
+      return fail(RESHARD_ERR_INVALID_ARGUMENT, "call reshard_plan_upload before capturing an execute");
+    if (plan->n_ptrs > kKargPtrs)
+      return fail(RESHARD_ERR_INVALID_ARGUMENT,
+                  "a plan with more than " + std::to_string(kKargPtrs) +
+                      " shard pointers cannot be captured into a graph");
+  }
   reshard_status_t st = upload_locked(plan, stream);
   if (st != RESHARD_OK) return st;
   if (H.descs.empty()) return RESHARD_OK;

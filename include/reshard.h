@@ -259,6 +259,11 @@ reshard_status_t reshard_plan_upload(reshard_plan_t plan, void* stream);
  * plan-owned device slot with one asynchronous host-to-device copy.  Device
  * faults surface at the caller's next synchronisation, as with any HIP launch.
  * Calls on several streams may overlap.
+ * Graph capture: an execute may be captured into a HIP graph (stream capture
+ * on `stream`) when the plan was uploaded beforehand and its pointer arrays fit
+ * in the kernel arguments (n_src_ptrs + n_dst_ptrs <= 120); the graph then holds
+ * exactly one kernel node with the pointers given at capture time.  Otherwise a
+ * capturing call records nothing and fails with RESHARD_ERR_INVALID_ARGUMENT.
  * Errors: RESHARD_ERR_INVALID_ARGUMENT, RESHARD_ERR_NULL_SHARD, RESHARD_ERR_HIP,
  * RESHARD_ERR_DEVICE_MISMATCH, RESHARD_ERR_OUT_OF_MEMORY.
  */

@@ -9,7 +9,7 @@ import dtensor_layout_movement_amd as R
 import oracle_pins as P
 from dtensor_layout_movement_amd import workloads as W
 from gpu_harness import GuardedShards, run_parity, shard_nbytes
-from reshard_harness import Plan, assert_boxes_agree, assert_descriptors_in_bounds, oracle_boxes
+from reshard_harness import Plan, assert_boxes_agree, assert_descriptors_in_bounds, box_shape, oracle_boxes
 from test_planner import random_specs, small_specs
 
 pytestmark = pytest.mark.gpu
@@ -378,3 +378,57 @@ def test_random_layouts_batched(batch):
     six per fused launch."""
     specs = random_specs(100 + batch, 6)
     run_parity(specs, "raw", batch)
+
+
+def test_graph_capture_replays_match_oracle():
+    """An execute captured into a HIP graph (torch.cuda.CUDAGraph on a side
+    stream) replays the reshard: three replays, each after eager work that
+    clears the destinations and changes the sources, each checked against the
+    oracle for the sources of that replay."""
+    from reshard_harness import oracle_dsts
+    spec = W.uneven(301, 257).tensors[0]
+    with Plan([spec]) as plan:
+        stream = torch.cuda.Stream()
+        R.reshard_plan_upload(plan.handle, stream.cuda_stream)
+        sboxes = oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements)
+        srcs = [s.cuda() for s in W.cut(W.make_global(spec, "raw", 0, 0), sboxes)]
+        dsts = [torch.zeros(box_shape(b), dtype=spec.dtype, device="cuda")
+                for b in oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements)]
+        sp = R.pointer_array([s.data_ptr() for s in srcs])
+        dp = R.pointer_array([d.data_ptr() for d in dsts])
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            R.reshard_execute(plan.handle, sp, dp, stream.cuda_stream)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            fresh = W.cut(W.make_global(spec, "raw", 10 + rep, 0), sboxes)
+            for s, f in zip(srcs, fresh):
+                s.copy_(f)          # eager work between replays: new sources ...
+            for d in dsts:
+                d.zero_()           # ... and cleared destinations (fill kernels)
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            want = oracle_dsts(spec, fresh)
+            for got, w in zip(dsts, want):
+                assert torch.equal(got.cpu().view(torch.uint8), w.view(torch.uint8)), rep
+
+
+def test_graph_capture_refused_for_pointer_table_plans():
+    """A plan whose pointers need the device slot ring refuses to be captured
+    and records nothing; it still runs eagerly afterwards."""
+    specs = W.ffn_refit(16, 64, 224).tensors      # 48 tensors x 10 ranks > 120 pointers
+    with Plan(specs) as plan:
+        stream = torch.cuda.Stream()
+        R.reshard_plan_upload(plan.handle, stream.cuda_stream)
+        st = plan.stats()
+        assert st["n_src_ptrs"] + st["n_dst_ptrs"] > 120
+        graph = torch.cuda.CUDAGraph()
+        with pytest.raises(R.ReshardError) as e:
+            with torch.cuda.graph(graph, stream=stream):
+                R.reshard_execute(plan.handle, [0x1000] * st["n_src_ptrs"], [0x2000] * st["n_dst_ptrs"],
+                                  stream.cuda_stream)
+        assert e.value.status == R.ERR_INVALID_ARGUMENT and "captured" in str(e.value)
+        torch.cuda.synchronize()
+    run_parity(list(W.ffn_refit(16, 64, 224).tensors), "raw", 9)
