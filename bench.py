@@ -15,6 +15,10 @@ pages' baseline scheme, gather-then-slice, built from two plans of the same
 library (sources -> one global buffer -> destinations); its step time and the
 reshard's speed-up over it are reported as ``gather_then_slice_gpu``.
 
+``contiguous_same_bytes`` is the same kernel moving the same bytes as one
+contiguous buffer with the same fan-out: the practical ceiling for the
+workload's read:write mix on this GPU.
+
 The two-stage transport of the pages (each destination box delivered once,
 split over its replicas, then assembled by every replica; pipelined over
 tensor chunks on two streams) is timed the same way as ``two_stage_gpu``, and
@@ -143,6 +147,44 @@ def alloc_set(torch, R, wl, lay_src, lay_dst, dev, seed):
     sp = R.pointer_array([b.data_ptr() if b is not None else 0 for b in src_bufs])
     dp = R.pointer_array([b.data_ptr() if b is not None else 0 for b in dst_bufs])
     return src_bufs, dst_bufs, sp, dp
+
+
+def contiguous_reference(torch, R, st, dev, stream, steps: int, min_footprint_gb: float):
+    """The same kernel moving the same bytes with no layout structure: one
+    contiguous byte buffer of `bytes_read` bytes replicated to `fan` destinations,
+    (1,)[R] -> (fan,)[R], fan = bytes_written / bytes_read when that is whole.
+    Timed cold like the main step: its rate is what this kernel reaches on this
+    read:write mix, the practical ceiling for the workload."""
+    n, w = st["bytes_read"], st["bytes_written"]
+    if n == 0 or w % n:
+        return None
+    fan = w // n
+    lay_s = R.reshard_layout_create((n,), R.DTYPE_U8, (1,), (R.REPLICATE,))
+    lay_d = R.reshard_layout_create((n,), R.DTYPE_U8, (fan,), (R.REPLICATE,))
+    plan = R.reshard_plan_create(lay_s, lay_d)
+    try:
+        R.reshard_plan_upload(plan, stream.cuda_stream)
+        n_sets = max(1, min(16, int(-(-min_footprint_gb * 1e9 // (n * (1 + fan))))))
+        bufs = [[torch.empty(n, dtype=torch.uint8, device=dev) for _ in range(1 + fan)] for _ in range(n_sets)]
+        arrays = [(R.pointer_array([b[0].data_ptr()]), R.pointer_array([x.data_ptr() for x in b[1:]]))
+                  for b in bufs]
+        for i in range(3):
+            R.reshard_execute(plan, *arrays[i % n_sets], stream.cuda_stream)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(steps):
+            R.reshard_execute(plan, *arrays[i % n_sets], stream.cuda_stream)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        gbps = (n + w) / (ms * 1e-3) / 1e9
+        return {"gbps": round(gbps, 1), "pct_of_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+                "fanout": fan, "steps": steps, "buffer_sets_rotated": n_sets}
+    finally:
+        R.reshard_plan_destroy(plan)
+        R.reshard_layout_destroy(lay_s)
+        R.reshard_layout_destroy(lay_d)
 
 
 def gather_then_slice(torch, R, wl, lay_src, lay_dst, sets, stream, steps: int, reshard_ms: float) -> dict:
@@ -394,6 +436,11 @@ def main() -> int:
     copy_gbps = 2 * half / (c0.elapsed_time(c1) / 20 * 1e-3) / 1e9
     del a, b
 
+    reference = None
+    if not args.no_comparator:
+        reference = contiguous_reference(torch, R, st, dev, stream, max(5, K // 4), args.min_footprint_gb)
+        if reference:
+            reference["workload_vs_reference"] = round(value / reference["gbps"], 4)
     comparator = None
     if not args.no_comparator:
         comparator = gather_then_slice(torch, R, wl, lay_src, lay_dst, sets, stream,
@@ -458,6 +505,7 @@ def main() -> int:
                            "p90": round(per_launch[(9 * len(per_launch)) // 10], 2), "n": n_dist},
         "warm_same_buffers_gbps": round(algo_bytes / (warm_ms * 1e-3) / 1e9, 1),
         "copy_reference_gbps": round(copy_gbps, 1),
+        "contiguous_same_bytes": reference,
         "gather_then_slice_gpu": comparator,
         "two_stage_gpu": two,
         "hybrid_gpu": mixed,

@@ -651,6 +651,7 @@ __device__ __forceinline__ uint32_t convert_elem(uint32_t x) {
 template <int kConv, class Sh>
 __device__ __forceinline__ void convert_items(const reshard_descriptor_t& D, const uint8_t* src,
                                               const Sh& sh, uint32_t lo, uint32_t hi, bool aligned) {
+  static_assert(rs::kItemsPerThread == 1, "a CONVERT tile holds one item per thread");
   constexpr bool kNarrow = kConv == RESHARD_CONVERT_F32_BF16 || kConv == RESHARD_CONVERT_F32_F16;
   constexpr uint32_t kEs = kNarrow ? 4 : 2, kEd = kNarrow ? 2 : 4;
   const uint32_t f = lo + threadIdx.x;
@@ -708,13 +709,26 @@ __device__ __forceinline__ void convert_items(const reshard_descriptor_t& D, con
   }
 }
 
-template <bool kKarg>
+// Kernel variants.  A plan runs the smallest variant that covers the modes of
+// its descriptors: short launches pay for code size, for branches in the tile
+// prologue and for an LDS allocation they do not use.
+enum KernelKind : int {
+  kKindItems16 = 0,  // every descriptor ITEMS with 16-byte items
+  kKindChunks = 1,   // every descriptor DST_CHUNKS
+  kKindCopy = 2,     // ITEMS, DST_CHUNKS and CONVERT; no LDS
+  kKindAll = 3,      // any mode, LDS window included
+  kKindAligned = 4,  // added to kKindChunks when every shard pointer is 16-byte
+                     // aligned: no bytewise fallback is compiled in
+};
+
+template <bool kKarg, int kVariant>
 __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     const reshard_descriptor_t* __restrict__ descs, uint32_t n_desc,
     const uint32_t* __restrict__ tile_begin, const uint32_t* __restrict__ refs,
     const reshard_segment_t* __restrict__ segs, const void* const* __restrict__ table, KargPtrs karg,
     uint32_t n_tiles, uint32_t per_xcd, uint32_t flags) {
-  __shared__ __attribute__((aligned(16))) uint8_t window[rs::kWindowBytes];
+  constexpr int kKind = kVariant % kKindAligned;
+  constexpr bool kAligned = kVariant >= kKindAligned;
   // Block b runs on XCD b % kXcds.  Each XCD takes groups of kXcdGroup
   // consecutive tiles, the XCDs side by side: nearby tiles share an XCD's L2
   // while all XCDs stream through the same region of memory.  Plans smaller
@@ -731,29 +745,37 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const reshard_descriptor_t& D = descs[lo];
   uint32_t unit_mode;  // the two 16-bit fields as one scalar word
   __builtin_memcpy(&unit_mode, &D.unit, sizeof(unit_mode));
-  const uint32_t unit = unit_mode & 0xffffu, mode = unit_mode >> 16;
-  if (mode == RESHARD_DESC_WINDOW) {  // any alignment: global chunks follow the addresses
-    const Shards<kKarg> wsh{table, &karg, refs};
-    if (D.run_bytes <= uint32_t(rs::kRowModeBytes)) window_rows(D, segs, refs, wsh, t - tile_begin[lo]);
-    else window_tile(D, segs, refs, wsh, t - tile_begin[lo], window);
-    return;
+  const uint32_t unit = kKind == kKindItems16 ? 16u : unit_mode & 0xffffu;
+  const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
+                        : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
+                                               : unit_mode >> 16;
+  if constexpr (kKind == kKindAll) {
+    if (mode == RESHARD_DESC_WINDOW) {  // any alignment: global chunks follow the addresses
+      __shared__ __attribute__((aligned(16))) uint8_t window[rs::kWindowBytes];
+      const Shards<kKarg> wsh{table, &karg, refs};
+      if (D.run_bytes <= uint32_t(rs::kRowModeBytes)) window_rows(D, segs, refs, wsh, t - tile_begin[lo]);
+      else window_tile(D, segs, refs, wsh, t - tile_begin[lo], window);
+      return;
+    }
   }
   const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;
   const uint32_t first = (t - tile_begin[lo]) * rs::kTileItems;
   const uint32_t last = min(first + rs::kTileItems, items);
   const Shards<kKarg> sh{table, &karg, refs + D.dst_ref_begin};
   const uint8_t* src = reinterpret_cast<const uint8_t*>(sh.ptr(D.src_ptr));
-  if (mode == RESHARD_DESC_CONVERT) {  // checks its own alignment per item
-    const bool aligned = (flags & kAllAligned16) != 0;
-    switch (unit) {
-      case RESHARD_CONVERT_F32_BF16: convert_items<RESHARD_CONVERT_F32_BF16>(D, src, sh, first, last, aligned); break;
-      case RESHARD_CONVERT_F32_F16: convert_items<RESHARD_CONVERT_F32_F16>(D, src, sh, first, last, aligned); break;
-      case RESHARD_CONVERT_BF16_F32: convert_items<RESHARD_CONVERT_BF16_F32>(D, src, sh, first, last, aligned); break;
-      default: convert_items<RESHARD_CONVERT_F16_F32>(D, src, sh, first, last, aligned); break;
+  if constexpr (kKind >= kKindCopy) {
+    if (mode == RESHARD_DESC_CONVERT) {  // checks its own alignment per item
+      const bool aligned = (flags & kAllAligned16) != 0;
+      switch (unit) {
+        case RESHARD_CONVERT_F32_BF16: convert_items<RESHARD_CONVERT_F32_BF16>(D, src, sh, first, last, aligned); break;
+        case RESHARD_CONVERT_F32_F16: convert_items<RESHARD_CONVERT_F32_F16>(D, src, sh, first, last, aligned); break;
+        case RESHARD_CONVERT_BF16_F32: convert_items<RESHARD_CONVERT_BF16_F32>(D, src, sh, first, last, aligned); break;
+        default: convert_items<RESHARD_CONVERT_F16_F32>(D, src, sh, first, last, aligned); break;
+      }
+      return;
     }
-    return;
   }
-  if (!(flags & kAllAligned16)) {
+  if (!kAligned && !(flags & kAllAligned16)) {
     // alignment every access width relies on: the unit for ITEMS; for
     // DST_CHUNKS, replicas in the same 16-byte phase as replica 0
     const uintptr_t d0 = sh.dst(0);
@@ -768,16 +790,72 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
       return;
     }
   }
-  if (mode == RESHARD_DESC_DST_CHUNKS) {
+  if constexpr (kKind == kKindItems16) {
+    copy_items<u32x4, rs::kItemsPerThread>(D, src, sh, first, last);
+  } else if constexpr (kKind == kKindChunks) {
     copy_chunks<rs::kItemsPerThread>(D, src, sh, first, last);
-    return;
+  } else {
+    if (mode == RESHARD_DESC_DST_CHUNKS) {
+      copy_chunks<rs::kItemsPerThread>(D, src, sh, first, last);
+      return;
+    }
+    switch (unit) {
+      case 16: copy_items<u32x4, rs::kItemsPerThread>(D, src, sh, first, last); break;
+      case 8: copy_items<u32x2, rs::kItemsPerThread>(D, src, sh, first, last); break;
+      case 4: copy_items<uint32_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
+      case 2: copy_items<uint16_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
+      default: copy_items<uint8_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
+    }
   }
-  switch (unit) {
-    case 16: copy_items<u32x4, rs::kItemsPerThread>(D, src, sh, first, last); break;
-    case 8: copy_items<u32x2, rs::kItemsPerThread>(D, src, sh, first, last); break;
-    case 4: copy_items<uint32_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
-    case 2: copy_items<uint16_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
-    default: copy_items<uint8_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
+}
+
+// The kernel variant of a plan's descriptors.
+int kernel_kind(const std::vector<reshard_descriptor_t>& descs) {
+  bool items16 = true, chunks = true, window = false;
+  for (const reshard_descriptor_t& D : descs) {
+    if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
+    if (D.mode != RESHARD_DESC_DST_CHUNKS) chunks = false;
+    if (D.mode == RESHARD_DESC_WINDOW) window = true;
+  }
+  return items16 ? kKindItems16 : chunks ? kKindChunks : window ? kKindAll : kKindCopy;
+}
+
+template <bool kKarg, int kVariant>
+void launch_kind(uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
+                 const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
+                 const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
+                 uint32_t flags) {
+  hipLaunchKernelGGL((reshard_copy_kernel<kKarg, kVariant>), dim3(n_wg), dim3(kBlock), 0, stream, descs, n_desc,
+                     tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags);
+}
+
+template <bool kKarg>
+void launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
+            const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
+            const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
+            uint32_t flags) {
+  const bool aligned = (flags & kAllAligned16) != 0;
+  switch (kind) {
+    case kKindItems16:  // (an aligned-only build of this one measured slower on long copies)
+      launch_kind<kKarg, kKindItems16>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
+                                       n_tiles, per_xcd, flags);
+      break;
+    case kKindChunks:
+      if (aligned)
+        launch_kind<kKarg, kKindChunks + kKindAligned>(n_wg, stream, descs, n_desc, tile_begin, refs, segs,
+                                                       table, karg, n_tiles, per_xcd, flags);
+      else
+        launch_kind<kKarg, kKindChunks>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
+                                        n_tiles, per_xcd, flags);
+      break;
+    case kKindCopy:
+      launch_kind<kKarg, kKindCopy>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
+                                    n_tiles, per_xcd, flags);
+      break;
+    default:
+      launch_kind<kKarg, kKindAll>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
+                                   n_tiles, per_xcd, flags);
+      break;
   }
 }
 
@@ -794,6 +872,7 @@ struct reshard_plan_s {
   int device = -1;
   uint32_t n_wg = 0;       // grid of one launch: kXcds * per_xcd blocks (surplus ones exit)
   uint32_t per_xcd = 0;    // blocks per XCD, a multiple of kXcdGroup (0: one block per tile)
+  int kind = kKindAll;     // kernel variant (KernelKind)
   void* table = nullptr;  // device: descriptors | refs (absolute pointer slots) | tile_begin
   const reshard_descriptor_t* d_descs = nullptr;
   const uint32_t* d_refs = nullptr;
@@ -877,6 +956,7 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   p->d_segs = reinterpret_cast<const reshard_segment_t*>(static_cast<uint8_t*>(table) + segs_off);
   p->per_xcd = per_xcd;
   p->n_wg = per_xcd ? per_xcd * kXcds : uint32_t(H.n_tiles);
+  p->kind = kernel_kind(H.descs);
   p->device = dev;
   p->uploaded = true;
   return RESHARD_OK;
@@ -1056,13 +1136,11 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
     table = reinterpret_cast<const void* const*>(static_cast<void**>(plan->d_slots) + size_t(slot) * n);
   }
   if (table)
-    hipLaunchKernelGGL(reshard_copy_kernel<false>, dim3(plan->n_wg), dim3(kBlock), 0, stream,
-                       plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin, plan->d_refs,
-                       plan->d_segs, table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
+    launch<false>(plan->kind, plan->n_wg, stream, plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin,
+                  plan->d_refs, plan->d_segs, table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
   else
-    hipLaunchKernelGGL(reshard_copy_kernel<true>, dim3(plan->n_wg), dim3(kBlock), 0, stream,
-                       plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin, plan->d_refs,
-                       plan->d_segs, table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
+    launch<true>(plan->kind, plan->n_wg, stream, plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin,
+                 plan->d_refs, plan->d_segs, table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "reshard_copy_kernel launch");
   if (slot >= 0) {
