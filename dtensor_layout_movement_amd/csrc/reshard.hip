@@ -175,26 +175,29 @@ __device__ __forceinline__ u32x4 shift_right_bytes(u32x4 v, uint32_t s) {
   return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
 }
 
-// The first n < 16 bytes of v to address d, with at most four stores.
+// The first n < 16 bytes of v to address d, with at most four stores.  They are
+// streaming (non-temporal) like the full 16-byte stores around them: a partial
+// chunk shares its destination line with full chunks, and mixing temporal and
+// streaming stores on one line measured 5% slower on misaligned column strips.
 __device__ __forceinline__ void store_head_bytes(uintptr_t d, u32x4 v, uint32_t n) {
   uint64_t lo = (uint64_t(v.y) << 32) | v.x;
   const uint64_t hi = (uint64_t(v.w) << 32) | v.z;
   if (n & 8) {
-    *as_global<u64_u>(d) = lo;
+    __builtin_nontemporal_store(lo, as_global<u64_u>(d));
     d += 8;
     lo = hi;
   }
   if (n & 4) {
-    *as_global<u32_u>(d) = uint32_t(lo);
+    __builtin_nontemporal_store(uint32_t(lo), as_global<u32_u>(d));
     d += 4;
     lo >>= 32;
   }
   if (n & 2) {
-    *as_global<u16_u>(d) = uint16_t(lo);
+    __builtin_nontemporal_store(uint16_t(lo), as_global<u16_u>(d));
     d += 2;
     lo >>= 16;
   }
-  if (n & 1) *as_global<uint8_t>(d) = uint8_t(lo);
+  if (n & 1) __builtin_nontemporal_store(uint8_t(lo), as_global<uint8_t>(d));
 }
 
 // DST_CHUNKS mode: chunks [lo, hi).  Every non-empty chunk is one 16-byte load
@@ -341,9 +344,10 @@ __device__ __forceinline__ u32x4 load_in_run(uintptr_t base, uint32_t n, uintptr
   return u32x4{uint32_t(w[0]), uint32_t(w[0] >> 32), uint32_t(w[1]), uint32_t(w[1] >> 32)};
 }
 
-// Bytes [0, len) of v to global address d (len < 16: at most four stores).
+// Bytes [0, len) of v to global address d (len < 16: at most four stores), all
+// streaming.
 __device__ __forceinline__ void store_chunk(uintptr_t d, u32x4 v, uint32_t len) {
-  if (len == 16) *as_global<u32x4_u>(d) = v;
+  if (len == 16) __builtin_nontemporal_store(v, as_global<u32x4_u>(d));
   else store_head_bytes(d, v, len);
 }
 

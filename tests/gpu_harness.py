@@ -16,31 +16,41 @@ CANARY = 0x5A
 PREFILL = 0xA5
 
 
+def shard_misalign(misalign, i):
+    """Byte offset of shard i from the 16-byte grid: the same for every shard
+    (an int), or 'mixed': a different phase for neighbouring shards, so that
+    destination replicas do not share their 16-byte phase."""
+    if misalign == "mixed":
+        return (5 * i + 3) % 16
+    return misalign
+
+
 class GuardedShards:
     def __init__(self, nbytes, device, misalign=0, prefill=PREFILL):
         self.nbytes = list(nbytes)
-        self.misalign = misalign
+        self.mis = [shard_misalign(misalign, i) for i in range(len(self.nbytes))]
         self.bufs, self.ptrs = [], []
-        for n in self.nbytes:
+        for n, m in zip(self.nbytes, self.mis):
             if n == 0:
                 self.bufs.append(None)
                 self.ptrs.append(0)
                 continue
-            b = torch.full((GUARD + misalign + n + GUARD,), CANARY, dtype=torch.uint8, device=device)
-            b[GUARD + misalign:GUARD + misalign + n].fill_(prefill)
+            b = torch.full((GUARD + m + n + GUARD,), CANARY, dtype=torch.uint8, device=device)
+            b[GUARD + m:GUARD + m + n].fill_(prefill)
             self.bufs.append(b)
-            self.ptrs.append(b.data_ptr() + GUARD + misalign)
+            self.ptrs.append(b.data_ptr() + GUARD + m)
 
     def region(self, i):
-        n = self.nbytes[i]
-        return self.bufs[i][GUARD + self.misalign:GUARD + self.misalign + n]
+        n, m = self.nbytes[i], self.mis[i]
+        return self.bufs[i][GUARD + m:GUARD + m + n]
 
     def guards_intact(self, i):
         b = self.bufs[i]
         if b is None:
             return True
-        lo = b[:GUARD + self.misalign]
-        hi = b[GUARD + self.misalign + self.nbytes[i]:]
+        m = self.mis[i]
+        lo = b[:GUARD + m]
+        hi = b[GUARD + m + self.nbytes[i]:]
         return bool((lo == CANARY).all().item()) and bool((hi == CANARY).all().item())
 
 

@@ -87,12 +87,15 @@ def test_small_layouts(spec):
     run_parity([spec], "raw", 3)
 
 
-@pytest.mark.parametrize("misalign", [1, 2, 4, 8])
+@pytest.mark.parametrize("misalign", [1, 2, 4, 8, "mixed"])
 def test_misaligned_shard_pointers(misalign):
-    """Shard pointers off the 16-byte grid take the bytewise path; results and
-    guard bands must be unaffected."""
+    """Shard pointers off the 16-byte grid (all by the same offset, or 'mixed':
+    each shard at its own phase, replicas included) take the bytewise or
+    unaligned paths; results and guard bands must be unaffected."""
     specs = [W.uneven(50, 31).tensors[0], W.ffn_up(112, 64).tensors[0]] + \
-        [s for s in small_specs() if s.name in ("conv_f32_bf16", "conv_bf16_f32_ragged")]
+        [s for s in small_specs() if s.name in ("conv_f32_bf16", "conv_bf16_f32_ragged", "strips_fanout",
+                                                "strips_rep_src", "chunked_bf16", "strips_nine",
+                                                "narrow_rep", "narrow_scatter")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 

@@ -56,6 +56,15 @@ def small_specs():
         T("narrow_fp8_3d", (6, 7, 24), torch.uint8, (2, 3), (0, 2), (4,), (2,)),
         T("narrow_rep", (301, 12), torch.float32, (3,), (1,), (2, 3), (RR, 1)),
         T("wide_window", (37, 4001), torch.bfloat16, (3,), (1,), (5,), (0,)),
+        # misaligned column strips (destination-aligned chunks): row cuts inside a
+        # destination shard, destination replicas, source replicas, nine strips,
+        # a split middle dim; and a 4-byte piece in rows too wide for a window
+        T("strips_row_cuts", (50, 301), torch.float32, (2, 2), (0, 1), (3,), (0,)),
+        T("strips_fanout", (50, 301), torch.float32, (2, 2), (0, 1), (2, 3), (RR, 0)),
+        T("strips_rep_src", (61, 301), torch.float32, (2, 3), (RR, 1), (4,), (0,)),
+        T("strips_nine", (20, 333), torch.float32, (9,), (1,), (2,), (0,)),
+        T("strips_mid_split", (6, 10, 301), torch.bfloat16, (2, 3), (1, 2), (3,), (2,)),
+        T("narrow_wide_rows", (5, 4201), torch.float32, (4,), (1,), (2,), (1,)),
         # converting reshards: ragged rows (not a multiple of 8 elements), fan-out,
         # nesting, peeled outer dims, empty shards
         T("conv_f32_bf16", (112, 64), torch.float32, (4,), (0,), (2, 2), (RR, 1), torch.bfloat16),
@@ -336,13 +345,20 @@ def test_magic_constants_exact():
 
 def test_descriptor_modes():
     """16-byte aligned rows copy as 16-byte items; long misaligned rows as
-    destination-aligned 16-byte chunks; short misaligned rows item by item."""
-    def modes(wl):
-        with Plan(wl.tensors) as plan:
+    destination-aligned 16-byte chunks; short misaligned rows item by item;
+    narrow rows of a 2-d view through windows, unless the rows are wider than a
+    window."""
+    def modes(specs):
+        with Plan(specs) as plan:
             return {(d["mode"], d["unit"]) for d in R.reshard_plan_descriptors(plan.handle)[0]}
-    assert modes(W.ffn_up()) == {(R.DESC_ITEMS, 16)}
-    assert modes(W.uneven()) == {(R.DESC_DST_CHUNKS, 4)}       # 12004-byte destination rows
-    assert {m for m, _ in modes(W.worked_example_8x8())} == {R.DESC_WINDOW}  # 4-byte rows
+    small = {s.name: s for s in small_specs()}
+    assert modes(W.ffn_up().tensors) == {(R.DESC_ITEMS, 16)}
+    assert modes(W.uneven().tensors) == {(R.DESC_DST_CHUNKS, 4)}       # 12004-byte destination rows
+    assert {m for m, _ in modes(W.worked_example_8x8().tensors)} == {R.DESC_WINDOW}  # 4-byte rows
+    for name in ("strips_row_cuts", "strips_fanout", "strips_rep_src", "strips_nine", "strips_mid_split"):
+        assert modes([small[name]]) == {(R.DESC_DST_CHUNKS, 4 if small[name].dtype == torch.float32 else 2)}, name
+    # a 4-byte piece in 16804-byte rows: too wide for a window, so per piece
+    assert {m for m, _ in modes([small["narrow_wide_rows"]])} == {R.DESC_DST_CHUNKS, R.DESC_ITEMS}
 
 
 def test_window_segments_worked_example():
