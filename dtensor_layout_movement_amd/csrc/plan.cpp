@@ -397,8 +397,7 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
   const int64_t width = v.cols * es;
   const int64_t pitch = (width + 15) / 16 * 16;
   if (width <= 0 || pitch > int64_t(kWindowBytes)) return false;
-  const int64_t rows_per_tile = width <= kRowModeBytes ? int64_t(kTileThreads) * kRowsPerLane
-                                                      : int64_t(kWindowBytes) / pitch;
+  const int64_t window_rows = int64_t(kWindowBytes) / pitch;  // rows per tile of an LDS window
   auto rlo = [&](const Box& b) { return b.lo[0] * v.row_mult; };
   auto rhi = [&](const Box& b) { return b.hi[0] * v.row_mult; };
   std::vector<int64_t> cuts;
@@ -474,7 +473,9 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
     b.d.run_bytes = uint32_t(width);
     b.d.row_items = uint32_t(pitch);
     b.d.extent[0] = uint32_t(rb - ra);
-    b.d.extent[1] = uint32_t(rows_per_tile);
+    const bool quad = width == kRowModeBytes && (quad_side(b.src) || quad_side(b.dst));
+    b.d.extent[1] = uint32_t(width > kRowModeBytes ? window_rows
+                             : int64_t(kTileThreads) * (quad ? kQuadRowsPerLane : kRowsPerLane));
     b.d.extent[2] = 1;
     b.d.piece = uint32_t(pc0);
     if (rb - ra > int64_t(kMaxItems)) return false;

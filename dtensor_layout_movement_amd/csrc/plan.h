@@ -89,9 +89,21 @@ constexpr uint32_t kWindowBytes = 16384;
 constexpr uint32_t kWindowMaxSegs = 64;
 constexpr int64_t kWindowMaxRun = 128;
 // Bands at most kRowModeBytes wide skip LDS: each lane assembles whole rows in a
-// 16-byte register, kRowsPerLane rows per lane and tile.
+// 16-byte register, kRowsPerLane rows per lane and tile.  A 16-byte band whose
+// source or destination side is four packed 4-byte column runs (the four lanes
+// of a quad exchange words) takes kQuadRowsPerLane rows per lane and tile.
 constexpr int64_t kRowModeBytes = 16;
 constexpr uint32_t kRowsPerLane = 4;
+constexpr uint32_t kQuadRowsPerLane = 2;
+
+// Whether the segments of one side of a 16-byte band are four packed 4-byte
+// column runs with one fan-out (the kernel's quad exchange applies).
+inline bool quad_side(const std::vector<reshard_segment_t>& segs) {
+  if (segs.size() != 4) return false;
+  for (const reshard_segment_t& s : segs)
+    if (s.width != 4 || s.row_stride != 4 || s.fanout != segs[0].fanout) return false;
+  return true;
+}
 
 // Elements per item of a RESHARD_DESC_CONVERT row.
 constexpr uint32_t kConvertElems = RESHARD_CONVERT_ELEMS;

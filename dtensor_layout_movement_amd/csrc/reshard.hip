@@ -403,7 +403,7 @@ __device__ __forceinline__ uint8_t* run_lds(uint8_t* lds, uint32_t pitch, uint32
 constexpr int kWindowBatch = 4;  // chunks per thread with loads in flight together
 
 template <class Sh>
-__device__ void window_tile(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
+__device__ __forceinline__ void window_tile(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
                             const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile,
                             uint8_t* lds) {
   const uint32_t rows = D.extent[0], per_tile = D.extent[1], pitch = D.row_items;
@@ -524,34 +524,145 @@ __device__ __forceinline__ void store_bytes(uintptr_t d, u32x4 v, uint32_t n) {
   else store_head_bytes(d, v, n);
 }
 
+// 4x4 transpose of 32-bit words across the four lanes of each quad: with row i
+// of a 4x4 matrix in lane i of the quad, lane j ends with column j.  Two
+// exchanges with DPP quad permutations: the off-diagonal words of each 2x2
+// block with the neighbour lane (quad_perm 1,0,3,2), then the off-diagonal 2x2
+// blocks with the lane two away (quad_perm 2,3,0,1).  Every lane of the wave
+// must be active.
+__device__ __forceinline__ u32x4 quad_transpose(u32x4 v) {
+  const uint32_t j = threadIdx.x & 3u;
+  uint32_t m[4] = {v.x, v.y, v.z, v.w};
+  const bool odd = (j & 1u) != 0, upper = (j & 2u) != 0;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const uint32_t x = odd ? m[2 * b] : m[2 * b + 1];
+    const uint32_t y = uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0xB1, 0xF, 0xF, false));
+    if (odd) m[2 * b] = y;
+    else m[2 * b + 1] = y;
+  }
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const uint32_t x = upper ? m[c] : m[2 + c];
+    const uint32_t y = uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x4E, 0xF, 0xF, false));
+    if (upper) m[c] = y;
+    else m[2 + c] = y;
+  }
+  return u32x4{m[0], m[1], m[2], m[3]};
+}
+
+// Whether segments [0, n) of a 16-byte band are four packed 4-byte column runs
+// (the band's row split into four 4-byte pieces, each stored contiguously) with
+// one fan-out: then four consecutive rows of one segment are 16 contiguous bytes.
+__device__ __forceinline__ bool quad_segments(const reshard_segment_t* __restrict__ S, uint32_t n,
+                                              uint32_t* fanout) {
+  if (n != 4) return false;
+  bool ok = true;
+#pragma unroll
+  for (int s = 0; s < 4; ++s)
+    ok = ok && S[s].width == 4u && S[s].row_stride == 4 && S[s].fanout == S[0].fanout;
+  *fanout = S[0].fanout;
+  return ok;
+}
+
+// Base address (tile row 0) of the segment at column 4 * (lane & 3) of a quad
+// band, replica f (source segments: f = 0 and fan-out 0).
+template <class Sh>
+__device__ __forceinline__ uintptr_t quad_base(const reshard_segment_t* __restrict__ S,
+                                               const uint32_t* __restrict__ refs, const Sh& sh, uint32_t r0,
+                                               bool dst, uint32_t f) {
+  const uint32_t want = 4u * (threadIdx.x & 3u);
+  uintptr_t base = 0;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const uintptr_t p = (dst ? sh.ptr(refs[S[s].ptr + f]) : sh.ptr(S[s].ptr)) + uint64_t(S[s].offset) +
+                        uint64_t(r0) * 4u;
+    base = S[s].col == want ? p : base;
+  }
+  return base;
+}
+
 // A window band at most 16 bytes wide, without LDS: each lane owns rows
 // r = k * kBlock + lane of the tile, builds each row in one 16-byte register
 // from every source segment (shifted to its column), then writes each
 // destination segment's bytes of it to every replica.  Consecutive lanes touch
-// consecutive rows, so packed segments give contiguous wave accesses.
-template <class Sh>
-__device__ void window_rows(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
+// consecutive rows, so packed segments give contiguous wave accesses.  When a
+// 16-byte band is cut into four packed 4-byte column runs (a bf16 pair or an
+// fp32 column per shard) on one side, the four lanes of a quad exchange words
+// (quad_transpose): a lane then moves four consecutive rows of one run, 16
+// contiguous bytes, in one access instead of four.
+template <int kRows, class Sh>
+__device__ __forceinline__ void window_rows(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
                             const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
-  constexpr int kRows = int(rs::kRowsPerLane);
   const uint32_t rows = D.extent[0], per_tile = D.extent[1];
   const uint32_t r0 = tile * per_tile;
   const uint32_t hr = min(per_tile, rows - r0);
   const reshard_segment_t* src_segs = segs + D.src_ptr;
   const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+  const uint32_t quad_row = threadIdx.x & ~3u;  // first of the quad's rows (plus k * kBlock)
+  const uint32_t used = (hr + kBlock - 1) / kBlock;  // row slots k of this tile that hold rows
+  const bool wide = D.run_bytes == 16u;
   u32x4 v[kRows];
 #pragma unroll
   for (int k = 0; k < kRows; ++k) v[k] = u32x4{0, 0, 0, 0};
-  for (uint32_t s = 0; s < D.dst_ref_begin; ++s) {
-    const reshard_segment_t S = src_segs[s];
-    const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+  uint32_t src_fan;
+  if (wide && quad_segments(src_segs, D.dst_ref_begin, &src_fan)) {
+    // lane j loads four rows of the run at column 4j, then the quad transposes
+    const uintptr_t g = quad_base(src_segs, refs, sh, r0, false, 0);
 #pragma unroll
     for (int k = 0; k < kRows; ++k) {
-      const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
-      if (r < hr) {
-        const u32x4 x = shift_left_bytes(load_bytes(g + uint64_t(r) * uint64_t(S.row_stride), S.width), S.col);
-        v[k] = u32x4{v[k].x | x.x, v[k].y | x.y, v[k].z | x.z, v[k].w | x.w};
+      const uint32_t r = uint32_t(k * kBlock) + quad_row;
+      if (uint32_t(k) >= used) continue;
+      if (r + 4 <= hr) {
+        v[k] = load_16_unaligned(g + uint64_t(r) * 4u);
+      } else {
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (uint32_t i = 0; i < 4; ++i)
+          if (r + i < hr) w[i] = __builtin_nontemporal_load(as_global<const u32_u>(g + uint64_t(r + i) * 4u));
+        v[k] = u32x4{w[0], w[1], w[2], w[3]};
       }
     }
+#pragma unroll
+    for (int k = 0; k < kRows; ++k)
+      if (uint32_t(k) < used) v[k] = quad_transpose(v[k]);  // uniform: every lane takes part
+  } else {
+    for (uint32_t s = 0; s < D.dst_ref_begin; ++s) {
+      const reshard_segment_t S = src_segs[s];
+      const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+        const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
+        if (r < hr) {
+          const u32x4 x = shift_left_bytes(load_bytes(g + uint64_t(r) * uint64_t(S.row_stride), S.width), S.col);
+          v[k] = u32x4{v[k].x | x.x, v[k].y | x.y, v[k].z | x.z, v[k].w | x.w};
+        }
+      }
+    }
+  }
+  uint32_t dst_fan;
+  if (wide && quad_segments(dst_segs, D.fanout, &dst_fan)) {
+    // the quad transposes, then lane j stores four rows of the run at column 4j
+#pragma unroll
+    for (int k = 0; k < kRows; ++k)
+      if (uint32_t(k) < used) v[k] = quad_transpose(v[k]);  // uniform: every lane takes part
+    for (uint32_t f = 0; f < dst_fan; ++f) {
+      const uintptr_t g = quad_base(dst_segs, refs, sh, r0, true, f);
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+        const uint32_t r = uint32_t(k * kBlock) + quad_row;
+        if (uint32_t(k) >= used) continue;
+        if (r + 4 <= hr) {
+          store_bytes(g + uint64_t(r) * 4u, v[k], 16);
+        } else {
+          const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+          for (uint32_t i = 0; i < 4; ++i)
+            if (r + i < hr) __builtin_nontemporal_store(w[i], as_global<u32_u>(g + uint64_t(r + i) * 4u));
+        }
+      }
+    }
+    return;
   }
   for (uint32_t s = 0; s < D.fanout; ++s) {
     const reshard_segment_t S = dst_segs[s];
@@ -573,7 +684,7 @@ __device__ void window_rows(const reshard_descriptor_t& D, const reshard_segment
 // Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
 // aligned to the descriptor's unit, or replicas differ in 16-byte phase.
 template <class Sh>
-__device__ void copy_bytes(const reshard_descriptor_t& D, uint32_t unit, uint32_t mode,
+__device__ __forceinline__ void copy_bytes(const reshard_descriptor_t& D, uint32_t unit, uint32_t mode,
                            const uint8_t* src, const Sh& sh, uint32_t lo, uint32_t hi) {
   const uintptr_t d0 = sh.dst(0);
   for (uint32_t f = lo + threadIdx.x; f < hi; f += kBlock) {
@@ -721,7 +832,9 @@ enum KernelKind : int {
   kKindChunks = 1,   // every descriptor DST_CHUNKS
   kKindCopy = 2,     // ITEMS, DST_CHUNKS and CONVERT; no LDS
   kKindAll = 3,      // any mode, LDS window included
-  kKindAligned = 4,  // added to kKindChunks when every shard pointer is 16-byte
+  kKindQuadRows = 4, // every descriptor a 16-byte row-mode band with the quad exchange
+                     // (kQuadRowsPerLane rows per lane): no LDS, fewer registers
+  kKindAligned = 8,  // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
 
@@ -752,22 +865,34 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t unit = kKind == kKindItems16 ? 16u : unit_mode & 0xffffu;
   const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
                         : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
+                        : kKind == kKindQuadRows ? uint32_t(RESHARD_DESC_WINDOW)
                                                : unit_mode >> 16;
+  if constexpr (kKind == kKindQuadRows) {
+    const Shards<kKarg> wsh{table, &karg, refs};
+    window_rows<int(rs::kQuadRowsPerLane)>(D, segs, refs, wsh, t - tile_begin[lo]);
+    return;
+  }
   if constexpr (kKind == kKindAll) {
     if (mode == RESHARD_DESC_WINDOW) {  // any alignment: global chunks follow the addresses
       __shared__ __attribute__((aligned(16))) uint8_t window[rs::kWindowBytes];
       const Shards<kKarg> wsh{table, &karg, refs};
-      if (D.run_bytes <= uint32_t(rs::kRowModeBytes)) window_rows(D, segs, refs, wsh, t - tile_begin[lo]);
-      else window_tile(D, segs, refs, wsh, t - tile_begin[lo], window);
+      // row mode takes the band's tile rows / kBlock rows per lane
+      if (D.run_bytes > uint32_t(rs::kRowModeBytes))
+        window_tile(D, segs, refs, wsh, t - tile_begin[lo], window);
+      else if (D.extent[1] == rs::kQuadRowsPerLane * uint32_t(kBlock))
+        window_rows<int(rs::kQuadRowsPerLane)>(D, segs, refs, wsh, t - tile_begin[lo]);
+      else
+        window_rows<int(rs::kRowsPerLane)>(D, segs, refs, wsh, t - tile_begin[lo]);
       return;
     }
   }
+  if constexpr (kKind != kKindQuadRows) {
   const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;
   const uint32_t first = (t - tile_begin[lo]) * rs::kTileItems;
   const uint32_t last = min(first + rs::kTileItems, items);
   const Shards<kKarg> sh{table, &karg, refs + D.dst_ref_begin};
   const uint8_t* src = reinterpret_cast<const uint8_t*>(sh.ptr(D.src_ptr));
-  if constexpr (kKind >= kKindCopy) {
+  if constexpr (kKind == kKindCopy || kKind == kKindAll) {
     if (mode == RESHARD_DESC_CONVERT) {  // checks its own alignment per item
       const bool aligned = (flags & kAllAligned16) != 0;
       switch (unit) {
@@ -811,17 +936,21 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
       default: copy_items<uint8_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
     }
   }
+  }  // kKind != kKindQuadRows
 }
 
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs) {
-  bool items16 = true, chunks = true, window = false;
+  bool items16 = true, chunks = true, quad_rows = true, window = false;
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
     if (D.mode != RESHARD_DESC_DST_CHUNKS) chunks = false;
+    if (D.mode != RESHARD_DESC_WINDOW || D.run_bytes > uint32_t(rs::kRowModeBytes) ||
+        D.extent[1] != rs::kQuadRowsPerLane * uint32_t(kBlock))
+      quad_rows = false;
     if (D.mode == RESHARD_DESC_WINDOW) window = true;
   }
-  return items16 ? kKindItems16 : chunks ? kKindChunks : window ? kKindAll : kKindCopy;
+  return items16 ? kKindItems16 : chunks ? kKindChunks : quad_rows ? kKindQuadRows : window ? kKindAll : kKindCopy;
 }
 
 template <bool kKarg, int kVariant>
@@ -855,6 +984,10 @@ void launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descripto
     case kKindCopy:
       launch_kind<kKarg, kKindCopy>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
                                     n_tiles, per_xcd, flags);
+      break;
+    case kKindQuadRows:
+      launch_kind<kKarg, kKindQuadRows>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
+                                        n_tiles, per_xcd, flags);
       break;
     default:
       launch_kind<kKarg, kKindAll>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,

@@ -95,7 +95,7 @@ def test_misaligned_shard_pointers(misalign):
     specs = [W.uneven(50, 31).tensors[0], W.ffn_up(112, 64).tensors[0]] + \
         [s for s in small_specs() if s.name in ("conv_f32_bf16", "conv_bf16_f32_ragged", "strips_fanout",
                                                 "strips_rep_src", "chunked_bf16", "strips_nine",
-                                                "narrow_rep", "narrow_scatter")]
+                                                "narrow_rep", "narrow_scatter", "narrow_gather_rep", "narrow_bf16_cols")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 

@@ -1,0 +1,50 @@
+"""Resource checks of the gfx950 copy kernel, from the compiler's own kernel
+descriptors (hipcc cross-compiles on a machine without a GPU): no kernel variant
+may use scratch memory (a stack frame or a spilled kernel argument turns the
+copy into a scratch-bound one), and each stays within 64 VGPRs so that eight
+waves fit on a SIMD."""
+import os
+import re
+import subprocess
+
+import pytest
+
+from dtensor_layout_movement_amd import build as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def kernel_meta(tmp_path_factory):
+    out = tmp_path_factory.mktemp("isa") / "reshard.s"
+    flags = [f for f in B.HIP_FLAGS if f not in ("-fPIC", "-Wall")]
+    cmd = [B.hipcc(), *flags, "--cuda-device-only", "-S", "-I", B.INCLUDE, "-I", B.CSRC,
+           os.path.join(B.CSRC, "reshard.hip"), "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr[-2000:]
+    text = out.read_text()
+    kernels = {}
+    for block in re.findall(r"\n  - \.agpr_count:.*?(?=\n  - \.agpr_count:|\namdhsa\.|\n\s*\.end_amdgpu_metadata)", text, re.S):
+        name = re.search(r"\.name:\s+(\S+)", block).group(1)
+        kernels[name] = {
+            "private": int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", block).group(1)),
+            "vgpr": int(re.search(r"\.vgpr_count:\s+(\d+)", block).group(1)),
+        }
+    return kernels
+
+
+def test_every_variant_is_compiled(kernel_meta):
+    names = [n for n in kernel_meta if "reshard_copy_kernel" in n]
+    # two pointer placements x six variants (16-byte items, destination chunks,
+    # aligned destination chunks, copy modes, quad row bands, all modes)
+    assert len(names) == 12, sorted(kernel_meta)
+
+
+def test_no_scratch(kernel_meta):
+    for name, meta in kernel_meta.items():
+        assert meta["private"] == 0, (name, meta)
+
+
+def test_eight_waves_per_simd(kernel_meta):
+    for name, meta in kernel_meta.items():
+        assert meta["vgpr"] <= 64, (name, meta)

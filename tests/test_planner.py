@@ -55,6 +55,14 @@ def small_specs():
         T("narrow_gather", (4099, 8), torch.bfloat16, (4,), (1,), (2,), (0,)),
         T("narrow_fp8_3d", (6, 7, 24), torch.uint8, (2, 3), (0, 2), (4,), (2,)),
         T("narrow_rep", (301, 12), torch.float32, (3,), (1,), (2, 3), (RR, 1)),
+        # 16-byte rows cut into four 4-byte column runs (quad transposes), row
+        # counts that leave partial quads
+        T("narrow_scatter_rep", (1031, 8), torch.bfloat16, (2,), (0,), (2, 4), (RR, 1)),
+        T("narrow_f32_cols", (2053, 4), torch.float32, (3,), (0,), (4,), (1,)),
+        T("narrow_gather_rep", (1029, 8), torch.bfloat16, (2, 4), (RR, 1), (3,), (0,)),
+        # row mode without the quad exchange: single bf16 columns, 8-byte rows
+        T("narrow_bf16_cols", (1037, 8), torch.bfloat16, (2,), (0,), (8,), (1,)),
+        T("narrow_8byte_rows", (2051, 4), torch.bfloat16, (3,), (0,), (2,), (1,)),
         T("wide_window", (37, 4001), torch.bfloat16, (3,), (1,), (5,), (0,)),
         # misaligned column strips (destination-aligned chunks): row cuts inside a
         # destination shard, destination replicas, source replicas, nine strips,
@@ -359,6 +367,21 @@ def test_descriptor_modes():
         assert modes([small[name]]) == {(R.DESC_DST_CHUNKS, 4 if small[name].dtype == torch.float32 else 2)}, name
     # a 4-byte piece in 16804-byte rows: too wide for a window, so per piece
     assert {m for m, _ in modes([small["narrow_wide_rows"]])} == {R.DESC_DST_CHUNKS, R.DESC_ITEMS}
+
+
+def test_row_mode_tile_rows():
+    """Row-mode bands (at most 16 bytes wide) take 1024 rows per tile, or 512 when
+    one side is four packed 4-byte column runs (quad exchange); wider bands as
+    many rows as fit a 16 KiB LDS window."""
+    small = {s.name: s for s in small_specs()}
+    want = {"narrow_scatter": 512, "narrow_gather": 512, "narrow_f32_cols": 512, "narrow_scatter_rep": 512,
+            "narrow_gather_rep": 512, "narrow_bf16_cols": 1024, "narrow_8byte_rows": 1024,
+            "narrow_fp8_3d": 16384 // 32}
+    for name, rows in want.items():
+        with Plan([small[name]]) as plan:
+            descs, _ = R.reshard_plan_descriptors(plan.handle)
+        assert {d["mode"] for d in descs} == {R.DESC_WINDOW}, name
+        assert {d["extent"][1] for d in descs} == {rows}, name
 
 
 def test_window_segments_worked_example():
