@@ -876,11 +876,11 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     if (mode == RESHARD_DESC_WINDOW) {  // any alignment: global chunks follow the addresses
       __shared__ __attribute__((aligned(16))) uint8_t window[rs::kWindowBytes];
       const Shards<kKarg> wsh{table, &karg, refs};
-      // row mode takes the band's tile rows / kBlock rows per lane
+      // one row-mode build serves every band here (a band's tile may have fewer
+      // rows than its slots): a second one would raise the register count of
+      // the whole kernel
       if (D.run_bytes > uint32_t(rs::kRowModeBytes))
         window_tile(D, segs, refs, wsh, t - tile_begin[lo], window);
-      else if (D.extent[1] == rs::kQuadRowsPerLane * uint32_t(kBlock))
-        window_rows<int(rs::kQuadRowsPerLane)>(D, segs, refs, wsh, t - tile_begin[lo]);
       else
         window_rows<int(rs::kRowsPerLane)>(D, segs, refs, wsh, t - tile_begin[lo]);
       return;

@@ -103,7 +103,8 @@ def test_misaligned_shard_pointers(misalign):
 def test_batched_mixed_dtypes():
     specs = list(W.ffn_refit(2, 64, 224).tensors) + [W.uneven(77, 53).tensors[0]] + \
         [s for s in small_specs() if s.name in ("u8_odd", "i64", "five_d", "rep_src", "conv_f32_f16_ragged",
-                                                "conv_f16_f32_nested")]
+                                                "conv_f16_f32_nested", "narrow_scatter", "narrow_gather_rep",
+                                                "narrow_bf16_cols", "wide_window")]
     run_parity(specs, "raw", 5)
 
 

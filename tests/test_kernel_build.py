@@ -1,8 +1,8 @@
 """Resource checks of the gfx950 copy kernel, from the compiler's own kernel
-descriptors (hipcc cross-compiles on a machine without a GPU): no kernel variant
-may use scratch memory (a stack frame or a spilled kernel argument turns the
-copy into a scratch-bound one), and each stays within 64 VGPRs so that eight
-waves fit on a SIMD."""
+descriptors and resource-usage remarks (hipcc cross-compiles on a machine
+without a GPU): no kernel variant may use scratch memory (a stack frame or a
+spilled kernel argument turns the copy into a scratch-bound one), and each keeps
+eight waves per SIMD."""
 import os
 import re
 import subprocess
@@ -18,17 +18,27 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 def kernel_meta(tmp_path_factory):
     out = tmp_path_factory.mktemp("isa") / "reshard.s"
     flags = [f for f in B.HIP_FLAGS if f not in ("-fPIC", "-Wall")]
-    cmd = [B.hipcc(), *flags, "--cuda-device-only", "-S", "-I", B.INCLUDE, "-I", B.CSRC,
-           os.path.join(B.CSRC, "reshard.hip"), "-o", str(out)]
+    cmd = [B.hipcc(), *flags, "--cuda-device-only", "-S", "-Rpass-analysis=kernel-resource-usage",
+           "-I", B.INCLUDE, "-I", B.CSRC, os.path.join(B.CSRC, "reshard.hip"), "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     text = out.read_text()
     kernels = {}
+    occupancy = {}
+    name = None
+    for line in res.stderr.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+        m = re.search(r"Occupancy \[waves/SIMD\]: (\d+)", line)
+        if m and name:
+            occupancy[name] = int(m.group(1))
     for block in re.findall(r"\n  - \.agpr_count:.*?(?=\n  - \.agpr_count:|\namdhsa\.|\n\s*\.end_amdgpu_metadata)", text, re.S):
         name = re.search(r"\.name:\s+(\S+)", block).group(1)
         kernels[name] = {
             "private": int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", block).group(1)),
             "vgpr": int(re.search(r"\.vgpr_count:\s+(\d+)", block).group(1)),
+            "occupancy": occupancy.get(name),
         }
     return kernels
 
@@ -47,4 +57,4 @@ def test_no_scratch(kernel_meta):
 
 def test_eight_waves_per_simd(kernel_meta):
     for name, meta in kernel_meta.items():
-        assert meta["vgpr"] <= 64, (name, meta)
+        assert meta["occupancy"] == 8 and meta["vgpr"] <= 64, (name, meta)
