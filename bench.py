@@ -49,7 +49,7 @@ HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, decimal GB/s
 METRIC = "reshard execute GB/s (bytes read+written) and % of MI355X HBM peak; plan time us"
 DEFAULT_WORKLOAD = "ffn_up_14336x4096"
 KERNEL_SOURCES = [os.path.join(ROOT, "dtensor_layout_movement_amd", "csrc", f)
-                  for f in ("reshard.hip", "plan.h", "plan.cpp")]
+                  for f in ("kernel.hip", "kernel.h", "plan.h", "plan.cpp")]
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_NAME = "reshard_copy_kernel"
 

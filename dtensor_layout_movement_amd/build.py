@@ -16,7 +16,7 @@ REPO_DIR = os.path.dirname(PKG_DIR)
 CSRC = os.path.join(PKG_DIR, "csrc")
 INCLUDE = os.path.join(REPO_DIR, "include")
 LIB_PATH = os.path.join(PKG_DIR, "libreshard.so")
-SOURCES = [os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "reshard.hip")]
+SOURCES = [os.path.join(CSRC, "plan.cpp"), os.path.join(CSRC, "kernel.hip"), os.path.join(CSRC, "reshard.hip")]
 
 # Packed-fp32 instructions are kept out of every HIP object; the library does no
 # floating point, so this costs nothing.
@@ -35,7 +35,7 @@ def hipcc() -> str:
 
 
 def build(verbose: bool = False) -> str:
-    """Compile plan.cpp + reshard.hip into libreshard.so; return its path."""
+    """Compile plan.cpp + kernel.hip + reshard.hip into libreshard.so; return its path."""
     tmp = LIB_PATH + ".tmp"
     cmd = [hipcc(), *HIP_FLAGS, "-shared", "-I", INCLUDE, "-I", CSRC, *SOURCES, "-o", tmp]
     if verbose:

@@ -1,0 +1,37 @@
+// Launch interface of the gfx950 copy kernel (kernel.hip), used by the host
+// code of the C ABI (reshard.hip).
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <vector>
+
+#include "reshard.h"
+
+namespace rs {
+
+constexpr uint32_t kXcds = 8;       // MI355X: workgroups go round-robin over 8 XCDs
+constexpr uint32_t kXcdGroup = 64;  // consecutive tiles one XCD takes at a time
+constexpr int kKargPtrs = 120;      // pointer slots passed in kernel arguments
+
+// Shard pointers passed by value in the kernel arguments (plans with at most
+// kKargPtrs of them).
+struct KargPtrs {
+  const void* p[kKargPtrs];
+};
+
+// Bits of the kernel's `flags` argument.
+constexpr uint32_t kAllAligned16 = 1;  // every shard pointer of this execute is 16-byte aligned
+
+// The kernel variant of a plan: the smallest build that covers its descriptors.
+int kernel_kind(const std::vector<reshard_descriptor_t>& descs);
+
+// One launch of variant `kind` with `n_wg` workgroups on `stream`.  Shard
+// pointers come from `karg` when `table` is NULL, else from the device table.
+void launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,
+                 uint32_t n_desc, const uint32_t* tile_begin, const uint32_t* refs,
+                 const reshard_segment_t* segs, const void* const* table, const KargPtrs& karg,
+                 uint32_t n_tiles, uint32_t per_xcd, uint32_t flags);
+
+}  // namespace rs

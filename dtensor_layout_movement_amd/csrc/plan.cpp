@@ -1,5 +1,5 @@
 // Host planner: layouts -> boxes -> replica groups -> overlaps -> descriptors.
-// Plain C++17; the device side lives in reshard.hip.
+// Plain C++17; the device side lives in kernel.hip, the C ABI in reshard.hip.
 #include "plan.h"
 
 #include <algorithm>

@@ -1,15 +1,6 @@
-// C ABI of the reshard library and its gfx950 copy kernel.
-//
-// Execute = one launch of reshard_copy_kernel.  The plan's descriptor table
-// sits in device memory together with the first tile of every descriptor.  One
-// workgroup copies one tile (4 KiB of source for 16-byte items): it finds its
-// descriptor by a binary search over the tile prefix, then every thread loads
-// its item(s) once and stores them to each destination replica (the single-GPU
-// form of "send each contribution once, replicate locally": techfeed.io
-// write-up, "NVIDIA's NVLink implementation" section).  Many small workgroups
-// let the dispatcher balance the load; groups of consecutive tiles are kept on
-// one XCD so that rows straddling tile edges merge in that XCD's L2.  Data only moves
-// through integer registers, so the copy is bit-exact for every dtype.
+// C ABI of the reshard library: layouts, host plans, the device descriptor
+// table, the pointer slots of large plans and execute, which is one launch of
+// the gfx950 copy kernel (kernel.hip).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -19,6 +10,7 @@
 #include <string>
 #include <vector>
 
+#include "kernel.h"
 #include "plan.h"
 #include "reshard.h"
 
@@ -28,15 +20,7 @@ struct reshard_layout_s {
 
 namespace {
 
-constexpr int kBlock = int(rs::kTileThreads);  // threads per workgroup (4 wave64s)
-constexpr uint32_t kXcds = 8;          // MI355X: workgroups go round-robin over 8 XCDs
-constexpr uint32_t kXcdGroup = 64;     // consecutive tiles one XCD takes at a time
-constexpr int kKargPtrs = 120;         // pointer slots passed in kernel arguments
-constexpr int kSlots = 8;              // device pointer-table slots for bigger plans
-
-struct KargPtrs {
-  const void* p[kKargPtrs];
-};
+constexpr int kSlots = 8;  // device pointer-table slots for bigger plans
 
 thread_local std::string g_err;
 
@@ -50,952 +34,6 @@ reshard_status_t hip_fail(hipError_t e, const char* what) {
               std::string(what) + ": " + hipGetErrorString(e));
 }
 
-// ---------------------------------------------------------------- device code
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-// q = n / d for n < 2^31 with the planner's round-up multiplier (m, s).
-__device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t s) {
-  return (__umulhi(n, m) + n) >> s;
-}
-
-// Row origin offsets (relative to the shard pointers) and item index of item f.
-struct ItemPos {
-  uint64_t src, dst;  // byte offsets of the row origin
-  uint32_t col;       // item index inside the row
-};
-
-__device__ __forceinline__ ItemPos item_pos(const reshard_descriptor_t& D, uint32_t f) {
-  const uint32_t row = div_magic(f, D.magic[0][0], D.magic[0][1]);
-  const uint32_t t = div_magic(row, D.magic[1][0], D.magic[1][1]);
-  const uint32_t i2 = row - t * D.extent[2];
-  const uint32_t i0 = div_magic(t, D.magic[2][0], D.magic[2][1]);
-  const uint32_t i1 = t - i0 * D.extent[1];
-  ItemPos o;
-  o.col = f - row * D.row_items;
-  o.src = uint64_t(D.src_offset) + uint64_t(i0) * uint64_t(D.src_stride[0]) +
-          uint64_t(i1) * uint64_t(D.src_stride[1]) + uint64_t(i2) * uint64_t(D.src_stride[2]);
-  o.dst = uint64_t(D.dst_offset) + uint64_t(i0) * uint64_t(D.dst_stride[0]) +
-          uint64_t(i1) * uint64_t(D.dst_stride[1]) + uint64_t(i2) * uint64_t(D.dst_stride[2]);
-  return o;
-}
-
-template <typename V>
-__device__ __forceinline__ V load_item(const uint8_t* p) {
-  return __builtin_nontemporal_load(reinterpret_cast<const V*>(p));
-}
-
-template <typename V>
-__device__ __forceinline__ void store_item(uint8_t* p, V v) {
-  __builtin_nontemporal_store(v, reinterpret_cast<V*>(p));
-}
-
-// Global-memory (address space 1) pointer from an address computed as an
-// integer, so that accesses compile to global_* rather than flat_* instructions.
-template <typename T>
-using global_ptr = __attribute__((address_space(1))) T*;
-template <typename T>
-__device__ __forceinline__ global_ptr<T> as_global(uintptr_t a) {
-  return reinterpret_cast<global_ptr<T>>(a);
-}
-
-// 16 bytes from any byte address (gfx950 global loads need no alignment).
-typedef uint32_t u32x4_u __attribute__((ext_vector_type(4), aligned(1)));
-__device__ __forceinline__ u32x4 load_16_unaligned(uintptr_t a) {
-  return __builtin_nontemporal_load(as_global<const u32x4_u>(a));
-}
-
-// Shard pointers of one descriptor.  kKarg: the pointer array sits in the kernel
-// arguments; otherwise in a device table.  Either way every lookup is a scalar
-// load from a known address space.
-template <bool kKarg>
-struct Shards {
-  const void* const* table;
-  const KargPtrs* karg;
-  const uint32_t* refs;  // this descriptor's fan-out list
-  __device__ __forceinline__ uintptr_t ptr(uint32_t i) const {
-    if constexpr (kKarg) return reinterpret_cast<uintptr_t>(karg->p[i]);
-    else return reinterpret_cast<uintptr_t>(table[i]);
-  }
-  __device__ __forceinline__ uintptr_t dst(uint32_t r) const { return ptr(refs[r]); }
-};
-
-// ITEMS mode: items [lo, hi) (at most kBlock * U of them) with V-sized accesses.
-// All loads are issued before the stores; each item is stored to every replica.
-template <typename V, int U, class Sh>
-__device__ __forceinline__ void copy_items(const reshard_descriptor_t& D, const uint8_t* src,
-                                           const Sh& sh, uint32_t lo, uint32_t hi) {
-  V v[U];
-  uint64_t doff[U];
-  bool ok[U];
-#pragma unroll
-  for (int k = 0; k < U; ++k) {
-    const uint32_t f = lo + uint32_t(k * kBlock) + threadIdx.x;
-    ok[k] = f < hi;
-    const ItemPos o = item_pos(D, ok[k] ? f : lo);
-    const uint64_t c = uint64_t(o.col) * sizeof(V);
-    doff[k] = o.dst + c;
-    if (ok[k]) v[k] = load_item<V>(src + o.src + c);
-  }
-  for (uint32_t r = 0; r < D.fanout; ++r) {
-    uint8_t* dst = reinterpret_cast<uint8_t*>(sh.dst(r));
-#pragma unroll
-    for (int k = 0; k < U; ++k)
-      if (ok[k]) store_item<V>(dst + doff[k], v[k]);
-  }
-}
-
-// Byte range [lo, hi) of the destination row starting at `row` (absolute address
-// of replica 0) that chunk `col` covers: the row's part of the col-th 16-byte
-// aligned block it touches.
-__device__ __forceinline__ void chunk_range(uintptr_t row, uint32_t run, uint32_t col,
-                                            uintptr_t* lo, uintptr_t* hi) {
-  const uintptr_t block = (row & ~uintptr_t(15)) + uintptr_t(col) * 16;
-  *lo = block > row ? block : row;
-  *hi = block + 16 < row + run ? block + 16 : row + run;
-  if (*hi < *lo) *hi = *lo;  // a block past the row's end: empty
-}
-
-typedef uint64_t u64_u __attribute__((aligned(1)));
-typedef uint32_t u32_u __attribute__((aligned(1)));
-typedef uint16_t u16_u __attribute__((aligned(1)));
-
-// v >> (8 * s) as a 128-bit little-endian value, 1 <= s <= 15.
-__device__ __forceinline__ u32x4 shift_right_bytes(u32x4 v, uint32_t s) {
-  uint64_t lo = (uint64_t(v.y) << 32) | v.x, hi = (uint64_t(v.w) << 32) | v.z;
-  const uint32_t b = 8 * s;
-  if (b >= 64) {
-    lo = hi >> (b - 64);
-    hi = 0;
-  } else {
-    lo = (lo >> b) | (hi << (64 - b));
-    hi >>= b;
-  }
-  return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
-}
-
-// The first n < 16 bytes of v to address d, with at most four stores.  They are
-// streaming (non-temporal) like the full 16-byte stores around them: a partial
-// chunk shares its destination line with full chunks, and mixing temporal and
-// streaming stores on one line measured 5% slower on misaligned column strips.
-__device__ __forceinline__ void store_head_bytes(uintptr_t d, u32x4 v, uint32_t n) {
-  uint64_t lo = (uint64_t(v.y) << 32) | v.x;
-  const uint64_t hi = (uint64_t(v.w) << 32) | v.z;
-  if (n & 8) {
-    __builtin_nontemporal_store(lo, as_global<u64_u>(d));
-    d += 8;
-    lo = hi;
-  }
-  if (n & 4) {
-    __builtin_nontemporal_store(uint32_t(lo), as_global<u32_u>(d));
-    d += 4;
-    lo >>= 32;
-  }
-  if (n & 2) {
-    __builtin_nontemporal_store(uint16_t(lo), as_global<u16_u>(d));
-    d += 2;
-    lo >>= 16;
-  }
-  if (n & 1) __builtin_nontemporal_store(uint8_t(lo), as_global<uint8_t>(d));
-}
-
-// DST_CHUNKS mode: chunks [lo, hi).  Every non-empty chunk is one 16-byte load
-// that stays inside its source row: at the chunk's own bytes for a full chunk,
-// at the row start for the head chunk and at the row end minus 16 for the tail
-// chunk (rows are at least kChunkedMinRun bytes).  A full chunk is then one
-// aligned 16-byte store per replica; a partial one (fewer than 16 bytes) at most
-// four.  All loads are issued before any store.  Replicas share replica 0's
-// 16-byte phase.
-template <int U, class Sh>
-__device__ __forceinline__ void copy_chunks(const reshard_descriptor_t& D, const uint8_t* src,
-                                            const Sh& sh, uint32_t lo, uint32_t hi) {
-  const uintptr_t d0 = sh.dst(0);
-  const uint32_t run = D.run_bytes;
-  u32x4 v[U];
-  uintptr_t clo[U];  // first covered destination byte, replica-0 address
-  uint32_t n[U];     // covered bytes: 16 (full), 1..15 (partial) or 0
-  uint32_t skip[U];  // leading bytes of the load that precede the chunk (tail chunk only)
-#pragma unroll
-  for (int k = 0; k < U; ++k) {
-    const uint32_t f = lo + uint32_t(k * kBlock) + threadIdx.x;
-    const ItemPos o = item_pos(D, f < hi ? f : lo);
-    const uintptr_t row = d0 + o.dst;
-    uintptr_t chi;
-    chunk_range(row, run, o.col, &clo[k], &chi);
-    n[k] = f < hi ? uint32_t(chi - clo[k]) : 0u;
-    const uint32_t off = uint32_t(clo[k] - row);            // chunk's first byte within the row
-    const uint32_t load_off = off < run - 16 ? off : run - 16;
-    skip[k] = off - load_off;
-    if (n[k] != 0) v[k] = load_16_unaligned(reinterpret_cast<uintptr_t>(src) + o.src + load_off);
-  }
-#pragma unroll
-  for (int k = 0; k < U; ++k)
-    if (n[k] != 0 && skip[k] != 0) v[k] = shift_right_bytes(v[k], skip[k]);
-  for (uint32_t r = 0; r < D.fanout; ++r) {
-    const uintptr_t shift = sh.dst(r) - d0;
-#pragma unroll
-    for (int k = 0; k < U; ++k) {
-      const uintptr_t d = clo[k] + shift;
-      if (n[k] == 16) __builtin_nontemporal_store(v[k], as_global<u32x4>(d));
-      else if (n[k] != 0) store_head_bytes(d, v[k], n[k]);
-    }
-  }
-}
-
-// ---------------------------------------------------------------- windows
-//
-// A RESHARD_DESC_WINDOW tile moves rows [r0, r0 + hr) of a band through an LDS
-// window (row r at r * pitch).  Phase 1 reads every source segment into the
-// window, phase 2 writes every destination segment from it to each replica.
-// Global accesses are 16-byte chunks aligned to the global address; the LDS side
-// takes whatever alignment that leaves.  A segment whose rows are packed in its
-// shard (row stride == width) is handled as one contiguous run, so narrow column
-// runs still move in 16-byte global accesses.
-
-typedef uint32_t u32x4_u1 __attribute__((ext_vector_type(4), aligned(1)));
-
-__device__ __forceinline__ u32x4 shift_left_bytes(u32x4 v, uint32_t s) {  // s in [0, 15]
-  if (s == 0) return v;
-  uint64_t lo = (uint64_t(v.y) << 32) | v.x, hi = (uint64_t(v.w) << 32) | v.z;
-  const uint32_t b = 8 * s;
-  if (b >= 64) {
-    hi = lo << (b - 64);
-    lo = 0;
-  } else {
-    hi = (hi << b) | (lo >> (64 - b));
-    lo <<= b;
-  }
-  return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
-}
-
-// Bytes [0, n) of v (n <= 16) into LDS at p, with at most four writes.
-__device__ __forceinline__ void lds_put(uint8_t* p, u32x4 v, uint32_t n) {
-  if (n == 16) {
-    *reinterpret_cast<u32x4_u1*>(p) = v;
-    return;
-  }
-  uint64_t lo = (uint64_t(v.y) << 32) | v.x;
-  const uint64_t hi = (uint64_t(v.w) << 32) | v.z;
-  if (n & 8) {
-    *reinterpret_cast<u64_u*>(p) = lo;
-    p += 8;
-    lo = hi;
-  }
-  if (n & 4) {
-    *reinterpret_cast<u32_u*>(p) = uint32_t(lo);
-    p += 4;
-    lo >>= 32;
-  }
-  if (n & 2) {
-    *reinterpret_cast<u16_u*>(p) = uint16_t(lo);
-    p += 2;
-    lo >>= 16;
-  }
-  if (n & 1) *p = uint8_t(lo);
-}
-
-// n <= 16 bytes from LDS at p into bytes [0, n) of the result.
-__device__ __forceinline__ u32x4 lds_get(const uint8_t* p, uint32_t n) {
-  if (n == 16) return *reinterpret_cast<const u32x4_u1*>(p);
-  uint64_t lo = 0, hi = 0;
-  uint32_t at = 0;  // bytes gathered so far
-  if (n & 8) {
-    lo = *reinterpret_cast<const u64_u*>(p);
-    at = 8;
-  }
-  if (n & 4) {
-    const uint64_t x = *reinterpret_cast<const u32_u*>(p + at);
-    if (at < 8) lo |= x << (8 * at); else hi |= x;
-    at += 4;
-  }
-  if (n & 2) {
-    const uint64_t x = *reinterpret_cast<const u16_u*>(p + at);
-    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
-    at += 2;
-  }
-  if (n & 1) {
-    const uint64_t x = p[at];
-    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
-  }
-  return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
-}
-
-// The len <= 16 bytes at global address lo of a run [base, base + n): bytes
-// [0, len) of the result.  Reads stay inside the run: one 16-byte load when the
-// run is at least 16 bytes long, else pieces of `unit` bytes.
-__device__ __forceinline__ u32x4 load_in_run(uintptr_t base, uint32_t n, uintptr_t lo, uint32_t len,
-                                             uint32_t unit) {
-  if (n >= 16) {
-    const uint32_t off = uint32_t(lo - base);
-    const uint32_t at = off < n - 16 ? off : n - 16;
-    u32x4 v = load_16_unaligned(base + at);
-    return off > at ? shift_right_bytes(v, off - at) : v;
-  }
-  uint64_t w[2] = {0, 0};
-  for (uint32_t b = 0; b < len; b += unit) {
-    uint64_t x;
-    if (unit >= 8) x = *as_global<const u64_u>(lo + b);
-    else if (unit == 4) x = *as_global<const u32_u>(lo + b);
-    else if (unit == 2) x = *as_global<const u16_u>(lo + b);
-    else x = *as_global<const uint8_t>(lo + b);
-    w[b / 8] |= x << (8 * (b % 8));
-  }
-  return u32x4{uint32_t(w[0]), uint32_t(w[0] >> 32), uint32_t(w[1]), uint32_t(w[1] >> 32)};
-}
-
-// Bytes [0, len) of v to global address d (len < 16: at most four stores), all
-// streaming.
-__device__ __forceinline__ void store_chunk(uintptr_t d, u32x4 v, uint32_t len) {
-  if (len == 16) __builtin_nontemporal_store(v, as_global<u32x4_u>(d));
-  else store_head_bytes(d, v, len);
-}
-
-// Where chunk j of a segment's tile lies.  Packed segments: one run of hr*w
-// bytes at g.  Otherwise row r of the tile starts at g + r*stride and has
-// chunks_per_row chunk slots.
-struct SegChunk {
-  uintptr_t lo;      // first global byte (replica-0 address for destinations)
-  uint32_t len;      // bytes, 0 if the slot is empty
-  uint32_t run_off;  // packed: offset of lo in the run; else offset of lo in its row
-  uint32_t row;      // row of lo inside the tile
-  uintptr_t base;    // start of the run (packed) or of the row
-  uint32_t n;        // bytes of the run (packed) or of the row
-};
-
-__device__ __forceinline__ SegChunk seg_chunk(uintptr_t g, uint64_t stride, uint32_t w, uint32_t hr,
-                                              bool packed, uint32_t chunks_per_row, uint32_t j) {
-  SegChunk c;
-  if (packed) {
-    c.base = g;
-    c.n = hr * w;
-    c.row = 0;
-  } else {
-    c.row = j / chunks_per_row;
-    j -= c.row * chunks_per_row;
-    c.base = g + c.row * stride;
-    c.n = w;
-  }
-  const uintptr_t block = (c.base & ~uintptr_t(15)) + uintptr_t(j) * 16;
-  const uintptr_t lo = block > c.base ? block : c.base;
-  const uintptr_t end = c.base + c.n;
-  const uintptr_t hi = block + 16 < end ? block + 16 : end;
-  c.lo = lo;
-  c.len = hi > lo ? uint32_t(hi - lo) : 0u;
-  c.run_off = uint32_t(lo - c.base);
-  return c;
-}
-
-__device__ __forceinline__ uint32_t seg_chunks(uintptr_t g, uint32_t w, uint32_t hr, bool packed,
-                                               uint32_t* chunks_per_row) {
-  *chunks_per_row = (w + 30) / 16;
-  if (packed) return uint32_t(((g & 15) + uint64_t(hr) * w + 15) / 16);
-  return hr * *chunks_per_row;
-}
-
-// LDS address of byte `off` of a packed run (rows of w bytes, window column col).
-__device__ __forceinline__ uint8_t* run_lds(uint8_t* lds, uint32_t pitch, uint32_t col, uint32_t w,
-                                           uint32_t off) {
-  const uint32_t r = off / w;
-  return lds + r * pitch + col + (off - r * w);
-}
-
-constexpr int kWindowBatch = 4;  // chunks per thread with loads in flight together
-
-template <class Sh>
-__device__ __forceinline__ void window_tile(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
-                            const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile,
-                            uint8_t* lds) {
-  const uint32_t rows = D.extent[0], per_tile = D.extent[1], pitch = D.row_items;
-  const uint32_t r0 = tile * per_tile;
-  const uint32_t hr = min(per_tile, rows - r0);
-  const uint32_t unit = D.unit;
-  const reshard_segment_t* src_segs = segs + D.src_ptr;
-  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
-
-  // phase 1: source segments -> window
-  for (uint32_t s = 0; s < D.dst_ref_begin; ++s) {
-    const reshard_segment_t S = src_segs[s];
-    const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
-    const bool packed = uint64_t(S.row_stride) == S.width;
-    uint32_t cpr;
-    const uint32_t n = seg_chunks(g, S.width, hr, packed, &cpr);
-    for (uint32_t base = 0; base < n; base += kBlock * kWindowBatch) {
-      u32x4 v[kWindowBatch];
-      SegChunk c[kWindowBatch];
-#pragma unroll
-      for (int k = 0; k < kWindowBatch; ++k) {
-        const uint32_t j = base + uint32_t(k * kBlock) + threadIdx.x;
-        c[k] = seg_chunk(g, uint64_t(S.row_stride), S.width, hr, packed, cpr, j < n ? j : 0);
-        if (j >= n) c[k].len = 0;
-        if (c[k].len) v[k] = load_in_run(c[k].base, c[k].n, c[k].lo, c[k].len, unit);
-      }
-#pragma unroll
-      for (int k = 0; k < kWindowBatch; ++k) {
-        if (!c[k].len) continue;
-        if (!packed) {
-          lds_put(lds + c[k].row * pitch + S.col + c[k].run_off, v[k], c[k].len);
-          continue;
-        }
-        // a packed chunk may cover several window rows
-        uint32_t off = c[k].run_off, left = c[k].len;
-        u32x4 x = v[k];
-        while (left) {
-          const uint32_t in_row = S.width - off % S.width;
-          const uint32_t take = left < in_row ? left : in_row;
-          lds_put(run_lds(lds, pitch, S.col, S.width, off), x, take);
-          left -= take;
-          off += take;
-          if (left) x = shift_right_bytes(x, take);
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  // phase 2: window -> destination segments, every replica
-  for (uint32_t s = 0; s < D.fanout; ++s) {
-    const reshard_segment_t S = dst_segs[s];
-    const uint64_t row_off = uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
-    const uintptr_t g = sh.ptr(refs[S.ptr]) + row_off;
-    const bool packed = uint64_t(S.row_stride) == S.width;
-    uint32_t cpr;
-    const uint32_t n = seg_chunks(g, S.width, hr, packed, &cpr);
-    for (uint32_t j = threadIdx.x; j < n; j += kBlock) {
-      const SegChunk c = seg_chunk(g, uint64_t(S.row_stride), S.width, hr, packed, cpr, j);
-      if (!c.len) continue;
-      u32x4 v;
-      if (!packed) {
-        v = lds_get(lds + c.row * pitch + S.col + c.run_off, c.len);
-      } else {
-        uint32_t off = c.run_off, got = 0;
-        v = u32x4{0, 0, 0, 0};
-        while (got < c.len) {
-          const uint32_t in_row = S.width - off % S.width;
-          const uint32_t take = c.len - got < in_row ? c.len - got : in_row;
-          const u32x4 part = lds_get(run_lds(lds, pitch, S.col, S.width, off), take);
-          const u32x4 sh_part = shift_left_bytes(part, got);
-          v = u32x4{v.x | sh_part.x, v.y | sh_part.y, v.z | sh_part.z, v.w | sh_part.w};
-          got += take;
-          off += take;
-        }
-      }
-      for (uint32_t r = 0; r < S.fanout; ++r) {
-        const uintptr_t d = sh.ptr(refs[S.ptr + r]) + row_off + (c.lo - g);
-        store_chunk(d, v, c.len);
-      }
-    }
-  }
-}
-
-// n <= 16 bytes from global address a into bytes [0, n) of the result (any
-// alignment: gfx950 global accesses need none).  Streaming (non-temporal).
-__device__ __forceinline__ u32x4 load_bytes(uintptr_t a, uint32_t n) {
-  if (n == 16) return load_16_unaligned(a);
-  uint64_t lo = 0, hi = 0;
-  uint32_t at = 0;
-  if (n & 8) {
-    lo = __builtin_nontemporal_load(as_global<const u64_u>(a));
-    at = 8;
-  }
-  if (n & 4) {
-    const uint64_t x = __builtin_nontemporal_load(as_global<const u32_u>(a + at));
-    if (at < 8) lo |= x << (8 * at); else hi |= x;
-    at += 4;
-  }
-  if (n & 2) {
-    const uint64_t x = *as_global<const u16_u>(a + at);
-    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
-    at += 2;
-  }
-  if (n & 1) {
-    const uint64_t x = *as_global<const uint8_t>(a + at);
-    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
-  }
-  return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
-}
-
-// Bytes [0, n) of v (n <= 16) to global address d, streaming stores for the
-// whole-word widths, at most four stores otherwise.
-__device__ __forceinline__ void store_bytes(uintptr_t d, u32x4 v, uint32_t n) {
-  if (n == 16) __builtin_nontemporal_store(v, as_global<u32x4_u>(d));
-  else if (n == 8) __builtin_nontemporal_store((uint64_t(v.y) << 32) | v.x, as_global<u64_u>(d));
-  else if (n == 4) __builtin_nontemporal_store(v.x, as_global<u32_u>(d));
-  else store_head_bytes(d, v, n);
-}
-
-// 4x4 transpose of 32-bit words across the four lanes of each quad: with row i
-// of a 4x4 matrix in lane i of the quad, lane j ends with column j.  Two
-// exchanges with DPP quad permutations: the off-diagonal words of each 2x2
-// block with the neighbour lane (quad_perm 1,0,3,2), then the off-diagonal 2x2
-// blocks with the lane two away (quad_perm 2,3,0,1).  Every lane of the wave
-// must be active.
-__device__ __forceinline__ u32x4 quad_transpose(u32x4 v) {
-  const uint32_t j = threadIdx.x & 3u;
-  uint32_t m[4] = {v.x, v.y, v.z, v.w};
-  const bool odd = (j & 1u) != 0, upper = (j & 2u) != 0;
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const uint32_t x = odd ? m[2 * b] : m[2 * b + 1];
-    const uint32_t y = uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0xB1, 0xF, 0xF, false));
-    if (odd) m[2 * b] = y;
-    else m[2 * b + 1] = y;
-  }
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const uint32_t x = upper ? m[c] : m[2 + c];
-    const uint32_t y = uint32_t(__builtin_amdgcn_mov_dpp(int(x), 0x4E, 0xF, 0xF, false));
-    if (upper) m[c] = y;
-    else m[2 + c] = y;
-  }
-  return u32x4{m[0], m[1], m[2], m[3]};
-}
-
-// Whether segments [0, n) of a 16-byte band are four packed 4-byte column runs
-// (the band's row split into four 4-byte pieces, each stored contiguously) with
-// one fan-out: then four consecutive rows of one segment are 16 contiguous bytes.
-__device__ __forceinline__ bool quad_segments(const reshard_segment_t* __restrict__ S, uint32_t n,
-                                              uint32_t* fanout) {
-  if (n != 4) return false;
-  bool ok = true;
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-    ok = ok && S[s].width == 4u && S[s].row_stride == 4 && S[s].fanout == S[0].fanout;
-  *fanout = S[0].fanout;
-  return ok;
-}
-
-// Base address (tile row 0) of the segment at column 4 * (lane & 3) of a quad
-// band, replica f (source segments: f = 0 and fan-out 0).
-template <class Sh>
-__device__ __forceinline__ uintptr_t quad_base(const reshard_segment_t* __restrict__ S,
-                                               const uint32_t* __restrict__ refs, const Sh& sh, uint32_t r0,
-                                               bool dst, uint32_t f) {
-  const uint32_t want = 4u * (threadIdx.x & 3u);
-  uintptr_t base = 0;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const uintptr_t p = (dst ? sh.ptr(refs[S[s].ptr + f]) : sh.ptr(S[s].ptr)) + uint64_t(S[s].offset) +
-                        uint64_t(r0) * 4u;
-    base = S[s].col == want ? p : base;
-  }
-  return base;
-}
-
-// A window band at most 16 bytes wide, without LDS: each lane owns rows
-// r = k * kBlock + lane of the tile, builds each row in one 16-byte register
-// from every source segment (shifted to its column), then writes each
-// destination segment's bytes of it to every replica.  Consecutive lanes touch
-// consecutive rows, so packed segments give contiguous wave accesses.  When a
-// 16-byte band is cut into four packed 4-byte column runs (a bf16 pair or an
-// fp32 column per shard) on one side, the four lanes of a quad exchange words
-// (quad_transpose): a lane then moves four consecutive rows of one run, 16
-// contiguous bytes, in one access instead of four.
-template <int kRows, class Sh>
-__device__ __forceinline__ void window_rows(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
-                            const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
-  const uint32_t rows = D.extent[0], per_tile = D.extent[1];
-  const uint32_t r0 = tile * per_tile;
-  const uint32_t hr = min(per_tile, rows - r0);
-  const reshard_segment_t* src_segs = segs + D.src_ptr;
-  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
-  const uint32_t quad_row = threadIdx.x & ~3u;  // first of the quad's rows (plus k * kBlock)
-  const uint32_t used = (hr + kBlock - 1) / kBlock;  // row slots k of this tile that hold rows
-  const bool wide = D.run_bytes == 16u;
-  u32x4 v[kRows];
-#pragma unroll
-  for (int k = 0; k < kRows; ++k) v[k] = u32x4{0, 0, 0, 0};
-  uint32_t src_fan;
-  if (wide && quad_segments(src_segs, D.dst_ref_begin, &src_fan)) {
-    // lane j loads four rows of the run at column 4j, then the quad transposes
-    const uintptr_t g = quad_base(src_segs, refs, sh, r0, false, 0);
-#pragma unroll
-    for (int k = 0; k < kRows; ++k) {
-      const uint32_t r = uint32_t(k * kBlock) + quad_row;
-      if (uint32_t(k) >= used) continue;
-      if (r + 4 <= hr) {
-        v[k] = load_16_unaligned(g + uint64_t(r) * 4u);
-      } else {
-        uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (uint32_t i = 0; i < 4; ++i)
-          if (r + i < hr) w[i] = __builtin_nontemporal_load(as_global<const u32_u>(g + uint64_t(r + i) * 4u));
-        v[k] = u32x4{w[0], w[1], w[2], w[3]};
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kRows; ++k)
-      if (uint32_t(k) < used) v[k] = quad_transpose(v[k]);  // uniform: every lane takes part
-  } else {
-    for (uint32_t s = 0; s < D.dst_ref_begin; ++s) {
-      const reshard_segment_t S = src_segs[s];
-      const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
-#pragma unroll
-      for (int k = 0; k < kRows; ++k) {
-        const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
-        if (r < hr) {
-          const u32x4 x = shift_left_bytes(load_bytes(g + uint64_t(r) * uint64_t(S.row_stride), S.width), S.col);
-          v[k] = u32x4{v[k].x | x.x, v[k].y | x.y, v[k].z | x.z, v[k].w | x.w};
-        }
-      }
-    }
-  }
-  uint32_t dst_fan;
-  if (wide && quad_segments(dst_segs, D.fanout, &dst_fan)) {
-    // the quad transposes, then lane j stores four rows of the run at column 4j
-#pragma unroll
-    for (int k = 0; k < kRows; ++k)
-      if (uint32_t(k) < used) v[k] = quad_transpose(v[k]);  // uniform: every lane takes part
-    for (uint32_t f = 0; f < dst_fan; ++f) {
-      const uintptr_t g = quad_base(dst_segs, refs, sh, r0, true, f);
-#pragma unroll
-      for (int k = 0; k < kRows; ++k) {
-        const uint32_t r = uint32_t(k * kBlock) + quad_row;
-        if (uint32_t(k) >= used) continue;
-        if (r + 4 <= hr) {
-          store_bytes(g + uint64_t(r) * 4u, v[k], 16);
-        } else {
-          const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
-#pragma unroll
-          for (uint32_t i = 0; i < 4; ++i)
-            if (r + i < hr) __builtin_nontemporal_store(w[i], as_global<u32_u>(g + uint64_t(r + i) * 4u));
-        }
-      }
-    }
-    return;
-  }
-  for (uint32_t s = 0; s < D.fanout; ++s) {
-    const reshard_segment_t S = dst_segs[s];
-    const uint64_t row_off = uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
-    u32x4 x[kRows];
-#pragma unroll
-    for (int k = 0; k < kRows; ++k) x[k] = S.col == 0 ? v[k] : shift_right_bytes(v[k], S.col);
-    for (uint32_t f = 0; f < S.fanout; ++f) {
-      const uintptr_t g = sh.ptr(refs[S.ptr + f]) + row_off;
-#pragma unroll
-      for (int k = 0; k < kRows; ++k) {
-        const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
-        if (r < hr) store_bytes(g + uint64_t(r) * uint64_t(S.row_stride), x[k], S.width);
-      }
-    }
-  }
-}
-
-// Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
-// aligned to the descriptor's unit, or replicas differ in 16-byte phase.
-template <class Sh>
-__device__ __forceinline__ void copy_bytes(const reshard_descriptor_t& D, uint32_t unit, uint32_t mode,
-                           const uint8_t* src, const Sh& sh, uint32_t lo, uint32_t hi) {
-  const uintptr_t d0 = sh.dst(0);
-  for (uint32_t f = lo + threadIdx.x; f < hi; f += kBlock) {
-    const ItemPos o = item_pos(D, f);
-    uintptr_t a, b;
-    if (mode == RESHARD_DESC_DST_CHUNKS) {
-      chunk_range(d0 + o.dst, D.run_bytes, o.col, &a, &b);
-      a -= d0;
-      b -= d0;
-    } else {
-      a = o.dst + uint64_t(o.col) * unit;
-      b = a + unit;
-    }
-    const uintptr_t s0 = reinterpret_cast<uintptr_t>(src) + o.src;
-    for (uint32_t r = 0; r < D.fanout; ++r) {
-      const uintptr_t dr = sh.dst(r);
-      for (uintptr_t x = a; x < b; ++x)  // same place in the row on both sides
-        *as_global<uint8_t>(dr + x) = *as_global<const uint8_t>(s0 + (x - o.dst));
-    }
-  }
-}
-
-// Bits of the kernel's `flags` argument.
-constexpr uint32_t kAllAligned16 = 1;  // every shard pointer of this execute is 16-byte aligned
-
-// ---------------------------------------------------------------- conversion
-//
-// Float conversions of a RESHARD_DESC_CONVERT descriptor, on bit patterns with
-// integer operations only (no dependence on the hardware's rounding mode).
-// Narrowing rounds to nearest, ties to even: adding 2^(k-1) - 1 plus the last
-// kept bit and dropping the k low bits rounds the magnitude that way, and a
-// carry out of the fraction lands in the exponent, up to infinity.  A NaN keeps
-// its sign and leading payload bits and gets the quiet bit.
-
-__device__ __forceinline__ uint32_t f32_to_bf16(uint32_t u) {
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x0040u;
-  return (u + 0x7fffu + ((u >> 16) & 1u)) >> 16;
-}
-
-__device__ __forceinline__ uint32_t f32_to_f16(uint32_t u) {
-  const uint32_t sign = (u >> 16) & 0x8000u, a = u & 0x7fffffffu;
-  if (a > 0x7f800000u) return sign | 0x7e00u | ((a >> 13) & 0x3ffu);
-  if (a >= 0x477ff000u) return sign | 0x7c00u;  // rounds past 65504: infinity
-  if (a >= 0x38800000u)                         // normal binary16 (>= 2^-14): rebias 127 -> 15
-    return sign | (((a + 0xfffu + ((a >> 13) & 1u)) >> 13) - (112u << 10));
-  // below 2^-14: a multiple of 2^-24 (subnormal), rounded to nearest even
-  const uint32_t e = a >> 23;
-  if (e < 102) return sign;  // below 2^-25: rounds to zero
-  const uint32_t m = (a & 0x7fffffu) | 0x800000u, sh = 126u - e;  // value = m * 2^(e - 150)
-  const uint32_t q = m >> sh, rem = m & ((1u << sh) - 1u), half = 1u << (sh - 1u);
-  return sign | (q + ((rem > half || (rem == half && (q & 1u))) ? 1u : 0u));
-}
-
-__device__ __forceinline__ uint32_t bf16_to_f32(uint32_t h) {
-  const uint32_t u = h << 16;
-  return (u & 0x7fffffffu) > 0x7f800000u ? u | 0x00400000u : u;
-}
-
-__device__ __forceinline__ uint32_t f16_to_f32(uint32_t h) {
-  const uint32_t sign = (h & 0x8000u) << 16, e = (h >> 10) & 0x1fu, m = h & 0x3ffu;
-  if (e == 0x1fu) return sign | 0x7f800000u | (m << 13) | (m ? 0x00400000u : 0u);
-  if (e != 0) return sign | ((e + 112u) << 23) | (m << 13);
-  if (m == 0) return sign;
-  const uint32_t p = 31u - __clz(m);  // subnormal m * 2^-24: leading bit at p < 10
-  return sign | ((p + 103u) << 23) | ((m << (23u - p)) & 0x7fffffu);
-}
-
-template <int kConv>
-__device__ __forceinline__ uint32_t convert_elem(uint32_t x) {
-  if constexpr (kConv == RESHARD_CONVERT_F32_BF16) return f32_to_bf16(x);
-  else if constexpr (kConv == RESHARD_CONVERT_F32_F16) return f32_to_f16(x);
-  else if constexpr (kConv == RESHARD_CONVERT_BF16_F32) return bf16_to_f32(x);
-  else return f16_to_f32(x);
-}
-
-// CONVERT mode: item f is up to 8 elements of a row.  A full item whose source
-// and destination are 16-byte aligned moves as 16-byte accesses (32 bytes of
-// fp32 in, 16 of 16-bit out, or the reverse); anything else element by element.
-template <int kConv, class Sh>
-__device__ __forceinline__ void convert_items(const reshard_descriptor_t& D, const uint8_t* src,
-                                              const Sh& sh, uint32_t lo, uint32_t hi, bool aligned) {
-  static_assert(rs::kItemsPerThread == 1, "a CONVERT tile holds one item per thread");
-  constexpr bool kNarrow = kConv == RESHARD_CONVERT_F32_BF16 || kConv == RESHARD_CONVERT_F32_F16;
-  constexpr uint32_t kEs = kNarrow ? 4 : 2, kEd = kNarrow ? 2 : 4;
-  const uint32_t f = lo + threadIdx.x;
-  if (f >= hi) return;
-  const ItemPos o = item_pos(D, f);
-  const uint32_t e0 = o.col * rs::kConvertElems;
-  const uint32_t n = min(rs::kConvertElems, D.run_bytes - e0);
-  const uintptr_t s = reinterpret_cast<uintptr_t>(src) + o.src + uint64_t(e0) * kEs;
-  const uint64_t doff = o.dst + uint64_t(e0) * kEd;
-  if (aligned && n == rs::kConvertElems && ((s | doff) & 15) == 0) {
-    uint32_t x[8];
-    if constexpr (kNarrow) {
-      const u32x4 a = __builtin_nontemporal_load(as_global<const u32x4>(s));
-      const u32x4 b = __builtin_nontemporal_load(as_global<const u32x4>(s + 16));
-      x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
-      x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
-    } else {
-      const u32x4 a = __builtin_nontemporal_load(as_global<const u32x4>(s));
-      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        x[2 * k] = w[k] & 0xffffu;
-        x[2 * k + 1] = w[k] >> 16;
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = convert_elem<kConv>(x[k]);
-    for (uint32_t r = 0; r < D.fanout; ++r) {
-      const uintptr_t d = sh.dst(r) + doff;
-      if constexpr (kNarrow) {
-        const u32x4 v{x[0] | (x[1] << 16), x[2] | (x[3] << 16), x[4] | (x[5] << 16), x[6] | (x[7] << 16)};
-        __builtin_nontemporal_store(v, as_global<u32x4>(d));
-      } else {
-        __builtin_nontemporal_store(u32x4{x[0], x[1], x[2], x[3]}, as_global<u32x4>(d));
-        __builtin_nontemporal_store(u32x4{x[4], x[5], x[6], x[7]}, as_global<u32x4>(d + 16));
-      }
-    }
-    return;
-  }
-  uint32_t x[8];
-#pragma unroll
-  for (uint32_t k = 0; k < 8; ++k) {
-    if (k >= n) break;
-    if constexpr (kNarrow) x[k] = convert_elem<kConv>(*as_global<const u32_u>(s + 4 * k));
-    else x[k] = convert_elem<kConv>(*as_global<const u16_u>(s + 2 * k));
-  }
-  for (uint32_t r = 0; r < D.fanout; ++r) {
-    const uintptr_t d = sh.dst(r) + doff;
-#pragma unroll
-    for (uint32_t k = 0; k < 8; ++k) {
-      if (k >= n) break;
-      if constexpr (kNarrow) *as_global<u16_u>(d + 2 * k) = uint16_t(x[k]);
-      else *as_global<u32_u>(d + 4 * k) = x[k];
-    }
-  }
-}
-
-// Kernel variants.  A plan runs the smallest variant that covers the modes of
-// its descriptors: short launches pay for code size, for branches in the tile
-// prologue and for an LDS allocation they do not use.
-enum KernelKind : int {
-  kKindItems16 = 0,  // every descriptor ITEMS with 16-byte items
-  kKindChunks = 1,   // every descriptor DST_CHUNKS
-  kKindCopy = 2,     // ITEMS, DST_CHUNKS and CONVERT; no LDS
-  kKindAll = 3,      // any mode, LDS window included
-  kKindQuadRows = 4, // every descriptor a 16-byte row-mode band with the quad exchange
-                     // (kQuadRowsPerLane rows per lane): no LDS, fewer registers
-  kKindAligned = 8,  // added to kKindChunks when every shard pointer is 16-byte
-                     // aligned: no bytewise fallback is compiled in
-};
-
-template <bool kKarg, int kVariant>
-__global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
-    const reshard_descriptor_t* __restrict__ descs, uint32_t n_desc,
-    const uint32_t* __restrict__ tile_begin, const uint32_t* __restrict__ refs,
-    const reshard_segment_t* __restrict__ segs, const void* const* __restrict__ table, KargPtrs karg,
-    uint32_t n_tiles, uint32_t per_xcd, uint32_t flags) {
-  constexpr int kKind = kVariant % kKindAligned;
-  constexpr bool kAligned = kVariant >= kKindAligned;
-  // Block b runs on XCD b % kXcds.  Each XCD takes groups of kXcdGroup
-  // consecutive tiles, the XCDs side by side: nearby tiles share an XCD's L2
-  // while all XCDs stream through the same region of memory.  Plans smaller
-  // than one round of groups (per_xcd == 0) use block b for tile b.
-  const uint32_t kx = blockIdx.x / kXcds;
-  const uint32_t t = per_xcd == 0 ? blockIdx.x
-                                  : ((kx / kXcdGroup) * kXcds + blockIdx.x % kXcds) * kXcdGroup + kx % kXcdGroup;
-  if (t >= n_tiles) return;
-  uint32_t lo = 0, hi = n_desc;  // last descriptor whose first tile is <= t
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (tile_begin[mid] <= t) lo = mid; else hi = mid;
-  }
-  const reshard_descriptor_t& D = descs[lo];
-  uint32_t unit_mode;  // the two 16-bit fields as one scalar word
-  __builtin_memcpy(&unit_mode, &D.unit, sizeof(unit_mode));
-  const uint32_t unit = kKind == kKindItems16 ? 16u : unit_mode & 0xffffu;
-  const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
-                        : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
-                        : kKind == kKindQuadRows ? uint32_t(RESHARD_DESC_WINDOW)
-                                               : unit_mode >> 16;
-  if constexpr (kKind == kKindQuadRows) {
-    const Shards<kKarg> wsh{table, &karg, refs};
-    window_rows<int(rs::kQuadRowsPerLane)>(D, segs, refs, wsh, t - tile_begin[lo]);
-    return;
-  }
-  if constexpr (kKind == kKindAll) {
-    if (mode == RESHARD_DESC_WINDOW) {  // any alignment: global chunks follow the addresses
-      __shared__ __attribute__((aligned(16))) uint8_t window[rs::kWindowBytes];
-      const Shards<kKarg> wsh{table, &karg, refs};
-      // one row-mode build serves every band here (a band's tile may have fewer
-      // rows than its slots): a second one would raise the register count of
-      // the whole kernel
-      if (D.run_bytes > uint32_t(rs::kRowModeBytes))
-        window_tile(D, segs, refs, wsh, t - tile_begin[lo], window);
-      else
-        window_rows<int(rs::kRowsPerLane)>(D, segs, refs, wsh, t - tile_begin[lo]);
-      return;
-    }
-  }
-  if constexpr (kKind != kKindQuadRows) {
-  const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;
-  const uint32_t first = (t - tile_begin[lo]) * rs::kTileItems;
-  const uint32_t last = min(first + rs::kTileItems, items);
-  const Shards<kKarg> sh{table, &karg, refs + D.dst_ref_begin};
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(sh.ptr(D.src_ptr));
-  if constexpr (kKind == kKindCopy || kKind == kKindAll) {
-    if (mode == RESHARD_DESC_CONVERT) {  // checks its own alignment per item
-      const bool aligned = (flags & kAllAligned16) != 0;
-      switch (unit) {
-        case RESHARD_CONVERT_F32_BF16: convert_items<RESHARD_CONVERT_F32_BF16>(D, src, sh, first, last, aligned); break;
-        case RESHARD_CONVERT_F32_F16: convert_items<RESHARD_CONVERT_F32_F16>(D, src, sh, first, last, aligned); break;
-        case RESHARD_CONVERT_BF16_F32: convert_items<RESHARD_CONVERT_BF16_F32>(D, src, sh, first, last, aligned); break;
-        default: convert_items<RESHARD_CONVERT_F16_F32>(D, src, sh, first, last, aligned); break;
-      }
-      return;
-    }
-  }
-  if (!kAligned && !(flags & kAllAligned16)) {
-    // alignment every access width relies on: the unit for ITEMS; for
-    // DST_CHUNKS, replicas in the same 16-byte phase as replica 0
-    const uintptr_t d0 = sh.dst(0);
-    uintptr_t bits = reinterpret_cast<uintptr_t>(src) | d0, phase = 0;
-    for (uint32_t r = 1; r < D.fanout; ++r) {
-      bits |= sh.dst(r);
-      phase |= sh.dst(r) - d0;
-    }
-    const bool ok = mode == RESHARD_DESC_DST_CHUNKS ? (phase & 15) == 0 : (bits & (unit - 1)) == 0;
-    if (!ok) {
-      copy_bytes(D, unit, mode, src, sh, first, last);
-      return;
-    }
-  }
-  if constexpr (kKind == kKindItems16) {
-    copy_items<u32x4, rs::kItemsPerThread>(D, src, sh, first, last);
-  } else if constexpr (kKind == kKindChunks) {
-    copy_chunks<rs::kItemsPerThread>(D, src, sh, first, last);
-  } else {
-    if (mode == RESHARD_DESC_DST_CHUNKS) {
-      copy_chunks<rs::kItemsPerThread>(D, src, sh, first, last);
-      return;
-    }
-    switch (unit) {
-      case 16: copy_items<u32x4, rs::kItemsPerThread>(D, src, sh, first, last); break;
-      case 8: copy_items<u32x2, rs::kItemsPerThread>(D, src, sh, first, last); break;
-      case 4: copy_items<uint32_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
-      case 2: copy_items<uint16_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
-      default: copy_items<uint8_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
-    }
-  }
-  }  // kKind != kKindQuadRows
-}
-
-// The kernel variant of a plan's descriptors.
-int kernel_kind(const std::vector<reshard_descriptor_t>& descs) {
-  bool items16 = true, chunks = true, quad_rows = true, window = false;
-  for (const reshard_descriptor_t& D : descs) {
-    if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
-    if (D.mode != RESHARD_DESC_DST_CHUNKS) chunks = false;
-    if (D.mode != RESHARD_DESC_WINDOW || D.run_bytes > uint32_t(rs::kRowModeBytes) ||
-        D.extent[1] != rs::kQuadRowsPerLane * uint32_t(kBlock))
-      quad_rows = false;
-    if (D.mode == RESHARD_DESC_WINDOW) window = true;
-  }
-  return items16 ? kKindItems16 : chunks ? kKindChunks : quad_rows ? kKindQuadRows : window ? kKindAll : kKindCopy;
-}
-
-template <bool kKarg, int kVariant>
-void launch_kind(uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
-                 const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
-                 const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
-                 uint32_t flags) {
-  hipLaunchKernelGGL((reshard_copy_kernel<kKarg, kVariant>), dim3(n_wg), dim3(kBlock), 0, stream, descs, n_desc,
-                     tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags);
-}
-
-template <bool kKarg>
-void launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
-            const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
-            const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
-            uint32_t flags) {
-  const bool aligned = (flags & kAllAligned16) != 0;
-  switch (kind) {
-    case kKindItems16:  // (an aligned-only build of this one measured slower on long copies)
-      launch_kind<kKarg, kKindItems16>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                       n_tiles, per_xcd, flags);
-      break;
-    case kKindChunks:
-      if (aligned)
-        launch_kind<kKarg, kKindChunks + kKindAligned>(n_wg, stream, descs, n_desc, tile_begin, refs, segs,
-                                                       table, karg, n_tiles, per_xcd, flags);
-      else
-        launch_kind<kKarg, kKindChunks>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                        n_tiles, per_xcd, flags);
-      break;
-    case kKindCopy:
-      launch_kind<kKarg, kKindCopy>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                    n_tiles, per_xcd, flags);
-      break;
-    case kKindQuadRows:
-      launch_kind<kKarg, kKindQuadRows>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                        n_tiles, per_xcd, flags);
-      break;
-    default:
-      launch_kind<kKarg, kKindAll>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                   n_tiles, per_xcd, flags);
-      break;
-  }
-}
-
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 }  // namespace
@@ -1007,9 +45,9 @@ struct reshard_plan_s {
   std::mutex mu;
   bool uploaded = false;
   int device = -1;
-  uint32_t n_wg = 0;       // grid of one launch: kXcds * per_xcd blocks (surplus ones exit)
-  uint32_t per_xcd = 0;    // blocks per XCD, a multiple of kXcdGroup (0: one block per tile)
-  int kind = kKindAll;     // kernel variant (KernelKind)
+  uint32_t n_wg = 0;       // grid of one launch: rs::kXcds * per_xcd blocks (surplus ones exit)
+  uint32_t per_xcd = 0;    // blocks per XCD, a multiple of rs::kXcdGroup (0: one block per tile)
+  int kind = 0;            // kernel variant (rs::kernel_kind)
   void* table = nullptr;  // device: descriptors | refs (absolute pointer slots) | tile_begin
   const reshard_descriptor_t* d_descs = nullptr;
   const uint32_t* d_refs = nullptr;
@@ -1019,8 +57,9 @@ struct reshard_plan_s {
   int64_t n_ptrs = 0;
   void* d_slots = nullptr;
   void** h_slots = nullptr;  // pinned host staging, kSlots * n_ptrs entries
-  hipEvent_t ev[kSlots] = {};
+  hipEvent_t ev[kSlots] = {};      // recorded after the last launch that read the slot
   bool ev_live[kSlots] = {};
+  hipStream_t ev_stream[kSlots] = {};  // the stream of that launch
   int next_slot = 0;
   int last_slot = -1;
 };
@@ -1040,10 +79,10 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   }
   const rs::HostPlan& H = p->host;
   // blocks per XCD, a whole number of tile groups; 0: too few tiles to group
-  const uint64_t per_xcd_min = (H.n_tiles + kXcds - 1) / kXcds;
+  const uint64_t per_xcd_min = (H.n_tiles + rs::kXcds - 1) / rs::kXcds;
   const uint32_t per_xcd =
-      H.n_tiles < uint64_t(kXcds) * kXcdGroup ? 0u
-                                              : uint32_t((per_xcd_min + kXcdGroup - 1) / kXcdGroup * kXcdGroup);
+      H.n_tiles < uint64_t(rs::kXcds) * rs::kXcdGroup ? 0u
+                                              : uint32_t((per_xcd_min + rs::kXcdGroup - 1) / rs::kXcdGroup * rs::kXcdGroup);
   const size_t desc_bytes = H.descs.size() * sizeof(reshard_descriptor_t);
   const size_t refs_off = align_up(desc_bytes, 256);
   const size_t tiles_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);
@@ -1068,7 +107,7 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
     return hip_fail(e, "descriptor table upload");
   }
   p->n_ptrs = H.n_src_ptrs + H.n_dst_ptrs;
-  if (p->n_ptrs > kKargPtrs) {
+  if (p->n_ptrs > rs::kKargPtrs) {
     const size_t bytes = size_t(kSlots) * size_t(p->n_ptrs) * sizeof(void*);
     e = hipMalloc(&p->d_slots, bytes);
     if (e == hipSuccess) e = hipHostMalloc(reinterpret_cast<void**>(&p->h_slots), bytes, hipHostMallocDefault);
@@ -1092,8 +131,8 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   p->d_tile_begin = reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + tiles_off);
   p->d_segs = reinterpret_cast<const reshard_segment_t*>(static_cast<uint8_t*>(table) + segs_off);
   p->per_xcd = per_xcd;
-  p->n_wg = per_xcd ? per_xcd * kXcds : uint32_t(H.n_tiles);
-  p->kind = kernel_kind(H.descs);
+  p->n_wg = per_xcd ? per_xcd * rs::kXcds : uint32_t(H.n_tiles);
+  p->kind = rs::kernel_kind(H.descs);
   p->device = dev;
   p->uploaded = true;
   return RESHARD_OK;
@@ -1219,16 +258,16 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
   if (capture != hipStreamCaptureStatusNone) {
     if (!plan->uploaded)
       return fail(RESHARD_ERR_INVALID_ARGUMENT, "call reshard_plan_upload before capturing an execute");
-    if (plan->n_ptrs > kKargPtrs)
+    if (plan->n_ptrs > rs::kKargPtrs)
       return fail(RESHARD_ERR_INVALID_ARGUMENT,
-                  "a plan with more than " + std::to_string(kKargPtrs) +
+                  "a plan with more than " + std::to_string(rs::kKargPtrs) +
                       " shard pointers cannot be captured into a graph");
   }
   reshard_status_t st = upload_locked(plan, stream);
   if (st != RESHARD_OK) return st;
   if (H.descs.empty()) return RESHARD_OK;
 
-  KargPtrs karg;
+  rs::KargPtrs karg;
   std::memset(&karg, 0, sizeof(karg));
   const void* const* table = nullptr;
   int slot = -1;
@@ -1236,8 +275,8 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
   uintptr_t ptr_bits = 0;  // low bits of every pointer, for the all-aligned fast path
   for (int64_t i = 0; i < H.n_src_ptrs; ++i) ptr_bits |= reinterpret_cast<uintptr_t>(src_ptrs[i]);
   for (int64_t i = 0; i < H.n_dst_ptrs; ++i) ptr_bits |= reinterpret_cast<uintptr_t>(dst_ptrs[i]);
-  const uint32_t flags = (ptr_bits & 15) == 0 ? kAllAligned16 : 0;
-  if (plan->n_ptrs <= kKargPtrs) {
+  const uint32_t flags = (ptr_bits & 15) == 0 ? rs::kAllAligned16 : 0;
+  if (plan->n_ptrs <= rs::kKargPtrs) {
     for (int64_t i = 0; i < H.n_src_ptrs; ++i) karg.p[i] = src_ptrs[i];
     for (int64_t i = 0; i < H.n_dst_ptrs; ++i) karg.p[H.n_src_ptrs + i] = dst_ptrs[i];
   } else {
@@ -1252,6 +291,13 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
     };
     if (plan->last_slot >= 0 && same(plan->last_slot)) {
       slot = plan->last_slot;  // already on the device; no copy
+      // On another stream, the copy that filled the slot (and the launches that
+      // read it) must come first: the ring overwrites a slot only after its
+      // latest launch, so that launch has to follow every earlier one.
+      if (plan->ev_live[slot] && plan->ev_stream[slot] != stream) {
+        e = hipStreamWaitEvent(stream, plan->ev[slot], 0);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamWaitEvent(pointer slot)");
+      }
     } else {
       slot = plan->next_slot;
       plan->next_slot = (plan->next_slot + 1) % kSlots;
@@ -1272,18 +318,15 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
     }
     table = reinterpret_cast<const void* const*>(static_cast<void**>(plan->d_slots) + size_t(slot) * n);
   }
-  if (table)
-    launch<false>(plan->kind, plan->n_wg, stream, plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin,
+  rs::launch_copy(plan->kind, plan->n_wg, stream, plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin,
                   plan->d_refs, plan->d_segs, table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
-  else
-    launch<true>(plan->kind, plan->n_wg, stream, plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin,
-                 plan->d_refs, plan->d_segs, table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "reshard_copy_kernel launch");
   if (slot >= 0) {
     e = hipEventRecord(plan->ev[slot], stream);
     if (e != hipSuccess) return hip_fail(e, "hipEventRecord(pointer slot)");
     plan->ev_live[slot] = true;
+    plan->ev_stream[slot] = stream;
   }
   return RESHARD_OK;
 }

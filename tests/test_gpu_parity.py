@@ -182,6 +182,60 @@ def test_pointer_slot_ring():
                     assert dsts[t].guards_intact(i)
 
 
+def test_pointer_slot_reused_from_another_stream():
+    """A pointer set just copied into a device slot on a busy stream, executed
+    again on another stream: the second launch must wait for the copy that
+    fills the slot.  Every slot first holds a valid older set, and the set the
+    slot held before (set 0) had its destinations overwritten with a canary: a
+    launch that read the slot too early would copy set 0 again and destroy it."""
+    from reshard_harness import oracle_dsts
+    specs = list(W.ffn_refit(16, 64, 96).tensors)  # 480 pointers: device slots
+    with Plan(specs) as plan:
+        sets = []
+        for seed in (31, 32, 33):  # three source sets with different values
+            want, srcs_d = [], []
+            for t, spec in enumerate(specs):
+                g = W.make_global(spec, "raw", seed, t)
+                sb = oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements)
+                srcs = W.cut(g, sb)
+                want.append(oracle_dsts(spec, srcs))
+                gs = GuardedShards(shard_nbytes(sb, spec.dtype), "cuda")
+                for i, x in enumerate(srcs):
+                    gs.region(i).copy_(x.reshape(-1).view(torch.uint8).cuda())
+                srcs_d.append(gs)
+            dsts = [GuardedShards(shard_nbytes(oracle_boxes(s.shape, s.dst_mesh, s.dst_placements), s.dtype),
+                                  "cuda") for s in specs]
+            sets.append((want, srcs_d, dsts))
+        ptrs = [([p for g in sd for p in g.ptrs], [p for d in dd for p in d.ptrs]) for _, sd, dd in sets]
+        a, b = torch.cuda.Stream(), torch.cuda.Stream()
+        torch.cuda.synchronize()
+        for k in range(8):  # every slot of the ring holds set 0 or set 1; slot 0 holds set 0
+            R.reshard_execute(plan.handle, *ptrs[k % 2], a.cuda_stream)
+        torch.cuda.synchronize()
+        for d in sets[0][2]:
+            for i in range(len(d.nbytes)):
+                if d.nbytes[i]:
+                    d.region(i).fill_(0x5A)
+        busy = torch.empty(1 << 28, dtype=torch.uint8, device="cuda")
+        torch.cuda.synchronize()
+        with torch.cuda.stream(a):
+            for _ in range(20):  # keep stream a busy ahead of the next copy
+                busy.add_(1)
+        R.reshard_execute(plan.handle, *ptrs[2], a.cuda_stream)  # slot 0, copied on a
+        R.reshard_execute(plan.handle, *ptrs[2], b.cuda_stream)  # same pointers, on b
+        torch.cuda.synchronize()
+        for d in sets[0][2]:
+            for i in range(len(d.nbytes)):
+                if d.nbytes[i]:
+                    assert bool((d.region(i) == 0x5A).all().item()), "set 0 was copied again"
+        for k in (1, 2):
+            want, _, dsts = sets[k]
+            for t in range(len(specs)):
+                for i, w in enumerate(want[t]):
+                    assert torch.equal(dsts[t].region(i).cpu(), w.reshape(-1).view(torch.uint8))
+                    assert dsts[t].guards_intact(i)
+
+
 def test_two_streams_concurrently():
     spec = W.ffn_up(1024, 512).tensors[0]
     with Plan([spec]) as plan:

@@ -19,7 +19,7 @@ def kernel_meta(tmp_path_factory):
     out = tmp_path_factory.mktemp("isa") / "reshard.s"
     flags = [f for f in B.HIP_FLAGS if f not in ("-fPIC", "-Wall")]
     cmd = [B.hipcc(), *flags, "--cuda-device-only", "-S", "-Rpass-analysis=kernel-resource-usage",
-           "-I", B.INCLUDE, "-I", B.CSRC, os.path.join(B.CSRC, "reshard.hip"), "-o", str(out)]
+           "-I", B.INCLUDE, "-I", B.CSRC, os.path.join(B.CSRC, "kernel.hip"), "-o", str(out)]
     res = subprocess.run(cmd, capture_output=True, text=True)
     assert res.returncode == 0, res.stderr[-2000:]
     text = out.read_text()
