@@ -93,7 +93,9 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   uint32_t* r = reinterpret_cast<uint32_t*>(img.data() + refs_off);
   for (size_t i = 0; i < H.refs.size(); ++i) r[i] = uint32_t(H.n_src_ptrs) + H.refs[i];
   std::memcpy(img.data() + tiles_off, H.tile_begin.data(), H.tile_begin.size() * sizeof(uint32_t));
-  // window segments: source pointer indices become absolute pointer slots
+  // window segments as planned: a source segment indexes the source pointers,
+  // which come first in the pointer array; a destination segment indexes the
+  // fan-out list, whose entries were made absolute above
   reshard_segment_t* sg = reinterpret_cast<reshard_segment_t*>(img.data() + segs_off);
   for (size_t i = 0; i < H.segs.size(); ++i) sg[i] = H.segs[i];
 
@@ -143,17 +145,17 @@ reshard_status_t make_plan(int n, const reshard_layout_t* src, const reshard_lay
   if (!out) return fail(RESHARD_ERR_INVALID_ARGUMENT, "out is NULL");
   *out = nullptr;
   if (n < 1 || !src || !dst) return fail(RESHARD_ERR_INVALID_ARGUMENT, "need n >= 1 layouts");
-  std::vector<const rs::Layout*> s(n), d(n);
-  for (int t = 0; t < n; ++t) {
-    if (!src[t] || !dst[t]) return fail(RESHARD_ERR_INVALID_ARGUMENT, "NULL layout");
-    s[t] = &src[t]->L;
-    d[t] = &dst[t]->L;
-  }
-  reshard_plan_s* p = new (std::nothrow) reshard_plan_s();
-  if (!p) return fail(RESHARD_ERR_OUT_OF_MEMORY, "plan allocation");
+  reshard_plan_s* p = nullptr;
   std::string err;
   reshard_status_t st;
-  try {
+  try {  // no exception may cross the C ABI
+    std::vector<const rs::Layout*> s(n), d(n);
+    for (int t = 0; t < n; ++t) {
+      if (!src[t] || !dst[t]) return fail(RESHARD_ERR_INVALID_ARGUMENT, "NULL layout");
+      s[t] = &src[t]->L;
+      d[t] = &dst[t]->L;
+    }
+    p = new reshard_plan_s();
     st = rs::build_plan(n, s.data(), d.data(), &p->host, &err);
   } catch (const std::bad_alloc&) {
     st = RESHARD_ERR_OUT_OF_MEMORY;
