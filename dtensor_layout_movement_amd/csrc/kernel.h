@@ -24,8 +24,9 @@ struct KargPtrs {
 // Bits of the kernel's `flags` argument.
 constexpr uint32_t kAllAligned16 = 1;  // every shard pointer of this execute is 16-byte aligned
 
-// The kernel variant of a plan: the smallest build that covers its descriptors.
-int kernel_kind(const std::vector<reshard_descriptor_t>& descs);
+// The kernel variant of a plan: the smallest build that covers its descriptors
+// (and their window segments).
+int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs);
 
 // One launch of variant `kind` with `n_wg` workgroups on `stream`.  Shard
 // pointers come from `karg` when `table` is NULL, else from the device table.

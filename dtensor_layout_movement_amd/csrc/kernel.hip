@@ -651,6 +651,162 @@ __device__ __forceinline__ void window_rows(const reshard_descriptor_t& D, const
   }
 }
 
+// The value of v held by lane (this lane) ^ X, for X = 1, 2 (DPP quad
+// permutations) and X = 4, 8 (LDS-crossbar swizzle, bit mode: and-mask 0x1f,
+// xor-mask X).  Every lane of the wave must be active.
+template <int X>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
+  if constexpr (X == 1) return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0xB1, 0xF, 0xF, false));
+  else if constexpr (X == 2) return uint32_t(__builtin_amdgcn_mov_dpp(int(v), 0x4E, 0xF, 0xF, false));
+  else return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x1F | (X << 10)));
+}
+
+// One butterfly stage of a transpose across K lanes: word i of lane L and word
+// i ^ X of lane L ^ X trade places wherever bit X of L and of i differ.  X is a
+// template argument so that every word index is a constant (an index known
+// only at run time would move m to scratch memory).
+template <int X, int K>
+__device__ __forceinline__ void transpose_stage(uint32_t (&m)[K]) {
+  const bool hi = (threadIdx.x & uint32_t(X)) != 0;
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    if (i & X) continue;  // i is the low word of the pair (i, i ^ X)
+    const uint32_t got = lane_xor<X>(hi ? m[i] : m[i ^ X]);
+    if (hi) m[i] = got;
+    else m[i ^ X] = got;
+  }
+}
+
+// K x K transpose of 32-bit words across each group of K consecutive lanes:
+// with row i of a K x K matrix in lane i of the group, lane j ends with column
+// j, after log2(K) butterfly stages.
+template <int K>
+__device__ __forceinline__ void lanes_transpose(uint32_t (&m)[K]) {
+  static_assert(K == 4 || K == 8 || K == 16, "K lanes exchange within 32-lane halves");
+  transpose_stage<1>(m);
+  transpose_stage<2>(m);
+  if constexpr (K > 4) transpose_stage<4>(m);
+  if constexpr (K > 8) transpose_stage<8>(m);
+}
+
+// Whether segments [0, n) of a band are K packed 4-byte column runs with one
+// fan-out, or one packed run of the whole 4K-byte row.
+__host__ __device__ __forceinline__ bool runs_side(const reshard_segment_t* __restrict__ S, uint32_t n,
+                                                   uint32_t k) {
+  if (n != k) return false;
+  bool ok = true;
+  for (uint32_t s = 0; s < n; ++s)
+    ok = ok && S[s].width == 4u && S[s].row_stride == 4 && S[s].fanout == S[0].fanout;
+  return ok;
+}
+__host__ __device__ __forceinline__ bool full_side(const reshard_segment_t* __restrict__ S, uint32_t n,
+                                                   uint32_t w) {
+  return n == 1 && S[0].width == w && uint64_t(S[0].row_stride) == w;
+}
+
+// A window band of K 4-byte columns (rows of 4K bytes) whose one
+// side is K packed 4-byte column runs (bf16 pairs or fp32 columns, one per
+// shard) and whose other side is one packed run of whole rows or K such runs
+// too.  Without LDS: a lane holds whole rows; the K lanes of a group exchange
+// words (lanes_transpose) so that a lane holds K consecutive rows of one run,
+// 4K contiguous bytes.  Rows per lane: the band's tile rows / kBlock.
+template <int K, class Sh>
+__device__ __forceinline__ void window_runs(const reshard_descriptor_t& D,
+                                            const reshard_segment_t* __restrict__ segs,
+                                            const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
+  constexpr int kRows = int(rs::kWindowBytes) / (4 * K) / kBlock;  // the window's rows per tile
+  constexpr int kVec = K / 4;                                        // 16-byte words per row
+  const uint32_t rows = D.extent[0], per_tile = D.extent[1];
+  const uint32_t r0 = tile * per_tile;
+  const uint32_t hr = min(per_tile, rows - r0);
+  const reshard_segment_t* src_segs = segs + D.src_ptr;
+  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+  const uint32_t j = threadIdx.x & uint32_t(K - 1);   // lane within its group
+  const uint32_t group_row = threadIdx.x & ~uint32_t(K - 1);
+  uint32_t m[kRows][K];
+  if (runs_side(src_segs, D.dst_ref_begin, K)) {
+    // lane j reads K consecutive rows of the run at column 4j, then the group transposes
+    uintptr_t g = 0;
+    for (uint32_t s = 0; s < uint32_t(K); ++s)
+      if (src_segs[s].col == 4u * j) g = sh.ptr(src_segs[s].ptr) + uint64_t(src_segs[s].offset) + uint64_t(r0) * 4u;
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const uint32_t r = uint32_t(k * kBlock) + group_row;
+#pragma unroll
+      for (int i = 0; i < K; ++i) m[k][i] = 0;
+      if (r + K <= hr) {
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) {
+          const u32x4 x = load_16_unaligned(g + uint64_t(r) * 4u + 16u * q);
+          m[k][4 * q] = x.x; m[k][4 * q + 1] = x.y; m[k][4 * q + 2] = x.z; m[k][4 * q + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < K; ++i)
+          if (r + i < hr) m[k][i] = __builtin_nontemporal_load(as_global<const u32_u>(g + uint64_t(r + i) * 4u));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) lanes_transpose<K>(m[k]);
+  } else {  // one packed run of whole rows
+    const reshard_segment_t S = src_segs[0];
+    const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * (4u * K);
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
+#pragma unroll
+      for (int i = 0; i < K; ++i) m[k][i] = 0;
+      if (r < hr) {
+#pragma unroll
+        for (int q = 0; q < kVec; ++q) {
+          const u32x4 x = load_16_unaligned(g + uint64_t(r) * (4u * K) + 16u * q);
+          m[k][4 * q] = x.x; m[k][4 * q + 1] = x.y; m[k][4 * q + 2] = x.z; m[k][4 * q + 3] = x.w;
+        }
+      }
+    }
+  }
+  if (runs_side(dst_segs, D.fanout, K)) {
+    // the group transposes, then lane j writes K consecutive rows of the run at column 4j
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) lanes_transpose<K>(m[k]);
+    for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {
+      uintptr_t g = 0;
+      for (uint32_t s = 0; s < uint32_t(K); ++s)
+        if (dst_segs[s].col == 4u * j)
+          g = sh.ptr(refs[dst_segs[s].ptr + f]) + uint64_t(dst_segs[s].offset) + uint64_t(r0) * 4u;
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+        const uint32_t r = uint32_t(k * kBlock) + group_row;
+        if (r + K <= hr) {
+#pragma unroll
+          for (int q = 0; q < kVec; ++q)
+            store_bytes(g + uint64_t(r) * 4u + 16u * q,
+                        u32x4{m[k][4 * q], m[k][4 * q + 1], m[k][4 * q + 2], m[k][4 * q + 3]}, 16);
+        } else {
+#pragma unroll
+          for (int i = 0; i < K; ++i)
+            if (r + i < hr) __builtin_nontemporal_store(m[k][i], as_global<u32_u>(g + uint64_t(r + i) * 4u));
+        }
+      }
+    }
+  } else {  // one packed run of whole rows
+    const reshard_segment_t S = dst_segs[0];
+    for (uint32_t f = 0; f < S.fanout; ++f) {
+      const uintptr_t g = sh.ptr(refs[S.ptr + f]) + uint64_t(S.offset) + uint64_t(r0) * (4u * K);
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+        const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
+        if (r < hr) {
+#pragma unroll
+          for (int q = 0; q < kVec; ++q)
+            store_bytes(g + uint64_t(r) * (4u * K) + 16u * q,
+                        u32x4{m[k][4 * q], m[k][4 * q + 1], m[k][4 * q + 2], m[k][4 * q + 3]}, 16);
+        }
+      }
+    }
+  }
+}
+
 // Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
 // aligned to the descriptor's unit, or replicas differ in 16-byte phase.
 template <class Sh>
@@ -801,6 +957,8 @@ enum KernelKind : int {
   kKindAll = 3,      // any mode, LDS window included
   kKindQuadRows = 4, // every descriptor a 16-byte row-mode band with the quad exchange
                      // (kQuadRowsPerLane rows per lane): no LDS, fewer registers
+  kKindRuns = 5,     // every descriptor a 32-byte window band of 4-byte column runs
+                     // (window_runs<8>): no LDS
   kKindAligned = 8,  // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
@@ -832,11 +990,16 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t unit = kKind == kKindItems16 ? 16u : unit_mode & 0xffffu;
   const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
                         : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
-                        : kKind == kKindQuadRows ? uint32_t(RESHARD_DESC_WINDOW)
+                        : kKind == kKindQuadRows || kKind == kKindRuns ? uint32_t(RESHARD_DESC_WINDOW)
                                                : unit_mode >> 16;
   if constexpr (kKind == kKindQuadRows) {
     const Shards<kKarg> wsh{table, &karg, refs};
     window_rows<int(rs::kQuadRowsPerLane)>(D, segs, refs, wsh, t - tile_begin[lo]);
+    return;
+  }
+  if constexpr (kKind == kKindRuns) {
+    const Shards<kKarg> wsh{table, &karg, refs};
+    window_runs<8>(D, segs, refs, wsh, t - tile_begin[lo]);
     return;
   }
   if constexpr (kKind == kKindAll) {
@@ -853,7 +1016,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
       return;
     }
   }
-  if constexpr (kKind != kKindQuadRows) {
+  if constexpr (kKind != kKindQuadRows && kKind != kKindRuns) {
   const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;
   const uint32_t first = (t - tile_begin[lo]) * rs::kTileItems;
   const uint32_t last = min(first + rs::kTileItems, items);
@@ -903,7 +1066,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
       default: copy_items<uint8_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
     }
   }
-  }  // kKind != kKindQuadRows
+  }  // kKind != kKindQuadRows && kKind != kKindRuns
 }
 
 template <bool kKarg, int kVariant>
@@ -942,6 +1105,10 @@ void launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descripto
       launch_kind<kKarg, kKindQuadRows>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
                                         n_tiles, per_xcd, flags);
       break;
+    case kKindRuns:
+      launch_kind<kKarg, kKindRuns>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
+                                    n_tiles, per_xcd, flags);
+      break;
     default:
       launch_kind<kKarg, kKindAll>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
                                    n_tiles, per_xcd, flags);
@@ -951,18 +1118,38 @@ void launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descripto
 
 }  // namespace
 
+namespace {
+
+// Whether a descriptor is a band window_runs<8> moves: 32 bytes wide, tiles of
+// the window's rows, one side eight packed 4-byte runs, the other eight runs or
+// one packed run of whole rows (the same tests the kernel makes).  (Sixteen
+// lanes for 64-byte bands would need 71 VGPRs: one wave per SIMD fewer.)
+bool runs_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
+  const uint32_t w = D.run_bytes;
+  if (D.mode != RESHARD_DESC_WINDOW || w != 32 || D.extent[1] != kWindowBytes / w) return false;
+  const reshard_segment_t* S = segs.data() + D.src_ptr;
+  const reshard_segment_t* T = S + D.dst_ref_begin;
+  const bool src_runs = runs_side(S, D.dst_ref_begin, w / 4), dst_runs = runs_side(T, D.fanout, w / 4);
+  return (src_runs || full_side(S, D.dst_ref_begin, w)) && (dst_runs || full_side(T, D.fanout, w)) &&
+         (src_runs || dst_runs);
+}
+
+}  // namespace
+
 // The kernel variant of a plan's descriptors.
-int kernel_kind(const std::vector<reshard_descriptor_t>& descs) {
-  bool items16 = true, chunks = true, quad_rows = true, window = false;
+int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
+  bool items16 = true, chunks = true, quad_rows = true, runs = true, window = false;
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
     if (D.mode != RESHARD_DESC_DST_CHUNKS) chunks = false;
     if (D.mode != RESHARD_DESC_WINDOW || D.run_bytes > uint32_t(rs::kRowModeBytes) ||
         D.extent[1] != rs::kQuadRowsPerLane * uint32_t(kBlock))
       quad_rows = false;
+    if (!runs_band(D, segs)) runs = false;
     if (D.mode == RESHARD_DESC_WINDOW) window = true;
   }
-  return items16 ? kKindItems16 : chunks ? kKindChunks : quad_rows ? kKindQuadRows : window ? kKindAll : kKindCopy;
+  return items16 ? kKindItems16 : chunks ? kKindChunks : quad_rows ? kKindQuadRows : runs ? kKindRuns
+         : window ? kKindAll : kKindCopy;
 }
 
 void launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,

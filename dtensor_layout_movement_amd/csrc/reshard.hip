@@ -134,7 +134,7 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   p->d_segs = reinterpret_cast<const reshard_segment_t*>(static_cast<uint8_t*>(table) + segs_off);
   p->per_xcd = per_xcd;
   p->n_wg = per_xcd ? per_xcd * rs::kXcds : uint32_t(H.n_tiles);
-  p->kind = rs::kernel_kind(H.descs);
+  p->kind = rs::kernel_kind(H.descs, H.segs);
   p->device = dev;
   p->uploaded = true;
   return RESHARD_OK;

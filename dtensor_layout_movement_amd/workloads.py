@@ -164,6 +164,16 @@ def narrow_columns(rows: int = 1 << 22) -> Workload:
                     f"{rows}x8 bf16 N(0,0.02), (2,)[S0] -> (4,)[S1]: 2-element column slices")
 
 
+def narrow_columns_tp8(rows: int = 1 << 21) -> Workload:
+    """16 bf16 columns (32-byte rows: the shape of a rank-16 low-rank factor),
+    rows split over two sources, columns over eight destinations: every
+    destination row is a 2-element (4-byte) slice of a 32-byte source row, wider
+    than a register row, so the band goes through an LDS window."""
+    t = TensorSpec("narrow16", (rows, 16), torch.bfloat16, (2,), (0,), (8,), (1,))
+    return Workload(f"narrow_columns_tp8_{rows}x16", (t,), "normal",
+                    f"{rows}x16 bf16 N(0,0.02), (2,)[S0] -> (8,)[S1]: 2-element slices of 32-byte rows")
+
+
 WORKLOADS = {
     "worked_example_8x8": worked_example_8x8,
     "ffn_up_14336x4096": ffn_up,
@@ -171,6 +181,7 @@ WORKLOADS = {
     "uneven_5000x3001": uneven,
     "ffn_refit_32_layers": ffn_refit,
     "narrow_columns_4194304x8": narrow_columns,
+    "narrow_columns_tp8_2097152x16": narrow_columns_tp8,
     "ffn_up_f32_to_bf16_14336x4096": ffn_up_f32_to_bf16,
     "dense_layer_refit_32_layers": dense_layer_refit,
 }

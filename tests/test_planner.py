@@ -60,6 +60,12 @@ def small_specs():
         T("narrow_scatter_rep", (1031, 8), torch.bfloat16, (2,), (0,), (2, 4), (RR, 1)),
         T("narrow_f32_cols", (2053, 4), torch.float32, (3,), (0,), (4,), (1,)),
         T("narrow_gather_rep", (1029, 8), torch.bfloat16, (2, 4), (RR, 1), (3,), (0,)),
+        # 32-byte rows cut into eight 4-byte column runs (8-lane exchange), row
+        # counts that leave partial groups of eight
+        T("runs_scatter", (1043, 16), torch.bfloat16, (2,), (0,), (8,), (1,)),
+        T("runs_gather", (1043, 16), torch.bfloat16, (8,), (1,), (3,), (0,)),
+        T("runs_scatter_rep", (517, 16), torch.bfloat16, (2,), (0,), (2, 8), (RR, 1)),
+        T("runs_f32_cols", (1029, 8), torch.float32, (3,), (0,), (8,), (1,)),
         # row mode without the quad exchange: single bf16 columns, 8-byte rows
         T("narrow_bf16_cols", (1037, 8), torch.bfloat16, (2,), (0,), (8,), (1,)),
         T("narrow_8byte_rows", (2051, 4), torch.bfloat16, (3,), (0,), (2,), (1,)),
@@ -275,6 +281,7 @@ def test_worked_example_plan():
 def test_piece_counts_of_workloads():
     counts = {"worked_example_8x8": 8, "ffn_up_14336x4096": 8, "moe_experts_64x2048x7168": 128,
               "uneven_5000x3001": 42, "ffn_refit_32_layers": 384, "narrow_columns_4194304x8": 8, "ffn_up_f32_to_bf16_14336x4096": 8,
+                  "narrow_columns_tp8_2097152x16": 16,
               "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1)}
     for wl in full_workload_plans():
         with Plan(wl.tensors) as plan:
@@ -372,11 +379,13 @@ def test_descriptor_modes():
 def test_row_mode_tile_rows():
     """Row-mode bands (at most 16 bytes wide) take 1024 rows per tile, or 512 when
     one side is four packed 4-byte column runs (quad exchange); wider bands as
-    many rows as fit a 16 KiB LDS window."""
+    many rows as fit a 16 KiB LDS window (512 for the 32-byte bands of eight
+    4-byte runs that the 8-lane exchange moves)."""
     small = {s.name: s for s in small_specs()}
     want = {"narrow_scatter": 512, "narrow_gather": 512, "narrow_f32_cols": 512, "narrow_scatter_rep": 512,
             "narrow_gather_rep": 512, "narrow_bf16_cols": 1024, "narrow_8byte_rows": 1024,
-            "narrow_fp8_3d": 16384 // 32}
+            "narrow_fp8_3d": 16384 // 32, "runs_scatter": 512, "runs_gather": 512, "runs_scatter_rep": 512,
+            "runs_f32_cols": 512}
     for name, rows in want.items():
         with Plan([small[name]]) as plan:
             descs, _ = R.reshard_plan_descriptors(plan.handle)
