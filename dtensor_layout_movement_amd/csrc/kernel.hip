@@ -24,6 +24,7 @@ constexpr int kBlock = int(kTileThreads);  // threads per workgroup (4 wave64s)
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
 
 // q = n / d for n < 2^31 with the planner's round-up multiplier (m, s).
 __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t s) {
@@ -661,32 +662,32 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
   else return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x1F | (X << 10)));
 }
 
-// One butterfly stage of a transpose across K lanes: word i of lane L and word
-// i ^ X of lane L ^ X trade places wherever bit X of L and of i differ.  X is a
-// template argument so that every word index is a constant (an index known
-// only at run time would move m to scratch memory).
-template <int X, int K>
-__device__ __forceinline__ void transpose_stage(uint32_t (&m)[K]) {
-  const bool hi = (threadIdx.x & uint32_t(X)) != 0;
-#pragma unroll
-  for (int i = 0; i < K; ++i) {
-    if (i & X) continue;  // i is the low word of the pair (i, i ^ X)
-    const uint32_t got = lane_xor<X>(hi ? m[i] : m[i ^ X]);
-    if (hi) m[i] = got;
-    else m[i ^ X] = got;
+// One butterfly stage of an 8 x 8 transpose of 32-bit words across each group
+// of eight consecutive lanes: word i of lane L and word i ^ X of lane L ^ X
+// trade places wherever bit X of L and of i differ.  The words travel by value
+// and every index is a compile-time constant (recursion over I): through a
+// reference, the select between the pair's two words is folded into a select
+// between their addresses, and the array then stays in memory (scratch or LDS).
+template <int X, int I = 0>
+__device__ __forceinline__ u32x8 transpose_stage(u32x8 m) {
+  if constexpr (I < 8) {
+    if constexpr ((I & X) == 0) {  // I is the low word of the pair (I, I ^ X)
+      const bool hi = (threadIdx.x & uint32_t(X)) != 0;
+      const uint32_t lo = m[I], up = m[I ^ X];
+      const uint32_t got = lane_xor<X>(hi ? lo : up);
+      m[I] = hi ? got : lo;
+      m[I ^ X] = hi ? up : got;
+    }
+    return transpose_stage<X, I + 1>(m);
+  } else {
+    return m;
   }
 }
 
-// K x K transpose of 32-bit words across each group of K consecutive lanes:
-// with row i of a K x K matrix in lane i of the group, lane j ends with column
-// j, after log2(K) butterfly stages.
-template <int K>
-__device__ __forceinline__ void lanes_transpose(uint32_t (&m)[K]) {
-  static_assert(K == 4 || K == 8 || K == 16, "K lanes exchange within 32-lane halves");
-  transpose_stage<1>(m);
-  transpose_stage<2>(m);
-  if constexpr (K > 4) transpose_stage<4>(m);
-  if constexpr (K > 8) transpose_stage<8>(m);
+// With row i of an 8 x 8 matrix in lane i of the group, lane j ends with
+// column j, after three butterfly stages.
+__device__ __forceinline__ u32x8 lanes_transpose8(u32x8 m) {
+  return transpose_stage<4>(transpose_stage<2>(transpose_stage<1>(m)));
 }
 
 // Whether segments [0, n) of a band are K packed 4-byte column runs with one
@@ -704,107 +705,162 @@ __host__ __device__ __forceinline__ bool full_side(const reshard_segment_t* __re
   return n == 1 && S[0].width == w && uint64_t(S[0].row_stride) == w;
 }
 
-// A window band of K 4-byte columns (rows of 4K bytes) whose one
-// side is K packed 4-byte column runs (bf16 pairs or fp32 columns, one per
-// shard) and whose other side is one packed run of whole rows or K such runs
-// too.  Without LDS: a lane holds whole rows; the K lanes of a group exchange
-// words (lanes_transpose) so that a lane holds K consecutive rows of one run,
-// 4K contiguous bytes.  Rows per lane: the band's tile rows / kBlock.
-template <int K, class Sh>
-__device__ __forceinline__ void window_runs(const reshard_descriptor_t& D,
-                                            const reshard_segment_t* __restrict__ segs,
-                                            const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
-  constexpr int kRows = int(rs::kWindowBytes) / (4 * K) / kBlock;  // the window's rows per tile
-  constexpr int kVec = K / 4;                                        // 16-byte words per row
-  const uint32_t rows = D.extent[0], per_tile = D.extent[1];
+// A 32-byte window band whose one side is eight packed 4-byte column runs
+// (bf16 pairs or fp32 columns, one per shard) and whose other side is one packed
+// run of whole rows or eight runs too.  No LDS: the tile's 512 rows are split so
+// that every 16-byte access of a wave is contiguous on both sides.
+//  - whole-row side: slice q (0..3) of lane L is bytes [16 L, 16 L + 16) of the
+//    tile's q-th 4 KiB, i.e. half L & 1 of row L / 2 + 128 q;
+//  - run side: lane j of group G (eight lanes) holds rows 4G..4G+3 (+128 q) of
+//    the run at column 4j, 16 contiguous bytes.
+// Slices q = 2p (set A) and 2p + 1 (set B) travel together: the halves layout
+// (words 0-3: set A half h of row 4G + r, words 4-7: the same of set B, in lane
+// 8G + 2r + h) turns into whole rows with one exchange between lanes 1 apart
+// (lane 2r: row r of set A, lane 2r + 1: row r of set B), and then into the run
+// layout by the 8x8 transpose (word 2r: set A row r, word 2r + 1: set B row r,
+// of column j).  The reverse takes the same steps backwards.
+// The exchange between lanes 1 apart of words 0-3 (odd lanes) against words
+// 4-7 (even lanes), used both ways.  Value selects only (see transpose_stage).
+template <int I = 0>
+__device__ __forceinline__ u32x8 swap_halves(u32x8 m) {
+  if constexpr (I < 4) {
+    const bool h = (threadIdx.x & 1u) != 0;
+    const uint32_t a = m[I], b = m[4 + I];
+    const uint32_t got = lane_xor<1>(h ? a : b);
+    m[I] = h ? got : a;
+    m[4 + I] = h ? b : got;
+    return swap_halves<I + 1>(m);
+  } else {
+    return m;
+  }
+}
+// halves layout -> whole rows (lane 2r: set A row r = [own A half 0, the
+// neighbour's A half 1]; lane 2r + 1: set B row r = [the neighbour's B half 0,
+// own B half 1]) -> run layout
+__device__ __forceinline__ u32x8 halves_to_runs(u32x8 m) { return lanes_transpose8(swap_halves(m)); }
+__device__ __forceinline__ u32x8 runs_to_halves(u32x8 m) { return swap_halves(lanes_transpose8(m)); }
+
+// The run at column 4 * (lane & 7) of a run side, replica f, at tile row 0.
+template <class Sh>
+__device__ __forceinline__ uintptr_t run_base(const reshard_segment_t* __restrict__ S,
+                                              const uint32_t* __restrict__ refs, const Sh& sh, uint32_t r0,
+                                              bool dst, uint32_t f) {
+  const uint32_t want = 4u * (threadIdx.x & 7u);
+  uintptr_t base = 0;
+#pragma unroll 1  // one segment's fields at a time: unrolled, they take ~100 SGPRs
+  for (int s = 0; s < 8; ++s) {
+    const uintptr_t p = (dst ? sh.ptr(refs[S[s].ptr + f]) : sh.ptr(S[s].ptr)) + uint64_t(S[s].offset) +
+                        uint64_t(r0) * 4u;
+    base = S[s].col == want ? p : base;
+  }
+  return base;
+}
+
+// Slices 2P and 2P + 1 of a window_runs8 tile (P a template argument, so that
+// no word index is left to run time).
+template <int P, bool src_runs>
+__device__ __forceinline__ u32x8 runs8_load(uintptr_t g, uint32_t hr) {
+  const uint32_t lane = threadIdx.x;
+  u32x8 m;
+#pragma unroll
+  for (int set = 0; set < 2; ++set) {
+    if constexpr (src_runs) {  // lane j of group G: rows 4G..4G+3 of the run at column 4j
+      const uint32_t r = 4u * (lane >> 3) + 128u * uint32_t(2 * P + set);
+      uint32_t w[4] = {0, 0, 0, 0};
+      if (r + 4 <= hr) {
+        const u32x4 x = load_16_unaligned(g + uint64_t(r) * 4u);
+        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r + i < hr) w[i] = __builtin_nontemporal_load(as_global<const u32_u>(g + uint64_t(r + i) * 4u));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) m[2 * i + set] = w[i];
+    } else {  // half lane & 1 of row lane / 2 of whole 32-byte rows
+      const uint32_t r = (lane >> 1) + 128u * uint32_t(2 * P + set);
+      u32x4 x = u32x4{0, 0, 0, 0};
+      if (r < hr) x = load_16_unaligned(g + uint64_t(r) * 32u);
+      m[4 * set] = x.x; m[4 * set + 1] = x.y; m[4 * set + 2] = x.z; m[4 * set + 3] = x.w;
+    }
+  }
+  return m;
+}
+
+template <int P, bool dst_runs>
+__device__ __forceinline__ void runs8_store(u32x8 m, uintptr_t g, uint32_t hr) {
+  const uint32_t lane = threadIdx.x;
+#pragma unroll
+  for (int set = 0; set < 2; ++set) {
+    if constexpr (dst_runs) {
+      const uint32_t r = 4u * (lane >> 3) + 128u * uint32_t(2 * P + set);
+      const uint32_t w[4] = {m[set], m[2 + set], m[4 + set], m[6 + set]};
+      if (r + 4 <= hr) {
+        store_bytes(g + uint64_t(r) * 4u, u32x4{w[0], w[1], w[2], w[3]}, 16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (r + i < hr) __builtin_nontemporal_store(w[i], as_global<u32_u>(g + uint64_t(r + i) * 4u));
+      }
+    } else {
+      const uint32_t r = (lane >> 1) + 128u * uint32_t(2 * P + set);
+      if (r < hr)
+        store_bytes(g + uint64_t(r) * 32u, u32x4{m[4 * set], m[4 * set + 1], m[4 * set + 2], m[4 * set + 3]}, 16);
+    }
+  }
+}
+
+// One body per pair of sides, so that each is straight-line code with no
+// values merged across the two layouts.
+template <bool src_runs, bool dst_runs, class Sh>
+__device__ __forceinline__ void window_runs8_sides(const reshard_descriptor_t& D,
+                                                   const reshard_segment_t* __restrict__ src_segs,
+                                                   const reshard_segment_t* __restrict__ dst_segs,
+                                                   const uint32_t* __restrict__ refs, const Sh& sh,
+                                                   uint32_t r0, uint32_t hr) {
+  const uint32_t h = threadIdx.x & 1u;
+  uintptr_t gs;
+  if constexpr (src_runs)
+    gs = run_base(src_segs, refs, sh, r0, false, 0);
+  else
+    gs = sh.ptr(src_segs[0].ptr) + uint64_t(src_segs[0].offset) + uint64_t(r0) * 32u + 16u * h;
+  u32x8 m0 = runs8_load<0, src_runs>(gs, hr);
+  u32x8 m1 = runs8_load<1, src_runs>(gs, hr);
+  if constexpr (src_runs && !dst_runs) {
+    m0 = runs_to_halves(m0);
+    m1 = runs_to_halves(m1);
+  } else if constexpr (!src_runs && dst_runs) {
+    m0 = halves_to_runs(m0);
+    m1 = halves_to_runs(m1);
+  }
+  for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {  // one fan-out on a run side
+    uintptr_t gd;
+    if constexpr (dst_runs)
+      gd = run_base(dst_segs, refs, sh, r0, true, f);
+    else
+      gd = sh.ptr(refs[dst_segs[0].ptr + f]) + uint64_t(dst_segs[0].offset) + uint64_t(r0) * 32u + 16u * h;
+    runs8_store<0, dst_runs>(m0, gd, hr);
+    runs8_store<1, dst_runs>(m1, gd, hr);
+  }
+}
+
+template <class Sh>
+__device__ __forceinline__ void window_runs8(const reshard_descriptor_t& D,
+                                             const reshard_segment_t* __restrict__ segs,
+                                             const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
+  const uint32_t rows = D.extent[0], per_tile = D.extent[1];  // 512 rows per tile
   const uint32_t r0 = tile * per_tile;
   const uint32_t hr = min(per_tile, rows - r0);
   const reshard_segment_t* src_segs = segs + D.src_ptr;
   const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
-  const uint32_t j = threadIdx.x & uint32_t(K - 1);   // lane within its group
-  const uint32_t group_row = threadIdx.x & ~uint32_t(K - 1);
-  uint32_t m[kRows][K];
-  if (runs_side(src_segs, D.dst_ref_begin, K)) {
-    // lane j reads K consecutive rows of the run at column 4j, then the group transposes
-    uintptr_t g = 0;
-    for (uint32_t s = 0; s < uint32_t(K); ++s)
-      if (src_segs[s].col == 4u * j) g = sh.ptr(src_segs[s].ptr) + uint64_t(src_segs[s].offset) + uint64_t(r0) * 4u;
-#pragma unroll
-    for (int k = 0; k < kRows; ++k) {
-      const uint32_t r = uint32_t(k * kBlock) + group_row;
-#pragma unroll
-      for (int i = 0; i < K; ++i) m[k][i] = 0;
-      if (r + K <= hr) {
-#pragma unroll
-        for (int q = 0; q < kVec; ++q) {
-          const u32x4 x = load_16_unaligned(g + uint64_t(r) * 4u + 16u * q);
-          m[k][4 * q] = x.x; m[k][4 * q + 1] = x.y; m[k][4 * q + 2] = x.z; m[k][4 * q + 3] = x.w;
-        }
-      } else {
-#pragma unroll
-        for (int i = 0; i < K; ++i)
-          if (r + i < hr) m[k][i] = __builtin_nontemporal_load(as_global<const u32_u>(g + uint64_t(r + i) * 4u));
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < kRows; ++k) lanes_transpose<K>(m[k]);
-  } else {  // one packed run of whole rows
-    const reshard_segment_t S = src_segs[0];
-    const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * (4u * K);
-#pragma unroll
-    for (int k = 0; k < kRows; ++k) {
-      const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
-#pragma unroll
-      for (int i = 0; i < K; ++i) m[k][i] = 0;
-      if (r < hr) {
-#pragma unroll
-        for (int q = 0; q < kVec; ++q) {
-          const u32x4 x = load_16_unaligned(g + uint64_t(r) * (4u * K) + 16u * q);
-          m[k][4 * q] = x.x; m[k][4 * q + 1] = x.y; m[k][4 * q + 2] = x.z; m[k][4 * q + 3] = x.w;
-        }
-      }
-    }
-  }
-  if (runs_side(dst_segs, D.fanout, K)) {
-    // the group transposes, then lane j writes K consecutive rows of the run at column 4j
-#pragma unroll
-    for (int k = 0; k < kRows; ++k) lanes_transpose<K>(m[k]);
-    for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {
-      uintptr_t g = 0;
-      for (uint32_t s = 0; s < uint32_t(K); ++s)
-        if (dst_segs[s].col == 4u * j)
-          g = sh.ptr(refs[dst_segs[s].ptr + f]) + uint64_t(dst_segs[s].offset) + uint64_t(r0) * 4u;
-#pragma unroll
-      for (int k = 0; k < kRows; ++k) {
-        const uint32_t r = uint32_t(k * kBlock) + group_row;
-        if (r + K <= hr) {
-#pragma unroll
-          for (int q = 0; q < kVec; ++q)
-            store_bytes(g + uint64_t(r) * 4u + 16u * q,
-                        u32x4{m[k][4 * q], m[k][4 * q + 1], m[k][4 * q + 2], m[k][4 * q + 3]}, 16);
-        } else {
-#pragma unroll
-          for (int i = 0; i < K; ++i)
-            if (r + i < hr) __builtin_nontemporal_store(m[k][i], as_global<u32_u>(g + uint64_t(r + i) * 4u));
-        }
-      }
-    }
-  } else {  // one packed run of whole rows
-    const reshard_segment_t S = dst_segs[0];
-    for (uint32_t f = 0; f < S.fanout; ++f) {
-      const uintptr_t g = sh.ptr(refs[S.ptr + f]) + uint64_t(S.offset) + uint64_t(r0) * (4u * K);
-#pragma unroll
-      for (int k = 0; k < kRows; ++k) {
-        const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
-        if (r < hr) {
-#pragma unroll
-          for (int q = 0; q < kVec; ++q)
-            store_bytes(g + uint64_t(r) * (4u * K) + 16u * q,
-                        u32x4{m[k][4 * q], m[k][4 * q + 1], m[k][4 * q + 2], m[k][4 * q + 3]}, 16);
-        }
-      }
-    }
-  }
+  const bool src_runs = runs_side(src_segs, D.dst_ref_begin, 8);
+  const bool dst_runs = runs_side(dst_segs, D.fanout, 8);
+  if (src_runs && dst_runs)
+    window_runs8_sides<true, true>(D, src_segs, dst_segs, refs, sh, r0, hr);
+  else if (src_runs)
+    window_runs8_sides<true, false>(D, src_segs, dst_segs, refs, sh, r0, hr);
+  else
+    window_runs8_sides<false, true>(D, src_segs, dst_segs, refs, sh, r0, hr);
 }
 
 // Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
@@ -958,7 +1014,7 @@ enum KernelKind : int {
   kKindQuadRows = 4, // every descriptor a 16-byte row-mode band with the quad exchange
                      // (kQuadRowsPerLane rows per lane): no LDS, fewer registers
   kKindRuns = 5,     // every descriptor a 32-byte window band of 4-byte column runs
-                     // (window_runs<8>): no LDS
+                     // (window_runs8): no LDS
   kKindAligned = 8,  // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
@@ -999,7 +1055,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   }
   if constexpr (kKind == kKindRuns) {
     const Shards<kKarg> wsh{table, &karg, refs};
-    window_runs<8>(D, segs, refs, wsh, t - tile_begin[lo]);
+    window_runs8(D, segs, refs, wsh, t - tile_begin[lo]);
     return;
   }
   if constexpr (kKind == kKindAll) {
@@ -1120,7 +1176,7 @@ void launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descripto
 
 namespace {
 
-// Whether a descriptor is a band window_runs<8> moves: 32 bytes wide, tiles of
+// Whether a descriptor is a band window_runs8 moves: 32 bytes wide, tiles of
 // the window's rows, one side eight packed 4-byte runs, the other eight runs or
 // one packed run of whole rows (the same tests the kernel makes).  (Sixteen
 // lanes for 64-byte bands would need 71 VGPRs: one wave per SIMD fewer.)

@@ -39,6 +39,7 @@ def kernel_meta(tmp_path_factory):
             "private": int(re.search(r"\.private_segment_fixed_size:\s+(\d+)", block).group(1)),
             "vgpr": int(re.search(r"\.vgpr_count:\s+(\d+)", block).group(1)),
             "occupancy": occupancy.get(name),
+            "lds": int(re.search(r"\.group_segment_fixed_size:\s+(\d+)", block).group(1)),
         }
     return kernels
 
@@ -54,6 +55,14 @@ def test_every_variant_is_compiled(kernel_meta):
 def test_no_scratch(kernel_meta):
     for name, meta in kernel_meta.items():
         assert meta["private"] == 0, (name, meta)
+
+
+def test_lds_only_in_the_window_variant(kernel_meta):
+    """Only the all-modes variant (LDS windows) allocates LDS: a private array
+    the compiler moved to LDS (an index it could not resolve) shows up here."""
+    for name, meta in kernel_meta.items():
+        want = 16384 if re.search(r"reshard_copy_kernelILb[01]ELi3E", name) else 0
+        assert meta["lds"] == want, (name, meta)
 
 
 def test_eight_waves_per_simd(kernel_meta):
