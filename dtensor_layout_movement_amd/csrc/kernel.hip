@@ -690,18 +690,18 @@ __device__ __forceinline__ u32x8 lanes_transpose8(u32x8 m) {
   return transpose_stage<4>(transpose_stage<2>(transpose_stage<1>(m)));
 }
 
-// Whether segments [0, n) of a band are K packed 4-byte column runs with one
-// fan-out, or one packed run of the whole 4K-byte row.
-__host__ __device__ __forceinline__ bool runs_side(const reshard_segment_t* __restrict__ S, uint32_t n,
-                                                   uint32_t k) {
+// Whether segments [0, n) of a band are K packed 4-byte column runs in column
+// order (run s at column 4s) with one fan-out, or one packed run of the whole
+// 4K-byte row.  Host-side checks: in a plan that runs the band kernel every
+// descriptor passed them, so on the device a side's segment count tells the two
+// apart (K segments: runs, one: whole rows).
+inline bool runs_side(const reshard_segment_t* S, uint32_t n, uint32_t k) {
   if (n != k) return false;
-  bool ok = true;
   for (uint32_t s = 0; s < n; ++s)
-    ok = ok && S[s].width == 4u && S[s].row_stride == 4 && S[s].fanout == S[0].fanout;
-  return ok;
+    if (S[s].width != 4u || S[s].row_stride != 4 || S[s].col != 4u * s || S[s].fanout != S[0].fanout) return false;
+  return true;
 }
-__host__ __device__ __forceinline__ bool full_side(const reshard_segment_t* __restrict__ S, uint32_t n,
-                                                   uint32_t w) {
+inline bool full_side(const reshard_segment_t* S, uint32_t n, uint32_t w) {
   return n == 1 && S[0].width == w && uint64_t(S[0].row_stride) == w;
 }
 
@@ -740,20 +740,17 @@ __device__ __forceinline__ u32x8 swap_halves(u32x8 m) {
 __device__ __forceinline__ u32x8 halves_to_runs(u32x8 m) { return lanes_transpose8(swap_halves(m)); }
 __device__ __forceinline__ u32x8 runs_to_halves(u32x8 m) { return swap_halves(lanes_transpose8(m)); }
 
-// The run at column 4 * (lane & 7) of a run side, replica f, at tile row 0.
-template <class Sh>
+// The run at column 4 * (lane & 7) of a run side (segment lane & 7: the runs
+// are in column order), replica f, at tile row 0.  Each lane resolves its own
+// run, so the three dependent lookups (segment, fan-out list, pointer) are
+// paid once, not once per segment.
+template <bool dst, class Sh>
 __device__ __forceinline__ uintptr_t run_base(const reshard_segment_t* __restrict__ S,
                                               const uint32_t* __restrict__ refs, const Sh& sh, uint32_t r0,
-                                              bool dst, uint32_t f) {
-  const uint32_t want = 4u * (threadIdx.x & 7u);
-  uintptr_t base = 0;
-#pragma unroll 1  // one segment's fields at a time: unrolled, they take ~100 SGPRs
-  for (int s = 0; s < 8; ++s) {
-    const uintptr_t p = (dst ? sh.ptr(refs[S[s].ptr + f]) : sh.ptr(S[s].ptr)) + uint64_t(S[s].offset) +
-                        uint64_t(r0) * 4u;
-    base = S[s].col == want ? p : base;
-  }
-  return base;
+                                              uint32_t f) {
+  const reshard_segment_t& seg = S[threadIdx.x & 7u];
+  const uint32_t i = dst ? refs[seg.ptr + f] : seg.ptr;
+  return sh.ptr(i) + uint64_t(seg.offset) + uint64_t(r0) * 4u;
 }
 
 // Slices 2P and 2P + 1 of a window_runs8 tile (P a template argument, so that
@@ -821,7 +818,7 @@ __device__ __forceinline__ void window_runs8_sides(const reshard_descriptor_t& D
   const uint32_t h = threadIdx.x & 1u;
   uintptr_t gs;
   if constexpr (src_runs)
-    gs = run_base(src_segs, refs, sh, r0, false, 0);
+    gs = run_base<false>(src_segs, refs, sh, r0, 0);
   else
     gs = sh.ptr(src_segs[0].ptr) + uint64_t(src_segs[0].offset) + uint64_t(r0) * 32u + 16u * h;
   u32x8 m0 = runs8_load<0, src_runs>(gs, hr);
@@ -836,7 +833,7 @@ __device__ __forceinline__ void window_runs8_sides(const reshard_descriptor_t& D
   for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {  // one fan-out on a run side
     uintptr_t gd;
     if constexpr (dst_runs)
-      gd = run_base(dst_segs, refs, sh, r0, true, f);
+      gd = run_base<true>(dst_segs, refs, sh, r0, f);
     else
       gd = sh.ptr(refs[dst_segs[0].ptr + f]) + uint64_t(dst_segs[0].offset) + uint64_t(r0) * 32u + 16u * h;
     runs8_store<0, dst_runs>(m0, gd, hr);
@@ -853,8 +850,8 @@ __device__ __forceinline__ void window_runs8(const reshard_descriptor_t& D,
   const uint32_t hr = min(per_tile, rows - r0);
   const reshard_segment_t* src_segs = segs + D.src_ptr;
   const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
-  const bool src_runs = runs_side(src_segs, D.dst_ref_begin, 8);
-  const bool dst_runs = runs_side(dst_segs, D.fanout, 8);
+  const bool src_runs = D.dst_ref_begin == 8;  // else one segment of whole rows
+  const bool dst_runs = D.fanout == 8;
   if (src_runs && dst_runs)
     window_runs8_sides<true, true>(D, src_segs, dst_segs, refs, sh, r0, hr);
   else if (src_runs)

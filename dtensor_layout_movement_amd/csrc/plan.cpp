@@ -464,6 +464,18 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
       merged.push_back(s);
     }
     b.src = merged;
+    // destinations in column order too (with their fan-out lists)
+    std::vector<size_t> order(b.dst.size());
+    for (size_t k = 0; k < order.size(); ++k) order[k] = k;
+    std::sort(order.begin(), order.end(), [&](size_t x, size_t y) { return b.dst[x].col < b.dst[y].col; });
+    std::vector<reshard_segment_t> dst_sorted;
+    std::vector<std::vector<uint32_t>> refs_sorted;
+    for (size_t k : order) {
+      dst_sorted.push_back(b.dst[k]);
+      refs_sorted.push_back(std::move(b.dst_refs[k]));
+    }
+    b.dst = std::move(dst_sorted);
+    b.dst_refs = std::move(refs_sorted);
     if (b.src.size() > kWindowMaxSegs || b.dst.size() > kWindowMaxSegs) return false;
     for (const auto& s : b.src) bits |= s.offset | s.row_stride | s.col | s.width;
     for (const auto& d : b.dst) bits |= d.offset | d.row_stride | d.col | d.width;
