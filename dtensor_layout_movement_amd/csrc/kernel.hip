@@ -528,10 +528,13 @@ __device__ __forceinline__ u32x4 quad_transpose(u32x4 v) {
 __device__ __forceinline__ bool quad_segments(const reshard_segment_t* __restrict__ S, uint32_t n,
                                               uint32_t* fanout) {
   if (n != 4) return false;
+  // every field is read and the tests are combined with &, not &&: a
+  // short-circuit chain makes each load wait for the previous test (a dozen
+  // dependent scalar round trips at the start of every tile)
   bool ok = true;
 #pragma unroll
   for (int s = 0; s < 4; ++s)
-    ok = ok && S[s].width == 4u && S[s].row_stride == 4 && S[s].fanout == S[0].fanout;
+    ok &= (S[s].width == 4u) & (S[s].row_stride == 4) & (S[s].fanout == S[0].fanout);
   *fanout = S[0].fanout;
   return ok;
 }
@@ -598,16 +601,27 @@ __device__ __forceinline__ void window_rows(const reshard_descriptor_t& D, const
     for (int k = 0; k < kRows; ++k)
       if (uint32_t(k) < used) v[k] = quad_transpose(v[k]);  // uniform: every lane takes part
   } else {
+    // every slot's load is issued before any is used (a load under a per-lane
+    // test would wait for the one before it): slots past the tile read its
+    // last row again, in bounds, and drop it
+    uint32_t rr[kRows];
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) rr[k] = min(uint32_t(k * kBlock) + threadIdx.x, hr - 1);
     for (uint32_t s = 0; s < D.dst_ref_begin; ++s) {
       const reshard_segment_t S = src_segs[s];
       const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+      u32x4 x[kRows];
+      if (S.width == 16u) {  // uniform: whole 16-byte rows
+#pragma unroll
+        for (int k = 0; k < kRows; ++k) x[k] = load_16_unaligned(g + uint64_t(rr[k]) * uint64_t(S.row_stride));
+      } else {
+#pragma unroll
+        for (int k = 0; k < kRows; ++k) x[k] = load_bytes(g + uint64_t(rr[k]) * uint64_t(S.row_stride), S.width);
+      }
 #pragma unroll
       for (int k = 0; k < kRows; ++k) {
-        const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
-        if (r < hr) {
-          const u32x4 x = shift_left_bytes(load_bytes(g + uint64_t(r) * uint64_t(S.row_stride), S.width), S.col);
-          v[k] = u32x4{v[k].x | x.x, v[k].y | x.y, v[k].z | x.z, v[k].w | x.w};
-        }
+        const u32x4 y = shift_left_bytes(x[k], S.col);
+        v[k] = u32x4{v[k].x | y.x, v[k].y | y.y, v[k].z | y.z, v[k].w | y.w};
       }
     }
   }
