@@ -393,6 +393,30 @@ def test_row_mode_tile_rows():
         assert {d["extent"][1] for d in descs} == {rows}, name
 
 
+@pytest.mark.parametrize("name", ["w", "up_proj", "layer0.down", "rep_src", "rep_both", "empty_src", "nested",
+                                  "narrow_scatter", "narrow_gather", "narrow_scatter_rep", "narrow_gather_rep",
+                                  "narrow_f32_cols", "narrow_bf16_cols", "narrow_8byte_rows", "narrow_fp8_3d",
+                                  "runs_scatter", "runs_gather", "runs_scatter_rep", "runs_f32_cols"])
+def test_window_segments_in_column_order(name):
+    """Every window band lists its source segments, and its destination segments,
+    by column and without overlap, covering the band's full width on each side
+    (the register paths take lane j's 4-byte run to be segment j)."""
+    spec = {s.name: s for s in small_specs()}[name]
+    with Plan([spec]) as plan:
+        descs, _ = R.reshard_plan_descriptors(plan.handle)
+        segs = R.reshard_plan_segments(plan.handle)
+        windows = [D for D in descs if D["mode"] == R.DESC_WINDOW]
+        assert windows, name
+        for D in windows:
+            first = D["src_ptr"]
+            for side in (segs[first:first + D["dst_ref_begin"]],
+                         segs[first + D["dst_ref_begin"]:first + D["dst_ref_begin"] + D["fanout"]]):
+                cols = [(sg["col"], sg["col"] + sg["width"]) for sg in side]
+                assert cols == sorted(cols), (name, cols)
+                assert cols[0][0] == 0 and cols[-1][1] == D["run_bytes"], (name, cols)
+                assert all(a[1] == b[0] for a, b in zip(cols, cols[1:])), (name, cols)
+
+
 def test_window_segments_worked_example():
     """The pages' example as one window band per source shard: one source segment
     (the whole 16-byte rows, merged across the four pieces) and four destination
