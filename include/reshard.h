@@ -149,11 +149,18 @@ typedef struct reshard_piece {
  *                            pitch `row_items`.  Its segments are
  *                            segments[src_ptr .. src_ptr + dst_ref_begin) (sources,
  *                            read into the window) followed by `fanout` destination
- *                            segments (written from it); offsets and strides are
- *                            ignored.  Used for narrow or misaligned pieces.
- *                            A band at most 16 bytes wide skips LDS: one lane
- *                            per row assembles the row in registers; then
- *                            `extent[1]` = 1024 rows per tile.
+ *                            segments (written from it), each side in column
+ *                            order; offsets and strides are ignored.  Used for
+ *                            narrow or misaligned pieces.  A band at most 16
+ *                            bytes wide skips LDS: one lane per row assembles
+ *                            the row in registers, `extent[1]` = 1024 rows per
+ *                            tile (512 when one side is four packed 4-byte
+ *                            column runs, which the four lanes of a quad
+ *                            exchange).  A 32-byte band whose sides are eight
+ *                            packed 4-byte runs or whole rows (at least one side
+ *                            runs) skips LDS too when every descriptor of the
+ *                            plan is such a band: eight lanes exchange words,
+ *                            512 rows per tile.
  *   RESHARD_DESC_CONVERT     rows of `run_bytes` ELEMENTS (not bytes) converted by
  *                            conversion `unit`; item c is elements
  *                            [c*8, min(c*8+8, run)) of the row; row_items =
