@@ -28,11 +28,17 @@ constexpr uint32_t kAllAligned16 = 1;  // every shard pointer of this execute is
 // (and their window segments).
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs);
 
-// One launch of variant `kind` with `n_wg` workgroups on `stream`.  Shard
-// pointers come from `karg` when `table` is NULL, else from the device table.
-void launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,
-                 uint32_t n_desc, const uint32_t* tile_begin, const uint32_t* refs,
-                 const reshard_segment_t* segs, const void* const* table, const KargPtrs& karg,
-                 uint32_t n_tiles, uint32_t per_xcd, uint32_t flags);
+// Workgroups of one launch at most: a dispatch counts its work-items in 32
+// bits.  A multiple of kXcds, so that every launch starts on XCD 0's turn.
+constexpr uint32_t kMaxLaunchBlocks = (0xffffffffu / 256u) & ~(kXcds - 1);
+
+// Variant `kind` over workgroups [0, n_wg) on `stream`, as one launch, or as
+// several back-to-back launches of at most kMaxLaunchBlocks workgroups each
+// when n_wg is larger.  Shard pointers come from `karg` when `table` is NULL,
+// else from the device table.  Returns the first launch error.
+hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,
+                       uint32_t n_desc, const uint32_t* tile_begin, const uint32_t* refs,
+                       const reshard_segment_t* segs, const void* const* table, const KargPtrs& karg,
+                       uint32_t n_tiles, uint32_t per_xcd, uint32_t flags);
 
 }  // namespace rs

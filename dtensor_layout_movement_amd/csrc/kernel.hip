@@ -1035,16 +1035,18 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     const reshard_descriptor_t* __restrict__ descs, uint32_t n_desc,
     const uint32_t* __restrict__ tile_begin, const uint32_t* __restrict__ refs,
     const reshard_segment_t* __restrict__ segs, const void* const* __restrict__ table, KargPtrs karg,
-    uint32_t n_tiles, uint32_t per_xcd, uint32_t flags) {
+    uint32_t n_tiles, uint32_t per_xcd, uint32_t flags, uint32_t block_base) {
   constexpr int kKind = kVariant % kKindAligned;
   constexpr bool kAligned = kVariant >= kKindAligned;
-  // Block b runs on XCD b % kXcds.  Each XCD takes groups of kXcdGroup
-  // consecutive tiles, the XCDs side by side: nearby tiles share an XCD's L2
-  // while all XCDs stream through the same region of memory.  Plans smaller
-  // than one round of groups (per_xcd == 0) use block b for tile b.
-  const uint32_t kx = blockIdx.x / kXcds;
-  const uint32_t t = per_xcd == 0 ? blockIdx.x
-                                  : ((kx / kXcdGroup) * kXcds + blockIdx.x % kXcds) * kXcdGroup + kx % kXcdGroup;
+  // Block b of the plan (block_base + blockIdx.x: a plan larger than one
+  // launch is split into launches of a multiple of kXcds blocks) runs on XCD
+  // b % kXcds.  Each XCD takes groups of kXcdGroup consecutive tiles, the
+  // XCDs side by side: nearby tiles share an XCD's L2 while all XCDs stream
+  // through the same region of memory.  Plans smaller than one round of groups
+  // (per_xcd == 0) use block b for tile b.
+  const uint32_t b = block_base + blockIdx.x;
+  const uint32_t kx = b / kXcds;
+  const uint32_t t = per_xcd == 0 ? b : ((kx / kXcdGroup) * kXcds + b % kXcds) * kXcdGroup + kx % kXcdGroup;
   if (t >= n_tiles) return;
   uint32_t lo = 0, hi = n_desc;  // last descriptor whose first tile is <= t
   while (hi - lo > 1) {
@@ -1137,50 +1139,43 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
 }
 
 template <bool kKarg, int kVariant>
-void launch_kind(uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
-                 const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
-                 const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
-                 uint32_t flags) {
-  hipLaunchKernelGGL((reshard_copy_kernel<kKarg, kVariant>), dim3(n_wg), dim3(kBlock), 0, stream, descs, n_desc,
-                     tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags);
+hipError_t launch_kind(uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
+                       const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
+                       const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
+                       uint32_t flags) {
+  for (uint32_t base = 0; base < n_wg; base += kMaxLaunchBlocks) {
+    const uint32_t grid = n_wg - base < kMaxLaunchBlocks ? n_wg - base : kMaxLaunchBlocks;
+    hipLaunchKernelGGL((reshard_copy_kernel<kKarg, kVariant>), dim3(grid), dim3(kBlock), 0, stream, descs,
+                       n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags, base);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 template <bool kKarg>
-void launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
-            const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
-            const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
-            uint32_t flags) {
+hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
+                  const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
+                  const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
+                  uint32_t flags) {
   const bool aligned = (flags & kAllAligned16) != 0;
+#define RS_LAUNCH(V) \
+  launch_kind<kKarg, V>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags)
   switch (kind) {
     case kKindItems16:  // (an aligned-only build of this one measured slower on long copies)
-      launch_kind<kKarg, kKindItems16>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                       n_tiles, per_xcd, flags);
-      break;
+      return RS_LAUNCH(kKindItems16);
     case kKindChunks:
-      if (aligned)
-        launch_kind<kKarg, kKindChunks + kKindAligned>(n_wg, stream, descs, n_desc, tile_begin, refs, segs,
-                                                       table, karg, n_tiles, per_xcd, flags);
-      else
-        launch_kind<kKarg, kKindChunks>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                        n_tiles, per_xcd, flags);
-      break;
+      return aligned ? RS_LAUNCH(kKindChunks + kKindAligned) : RS_LAUNCH(kKindChunks);
     case kKindCopy:
-      launch_kind<kKarg, kKindCopy>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                    n_tiles, per_xcd, flags);
-      break;
+      return RS_LAUNCH(kKindCopy);
     case kKindQuadRows:
-      launch_kind<kKarg, kKindQuadRows>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                        n_tiles, per_xcd, flags);
-      break;
+      return RS_LAUNCH(kKindQuadRows);
     case kKindRuns:
-      launch_kind<kKarg, kKindRuns>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                    n_tiles, per_xcd, flags);
-      break;
+      return RS_LAUNCH(kKindRuns);
     default:
-      launch_kind<kKarg, kKindAll>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg,
-                                   n_tiles, per_xcd, flags);
-      break;
+      return RS_LAUNCH(kKindAll);
   }
+#undef RS_LAUNCH
 }
 
 }  // namespace
@@ -1219,16 +1214,15 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
          : window ? kKindAll : kKindCopy;
 }
 
-void launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,
-                 uint32_t n_desc, const uint32_t* tile_begin, const uint32_t* refs,
-                 const reshard_segment_t* segs, const void* const* table, const KargPtrs& karg,
-                 uint32_t n_tiles, uint32_t per_xcd, uint32_t flags) {
+hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,
+                       uint32_t n_desc, const uint32_t* tile_begin, const uint32_t* refs,
+                       const reshard_segment_t* segs, const void* const* table, const KargPtrs& karg,
+                       uint32_t n_tiles, uint32_t per_xcd, uint32_t flags) {
   if (table)
-    launch<false>(kind, n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd,
-                  flags);
-  else
-    launch<true>(kind, n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd,
-                 flags);
+    return launch<false>(kind, n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles,
+                         per_xcd, flags);
+  return launch<true>(kind, n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd,
+                      flags);
 }
 
 }  // namespace rs

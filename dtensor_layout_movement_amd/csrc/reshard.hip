@@ -320,16 +320,21 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
     }
     table = reinterpret_cast<const void* const*>(static_cast<void**>(plan->d_slots) + size_t(slot) * n);
   }
-  rs::launch_copy(plan->kind, plan->n_wg, stream, plan->d_descs, uint32_t(H.descs.size()), plan->d_tile_begin,
-                  plan->d_refs, plan->d_segs, table, karg, uint32_t(H.n_tiles), plan->per_xcd, flags);
-  e = hipGetLastError();
-  if (e != hipSuccess) return hip_fail(e, "reshard_copy_kernel launch");
+  const hipError_t le = rs::launch_copy(plan->kind, plan->n_wg, stream, plan->d_descs, uint32_t(H.descs.size()),
+                                        plan->d_tile_begin, plan->d_refs, plan->d_segs, table, karg,
+                                        uint32_t(H.n_tiles), plan->per_xcd, flags);
   if (slot >= 0) {
+    // recorded even when a launch failed: the launches of a split plan that
+    // went out before it may still read the slot
     e = hipEventRecord(plan->ev[slot], stream);
-    if (e != hipSuccess) return hip_fail(e, "hipEventRecord(pointer slot)");
-    plan->ev_live[slot] = true;
-    plan->ev_stream[slot] = stream;
+    if (e == hipSuccess) {
+      plan->ev_live[slot] = true;
+      plan->ev_stream[slot] = stream;
+    } else if (le == hipSuccess) {
+      return hip_fail(e, "hipEventRecord(pointer slot)");
+    }
   }
+  if (le != hipSuccess) return hip_fail(le, "reshard_copy_kernel launch");
   return RESHARD_OK;
 }
 

@@ -102,7 +102,8 @@ typedef struct reshard_plan_stats {
                              destination dtype) */
   int64_t n_descriptors;  /* device copy descriptors after dim merging / splitting */
   int64_t table_bytes;    /* size of the device-resident descriptor table */
-  int64_t n_workgroups;   /* grid of one execute launch: one workgroup per tile (0 until upload) */
+  int64_t n_workgroups;   /* workgroups of one execute, one per tile (0 until upload); more than
+                             16,777,208 go out as several launches of at most that many */
   double plan_host_us;    /* host time spent planning in reshard_plan_create* */
 } reshard_plan_stats_t;
 
