@@ -10,7 +10,7 @@ import oracle_pins as P
 from dtensor_layout_movement_amd import workloads as W
 from gpu_harness import GuardedShards, run_parity, shard_nbytes
 from reshard_harness import Plan, assert_boxes_agree, assert_descriptors_in_bounds, box_shape, oracle_boxes
-from test_planner import random_specs, small_specs
+from test_planner import narrow_random_specs, random_specs, small_specs
 
 pytestmark = pytest.mark.gpu
 
@@ -437,6 +437,16 @@ def test_random_layouts_batched(batch):
     six per fused launch."""
     specs = random_specs(100 + batch, 6)
     run_parity(specs, "raw", batch)
+
+
+@pytest.mark.parametrize("batch", range(4))
+def test_narrow_random_layouts(batch):
+    """Seeded random narrow layouts (rows of at most 32 bytes; whole rows against
+    4-byte runs, replicas, ragged row counts), one plan each, so that each runs
+    the build its descriptors select: row bands, quad and 8-lane exchanges, LDS
+    windows, items or chunks."""
+    for spec in narrow_random_specs(300 + batch, 10):
+        run_parity([spec], "raw", 8)
 
 
 def test_graph_capture_replays_match_oracle():

@@ -191,6 +191,59 @@ def random_specs(seed, count, max_numel=400_000):
     return out
 
 
+def narrow_random_specs(seed, count):
+    """Seeded random 2-d layouts whose rows are at most 32 bytes and whose column
+    splits give 1-, 2-, 4- or 8-byte runs: the register row mode, the quad and
+    8-lane exchanges and the LDS windows, with ragged row counts (partial
+    groups of four and eight rows, short last tiles), row splits on either side,
+    replicas on either side and every element size."""
+    rng = random.Random(seed)
+    out = []
+    while len(out) < count:
+        dtype = rng.choice([torch.uint8, torch.bfloat16, torch.float32, torch.float64])
+        es = torch.tensor([], dtype=dtype).element_size()
+        width = rng.choice([b for b in (4, 8, 16, 32) if b >= es])
+        cols = width // es
+        rows = rng.choice([rng.randint(1, 40), rng.randint(500, 1100), rng.randint(2000, 5000)])
+        runs4 = width // 4 if width in (16, 32) and es <= 4 else 0  # 4-byte runs: quad / 8-lane exchange
+        def layout():
+            k = rng.choice([c for c in (1, 2, 4, 8) if c <= cols])
+            if runs4 and rng.random() < 0.5:
+                k = runs4
+            r = rng.choice([1, 2, 3])
+            kind = rng.randint(0, 3)
+            if kind == 0:
+                return (k,), (1,)
+            if kind == 1:
+                return (r,), (0,)
+            if kind == 2:
+                return (r, k), (0, 1)
+            return (2, k), (RR, 1)
+        (sm, sp), (dm, dp) = layout(), layout()
+        if runs4 and rng.random() < 0.4:  # whole rows on one side, 4-byte runs on the other
+            rows_side = ((rng.choice([1, 2, 3]),), (0,))
+            runs_side = rng.choice([((runs4,), (1,)), ((2, runs4), (RR, 1))])
+            (sm, sp), (dm, dp) = (rows_side, runs_side) if rng.random() < 0.5 else (runs_side, rows_side)
+        out.append(T(f"nrand{seed}_{len(out)}", (rows, cols), dtype, sm, sp, dm, dp))
+    return out
+
+
+def test_narrow_random_layouts_descriptor_walk():
+    """40 seeded random narrow layouts: planned pieces and the byte-level walk of
+    the descriptor table both equal the oracle."""
+    for spec in narrow_random_specs(21, 40):
+        with Plan([spec]) as plan:
+            assert_boxes_agree(plan)
+            assert_descriptors_in_bounds(plan)
+            _, srcs = sources_for(spec, "raw", seed=6)
+            want = oracle_dsts(spec, srcs)
+            sflat = [None if s is None else s.contiguous().view(torch.uint8).reshape(-1).numpy() for s in srcs]
+            dflat = [np.zeros(b.numel() * b.element_size(), dtype=np.uint8) for b in want]
+            run_descriptors(plan, sflat, dflat)
+            for a, b in zip(dflat, want):
+                assert a.tobytes() == b.view(torch.uint8).reshape(-1).numpy().tobytes(), spec
+
+
 def test_random_moderate_layouts_descriptor_walk():
     """40 seeded random layout pairs of moderate size: planned pieces and the
     byte-level walk of the descriptor table both equal the oracle."""
