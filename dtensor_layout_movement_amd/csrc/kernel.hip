@@ -25,6 +25,7 @@ constexpr int kBlock = int(kTileThreads);  // threads per workgroup (4 wave64s)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x16 __attribute__((ext_vector_type(16)));
 
 // q = n / d for n < 2^31 with the planner's round-up multiplier (m, s).
 __device__ __forceinline__ uint32_t div_magic(uint32_t n, uint32_t m, uint32_t s) {
@@ -704,15 +705,16 @@ __device__ __forceinline__ u32x8 lanes_transpose8(u32x8 m) {
   return transpose_stage<4>(transpose_stage<2>(transpose_stage<1>(m)));
 }
 
-// Whether segments [0, n) of a band are K packed 4-byte column runs in column
-// order (run s at column 4s) with one fan-out, or one packed run of the whole
-// 4K-byte row.  Host-side checks: in a plan that runs the band kernel every
-// descriptor passed them, so on the device a side's segment count tells the two
-// apart (K segments: runs, one: whole rows).
-inline bool runs_side(const reshard_segment_t* S, uint32_t n, uint32_t k) {
+// Whether segments [0, n) of a band are K packed rw-byte column runs in column
+// order (run s at column rw * s) with one fan-out, or one packed run of the
+// whole row of w bytes.  Host-side checks: in a plan that runs a band kernel
+// every descriptor passed them, so on the device a side's segment count tells
+// the two apart (K segments: runs, one: whole rows).
+inline bool runs_side(const reshard_segment_t* S, uint32_t n, uint32_t k, uint32_t rw) {
   if (n != k) return false;
   for (uint32_t s = 0; s < n; ++s)
-    if (S[s].width != 4u || S[s].row_stride != 4 || S[s].col != 4u * s || S[s].fanout != S[0].fanout) return false;
+    if (S[s].width != rw || uint64_t(S[s].row_stride) != rw || S[s].col != rw * s || S[s].fanout != S[0].fanout)
+      return false;
   return true;
 }
 inline bool full_side(const reshard_segment_t* S, uint32_t n, uint32_t w) {
@@ -874,6 +876,133 @@ __device__ __forceinline__ void window_runs8(const reshard_descriptor_t& D,
     window_runs8_sides<false, true>(D, src_segs, dst_segs, refs, sh, r0, hr);
 }
 
+// A 64-byte window band whose one side is eight packed 8-byte column runs (four
+// bf16 or two fp32 columns per shard over eight shards) and whose other side is
+// one packed run of whole rows.  No LDS: a tile is 256 rows, 64 per wave, and
+// every 16-byte access of a wave is contiguous on both sides.
+//  - whole-row side: slice q (0..3) of lane L = 4a + b is quarter b of row
+//    16 q + a of the wave's 64 (one 1 KiB piece per slice);
+//  - run side: lane L = 8G + j holds run j at rows 16 m + 2G and 16 m + 2G + 1
+//    of the wave's 64 for m = 0..3 (16 bytes per m; the eight lanes that hold
+//    run j cover its rows 16 m .. 16 m + 15 in one access).
+// Between the two: a 4 x 4 transpose of 16-byte quarters across each quad
+// (lane 4a + b then holds all of row 16 b + a), then an 8 x 8 transpose of
+// 8-byte elements across each group of eight lanes: lane offset o = 4e + m
+// holds row 16 m + 2G + e, so after it lane j holds run j at those eight rows
+// in the order o, and the 16-byte piece m is elements m and 4 + m.
+//
+// Stage X of the 8 x 8 transpose on 8-byte elements (words 2k and 2k + 1 of
+// element k): element k of lane o and element k ^ X of lane o ^ X trade places
+// wherever bit X of o and of k differ.  Values and constant indices only.
+template <int X, int K = 0>
+__device__ __forceinline__ u32x16 transpose_stage64(u32x16 m) {
+  if constexpr (K < 8) {
+    if constexpr ((K & X) == 0) {
+      const bool hi = (threadIdx.x & uint32_t(X)) != 0;
+      constexpr int A = 2 * K, B = 2 * (K ^ X);
+      const uint32_t lo0 = m[A], lo1 = m[A + 1], up0 = m[B], up1 = m[B + 1];
+      const uint32_t got0 = lane_xor<X>(hi ? lo0 : up0), got1 = lane_xor<X>(hi ? lo1 : up1);
+      m[A] = hi ? got0 : lo0;
+      m[A + 1] = hi ? got1 : lo1;
+      m[B] = hi ? up0 : got0;
+      m[B + 1] = hi ? up1 : got1;
+    }
+    return transpose_stage64<X, K + 1>(m);
+  } else {
+    return m;
+  }
+}
+__device__ __forceinline__ u32x16 lanes_transpose8x64(u32x16 m) {
+  return transpose_stage64<4>(transpose_stage64<2>(transpose_stage64<1>(m)));
+}
+// Quarter q of the row is words 4q..4q+3: word i of every quarter goes through
+// one 4 x 4 word transpose of the quad.
+template <int I = 0>
+__device__ __forceinline__ u32x16 quarters_transpose(u32x16 m) {
+  if constexpr (I < 4) {
+    const u32x4 v = quad_transpose(u32x4{m[I], m[4 + I], m[8 + I], m[12 + I]});
+    m[I] = v.x;
+    m[4 + I] = v.y;
+    m[8 + I] = v.z;
+    m[12 + I] = v.w;
+    return quarters_transpose<I + 1>(m);
+  } else {
+    return m;
+  }
+}
+
+template <bool src_runs, class Sh>
+__device__ __forceinline__ void window_runs64_sides(const reshard_segment_t* __restrict__ src_segs,
+                                                    const reshard_segment_t* __restrict__ dst_segs,
+                                                    const uint32_t* __restrict__ refs, const Sh& sh,
+                                                    uint32_t r0, uint32_t hr) {
+  const uint32_t lane = threadIdx.x & 63u, w0 = (threadIdx.x >> 6) * 64u;  // the wave's first tile row
+  const uint32_t a = lane >> 2, b = lane & 3u, G = lane >> 3;
+  u32x16 m;
+  if constexpr (!src_runs) {  // whole rows in: slice q of lane 4a + b is quarter b of row 16q + a
+    const uintptr_t g = sh.ptr(src_segs[0].ptr) + uint64_t(src_segs[0].offset) + uint64_t(r0) * 64u + 16u * b;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t r = w0 + 16u * uint32_t(q) + a;
+      const u32x4 x = load_16_unaligned(g + uint64_t(min(r, hr - 1)) * 64u);  // past hr: never stored
+      m[4 * q] = x.x; m[4 * q + 1] = x.y; m[4 * q + 2] = x.z; m[4 * q + 3] = x.w;
+    }
+    m = lanes_transpose8x64(quarters_transpose(m));
+  } else {  // run lane & 7 in: rows 16m + 2G, 16m + 2G + 1 of the wave's 64, for m = 0..3
+    const reshard_segment_t& seg = src_segs[lane & 7u];
+    const uintptr_t g = sh.ptr(seg.ptr) + uint64_t(seg.offset) + uint64_t(r0) * 8u;
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm) {
+      const uint32_t r = w0 + 16u * uint32_t(mm) + 2u * G;
+      u32x4 x = u32x4{0, 0, 0, 0};
+      if (r + 2 <= hr) {
+        x = load_16_unaligned(g + uint64_t(r) * 8u);
+      } else if (r < hr) {
+        const uint64_t y = __builtin_nontemporal_load(as_global<const u64_u>(g + uint64_t(r) * 8u));
+        x = u32x4{uint32_t(y), uint32_t(y >> 32), 0, 0};
+      }
+      m[2 * mm] = x.x; m[2 * mm + 1] = x.y; m[8 + 2 * mm] = x.z; m[8 + 2 * mm + 1] = x.w;
+    }
+    m = quarters_transpose(lanes_transpose8x64(m));
+  }
+  for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {
+    if constexpr (!src_runs) {  // run lane & 7 out
+      const reshard_segment_t& seg = dst_segs[lane & 7u];
+      const uintptr_t g = sh.ptr(refs[seg.ptr + f]) + uint64_t(seg.offset) + uint64_t(r0) * 8u;
+#pragma unroll
+      for (int mm = 0; mm < 4; ++mm) {
+        const uint32_t r = w0 + 16u * uint32_t(mm) + 2u * G;
+        const u32x4 x = u32x4{m[2 * mm], m[2 * mm + 1], m[8 + 2 * mm], m[8 + 2 * mm + 1]};
+        if (r + 2 <= hr) store_bytes(g + uint64_t(r) * 8u, x, 16);
+        else if (r < hr) store_bytes(g + uint64_t(r) * 8u, x, 8);
+      }
+    } else {  // whole rows out
+      const uintptr_t g =
+          sh.ptr(refs[dst_segs[0].ptr + f]) + uint64_t(dst_segs[0].offset) + uint64_t(r0) * 64u + 16u * b;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t r = w0 + 16u * uint32_t(q) + a;
+        if (r < hr) store_bytes(g + uint64_t(r) * 64u, u32x4{m[4 * q], m[4 * q + 1], m[4 * q + 2], m[4 * q + 3]}, 16);
+      }
+    }
+  }
+}
+
+template <class Sh>
+__device__ __forceinline__ void window_runs64(const reshard_descriptor_t& D,
+                                              const reshard_segment_t* __restrict__ segs,
+                                              const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
+  const uint32_t rows = D.extent[0], per_tile = D.extent[1];  // 256 rows per tile
+  const uint32_t r0 = tile * per_tile;
+  const uint32_t hr = min(per_tile, rows - r0);
+  const reshard_segment_t* src_segs = segs + D.src_ptr;
+  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+  if (D.dst_ref_begin == 8)  // else one segment of whole rows (and eight runs out)
+    window_runs64_sides<true>(src_segs, dst_segs, refs, sh, r0, hr);
+  else
+    window_runs64_sides<false>(src_segs, dst_segs, refs, sh, r0, hr);
+}
+
 // Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
 // aligned to the descriptor's unit, or replicas differ in 16-byte phase.
 template <class Sh>
@@ -1026,6 +1155,8 @@ enum KernelKind : int {
                      // (kQuadRowsPerLane rows per lane): no LDS, fewer registers
   kKindRuns = 5,     // every descriptor a 32-byte window band of 4-byte column runs
                      // (window_runs8): no LDS
+  kKindRuns64 = 6,   // every descriptor a 64-byte window band of 8-byte column runs
+                     // (window_runs64): no LDS
   kKindAligned = 8,  // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
@@ -1059,7 +1190,8 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t unit = kKind == kKindItems16 ? 16u : unit_mode & 0xffffu;
   const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
                         : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
-                        : kKind == kKindQuadRows || kKind == kKindRuns ? uint32_t(RESHARD_DESC_WINDOW)
+                        : kKind == kKindQuadRows || kKind == kKindRuns || kKind == kKindRuns64
+                            ? uint32_t(RESHARD_DESC_WINDOW)
                                                : unit_mode >> 16;
   if constexpr (kKind == kKindQuadRows) {
     const Shards<kKarg> wsh{table, &karg, refs};
@@ -1069,6 +1201,11 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   if constexpr (kKind == kKindRuns) {
     const Shards<kKarg> wsh{table, &karg, refs};
     window_runs8(D, segs, refs, wsh, t - tile_begin[lo]);
+    return;
+  }
+  if constexpr (kKind == kKindRuns64) {
+    const Shards<kKarg> wsh{table, &karg, refs};
+    window_runs64(D, segs, refs, wsh, t - tile_begin[lo]);
     return;
   }
   if constexpr (kKind == kKindAll) {
@@ -1085,7 +1222,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
       return;
     }
   }
-  if constexpr (kKind != kKindQuadRows && kKind != kKindRuns) {
+  if constexpr (kKind != kKindQuadRows && kKind != kKindRuns && kKind != kKindRuns64) {
   const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;
   const uint32_t first = (t - tile_begin[lo]) * rs::kTileItems;
   const uint32_t last = min(first + rs::kTileItems, items);
@@ -1135,7 +1272,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
       default: copy_items<uint8_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
     }
   }
-  }  // kKind != kKindQuadRows && kKind != kKindRuns
+  }  // kKind != kKindQuadRows && kKind != kKindRuns && kKind != kKindRuns64
 }
 
 template <bool kKarg, int kVariant>
@@ -1172,6 +1309,8 @@ hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_des
       return RS_LAUNCH(kKindQuadRows);
     case kKindRuns:
       return RS_LAUNCH(kKindRuns);
+    case kKindRuns64:
+      return RS_LAUNCH(kKindRuns64);
     default:
       return RS_LAUNCH(kKindAll);
   }
@@ -1191,16 +1330,28 @@ bool runs_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_
   if (D.mode != RESHARD_DESC_WINDOW || w != 32 || D.extent[1] != kWindowBytes / w) return false;
   const reshard_segment_t* S = segs.data() + D.src_ptr;
   const reshard_segment_t* T = S + D.dst_ref_begin;
-  const bool src_runs = runs_side(S, D.dst_ref_begin, w / 4), dst_runs = runs_side(T, D.fanout, w / 4);
+  const bool src_runs = runs_side(S, D.dst_ref_begin, 8, 4), dst_runs = runs_side(T, D.fanout, 8, 4);
   return (src_runs || full_side(S, D.dst_ref_begin, w)) && (dst_runs || full_side(T, D.fanout, w)) &&
          (src_runs || dst_runs);
+}
+
+// Whether a descriptor is a band window_runs64 moves: 64 bytes wide, tiles of
+// kWindowBytes / 64 rows, one side eight 8-byte runs in column order, the
+// other one packed run of whole rows.
+bool runs64_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
+  const uint32_t w = D.run_bytes;
+  if (D.mode != RESHARD_DESC_WINDOW || w != 64 || D.extent[1] != kWindowBytes / w) return false;
+  const reshard_segment_t* S = segs.data() + D.src_ptr;
+  const reshard_segment_t* T = S + D.dst_ref_begin;
+  const bool src_runs = runs_side(S, D.dst_ref_begin, 8, 8), dst_runs = runs_side(T, D.fanout, 8, 8);
+  return (src_runs && full_side(T, D.fanout, w)) || (dst_runs && full_side(S, D.dst_ref_begin, w));
 }
 
 }  // namespace
 
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
-  bool items16 = true, chunks = true, quad_rows = true, runs = true, window = false;
+  bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, window = false;
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
     if (D.mode != RESHARD_DESC_DST_CHUNKS) chunks = false;
@@ -1208,10 +1359,11 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
         D.extent[1] != rs::kQuadRowsPerLane * uint32_t(kBlock))
       quad_rows = false;
     if (!runs_band(D, segs)) runs = false;
+    if (!runs64_band(D, segs)) runs64 = false;
     if (D.mode == RESHARD_DESC_WINDOW) window = true;
   }
   return items16 ? kKindItems16 : chunks ? kKindChunks : quad_rows ? kKindQuadRows : runs ? kKindRuns
-         : window ? kKindAll : kKindCopy;
+         : runs64 ? kKindRuns64 : window ? kKindAll : kKindCopy;
 }
 
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,

@@ -167,11 +167,21 @@ def narrow_columns(rows: int = 1 << 22) -> Workload:
 def narrow_columns_tp8(rows: int = 1 << 21) -> Workload:
     """16 bf16 columns (32-byte rows: the shape of a rank-16 low-rank factor),
     rows split over two sources, columns over eight destinations: every
-    destination row is a 2-element (4-byte) slice of a 32-byte source row, wider
-    than a register row, so the band goes through an LDS window."""
+    destination row is a 2-element (4-byte) slice of a 32-byte source row (the
+    8-lane word exchange)."""
     t = TensorSpec("narrow16", (rows, 16), torch.bfloat16, (2,), (0,), (8,), (1,))
     return Workload(f"narrow_columns_tp8_{rows}x16", (t,), "normal",
                     f"{rows}x16 bf16 N(0,0.02), (2,)[S0] -> (8,)[S1]: 2-element slices of 32-byte rows")
+
+
+def narrow_columns_64b_tp8(rows: int = 1 << 20) -> Workload:
+    """32 bf16 columns (64-byte rows: a rank-32 low-rank factor), rows split over
+    two sources, columns over eight destinations: every destination row is a
+    4-element (8-byte) slice of a 64-byte source row, moved through an LDS
+    window."""
+    t = TensorSpec("narrow32", (rows, 32), torch.bfloat16, (2,), (0,), (8,), (1,))
+    return Workload(f"narrow_columns_64b_tp8_{rows}x32", (t,), "normal",
+                    f"{rows}x32 bf16 N(0,0.02), (2,)[S0] -> (8,)[S1]: 4-element slices of 64-byte rows")
 
 
 WORKLOADS = {
@@ -182,6 +192,7 @@ WORKLOADS = {
     "ffn_refit_32_layers": ffn_refit,
     "narrow_columns_4194304x8": narrow_columns,
     "narrow_columns_tp8_2097152x16": narrow_columns_tp8,
+    "narrow_columns_64b_tp8_1048576x32": narrow_columns_64b_tp8,
     "ffn_up_f32_to_bf16_14336x4096": ffn_up_f32_to_bf16,
     "dense_layer_refit_32_layers": dense_layer_refit,
 }

@@ -47,7 +47,8 @@ def test_worked_example_golden():
 
 
 SMALL_FULL = ["worked_example_8x8", "ffn_up_14336x4096", "moe_experts_64x2048x7168", "uneven_5000x3001",
-              "narrow_columns_4194304x8", "narrow_columns_tp8_2097152x16", "ffn_up_f32_to_bf16_14336x4096"]
+              "narrow_columns_4194304x8", "narrow_columns_tp8_2097152x16", "narrow_columns_64b_tp8_1048576x32",
+              "ffn_up_f32_to_bf16_14336x4096"]
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -96,7 +97,8 @@ def test_misaligned_shard_pointers(misalign):
         [s for s in small_specs() if s.name in ("conv_f32_bf16", "conv_bf16_f32_ragged", "strips_fanout",
                                                 "strips_rep_src", "chunked_bf16", "strips_nine",
                                                 "narrow_rep", "narrow_scatter", "narrow_gather_rep", "narrow_bf16_cols",
-                                                "runs_scatter_rep", "runs_gather")]
+                                                "runs_scatter_rep", "runs_gather", "runs64_scatter_rep",
+                                                "runs64_gather")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 
