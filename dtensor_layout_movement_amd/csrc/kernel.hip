@@ -1003,6 +1003,46 @@ __device__ __forceinline__ void window_runs64(const reshard_descriptor_t& D,
     window_runs64_sides<false>(src_segs, dst_segs, refs, sh, r0, hr);
 }
 
+// A window band 32, 64, 128 or 256 bytes wide whose sides are each n packed
+// segments of one width, a multiple of 16 bytes (whole rows, or the equal
+// column shards of a split), in column order: every 16-byte chunk of a row lies
+// in one segment on each side, so the band moves as 16-byte chunks with no LDS
+// and no exchange.  Chunk f of the tile is chunk f % cpr of row f / cpr (cpr
+// chunks per row, a power of two): a wave's accesses are contiguous in every
+// packed segment, and lane L always takes chunk column L % cpr, so each lane
+// resolves its two segment addresses once.  A tile is kWindowBytes, four
+// chunks per thread.
+template <class Sh>
+__device__ __forceinline__ void window_chunks16(const reshard_descriptor_t& D,
+                                                const reshard_segment_t* __restrict__ segs,
+                                                const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
+  const uint32_t w = D.run_bytes, rows = D.extent[0], per_tile = D.extent[1];
+  const uint32_t r0 = tile * per_tile;
+  const uint32_t hr = min(per_tile, rows - r0);
+  const uint32_t shift = 31u - __clz(w >> 4);  // log2 of the chunks per row
+  const uint32_t c = threadIdx.x & ((w >> 4) - 1u);
+  const reshard_segment_t* src_segs = segs + D.src_ptr;
+  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+  const uint32_t ws = w / D.dst_ref_begin, wd = w / D.fanout;  // segment widths
+  const reshard_segment_t& ss = src_segs[16u * c / ws];
+  const reshard_segment_t& sd = dst_segs[16u * c / wd];
+  const uintptr_t gs = sh.ptr(ss.ptr) + uint64_t(ss.offset) + (16u * c - ss.col) + uint64_t(r0) * ws;
+  u32x4 v[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {  // unconditional: rows past the tile re-read its last row, never stored
+    const uint32_t r = (uint32_t(k * kBlock) + threadIdx.x) >> shift;
+    v[k] = load_16_unaligned(gs + uint64_t(min(r, hr - 1)) * ws);
+  }
+  for (uint32_t f = 0; f < sd.fanout; ++f) {
+    const uintptr_t gd = sh.ptr(refs[sd.ptr + f]) + uint64_t(sd.offset) + (16u * c - sd.col) + uint64_t(r0) * wd;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t r = (uint32_t(k * kBlock) + threadIdx.x) >> shift;
+      if (r < hr) store_bytes(gd + uint64_t(r) * wd, v[k], 16);
+    }
+  }
+}
+
 // Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
 // aligned to the descriptor's unit, or replicas differ in 16-byte phase.
 template <class Sh>
@@ -1157,6 +1197,8 @@ enum KernelKind : int {
                      // (window_runs8): no LDS
   kKindRuns64 = 6,   // every descriptor a 64-byte window band of 8-byte column runs
                      // (window_runs64): no LDS
+  kKindBands16 = 7,  // every descriptor a window band of 16-byte-aligned packed
+                     // segments (window_chunks16): no LDS
   kKindAligned = 8,  // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
@@ -1190,7 +1232,8 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t unit = kKind == kKindItems16 ? 16u : unit_mode & 0xffffu;
   const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
                         : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
-                        : kKind == kKindQuadRows || kKind == kKindRuns || kKind == kKindRuns64
+                        : kKind == kKindQuadRows || kKind == kKindRuns || kKind == kKindRuns64 ||
+                                  kKind == kKindBands16
                             ? uint32_t(RESHARD_DESC_WINDOW)
                                                : unit_mode >> 16;
   if constexpr (kKind == kKindQuadRows) {
@@ -1208,6 +1251,11 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     window_runs64(D, segs, refs, wsh, t - tile_begin[lo]);
     return;
   }
+  if constexpr (kKind == kKindBands16) {
+    const Shards<kKarg> wsh{table, &karg, refs};
+    window_chunks16(D, segs, refs, wsh, t - tile_begin[lo]);
+    return;
+  }
   if constexpr (kKind == kKindAll) {
     if (mode == RESHARD_DESC_WINDOW) {  // any alignment: global chunks follow the addresses
       __shared__ __attribute__((aligned(16))) uint8_t window[rs::kWindowBytes];
@@ -1222,7 +1270,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
       return;
     }
   }
-  if constexpr (kKind != kKindQuadRows && kKind != kKindRuns && kKind != kKindRuns64) {
+  if constexpr (kKind != kKindQuadRows && kKind != kKindRuns && kKind != kKindRuns64 && kKind != kKindBands16) {
   const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;
   const uint32_t first = (t - tile_begin[lo]) * rs::kTileItems;
   const uint32_t last = min(first + rs::kTileItems, items);
@@ -1272,7 +1320,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
       default: copy_items<uint8_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
     }
   }
-  }  // kKind != kKindQuadRows && kKind != kKindRuns && kKind != kKindRuns64
+  }  // kKind != kKindQuadRows && kKind != kKindRuns && kKind != kKindRuns64 && kKind != kKindBands16
 }
 
 template <bool kKarg, int kVariant>
@@ -1311,6 +1359,8 @@ hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_des
       return RS_LAUNCH(kKindRuns);
     case kKindRuns64:
       return RS_LAUNCH(kKindRuns64);
+    case kKindBands16:
+      return RS_LAUNCH(kKindBands16);
     default:
       return RS_LAUNCH(kKindAll);
   }
@@ -1335,6 +1385,26 @@ bool runs_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_
          (src_runs || dst_runs);
 }
 
+// Whether a descriptor is a band window_chunks16 moves: 32 to 256 bytes wide
+// (a power of two), tiles of kWindowBytes, each side n packed segments of one
+// width, a multiple of 16, in column order, with one fan-out.
+bool chunks16_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
+  const uint32_t w = D.run_bytes;
+  if (D.mode != RESHARD_DESC_WINDOW || (w != 32 && w != 64 && w != 128 && w != 256) ||
+      D.extent[1] != kWindowBytes / w)
+    return false;
+  auto side = [&](const reshard_segment_t* S, uint32_t n) {
+    if (n == 0 || w % n != 0 || (w / n) % 16 != 0) return false;
+    for (uint32_t s = 0; s < n; ++s)
+      if (S[s].width != w / n || uint64_t(S[s].row_stride) != w / n || S[s].col != s * (w / n) ||
+          S[s].fanout != S[0].fanout)
+        return false;
+    return true;
+  };
+  const reshard_segment_t* S = segs.data() + D.src_ptr;
+  return side(S, D.dst_ref_begin) && side(S + D.dst_ref_begin, D.fanout);
+}
+
 // Whether a descriptor is a band window_runs64 moves: 64 bytes wide, tiles of
 // kWindowBytes / 64 rows, one side eight 8-byte runs in column order, the
 // other one packed run of whole rows.
@@ -1351,7 +1421,7 @@ bool runs64_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
 
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
-  bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, window = false;
+  bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, bands16 = true, window = false;
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
     if (D.mode != RESHARD_DESC_DST_CHUNKS) chunks = false;
@@ -1360,10 +1430,11 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
       quad_rows = false;
     if (!runs_band(D, segs)) runs = false;
     if (!runs64_band(D, segs)) runs64 = false;
+    if (!chunks16_band(D, segs)) bands16 = false;
     if (D.mode == RESHARD_DESC_WINDOW) window = true;
   }
   return items16 ? kKindItems16 : chunks ? kKindChunks : quad_rows ? kKindQuadRows : runs ? kKindRuns
-         : runs64 ? kKindRuns64 : window ? kKindAll : kKindCopy;
+         : runs64 ? kKindRuns64 : bands16 ? kKindBands16 : window ? kKindAll : kKindCopy;
 }
 
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,

@@ -184,6 +184,15 @@ def narrow_columns_64b_tp8(rows: int = 1 << 20) -> Workload:
                     f"{rows}x32 bf16 N(0,0.02), (2,)[S0] -> (8,)[S1]: 4-element slices of 64-byte rows")
 
 
+def narrow_columns_64b_tp4(rows: int = 1 << 20) -> Workload:
+    """32 bf16 columns (64-byte rows), rows split over two sources, columns over
+    four destinations: every destination row is an 8-element (16-byte) slice of
+    a 64-byte source row, moved as 16-byte chunks."""
+    t = TensorSpec("narrow32q", (rows, 32), torch.bfloat16, (2,), (0,), (4,), (1,))
+    return Workload(f"narrow_columns_64b_tp4_{rows}x32", (t,), "normal",
+                    f"{rows}x32 bf16 N(0,0.02), (2,)[S0] -> (4,)[S1]: 8-element slices of 64-byte rows")
+
+
 WORKLOADS = {
     "worked_example_8x8": worked_example_8x8,
     "ffn_up_14336x4096": ffn_up,
@@ -193,6 +202,7 @@ WORKLOADS = {
     "narrow_columns_4194304x8": narrow_columns,
     "narrow_columns_tp8_2097152x16": narrow_columns_tp8,
     "narrow_columns_64b_tp8_1048576x32": narrow_columns_64b_tp8,
+    "narrow_columns_64b_tp4_1048576x32": narrow_columns_64b_tp4,
     "ffn_up_f32_to_bf16_14336x4096": ffn_up_f32_to_bf16,
     "dense_layer_refit_32_layers": dense_layer_refit,
 }

@@ -72,6 +72,14 @@ def small_specs():
         T("runs64_gather", (1037, 32), torch.bfloat16, (8,), (1,), (3,), (0,)),
         T("runs64_scatter_rep", (517, 16), torch.float32, (3,), (0,), (2, 8), (RR, 1)),
         T("runs64_tiny", (3, 32), torch.bfloat16, (1,), (0,), (8,), (1,)),
+        # bands of packed 16-byte-aligned segments (16-byte chunks, no LDS):
+        # 16-byte runs in 64-byte rows, 32-byte runs in 128- and 256-byte rows,
+        # gather, fan-out, ragged tails
+        T("bands16_scatter", (1043, 32), torch.bfloat16, (2,), (0,), (4,), (1,)),
+        T("bands16_gather", (1037, 64), torch.bfloat16, (4,), (1,), (3,), (0,)),
+        T("bands16_rep", (517, 32), torch.float32, (3,), (0,), (2, 8), (RR, 1)),
+        T("bands16_256", (1029, 128), torch.bfloat16, (2,), (0,), (8,), (1,)),
+        T("bands16_tiny", (2, 16), torch.float32, (1,), (0,), (2,), (1,)),
         # row mode without the quad exchange: single bf16 columns, 8-byte rows
         T("narrow_bf16_cols", (1037, 8), torch.bfloat16, (2,), (0,), (8,), (1,)),
         T("narrow_8byte_rows", (2051, 4), torch.bfloat16, (3,), (0,), (2,), (1,)),
@@ -198,9 +206,9 @@ def random_specs(seed, count, max_numel=400_000):
 
 
 def narrow_random_specs(seed, count):
-    """Seeded random 2-d layouts whose rows are at most 64 bytes and whose column
-    splits give runs of 1 to 8 bytes: the register row mode, the quad and 8-lane
-    exchanges and the LDS windows, with ragged row counts (partial groups of
+    """Seeded random 2-d layouts whose rows are at most 256 bytes and whose column
+    splits give runs of 1 to 128 bytes: the register row mode, the quad and
+    8-lane exchanges, the 16-byte chunk bands and the LDS windows, with ragged row counts (partial groups of
     four and eight rows, short last tiles), row splits on either side, replicas
     on either side and every element size."""
     rng = random.Random(seed)
@@ -208,7 +216,7 @@ def narrow_random_specs(seed, count):
     while len(out) < count:
         dtype = rng.choice([torch.uint8, torch.bfloat16, torch.float32, torch.float64])
         es = torch.tensor([], dtype=dtype).element_size()
-        width = rng.choice([b for b in (4, 8, 16, 32, 64) if b >= es])
+        width = rng.choice([b for b in (4, 8, 16, 32, 64, 128, 256) if b >= es])
         cols = width // es
         rows = rng.choice([rng.randint(1, 40), rng.randint(500, 1100), rng.randint(2000, 5000)])
         # runs the register exchanges move: four or eight 4-byte runs, eight 8-byte runs
@@ -341,7 +349,7 @@ def test_worked_example_plan():
 def test_piece_counts_of_workloads():
     counts = {"worked_example_8x8": 8, "ffn_up_14336x4096": 8, "moe_experts_64x2048x7168": 128,
               "uneven_5000x3001": 42, "ffn_refit_32_layers": 384, "narrow_columns_4194304x8": 8, "ffn_up_f32_to_bf16_14336x4096": 8,
-              "narrow_columns_tp8_2097152x16": 16, "narrow_columns_64b_tp8_1048576x32": 16,
+              "narrow_columns_tp8_2097152x16": 16, "narrow_columns_64b_tp8_1048576x32": 16, "narrow_columns_64b_tp4_1048576x32": 8,
               "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1)}
     for wl in full_workload_plans():
         with Plan(wl.tensors) as plan:
@@ -445,7 +453,8 @@ def test_row_mode_tile_rows():
     want = {"narrow_scatter": 512, "narrow_gather": 512, "narrow_f32_cols": 512, "narrow_scatter_rep": 512,
             "narrow_gather_rep": 512, "narrow_bf16_cols": 1024, "narrow_8byte_rows": 1024,
             "narrow_fp8_3d": 16384 // 32, "runs_scatter": 512, "runs_gather": 512, "runs_scatter_rep": 512,
-            "runs_f32_cols": 512, "runs64_scatter": 256, "runs64_gather": 256, "runs64_scatter_rep": 256}
+            "runs_f32_cols": 512, "runs64_scatter": 256, "runs64_gather": 256, "runs64_scatter_rep": 256,
+            "bands16_scatter": 256, "bands16_gather": 128, "bands16_rep": 128, "bands16_256": 64}
     for name, rows in want.items():
         with Plan([small[name]]) as plan:
             descs, _ = R.reshard_plan_descriptors(plan.handle)
