@@ -1043,6 +1043,134 @@ __device__ __forceinline__ void window_chunks16(const reshard_descriptor_t& D,
   }
 }
 
+// A 32-byte window band whose one side is four packed 8-byte column runs (four
+// bf16 or two fp32 columns per shard over four shards) and whose other side is
+// one packed run of whole rows.  No LDS: a tile is 512 rows, 128 per wave, and
+// every 16-byte access of a wave is contiguous on both sides.
+//  - whole-row side: slice q (0..3) of lane L = 2a + b is half b of row
+//    32 q + a of the wave's 128 (one 1 KiB piece per slice);
+//  - run side: lane L = 4g + j holds run j at rows 64 p + 2g, + 1 (piece A) and
+//    64 p + 32 + 2g, + 1 (piece B) for p = 0, 1; the sixteen lanes that hold
+//    run j cover its rows 64 p .. 64 p + 31 (or + 32 .. + 63) in one access.
+// Between the two: slices 2p and 2p + 1 (words 8p .. 8p + 7) become whole rows
+// by one exchange between lanes 1 apart (lane 2a + b: row 64 p + 32 b + a), then
+// a 4 x 4 transpose of 8-byte elements across each quad (lane offset o = 2e + b
+// holds row 64 p + 32 b + 2g + e) leaves lane j with run j at those rows, so
+// piece A is elements 0 and 2, piece B elements 1 and 3.
+template <int P, int I = 0>
+__device__ __forceinline__ u32x16 swap_halves16(u32x16 m) {
+  if constexpr (I < 4) {
+    const bool h = (threadIdx.x & 1u) != 0;
+    constexpr int A = 8 * P + I, B = 8 * P + 4 + I;
+    const uint32_t a = m[A], b = m[B];
+    const uint32_t got = lane_xor<1>(h ? a : b);
+    m[A] = h ? got : a;
+    m[B] = h ? b : got;
+    return swap_halves16<P, I + 1>(m);
+  } else {
+    return m;
+  }
+}
+// Stage X (1 or 2) of the 4 x 4 transpose of 8-byte elements k = 0..3 at words
+// 8P + 2k, 8P + 2k + 1 across the quad.
+template <int P, int X, int K = 0>
+__device__ __forceinline__ u32x16 quad_stage64(u32x16 m) {
+  if constexpr (K < 4) {
+    if constexpr ((K & X) == 0) {
+      const bool hi = (threadIdx.x & uint32_t(X)) != 0;
+      constexpr int A = 8 * P + 2 * K, B = 8 * P + 2 * (K ^ X);
+      const uint32_t lo0 = m[A], lo1 = m[A + 1], up0 = m[B], up1 = m[B + 1];
+      const uint32_t got0 = lane_xor<X>(hi ? lo0 : up0), got1 = lane_xor<X>(hi ? lo1 : up1);
+      m[A] = hi ? got0 : lo0;
+      m[A + 1] = hi ? got1 : lo1;
+      m[B] = hi ? up0 : got0;
+      m[B + 1] = hi ? up1 : got1;
+    }
+    return quad_stage64<P, X, K + 1>(m);
+  } else {
+    return m;
+  }
+}
+template <int P>
+__device__ __forceinline__ u32x16 quad_transpose64(u32x16 m) {
+  return quad_stage64<P, 2>(quad_stage64<P, 1>(m));
+}
+
+template <bool src_runs, class Sh>
+__device__ __forceinline__ void window_runs32_sides(const reshard_segment_t* __restrict__ src_segs,
+                                                    const reshard_segment_t* __restrict__ dst_segs,
+                                                    const uint32_t* __restrict__ refs, const Sh& sh,
+                                                    uint32_t r0, uint32_t hr) {
+  const uint32_t lane = threadIdx.x & 63u, w0 = (threadIdx.x >> 6) * 128u;  // the wave's first tile row
+  const uint32_t a = lane >> 1, b = lane & 1u, g = lane >> 2;
+  u32x16 m;
+  if constexpr (!src_runs) {  // whole rows in: slice q of lane 2a + b is half b of row 32q + a
+    const uintptr_t gr = sh.ptr(src_segs[0].ptr) + uint64_t(src_segs[0].offset) + uint64_t(r0) * 32u + 16u * b;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t r = w0 + 32u * uint32_t(q) + a;
+      const u32x4 x = load_16_unaligned(gr + uint64_t(min(r, hr - 1)) * 32u);  // past hr: never stored
+      m[4 * q] = x.x; m[4 * q + 1] = x.y; m[4 * q + 2] = x.z; m[4 * q + 3] = x.w;
+    }
+    m = quad_transpose64<1>(quad_transpose64<0>(swap_halves16<1>(swap_halves16<0>(m))));
+  } else {  // run lane & 3 in: pieces A and B of sets p = 0, 1
+    const reshard_segment_t& seg = src_segs[lane & 3u];
+    const uintptr_t gr = sh.ptr(seg.ptr) + uint64_t(seg.offset) + uint64_t(r0) * 8u;
+#pragma unroll
+    for (int pc = 0; pc < 4; ++pc) {  // pc = 2p + piece
+      const uint32_t r = w0 + 64u * uint32_t(pc >> 1) + 32u * uint32_t(pc & 1) + 2u * g;
+      u32x4 x = u32x4{0, 0, 0, 0};
+      if (r + 2 <= hr) {
+        x = load_16_unaligned(gr + uint64_t(r) * 8u);
+      } else if (r < hr) {
+        const uint64_t y = __builtin_nontemporal_load(as_global<const u64_u>(gr + uint64_t(r) * 8u));
+        x = u32x4{uint32_t(y), uint32_t(y >> 32), 0, 0};
+      }
+      // piece A: elements 0 and 2; piece B: elements 1 and 3 (of set p)
+      const int e0 = 8 * (pc >> 1) + 2 * (pc & 1), e1 = e0 + 4;
+      m[e0] = x.x; m[e0 + 1] = x.y; m[e1] = x.z; m[e1 + 1] = x.w;
+    }
+    m = swap_halves16<1>(swap_halves16<0>(quad_transpose64<1>(quad_transpose64<0>(m))));
+  }
+  for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {
+    if constexpr (!src_runs) {  // run lane & 3 out
+      const reshard_segment_t& seg = dst_segs[lane & 3u];
+      const uintptr_t gr = sh.ptr(refs[seg.ptr + f]) + uint64_t(seg.offset) + uint64_t(r0) * 8u;
+#pragma unroll
+      for (int pc = 0; pc < 4; ++pc) {
+        const uint32_t r = w0 + 64u * uint32_t(pc >> 1) + 32u * uint32_t(pc & 1) + 2u * g;
+        const int e0 = 8 * (pc >> 1) + 2 * (pc & 1), e1 = e0 + 4;
+        const u32x4 x = u32x4{m[e0], m[e0 + 1], m[e1], m[e1 + 1]};
+        if (r + 2 <= hr) store_bytes(gr + uint64_t(r) * 8u, x, 16);
+        else if (r < hr) store_bytes(gr + uint64_t(r) * 8u, x, 8);
+      }
+    } else {  // whole rows out
+      const uintptr_t gr =
+          sh.ptr(refs[dst_segs[0].ptr + f]) + uint64_t(dst_segs[0].offset) + uint64_t(r0) * 32u + 16u * b;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint32_t r = w0 + 32u * uint32_t(q) + a;
+        if (r < hr) store_bytes(gr + uint64_t(r) * 32u, u32x4{m[4 * q], m[4 * q + 1], m[4 * q + 2], m[4 * q + 3]}, 16);
+      }
+    }
+  }
+}
+
+template <class Sh>
+__device__ __forceinline__ void window_runs32(const reshard_descriptor_t& D,
+                                              const reshard_segment_t* __restrict__ segs,
+                                              const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
+  const uint32_t rows = D.extent[0], per_tile = D.extent[1];  // 512 rows per tile
+  const uint32_t r0 = tile * per_tile;
+  const uint32_t hr = min(per_tile, rows - r0);
+  const reshard_segment_t* src_segs = segs + D.src_ptr;
+  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+  if (D.dst_ref_begin == 4)  // else one segment of whole rows (and four runs out)
+    window_runs32_sides<true>(src_segs, dst_segs, refs, sh, r0, hr);
+  else
+    window_runs32_sides<false>(src_segs, dst_segs, refs, sh, r0, hr);
+}
+
 // Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
 // aligned to the descriptor's unit, or replicas differ in 16-byte phase.
 template <class Sh>
@@ -1199,7 +1327,9 @@ enum KernelKind : int {
                      // (window_runs64): no LDS
   kKindBands16 = 7,  // every descriptor a window band of 16-byte-aligned packed
                      // segments (window_chunks16): no LDS
-  kKindAligned = 8,  // added to kKindChunks when every shard pointer is 16-byte
+  kKindRuns32 = 8,   // every descriptor a 32-byte window band of four 8-byte column
+                     // runs (window_runs32): no LDS
+  kKindAligned = 16, // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
 
@@ -1233,7 +1363,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
                         : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
                         : kKind == kKindQuadRows || kKind == kKindRuns || kKind == kKindRuns64 ||
-                                  kKind == kKindBands16
+                                  kKind == kKindBands16 || kKind == kKindRuns32
                             ? uint32_t(RESHARD_DESC_WINDOW)
                                                : unit_mode >> 16;
   if constexpr (kKind == kKindQuadRows) {
@@ -1256,6 +1386,11 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     window_chunks16(D, segs, refs, wsh, t - tile_begin[lo]);
     return;
   }
+  if constexpr (kKind == kKindRuns32) {
+    const Shards<kKarg> wsh{table, &karg, refs};
+    window_runs32(D, segs, refs, wsh, t - tile_begin[lo]);
+    return;
+  }
   if constexpr (kKind == kKindAll) {
     if (mode == RESHARD_DESC_WINDOW) {  // any alignment: global chunks follow the addresses
       __shared__ __attribute__((aligned(16))) uint8_t window[rs::kWindowBytes];
@@ -1270,7 +1405,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
       return;
     }
   }
-  if constexpr (kKind != kKindQuadRows && kKind != kKindRuns && kKind != kKindRuns64 && kKind != kKindBands16) {
+  if constexpr (kKind == kKindItems16 || kKind == kKindChunks || kKind == kKindCopy || kKind == kKindAll) {
   const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;
   const uint32_t first = (t - tile_begin[lo]) * rs::kTileItems;
   const uint32_t last = min(first + rs::kTileItems, items);
@@ -1320,7 +1455,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
       default: copy_items<uint8_t, rs::kItemsPerThread>(D, src, sh, first, last); break;
     }
   }
-  }  // kKind != kKindQuadRows && kKind != kKindRuns && kKind != kKindRuns64 && kKind != kKindBands16
+  }  // the item, chunk, copy and all-modes builds
 }
 
 template <bool kKarg, int kVariant>
@@ -1361,6 +1496,8 @@ hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_des
       return RS_LAUNCH(kKindRuns64);
     case kKindBands16:
       return RS_LAUNCH(kKindBands16);
+    case kKindRuns32:
+      return RS_LAUNCH(kKindRuns32);
     default:
       return RS_LAUNCH(kKindAll);
   }
@@ -1405,6 +1542,18 @@ bool chunks16_band(const reshard_descriptor_t& D, const std::vector<reshard_segm
   return side(S, D.dst_ref_begin) && side(S + D.dst_ref_begin, D.fanout);
 }
 
+// Whether a descriptor is a band window_runs32 moves: 32 bytes wide, tiles of
+// kWindowBytes / 32 rows, one side four 8-byte runs in column order, the other
+// one packed run of whole rows.
+bool runs32_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
+  const uint32_t w = D.run_bytes;
+  if (D.mode != RESHARD_DESC_WINDOW || w != 32 || D.extent[1] != kWindowBytes / w) return false;
+  const reshard_segment_t* S = segs.data() + D.src_ptr;
+  const reshard_segment_t* T = S + D.dst_ref_begin;
+  const bool src_runs = runs_side(S, D.dst_ref_begin, 4, 8), dst_runs = runs_side(T, D.fanout, 4, 8);
+  return (src_runs && full_side(T, D.fanout, w)) || (dst_runs && full_side(S, D.dst_ref_begin, w));
+}
+
 // Whether a descriptor is a band window_runs64 moves: 64 bytes wide, tiles of
 // kWindowBytes / 64 rows, one side eight 8-byte runs in column order, the
 // other one packed run of whole rows.
@@ -1421,7 +1570,8 @@ bool runs64_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
 
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
-  bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, bands16 = true, window = false;
+  bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, bands16 = true, runs32 = true;
+  bool window = false;
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
     if (D.mode != RESHARD_DESC_DST_CHUNKS) chunks = false;
@@ -1431,10 +1581,11 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
     if (!runs_band(D, segs)) runs = false;
     if (!runs64_band(D, segs)) runs64 = false;
     if (!chunks16_band(D, segs)) bands16 = false;
+    if (!runs32_band(D, segs)) runs32 = false;
     if (D.mode == RESHARD_DESC_WINDOW) window = true;
   }
   return items16 ? kKindItems16 : chunks ? kKindChunks : quad_rows ? kKindQuadRows : runs ? kKindRuns
-         : runs64 ? kKindRuns64 : bands16 ? kKindBands16 : window ? kKindAll : kKindCopy;
+         : runs64 ? kKindRuns64 : bands16 ? kKindBands16 : runs32 ? kKindRuns32 : window ? kKindAll : kKindCopy;
 }
 
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,

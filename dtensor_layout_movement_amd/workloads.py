@@ -193,6 +193,15 @@ def narrow_columns_64b_tp4(rows: int = 1 << 20) -> Workload:
                     f"{rows}x32 bf16 N(0,0.02), (2,)[S0] -> (4,)[S1]: 8-element slices of 64-byte rows")
 
 
+def narrow_columns_32b_tp4(rows: int = 1 << 21) -> Workload:
+    """16 bf16 columns (32-byte rows: a rank-16 factor), rows split over two
+    sources, columns over four destinations: every destination row is a
+    4-element (8-byte) slice of a 32-byte source row (half and quad exchanges)."""
+    t = TensorSpec("narrow16q", (rows, 16), torch.bfloat16, (2,), (0,), (4,), (1,))
+    return Workload(f"narrow_columns_32b_tp4_{rows}x16", (t,), "normal",
+                    f"{rows}x16 bf16 N(0,0.02), (2,)[S0] -> (4,)[S1]: 4-element slices of 32-byte rows")
+
+
 WORKLOADS = {
     "worked_example_8x8": worked_example_8x8,
     "ffn_up_14336x4096": ffn_up,
@@ -203,6 +212,7 @@ WORKLOADS = {
     "narrow_columns_tp8_2097152x16": narrow_columns_tp8,
     "narrow_columns_64b_tp8_1048576x32": narrow_columns_64b_tp8,
     "narrow_columns_64b_tp4_1048576x32": narrow_columns_64b_tp4,
+    "narrow_columns_32b_tp4_2097152x16": narrow_columns_32b_tp4,
     "ffn_up_f32_to_bf16_14336x4096": ffn_up_f32_to_bf16,
     "dense_layer_refit_32_layers": dense_layer_refit,
 }
