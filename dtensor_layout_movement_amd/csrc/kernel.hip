@@ -1171,6 +1171,105 @@ __device__ __forceinline__ void window_runs32(const reshard_descriptor_t& D,
     window_runs32_sides<false>(src_segs, dst_segs, refs, sh, r0, hr);
 }
 
+// A 16-byte window band whose one side is eight packed 2-byte column runs (one
+// bf16 or fp16 column per shard over eight shards) and whose other side is one
+// packed run of whole rows.  No LDS: each lane holds one 16-byte row per slot
+// (row k * kBlock + lane), and an 8 x 8 transpose of halfwords across each group
+// of eight lanes leaves lane j of group G with run j at rows 8G .. 8G + 7 (16
+// contiguous bytes; the eight lanes that hold run j cover 128 contiguous bytes
+// in one access).  Transpose stages: lanes 1 apart trade halfwords (bit 0 of
+// the element index), lanes 2 and 4 apart whole words (bits 1 and 2).
+__device__ __forceinline__ u32x4 octet_transpose(u32x4 v) {
+  const bool odd = (threadIdx.x & 1u) != 0, b1 = (threadIdx.x & 2u) != 0, b2 = (threadIdx.x & 4u) != 0;
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {  // an odd lane's low halves for the even partner's high halves
+    const uint32_t got = lane_xor<1>(odd ? (w[i] & 0xffffu) : (w[i] >> 16));
+    w[i] = odd ? ((w[i] & 0xffff0000u) | got) : ((w[i] & 0xffffu) | (got << 16));
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {  // words 2p and 2p + 1 against lanes 2 apart
+    const uint32_t lo = w[2 * p], up = w[2 * p + 1];
+    const uint32_t got = lane_xor<2>(b1 ? lo : up);
+    w[2 * p] = b1 ? got : lo;
+    w[2 * p + 1] = b1 ? up : got;
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {  // words p and p + 2 against lanes 4 apart
+    const uint32_t lo = w[p], up = w[p + 2];
+    const uint32_t got = lane_xor<4>(b2 ? lo : up);
+    w[p] = b2 ? got : lo;
+    w[p + 2] = b2 ? up : got;
+  }
+  return u32x4{w[0], w[1], w[2], w[3]};
+}
+
+template <class Sh>
+__device__ __forceinline__ void window_octets(const reshard_descriptor_t& D,
+                                              const reshard_segment_t* __restrict__ segs,
+                                              const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
+  constexpr int kRows = int(rs::kQuadRowsPerLane);
+  const uint32_t rows = D.extent[0], per_tile = D.extent[1];  // kRows * kBlock rows per tile
+  const uint32_t r0 = tile * per_tile;
+  const uint32_t hr = min(per_tile, rows - r0);
+  const reshard_segment_t* src_segs = segs + D.src_ptr;
+  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+  const bool src_runs = D.dst_ref_begin == 8;  // else one segment of whole rows (and eight runs out)
+  const uint32_t j = threadIdx.x & 7u, group_row = threadIdx.x & ~7u;
+  u32x4 v[kRows];
+  if (src_runs) {  // lane j loads eight rows of run j, then the group transposes
+    const reshard_segment_t& seg = src_segs[j];
+    const uintptr_t g = sh.ptr(seg.ptr) + uint64_t(seg.offset) + uint64_t(r0) * 2u;
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) {
+      const uint32_t r = uint32_t(k * kBlock) + group_row;
+      if (r + 8 <= hr) {
+        v[k] = load_16_unaligned(g + uint64_t(r) * 2u);
+      } else {
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (uint32_t i = 0; i < 8; ++i)
+          if (r + i < hr) w[i / 2] |= uint32_t(*as_global<const u16_u>(g + uint64_t(r + i) * 2u)) << (16 * (i & 1));
+        v[k] = u32x4{w[0], w[1], w[2], w[3]};
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) v[k] = octet_transpose(v[k]);  // uniform: every lane takes part
+    for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {
+      const uintptr_t g = sh.ptr(refs[dst_segs[0].ptr + f]) + uint64_t(dst_segs[0].offset) + uint64_t(r0) * 16u;
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+        const uint32_t r = uint32_t(k * kBlock) + threadIdx.x;
+        if (r < hr) store_bytes(g + uint64_t(r) * 16u, v[k], 16);
+      }
+    }
+  } else {  // whole rows in (slots past the tile re-read its last row, never stored)
+    const uintptr_t g = sh.ptr(src_segs[0].ptr) + uint64_t(src_segs[0].offset) + uint64_t(r0) * 16u;
+#pragma unroll
+    for (int k = 0; k < kRows; ++k)
+      v[k] = load_16_unaligned(g + uint64_t(min(uint32_t(k * kBlock) + threadIdx.x, hr - 1)) * 16u);
+#pragma unroll
+    for (int k = 0; k < kRows; ++k) v[k] = octet_transpose(v[k]);
+    const reshard_segment_t& seg = dst_segs[j];
+    for (uint32_t f = 0; f < seg.fanout; ++f) {
+      const uintptr_t g2 = sh.ptr(refs[seg.ptr + f]) + uint64_t(seg.offset) + uint64_t(r0) * 2u;
+#pragma unroll
+      for (int k = 0; k < kRows; ++k) {
+        const uint32_t r = uint32_t(k * kBlock) + group_row;
+        if (r + 8 <= hr) {
+          store_bytes(g2 + uint64_t(r) * 2u, v[k], 16);
+        } else {
+          const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+          for (uint32_t i = 0; i < 8; ++i)
+            if (r + i < hr)
+              __builtin_nontemporal_store(uint16_t(w[i / 2] >> (16 * (i & 1))), as_global<u16_u>(g2 + uint64_t(r + i) * 2u));
+        }
+      }
+    }
+  }
+}
+
 // Bytewise copy of items [lo, hi) (either mode): taken when shard pointers are not
 // aligned to the descriptor's unit, or replicas differ in 16-byte phase.
 template <class Sh>
@@ -1329,6 +1428,8 @@ enum KernelKind : int {
                      // segments (window_chunks16): no LDS
   kKindRuns32 = 8,   // every descriptor a 32-byte window band of four 8-byte column
                      // runs (window_runs32): no LDS
+  kKindOctets = 9,   // every descriptor a 16-byte window band of eight 2-byte column
+                     // runs (window_octets): no LDS
   kKindAligned = 16, // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
@@ -1363,7 +1464,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
                         : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
                         : kKind == kKindQuadRows || kKind == kKindRuns || kKind == kKindRuns64 ||
-                                  kKind == kKindBands16 || kKind == kKindRuns32
+                                  kKind == kKindBands16 || kKind == kKindRuns32 || kKind == kKindOctets
                             ? uint32_t(RESHARD_DESC_WINDOW)
                                                : unit_mode >> 16;
   if constexpr (kKind == kKindQuadRows) {
@@ -1389,6 +1490,11 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   if constexpr (kKind == kKindRuns32) {
     const Shards<kKarg> wsh{table, &karg, refs};
     window_runs32(D, segs, refs, wsh, t - tile_begin[lo]);
+    return;
+  }
+  if constexpr (kKind == kKindOctets) {
+    const Shards<kKarg> wsh{table, &karg, refs};
+    window_octets(D, segs, refs, wsh, t - tile_begin[lo]);
     return;
   }
   if constexpr (kKind == kKindAll) {
@@ -1498,6 +1604,8 @@ hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_des
       return RS_LAUNCH(kKindBands16);
     case kKindRuns32:
       return RS_LAUNCH(kKindRuns32);
+    case kKindOctets:
+      return RS_LAUNCH(kKindOctets);
     default:
       return RS_LAUNCH(kKindAll);
   }
@@ -1542,6 +1650,19 @@ bool chunks16_band(const reshard_descriptor_t& D, const std::vector<reshard_segm
   return side(S, D.dst_ref_begin) && side(S + D.dst_ref_begin, D.fanout);
 }
 
+// Whether a descriptor is a band window_octets moves: 16 bytes wide, tiles of
+// kQuadRowsPerLane * kBlock rows, one side eight 2-byte runs in column order,
+// the other one packed run of whole rows.
+bool octets_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
+  const uint32_t w = D.run_bytes;
+  if (D.mode != RESHARD_DESC_WINDOW || w != 16 || D.extent[1] != rs::kQuadRowsPerLane * uint32_t(kBlock))
+    return false;
+  const reshard_segment_t* S = segs.data() + D.src_ptr;
+  const reshard_segment_t* T = S + D.dst_ref_begin;
+  const bool src_runs = runs_side(S, D.dst_ref_begin, 8, 2), dst_runs = runs_side(T, D.fanout, 8, 2);
+  return (src_runs && full_side(T, D.fanout, w)) || (dst_runs && full_side(S, D.dst_ref_begin, w));
+}
+
 // Whether a descriptor is a band window_runs32 moves: 32 bytes wide, tiles of
 // kWindowBytes / 32 rows, one side four 8-byte runs in column order, the other
 // one packed run of whole rows.
@@ -1571,6 +1692,7 @@ bool runs64_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
   bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, bands16 = true, runs32 = true;
+  bool octets = true;
   bool window = false;
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
@@ -1582,9 +1704,11 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
     if (!runs64_band(D, segs)) runs64 = false;
     if (!chunks16_band(D, segs)) bands16 = false;
     if (!runs32_band(D, segs)) runs32 = false;
+    if (!octets_band(D, segs)) octets = false;
     if (D.mode == RESHARD_DESC_WINDOW) window = true;
   }
-  return items16 ? kKindItems16 : chunks ? kKindChunks : quad_rows ? kKindQuadRows : runs ? kKindRuns
+  return items16 ? kKindItems16 : chunks ? kKindChunks : octets ? kKindOctets : quad_rows ? kKindQuadRows
+         : runs ? kKindRuns
          : runs64 ? kKindRuns64 : bands16 ? kKindBands16 : runs32 ? kKindRuns32 : window ? kKindAll : kKindCopy;
 }
 

@@ -485,7 +485,8 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
     b.d.run_bytes = uint32_t(width);
     b.d.row_items = uint32_t(pitch);
     b.d.extent[0] = uint32_t(rb - ra);
-    const bool quad = width == kRowModeBytes && (quad_side(b.src) || quad_side(b.dst));
+    const bool quad = width == kRowModeBytes && (quad_side(b.src) || quad_side(b.dst) || octet_side(b.src) ||
+                                                 octet_side(b.dst));
     b.d.extent[1] = uint32_t(width > kRowModeBytes ? window_rows
                              : int64_t(kTileThreads) * (quad ? kQuadRowsPerLane : kRowsPerLane));
     b.d.extent[2] = 1;

@@ -105,6 +105,15 @@ inline bool quad_side(const std::vector<reshard_segment_t>& segs) {
   return true;
 }
 
+// The same for eight packed 2-byte column runs (single bf16 or fp16 columns over
+// eight shards): the eight lanes of a group exchange halfwords.
+inline bool octet_side(const std::vector<reshard_segment_t>& segs) {
+  if (segs.size() != 8) return false;
+  for (const reshard_segment_t& s : segs)
+    if (s.width != 2 || s.row_stride != 2 || s.fanout != segs[0].fanout) return false;
+  return true;
+}
+
 // Elements per item of a RESHARD_DESC_CONVERT row.
 constexpr uint32_t kConvertElems = RESHARD_CONVERT_ELEMS;
 

@@ -202,6 +202,15 @@ def narrow_columns_32b_tp4(rows: int = 1 << 21) -> Workload:
                     f"{rows}x16 bf16 N(0,0.02), (2,)[S0] -> (4,)[S1]: 4-element slices of 32-byte rows")
 
 
+def narrow_columns_16b_tp8(rows: int = 1 << 22) -> Workload:
+    """8 bf16 columns (16-byte rows: a rank-8 factor), rows split over two
+    sources, columns over eight destinations: every destination row is one
+    element (2 bytes) of a 16-byte source row (halfword octet exchange)."""
+    t = TensorSpec("narrow8o", (rows, 8), torch.bfloat16, (2,), (0,), (8,), (1,))
+    return Workload(f"narrow_columns_16b_tp8_{rows}x8", (t,), "normal",
+                    f"{rows}x8 bf16 N(0,0.02), (2,)[S0] -> (8,)[S1]: single columns of 16-byte rows")
+
+
 WORKLOADS = {
     "worked_example_8x8": worked_example_8x8,
     "ffn_up_14336x4096": ffn_up,
@@ -213,6 +222,7 @@ WORKLOADS = {
     "narrow_columns_64b_tp8_1048576x32": narrow_columns_64b_tp8,
     "narrow_columns_64b_tp4_1048576x32": narrow_columns_64b_tp4,
     "narrow_columns_32b_tp4_2097152x16": narrow_columns_32b_tp4,
+    "narrow_columns_16b_tp8_4194304x8": narrow_columns_16b_tp8,
     "ffn_up_f32_to_bf16_14336x4096": ffn_up_f32_to_bf16,
     "dense_layer_refit_32_layers": dense_layer_refit,
 }

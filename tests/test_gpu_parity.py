@@ -49,6 +49,7 @@ def test_worked_example_golden():
 SMALL_FULL = ["worked_example_8x8", "ffn_up_14336x4096", "moe_experts_64x2048x7168", "uneven_5000x3001",
               "narrow_columns_4194304x8", "narrow_columns_tp8_2097152x16", "narrow_columns_64b_tp8_1048576x32",
               "narrow_columns_64b_tp4_1048576x32", "narrow_columns_32b_tp4_2097152x16",
+              "narrow_columns_16b_tp8_4194304x8",
               "ffn_up_f32_to_bf16_14336x4096"]
 
 
@@ -100,7 +101,7 @@ def test_misaligned_shard_pointers(misalign):
                                                 "narrow_rep", "narrow_scatter", "narrow_gather_rep", "narrow_bf16_cols",
                                                 "runs_scatter_rep", "runs_gather", "runs64_scatter_rep",
                                                 "runs64_gather", "bands16_rep", "bands16_gather", "runs32_scatter_rep",
-                                                "runs32_gather")]
+                                                "runs32_gather", "octets_gather", "octets_scatter_rep")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 

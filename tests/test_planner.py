@@ -85,6 +85,10 @@ def small_specs():
         T("runs32_gather", (1037, 8), torch.float32, (4,), (1,), (3,), (0,)),
         T("runs32_scatter_rep", (517, 16), torch.bfloat16, (3,), (0,), (2, 4), (RR, 1)),
         T("runs32_tiny", (3, 16), torch.bfloat16, (1,), (0,), (4,), (1,)),
+        # 16-byte rows cut into eight 2-byte column runs (halfword octet exchange)
+        T("octets_gather", (1041, 8), torch.bfloat16, (8,), (1,), (3,), (0,)),
+        T("octets_scatter_rep", (523, 8), torch.float16, (3,), (0,), (2, 8), (RR, 1)),
+        T("octets_tiny", (5, 8), torch.bfloat16, (1,), (0,), (8,), (1,)),
         # row mode without the quad exchange: single bf16 columns, 8-byte rows
         T("narrow_bf16_cols", (1037, 8), torch.bfloat16, (2,), (0,), (8,), (1,)),
         T("narrow_8byte_rows", (2051, 4), torch.bfloat16, (3,), (0,), (2,), (1,)),
@@ -355,7 +359,7 @@ def test_piece_counts_of_workloads():
     counts = {"worked_example_8x8": 8, "ffn_up_14336x4096": 8, "moe_experts_64x2048x7168": 128,
               "uneven_5000x3001": 42, "ffn_refit_32_layers": 384, "narrow_columns_4194304x8": 8, "ffn_up_f32_to_bf16_14336x4096": 8,
               "narrow_columns_tp8_2097152x16": 16, "narrow_columns_64b_tp8_1048576x32": 16, "narrow_columns_64b_tp4_1048576x32": 8,
-              "narrow_columns_32b_tp4_2097152x16": 8,
+              "narrow_columns_32b_tp4_2097152x16": 8, "narrow_columns_16b_tp8_4194304x8": 16,
               "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1)}
     for wl in full_workload_plans():
         with Plan(wl.tensors) as plan:
@@ -457,11 +461,12 @@ def test_row_mode_tile_rows():
     4-byte runs that the 8-lane exchange moves)."""
     small = {s.name: s for s in small_specs()}
     want = {"narrow_scatter": 512, "narrow_gather": 512, "narrow_f32_cols": 512, "narrow_scatter_rep": 512,
-            "narrow_gather_rep": 512, "narrow_bf16_cols": 1024, "narrow_8byte_rows": 1024,
+            "narrow_gather_rep": 512, "narrow_bf16_cols": 512, "narrow_8byte_rows": 1024,
             "narrow_fp8_3d": 16384 // 32, "runs_scatter": 512, "runs_gather": 512, "runs_scatter_rep": 512,
             "runs_f32_cols": 512, "runs64_scatter": 256, "runs64_gather": 256, "runs64_scatter_rep": 256,
             "bands16_scatter": 256, "bands16_gather": 128, "bands16_rep": 128, "bands16_256": 64,
-            "runs32_scatter": 512, "runs32_gather": 512, "runs32_scatter_rep": 512}
+            "runs32_scatter": 512, "runs32_gather": 512, "runs32_scatter_rep": 512,
+            "octets_gather": 512, "octets_scatter_rep": 512}
     for name, rows in want.items():
         with Plan([small[name]]) as plan:
             descs, _ = R.reshard_plan_descriptors(plan.handle)
