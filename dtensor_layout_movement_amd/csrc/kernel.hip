@@ -1003,15 +1003,16 @@ __device__ __forceinline__ void window_runs64(const reshard_descriptor_t& D,
     window_runs64_sides<false>(src_segs, dst_segs, refs, sh, r0, hr);
 }
 
-// A window band 32, 64, 128 or 256 bytes wide whose sides are each n packed
-// segments of one width, a multiple of 16 bytes (whole rows, or the equal
-// column shards of a split), in column order: every 16-byte chunk of a row lies
-// in one segment on each side, so the band moves as 16-byte chunks with no LDS
-// and no exchange.  Chunk f of the tile is chunk f % cpr of row f / cpr (cpr
-// chunks per row, a power of two): a wave's accesses are contiguous in every
-// packed segment, and lane L always takes chunk column L % cpr, so each lane
-// resolves its two segment addresses once.  A tile is kWindowBytes, four
-// chunks per thread.
+// A window band 32 to 256 bytes wide (a multiple of 16) whose sides are each n
+// packed segments of one width, a multiple of 16 bytes (whole rows, or the
+// equal column shards of a split), in column order: every 16-byte chunk of a
+// row lies in one segment on each side, so the band moves as 16-byte chunks
+// with no LDS and no exchange.  With cpr chunks per row, lane L < rps * cpr
+// (rps = 256 / cpr rows per step, rounded down) takes chunk column L % cpr of
+// row k * rps + L / cpr at step k: a wave's accesses are contiguous in every
+// packed segment, and each lane resolves its two segment addresses once.  A
+// tile is kWindowBytes / w rows: four steps, five when cpr is not a power of
+// two.
 template <class Sh>
 __device__ __forceinline__ void window_chunks16(const reshard_descriptor_t& D,
                                                 const reshard_segment_t* __restrict__ segs,
@@ -1019,26 +1020,27 @@ __device__ __forceinline__ void window_chunks16(const reshard_descriptor_t& D,
   const uint32_t w = D.run_bytes, rows = D.extent[0], per_tile = D.extent[1];
   const uint32_t r0 = tile * per_tile;
   const uint32_t hr = min(per_tile, rows - r0);
-  const uint32_t shift = 31u - __clz(w >> 4);  // log2 of the chunks per row
-  const uint32_t c = threadIdx.x & ((w >> 4) - 1u);
   const reshard_segment_t* src_segs = segs + D.src_ptr;
   const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+  const uint32_t cpr = w >> 4, rps = uint32_t(kBlock) / cpr;
+  const uint32_t c = threadIdx.x % cpr, q = threadIdx.x / cpr;  // q >= rps: an idle lane
   const uint32_t ws = w / D.dst_ref_begin, wd = w / D.fanout;  // segment widths
   const reshard_segment_t& ss = src_segs[16u * c / ws];
   const reshard_segment_t& sd = dst_segs[16u * c / wd];
   const uintptr_t gs = sh.ptr(ss.ptr) + uint64_t(ss.offset) + (16u * c - ss.col) + uint64_t(r0) * ws;
-  u32x4 v[4];
+  u32x4 v[5];
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {  // unconditional: rows past the tile re-read its last row, never stored
-    const uint32_t r = (uint32_t(k * kBlock) + threadIdx.x) >> shift;
-    v[k] = load_16_unaligned(gs + uint64_t(min(r, hr - 1)) * ws);
-  }
+  for (int k = 0; k < 4; ++k)  // unconditional: rows past the tile re-read its last row, never stored
+    v[k] = load_16_unaligned(gs + uint64_t(min(uint32_t(k) * rps + q, hr - 1)) * ws);
+  v[4] = u32x4{0, 0, 0, 0};
+  if (4u * rps < hr)  // uniform: a fifth step (chunks per row not a power of two)
+    v[4] = load_16_unaligned(gs + uint64_t(min(4u * rps + q, hr - 1)) * ws);
   for (uint32_t f = 0; f < sd.fanout; ++f) {
     const uintptr_t gd = sh.ptr(refs[sd.ptr + f]) + uint64_t(sd.offset) + (16u * c - sd.col) + uint64_t(r0) * wd;
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const uint32_t r = (uint32_t(k * kBlock) + threadIdx.x) >> shift;
-      if (r < hr) store_bytes(gd + uint64_t(r) * wd, v[k], 16);
+    for (int k = 0; k < 5; ++k) {
+      const uint32_t r = uint32_t(k) * rps + q;
+      if (q < rps && r < hr) store_bytes(gd + uint64_t(r) * wd, v[k], 16);
     }
   }
 }
@@ -1630,13 +1632,12 @@ bool runs_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_
          (src_runs || dst_runs);
 }
 
-// Whether a descriptor is a band window_chunks16 moves: 32 to 256 bytes wide
-// (a power of two), tiles of kWindowBytes, each side n packed segments of one
-// width, a multiple of 16, in column order, with one fan-out.
+// Whether a descriptor is a band window_chunks16 moves: 32 to 256 bytes wide (a
+// multiple of 16), tiles of kWindowBytes / w rows, each side n packed segments
+// of one width, a multiple of 16, in column order, with one fan-out.
 bool chunks16_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
   const uint32_t w = D.run_bytes;
-  if (D.mode != RESHARD_DESC_WINDOW || (w != 32 && w != 64 && w != 128 && w != 256) ||
-      D.extent[1] != kWindowBytes / w)
+  if (D.mode != RESHARD_DESC_WINDOW || w < 32 || w > 256 || w % 16 != 0 || D.extent[1] != kWindowBytes / w)
     return false;
   auto side = [&](const reshard_segment_t* S, uint32_t n) {
     if (n == 0 || w % n != 0 || (w / n) % 16 != 0) return false;

@@ -80,6 +80,10 @@ def small_specs():
         T("bands16_rep", (517, 32), torch.float32, (3,), (0,), (2, 8), (RR, 1)),
         T("bands16_256", (1029, 128), torch.bfloat16, (2,), (0,), (8,), (1,)),
         T("bands16_tiny", (2, 16), torch.float32, (1,), (0,), (2,), (1,)),
+        # chunks per row not a power of two: 96-, 48- and 80-byte rows
+        T("bands16_96", (1031, 48), torch.bfloat16, (2,), (0,), (3,), (1,)),
+        T("bands16_48_gather", (1033, 24), torch.bfloat16, (3,), (1,), (2,), (0,)),
+        T("bands16_80_rep", (517, 20), torch.float32, (1,), (0,), (2, 5), (RR, 1)),
         # 32-byte rows cut into four 8-byte column runs (half and quad exchanges)
         T("runs32_scatter", (1043, 16), torch.bfloat16, (2,), (0,), (4,), (1,)),
         T("runs32_gather", (1037, 8), torch.float32, (4,), (1,), (3,), (0,)),
@@ -225,7 +229,7 @@ def narrow_random_specs(seed, count):
     while len(out) < count:
         dtype = rng.choice([torch.uint8, torch.bfloat16, torch.float32, torch.float64])
         es = torch.tensor([], dtype=dtype).element_size()
-        width = rng.choice([b for b in (4, 8, 16, 32, 64, 128, 256) if b >= es])
+        width = rng.choice([b for b in (4, 8, 16, 32, 48, 64, 96, 128, 256) if b >= es])
         cols = width // es
         rows = rng.choice([rng.randint(1, 40), rng.randint(500, 1100), rng.randint(2000, 5000)])
         # runs the register exchanges move: four or eight 4-byte runs, eight 8-byte runs
@@ -466,7 +470,8 @@ def test_row_mode_tile_rows():
             "runs_f32_cols": 512, "runs64_scatter": 256, "runs64_gather": 256, "runs64_scatter_rep": 256,
             "bands16_scatter": 256, "bands16_gather": 128, "bands16_rep": 128, "bands16_256": 64,
             "runs32_scatter": 512, "runs32_gather": 512, "runs32_scatter_rep": 512,
-            "octets_gather": 512, "octets_scatter_rep": 512}
+            "octets_gather": 512, "octets_scatter_rep": 512, "bands16_96": 170, "bands16_48_gather": 341,
+            "bands16_80_rep": 204}
     for name, rows in want.items():
         with Plan([small[name]]) as plan:
             descs, _ = R.reshard_plan_descriptors(plan.handle)
