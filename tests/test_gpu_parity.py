@@ -102,7 +102,7 @@ def test_misaligned_shard_pointers(misalign):
                                                 "runs_scatter_rep", "runs_gather", "runs64_scatter_rep",
                                                 "runs64_gather", "bands16_rep", "bands16_gather", "runs32_scatter_rep",
                                                 "runs32_gather", "octets_gather", "octets_scatter_rep", "bands16_96",
-                                                "bands16_80_rep")]
+                                                "bands16_80_rep", "pairs_gather", "pairs_rep", "narrow_8byte_rows")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 

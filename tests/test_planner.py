@@ -93,6 +93,10 @@ def small_specs():
         T("octets_gather", (1041, 8), torch.bfloat16, (8,), (1,), (3,), (0,)),
         T("octets_scatter_rep", (523, 8), torch.float16, (3,), (0,), (2, 8), (RR, 1)),
         T("octets_tiny", (5, 8), torch.bfloat16, (1,), (0,), (8,), (1,)),
+        # 8-byte rows cut into two 4-byte column runs (register row mode)
+        T("pairs_gather", (1029, 4), torch.bfloat16, (2,), (1,), (3,), (0,)),
+        T("pairs_rep", (517, 2), torch.float32, (3,), (0,), (2, 2), (RR, 1)),
+        T("pairs_tiny", (3, 4), torch.bfloat16, (1,), (0,), (2,), (1,)),
         # row mode without the quad exchange: single bf16 columns, 8-byte rows
         T("narrow_bf16_cols", (1037, 8), torch.bfloat16, (2,), (0,), (8,), (1,)),
         T("narrow_8byte_rows", (2051, 4), torch.bfloat16, (3,), (0,), (2,), (1,)),
