@@ -107,6 +107,19 @@ def test_misaligned_shard_pointers(misalign):
         run_parity([spec], "raw", 4, misalign=misalign)
 
 
+@pytest.mark.parametrize("name", ["narrow_scatter_rep", "runs_scatter", "runs64_scatter", "runs32_scatter",
+                                  "bands16_scatter", "octets_gather"])
+def test_band_builds_with_pointer_table(name):
+    """Each register band build with its shard pointers in the device table (a
+    batch of copies of one narrow layout, more pointers than the kernel
+    arguments hold), so every lane's own pointer lookup goes through the table."""
+    spec = {s.name: s for s in small_specs()}[name]
+    per_copy = int(np.prod(spec.src_mesh)) + int(np.prod(spec.dst_mesh))
+    copies = 120 // per_copy + 1
+    st = run_parity([spec] * copies, "raw", 9)
+    assert st["n_src_ptrs"] + st["n_dst_ptrs"] > 120
+
+
 def test_batched_mixed_dtypes():
     specs = list(W.ffn_refit(2, 64, 224).tensors) + [W.uneven(77, 53).tensors[0]] + \
         [s for s in small_specs() if s.name in ("u8_odd", "i64", "five_d", "rep_src", "conv_f32_f16_ragged",
