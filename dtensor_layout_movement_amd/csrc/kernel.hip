@@ -939,6 +939,9 @@ __device__ __forceinline__ void window_runs64_sides(const reshard_segment_t* __r
   const uint32_t lane = threadIdx.x & 63u, w0 = (threadIdx.x >> 6) * 64u;  // the wave's first tile row
   const uint32_t a = lane >> 2, b = lane & 3u, G = lane >> 3;
   u32x16 m;
+  // replica 0's run address (rows in) is looked up next to the data loads
+  const reshard_segment_t& dseg = dst_segs[lane & 7u];
+  const uintptr_t gd0 = src_runs ? 0 : sh.ptr(refs[dseg.ptr]) + uint64_t(dseg.offset) + uint64_t(r0) * 8u;
   if constexpr (!src_runs) {  // whole rows in: slice q of lane 4a + b is quarter b of row 16q + a
     const uintptr_t g = sh.ptr(src_segs[0].ptr) + uint64_t(src_segs[0].offset) + uint64_t(r0) * 64u + 16u * b;
 #pragma unroll
@@ -967,8 +970,7 @@ __device__ __forceinline__ void window_runs64_sides(const reshard_segment_t* __r
   }
   for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {
     if constexpr (!src_runs) {  // run lane & 7 out
-      const reshard_segment_t& seg = dst_segs[lane & 7u];
-      const uintptr_t g = sh.ptr(refs[seg.ptr + f]) + uint64_t(seg.offset) + uint64_t(r0) * 8u;
+      const uintptr_t g = f == 0 ? gd0 : sh.ptr(refs[dseg.ptr + f]) + uint64_t(dseg.offset) + uint64_t(r0) * 8u;
 #pragma unroll
       for (int mm = 0; mm < 4; ++mm) {
         const uint32_t r = w0 + 16u * uint32_t(mm) + 2u * G;
@@ -1246,15 +1248,17 @@ __device__ __forceinline__ void window_octets(const reshard_descriptor_t& D,
       }
     }
   } else {  // whole rows in (slots past the tile re-read its last row, never stored)
+    // replica 0's run address is looked up next to the data loads, not after them
+    const reshard_segment_t& seg = dst_segs[j];
+    const uintptr_t gd0 = sh.ptr(refs[seg.ptr]) + uint64_t(seg.offset) + uint64_t(r0) * 2u;
     const uintptr_t g = sh.ptr(src_segs[0].ptr) + uint64_t(src_segs[0].offset) + uint64_t(r0) * 16u;
 #pragma unroll
     for (int k = 0; k < kRows; ++k)
       v[k] = load_16_unaligned(g + uint64_t(min(uint32_t(k * kBlock) + threadIdx.x, hr - 1)) * 16u);
 #pragma unroll
     for (int k = 0; k < kRows; ++k) v[k] = octet_transpose(v[k]);
-    const reshard_segment_t& seg = dst_segs[j];
     for (uint32_t f = 0; f < seg.fanout; ++f) {
-      const uintptr_t g2 = sh.ptr(refs[seg.ptr + f]) + uint64_t(seg.offset) + uint64_t(r0) * 2u;
+      const uintptr_t g2 = f == 0 ? gd0 : sh.ptr(refs[seg.ptr + f]) + uint64_t(seg.offset) + uint64_t(r0) * 2u;
 #pragma unroll
       for (int k = 0; k < kRows; ++k) {
         const uint32_t r = uint32_t(k * kBlock) + group_row;
