@@ -1,6 +1,6 @@
 // C ABI of the reshard library: layouts, host plans, the device descriptor
-// table, the pointer slots of large plans and execute, which is one launch of
-// the gfx950 copy kernel (kernel.hip).
+// table, the pointer slots of large plans and execute, which launches the
+// gfx950 copy kernel (kernel.hip) once per launch group of the plan.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -45,13 +45,21 @@ struct reshard_plan_s {
   std::mutex mu;
   bool uploaded = false;
   int device = -1;
-  uint32_t n_wg = 0;       // grid of one launch: rs::kXcds * per_xcd blocks (surplus ones exit)
-  uint32_t per_xcd = 0;    // blocks per XCD, a multiple of rs::kXcdGroup (0: one block per tile)
-  int kind = 0;            // kernel variant (rs::kernel_kind)
-  void* table = nullptr;  // device: descriptors | refs (absolute pointer slots) | tile_begin
-  const reshard_descriptor_t* d_descs = nullptr;
+  // One launch group: descriptors that run in one kernel variant.
+  struct Launch {
+    int kind = 0;          // kernel variant (rs::kernel_kind of the group's descriptors)
+    uint32_t n_desc = 0;
+    uint32_t n_tiles = 0;
+    uint32_t per_xcd = 0;  // blocks per XCD, a multiple of rs::kXcdGroup (0: one block per tile)
+    uint32_t n_wg = 0;     // grid: rs::kXcds * per_xcd blocks (surplus ones exit), else n_tiles
+    const reshard_descriptor_t* descs = nullptr;  // the group's descriptors in the device table
+    const uint32_t* tile_begin = nullptr;         // its first tile of each, from 0; n_desc + 1 entries
+  };
+  std::vector<Launch> launches;
+  int64_t table_bytes = 0;
+  // device: descriptors by group | refs (absolute pointer slots) | tile_begin by group | segments
+  void* table = nullptr;
   const uint32_t* d_refs = nullptr;
-  const uint32_t* d_tile_begin = nullptr;
   const reshard_segment_t* d_segs = nullptr;
   // pointer-table slots, used when the pointers do not fit in kernel arguments
   int64_t n_ptrs = 0;
@@ -66,6 +74,59 @@ struct reshard_plan_s {
 
 namespace {
 
+// A kind's descriptors get a launch of their own when their tiles fill the
+// chip at least once (256 CUs x 8 resident 256-thread workgroups, one tile
+// each); a smaller launch would leave CUs idle for its whole duration.
+constexpr uint64_t kSplitMinTiles = 2048;
+
+// Descriptors that run in one launch, in plan order, and their tiles.
+struct Group {
+  int kind = 0;
+  std::vector<uint32_t> descs;
+  uint64_t tiles = 0;
+};
+
+// The launches of one execute.  Each variant but the general one (rs::kKindAll)
+// moves only the descriptor kinds it was built for, and a plan that mixes kinds
+// would otherwise run them all in the general one, which stages windows through
+// LDS and holds more registers.  So each kind with at least kSplitMinTiles tiles
+// runs in the variant of its own kind; the others share one launch of the
+// variant that covers them.  A plan of one kind is one group in plan order.
+std::vector<Group> launch_groups(const rs::HostPlan& H) {
+  std::vector<Group> by_kind;  // in order of first appearance
+  std::vector<reshard_descriptor_t> one(1);
+  for (uint32_t i = 0; i < uint32_t(H.descs.size()); ++i) {
+    one[0] = H.descs[i];
+    const int kind = rs::kernel_kind(one, H.segs);
+    auto g = std::find_if(by_kind.begin(), by_kind.end(), [&](const Group& x) { return x.kind == kind; });
+    if (g == by_kind.end()) g = by_kind.insert(by_kind.end(), Group{kind, {}, 0});
+    g->descs.push_back(i);
+    g->tiles += H.tile_begin[i + 1] - H.tile_begin[i];
+  }
+  std::vector<Group> out;
+  Group rest;
+  for (Group& g : by_kind) {
+    if (g.tiles >= kSplitMinTiles) {
+      out.push_back(std::move(g));
+    } else {
+      rest.descs.insert(rest.descs.end(), g.descs.begin(), g.descs.end());
+      rest.tiles += g.tiles;
+    }
+  }
+  if (!rest.descs.empty()) out.push_back(std::move(rest));
+  if (out.size() == 1) {  // everything in one launch, in plan order
+    out[0].descs.resize(H.descs.size());
+    for (uint32_t i = 0; i < uint32_t(H.descs.size()); ++i) out[0].descs[i] = i;
+  }
+  for (Group& g : out) {
+    std::sort(g.descs.begin(), g.descs.end());
+    std::vector<reshard_descriptor_t> ds;
+    for (const uint32_t i : g.descs) ds.push_back(H.descs[i]);
+    g.kind = rs::kernel_kind(ds, H.segs);
+  }
+  return out;
+}
+
 reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
@@ -78,21 +139,44 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
     return RESHARD_OK;
   }
   const rs::HostPlan& H = p->host;
-  // blocks per XCD, a whole number of tile groups; 0: too few tiles to group
-  const uint64_t per_xcd_min = (H.n_tiles + rs::kXcds - 1) / rs::kXcds;
-  const uint32_t per_xcd =
-      H.n_tiles < uint64_t(rs::kXcds) * rs::kXcdGroup ? 0u
-                                              : uint32_t((per_xcd_min + rs::kXcdGroup - 1) / rs::kXcdGroup * rs::kXcdGroup);
+  const std::vector<Group> groups = launch_groups(H);
+  size_t n_tb = 0;
+  for (const Group& g : groups) n_tb += g.descs.size() + 1;
   const size_t desc_bytes = H.descs.size() * sizeof(reshard_descriptor_t);
   const size_t refs_off = align_up(desc_bytes, 256);
   const size_t tiles_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);
-  const size_t segs_off = align_up(tiles_off + H.tile_begin.size() * sizeof(uint32_t), 256);
+  const size_t segs_off = align_up(tiles_off + n_tb * sizeof(uint32_t), 256);
   const size_t total = segs_off + H.segs.size() * sizeof(reshard_segment_t);
   std::vector<uint8_t> img(total, 0);
-  if (desc_bytes) std::memcpy(img.data(), H.descs.data(), desc_bytes);
+  reshard_descriptor_t* dd = reinterpret_cast<reshard_descriptor_t*>(img.data());
+  uint32_t* tb = reinterpret_cast<uint32_t*>(img.data() + tiles_off);
+  std::vector<reshard_plan_s::Launch> launches;
+  std::vector<size_t> desc_at, tb_at;  // each group's first descriptor and tile_begin entry
+  size_t k = 0, t = 0;
+  for (const Group& g : groups) {
+    reshard_plan_s::Launch L;
+    L.kind = g.kind;
+    L.n_desc = uint32_t(g.descs.size());
+    L.n_tiles = uint32_t(g.tiles);
+    // blocks per XCD, a whole number of tile groups; 0: too few tiles to group
+    const uint64_t per_xcd_min = (g.tiles + rs::kXcds - 1) / rs::kXcds;
+    L.per_xcd = g.tiles < uint64_t(rs::kXcds) * rs::kXcdGroup
+                    ? 0u
+                    : uint32_t((per_xcd_min + rs::kXcdGroup - 1) / rs::kXcdGroup * rs::kXcdGroup);
+    L.n_wg = L.per_xcd ? L.per_xcd * rs::kXcds : L.n_tiles;
+    desc_at.push_back(k);
+    tb_at.push_back(t);
+    uint32_t first = 0;
+    for (const uint32_t i : g.descs) {
+      dd[k++] = H.descs[i];
+      tb[t++] = first;
+      first += H.tile_begin[i + 1] - H.tile_begin[i];
+    }
+    tb[t++] = first;
+    launches.push_back(L);
+  }
   uint32_t* r = reinterpret_cast<uint32_t*>(img.data() + refs_off);
   for (size_t i = 0; i < H.refs.size(); ++i) r[i] = uint32_t(H.n_src_ptrs) + H.refs[i];
-  std::memcpy(img.data() + tiles_off, H.tile_begin.data(), H.tile_begin.size() * sizeof(uint32_t));
   // window segments as planned: a source segment indexes the source pointers,
   // which come first in the pointer array; a destination segment indexes the
   // fan-out list, whose entries were made absolute above
@@ -128,13 +212,15 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
     }
   }
   p->table = table;
-  p->d_descs = reinterpret_cast<const reshard_descriptor_t*>(table);
   p->d_refs = reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + refs_off);
-  p->d_tile_begin = reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + tiles_off);
   p->d_segs = reinterpret_cast<const reshard_segment_t*>(static_cast<uint8_t*>(table) + segs_off);
-  p->per_xcd = per_xcd;
-  p->n_wg = per_xcd ? per_xcd * rs::kXcds : uint32_t(H.n_tiles);
-  p->kind = rs::kernel_kind(H.descs, H.segs);
+  for (size_t g = 0; g < launches.size(); ++g) {
+    launches[g].descs = reinterpret_cast<const reshard_descriptor_t*>(table) + desc_at[g];
+    launches[g].tile_begin =
+        reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + tiles_off) + tb_at[g];
+  }
+  p->launches = std::move(launches);
+  p->table_bytes = int64_t(total);
   p->device = dev;
   p->uploaded = true;
   return RESHARD_OK;
@@ -320,9 +406,12 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
     }
     table = reinterpret_cast<const void* const*>(static_cast<void**>(plan->d_slots) + size_t(slot) * n);
   }
-  const hipError_t le = rs::launch_copy(plan->kind, plan->n_wg, stream, plan->d_descs, uint32_t(H.descs.size()),
-                                        plan->d_tile_begin, plan->d_refs, plan->d_segs, table, karg,
-                                        uint32_t(H.n_tiles), plan->per_xcd, flags);
+  hipError_t le = hipSuccess;
+  for (const reshard_plan_s::Launch& L : plan->launches) {  // in order on one stream
+    le = rs::launch_copy(L.kind, L.n_wg, stream, L.descs, L.n_desc, L.tile_begin, plan->d_refs, plan->d_segs,
+                         table, karg, L.n_tiles, L.per_xcd, flags);
+    if (le != hipSuccess) break;
+  }
   if (slot >= 0) {
     // recorded even when a launch failed: the launches of a split plan that
     // went out before it may still read the slot
@@ -351,9 +440,13 @@ reshard_status_t reshard_plan_stats(reshard_plan_t plan, reshard_plan_stats_t* o
   out->bytes_read = H.bytes_read;
   out->bytes_written = H.bytes_written;
   out->n_descriptors = int64_t(H.descs.size());
-  out->table_bytes = int64_t(H.descs.size() * sizeof(reshard_descriptor_t) + H.refs.size() * 4 +
-                             H.tile_begin.size() * 4 + H.segs.size() * sizeof(reshard_segment_t));
-  out->n_workgroups = plan->n_wg;
+  out->table_bytes = plan->uploaded ? plan->table_bytes
+                                    : int64_t(H.descs.size() * sizeof(reshard_descriptor_t) + H.refs.size() * 4 +
+                                              H.tile_begin.size() * 4 + H.segs.size() * sizeof(reshard_segment_t));
+  for (const reshard_plan_s::Launch& L : plan->launches) {
+    out->n_workgroups += L.n_wg;
+    out->n_launches += (int64_t(L.n_wg) + rs::kMaxLaunchBlocks - 1) / rs::kMaxLaunchBlocks;
+  }
   out->plan_host_us = H.plan_host_us;
   return RESHARD_OK;
 }

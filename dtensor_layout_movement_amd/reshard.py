@@ -65,7 +65,7 @@ class ReshardError(RuntimeError):
 class PlanStats(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int64) for n in (
         "n_tensors", "n_src_ptrs", "n_dst_ptrs", "n_pieces", "n_dst_writes", "global_bytes",
-        "bytes_read", "bytes_written", "n_descriptors", "table_bytes", "n_workgroups")] + [
+        "bytes_read", "bytes_written", "n_descriptors", "table_bytes", "n_workgroups", "n_launches")] + [
         ("plan_host_us", ctypes.c_double)]
 
 

@@ -520,3 +520,71 @@ def test_graph_capture_refused_for_pointer_table_plans():
         assert e.value.status == R.ERR_INVALID_ARGUMENT and "captured" in str(e.value)
         torch.cuda.synchronize()
     run_parity(list(W.ffn_refit(16, 64, 224).tensors), "raw", 9)
+
+
+def _mixed_kind_specs():
+    """A batch that mixes descriptor kinds in amounts that each get their own
+    launch (16-byte items of a 32 MiB projection, 64-byte run bands of 64 MiB of
+    narrow columns) with small ones that share one launch (destination chunks,
+    quad row bands, a general LDS window)."""
+    small = {s.name: s for s in small_specs()}
+    return [T("mix_rows", (4096, 4096), torch.bfloat16, (4,), (0,), (2, 2), (RR, 1)),
+            W.narrow_columns_64b_tp8(1 << 20).tensors[0],
+            W.uneven(301, 257).tensors[0], small["narrow_bf16_cols"], small["wide_window"]]
+
+
+def test_mixed_kinds_one_launch_per_group():
+    """Each descriptor kind of at least 2048 tiles runs in the build made for it,
+    the rest in one shared launch: three launches here, bit-exact."""
+    st = run_parity(_mixed_kind_specs(), "raw", 12)
+    assert st["n_launches"] == 3
+    # a plan of one kind stays one launch
+    assert run_parity([_mixed_kind_specs()[1]], "raw", 13)["n_launches"] == 1
+
+
+def test_mixed_kinds_with_pointer_table():
+    """The same groups with the shard pointers in the device slot ring (small
+    copies appended to pass the kernel-argument slots): every launch of the
+    execute reads the same slot."""
+    spec = {s.name: s for s in small_specs()}["narrow_scatter_rep"]
+    specs = _mixed_kind_specs() + [spec] * 12
+    st = run_parity(specs, "raw", 14, executes=2)
+    assert st["n_src_ptrs"] + st["n_dst_ptrs"] > 120 and st["n_launches"] == 3
+
+
+def test_mixed_kinds_graph_capture_replays():
+    """A mixed plan's launches captured into one HIP graph replay correctly:
+    three replays after eager work that changes the sources and clears the
+    destinations, each checked against the oracle."""
+    from reshard_harness import oracle_dsts
+    specs = _mixed_kind_specs()
+    with Plan(specs) as plan:
+        stream = torch.cuda.Stream()
+        R.reshard_plan_upload(plan.handle, stream.cuda_stream)
+        assert plan.stats()["n_launches"] == 3
+        sboxes = [oracle_boxes(s.shape, s.src_mesh, s.src_placements) for s in specs]
+        srcs = [[p.cuda() for p in W.cut(W.make_global(s, "raw", 0, t), b)] for t, (s, b) in
+                enumerate(zip(specs, sboxes))]
+        dsts = [[torch.zeros(box_shape(b), dtype=s.dtype, device="cuda")
+                 for b in oracle_boxes(s.shape, s.dst_mesh, s.dst_placements)] for s in specs]
+        sp = R.pointer_array([x.data_ptr() for xs in srcs for x in xs])
+        dp = R.pointer_array([x.data_ptr() for xs in dsts for x in xs])
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            R.reshard_execute(plan.handle, sp, dp, stream.cuda_stream)
+        torch.cuda.synchronize()
+        for rep in range(3):
+            fresh = [W.cut(W.make_global(s, "raw", 20 + rep, t), b) for t, (s, b) in enumerate(zip(specs, sboxes))]
+            for xs, fs in zip(srcs, fresh):
+                for x, f in zip(xs, fs):
+                    x.copy_(f)
+            for xs in dsts:
+                for x in xs:
+                    x.zero_()
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            for s, xs, fs in zip(specs, dsts, fresh):
+                for got, w in zip(xs, oracle_dsts(s, fs, threads=8)):
+                    assert torch.equal(got.cpu().view(torch.uint8), w.view(torch.uint8)), (rep, s.name)

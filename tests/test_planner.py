@@ -614,7 +614,7 @@ def test_plan_stats_fields():
         st = plan.stats()
         assert st["n_src_ptrs"] == 4 and st["n_dst_ptrs"] == 4
         assert st["n_dst_writes"] == 16 and st["n_descriptors"] == 8
-        assert st["n_workgroups"] == 0  # not uploaded: no device touched
+        assert st["n_workgroups"] == 0 and st["n_launches"] == 0  # not uploaded: no device touched
         assert st["plan_host_us"] > 0
 
 
