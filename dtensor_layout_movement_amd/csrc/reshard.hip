@@ -74,9 +74,8 @@ struct reshard_plan_s {
 
 namespace {
 
-// A kind's descriptors get a launch of their own when their tiles fill the
-// chip at least once (256 CUs x 8 resident 256-thread workgroups, one tile
-// each); a smaller launch would leave CUs idle for its whole duration.
+// A band kind gets a launch of its own when its tiles fill the chip at least
+// once (256 CUs x 8 resident 256-thread workgroups, one tile each).
 constexpr uint64_t kSplitMinTiles = 2048;
 
 // Descriptors that run in one launch, in plan order, and their tiles.
@@ -84,33 +83,44 @@ struct Group {
   int kind = 0;
   std::vector<uint32_t> descs;
   uint64_t tiles = 0;
+
+  void add(uint32_t i, const rs::HostPlan& H) {
+    descs.push_back(i);
+    tiles += H.tile_begin[i + 1] - H.tile_begin[i];
+  }
 };
 
-// The launches of one execute.  Each variant but the general one (rs::kKindAll)
-// moves only the descriptor kinds it was built for, and a plan that mixes kinds
-// would otherwise run them all in the general one, which stages windows through
-// LDS and holds more registers.  So each kind with at least kSplitMinTiles tiles
-// runs in the variant of its own kind; the others share one launch of the
-// variant that covers them.  A plan of one kind is one group in plan order.
+// The launches of one execute.  Only the general build (rs::kKindAll) runs
+// item, chunk and convert descriptors together with bands, and it stages bands
+// through LDS and holds more registers, so a plan that mixes them would run
+// everything slower.  Instead the descriptors that are not bands share one
+// launch (the item, chunk or copy build already covers any mix of them), each
+// band kind with at least kSplitMinTiles tiles runs in the build made for it,
+// and the other bands share one more launch.  A plan that needs only one of
+// these launches runs its descriptors in plan order.
 std::vector<Group> launch_groups(const rs::HostPlan& H) {
-  std::vector<Group> by_kind;  // in order of first appearance
+  Group rows;                 // descriptors that are not bands
+  std::vector<Group> bands;   // bands by kind, in order of first appearance
   std::vector<reshard_descriptor_t> one(1);
   for (uint32_t i = 0; i < uint32_t(H.descs.size()); ++i) {
+    if (H.descs[i].mode != RESHARD_DESC_WINDOW) {
+      rows.add(i, H);
+      continue;
+    }
     one[0] = H.descs[i];
     const int kind = rs::kernel_kind(one, H.segs);
-    auto g = std::find_if(by_kind.begin(), by_kind.end(), [&](const Group& x) { return x.kind == kind; });
-    if (g == by_kind.end()) g = by_kind.insert(by_kind.end(), Group{kind, {}, 0});
-    g->descs.push_back(i);
-    g->tiles += H.tile_begin[i + 1] - H.tile_begin[i];
+    auto g = std::find_if(bands.begin(), bands.end(), [&](const Group& x) { return x.kind == kind; });
+    if (g == bands.end()) g = bands.insert(bands.end(), Group{kind, {}, 0});
+    g->add(i, H);
   }
   std::vector<Group> out;
+  if (!rows.descs.empty()) out.push_back(std::move(rows));
   Group rest;
-  for (Group& g : by_kind) {
+  for (Group& g : bands) {
     if (g.tiles >= kSplitMinTiles) {
       out.push_back(std::move(g));
     } else {
-      rest.descs.insert(rest.descs.end(), g.descs.begin(), g.descs.end());
-      rest.tiles += g.tiles;
+      for (const uint32_t i : g.descs) rest.add(i, H);
     }
   }
   if (!rest.descs.empty()) out.push_back(std::move(rest));

@@ -18,8 +18,8 @@
  * One process, one GPU.  Every source rank and destination rank is a separate
  * shard buffer in the HBM of the GPU that is current when the plan is first
  * executed.  The library computes the plan on the host, keeps a copy-descriptor
- * table in device memory, and runs one fused copy kernel per execute (one launch
- * per descriptor kind when a plan mixes kinds in large amounts: see n_launches).
+ * table in device memory, and runs one fused copy kernel per execute (a few launches
+ * when a plan mixes WINDOW bands with other descriptors: see n_launches).
  *
  * Layout semantics (readings the library fixes where the pages are silent):
  *   - placement codes: RESHARD_REPLICATE (-1) or k >= 0 for Shard(k);
@@ -105,10 +105,11 @@ typedef struct reshard_plan_stats {
   int64_t table_bytes;    /* size of the device-resident descriptor table (once uploaded: as
                              allocated, with padding and one tile list per launch group) */
   int64_t n_workgroups;   /* workgroups of one execute, about one per tile (0 until upload) */
-  int64_t n_launches;     /* kernel launches of one execute (0 until upload): one per launch
-                             group, where each descriptor kind of at least 2048 tiles is a group
-                             of its own and the other descriptors share one; a group of more than
-                             16,777,208 workgroups goes out as several launches of at most that many */
+  int64_t n_launches;     /* kernel launches of one execute (0 until upload): the descriptors that
+                             are not WINDOW bands share one launch group, each band kind of at
+                             least 2048 tiles is a group of its own and the other bands share
+                             one; a group of more than 16,777,208 workgroups goes out as several
+                             launches of at most that many */
   double plan_host_us;    /* host time spent planning in reshard_plan_create* */
 } reshard_plan_stats_t;
 
@@ -247,7 +248,7 @@ reshard_status_t reshard_plan_create(reshard_layout_t src, reshard_layout_t dst,
 
 /*
  * Plan n tensors that are moved together by one execute (one fused kernel launch,
- * or one per descriptor kind when large amounts of several kinds are mixed).
+ * or a few when WINDOW bands are mixed with other descriptors: see n_launches).
  * Pointer arrays of reshard_execute are then concatenated tensor-major: tensor
  * 0's ranks first, each tensor's ranks in row-major mesh order.
  */

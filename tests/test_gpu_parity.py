@@ -523,10 +523,9 @@ def test_graph_capture_refused_for_pointer_table_plans():
 
 
 def _mixed_kind_specs():
-    """A batch that mixes descriptor kinds in amounts that each get their own
-    launch (16-byte items of a 32 MiB projection, 64-byte run bands of 64 MiB of
-    narrow columns) with small ones that share one launch (destination chunks,
-    quad row bands, a general LDS window)."""
+    """A batch that mixes descriptor kinds: 16-byte items of a 32 MiB projection,
+    64-byte run bands of 64 MiB of narrow columns, destination chunks (two
+    tensors) and a small band of 2-byte column runs."""
     small = {s.name: s for s in small_specs()}
     return [T("mix_rows", (4096, 4096), torch.bfloat16, (4,), (0,), (2, 2), (RR, 1)),
             W.narrow_columns_64b_tp8(1 << 20).tensors[0],
@@ -534,12 +533,14 @@ def _mixed_kind_specs():
 
 
 def test_mixed_kinds_one_launch_per_group():
-    """Each descriptor kind of at least 2048 tiles runs in the build made for it,
-    the rest in one shared launch: three launches here, bit-exact."""
-    st = run_parity(_mixed_kind_specs(), "raw", 12)
-    assert st["n_launches"] == 3
-    # a plan of one kind stays one launch
-    assert run_parity([_mixed_kind_specs()[1]], "raw", 13)["n_launches"] == 1
+    """The descriptors that are not bands share one launch, the 64-byte run bands
+    (4096 tiles) run in their own build, the small bands share a third launch;
+    bit-exact.  Items with chunks, or one band kind alone, stay one launch."""
+    specs = _mixed_kind_specs()
+    assert run_parity(specs, "raw", 12)["n_launches"] == 3
+    assert run_parity([specs[1]], "raw", 13)["n_launches"] == 1
+    assert run_parity([specs[0], specs[2], specs[4]], "raw", 15)["n_launches"] == 1
+    assert run_parity([specs[1], specs[3]], "raw", 16)["n_launches"] == 2
 
 
 def test_mixed_kinds_with_pointer_table():
