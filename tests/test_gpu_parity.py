@@ -589,3 +589,19 @@ def test_mixed_kinds_graph_capture_replays():
             for s, xs, fs in zip(specs, dsts, fresh):
                 for got, w in zip(xs, oracle_dsts(s, fs, threads=8)):
                     assert torch.equal(got.cpu().view(torch.uint8), w.view(torch.uint8)), (rep, s.name)
+
+
+@pytest.mark.parametrize("seed", range(3))
+def test_random_mixed_launch_groups(seed):
+    """Three narrow band kinds of 4096 tiles each, drawn at random, batched with
+    seeded random layouts and small narrow ones in shuffled order: the plan
+    runs as several launch groups, and every destination is bit-exact."""
+    import random
+    rng = random.Random(seed)
+    bands = [W.narrow_columns(1 << 21), W.narrow_columns_tp8(1 << 21), W.narrow_columns_64b_tp8(1 << 20),
+             W.narrow_columns_64b_tp4(1 << 20), W.narrow_columns_32b_tp4(1 << 21), W.narrow_columns_16b_tp8(1 << 21)]
+    specs = [w.tensors[0] for w in rng.sample(bands, 3)] + random_specs(400 + seed, 4) + \
+        narrow_random_specs(500 + seed, 3)
+    rng.shuffle(specs)
+    st = run_parity(specs, "raw", 30 + seed)
+    assert st["n_launches"] >= 4  # the descriptors that are not bands, and the three band kinds
