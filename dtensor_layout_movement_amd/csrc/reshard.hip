@@ -440,6 +440,7 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
 reshard_status_t reshard_plan_stats(reshard_plan_t plan, reshard_plan_stats_t* out) {
   if (!plan || !out) return fail(RESHARD_ERR_INVALID_ARGUMENT, "NULL argument");
   const rs::HostPlan& H = plan->host;
+  std::lock_guard<std::mutex> lock(plan->mu);  // the first execute may be uploading on another thread
   std::memset(out, 0, sizeof(*out));
   out->n_tensors = H.n_tensors;
   out->n_src_ptrs = H.n_src_ptrs;

@@ -339,7 +339,8 @@ def test_gather_then_slice_two_plans_match_oracle():
 def test_execute_from_many_threads(layers):
     """One plan executed concurrently from several host threads, each on its own
     stream with its own destination buffers; with more pointers than kernel
-    arguments hold, every call goes through the shared slot ring."""
+    arguments hold, every call goes through the shared slot ring.  Plan stats
+    are read between the calls, racing the first call's upload."""
     import threading
     from reshard_harness import oracle_dsts
     specs = list(W.ffn_refit(layers, 64, 96).tensors)
@@ -360,7 +361,7 @@ def test_execute_from_many_threads(layers):
         outs = [[GuardedShards(shard_nbytes(oracle_boxes(s.shape, s.dst_mesh, s.dst_placements), s.dtype),
                                "cuda") for s in specs] for _ in range(4)]
         torch.cuda.synchronize()
-        errors = []
+        errors, seen, after = [], [], []
 
         def work(k):
             try:
@@ -368,7 +369,9 @@ def test_execute_from_many_threads(layers):
                 dst_ptrs = [p for d in outs[k] for p in d.ptrs]
                 with torch.cuda.stream(st):
                     for _ in range(5):
+                        seen.append(R.reshard_plan_stats(plan.handle)["n_launches"])  # racing the upload
                         R.reshard_execute(plan.handle, src_ptrs, dst_ptrs, st.cuda_stream)
+                        after.append(R.reshard_plan_stats(plan.handle)["n_launches"])
                 st.synchronize()
             except Exception as e:  # noqa: BLE001
                 errors.append(e)
@@ -379,6 +382,8 @@ def test_execute_from_many_threads(layers):
             th.join()
         torch.cuda.synchronize()
         assert not errors, errors
+        final = plan.stats()["n_launches"]
+        assert final >= 1 and set(after) == {final} and set(seen) <= {0, final}
         for dsts in outs:
             for t in range(len(specs)):
                 for i, w in enumerate(want[t]):
