@@ -546,6 +546,9 @@ def test_mixed_kinds_one_launch_per_group():
     assert run_parity([specs[1]], "raw", 13)["n_launches"] == 1
     assert run_parity([specs[0], specs[2], specs[4]], "raw", 15)["n_launches"] == 1
     assert run_parity([specs[1], specs[3]], "raw", 16)["n_launches"] == 2
+    # a plan smaller than one pass over the chip is split the same way
+    small = [W.ffn_up(1024, 1024).tensors[0], W.narrow_columns_64b_tp8(1 << 14).tensors[0]]
+    assert run_parity(small, "raw", 17)["n_launches"] == 2
 
 
 def test_mixed_kinds_with_pointer_table():
