@@ -74,10 +74,6 @@ struct reshard_plan_s {
 
 namespace {
 
-// A band kind gets a launch of its own when its tiles fill the chip at least
-// once (256 CUs x 8 resident 256-thread workgroups, one tile each).
-constexpr uint64_t kSplitMinTiles = 2048;
-
 // Descriptors that run in one launch, in plan order, and their tiles.
 struct Group {
   int kind = 0;
@@ -91,13 +87,13 @@ struct Group {
 };
 
 // The launches of one execute.  Only the general build (rs::kKindAll) runs
-// item, chunk and convert descriptors together with bands, and it stages bands
-// through LDS and holds more registers, so a plan that mixes them would run
-// everything slower.  Instead the descriptors that are not bands share one
-// launch (the item, chunk or copy build already covers any mix of them), each
-// band kind with at least kSplitMinTiles tiles runs in the build made for it,
-// and the other bands share one more launch.  A plan that needs only one of
-// these launches runs its descriptors in plan order.
+// item, chunk and convert descriptors together with bands, or bands of several
+// kinds together, and it stages bands through LDS and holds more registers, so
+// a plan that mixes them would run everything slower.  Instead the descriptors
+// that are not bands share one launch (the item, chunk or copy build already
+// covers any mix of them), and each band kind runs in a launch of its own
+// build; bands that no special build moves share the general one.  A plan with
+// only one of these groups runs its descriptors in plan order.
 std::vector<Group> launch_groups(const rs::HostPlan& H) {
   Group rows;                 // descriptors that are not bands
   std::vector<Group> bands;   // bands by kind, in order of first appearance
@@ -115,21 +111,8 @@ std::vector<Group> launch_groups(const rs::HostPlan& H) {
   }
   std::vector<Group> out;
   if (!rows.descs.empty()) out.push_back(std::move(rows));
-  Group rest;
-  for (Group& g : bands) {
-    if (g.tiles >= kSplitMinTiles) {
-      out.push_back(std::move(g));
-    } else {
-      for (const uint32_t i : g.descs) rest.add(i, H);
-    }
-  }
-  if (!rest.descs.empty()) out.push_back(std::move(rest));
-  if (out.size() == 1) {  // everything in one launch, in plan order
-    out[0].descs.resize(H.descs.size());
-    for (uint32_t i = 0; i < uint32_t(H.descs.size()); ++i) out[0].descs[i] = i;
-  }
+  for (Group& g : bands) out.push_back(std::move(g));
   for (Group& g : out) {
-    std::sort(g.descs.begin(), g.descs.end());
     std::vector<reshard_descriptor_t> ds;
     for (const uint32_t i : g.descs) ds.push_back(H.descs[i]);
     g.kind = rs::kernel_kind(ds, H.segs);

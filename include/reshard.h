@@ -106,10 +106,10 @@ typedef struct reshard_plan_stats {
                              allocated, with padding and one tile list per launch group) */
   int64_t n_workgroups;   /* workgroups of one execute, about one per tile (0 until upload) */
   int64_t n_launches;     /* kernel launches of one execute (0 until upload): the descriptors that
-                             are not WINDOW bands share one launch group, each band kind of at
-                             least 2048 tiles is a group of its own and the other bands share
-                             one; a group of more than 16,777,208 workgroups goes out as several
-                             launches of at most that many */
+                             are not WINDOW bands share one launch group and each kind of band
+                             (the kernel build that moves it) is a group of its own; a group of
+                             more than 16,777,208 workgroups goes out as several launches of at
+                             most that many */
   double plan_host_us;    /* host time spent planning in reshard_plan_create* */
 } reshard_plan_stats_t;
 
