@@ -269,7 +269,10 @@ reshard_status_t reshard_plan_upload(reshard_plan_t plan, void* stream);
  *   dst_ptrs[n_dst_ptrs]  device pointers to the destination shards (written)
  * Pointers are borrowed: keep the buffers alive until the stream has passed the
  * work.  NULL is allowed only for empty shards.  Sources and destinations must
- * not overlap.  One kernel launch moves every piece of every tensor; when the
+ * not overlap.  The plan's n_launches kernel launches (one unless WINDOW bands
+ * are mixed with other descriptors), back to back on `stream`, move every piece
+ * of every tensor; if one of them fails to launch, the ones before it may still
+ * run and the error is returned.  When the
  * pointer arrays exceed the kernel-argument capacity they are first copied to a
  * plan-owned device slot with one asynchronous host-to-device copy.  Device
  * faults surface at the caller's next synchronisation, as with any HIP launch.
@@ -277,7 +280,7 @@ reshard_status_t reshard_plan_upload(reshard_plan_t plan, void* stream);
  * Graph capture: an execute may be captured into a HIP graph (stream capture
  * on `stream`) when the plan was uploaded beforehand and its pointer arrays fit
  * in the kernel arguments (n_src_ptrs + n_dst_ptrs <= 120); the graph then holds
- * exactly one kernel node with the pointers given at capture time.  Otherwise a
+ * n_launches kernel nodes with the pointers given at capture time.  Otherwise a
  * capturing call records nothing and fails with RESHARD_ERR_INVALID_ARGUMENT.
  * Errors: RESHARD_ERR_INVALID_ARGUMENT, RESHARD_ERR_NULL_SHARD, RESHARD_ERR_HIP,
  * RESHARD_ERR_DEVICE_MISMATCH, RESHARD_ERR_OUT_OF_MEMORY.
