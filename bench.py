@@ -1,10 +1,17 @@
 """Benchmark of the reshard execute on one MI355X.
 
-A step is one reshard_execute of the workload's plan: one fused launch that
-reads every source byte once and writes every destination shard.  The plan
+A step is one reshard_execute of the workload's plan: the fused launch(es) that
+read every source byte once and write every destination shard.  The plan
 (boxes, replica groups, intersections, replica choice, descriptors) is built
 once per layout pair and reused for every refit; its host time is reported
 separately as ``plan_us``.
+
+The headline workload is the 32-layer FFN refit (96 tensors in one launch).
+The other configurations of the same benchmark family are measured in the same
+run and reported in ``per_config``: the pages' 8x8 worked example (parity only),
+one FFN up-projection, an MoE expert stack and the uneven fp32 nested split.
+Each row carries its own cold timing, roofline fraction, counter traffic and CPU
+baseline.
 
 Inputs are resident in HBM before timing starts.  To keep every step cold in
 the 256 MB Infinity Cache, steps rotate over several independent sets of
@@ -25,11 +32,15 @@ tensor chunks on two streams) is timed the same way as ``two_stage_gpu``, and
 the pages' hybrid refit (FFN projections by the reshard, other weights by
 gather-then-slice) as ``hybrid_gpu`` where the workload has both kinds.
 
+``cpu_baseline`` times the oracle (the pages' gather-then-slice scheme, run on
+the host) on the same input bytes the GPU consumed and checks that its output
+equals the GPU's, byte for byte.
+
 Prints one JSON line.  ``value`` = algorithmic bytes (global bytes read once +
 every destination shard written once) per second over the timed steps;
 ``roofline.achieved`` = the same bytes over the kernel's mean launch duration:
 HIP events on the launch stream around the K back-to-back launches of the timed
-region, divided by K.
+region, divided by K (one launch per step for the headline plan).
 """
 from __future__ import annotations
 
@@ -47,9 +58,13 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0  # MI355X HBM3E, decimal GB/s
 METRIC = "reshard execute GB/s (bytes read+written) and % of MI355X HBM peak; plan time us"
-DEFAULT_WORKLOAD = "ffn_up_14336x4096"
+DEFAULT_WORKLOAD = "ffn_refit_32_layers"
+# the benchmark family, in order: the worked example (parity only), one FFN
+# up-projection, an MoE expert stack, the uneven fp32 nested split, the 32-layer refit
+CONFIGS = ["worked_example_8x8", "ffn_up_14336x4096", "moe_experts_64x2048x7168", "uneven_5000x3001",
+           "ffn_refit_32_layers"]
 KERNEL_SOURCES = [os.path.join(ROOT, "dtensor_layout_movement_amd", "csrc", f)
-                  for f in ("kernel.hip", "kernel.h", "plan.h", "plan.cpp")]
+                  for f in ("kernel.hip", "kernel.h", "plan.h", "plan.cpp", "reshard.hip")]
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_NAME = "reshard_copy_kernel"
 
@@ -293,60 +308,200 @@ def hybrid(torch, wl, sets_boxes, stream, steps: int, reshard_ms: float):
         hp.close()
 
 
-def cpu_baseline(wl, budget_s: float, cores: int | None = None) -> dict:
-    """The oracle (gather-then-slice) timed on this host's cores on the same workload."""
-    import torch
+def cpu_info() -> dict:
+    """Host threads this process may use and the CPU model string."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"cores": len(os.sched_getaffinity(0)), "cpu_model": model}
+
+
+def tensor_slices(R, lay_src, lay_dst):
+    """Per tensor, its ranges in the flat source and destination buffer lists."""
+    out, i_s, i_d = [], 0, 0
+    for ls, ld in zip(lay_src, lay_dst):
+        ns, nd = R.reshard_layout_num_ranks(ls), R.reshard_layout_num_ranks(ld)
+        out.append(((i_s, i_s + ns), (i_d, i_d + nd)))
+        i_s += ns
+        i_d += nd
+    return out
+
+
+def cpu_baseline(torch, R, wl, lay_src, lay_dst, gpu_set, reps: int, single_core_tensors: int | None,
+                 algo_bytes: int) -> dict:
+    """The oracle (the pages' gather-then-slice scheme on the host) timed on this
+    host's cores over the input bytes of one GPU buffer set, tensor by tensor; its
+    output is compared byte for byte with what the GPU wrote into that set.
+    All-cores time: median of `reps` passes over every tensor.  One-core time:
+    median of `reps` passes over the first `single_core_tensors` tensors (all
+    when None).  Rates are GB/s over the reshard's algorithmic bytes of the
+    tensors timed."""
     import oracle
-    from dtensor_layout_movement_amd import workloads as W
-    cores = cores or len(os.sched_getaffinity(0))
-    secs, reps = 0.0, 0
-    algo = 0
-    prepared = []
-    for t, spec in enumerate(wl.tensors):
-        n = 1
-        for m in spec.src_mesh:
-            n *= m
-        boxes = [oracle.shard_box(list(spec.shape), list(spec.src_mesh), list(spec.src_placements), r)
-                 for r in range(n)]
-        nd = 1
-        for m in spec.dst_mesh:
-            nd *= m
-        dboxes = [oracle.shard_box(list(spec.shape), list(spec.dst_mesh), list(spec.dst_placements), r)
-                  for r in range(nd)]
-        prepared.append((spec, boxes, dboxes))
-        if len(prepared) >= 3:  # a bounded sample of a many-tensor workload
-            break
-    while reps < 1 or (secs < budget_s and reps < 50):
-        for t, (spec, boxes, dboxes) in enumerate(prepared):
-            g = W.make_global(spec, wl.values, 0, t)
-            srcs = W.cut(g, boxes)
-            dsts = [torch.empty([max(0, h - l) for l, h in zip(lo, hi)], dtype=spec.dtype)
-                    for lo, hi in dboxes]
-            es = g.element_size()
+    info = cpu_info()
+    src_bufs, dst_bufs, _, _ = gpu_set
+    spans = tensor_slices(R, lay_src, lay_dst)
+    one_n = len(wl.tensors) if single_core_tensors is None else min(single_core_tensors, len(wl.tensors))
+    all_s, one_s = [], []
+    matches = True
+    algo_one = 0
+    for rep in range(reps):
+        t_all = t_one = 0.0
+        for t, spec in enumerate(wl.tensors):
+            (s0, s1), (d0, d1) = spans[t]
+            srcs = [b.cpu().contiguous() if b is not None else None for b in src_bufs[s0:s1]]
+            es = torch.empty((), dtype=spec.dtype).element_size()
+            dsts = [torch.empty(b.shape, dtype=spec.dtype) if b is not None else None for b in dst_bufs[d0:d1]]
+            args = (list(spec.shape), es, list(spec.src_mesh), list(spec.src_placements),
+                    [x if x is not None and x.numel() else None for x in srcs], list(spec.dst_mesh),
+                    list(spec.dst_placements), [x if x is not None and x.numel() else None for x in dsts])
             t0 = time.perf_counter()
-            oracle.reshard(list(spec.shape), es, list(spec.src_mesh), list(spec.src_placements), srcs,
-                           list(spec.dst_mesh), list(spec.dst_placements),
-                           [d if d.numel() else None for d in dsts], threads=cores)
-            secs += time.perf_counter() - t0
-            algo += g.numel() * es + sum(d.numel() for d in dsts) * es
-        reps += 1
-    names = ", ".join(p[0].name for p in prepared)
-    return {"value": round(algo / secs / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
-            "sample": f"{reps} x gather-then-slice of [{names}] from {wl.name} (replica and coverage "
-                      f"checks on), {secs:.2f} s timed, GB/s over the reshard's algorithmic bytes"}
+            oracle.reshard(*args, threads=info["cores"])
+            t_all += time.perf_counter() - t0
+            if t < one_n:
+                t0 = time.perf_counter()
+                oracle.reshard(*args, threads=1)
+                t_one += time.perf_counter() - t0
+                if rep == 0:
+                    algo_one += sum(x.numel() for x in srcs if x is not None) // max(1, _src_replicas(spec)) * es
+                    algo_one += sum(x.numel() for x in dsts if x is not None) * es
+            if rep == 0:  # the GPU's bytes of this set
+                for g, c in zip(dst_bufs[d0:d1], dsts):
+                    if g is not None and not torch.equal(g.cpu().view(torch.uint8), c.view(torch.uint8)):
+                        matches = False
+            del srcs, dsts
+        all_s.append(t_all)
+        one_s.append(t_one)
+    t_all, t_one = statistics.median(all_s), statistics.median(one_s)
+    names = wl.name if one_n == len(wl.tensors) else f"the first {one_n} of {len(wl.tensors)} tensors of {wl.name}"
+    return {"value": round(algo_bytes / t_all / 1e9, 3), "unit": "GB/s", "cores": info["cores"], "kind": "oracle",
+            "cpu_model": info["cpu_model"], "seconds_all_cores": round(t_all, 6),
+            "single_core_value": round(algo_one / t_one / 1e9, 3), "seconds_single_core": round(t_one, 6),
+            "matches_gpu": matches,
+            "sample": f"gather-then-slice of every tensor of {wl.name} (replica and coverage checks on), median of "
+                      f"{reps} pass(es) on {info['cores']} threads; single core: {names}, median of {reps}; "
+                      f"GB/s over the reshard's algorithmic bytes"}
+
+
+def _src_replicas(spec) -> int:
+    """Replicas of each source box (product of the Replicate mesh sizes)."""
+    n = 1
+    for m, p in zip(spec.src_mesh, spec.src_placements):
+        if p < 0:
+            n *= m
+    return n
+
+
+def steps_for(algo_bytes: int) -> int:
+    """Timed steps of a per-config row: about 1e11 bytes, between 50 and 1000."""
+    return max(50, min(1000, int(1e11 // max(1, algo_bytes))))
+
+
+def measure(torch, R, wl, dev, stream, steps: int, warmup: int, min_footprint_gb: float):
+    """Plan, allocate rotating buffer sets and time `steps` cold executes.
+    Returns (row dict, plan, layouts, sets)."""
+    plan, lay_src, lay_dst = build_plan(R, wl)
+    R.reshard_plan_upload(plan, stream.cuda_stream)
+    st = R.reshard_plan_stats(plan)
+    algo = st["bytes_read"] + st["bytes_written"]
+    n_sets = max(1, min(16, int(-(-min_footprint_gb * 1e9 // algo))))
+    sets = [alloc_set(torch, R, wl, lay_src, lay_dst, dev, seed=s) for s in range(n_sets)]
+    torch.cuda.synchronize()
+    for i in range(warmup):
+        _, _, sp, dp = sets[i % n_sets]
+        R.reshard_execute(plan, sp, dp, stream.cuda_stream)
+    torch.cuda.synchronize()
+    t_begin, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    t_begin.record(stream)
+    for i in range(steps):
+        _, _, sp, dp = sets[i % n_sets]
+        R.reshard_execute(plan, sp, dp, stream.cuda_stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms = t_begin.elapsed_time(t_end) / steps
+    gbps = algo / (ms * 1e-3) / 1e9
+    st = R.reshard_plan_stats(plan)
+    row = {
+        "workload": wl.name, "tensors": len(wl.tensors), "bytes_read": st["bytes_read"],
+        "bytes_written": st["bytes_written"], "algorithmic_bytes": algo, "pieces": st["n_pieces"],
+        "descriptors": st["n_descriptors"], "grid_workgroups": st["n_workgroups"],
+        "launches_per_step": st["n_launches"], "steps": steps, "buffer_sets_rotated": n_sets,
+        "ms_per_step": round(ms, 5), "gbps": round(gbps, 2), "frac": round(gbps / HBM_PEAK_GBPS, 4),
+        # one launch per step: the mean launch duration on the launch stream;
+        # several: the step time of all of them, gaps included
+        ("kernel_mean_us" if st["n_launches"] == 1 else "step_us_all_launches"): round(ms * 1e3, 3),
+        "traffic": traffic_from_profile(wl.name), "wall_s": round(wall, 4), "plan_host_us": st["plan_host_us"],
+    }
+    return row, plan, lay_src, lay_dst, sets
+
+
+def release(R, plan, lay_src, lay_dst):
+    R.reshard_plan_destroy(plan)
+    for h in lay_src + lay_dst:
+        R.reshard_layout_destroy(h)
+
+
+def worked_example_row(torch, R, dev, stream, reps: int) -> dict:
+    """The pages' 8x8 example: parity only.  Destination c must hold
+    v[i][2c + k] = 8 i + 2 c + k (the example's closed form for v[i][j] = 8 i + j),
+    and the oracle must produce the same bytes."""
+    from dtensor_layout_movement_amd import workloads as W
+    wl = W.worked_example_8x8()
+    row, plan, lay_src, lay_dst, sets = measure(torch, R, wl, dev, stream, 5, 1, 0.0)
+    _, dst_bufs, _, _ = sets[0]
+    closed = all(torch.equal(d.cpu().float(), torch.tensor([[8 * i + 2 * c + k for k in range(2)]
+                                                             for i in range(8)], dtype=torch.float32))
+                 for c, d in enumerate(dst_bufs))
+    cpu = cpu_baseline(torch, R, wl, lay_src, lay_dst, sets[0], reps, None, row["algorithmic_bytes"])
+    release(R, plan, lay_src, lay_dst)
+    return {"workload": wl.name, "parity": "bit-exact" if closed and cpu["matches_gpu"] else "MISMATCH",
+            "closed_form": closed, "launches_per_step": row["launches_per_step"], "cpu_baseline": cpu}
+
+
+def config_row(torch, R, name, dev, stream, min_footprint_gb: float, cpu: bool) -> dict:
+    """One configuration of the benchmark family, measured cold like the headline."""
+    from dtensor_layout_movement_amd import workloads as W
+    wl = W.WORKLOADS[name]()
+    plan, lay_src, lay_dst = build_plan(R, wl)
+    st = R.reshard_plan_stats(plan)
+    release(R, plan, lay_src, lay_dst)
+    steps = steps_for(st["bytes_read"] + st["bytes_written"])
+    row, plan, lay_src, lay_dst, sets = measure(torch, R, wl, dev, stream, steps, 10, min_footprint_gb)
+    ref = contiguous_reference(torch, R, st, dev, stream, max(20, steps // 4), min_footprint_gb)
+    if ref:
+        row["contiguous_same_bytes_gbps"] = ref["gbps"]
+    if cpu:
+        _, _, sp, dp = sets[0]
+        R.reshard_execute(plan, sp, dp, stream.cuda_stream)
+        torch.cuda.synchronize()
+        row["cpu_baseline"] = cpu_baseline(torch, R, wl, lay_src, lay_dst, sets[0], 3, None,
+                                           row["algorithmic_bytes"])
+        row["parity"] = "bit-exact" if row["cpu_baseline"]["matches_gpu"] else "MISMATCH"
+    release(R, plan, lay_src, lay_dst)
+    del sets
+    torch.cuda.empty_cache()
+    return row
 
 
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=400)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
     ap.add_argument("--min-footprint-gb", type=float, default=2.0)
-    ap.add_argument("--cpu-budget-s", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-comparator", action="store_true",
-                    help="skip the gather-then-slice comparator run on the GPU")
+                    help="skip the gather-then-slice, two-stage, hybrid and contiguous comparators")
+    ap.add_argument("--no-per-config", action="store_true",
+                    help="measure only --workload (profiling runs)")
     ap.add_argument("--plan-reps", type=int, default=200)
     args = ap.parse_args()
 
@@ -365,39 +520,19 @@ def main() -> int:
         return 1
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    wl = W.WORKLOADS[args.workload]()
-
-    plan, lay_src, lay_dst = build_plan(R, wl)
     stream = torch.cuda.current_stream()
-    R.reshard_plan_upload(plan, stream.cuda_stream)
+    wl = W.WORKLOADS[args.workload]()
+    print(f"[bench] {wl.name}: {len(wl.tensors)} tensors", file=sys.stderr, flush=True)
+
+    head, plan, lay_src, lay_dst, sets = measure(torch, R, wl, dev, stream, args.steps, args.warmup,
+                                                 args.min_footprint_gb)
     st = R.reshard_plan_stats(plan)
-    algo_bytes = st["bytes_read"] + st["bytes_written"]
-    n_sets = max(1, min(16, int(-(-args.min_footprint_gb * 1e9 // algo_bytes))))
-    sets = [alloc_set(torch, R, wl, lay_src, lay_dst, dev, seed=s) for s in range(n_sets)]
-    torch.cuda.synchronize()
-
-    for i in range(args.warmup):
-        _, _, sp, dp = sets[i % n_sets]
-        R.reshard_execute(plan, sp, dp, stream.cuda_stream)
-    torch.cuda.synchronize()
-
+    algo_bytes = head["algorithmic_bytes"]
+    n_sets = head["buffer_sets_rotated"]
+    ms_per_step = head["ms_per_step"]
     K = args.steps
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t_begin.record(stream)
-    for i in range(K):
-        _, _, sp, dp = sets[i % n_sets]
-        R.reshard_execute(plan, sp, dp, stream.cuda_stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    total_ms = t_begin.elapsed_time(t_end)
-    ms_per_step = total_ms / K          # one launch per step: the mean launch duration,
-    kernel_ms = ms_per_step             # back to back on the launch stream
-    value = algo_bytes / (ms_per_step * 1e-3) / 1e9
-    achieved = algo_bytes / (kernel_ms * 1e-3) / 1e9
+    value = head["gbps"]
+    achieved = value  # one launch per step (the headline plan): mean launch = step time
 
     # outside the timed region: per-launch event distribution, and warm steps on
     # one buffer set (inputs partly cache-resident)
@@ -421,46 +556,24 @@ def main() -> int:
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / n_dist
 
-    # context: a plain device copy moving the same number of bytes (read + write)
-    half = algo_bytes // 2
-    a = torch.empty(half, dtype=torch.uint8, device=dev)
-    b = torch.empty(half, dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        b.copy_(a)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(20):
-        b.copy_(a)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * half / (c0.elapsed_time(c1) / 20 * 1e-3) / 1e9
-    del a, b
-
-    reference = None
+    reference = comparator = two = mixed = None
     if not args.no_comparator:
+        print("[bench] comparators", file=sys.stderr, flush=True)
         reference = contiguous_reference(torch, R, st, dev, stream, max(5, K // 4), args.min_footprint_gb)
         if reference:
             reference["workload_vs_reference"] = round(value / reference["gbps"], 4)
-    comparator = None
-    if not args.no_comparator:
-        comparator = gather_then_slice(torch, R, wl, lay_src, lay_dst, sets, stream,
-                                       max(5, K // 4), ms_per_step)
-    two = mixed = None
-    if not args.no_comparator:
+        comparator = gather_then_slice(torch, R, wl, lay_src, lay_dst, sets, stream, max(5, K // 4), ms_per_step)
         per_tensor = []
         for src_bufs, dst_bufs, _, _ in sets:
-            sp, dp, i_s, i_d = [], [], 0, 0
-            for t in range(len(wl.tensors)):
-                ns, nd = R.reshard_layout_num_ranks(lay_src[t]), R.reshard_layout_num_ranks(lay_dst[t])
-                sp.append([b.data_ptr() if b is not None else 0 for b in src_bufs[i_s:i_s + ns]])
-                dp.append([b.data_ptr() if b is not None else 0 for b in dst_bufs[i_d:i_d + nd]])
-                i_s += ns
-                i_d += nd
+            sp, dp = [], []
+            for (s0, s1), (d0, d1) in tensor_slices(R, lay_src, lay_dst):
+                sp.append([b.data_ptr() if b is not None else 0 for b in src_bufs[s0:s1]])
+                dp.append([b.data_ptr() if b is not None else 0 for b in dst_bufs[d0:d1]])
             per_tensor.append((sp, dp))
         two = two_stage(torch, wl, per_tensor, max(5, K // 4), ms_per_step)
         mixed = hybrid(torch, wl, per_tensor, stream, max(5, K // 4), ms_per_step)
+        torch.cuda.empty_cache()
     plan_us = plan_timing(R, wl, args.plan_reps if algo_bytes < 2e10 else max(5, args.plan_reps // 20))
-    traffic = traffic_from_profile(wl.name)
     spec0 = wl.tensors[0]
     out = {
         "metric": METRIC,
@@ -486,6 +599,7 @@ def main() -> int:
             "pieces": st["n_pieces"],
             "descriptors": st["n_descriptors"],
             "grid_workgroups": st["n_workgroups"],
+            "launches_per_step": st["n_launches"],
             "buffer_sets_rotated": n_sets,
             "pct_of_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         },
@@ -496,30 +610,49 @@ def main() -> int:
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
+            "traffic": head["traffic"],
             "kernel": KERNEL_NAME,
-            "kernel_mean_us": round(kernel_ms * 1e3, 3),
+            ("kernel_mean_us" if st["n_launches"] == 1 else "step_us_all_launches"): round(ms_per_step * 1e3, 3),
         },
         "launch_us_cold": {"p10": round(per_launch[len(per_launch) // 10], 2),
                            "p50": round(per_launch[len(per_launch) // 2], 2),
                            "p90": round(per_launch[(9 * len(per_launch)) // 10], 2), "n": n_dist},
         "warm_same_buffers_gbps": round(algo_bytes / (warm_ms * 1e-3) / 1e9, 1),
-        "copy_reference_gbps": round(copy_gbps, 1),
         "contiguous_same_bytes": reference,
         "gather_then_slice_gpu": comparator,
         "two_stage_gpu": two,
         "hybrid_gpu": mixed,
-        "wall_s": round(wall, 4),
+        "wall_s": head["wall_s"],
     }
     if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(wl, args.cpu_budget_s)
-        one = cpu_baseline(wl, min(5.0, args.cpu_budget_s), cores=1)
-        out["cpu_baseline"]["single_core_value"] = one["value"]
-    print(json.dumps(out), flush=True)
+        print("[bench] cpu baseline", file=sys.stderr, flush=True)
+        R.reshard_execute(plan, sp0, dp0, stream.cuda_stream)
+        torch.cuda.synchronize()
+        many = len(wl.tensors) > 3
+        out["cpu_baseline"] = cpu_baseline(torch, R, wl, lay_src, lay_dst, sets[0], 1 if many else 3,
+                                           12 if many else None, algo_bytes)
+    release(R, plan, lay_src, lay_dst)
+    del sets
+    torch.cuda.empty_cache()
 
-    R.reshard_plan_destroy(plan)
-    for h in lay_src + lay_dst:
-        R.reshard_layout_destroy(h)
+    if not args.no_per_config:
+        rows = {}
+        for i, name in enumerate(CONFIGS):
+            if name == wl.name:
+                rows[name] = {"config_index": i, "headline": True}
+                continue
+            print(f"[bench] per-config {name}", file=sys.stderr, flush=True)
+            try:
+                if name == "worked_example_8x8":
+                    row = worked_example_row(torch, R, dev, stream, 3)
+                else:
+                    row = config_row(torch, R, name, dev, stream, args.min_footprint_gb, not args.no_cpu_baseline)
+            except Exception as e:  # a failing row is reported, not fatal to the headline
+                row = {"error": f"{type(e).__name__}: {e}"}
+            row["config_index"] = i
+            rows[name] = row
+        out["per_config"] = rows
+    print(json.dumps(out), flush=True)
     return 0
 
 

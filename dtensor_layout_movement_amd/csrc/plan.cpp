@@ -759,6 +759,7 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
     }
     P->tile_begin.push_back(uint32_t(P->n_tiles));
   }
+  P->src_load = std::move(load);
   auto t1 = std::chrono::steady_clock::now();
   P->plan_host_us = std::chrono::duration<double, std::micro>(t1 - t0).count();
   return RESHARD_OK;

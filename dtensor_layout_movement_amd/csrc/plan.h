@@ -131,6 +131,7 @@ struct HostPlan {
   std::vector<int64_t> src_base, dst_base;  // first pointer-array slot of each tensor
   int64_t n_src_ptrs = 0, n_dst_ptrs = 0;
   std::vector<uint8_t> src_needed, dst_needed;  // 1 if that pointer slot holds a non-empty shard
+  std::vector<int64_t> src_load;                // bytes read from each source pointer slot
   std::vector<Group> src_groups, dst_groups;
   std::vector<Piece> pieces;
   std::vector<reshard_descriptor_t> descs;

@@ -445,6 +445,16 @@ reshard_status_t reshard_plan_stats(reshard_plan_t plan, reshard_plan_stats_t* o
   return RESHARD_OK;
 }
 
+reshard_status_t reshard_plan_src_load(reshard_plan_t plan, int64_t capacity, int64_t* bytes,
+                                       int64_t* n_total) {
+  if (!plan || !n_total || capacity < 0 || (capacity > 0 && !bytes))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "bad argument");
+  const rs::HostPlan& H = plan->host;
+  *n_total = H.n_src_ptrs;
+  for (int64_t i = 0; i < std::min<int64_t>(capacity, H.n_src_ptrs); ++i) bytes[i] = H.src_load[size_t(i)];
+  return RESHARD_OK;
+}
+
 reshard_status_t reshard_plan_pieces(reshard_plan_t plan, int64_t capacity, reshard_piece_t* out,
                                      int64_t* n_total) {
   if (!plan || !n_total || capacity < 0 || (capacity > 0 && !out))

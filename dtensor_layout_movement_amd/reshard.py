@@ -50,7 +50,7 @@ EXPORTED = (
     "reshard_dtype_size", "reshard_layout_create", "reshard_layout_destroy",
     "reshard_layout_num_ranks", "reshard_layout_shard_box", "reshard_plan_create",
     "reshard_plan_create_batched", "reshard_plan_upload", "reshard_execute",
-    "reshard_plan_stats", "reshard_plan_pieces", "reshard_plan_piece_fanout",
+    "reshard_plan_stats", "reshard_plan_src_load", "reshard_plan_pieces", "reshard_plan_piece_fanout",
     "reshard_plan_descriptors", "reshard_plan_segments", "reshard_plan_destroy",
     "reshard_last_error",
 )
@@ -129,6 +129,7 @@ def _load() -> ctypes.CDLL:
         "reshard_plan_upload": (st, [_VP, _VP]),
         "reshard_execute": (st, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _VP]),
         "reshard_plan_stats": (st, [_VP, ctypes.POINTER(PlanStats)]),
+        "reshard_plan_src_load": (st, [_VP, _I64, _I64P, _I64P]),
         "reshard_plan_pieces": (st, [_VP, _I64, ctypes.POINTER(Piece), _I64P]),
         "reshard_plan_piece_fanout": (st, [_VP, _I64, _I64, _I64P, _I64P]),
         "reshard_plan_descriptors": (st, [_VP, _I64, ctypes.POINTER(Descriptor), _I64P, _I64,
@@ -238,6 +239,15 @@ def reshard_plan_stats(plan: int) -> dict:
     out = PlanStats()
     _check(_load().reshard_plan_stats(plan, ctypes.byref(out)))
     return {name: getattr(out, name) for name, _ in PlanStats._fields_}
+
+
+def reshard_plan_src_load(plan: int) -> list[int]:
+    """Bytes read from each source pointer slot by one execute (src_ptrs order)."""
+    n = ctypes.c_int64()
+    _check(_load().reshard_plan_src_load(plan, 0, None, ctypes.byref(n)))
+    arr = (ctypes.c_int64 * max(1, n.value))()
+    _check(_load().reshard_plan_src_load(plan, n.value, arr, ctypes.byref(n)))
+    return list(arr[:n.value])
 
 
 def reshard_plan_pieces(plan: int) -> list[dict]:

@@ -24,40 +24,14 @@ from __future__ import annotations
 from . import reshard as R
 
 
-def _coords(rank, mesh):
-    out = []
-    for m in reversed(mesh):
-        out.append(rank % m)
-        rank //= m
-    return list(reversed(out))
-
-
-def _rank(coords, mesh):
-    r = 0
-    for c, m in zip(coords, mesh):
-        r = r * m + c
-    return r
-
-
 def stage1_layout(mesh, placements):
-    """(mesh, placements, map) of the stage-1 layout; map[r1] = destination rank
-    whose box contains stage-1 rank r1's slice."""
+    """(mesh, placements) of the stage-1 layout: the destination's non-Replicate
+    mesh dims in order, then its Replicate dims turned into Shard(0)."""
     non = [i for i, p in enumerate(placements) if p != R.REPLICATE]
     rep = [i for i, p in enumerate(placements) if p == R.REPLICATE]
     mesh1 = [mesh[i] for i in non] + [mesh[i] for i in rep]
     pl1 = [placements[i] for i in non] + [0] * len(rep)
-    n = 1
-    for m in mesh1:
-        n *= m
-    order = non + rep
-    rank_map = []
-    for r1 in range(n):
-        c1 = _coords(r1, mesh1)
-        cd = [0] * len(mesh)
-        for j, i in enumerate(order):
-            cd[i] = c1[j]
-        rank_map.append(_rank(cd, mesh))
-    return tuple(mesh1), tuple(pl1), rank_map
+    return tuple(mesh1), tuple(pl1)
 
 
 class TwoStagePlan:
@@ -73,11 +47,11 @@ class TwoStagePlan:
         chunks = max(1, min(chunks, n))
         self.bounds = [n * c // chunks for c in range(chunks + 1)]
         self._layouts = []
-        self.src_l, self.mid_l, self.dst_l, self.mid_map = [], [], [], []
+        self.src_l, self.mid_l, self.dst_l = [], [], []
         for spec in self.specs:
             code = R.dtype_code(spec.dtype)
             out = R.dtype_code(getattr(spec, "out_dtype", spec.dtype))  # a conversion happens in stage 1
-            m1, p1, rank_map = stage1_layout(spec.dst_mesh, spec.dst_placements)
+            m1, p1 = stage1_layout(spec.dst_mesh, spec.dst_placements)
             s = R.reshard_layout_create(spec.shape, code, spec.src_mesh, spec.src_placements)
             m = R.reshard_layout_create(spec.shape, out, m1, p1)
             d = R.reshard_layout_create(spec.shape, out, spec.dst_mesh, spec.dst_placements)
@@ -85,7 +59,6 @@ class TwoStagePlan:
             self.src_l.append(s)
             self.mid_l.append(m)
             self.dst_l.append(d)
-            self.mid_map.append(rank_map)
         self.stage1, self.stage2 = [], []
         for c in range(chunks):
             a, b = self.bounds[c], self.bounds[c + 1]

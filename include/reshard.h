@@ -163,11 +163,13 @@ typedef struct reshard_piece {
  *                            the row in registers, `extent[1]` = 1024 rows per
  *                            tile (512 when one side is four packed 4-byte
  *                            column runs, which the four lanes of a quad
- *                            exchange).  A 32-byte band whose sides are eight
- *                            packed 4-byte runs or whole rows (at least one side
- *                            runs) skips LDS too when every descriptor of the
- *                            plan is such a band: eight lanes exchange words,
- *                            512 rows per tile.
+ *                            exchange).  Some band shapes skip LDS in a kernel
+ *                            build of their own (whole rows against packed
+ *                            column runs of 2, 4 or 8 bytes, or against
+ *                            16-byte-aligned column slices: lanes exchange
+ *                            values in registers); each such band kind runs in
+ *                            a launch of its own, whatever the rest of the plan
+ *                            holds (n_launches counts them).
  *   RESHARD_DESC_CONVERT     rows of `run_bytes` ELEMENTS (not bytes) converted by
  *                            conversion `unit`; item c is elements
  *                            [c*8, min(c*8+8, run)) of the row; row_items =
@@ -235,11 +237,18 @@ reshard_status_t reshard_layout_shard_box(reshard_layout_t layout, int64_t rank,
 
 /*
  * Plan the reshard of one tensor from layout src to layout dst (same global
- * shape; same dtype or a supported conversion).  Host-only: intersects every source box with every unique
- * destination box, picks one source replica per overlap (least-loaded first),
- * merges contiguous dims and builds the descriptor table.  The layouts may be
- * destroyed afterwards.  The device table is uploaded by reshard_plan_upload or
- * by the first reshard_execute.
+ * shape; same dtype or a supported conversion).  The pages define the
+ * operation this plans: the transfer pattern follows from the two DTensor
+ * descriptions alone, by computing every source shard's overlap with every
+ * destination shard before any data moves (news.bpdata.com write-up, "the
+ * Reshard collective" section; techfeed.io write-up, "reformulation" section,
+ * whose 8x8 example has each of four column shards receive one 4x2 block from
+ * each of two row shards).  Host-only: intersects every source box with every
+ * unique destination box, picks one source replica per overlap (least-loaded
+ * first: replicated weights can be read at any of their holders, news.bpdata.com,
+ * "the approach" section), merges contiguous dims and builds the descriptor
+ * table.  The layouts may be destroyed afterwards.  The device table is
+ * uploaded by reshard_plan_upload or by the first reshard_execute.
  * Errors: RESHARD_ERR_INVALID_ARGUMENT, RESHARD_ERR_LAYOUT_MISMATCH,
  * RESHARD_ERR_OUT_OF_MEMORY.
  */
@@ -248,9 +257,14 @@ reshard_status_t reshard_plan_create(reshard_layout_t src, reshard_layout_t dst,
 
 /*
  * Plan n tensors that are moved together by one execute (one fused kernel launch,
- * or a few when WINDOW bands are mixed with other descriptors: see n_launches).
- * Pointer arrays of reshard_execute are then concatenated tensor-major: tensor
- * 0's ranks first, each tensor's ranks in row-major mesh order.
+ * or a few when band descriptors are mixed with other descriptors: see
+ * n_launches).  A refit moves every weight of a model in one collective call
+ * (techfeed.io write-up, "reformulation" section: one call given the two
+ * DTensor descriptions; news.bpdata.com, "integration and hybrid solution in
+ * NeMo RL" section: the FFN projections, about 95% of the payload, go through
+ * the reshard together).  Pointer arrays of reshard_execute are then
+ * concatenated tensor-major: tensor 0's ranks first, each tensor's ranks in
+ * row-major mesh order.  Errors as reshard_plan_create.
  */
 reshard_status_t reshard_plan_create_batched(int n, const reshard_layout_t* src,
                                              const reshard_layout_t* dst, reshard_plan_t* out);
@@ -265,6 +279,13 @@ reshard_status_t reshard_plan_upload(reshard_plan_t plan, void* stream);
 
 /*
  * Run the reshard on `stream` (hipStream_t, NULL = default stream); asynchronous.
+ * Every planned overlap is read once from its source shard and written to every
+ * destination replica that holds it: the single-GPU form of sending each
+ * contribution once and replicating it inside the destination domain
+ * (techfeed.io write-up, "NVIDIA's NVLink implementation" section;
+ * news.bpdata.com, "the Reshard collective" section).  Only the overlaps move,
+ * so the bytes written equal the destination shards' bytes, with no gathered
+ * copy of the full tensor in between (techfeed.io, "core problem" section).
  *   src_ptrs[n_src_ptrs]  device pointers to the source shards (read only)
  *   dst_ptrs[n_dst_ptrs]  device pointers to the destination shards (written)
  * Pointers are borrowed: keep the buffers alive until the stream has passed the
@@ -288,7 +309,20 @@ reshard_status_t reshard_plan_upload(reshard_plan_t plan, void* stream);
 reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptrs,
                                  void* const* dst_ptrs, void* stream);
 
+/* Statistics of the plan (one execute's bytes, pieces, launches; see the struct). */
 reshard_status_t reshard_plan_stats(reshard_plan_t plan, reshard_plan_stats_t* out);
+
+/*
+ * Inspection: bytes the kernel reads from each source pointer slot of one
+ * execute (the load the replica choice balances; replicated sources share the
+ * reads of their box: news.bpdata.com write-up, "the approach" section).
+ * Copies up to `capacity` entries, in the order of the src_ptrs array, into
+ * bytes[] and the slot count (n_src_ptrs) into *n_total.  Slots of empty or
+ * unread replicas hold 0.  bytes may be NULL when capacity is 0.
+ * Errors: RESHARD_ERR_INVALID_ARGUMENT.
+ */
+reshard_status_t reshard_plan_src_load(reshard_plan_t plan, int64_t capacity, int64_t* bytes,
+                                       int64_t* n_total);
 
 /*
  * Inspection: copy up to `capacity` pieces into out[] and the total count into

@@ -309,7 +309,10 @@ def pin_convert_library(lib, seed=3):
     for fmt, tdt in (("bf16", torch.bfloat16), ("f16", torch.float16)):
         h = allp.view(tdt)
         got = oracle.convert(h.contiguous(), fmt, "f32", lib=lib)
-        want = h.to(torch.float32) if fmt == "bf16" else torch.from_numpy(h.numpy().astype(np.float32))             if False else torch.from_numpy(allp.numpy().view(np.float16).astype(np.float32))
+        if fmt == "bf16":
+            want = h.to(torch.float32)
+        else:
+            want = torch.from_numpy(allp.numpy().view(np.float16).astype(np.float32))
         nan = torch.isnan(want)
         assert torch.equal(torch.isnan(got), nan), f"{fmt}->f32 NaN-ness"
         assert torch.equal(got[~nan].view(torch.int32), want[~nan].view(torch.int32)), f"{fmt}->f32 values"
@@ -322,6 +325,42 @@ def pin_convert_library(lib, seed=3):
         expo = 0x7F80 if fmt == "bf16" else 0x7C00      # exponent field all ones, fraction nonzero
         assert all((int(v) & expo) == expo and (int(v) & 0x7FFF & ~expo) for v in out), f"f32->{fmt}: NaN lost"
         assert [(int(v) >> 15) & 1 for v in out] == [(int(b) >> 31) & 1 for b in nans.tolist()], f"f32->{fmt}: NaN sign"
+
+
+def pin_convert_nan_payloads(lib, seed=5):
+    """Quiet-NaN payloads under conversion, pinned to library casts.  IEEE 754
+    (2019, clause 6.2.3) asks a conversion that propagates a NaN to keep as much
+    of its payload as the destination format holds; for quiet NaN inputs the
+    libraries below do exactly that, so there the convention (sign kept, leading
+    payload bits kept, quiet bit set) must agree with them bit for bit.
+      f32 -> f16:  numpy's float16 cast (drops the 13 low payload bits);
+      f16 -> f32:  numpy's float32 cast (appends 13 zero bits);
+      bf16 -> f32: torch's float32 cast (appends 16 zero bits);
+      f32 -> bf16: the f32 read back through torch's bf16 -> f32 cast must equal
+                   the input with its 16 low payload bits cleared.
+    Signalling NaNs are left out: numpy keeps them signalling, the convention
+    quiets them (checked by the hand-derived cases of pin_convert_closed)."""
+    rng = np.random.default_rng(seed)
+    n = 4096
+    pay = rng.integers(0, 1 << 22, size=n, dtype=np.int64)            # 22 payload bits below the quiet bit
+    sign = rng.integers(0, 2, size=n, dtype=np.int64) << 31
+    f32 = (sign | 0x7FC00000 | pay).astype(np.uint32)                     # quiet NaNs, any payload
+    f32 = np.concatenate([f32, np.array([0x7FC00000, 0xFFC00000, 0x7FFFFFFF, 0xFFFFFFFF], dtype=np.uint32)])
+    x = torch.from_numpy(f32.view(np.float32).copy())
+    got = oracle.convert(x, "f32", "f16", lib=lib).view(torch.int16).numpy().view(np.uint16)
+    want = f32.view(np.float32).astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want), "f32->f16 quiet-NaN payload differs from numpy"
+    got = oracle.convert(x, "f32", "bf16", lib=lib)
+    back = got.to(torch.float32).view(torch.int32).numpy().view(np.uint32)
+    assert np.array_equal(back, f32 & np.uint32(0xFFFF0000)), "f32->bf16 quiet-NaN payload"
+    h16 = (rng.integers(0, 2, size=n) << 15 | 0x7E00 | rng.integers(0, 1 << 9, size=n)).astype(np.uint16)
+    got = oracle.convert(torch.from_numpy(h16.view(np.float16).copy()), "f16", "f32", lib=lib)
+    want = h16.view(np.float16).astype(np.float32).view(np.uint32)
+    assert np.array_equal(got.view(torch.int32).numpy().view(np.uint32), want), "f16->f32 quiet-NaN payload"
+    b16 = (rng.integers(0, 2, size=n) << 15 | 0x7FC0 | rng.integers(0, 1 << 6, size=n)).astype(np.uint16)
+    hb = torch.from_numpy(b16.view(np.int16).copy()).view(torch.bfloat16)
+    got = oracle.convert(hb, "bf16", "f32", lib=lib).view(torch.int32)
+    assert torch.equal(got, hb.to(torch.float32).view(torch.int32)), "bf16->f32 quiet-NaN payload differs from torch"
 
 
 def pin_convert_closed(lib):
@@ -367,7 +406,7 @@ def pin_convert_closed(lib):
     assert got.tolist() == [0x7FC02000, 0xFFC00000 | (0x155 << 13)], [hex(v) for v in got]
 
 
-ALL_PINS = (pin_convert_library, pin_convert_closed,
+ALL_PINS = (pin_convert_library, pin_convert_nan_payloads, pin_convert_closed,
             pin_worked_example, pin_box_vs_dtensor, pin_box_vs_chunk, pin_end_to_end_chunk,
             pin_gather, pin_raw_bits)
 

@@ -44,6 +44,10 @@ def test_pin_convert_library(oracle_lib):
     P.pin_convert_library(oracle_lib)
 
 
+def test_pin_convert_nan_payloads(oracle_lib):
+    P.pin_convert_nan_payloads(oracle_lib)
+
+
 def test_pin_convert_closed(oracle_lib):
     P.pin_convert_closed(oracle_lib)
 
@@ -115,6 +119,9 @@ MUTANTS = {
     "no_overflow_to_inf": ("  if (y > max_finite(f)) y = INFINITY;", "  (void)0;"),
     "f16_bias_16": ("    {16, 10, 15},   // 2: IEEE binary16", "    {16, 10, 16},   // 2: IEEE binary16"),
     "nan_not_quiet": ("    m |= 1u << (to.frac - 1);  // quiet", "    m |= 0;"),
+    "nan_payload_dropped": ("    m |= 1u << (to.frac - 1);  // quiet", "    m = 1u << (to.frac - 1);"),
+    "nan_payload_low_bits": ("m = to.frac >= from.frac ? m << (to.frac - from.frac) : m >> (from.frac - to.frac);",
+                             "m = to.frac >= from.frac ? m << (to.frac - from.frac) : m & ((1u << to.frac) - 1);"),
     "nan_sign_dropped": ("return (sign << (to.bits - 1)) | (exp_all_ones(to) << to.frac) | m;",
                          "return (exp_all_ones(to) << to.frac) | m;"),
 }

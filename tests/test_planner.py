@@ -388,6 +388,74 @@ def test_source_replica_balance():
         for group, per_rank in loads.items():
             assert len(per_rank) == 4, per_rank  # all four replicas used
             assert max(per_rank.values()) - min(per_rank.values()) <= largest
+        # the same bound read through the C ABI's per-slot load: replicas of one
+        # source box are the slots 2 r + c for the four values of r
+        load = R.reshard_plan_src_load(plan.handle)
+        assert len(load) == 8 and sum(load) == plan.stats()["bytes_read"]
+        for c in range(2):
+            per = [load[2 * r + c] for r in range(4)]
+            assert min(per) > 0 and max(per) - min(per) <= largest, per
+            assert per == [loads[c][2 * r + c] for r in range(4)]
+
+
+def test_source_load_per_slot():
+    """reshard_plan_src_load: one entry per source pointer slot of a batched
+    plan, summing to bytes_read; slots whose shard is empty, and replicas that
+    the choice leaves unread, hold 0."""
+    specs = [T("a", (5, 3), torch.float32, (4,), (0,), (2,), (1,)),           # rank 3 of 4 is empty
+             T("b", (64, 64), torch.bfloat16, (3, 1), (RR, 0), (2,), (0,)),   # three replicas of one box
+             T("c", (64, 64), torch.bfloat16, (2,), (RR,), (4,), (1,))]       # two replicas, four pieces
+    with Plan(specs) as plan:
+        load = R.reshard_plan_src_load(plan.handle)
+        st = plan.stats()
+        assert len(load) == st["n_src_ptrs"] == 4 + 3 + 2
+        assert sum(load) == st["bytes_read"]
+        assert load[3] == 0 and all(x > 0 for x in load[:3])
+        assert sum(load[4:7]) == 64 * 64 * 2 and sum(1 for x in load[4:7] if x) == 2  # two pieces, two replicas
+        assert load[7] == load[8] == 64 * 64 * 2 // 2
+        for i, pc in enumerate(R.reshard_plan_pieces(plan.handle)):
+            assert load[[0, 4, 7][pc["tensor"]] + pc["src_rank"]] > 0
+
+
+def rank_loss_sequence(rows=448, cols=320):
+    """The single-GPU image of a refit whose communication groups are torn down
+    and rebuilt when ranks leave: the same weight planned again and again on
+    shrinking meshes (training ranks lost: fewer row shards; inference ranks
+    lost: fewer data-parallel replicas or tensor-parallel column shards, some
+    splits ragged)."""
+    layouts = [((4,), (0,), (2, 4), (RR, 1)), ((3,), (0,), (2, 4), (RR, 1)), ((3,), (0,), (2, 3), (RR, 1)),
+               ((3,), (0,), (1, 3), (RR, 1)), ((2,), (0,), (3,), (1,)), ((1,), (RR,), (2,), (1,))]
+    return [T(f"rank_loss_{i}", (rows, cols), torch.bfloat16, sm, sp, dm, dp)
+            for i, (sm, sp, dm, dp) in enumerate(layouts)]
+
+
+def test_replan_after_rank_loss():
+    """Destroy a plan, plan the same tensor again on a smaller mesh, and check
+    each new plan against the oracle: the planned pieces applied on the host and
+    the descriptor table walked byte by byte."""
+    prev = None
+    for spec in rank_loss_sequence():
+        plan = Plan([spec])
+        try:
+            assert_boxes_agree(plan)
+            _, srcs = sources_for(spec, "raw", seed=5)
+            want = oracle_dsts(spec, srcs)
+            got = apply_pieces(plan, [srcs])[0]
+            for a, b in zip(got, want):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), spec.name
+            sflat = [None if x is None else x.contiguous().view(torch.uint8).reshape(-1).numpy() for x in srcs]
+            dflat = [np.full(int(np.prod(box_shape(b))) * 2, 0xA5, dtype=np.uint8) for b in plan.dst_boxes(0)]
+            run_descriptors(plan, sflat, dflat)
+            for a, b in zip(dflat, want):
+                assert a.tobytes() == b.view(torch.uint8).numpy().tobytes(), spec.name
+            st = plan.stats()
+            assert st["bytes_read"] == 448 * 320 * 2
+            assert st["bytes_written"] == sum(int(np.prod(box_shape(b))) * 2 for b in plan.dst_boxes(0))
+            if prev is not None:
+                assert st["n_dst_ptrs"] <= prev["n_dst_ptrs"] and st["n_src_ptrs"] <= prev["n_src_ptrs"]
+            prev = st
+        finally:
+            plan.close()
 
 
 def test_dim_merging():
@@ -668,8 +736,19 @@ def test_two_stage_layout_slices_tile_each_box(wl):
     import oracle
     from dtensor_layout_movement_amd.two_stage import stage1_layout
     for spec in wl.tensors[:9]:
-        mesh1, pl1, rank_map = stage1_layout(spec.dst_mesh, spec.dst_placements)
+        mesh1, pl1 = stage1_layout(spec.dst_mesh, spec.dst_placements)
         n1 = int(np.prod(mesh1))
+        # stage-1 rank r1 has the coordinates of the destination rank that owns its
+        # slice, listed in stage-1 mesh order (non-Replicate dims, then Replicate)
+        order = [i for i, p in enumerate(spec.dst_placements) if p != R.REPLICATE] + \
+                [i for i, p in enumerate(spec.dst_placements) if p == R.REPLICATE]
+        rank_map = []
+        for r1 in range(n1):
+            c1 = np.unravel_index(r1, mesh1)
+            cd = [0] * len(spec.dst_mesh)
+            for j, i in enumerate(order):
+                cd[i] = int(c1[j])
+            rank_map.append(int(np.ravel_multi_index(cd, spec.dst_mesh)))
         covered = {}
         for r1 in range(n1):
             lo, hi = oracle.shard_box(list(spec.shape), list(mesh1), list(pl1), r1)
