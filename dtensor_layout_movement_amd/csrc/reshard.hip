@@ -43,24 +43,29 @@ size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 struct reshard_plan_s {
   rs::HostPlan host;
   std::mutex mu;
-  bool uploaded = false;
-  int device = -1;
-  // One launch group: descriptors that run in one kernel variant.
+  // One launch group: descriptors that run in one kernel variant.  Device
+  // addresses are offsets into the table image (the image is placed either in
+  // the plan's own allocation or in the library's static scratch array).
   struct Launch {
     int kind = 0;          // kernel variant (rs::kernel_kind of the group's descriptors)
     uint32_t n_desc = 0;
     uint32_t n_tiles = 0;
     uint32_t per_xcd = 0;  // blocks per XCD, a multiple of rs::kXcdGroup (0: one block per tile)
     uint32_t n_wg = 0;     // grid: rs::kXcds * per_xcd blocks (surplus ones exit), else n_tiles
-    const reshard_descriptor_t* descs = nullptr;  // the group's descriptors in the device table
-    const uint32_t* tile_begin = nullptr;         // its first tile of each, from 0; n_desc + 1 entries
+    size_t desc_off = 0;   // the group's descriptors in the image
+    size_t tb_off = 0;     // its first tile of each, from 0; n_desc + 1 entries
   };
+  // host image of the device table, built once: descriptors by group | refs
+  // (absolute pointer slots) | tile_begin by group | segments
+  bool image_built = false;
+  std::vector<uint8_t> image;
   std::vector<Launch> launches;
+  size_t refs_off = 0, segs_off = 0;
+  // the plan's own device copy of the image
+  bool uploaded = false;
+  int device = -1;
   int64_t table_bytes = 0;
-  // device: descriptors by group | refs (absolute pointer slots) | tile_begin by group | segments
   void* table = nullptr;
-  const uint32_t* d_refs = nullptr;
-  const reshard_segment_t* d_segs = nullptr;
   // pointer-table slots, used when the pointers do not fit in kernel arguments
   int64_t n_ptrs = 0;
   void* d_slots = nullptr;
@@ -120,17 +125,10 @@ std::vector<Group> launch_groups(const rs::HostPlan& H) {
   return out;
 }
 
-reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
-  if (p->uploaded) {
-    if (dev != p->device)
-      return fail(RESHARD_ERR_DEVICE_MISMATCH, "plan was uploaded to device " +
-                                                   std::to_string(p->device) + ", current device is " +
-                                                   std::to_string(dev));
-    return RESHARD_OK;
-  }
+// Builds the host image of the device table and the launch groups (host only,
+// once per plan).
+void build_image_locked(reshard_plan_s* p) {
+  if (p->image_built) return;
   const rs::HostPlan& H = p->host;
   const std::vector<Group> groups = launch_groups(H);
   size_t n_tb = 0;
@@ -139,12 +137,11 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   const size_t refs_off = align_up(desc_bytes, 256);
   const size_t tiles_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);
   const size_t segs_off = align_up(tiles_off + n_tb * sizeof(uint32_t), 256);
-  const size_t total = segs_off + H.segs.size() * sizeof(reshard_segment_t);
+  const size_t total = align_up(segs_off + H.segs.size() * sizeof(reshard_segment_t), 256);
   std::vector<uint8_t> img(total, 0);
   reshard_descriptor_t* dd = reinterpret_cast<reshard_descriptor_t*>(img.data());
   uint32_t* tb = reinterpret_cast<uint32_t*>(img.data() + tiles_off);
   std::vector<reshard_plan_s::Launch> launches;
-  std::vector<size_t> desc_at, tb_at;  // each group's first descriptor and tile_begin entry
   size_t k = 0, t = 0;
   for (const Group& g : groups) {
     reshard_plan_s::Launch L;
@@ -157,8 +154,8 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
                     ? 0u
                     : uint32_t((per_xcd_min + rs::kXcdGroup - 1) / rs::kXcdGroup * rs::kXcdGroup);
     L.n_wg = L.per_xcd ? L.per_xcd * rs::kXcds : L.n_tiles;
-    desc_at.push_back(k);
-    tb_at.push_back(t);
+    L.desc_off = k * sizeof(reshard_descriptor_t);
+    L.tb_off = tiles_off + t * sizeof(uint32_t);
     uint32_t first = 0;
     for (const uint32_t i : g.descs) {
       dd[k++] = H.descs[i];
@@ -175,17 +172,40 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
   // fan-out list, whose entries were made absolute above
   reshard_segment_t* sg = reinterpret_cast<reshard_segment_t*>(img.data() + segs_off);
   for (size_t i = 0; i < H.segs.size(); ++i) sg[i] = H.segs[i];
+  p->image = std::move(img);
+  p->launches = std::move(launches);
+  p->refs_off = refs_off;
+  p->segs_off = segs_off;
+  p->n_ptrs = H.n_src_ptrs + H.n_dst_ptrs;
+  p->image_built = true;
+}
 
+reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (p->uploaded) {
+    if (dev != p->device)
+      return fail(RESHARD_ERR_DEVICE_MISMATCH, "plan was uploaded to device " +
+                                                   std::to_string(p->device) + ", current device is " +
+                                                   std::to_string(dev));
+    return RESHARD_OK;
+  }
+  try {
+    build_image_locked(p);
+  } catch (const std::bad_alloc&) {
+    return fail(RESHARD_ERR_OUT_OF_MEMORY, "host memory exhausted while building the descriptor table");
+  }
+  const size_t total = p->image.size();
   void* table = nullptr;
   e = hipMalloc(&table, total);
   if (e != hipSuccess) return hip_fail(e, "hipMalloc(descriptor table)");
-  e = hipMemcpyAsync(table, img.data(), total, hipMemcpyHostToDevice, stream);
+  e = hipMemcpyAsync(table, p->image.data(), total, hipMemcpyHostToDevice, stream);
   if (e == hipSuccess) e = hipStreamSynchronize(stream);
   if (e != hipSuccess) {
     (void)hipFree(table);
     return hip_fail(e, "descriptor table upload");
   }
-  p->n_ptrs = H.n_src_ptrs + H.n_dst_ptrs;
   if (p->n_ptrs > rs::kKargPtrs) {
     const size_t bytes = size_t(kSlots) * size_t(p->n_ptrs) * sizeof(void*);
     e = hipMalloc(&p->d_slots, bytes);
@@ -205,17 +225,76 @@ reshard_status_t upload_locked(reshard_plan_s* p, hipStream_t stream) {
     }
   }
   p->table = table;
-  p->d_refs = reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + refs_off);
-  p->d_segs = reinterpret_cast<const reshard_segment_t*>(static_cast<uint8_t*>(table) + segs_off);
-  for (size_t g = 0; g < launches.size(); ++g) {
-    launches[g].descs = reinterpret_cast<const reshard_descriptor_t*>(table) + desc_at[g];
-    launches[g].tile_begin =
-        reinterpret_cast<const uint32_t*>(static_cast<uint8_t*>(table) + tiles_off) + tb_at[g];
-  }
-  p->launches = std::move(launches);
   p->table_bytes = int64_t(total);
   p->device = dev;
   p->uploaded = true;
+  return RESHARD_OK;
+}
+
+// Every launch group of the plan, in order on `stream`, with the table image at
+// device address `base`.  Returns the first launch error.
+hipError_t launch_groups_at(const reshard_plan_s* p, const uint8_t* base, const void* const* table,
+                            const rs::KargPtrs& karg, uint32_t flags, hipStream_t stream) {
+  const uint32_t* refs = reinterpret_cast<const uint32_t*>(base + p->refs_off);
+  const reshard_segment_t* segs = reinterpret_cast<const reshard_segment_t*>(base + p->segs_off);
+  for (const reshard_plan_s::Launch& L : p->launches) {
+    const hipError_t e =
+        rs::launch_copy(L.kind, L.n_wg, stream, reinterpret_cast<const reshard_descriptor_t*>(base + L.desc_off),
+                        L.n_desc, reinterpret_cast<const uint32_t*>(base + L.tb_off), refs, segs, table, karg,
+                        L.n_tiles, L.per_xcd, flags);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// Argument checks shared by the execute entry points.
+reshard_status_t check_pointers(const rs::HostPlan& H, const void* const* src_ptrs, void* const* dst_ptrs) {
+  if ((H.n_src_ptrs && !src_ptrs) || (H.n_dst_ptrs && !dst_ptrs))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "pointer array is NULL");
+  for (int64_t i = 0; i < H.n_src_ptrs; ++i)
+    if (H.src_needed[i] && !src_ptrs[i])
+      return fail(RESHARD_ERR_NULL_SHARD, "src_ptrs[" + std::to_string(i) + "] is NULL but its shard is not empty");
+  for (int64_t i = 0; i < H.n_dst_ptrs; ++i)
+    if (H.dst_needed[i] && !dst_ptrs[i])
+      return fail(RESHARD_ERR_NULL_SHARD, "dst_ptrs[" + std::to_string(i) + "] is NULL but its shard is not empty");
+  return RESHARD_OK;
+}
+
+// The kAllAligned16 flag when every shard pointer is 16-byte aligned.
+uint32_t alignment_flags(const rs::HostPlan& H, const void* const* src_ptrs, void* const* dst_ptrs) {
+  uintptr_t bits = 0;
+  for (int64_t i = 0; i < H.n_src_ptrs; ++i) bits |= reinterpret_cast<uintptr_t>(src_ptrs[i]);
+  for (int64_t i = 0; i < H.n_dst_ptrs; ++i) bits |= reinterpret_cast<uintptr_t>(dst_ptrs[i]);
+  return (bits & 15) == 0 ? rs::kAllAligned16 : 0;
+}
+
+// ------------------------------------------------------------ static scratch
+//
+// The allocation-free execute (reshard_execute_noalloc) places the plan's
+// table image, and the pointer array when it does not fit in the kernel
+// arguments, in this array instead of memory the library allocates.  Host code
+// never uses the array's name as an address: each device's copy is found once
+// with hipGetSymbolAddress and that address is used from then on.
+constexpr size_t kScratchBytes = RESHARD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+uint8_t* g_scratch_ptr[kMaxDevices] = {};
+
+reshard_status_t scratch_of_current_device(uint8_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(RESHARD_ERR_HIP, "device index beyond the scratch table");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = static_cast<uint8_t*>(ptr);
+  }
+  *out = g_scratch_ptr[dev];
   return RESHARD_OK;
 }
 
@@ -317,14 +396,8 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
                                  void* const* dst_ptrs, void* stream_arg) {
   if (!plan) return fail(RESHARD_ERR_INVALID_ARGUMENT, "plan is NULL");
   const rs::HostPlan& H = plan->host;
-  if ((H.n_src_ptrs && !src_ptrs) || (H.n_dst_ptrs && !dst_ptrs))
-    return fail(RESHARD_ERR_INVALID_ARGUMENT, "pointer array is NULL");
-  for (int64_t i = 0; i < H.n_src_ptrs; ++i)
-    if (H.src_needed[i] && !src_ptrs[i])
-      return fail(RESHARD_ERR_NULL_SHARD, "src_ptrs[" + std::to_string(i) + "] is NULL but its shard is not empty");
-  for (int64_t i = 0; i < H.n_dst_ptrs; ++i)
-    if (H.dst_needed[i] && !dst_ptrs[i])
-      return fail(RESHARD_ERR_NULL_SHARD, "dst_ptrs[" + std::to_string(i) + "] is NULL but its shard is not empty");
+  reshard_status_t st = check_pointers(H, src_ptrs, dst_ptrs);
+  if (st != RESHARD_OK) return st;
 
   hipStream_t stream = static_cast<hipStream_t>(stream_arg);
   std::lock_guard<std::mutex> lock(plan->mu);
@@ -344,7 +417,7 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
                   "a plan with more than " + std::to_string(rs::kKargPtrs) +
                       " shard pointers cannot be captured into a graph");
   }
-  reshard_status_t st = upload_locked(plan, stream);
+  st = upload_locked(plan, stream);
   if (st != RESHARD_OK) return st;
   if (H.descs.empty()) return RESHARD_OK;
 
@@ -353,10 +426,7 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
   const void* const* table = nullptr;
   int slot = -1;
   hipError_t e;
-  uintptr_t ptr_bits = 0;  // low bits of every pointer, for the all-aligned fast path
-  for (int64_t i = 0; i < H.n_src_ptrs; ++i) ptr_bits |= reinterpret_cast<uintptr_t>(src_ptrs[i]);
-  for (int64_t i = 0; i < H.n_dst_ptrs; ++i) ptr_bits |= reinterpret_cast<uintptr_t>(dst_ptrs[i]);
-  const uint32_t flags = (ptr_bits & 15) == 0 ? rs::kAllAligned16 : 0;
+  const uint32_t flags = alignment_flags(H, src_ptrs, dst_ptrs);
   if (plan->n_ptrs <= rs::kKargPtrs) {
     for (int64_t i = 0; i < H.n_src_ptrs; ++i) karg.p[i] = src_ptrs[i];
     for (int64_t i = 0; i < H.n_dst_ptrs; ++i) karg.p[H.n_src_ptrs + i] = dst_ptrs[i];
@@ -399,12 +469,8 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
     }
     table = reinterpret_cast<const void* const*>(static_cast<void**>(plan->d_slots) + size_t(slot) * n);
   }
-  hipError_t le = hipSuccess;
-  for (const reshard_plan_s::Launch& L : plan->launches) {  // in order on one stream
-    le = rs::launch_copy(L.kind, L.n_wg, stream, L.descs, L.n_desc, L.tile_begin, plan->d_refs, plan->d_segs,
-                         table, karg, L.n_tiles, L.per_xcd, flags);
-    if (le != hipSuccess) break;
-  }
+  const hipError_t le =
+      launch_groups_at(plan, static_cast<const uint8_t*>(plan->table), table, karg, flags, stream);
   if (slot >= 0) {
     // recorded even when a launch failed: the launches of a split plan that
     // went out before it may still read the slot
@@ -417,6 +483,57 @@ reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptr
     }
   }
   if (le != hipSuccess) return hip_fail(le, "reshard_copy_kernel launch");
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_execute_noalloc(reshard_plan_t plan, const void* const* src_ptrs,
+                                         void* const* dst_ptrs, void* stream_arg) {
+  if (!plan) return fail(RESHARD_ERR_INVALID_ARGUMENT, "plan is NULL");
+  const rs::HostPlan& H = plan->host;
+  reshard_status_t st = check_pointers(H, src_ptrs, dst_ptrs);
+  if (st != RESHARD_OK) return st;
+  hipStream_t stream = static_cast<hipStream_t>(stream_arg);
+  uint8_t* base = nullptr;
+  st = scratch_of_current_device(&base);
+  if (st != RESHARD_OK) return st;
+  std::lock_guard<std::mutex> lock(plan->mu);
+  try {
+    build_image_locked(plan);
+  } catch (const std::bad_alloc&) {
+    return fail(RESHARD_ERR_OUT_OF_MEMORY, "host memory exhausted while building the descriptor table");
+  }
+  if (H.descs.empty()) return RESHARD_OK;
+  const size_t img = plan->image.size();  // a multiple of 256
+  const bool in_karg = plan->n_ptrs <= rs::kKargPtrs;
+  const size_t need = img + (in_karg ? 0 : size_t(plan->n_ptrs) * sizeof(void*));
+  if (need > kScratchBytes)
+    return fail(RESHARD_ERR_INVALID_ARGUMENT,
+                "plan needs " + std::to_string(need) + " bytes of table and pointers, more than the " +
+                    std::to_string(kScratchBytes) + " bytes of the static scratch array");
+  // The image is plan-owned and never changes, so the copy may still be in
+  // flight when this call returns.
+  hipError_t e = hipMemcpyAsync(base, plan->image.data(), img, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_fail(e, "descriptor table copy to scratch");
+  rs::KargPtrs karg;
+  std::memset(&karg, 0, sizeof(karg));
+  const void* const* table = nullptr;
+  if (in_karg) {
+    for (int64_t i = 0; i < H.n_src_ptrs; ++i) karg.p[i] = src_ptrs[i];
+    for (int64_t i = 0; i < H.n_dst_ptrs; ++i) karg.p[H.n_src_ptrs + i] = dst_ptrs[i];
+  } else {
+    // the caller's arrays: copied on the stream, then waited for, so that the
+    // call has read them before it returns
+    void** d = reinterpret_cast<void**>(base + img);
+    if (H.n_src_ptrs) e = hipMemcpyAsync(d, src_ptrs, size_t(H.n_src_ptrs) * sizeof(void*), hipMemcpyHostToDevice, stream);
+    if (e == hipSuccess && H.n_dst_ptrs)
+      e = hipMemcpyAsync(d + H.n_src_ptrs, dst_ptrs, size_t(H.n_dst_ptrs) * sizeof(void*), hipMemcpyHostToDevice,
+                         stream);
+    if (e == hipSuccess) e = hipStreamSynchronize(stream);
+    if (e != hipSuccess) return hip_fail(e, "pointer copy to scratch");
+    table = reinterpret_cast<const void* const*>(d);
+  }
+  e = launch_groups_at(plan, base, table, karg, alignment_flags(H, src_ptrs, dst_ptrs), stream);
+  if (e != hipSuccess) return hip_fail(e, "reshard_copy_kernel launch");
   return RESHARD_OK;
 }
 
@@ -437,10 +554,11 @@ reshard_status_t reshard_plan_stats(reshard_plan_t plan, reshard_plan_stats_t* o
   out->table_bytes = plan->uploaded ? plan->table_bytes
                                     : int64_t(H.descs.size() * sizeof(reshard_descriptor_t) + H.refs.size() * 4 +
                                               H.tile_begin.size() * 4 + H.segs.size() * sizeof(reshard_segment_t));
-  for (const reshard_plan_s::Launch& L : plan->launches) {
-    out->n_workgroups += L.n_wg;
-    out->n_launches += (int64_t(L.n_wg) + rs::kMaxLaunchBlocks - 1) / rs::kMaxLaunchBlocks;
-  }
+  if (plan->image_built)
+    for (const reshard_plan_s::Launch& L : plan->launches) {
+      out->n_workgroups += L.n_wg;
+      out->n_launches += (int64_t(L.n_wg) + rs::kMaxLaunchBlocks - 1) / rs::kMaxLaunchBlocks;
+    }
   out->plan_host_us = H.plan_host_us;
   return RESHARD_OK;
 }

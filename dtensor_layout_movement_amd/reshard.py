@@ -49,7 +49,7 @@ CONVERT_F16_F32 = 4
 EXPORTED = (
     "reshard_dtype_size", "reshard_layout_create", "reshard_layout_destroy",
     "reshard_layout_num_ranks", "reshard_layout_shard_box", "reshard_plan_create",
-    "reshard_plan_create_batched", "reshard_plan_upload", "reshard_execute",
+    "reshard_plan_create_batched", "reshard_plan_upload", "reshard_execute", "reshard_execute_noalloc",
     "reshard_plan_stats", "reshard_plan_src_load", "reshard_plan_pieces", "reshard_plan_piece_fanout",
     "reshard_plan_descriptors", "reshard_plan_segments", "reshard_plan_destroy",
     "reshard_last_error",
@@ -128,6 +128,7 @@ def _load() -> ctypes.CDLL:
                                              ctypes.POINTER(_VP)]),
         "reshard_plan_upload": (st, [_VP, _VP]),
         "reshard_execute": (st, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _VP]),
+        "reshard_execute_noalloc": (st, [_VP, ctypes.POINTER(_VP), ctypes.POINTER(_VP), _VP]),
         "reshard_plan_stats": (st, [_VP, ctypes.POINTER(PlanStats)]),
         "reshard_plan_src_load": (st, [_VP, _I64, _I64P, _I64P]),
         "reshard_plan_pieces": (st, [_VP, _I64, ctypes.POINTER(Piece), _I64P]),
@@ -233,6 +234,19 @@ def reshard_execute(plan: int, src_ptrs, dst_ptrs, stream: int | None = None) ->
     if not isinstance(dst_ptrs, ctypes.Array):
         dst_ptrs = pointer_array(dst_ptrs)
     _check(_load().reshard_execute(plan, src_ptrs, dst_ptrs, stream or None))
+
+
+def reshard_execute_noalloc(plan: int, src_ptrs, dst_ptrs, stream: int | None = None) -> None:
+    """reshard_execute with the plan's table in the library's static device array
+    (no allocation; calls that overlap on one GPU race)."""
+    if not isinstance(src_ptrs, ctypes.Array):
+        src_ptrs = pointer_array(src_ptrs)
+    if not isinstance(dst_ptrs, ctypes.Array):
+        dst_ptrs = pointer_array(dst_ptrs)
+    _check(_load().reshard_execute_noalloc(plan, src_ptrs, dst_ptrs, stream or None))
+
+
+NOALLOC_SCRATCH_BYTES = 2 << 20
 
 
 def reshard_plan_stats(plan: int) -> dict:

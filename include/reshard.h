@@ -104,8 +104,10 @@ typedef struct reshard_plan_stats {
   int64_t n_descriptors;  /* device copy descriptors after dim merging / splitting */
   int64_t table_bytes;    /* size of the device-resident descriptor table (once uploaded: as
                              allocated, with padding and one tile list per launch group) */
-  int64_t n_workgroups;   /* workgroups of one execute, about one per tile (0 until upload) */
-  int64_t n_launches;     /* kernel launches of one execute (0 until upload): the descriptors that
+  int64_t n_workgroups;   /* workgroups of one execute, about one per tile (0 until the first
+                             upload or execute) */
+  int64_t n_launches;     /* kernel launches of one execute (0 until the first upload or execute):
+                             the descriptors that
                              are not WINDOW bands share one launch group and each kind of band
                              (the kernel build that moves it) is a group of its own; a group of
                              more than 16,777,208 workgroups goes out as several launches of at
@@ -308,6 +310,31 @@ reshard_status_t reshard_plan_upload(reshard_plan_t plan, void* stream);
  */
 reshard_status_t reshard_execute(reshard_plan_t plan, const void* const* src_ptrs,
                                  void* const* dst_ptrs, void* stream);
+
+/*
+ * reshard_execute without any allocation, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc.  The same kernels run; the plan's descriptor table and,
+ * when src + dst pointers exceed the kernel-argument capacity (120), the
+ * pointer arrays go into a static device array of the library
+ * (RESHARD_NOALLOC_SCRATCH_BYTES per GPU, held until the process ends) instead
+ * of memory the library allocates.  The table is copied there on `stream`
+ * before the launches of every call; nothing in it must start at zero.
+ * Arguments, pointer rules and asynchrony are those of reshard_execute, except:
+ *   - every call on one GPU shares that GPU's array, which keeps the last
+ *     call's contents: calls whose work overlaps on one GPU (other streams,
+ *     other threads, any plan) race and may read each other's table; calls in
+ *     order on one stream are safe;
+ *   - with more than 120 pointers the call waits for `stream` to finish the
+ *     pointer copy (and everything enqueued before it) before returning;
+ *   - a plan whose table plus pointer arrays exceed the array is refused with
+ *     RESHARD_ERR_INVALID_ARGUMENT.
+ * It neither uploads the plan nor uses an uploaded table.
+ * Errors: RESHARD_ERR_INVALID_ARGUMENT, RESHARD_ERR_NULL_SHARD, RESHARD_ERR_HIP.
+ */
+#define RESHARD_NOALLOC_SCRATCH_BYTES (2u << 20)
+reshard_status_t reshard_execute_noalloc(reshard_plan_t plan, const void* const* src_ptrs,
+                                         void* const* dst_ptrs, void* stream);
 
 /* Statistics of the plan (one execute's bytes, pieces, launches; see the struct). */
 reshard_status_t reshard_plan_stats(reshard_plan_t plan, reshard_plan_stats_t* out);

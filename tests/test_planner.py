@@ -724,6 +724,12 @@ def test_device_calls_fail_cleanly_without_a_gpu():
         with pytest.raises(R.ReshardError) as e:
             R.reshard_execute(plan.handle, [0x1000] * 4, [0x2000] * 4, None)
         assert e.value.status == R.ERR_HIP
+        with pytest.raises(R.ReshardError) as e:
+            R.reshard_execute_noalloc(plan.handle, [0x1000] * 4, [0x2000] * 4, None)
+        assert e.value.status == R.ERR_HIP
+        with pytest.raises(R.ReshardError) as e:  # argument checks come before any device call
+            R.reshard_execute_noalloc(plan.handle, [0x1000, 0, 0x1000, 0x1000], [0x2000] * 4, None)
+        assert e.value.status == R.ERR_NULL_SHARD
         assert plan.stats()["n_pieces"] == 8
 
 
