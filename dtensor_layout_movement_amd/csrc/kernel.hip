@@ -1416,6 +1416,104 @@ __device__ __forceinline__ void convert_items(const reshard_descriptor_t& D, con
   }
 }
 
+// ------------------------------------------------------------ gather rows
+//
+// A RESHARD_DESC_GATHER_ROWS tile writes kGatherTileBytes consecutive bytes of
+// a band of whole destination rows (all replicas at the same offset), 16 bytes
+// a lane, so every destination line inside the band is written by one
+// workgroup in whole 16-byte blocks.  A lane's block holds bytes of one source
+// segment, or of two where segments meet (or where a row ends and the next
+// begins).  Every segment is at least 1 KiB wide, so one wave's 1 KiB span
+// touches at most two segments: the wave places its span once, in scalar
+// registers -- row, column, the segment holding its first byte and the one after
+// it -- and a lane only chooses between the two.  Bytes are counted from the
+// start of the wave's row ("pos"); segment i covers pos [col_i, col_i + width_i)
+// and the next row's first segment follows at pos >= W.
+
+// Bytes [0, n) set, n <= 16.
+__device__ __forceinline__ u32x4 low_bytes_mask(uint32_t n) {
+  u32x4 m;
+  m.x = n >= 4 ? 0xffffffffu : (n ? 0xffffffffu >> (32 - 8 * n) : 0u);
+  m.y = n >= 8 ? 0xffffffffu : (n > 4 ? 0xffffffffu >> (32 - 8 * (n - 4)) : 0u);
+  m.z = n >= 12 ? 0xffffffffu : (n > 8 ? 0xffffffffu >> (32 - 8 * (n - 8)) : 0u);
+  m.w = n >= 16 ? 0xffffffffu : (n > 12 ? 0xffffffffu >> (32 - 8 * (n - 12)) : 0u);
+  return m;
+}
+
+template <class Sh>
+__device__ __forceinline__ void gather_rows(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
+                                            const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
+  const uint32_t W = D.run_bytes, nseg = D.extent[1];
+  const uint32_t band = D.extent[0] * W;  // < 2^31 (the planner splits longer bands)
+  const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const uint32_t a_w = tile * rs::kGatherTileBytes + wave * 1024u;
+  if (a_w >= band) return;
+  const uint32_t row_w = div_magic(a_w, D.magic[0][0], D.magic[0][1]);
+  const uint32_t col_w = a_w - row_w * W;
+  const reshard_segment_t* __restrict__ S = segs + D.src_ptr;
+  // the last segment whose column is <= col_w: one entry of the descriptor's
+  // lookup (src_offset and the strides: a 16-bit entry per KiB of row holding
+  // the segment at the KiB's start and where, inside it, the next one begins),
+  // or a search over the segments for rows without one
+  uint32_t i0 = 0;
+  if (D.row_items) {
+    // the entries' words: 0 and 1 in src_offset (bytes 0-7 of the descriptor),
+    // 2 .. 13 in src_stride and dst_stride (bytes 16-63); dst_offset sits between
+    const uint32_t w = col_w >> 11;
+    const uint32_t word = reinterpret_cast<const uint32_t*>(&D)[w < 2 ? w : w + 2];
+    const uint32_t e = (col_w & 1024u) ? word >> 16 : word & 0xffffu;
+    const uint32_t split = e >> 6;
+    i0 = (e & 63u) + (split != 0 && (col_w & 1023u) >= split ? 1u : 0u);
+  } else {
+    uint32_t hi = nseg;
+    while (hi - i0 > 1) {
+      const uint32_t mid = (i0 + hi) >> 1;
+      if (S[mid].col <= col_w) i0 = mid; else hi = mid;
+    }
+  }
+  const bool wrap = i0 + 1 == nseg;
+  const reshard_segment_t s0 = S[i0], s1 = S[wrap ? 0u : i0 + 1];
+  const uint32_t B1 = s0.col + s0.width;                         // end of segment 0
+  const uint32_t E1 = wrap ? W + s1.width : s1.col + s1.width;   // end of segment 1
+  const uint64_t base0 = sh.ptr(s0.ptr) + uint64_t(s0.offset) + uint64_t(row_w) * uint64_t(s0.row_stride) - s0.col;
+  const uint64_t base1 = sh.ptr(s1.ptr) + uint64_t(s1.offset) +
+                         uint64_t(wrap ? row_w + 1 : row_w) * uint64_t(s1.row_stride) - (wrap ? W : s1.col);
+  const uint32_t lane16 = 16u * (threadIdx.x & 63u);
+  const uint32_t pos = col_w + lane16;
+  const uint32_t left = band - a_w;
+  const uint32_t n = left <= lane16 ? 0u : (left - lane16 < 16u ? left - lane16 : 16u);
+  const bool in1 = pos >= B1;
+  const uint64_t base = in1 ? base1 : base0;
+  const uint32_t E = in1 ? E1 : B1;
+  // one 16-byte load inside the segment's row (rows are >= 16 bytes wide);
+  // a block that runs past the segment's end takes the rest from the start of
+  // the next one
+  const uint32_t at = pos < E - 16 ? pos : E - 16;
+  const uint32_t L1 = (pos + n < E ? pos + n : E) - pos;
+  // The second segment's first 16 bytes sit at one address for the whole wave;
+  // kept in vector registers, since the compiler would read a wave-uniform
+  // address with a scalar load, and scalar loads ignore the low two address bits
+  // (the segment start need not be 4-byte aligned).
+  uint64_t at1 = base1 + B1;
+  asm volatile("" : "+v"(at1));
+  u32x4 v1 = u32x4{0, 0, 0, 0}, v2 = v1;
+  if (n) v1 = load_16_unaligned(base + at);
+  if (L1 < n) v2 = load_16_unaligned(at1);
+  if (!n) return;
+  u32x4 x = pos != at ? shift_right_bytes(v1, pos - at) : v1;
+  if (L1 < n) {
+    const u32x4 m = low_bytes_mask(L1);
+    const u32x4 y = shift_left_bytes(v2, L1);
+    x = (x & m) | (y & ~m);
+  }
+  const uint64_t off = uint64_t(D.dst_offset) + a_w + lane16;
+  for (uint32_t r = 0; r < D.fanout; ++r) {
+    const uintptr_t d = sh.ptr(refs[D.dst_ref_begin + r]) + off;
+    if (n == 16) __builtin_nontemporal_store(x, as_global<u32x4_u1>(d));
+    else store_head_bytes(d, x, n);
+  }
+}
+
 // Kernel variants.  A plan runs the smallest variant that covers the modes of
 // its descriptors: short launches pay for code size, for branches in the tile
 // prologue and for an LDS allocation they do not use.
@@ -1436,6 +1534,7 @@ enum KernelKind : int {
                      // runs (window_runs32): no LDS
   kKindOctets = 9,   // every descriptor a 16-byte window band of eight 2-byte column
                      // runs (window_octets): no LDS
+  kKindGatherRows = 10,  // every descriptor RESHARD_DESC_GATHER_ROWS (gather_rows)
   kKindAligned = 16, // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
@@ -1458,10 +1557,25 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t kx = b / kXcds;
   const uint32_t t = per_xcd == 0 ? b : ((kx / kXcdGroup) * kXcds + b % kXcds) * kXcdGroup + kx % kXcdGroup;
   if (t >= n_tiles) return;
-  uint32_t lo = 0, hi = n_desc;  // last descriptor whose first tile is <= t
-  while (hi - lo > 1) {
-    const uint32_t mid = (lo + hi) >> 1;
-    if (tile_begin[mid] <= t) lo = mid; else hi = mid;
+  // the descriptor of tile t: the last one whose first tile is <= t.  The
+  // gather-rows build reads the tile-group lookup behind tile_begin (one load;
+  // a search only where 64 tiles touch three or more descriptors); the others
+  // search tile_begin, which measured as fast for them.
+  uint32_t lo = 0;
+  bool search = true;
+  if constexpr (kKind == kKindGatherRows) {
+    const uint32_t grp = tile_begin[n_desc + 1 + t / kTileGroup];
+    if ((grp >> 24) != kTileGroupSearch) {
+      lo = (grp & 0xffffffu) + (t % kTileGroup >= (grp >> 24) ? 1u : 0u);
+      search = false;
+    }
+  }
+  if (search) {
+    uint32_t hi = n_desc;
+    while (hi - lo > 1) {
+      const uint32_t mid = (lo + hi) >> 1;
+      if (tile_begin[mid] <= t) lo = mid; else hi = mid;
+    }
   }
   const reshard_descriptor_t& D = descs[lo];
   uint32_t unit_mode;  // the two 16-bit fields as one scalar word
@@ -1472,6 +1586,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
                         : kKind == kKindQuadRows || kKind == kKindRuns || kKind == kKindRuns64 ||
                                   kKind == kKindBands16 || kKind == kKindRuns32 || kKind == kKindOctets
                             ? uint32_t(RESHARD_DESC_WINDOW)
+                        : kKind == kKindGatherRows ? uint32_t(RESHARD_DESC_GATHER_ROWS)
                                                : unit_mode >> 16;
   if constexpr (kKind == kKindQuadRows) {
     const Shards<kKarg> wsh{table, &karg, refs};
@@ -1496,6 +1611,11 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   if constexpr (kKind == kKindRuns32) {
     const Shards<kKarg> wsh{table, &karg, refs};
     window_runs32(D, segs, refs, wsh, t - tile_begin[lo]);
+    return;
+  }
+  if constexpr (kKind == kKindGatherRows) {
+    const Shards<kKarg> gsh{table, &karg, refs};
+    gather_rows(D, segs, refs, gsh, t - tile_begin[lo]);
     return;
   }
   if constexpr (kKind == kKindOctets) {
@@ -1612,6 +1732,8 @@ hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_des
       return RS_LAUNCH(kKindRuns32);
     case kKindOctets:
       return RS_LAUNCH(kKindOctets);
+    case kKindGatherRows:
+      return RS_LAUNCH(kKindGatherRows);
     default:
       return RS_LAUNCH(kKindAll);
   }
@@ -1697,7 +1819,7 @@ bool runs64_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
   bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, bands16 = true, runs32 = true;
-  bool octets = true;
+  bool octets = true, gather = true;
   bool window = false;
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
@@ -1710,8 +1832,10 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
     if (!chunks16_band(D, segs)) bands16 = false;
     if (!runs32_band(D, segs)) runs32 = false;
     if (!octets_band(D, segs)) octets = false;
+    if (D.mode != RESHARD_DESC_GATHER_ROWS) gather = false;
     if (D.mode == RESHARD_DESC_WINDOW) window = true;
   }
+  if (gather && !descs.empty()) return kKindGatherRows;
   return items16 ? kKindItems16 : chunks ? kKindChunks : octets ? kKindOctets : quad_rows ? kKindQuadRows
          : runs ? kKindRuns
          : runs64 ? kKindRuns64 : bands16 ? kKindBands16 : runs32 ? kKindRuns32 : window ? kKindAll : kKindCopy;

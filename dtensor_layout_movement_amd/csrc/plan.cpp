@@ -510,27 +510,155 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
   return true;
 }
 
+// Gather-rows bands of one tensor whose destination boxes are whole rows of
+// the 2-d view and whose source pieces are column strips, each at least
+// kGatherMinSeg bytes wide.  Rows are cut wherever a source or destination box
+// starts or ends; each band holds the source segments that tile its rows (in
+// column order, merged where one shard continues) and the one destination box
+// that holds them.  Returns false, emitting nothing it keeps, when the pieces
+// do not have that shape.
+bool emit_gather_rows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
+  const int nd = P->src[t].ndim;
+  const int64_t es = P->src[t].elem_size;
+  const int64_t W = v.cols * es;
+  if (W < kGatherMinSeg) return false;
+  auto rlo = [&](const Box& b) { return b.lo[0] * v.row_mult; };
+  auto rhi = [&](const Box& b) { return b.hi[0] * v.row_mult; };
+  for (size_t i = pc0; i < pc1; ++i) {
+    const Box& db = P->dst_groups[P->pieces[i].dst_group].box;
+    if (db.lo[nd - 1] != 0 || db.hi[nd - 1] != v.cols) return false;  // destination rows must be whole
+  }
+  std::vector<int64_t> cuts;
+  for (size_t i = pc0; i < pc1; ++i) {
+    cuts.push_back(rlo(P->pieces[i].box));
+    cuts.push_back(rhi(P->pieces[i].box));
+  }
+  std::sort(cuts.begin(), cuts.end());
+  cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
+  struct Band {
+    int64_t ra, rb;
+    int64_t dst_group;
+    std::vector<reshard_segment_t> src;
+  };
+  std::vector<Band> bands;
+  for (size_t c = 0; c + 1 < cuts.size(); ++c) {
+    Band b{cuts[c], cuts[c + 1], -1, {}};
+    for (size_t i = pc0; i < pc1; ++i) {
+      const Piece& pc = P->pieces[i];
+      if (rlo(pc.box) > b.ra || rhi(pc.box) < b.rb) continue;
+      if (b.dst_group >= 0 && b.dst_group != pc.dst_group) return false;
+      b.dst_group = pc.dst_group;
+      const Box& sb = P->src_groups[pc.src_group].box;
+      const int64_t s_cols = sb.hi[nd - 1] - sb.lo[nd - 1];
+      reshard_segment_t sg;
+      sg.offset = ((b.ra - rlo(sb)) * s_cols + (pc.box.lo[nd - 1] - sb.lo[nd - 1])) * es;
+      sg.row_stride = s_cols * es;
+      sg.col = uint32_t(pc.box.lo[nd - 1] * es);
+      sg.width = uint32_t((pc.box.hi[nd - 1] - pc.box.lo[nd - 1]) * es);
+      sg.ptr = uint32_t(P->src_base[t] + pc.src_rank);
+      sg.fanout = 0;
+      b.src.push_back(sg);
+    }
+    std::sort(b.src.begin(), b.src.end(),
+              [](const reshard_segment_t& x, const reshard_segment_t& y) { return x.col < y.col; });
+    std::vector<reshard_segment_t> merged;
+    for (const reshard_segment_t& sg : b.src) {
+      if (!merged.empty()) {
+        reshard_segment_t& m = merged.back();
+        if (m.ptr == sg.ptr && m.row_stride == sg.row_stride && m.col + m.width == sg.col &&
+            m.offset + int64_t(m.width) == sg.offset) {
+          m.width += sg.width;
+          continue;
+        }
+      }
+      merged.push_back(sg);
+    }
+    b.src = std::move(merged);
+    int64_t next = 0;  // the segments must tile [0, W)
+    for (const reshard_segment_t& sg : b.src) {
+      if (int64_t(sg.col) != next || int64_t(sg.width) < kGatherMinSeg) return false;
+      next += sg.width;
+    }
+    if (next != W || b.dst_group < 0) return false;
+    bands.push_back(std::move(b));
+  }
+  const int64_t max_rows = kGatherMaxBand / W;
+  for (const Band& b : bands) {
+    const Group& dg = P->dst_groups[b.dst_group];
+    const uint32_t ref_begin = uint32_t(P->refs.size());
+    for (int64_t r : dg.ranks) P->refs.push_back(uint32_t(P->dst_base[t] + r));
+    for (int64_t r0 = b.ra; r0 < b.rb; r0 += max_rows) {
+      const int64_t rows = std::min(max_rows, b.rb - r0);
+      reshard_descriptor_t D;
+      std::memset(&D, 0, sizeof(D));
+      D.mode = RESHARD_DESC_GATHER_ROWS;
+      D.dst_offset = (r0 - rlo(dg.box)) * W;
+      D.run_bytes = uint32_t(W);
+      D.extent[0] = uint32_t(rows);
+      D.extent[1] = uint32_t(b.src.size());
+      D.extent[2] = 1;
+      D.src_ptr = uint32_t(P->segs.size());
+      D.dst_ref_begin = ref_begin;
+      D.fanout = uint32_t(dg.ranks.size());
+      // the segment lookup, in the fields this mode leaves unused
+      uint16_t lut[kGatherLutKiB] = {};
+      static_assert(sizeof(lut) == sizeof(D.src_offset) + sizeof(D.src_stride) + sizeof(D.dst_stride),
+                    "lookup slots");
+      if (W <= int64_t(kGatherLutKiB) * 1024 && b.src.size() <= kGatherLutSegs) {
+        size_t i = 0;
+        for (uint32_t k = 0; int64_t(k) * 1024 < W; ++k) {
+          const uint32_t c = k * 1024;
+          while (i + 1 < b.src.size() && b.src[i + 1].col <= c) ++i;
+          const uint32_t next = i + 1 < b.src.size() ? b.src[i + 1].col : uint32_t(W);
+          const uint32_t off = next < c + 1024 && next < uint32_t(W) ? next - c : 0u;
+          lut[k] = uint16_t(i | (off << 6));
+        }
+        D.row_items = 1;
+      }
+      std::memcpy(&D.src_offset, lut, sizeof(D.src_offset));
+      std::memcpy(D.src_stride, lut + 4, sizeof(D.src_stride));
+      std::memcpy(D.dst_stride, lut + 16, sizeof(D.dst_stride));
+      int64_t bits = W | D.dst_offset;
+      for (reshard_segment_t sg : b.src) {
+        sg.offset += (r0 - b.ra) * sg.row_stride;
+        bits |= sg.offset | sg.row_stride | sg.col;
+        P->segs.push_back(sg);
+      }
+      D.unit = uint16_t(unit_for(bits));
+      magic_u31(D.run_bytes, &D.magic[0][0], &D.magic[0][1]);
+      D.piece = uint32_t(pc0);
+      P->descs.push_back(D);
+    }
+  }
+  return true;
+}
+
 // Descriptors of one tensor: windows when some piece has narrow rows and the
-// tensor has a 2-d view that fits, per-piece descriptors otherwise.
+// tensor has a 2-d view that fits; gather-rows bands when whole destination
+// rows are assembled from wide source column strips that meet off the 16-byte
+// grid (the per-piece path would write the lines where strips meet in part,
+// from two workgroups); per-piece descriptors otherwise.
 void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1) {
   if (pc0 == pc1) return;
   const size_t d0 = P->descs.size(), r0 = P->refs.size();
   emit_pieces(P, t, pc0, pc1);
   if (P->conv[t] != 0) return;  // converting rows always go element-group by element-group
-  bool narrow = false;
+  bool narrow = false, chunked = false;
   for (size_t i = d0; i < P->descs.size(); ++i) {
     const reshard_descriptor_t& D = P->descs[i];
     const uint64_t rows = uint64_t(D.extent[0]) * D.extent[1] * D.extent[2];
     if (rows > 1 && int64_t(D.run_bytes) < kWindowMaxRun) narrow = true;
+    if (rows > 1 && D.mode == RESHARD_DESC_DST_CHUNKS) chunked = true;
   }
   View2d v;
-  if (!narrow || !view_2d(*P, t, pc0, pc1, &v)) return;
+  if ((!narrow && !chunked) || !view_2d(*P, t, pc0, pc1, &v)) return;
   const size_t s0 = P->segs.size();
   std::vector<reshard_descriptor_t> saved(P->descs.begin() + d0, P->descs.end());
   std::vector<uint32_t> saved_refs(P->refs.begin() + r0, P->refs.end());
   P->descs.resize(d0);
   P->refs.resize(r0);
-  if (!emit_windows(P, t, pc0, pc1, v)) {  // keep the per-piece descriptors
+  const bool done = narrow ? emit_windows(P, t, pc0, pc1, v) : emit_gather_rows(P, t, pc0, pc1, v);
+  if (!done) {  // keep the per-piece descriptors
     P->descs.resize(d0);
     P->refs.resize(r0);
     P->segs.resize(s0);
@@ -540,6 +668,22 @@ void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1) {
 }
 
 }  // namespace
+
+void fill_tile_groups(const uint32_t* tb, uint32_t n_desc, uint32_t n_tiles, uint32_t* out) {
+  const uint64_t n_groups = tile_groups(n_tiles);
+  uint32_t d = 0;  // descriptor of the group's first tile: the last one starting at or before it
+  for (uint64_t g = 0; g < n_groups; ++g) {
+    const uint32_t t0 = uint32_t(g * kTileGroup);
+    const uint32_t t1 = uint32_t(std::min<uint64_t>(uint64_t(t0) + kTileGroup, n_tiles));  // exclusive
+    while (d + 1 < n_desc && tb[d + 1] <= t0) ++d;
+    uint32_t e = d;  // descriptor of the group's last tile
+    while (e + 1 < n_desc && tb[e + 1] <= t1 - 1) ++e;
+    if (n_desc >= (1u << 24)) out[g] = kTileGroupSearch << 24;
+    else if (e == d) out[g] = d | (kTileGroup << 24);
+    else if (e == d + 1) out[g] = d | ((tb[d + 1] - t0) << 24);
+    else out[g] = kTileGroupSearch << 24;
+  }
+}
 
 void magic_u31(uint32_t d, uint32_t* m, uint32_t* s) {
   uint32_t l = 0;

@@ -114,12 +114,23 @@ inline bool octet_side(const std::vector<reshard_segment_t>& segs) {
   return true;
 }
 
+// RESHARD_DESC_GATHER_ROWS bands: a tile is kGatherTileBytes of destination (16
+// bytes a lane, 1 KiB a wave), and every source segment is at least
+// kGatherMinSeg bytes wide, so that one wave's 1 KiB touches at most two
+// segments (or the end of one row and the start of the next).
+constexpr uint32_t kGatherTileBytes = 16 * kTileThreads;
+constexpr int64_t kGatherMinSeg = 1024;
+// Bytes of one band at most (the kernel indexes a band in 31 bits).
+constexpr int64_t kGatherMaxBand = (int64_t(1) << 31) - 2 * int64_t(kGatherTileBytes);
+
 // Elements per item of a RESHARD_DESC_CONVERT row.
 constexpr uint32_t kConvertElems = RESHARD_CONVERT_ELEMS;
 
 // Tiles of one descriptor.
 inline uint64_t desc_tiles(const reshard_descriptor_t& D) {
   if (D.mode == RESHARD_DESC_WINDOW) return (uint64_t(D.extent[0]) + D.extent[1] - 1) / D.extent[1];
+  if (D.mode == RESHARD_DESC_GATHER_ROWS)
+    return (uint64_t(D.extent[0]) * D.run_bytes + kGatherTileBytes - 1) / kGatherTileBytes;
   const uint64_t items = uint64_t(D.extent[0]) * D.extent[1] * D.extent[2] * D.row_items;
   return (items + kTileItems - 1) / kTileItems;
 }
@@ -152,6 +163,31 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
 // q = (mulhi(n, m) + n) >> s.  Granlund & Montgomery, "Division by invariant
 // integers using multiplication" (PLDI 1994), round-up multiplier.
 void magic_u31(uint32_t d, uint32_t* m, uint32_t* s);
+
+// Tile-group lookup of a launch group: one u32 per kTileGroup consecutive tiles,
+// stored after the group's tile_begin list, so that a workgroup can find its
+// descriptor with one load instead of a search.  Entry g describes tiles
+// [64 g, 64 g + 64): its low 24 bits are the index d of the descriptor holding
+// tile 64 g and its high 8 bits a split s in 1..64: the group's tiles from
+// 64 g + s on belong to descriptor d + 1 (s = 64: none do).  kTileGroupSearch
+// in the high bits marks a group that touches three or more descriptors; its
+// tiles search tile_begin instead.  (Only the gather-rows build reads it: for
+// the other builds a search over tile_begin measured as fast.)
+constexpr uint32_t kTileGroup = 64;
+constexpr uint32_t kTileGroupSearch = 255;
+inline uint64_t tile_groups(uint64_t n_tiles) { return (n_tiles + kTileGroup - 1) / kTileGroup; }
+// Fills the tile_groups(n_tiles) entries at out from tile_begin[0 .. n_desc].
+void fill_tile_groups(const uint32_t* tile_begin, uint32_t n_desc, uint32_t n_tiles, uint32_t* out);
+
+// A gather-rows descriptor keeps a segment lookup in the 56 bytes of src_offset
+// and the strides, which that mode does not use: uint16 entry k describes row
+// columns [1024 k, 1024 k + 1024) -- the index of the segment holding column
+// 1024 k in its low 6 bits and, in its high 10 bits, the offset inside the KiB
+// where the next segment starts (0: none starts there; segments are at least
+// 1 KiB wide, so at most one does).  Rows up to kGatherLutKiB KiB wide with at
+// most kGatherLutSegs segments have one (row_items = 1); other bands search.
+constexpr uint32_t kGatherLutKiB = 28;
+constexpr uint32_t kGatherLutSegs = 64;
 
 // Largest item count a descriptor may hold (items are indexed in 31 bits).
 constexpr uint64_t kMaxItems = (uint64_t(1) << 31) - 1;

@@ -92,8 +92,9 @@ struct Group {
 };
 
 // The launches of one execute.  Only the general build (rs::kKindAll) runs
-// item, chunk and convert descriptors together with bands, or bands of several
-// kinds together, and it stages bands through LDS and holds more registers, so
+// item, chunk and convert descriptors together with window bands, or bands of
+// several kinds together (gather-rows bands run in their own build only), and
+// it stages bands through LDS and holds more registers, so
 // a plan that mixes them would run everything slower.  Instead the descriptors
 // that are not bands share one launch (the item, chunk or copy build already
 // covers any mix of them), and each band kind runs in a launch of its own
@@ -104,7 +105,7 @@ std::vector<Group> launch_groups(const rs::HostPlan& H) {
   std::vector<Group> bands;   // bands by kind, in order of first appearance
   std::vector<reshard_descriptor_t> one(1);
   for (uint32_t i = 0; i < uint32_t(H.descs.size()); ++i) {
-    if (H.descs[i].mode != RESHARD_DESC_WINDOW) {
+    if (H.descs[i].mode != RESHARD_DESC_WINDOW && H.descs[i].mode != RESHARD_DESC_GATHER_ROWS) {
       rows.add(i, H);
       continue;
     }
@@ -131,8 +132,8 @@ void build_image_locked(reshard_plan_s* p) {
   if (p->image_built) return;
   const rs::HostPlan& H = p->host;
   const std::vector<Group> groups = launch_groups(H);
-  size_t n_tb = 0;
-  for (const Group& g : groups) n_tb += g.descs.size() + 1;
+  size_t n_tb = 0;  // per launch group: tile_begin (n_desc + 1 entries), then its tile-group lookup
+  for (const Group& g : groups) n_tb += g.descs.size() + 1 + rs::tile_groups(g.tiles);
   const size_t desc_bytes = H.descs.size() * sizeof(reshard_descriptor_t);
   const size_t refs_off = align_up(desc_bytes, 256);
   const size_t tiles_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);
@@ -157,12 +158,15 @@ void build_image_locked(reshard_plan_s* p) {
     L.desc_off = k * sizeof(reshard_descriptor_t);
     L.tb_off = tiles_off + t * sizeof(uint32_t);
     uint32_t first = 0;
+    const uint32_t* local = tb + t;
     for (const uint32_t i : g.descs) {
       dd[k++] = H.descs[i];
       tb[t++] = first;
       first += H.tile_begin[i + 1] - H.tile_begin[i];
     }
     tb[t++] = first;
+    rs::fill_tile_groups(local, L.n_desc, L.n_tiles, tb + t);
+    t += rs::tile_groups(g.tiles);
     launches.push_back(L);
   }
   uint32_t* r = reinterpret_cast<uint32_t*>(img.data() + refs_off);

@@ -39,6 +39,7 @@ DESC_ITEMS = 0       # rows of items of `unit` bytes
 DESC_DST_CHUNKS = 1  # rows cut into destination-aligned 16-byte chunks
 DESC_WINDOW = 2      # a band of rows staged through an LDS window
 DESC_CONVERT = 3     # rows of elements converted to another float format (run in elements)
+DESC_GATHER_ROWS = 4  # whole destination rows gathered from wide source column segments
 
 # conversions: the `unit` of a DESC_CONVERT descriptor
 CONVERT_F32_BF16 = 1

@@ -131,6 +131,7 @@ typedef struct reshard_piece {
 #define RESHARD_DESC_DST_CHUNKS 1 /* rows cut into 16-byte chunks aligned to the destination */
 #define RESHARD_DESC_WINDOW 2     /* a band of rows staged through LDS (see below) */
 #define RESHARD_DESC_CONVERT 3    /* rows of elements converted to another float format */
+#define RESHARD_DESC_GATHER_ROWS 4 /* whole destination rows gathered from column segments */
 
 /* Conversions (the `unit` field of a RESHARD_DESC_CONVERT descriptor). */
 #define RESHARD_CONVERT_F32_BF16 1
@@ -172,6 +173,25 @@ typedef struct reshard_piece {
  *                            values in registers); each such band kind runs in
  *                            a launch of its own, whatever the rest of the plan
  *                            holds (n_launches counts them).
+ *   RESHARD_DESC_GATHER_ROWS `extent[0]` whole rows of `run_bytes` bytes, packed in
+ *                            every destination replica from byte `dst_offset`
+ *                            on, gathered from `extent[1]` source segments
+ *                            (segments[src_ptr ...], in column order, tiling
+ *                            the row; each at least 1024 bytes wide) and
+ *                            written to the `fanout` shards listed in the
+ *                            fan-out list from `dst_ref_begin`.  The kernel
+ *                            walks the destination rows in 16-byte blocks, so
+ *                            no destination line is written in part by two
+ *                            workgroups where source column strips meet at an
+ *                            address that is not 16-byte aligned.  magic[0]
+ *                            divides by `run_bytes`.  When row_items is 1,
+ *                            src_offset, src_stride and dst_stride hold, as 28
+ *                            uint16 in that order, a segment lookup: entry k
+ *                            covers row bytes [1024 k, 1024 k + 1024) and holds
+ *                            the index of the segment at byte 1024 k (low 6
+ *                            bits) and the offset inside the KiB where the
+ *                            next segment starts (high 10 bits, 0 for none).
+ *                            row_items 0: no lookup, the kernel searches.
  *   RESHARD_DESC_CONVERT     rows of `run_bytes` ELEMENTS (not bytes) converted by
  *                            conversion `unit`; item c is elements
  *                            [c*8, min(c*8+8, run)) of the row; row_items =

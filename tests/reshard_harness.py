@@ -157,6 +157,9 @@ def run_descriptors(plan: Plan, srcs_flat, dsts_flat):
         if D["mode"] == R.DESC_WINDOW:
             _run_window(D, segs, refs, srcs_flat, dsts_flat)
             continue
+        if D["mode"] == R.DESC_GATHER_ROWS:
+            _run_gather_rows(D, segs, refs, srcs_flat, dsts_flat)
+            continue
         if D["mode"] == R.DESC_CONVERT:
             _run_convert(D, refs, srcs_flat, dsts_flat)
             continue
@@ -243,6 +246,69 @@ def _run_window(D, segs, refs, srcs_flat, dsts_flat):
             dsts_flat[refs[sg["ptr"] + k]][idx] = window[:, sg["col"]:sg["col"] + sg["width"]]
 
 
+def gather_lane_blocks(D, segs):
+    """The gather-rows kernel's addressing, replayed per 16-byte destination
+    block: (destination offset, bytes, [(segment, source byte offset, bytes)]).
+    Waves of 64 blocks place their span the way the kernel does (the segment
+    holding the wave's first byte and the next one, wrapping to the next row's
+    first segment), and every block reads inside its segments' rows."""
+    W, rows, nseg = D["run_bytes"], D["extent"][0], D["extent"][1]
+    S = segs[D["src_ptr"]:D["src_ptr"] + nseg]
+    band = rows * W
+    out = []
+    for a_w in range(0, band, 1024):
+        row_w, col_w = divmod(a_w, W)
+        assert magic_div(a_w, *D["magic"][0]) == row_w
+        i0 = max(i for i in range(nseg) if S[i]["col"] <= col_w)
+        if D["row_items"] == 1:  # the kernel's lookup, read the way it reads it, gives the same segment
+            raw = np.array([D["src_offset"], D["dst_offset"], *D["src_stride"], *D["dst_stride"]],
+                           dtype=np.int64).view(np.uint32)         # descriptor words 0 .. 15
+            w = col_w >> 11
+            word = int(raw[w if w < 2 else w + 2])
+            e = word >> 16 if col_w & 1024 else word & 0xFFFF
+            assert (e & 63) + (1 if (e >> 6) and (col_w & 1023) >= (e >> 6) else 0) == i0, (D, a_w)
+        wrap = i0 + 1 == nseg
+        s0, s1 = S[i0], S[0 if wrap else i0 + 1]
+        B1 = s0["col"] + s0["width"]
+        E1 = W + s1["width"] if wrap else s1["col"] + s1["width"]
+        for lane in range(64):
+            pos, a = col_w + 16 * lane, a_w + 16 * lane
+            n = max(0, min(16, band - a))
+            if n == 0:
+                continue
+            seg, row, start, end = (s1, row_w + 1 if wrap else row_w, W if wrap else s1["col"], E1) \
+                if pos >= B1 else (s0, row_w, s0["col"], B1)
+            at = min(pos, end - 16)
+            assert start <= at and at + 16 <= end, (D, a)      # the 16-byte load stays in the row
+            L1 = min(pos + n, end) - pos
+            parts = [(seg, seg["offset"] + row * seg["row_stride"] + (pos - start), L1)]
+            if L1 < n:
+                assert pos < B1 and n - L1 <= 16
+                r1 = row_w + 1 if wrap else row_w
+                parts.append((s1, s1["offset"] + r1 * s1["row_stride"], n - L1))
+            out.append((D["dst_offset"] + a, n, parts))
+    return out
+
+
+def _run_gather_rows(D, segs, refs, srcs_flat, dsts_flat):
+    """A gather-rows band block by block, as the kernel addresses it; also
+    checks that the segments tile the row."""
+    W, nseg = D["run_bytes"], D["extent"][1]
+    S = segs[D["src_ptr"]:D["src_ptr"] + nseg]
+    cover = np.zeros(W, dtype=np.int32)
+    for sg in S:
+        assert sg["fanout"] == 0 and sg["width"] >= 1024
+        cover[sg["col"]:sg["col"] + sg["width"]] += 1
+    assert (cover == 1).all()
+    blocks = gather_lane_blocks(D, segs)
+    assert sum(n for _, n, _ in blocks) == D["extent"][0] * W
+    for d_off, n, parts in blocks:
+        data = np.concatenate([srcs_flat[sg["ptr"]][o:o + k] for sg, o, k in parts])
+        assert len(data) == n
+        for r in range(D["fanout"]):
+            dsts_flat[refs[D["dst_ref_begin"] + r]][d_off:d_off + n] = data
+
+
 def shard_bytes(plan: Plan):
     """Bytes of every shard, in the src / dst pointer-array order of execute."""
     sb, db = [], []
@@ -260,6 +326,29 @@ def assert_descriptors_in_bounds(plan: Plan):
     segs = R.reshard_plan_segments(plan.handle)
     for D in descs:
         ext = D["extent"]
+        if D["mode"] == R.DESC_GATHER_ROWS:
+            rows, nseg, W = ext[0], ext[1], D["run_bytes"]
+            assert rows >= 1 and nseg >= 1 and rows * W < 2 ** 31 and D["dst_offset"] >= 0
+            # the segment lookup the kernel reads: the segment holding each KiB's
+            # first byte and where inside the KiB the next one starts
+            lut = np.array([D["src_offset"], *D["src_stride"], *D["dst_stride"]], dtype=np.int64).view(np.uint16)
+            S = segs[D["src_ptr"]:D["src_ptr"] + nseg]
+            if D["row_items"] == 1:
+                assert W <= 28 * 1024 and nseg <= 64
+                for k in range(-(-W // 1024)):
+                    c = 1024 * k
+                    i = max(j for j in range(nseg) if S[j]["col"] <= c)
+                    nxt = [S[j]["col"] for j in range(nseg) if c < S[j]["col"] < c + 1024]
+                    assert len(nxt) <= 1
+                    assert lut[k] == i | ((nxt[0] - c if nxt else 0) << 6), (D, k)
+            else:
+                assert D["row_items"] == 0 and (W > 28 * 1024 or nseg > 64)
+            for sg in segs[D["src_ptr"]:D["src_ptr"] + nseg]:
+                assert sg["offset"] >= 0 and sg["row_stride"] >= sg["width"] >= 1024
+                assert sg["offset"] + (rows - 1) * sg["row_stride"] + sg["width"] <= sb[sg["ptr"]], sg
+            for r in range(D["fanout"]):
+                assert D["dst_offset"] + rows * W <= db[refs[D["dst_ref_begin"] + r]], D
+            continue
         if D["mode"] == R.DESC_WINDOW:
             rows, per_tile, pitch, width = ext[0], ext[1], D["row_items"], D["run_bytes"]
             assert rows >= 1 and per_tile >= 1 and pitch % 16 == 0 and pitch >= width

@@ -114,7 +114,9 @@ def test_misaligned_shard_pointers(misalign):
                                                 "runs_scatter_rep", "runs_gather", "runs64_scatter_rep",
                                                 "runs64_gather", "bands16_rep", "bands16_gather", "runs32_scatter_rep",
                                                 "runs32_gather", "octets_gather", "octets_scatter_rep", "bands16_96",
-                                                "bands16_80_rep", "pairs_gather", "pairs_rep", "narrow_8byte_rows")]
+                                                "bands16_80_rep", "pairs_gather", "pairs_rep", "narrow_8byte_rows",
+                                                "gather_uneven", "gather_fanout", "gather_rep_src",
+                                                "gather_row_cuts")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 
@@ -541,8 +543,9 @@ def test_graph_capture_refused_for_pointer_table_plans():
 
 def _mixed_kind_specs():
     """A batch that mixes descriptor kinds: 16-byte items of a 32 MiB projection,
-    64-byte run bands of 64 MiB of narrow columns, destination chunks (two
-    tensors) and a small band of 2-byte column runs."""
+    64-byte run bands of 64 MiB of narrow columns, destination chunks, a small
+    band of 2-byte column runs and gather-rows bands (8002-byte rows from three
+    column strips)."""
     small = {s.name: s for s in small_specs()}
     return [T("mix_rows", (4096, 4096), torch.bfloat16, (4,), (0,), (2, 2), (RR, 1)),
             W.narrow_columns_64b_tp8(1 << 20).tensors[0],
@@ -551,12 +554,14 @@ def _mixed_kind_specs():
 
 def test_mixed_kinds_one_launch_per_group():
     """The descriptors that are not bands share one launch, and each band kind
-    (64-byte run bands, 2-byte column runs) runs in a launch of its own build;
-    bit-exact.  Items with chunks, or one band kind alone, stay one launch."""
+    (64-byte run bands, 2-byte column runs, gather rows) runs in a launch of its
+    own build; bit-exact.  Items with chunks, or one band kind alone, stay one
+    launch."""
     specs = _mixed_kind_specs()
-    assert run_parity(specs, "raw", 12)["n_launches"] == 3
+    assert run_parity(specs, "raw", 12)["n_launches"] == 4
     assert run_parity([specs[1]], "raw", 13)["n_launches"] == 1
-    assert run_parity([specs[0], specs[2], specs[4]], "raw", 15)["n_launches"] == 1
+    assert run_parity([specs[0], specs[2]], "raw", 15)["n_launches"] == 1
+    assert run_parity([specs[0], specs[2], specs[4]], "raw", 15)["n_launches"] == 2
     assert run_parity([specs[1], specs[3]], "raw", 16)["n_launches"] == 2
     # a plan smaller than one pass over the chip is split the same way
     small = [W.ffn_up(1024, 1024).tensors[0], W.narrow_columns_64b_tp8(1 << 14).tensors[0]]
@@ -570,7 +575,7 @@ def test_mixed_kinds_with_pointer_table():
     spec = {s.name: s for s in small_specs()}["narrow_scatter_rep"]
     specs = _mixed_kind_specs() + [spec] * 12
     st = run_parity(specs, "raw", 14, executes=2)
-    assert st["n_src_ptrs"] + st["n_dst_ptrs"] > 120 and st["n_launches"] == 4  # + the quad row bands
+    assert st["n_src_ptrs"] + st["n_dst_ptrs"] > 120 and st["n_launches"] == 5  # + the quad row bands
 
 
 def test_mixed_kinds_graph_capture_replays():
@@ -582,7 +587,7 @@ def test_mixed_kinds_graph_capture_replays():
     with Plan(specs) as plan:
         stream = torch.cuda.Stream()
         R.reshard_plan_upload(plan.handle, stream.cuda_stream)
-        assert plan.stats()["n_launches"] == 3
+        assert plan.stats()["n_launches"] == 4
         sboxes = [oracle_boxes(s.shape, s.src_mesh, s.src_placements) for s in specs]
         srcs = [[p.cuda() for p in W.cut(W.make_global(s, "raw", 0, t), b)] for t, (s, b) in
                 enumerate(zip(specs, sboxes))]

@@ -110,6 +110,19 @@ def small_specs():
         T("strips_nine", (20, 333), torch.float32, (9,), (1,), (2,), (0,)),
         T("strips_mid_split", (6, 10, 301), torch.bfloat16, (2, 3), (1, 2), (3,), (2,)),
         T("narrow_wide_rows", (5, 4201), torch.float32, (4,), (1,), (2,), (1,)),
+        # gather-rows bands (whole destination rows from source column strips of
+        # at least 1 KiB that meet off the 16-byte grid): ragged nested split,
+        # destination replicas, source replicas, row cuts inside destination
+        # shards (bands that start mid-shard), rows that end inside a wave, a
+        # split middle dim, and strips of exactly 1 KiB
+        T("gather_uneven", (301, 1543), torch.float32, (3, 2), (1, 1), (7,), (0,)),
+        T("gather_fanout", (256, 1030), torch.bfloat16, (2,), (1,), (2, 3), (RR, 0)),
+        T("gather_rep_src", (100, 2049), torch.uint8, (2, 2), (RR, 1), (3,), (0,)),
+        T("gather_row_cuts", (500, 1031), torch.float32, (3, 2), (0, 1), (4,), (0,)),
+        T("gather_short_rows", (77, 1545), torch.uint8, (3,), (1,), (5,), (0,)),
+        T("gather_mid_dim", (6, 4, 2051), torch.bfloat16, (2, 2), (0, 2), (3,), (0,)),
+        T("gather_1k", (129, 2049), torch.uint8, (2,), (1,), (2,), (0,)),
+        T("gather_17_strips", (40, 4384), torch.float32, (17,), (1,), (3,), (0,)),  # past the 14 column slots
         # converting reshards: ragged rows (not a multiple of 8 elements), fan-out,
         # nesting, peeled outer dims, empty shards
         T("conv_f32_bf16", (112, 64), torch.float32, (4,), (0,), (2, 2), (RR, 1), torch.bfloat16),
@@ -458,6 +471,53 @@ def test_replan_after_rank_loss():
             plan.close()
 
 
+def test_gather_rows_selection():
+    """The uneven fp32 split runs as one gather-rows band per destination shard
+    (six source segments each); strips narrower than 1 KiB, and 16-byte aligned
+    strips, keep the per-piece descriptors."""
+    with Plan(W.uneven().tensors) as plan:
+        descs, _ = R.reshard_plan_descriptors(plan.handle)
+        segs = R.reshard_plan_segments(plan.handle)
+        assert [d["mode"] for d in descs] == [R.DESC_GATHER_ROWS] * 7
+        assert [d["extent"][:2] for d in descs] == [[715, 6]] * 6 + [[710, 6]]
+        assert all(d["dst_offset"] == 0 and d["run_bytes"] == 3001 * 4 for d in descs)
+        assert [s["width"] for s in segs[:6]] == [2004, 2000, 2004, 2000, 2000, 1996]
+        assert [s["col"] for s in segs[:6]] == [0, 2004, 4004, 6008, 8008, 10008]
+    with Plan(W.uneven(500, 301).tensors) as plan:     # 500-byte strips: chunks
+        assert {d["mode"] for d in R.reshard_plan_descriptors(plan.handle)[0]} == {R.DESC_DST_CHUNKS}
+    with Plan(W.uneven(5000, 3072).tensors) as plan:   # 16-byte aligned strips: items
+        assert {d["mode"] for d in R.reshard_plan_descriptors(plan.handle)[0]} == {R.DESC_ITEMS}
+    spec = {s.name: s for s in small_specs()}["gather_row_cuts"]
+    with Plan([spec]) as plan:                         # bands cut where source row boxes end
+        descs, _ = R.reshard_plan_descriptors(plan.handle)
+        assert {d["mode"] for d in descs} == {R.DESC_GATHER_ROWS} and len(descs) == 6
+        assert any(d["dst_offset"] > 0 for d in descs)
+
+
+def test_gather_rows_long_band_is_split():
+    """Bands longer than the kernel's 31-bit byte index are split by rows; the
+    pieces still cover every row once (checked on the descriptors, no data)."""
+    spec = T("long", (600000, 4099), torch.float32, (2,), (1,), (3,), (0,))
+    with Plan([spec]) as plan:
+        descs, _ = R.reshard_plan_descriptors(plan.handle)
+        segs = R.reshard_plan_segments(plan.handle)
+        assert {d["mode"] for d in descs} == {R.DESC_GATHER_ROWS}
+        W_ = 4099 * 4
+        for dst in range(3):
+            mine = sorted((d["dst_offset"], d["extent"][0]) for d in descs
+                          if R.reshard_plan_descriptors(plan.handle)[1][d["dst_ref_begin"]] == dst)
+            at = 0
+            for off, rows in mine:
+                assert off == at * W_ and rows * W_ < 2 ** 31
+                at += rows
+            assert at == 200000
+        for d in descs:
+            first = d["src_ptr"]
+            rows = d["extent"][0]
+            for sg in segs[first:first + d["extent"][1]]:
+                assert sg["offset"] % sg["row_stride"] == 0  # starts at a row of the source strip
+
+
 def test_dim_merging():
     """Contiguous dims merge into one run; strided dims stay outer dims."""
     with Plan(W.ffn_refit(1, 4096, 14336).tensors) as plan:
@@ -502,6 +562,9 @@ def test_magic_constants_exact():
     for d in descs:
         if d["mode"] == R.DESC_WINDOW:  # windows divide nothing
             continue
+        if d["mode"] == R.DESC_GATHER_ROWS:  # gather-rows bands divide by the row width only
+            divisors[d["run_bytes"]] = tuple(d["magic"][0])
+            continue
         divisors[d["row_items"]] = tuple(d["magic"][0])
         divisors[d["extent"][2]] = tuple(d["magic"][1])
         divisors[d["extent"][1]] = tuple(d["magic"][2])
@@ -513,8 +576,10 @@ def test_magic_constants_exact():
 
 
 def test_descriptor_modes():
-    """16-byte aligned rows copy as 16-byte items; long misaligned rows as
-    destination-aligned 16-byte chunks; short misaligned rows item by item;
+    """16-byte aligned rows copy as 16-byte items; whole destination rows from
+    misaligned source strips of at least 1 KiB as gather-rows bands; other long
+    misaligned rows as destination-aligned 16-byte chunks; short misaligned rows
+    item by item;
     narrow rows of a 2-d view through windows, unless the rows are wider than a
     window."""
     def modes(specs):
@@ -522,7 +587,8 @@ def test_descriptor_modes():
             return {(d["mode"], d["unit"]) for d in R.reshard_plan_descriptors(plan.handle)[0]}
     small = {s.name: s for s in small_specs()}
     assert modes(W.ffn_up().tensors) == {(R.DESC_ITEMS, 16)}
-    assert modes(W.uneven().tensors) == {(R.DESC_DST_CHUNKS, 4)}       # 12004-byte destination rows
+    assert modes(W.uneven().tensors) == {(R.DESC_GATHER_ROWS, 4)}      # 12004-byte rows of ~2000-byte strips
+    assert modes(W.uneven(500, 301).tensors) == {(R.DESC_DST_CHUNKS, 4)}  # strips narrower than 1 KiB
     assert {m for m, _ in modes(W.worked_example_8x8().tensors)} == {R.DESC_WINDOW}  # 4-byte rows
     for name in ("strips_row_cuts", "strips_fanout", "strips_rep_src", "strips_nine", "strips_mid_split"):
         assert modes([small[name]]) == {(R.DESC_DST_CHUNKS, 4 if small[name].dtype == torch.float32 else 2)}, name
