@@ -28,9 +28,20 @@ constexpr uint32_t kAllAligned16 = 1;  // every shard pointer of this execute is
 // (and their window segments).
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs);
 
+// The kernel variant that moves RESHARD_DESC_GATHER_ROWS bands.
+int kernel_kind_gather_rows();
+
 // Workgroups of one launch at most: a dispatch counts its work-items in 32
 // bits.  A multiple of kXcds, so that every launch starts on XCD 0's turn.
 constexpr uint32_t kMaxLaunchBlocks = (0xffffffffu / 256u) & ~(kXcds - 1);
+
+// Descriptors of one launch that all span `tiles` tiles (the last ones may
+// leave some of theirs idle): tile t belongs to descriptor t / tiles, found with
+// the multiplier (m, s) and no table load.  tiles = 0: the tiles are looked up.
+// Only the gather-rows build reads it.
+struct TileStride {
+  uint32_t tiles = 0, m = 0, s = 0;
+};
 
 // Variant `kind` over workgroups [0, n_wg) on `stream`, as one launch, or as
 // several back-to-back launches of at most kMaxLaunchBlocks workgroups each
@@ -39,6 +50,6 @@ constexpr uint32_t kMaxLaunchBlocks = (0xffffffffu / 256u) & ~(kXcds - 1);
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,
                        uint32_t n_desc, const uint32_t* tile_begin, const uint32_t* refs,
                        const reshard_segment_t* segs, const void* const* table, const KargPtrs& karg,
-                       uint32_t n_tiles, uint32_t per_xcd, uint32_t flags);
+                       uint32_t n_tiles, uint32_t per_xcd, uint32_t flags, TileStride stride);
 
 }  // namespace rs

@@ -12,6 +12,7 @@
 // through integer registers, so the copy is bit-exact for every dtype.
 #include "kernel.h"
 
+#include <cstddef>
 #include <cstdint>
 #include <vector>
 
@@ -1440,27 +1441,40 @@ __device__ __forceinline__ u32x4 low_bytes_mask(uint32_t n) {
   return m;
 }
 
+// Field words of a descriptor read as sixteen-word vectors (one 64-byte
+// scalar load each), and of a segment as an eight-word one.
+__device__ __forceinline__ uint64_t word64(uint32_t lo, uint32_t hi) { return uint64_t(lo) | (uint64_t(hi) << 32); }
+
 template <class Sh>
 __device__ __forceinline__ void gather_rows(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
                                             const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
-  const uint32_t W = D.run_bytes, nseg = D.extent[1];
-  const uint32_t band = D.extent[0] * W;  // < 2^31 (the planner splits longer bands)
+  // Every scalar load is issued before the first branch: the descriptor (two
+  // 64-byte loads), the lookup word, both segments, then both pointers.  The
+  // loads stay inside the band's tables even for a wave past the band's end.
+  static_assert(offsetof(reshard_descriptor_t, dst_offset) == 8 && offsetof(reshard_descriptor_t, run_bytes) == 76 &&
+                    offsetof(reshard_descriptor_t, extent) == 64 && offsetof(reshard_descriptor_t, row_items) == 80 &&
+                    offsetof(reshard_descriptor_t, src_ptr) == 88 && offsetof(reshard_descriptor_t, dst_ref_begin) == 92 &&
+                    offsetof(reshard_descriptor_t, fanout) == 96 && offsetof(reshard_descriptor_t, magic) == 100,
+                "descriptor word layout");
+  const u32x16 d0 = reinterpret_cast<const u32x16*>(&D)[0];
+  const u32x16 d1 = reinterpret_cast<const u32x16*>(&D)[1];
+  const uint32_t rows = d1[0], nseg = d1[1], W = d1[3], lut_ok = d1[4];
+  const uint32_t src_ptr = d1[6], ref_begin = d1[7], fanout = d1[8], magic_m = d1[9], magic_s = d1[10];
+  const uint64_t dst_offset = word64(d0[2], d0[3]);
+  const uint32_t band = rows * W;  // < 2^31 (the planner splits longer bands)
   const uint32_t wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const uint32_t a_w = tile * rs::kGatherTileBytes + wave * 1024u;
-  if (a_w >= band) return;
-  const uint32_t row_w = div_magic(a_w, D.magic[0][0], D.magic[0][1]);
-  const uint32_t col_w = a_w - row_w * W;
-  const reshard_segment_t* __restrict__ S = segs + D.src_ptr;
+  const uint32_t row_w = div_magic(a_w, magic_m, magic_s);
+  const uint32_t col_w = a_w - row_w * W;  // < W: the lookup index is in range even past the band
+  const reshard_segment_t* __restrict__ S = segs + src_ptr;
   // the last segment whose column is <= col_w: one entry of the descriptor's
-  // lookup (src_offset and the strides: a 16-bit entry per KiB of row holding
-  // the segment at the KiB's start and where, inside it, the next one begins),
-  // or a search over the segments for rows without one
+  // lookup (a 16-bit entry per KiB of row: the segment at the KiB's start and
+  // where, inside it, the next one begins; its words 0-1 sit in src_offset,
+  // 2-13 in the strides, after dst_offset), or a search for rows without one
   uint32_t i0 = 0;
-  if (D.row_items) {
-    // the entries' words: 0 and 1 in src_offset (bytes 0-7 of the descriptor),
-    // 2 .. 13 in src_stride and dst_stride (bytes 16-63); dst_offset sits between
+  if (lut_ok) {
     const uint32_t w = col_w >> 11;
-    const uint32_t word = reinterpret_cast<const uint32_t*>(&D)[w < 2 ? w : w + 2];
+    const uint32_t word = w < 2 ? d0[w] : (w < 14 ? d0[w + 2] : 0u);
     const uint32_t e = (col_w & 1024u) ? word >> 16 : word & 0xffffu;
     const uint32_t split = e >> 6;
     i0 = (e & 63u) + (split != 0 && (col_w & 1023u) >= split ? 1u : 0u);
@@ -1471,13 +1485,24 @@ __device__ __forceinline__ void gather_rows(const reshard_descriptor_t& D, const
       if (S[mid].col <= col_w) i0 = mid; else hi = mid;
     }
   }
+  // segments i0 and i0 + 1 in one 64-byte load (the table holds one padding
+  // segment after the last), and segment 0 for a wave whose span wraps to the
+  // next row
   const bool wrap = i0 + 1 == nseg;
-  const reshard_segment_t s0 = S[i0], s1 = S[wrap ? 0u : i0 + 1];
-  const uint32_t B1 = s0.col + s0.width;                         // end of segment 0
-  const uint32_t E1 = wrap ? W + s1.width : s1.col + s1.width;   // end of segment 1
-  const uint64_t base0 = sh.ptr(s0.ptr) + uint64_t(s0.offset) + uint64_t(row_w) * uint64_t(s0.row_stride) - s0.col;
-  const uint64_t base1 = sh.ptr(s1.ptr) + uint64_t(s1.offset) +
-                         uint64_t(wrap ? row_w + 1 : row_w) * uint64_t(s1.row_stride) - (wrap ? W : s1.col);
+  const u32x16 g01 = *reinterpret_cast<const u32x16*>(S + i0);
+  const u32x8 gz = *reinterpret_cast<const u32x8*>(S);
+  const u32x8 g0 = g01.lo;
+  const u32x8 g1 = wrap ? gz : g01.hi;
+  // segment words: 0-1 offset, 2-3 row_stride, 4 col, 5 width, 6 ptr
+  const uint64_t p0 = sh.ptr(g0[6]), p1 = sh.ptr(g1[6]);
+  asm volatile("" ::"s"(p0), "s"(p1));  // both pointer loads in flight together, not one sunk past the return
+  if (a_w >= band) return;
+  const uint32_t c0 = g0[4], c1 = g1[4];
+  const uint32_t B1 = c0 + g0[5];                         // end of segment 0
+  const uint32_t E1 = wrap ? W + g1[5] : c1 + g1[5];      // end of segment 1
+  const uint64_t base0 = p0 + word64(g0[0], g0[1]) + uint64_t(row_w) * word64(g0[2], g0[3]) - c0;
+  const uint64_t base1 = p1 + word64(g1[0], g1[1]) +
+                         uint64_t(wrap ? row_w + 1 : row_w) * word64(g1[2], g1[3]) - (wrap ? W : c1);
   const uint32_t lane16 = 16u * (threadIdx.x & 63u);
   const uint32_t pos = col_w + lane16;
   const uint32_t left = band - a_w;
@@ -1506,9 +1531,9 @@ __device__ __forceinline__ void gather_rows(const reshard_descriptor_t& D, const
     const u32x4 y = shift_left_bytes(v2, L1);
     x = (x & m) | (y & ~m);
   }
-  const uint64_t off = uint64_t(D.dst_offset) + a_w + lane16;
-  for (uint32_t r = 0; r < D.fanout; ++r) {
-    const uintptr_t d = sh.ptr(refs[D.dst_ref_begin + r]) + off;
+  const uint64_t off = dst_offset + a_w + lane16;
+  for (uint32_t r = 0; r < fanout; ++r) {
+    const uintptr_t d = sh.ptr(refs[ref_begin + r]) + off;
     if (n == 16) __builtin_nontemporal_store(x, as_global<u32x4_u1>(d));
     else store_head_bytes(d, x, n);
   }
@@ -1544,7 +1569,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     const reshard_descriptor_t* __restrict__ descs, uint32_t n_desc,
     const uint32_t* __restrict__ tile_begin, const uint32_t* __restrict__ refs,
     const reshard_segment_t* __restrict__ segs, const void* const* __restrict__ table, KargPtrs karg,
-    uint32_t n_tiles, uint32_t per_xcd, uint32_t flags, uint32_t block_base) {
+    uint32_t n_tiles, uint32_t per_xcd, uint32_t flags, uint32_t block_base, TileStride stride) {
   constexpr int kKind = kVariant % kKindAligned;
   constexpr bool kAligned = kVariant >= kKindAligned;
   // Block b of the plan (block_base + blockIdx.x: a plan larger than one
@@ -1556,6 +1581,18 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t b = block_base + blockIdx.x;
   const uint32_t kx = b / kXcds;
   const uint32_t t = per_xcd == 0 ? b : ((kx / kXcdGroup) * kXcds + b % kXcds) * kXcdGroup + kx % kXcdGroup;
+  if constexpr (kKind == kKindGatherRows) {
+    if (stride.tiles) {
+      // every band of the launch spans stride.tiles tiles: the band is a
+      // division away, and a surplus block reads band 0's tables (in bounds)
+      // and returns once its loads are issued
+      const bool live = t < n_tiles;
+      const uint32_t lo = live ? div_magic(t, stride.m, stride.s) : 0u;
+      const Shards<kKarg> gsh{table, &karg, refs};
+      gather_rows(descs[lo], segs, refs, gsh, live ? t - lo * stride.tiles : stride.tiles);
+      return;
+    }
+  }
   if (t >= n_tiles) return;
   // the descriptor of tile t: the last one whose first tile is <= t.  The
   // gather-rows build reads the tile-group lookup behind tile_begin (one load;
@@ -1694,11 +1731,11 @@ template <bool kKarg, int kVariant>
 hipError_t launch_kind(uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
                        const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
                        const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
-                       uint32_t flags) {
+                       uint32_t flags, TileStride stride) {
   for (uint32_t base = 0; base < n_wg; base += kMaxLaunchBlocks) {
     const uint32_t grid = n_wg - base < kMaxLaunchBlocks ? n_wg - base : kMaxLaunchBlocks;
     hipLaunchKernelGGL((reshard_copy_kernel<kKarg, kVariant>), dim3(grid), dim3(kBlock), 0, stream, descs,
-                       n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags, base);
+                       n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags, base, stride);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
@@ -1709,10 +1746,11 @@ template <bool kKarg>
 hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
                   const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
                   const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
-                  uint32_t flags) {
+                  uint32_t flags, TileStride stride) {
   const bool aligned = (flags & kAllAligned16) != 0;
 #define RS_LAUNCH(V) \
-  launch_kind<kKarg, V>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags)
+  launch_kind<kKarg, V>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags, \
+                        stride)
   switch (kind) {
     case kKindItems16:  // (an aligned-only build of this one measured slower on long copies)
       return RS_LAUNCH(kKindItems16);
@@ -1816,6 +1854,8 @@ bool runs64_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
 
 }  // namespace
 
+int kernel_kind_gather_rows() { return kKindGatherRows; }
+
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
   bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, bands16 = true, runs32 = true;
@@ -1844,12 +1884,12 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,
                        uint32_t n_desc, const uint32_t* tile_begin, const uint32_t* refs,
                        const reshard_segment_t* segs, const void* const* table, const KargPtrs& karg,
-                       uint32_t n_tiles, uint32_t per_xcd, uint32_t flags) {
+                       uint32_t n_tiles, uint32_t per_xcd, uint32_t flags, TileStride stride) {
   if (table)
     return launch<false>(kind, n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles,
-                         per_xcd, flags);
+                         per_xcd, flags, stride);
   return launch<true>(kind, n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd,
-                      flags);
+                      flags, stride);
 }
 
 }  // namespace rs

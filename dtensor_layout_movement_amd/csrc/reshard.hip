@@ -52,6 +52,7 @@ struct reshard_plan_s {
     uint32_t n_tiles = 0;
     uint32_t per_xcd = 0;  // blocks per XCD, a multiple of rs::kXcdGroup (0: one block per tile)
     uint32_t n_wg = 0;     // grid: rs::kXcds * per_xcd blocks (surplus ones exit), else n_tiles
+    rs::TileStride stride; // gather-rows launches whose bands all span stride.tiles tiles
     size_t desc_off = 0;   // the group's descriptors in the image
     size_t tb_off = 0;     // its first tile of each, from 0; n_desc + 1 entries
   };
@@ -138,7 +139,9 @@ void build_image_locked(reshard_plan_s* p) {
   const size_t refs_off = align_up(desc_bytes, 256);
   const size_t tiles_off = align_up(refs_off + H.refs.size() * sizeof(uint32_t), 256);
   const size_t segs_off = align_up(tiles_off + n_tb * sizeof(uint32_t), 256);
-  const size_t total = align_up(segs_off + H.segs.size() * sizeof(reshard_segment_t), 256);
+  // one zero segment after the last: a gather-rows wave reads segments i and
+  // i + 1 together
+  const size_t total = align_up(segs_off + (H.segs.size() + 1) * sizeof(reshard_segment_t), 256);
   std::vector<uint8_t> img(total, 0);
   reshard_descriptor_t* dd = reinterpret_cast<reshard_descriptor_t*>(img.data());
   uint32_t* tb = reinterpret_cast<uint32_t*>(img.data() + tiles_off);
@@ -149,9 +152,23 @@ void build_image_locked(reshard_plan_s* p) {
     L.kind = g.kind;
     L.n_desc = uint32_t(g.descs.size());
     L.n_tiles = uint32_t(g.tiles);
+    // Gather-rows bands of (nearly) one size take a common tile stride, so that
+    // a workgroup finds its band by a division instead of a table load: the
+    // shorter bands leave their last tiles idle (at most 1/16 more tiles).
+    if (g.kind == rs::kernel_kind_gather_rows()) {
+      uint64_t most = 0;
+      for (const uint32_t i : g.descs) most = std::max<uint64_t>(most, H.tile_begin[i + 1] - H.tile_begin[i]);
+      const uint64_t padded = most * g.descs.size();
+      if (padded < (uint64_t(1) << 31) && padded <= g.tiles + std::max<uint64_t>(64, g.tiles / 16)) {
+        L.stride.tiles = uint32_t(most);
+        rs::magic_u31(L.stride.tiles, &L.stride.m, &L.stride.s);
+        L.n_tiles = uint32_t(padded);
+      }
+    }
+    const uint64_t grid_tiles = L.n_tiles;
     // blocks per XCD, a whole number of tile groups; 0: too few tiles to group
-    const uint64_t per_xcd_min = (g.tiles + rs::kXcds - 1) / rs::kXcds;
-    L.per_xcd = g.tiles < uint64_t(rs::kXcds) * rs::kXcdGroup
+    const uint64_t per_xcd_min = (grid_tiles + rs::kXcds - 1) / rs::kXcds;
+    L.per_xcd = grid_tiles < uint64_t(rs::kXcds) * rs::kXcdGroup
                     ? 0u
                     : uint32_t((per_xcd_min + rs::kXcdGroup - 1) / rs::kXcdGroup * rs::kXcdGroup);
     L.n_wg = L.per_xcd ? L.per_xcd * rs::kXcds : L.n_tiles;
@@ -165,7 +182,7 @@ void build_image_locked(reshard_plan_s* p) {
       first += H.tile_begin[i + 1] - H.tile_begin[i];
     }
     tb[t++] = first;
-    rs::fill_tile_groups(local, L.n_desc, L.n_tiles, tb + t);
+    rs::fill_tile_groups(local, L.n_desc, uint32_t(g.tiles), tb + t);
     t += rs::tile_groups(g.tiles);
     launches.push_back(L);
   }
@@ -245,7 +262,7 @@ hipError_t launch_groups_at(const reshard_plan_s* p, const uint8_t* base, const 
     const hipError_t e =
         rs::launch_copy(L.kind, L.n_wg, stream, reinterpret_cast<const reshard_descriptor_t*>(base + L.desc_off),
                         L.n_desc, reinterpret_cast<const uint32_t*>(base + L.tb_off), refs, segs, table, karg,
-                        L.n_tiles, L.per_xcd, flags);
+                        L.n_tiles, L.per_xcd, flags, L.stride);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;
