@@ -556,6 +556,22 @@ def main() -> int:
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / n_dist
 
+    # context, and the size calibration of rocprofv3's FETCH_SIZE / WRITE_SIZE
+    # counters: a plain device copy (torch copy_) of half the algorithmic bytes
+    half = min(algo_bytes // 2, 1 << 30)
+    a = torch.empty(half, dtype=torch.uint8, device=dev)
+    b = torch.empty(half, dtype=torch.uint8, device=dev)
+    for _ in range(3):
+        b.copy_(a)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(20):
+        b.copy_(a)
+    c1.record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * half / (c0.elapsed_time(c1) / 20 * 1e-3) / 1e9
+    del a, b
+
     reference = comparator = two = mixed = None
     if not args.no_comparator:
         print("[bench] comparators", file=sys.stderr, flush=True)
@@ -618,6 +634,7 @@ def main() -> int:
                            "p50": round(per_launch[len(per_launch) // 2], 2),
                            "p90": round(per_launch[(9 * len(per_launch)) // 10], 2), "n": n_dist},
         "warm_same_buffers_gbps": round(algo_bytes / (warm_ms * 1e-3) / 1e9, 1),
+        "copy_reference": {"bytes_each_way": half, "gbps": round(copy_gbps, 1)},
         "contiguous_same_bytes": reference,
         "gather_then_slice_gpu": comparator,
         "two_stage_gpu": two,
