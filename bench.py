@@ -24,7 +24,11 @@ reshard's speed-up over it are reported as ``gather_then_slice_gpu``.
 
 ``contiguous_same_bytes`` is the same kernel moving the same bytes as one
 contiguous buffer with the same fan-out: the practical ceiling for the
-workload's read:write mix on this GPU.
+workload's read:write mix on this GPU.  ``copy_reference`` (per config:
+``torch_copy_half_bytes_gbps``) is the runtime's own device copy (torch
+``copy_``) of half the algorithmic bytes, rotated over buffer pairs the same
+way: the 1:1 read:write ceiling at that size, and the size calibration of the
+rocprofv3 byte counters.
 
 The two-stage transport of the pages (each destination box delivered once,
 split over its replicas, then assembled by every replica; pipelined over
@@ -465,6 +469,30 @@ def worked_example_row(torch, R, dev, stream, reps: int) -> dict:
             "closed_form": closed, "launches_per_step": row["launches_per_step"], "cpu_baseline": cpu}
 
 
+def torch_copy_reference(torch, dev, stream, algo_bytes: int, min_footprint_gb: float) -> dict:
+    """A plain device copy (torch copy_, the runtime's own blit kernel) of half
+    the algorithmic bytes, rotated over buffer pairs of at least
+    min_footprint_gb like the reshard: context for the read:write mix 1:1, and
+    the size calibration of rocprofv3's FETCH_SIZE / WRITE_SIZE counters."""
+    half = min(algo_bytes // 2, 1 << 30)
+    n_pairs = max(2, min(16, int(-(-min_footprint_gb * 1e9 // (2 * half)))))
+    pairs = [(torch.empty(half, dtype=torch.uint8, device=dev), torch.empty(half, dtype=torch.uint8, device=dev))
+             for _ in range(n_pairs)]
+    for i in range(3):
+        pairs[i % n_pairs][1].copy_(pairs[i % n_pairs][0])
+    n_copy = max(20, n_pairs)
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for i in range(n_copy):
+        pairs[i % n_pairs][1].copy_(pairs[i % n_pairs][0])
+    c1.record(stream)
+    torch.cuda.synchronize()
+    ms = c0.elapsed_time(c1) / n_copy
+    del pairs
+    torch.cuda.empty_cache()
+    return {"bytes_each_way": half, "gbps": round(2 * half / (ms * 1e-3) / 1e9, 1), "buffer_pairs_rotated": n_pairs}
+
+
 def config_row(torch, R, name, dev, stream, min_footprint_gb: float, cpu: bool) -> dict:
     """One configuration of the benchmark family, measured cold like the headline."""
     from dtensor_layout_movement_amd import workloads as W
@@ -477,6 +505,8 @@ def config_row(torch, R, name, dev, stream, min_footprint_gb: float, cpu: bool) 
     ref = contiguous_reference(torch, R, st, dev, stream, max(20, steps // 4), min_footprint_gb)
     if ref:
         row["contiguous_same_bytes_gbps"] = ref["gbps"]
+    row["torch_copy_half_bytes_gbps"] = torch_copy_reference(torch, dev, stream, row["algorithmic_bytes"],
+                                                             min_footprint_gb)["gbps"]
     if cpu:
         _, _, sp, dp = sets[0]
         R.reshard_execute(plan, sp, dp, stream.cuda_stream)
@@ -556,21 +586,7 @@ def main() -> int:
     torch.cuda.synchronize()
     warm_ms = w0.elapsed_time(w1) / n_dist
 
-    # context, and the size calibration of rocprofv3's FETCH_SIZE / WRITE_SIZE
-    # counters: a plain device copy (torch copy_) of half the algorithmic bytes
-    half = min(algo_bytes // 2, 1 << 30)
-    a = torch.empty(half, dtype=torch.uint8, device=dev)
-    b = torch.empty(half, dtype=torch.uint8, device=dev)
-    for _ in range(3):
-        b.copy_(a)
-    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    c0.record(stream)
-    for _ in range(20):
-        b.copy_(a)
-    c1.record(stream)
-    torch.cuda.synchronize()
-    copy_gbps = 2 * half / (c0.elapsed_time(c1) / 20 * 1e-3) / 1e9
-    del a, b
+    copy_ref = torch_copy_reference(torch, dev, stream, algo_bytes, args.min_footprint_gb)
 
     reference = comparator = two = mixed = None
     if not args.no_comparator:
@@ -634,7 +650,7 @@ def main() -> int:
                            "p50": round(per_launch[len(per_launch) // 2], 2),
                            "p90": round(per_launch[(9 * len(per_launch)) // 10], 2), "n": n_dist},
         "warm_same_buffers_gbps": round(algo_bytes / (warm_ms * 1e-3) / 1e9, 1),
-        "copy_reference": {"bytes_each_way": half, "gbps": round(copy_gbps, 1)},
+        "copy_reference": copy_ref,
         "contiguous_same_bytes": reference,
         "gather_then_slice_gpu": comparator,
         "two_stage_gpu": two,
