@@ -11,7 +11,10 @@ gather-then-slice scheme that the reshard write-ups give as the usual refit path
 problem" section): rebuild the global tensor from the source shards, then cut
 every destination shard out of it.  This module only marshals arguments.
 
-Placements are ints: ``-1`` is Replicate, ``k >= 0`` is Shard(k).
+Placements are ints: ``-1`` is Replicate, ``k >= 0`` is Shard(k).  Layouts with
+right-to-left (strided) nesting add one split factor per mesh dim (1 = plain):
+``shard_indices`` and ``reshard_indexed`` take them, on explicit per-dim index
+lists.
 """
 from __future__ import annotations
 
@@ -61,7 +64,14 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
                                    ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
     lib.oracle_convert.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p,
                                    ctypes.c_int64, ctypes.c_int]
-    for f in (lib.oracle_num_ranks, lib.oracle_shard_box, lib.oracle_reshard, lib.oracle_convert):
+    lib.oracle_shard_indices.argtypes = [ctypes.c_int, _I64P, ctypes.c_int, _I64P, _I32P, _I64P,
+                                         ctypes.c_int64, ctypes.c_int, _I64P, ctypes.c_int64, _I64P]
+    lib.oracle_reshard_indexed.argtypes = [ctypes.c_int, _I64P, ctypes.c_int64,
+                                           ctypes.c_int, _I64P, _I32P, _I64P, ctypes.POINTER(ctypes.c_void_p),
+                                           ctypes.c_int, _I64P, _I32P, _I64P, ctypes.POINTER(ctypes.c_void_p),
+                                           ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+    for f in (lib.oracle_num_ranks, lib.oracle_shard_box, lib.oracle_reshard, lib.oracle_convert,
+              lib.oracle_shard_indices, lib.oracle_reshard_indexed):
         f.restype = ctypes.c_int
     if path == _LIB_PATH:
         _lib = lib
@@ -131,6 +141,40 @@ def reshard(shape, elem_size, src_mesh, src_pl, src_bufs, dst_mesh, dst_pl, dst_
                             len(src_mesh), _i64(src_mesh), _i32(src_pl), srcs,
                             len(dst_mesh), _i64(dst_mesh), _i32(dst_pl), dsts,
                             _addr(global_out), int(check), int(threads))
+    if rc:
+        raise OracleError(rc)
+
+
+def shard_indices(shape, mesh, placements, split, rank, lib=None):
+    """Per tensor dim, the list of global indices ``rank`` holds, in local
+    order, under a layout whose mesh dims have split factors ``split`` (1 for a
+    plain Shard or Replicate).  The local shard is the row-major buffer over the
+    product of these lists."""
+    lib = lib or load()
+    out = []
+    for dim in range(len(shape)):
+        n = ctypes.c_int64(0)
+        buf = (ctypes.c_int64 * max(1, shape[dim]))()
+        rc = lib.oracle_shard_indices(len(shape), _i64(shape), len(mesh), _i64(mesh), _i32(placements),
+                                      _i64(split), rank, dim, buf, max(1, shape[dim]), ctypes.byref(n))
+        if rc:
+            raise OracleError(rc)
+        out.append(list(buf[:n.value]))
+    return out
+
+
+def reshard_indexed(shape, elem_size, src_mesh, src_pl, src_split, src_bufs, dst_mesh, dst_pl, dst_split,
+                    dst_bufs, global_out=None, check: bool = True, threads: int = 1, lib=None) -> None:
+    """Gather-then-slice over explicit index lists (layouts with split factors):
+    fill every ``dst_bufs[d]`` from ``src_bufs``.  Buffers as for ``reshard``;
+    a shard's buffer is row-major over its ``shard_indices`` lists."""
+    lib = lib or load()
+    srcs = (ctypes.c_void_p * max(1, len(src_bufs)))(*[_addr(b) for b in src_bufs])
+    dsts = (ctypes.c_void_p * max(1, len(dst_bufs)))(*[_addr(b) for b in dst_bufs])
+    rc = lib.oracle_reshard_indexed(len(shape), _i64(shape), elem_size,
+                                    len(src_mesh), _i64(src_mesh), _i32(src_pl), _i64(src_split), srcs,
+                                    len(dst_mesh), _i64(dst_mesh), _i32(dst_pl), _i64(dst_split), dsts,
+                                    _addr(global_out), int(check), int(threads))
     if rc:
         raise OracleError(rc)
 

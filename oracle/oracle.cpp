@@ -35,6 +35,11 @@
  * Element conversion (oracle_convert) serves a reshard whose destination dtype
  * differs from the source's; see the comment above that function.
  *
+ * Strided (right-to-left) nesting is a separate, plainer path: index_list and
+ * oracle_reshard_indexed keep every rank's shard as one explicit list of global
+ * indices per tensor dim and move element by element; see the comment above
+ * index_list.
+ *
  * Built with g++ (plain C++17, std::thread); no HIP.
  */
 #include <atomic>
@@ -115,6 +120,55 @@ bool box_empty(int ndim, const int64_t* lo, const int64_t* hi) {
   for (int k = 0; k < ndim; ++k)
     if (hi[k] <= lo[k]) return true;
   return false;
+}
+
+/*
+ * Strided nesting.  The reshard write-ups say only that the refit guide lists
+ * the supported layouts (news.bpdata.com write-up, "practical access and setup"
+ * section).  The reading taken is PyTorch DTensor's right-to-left placement
+ * (_StridedShard(k, split_factor)), which FSDP2 + TP use when the TP mesh dim
+ * splits a tensor dim before the FSDP mesh dim does.  At mesh dim m with split
+ * factor f (f = 1 is a plain Shard(k)), a rank's current list of global indices
+ * along dim k, of length n, is cut into f torch.chunk pieces (size ceil(n / f),
+ * the trailing ones short or missing); each piece is cut the same way into
+ * mesh[m] parts; the rank keeps part coord[m] of every piece, pieces in order.
+ * Mesh dims apply left to right, each to the list the previous ones left.
+ * The local shard is the row-major buffer over the product of the per-dim lists.
+ */
+std::vector<int64_t> index_list(const Layout& L, const int64_t* split, int64_t rank, int dim) {
+  int64_t coord[kMaxDims];
+  int64_t rest = rank;
+  for (int m = L.mesh_ndim; m-- > 0;) {  // the last mesh dim varies fastest
+    coord[m] = rest % L.mesh[m];
+    rest /= L.mesh[m];
+  }
+  std::vector<int64_t> cur;
+  for (int64_t i = 0; i < L.shape[dim]; ++i) cur.push_back(i);
+  for (int m = 0; m < L.mesh_ndim; ++m) {
+    if (L.placements[m] != dim) continue;
+    const int64_t n = (int64_t)cur.size();
+    const int64_t f = split[m];
+    const int64_t piece = (n + f - 1) / f;  // ceil(n / f)
+    std::vector<int64_t> kept;
+    for (int64_t j = 0; j < f; ++j) {
+      const int64_t start = j * piece;
+      if (start >= n) break;  // torch.chunk made fewer pieces: the rest are empty
+      const int64_t len = n - start < piece ? n - start : piece;
+      const int64_t part = (len + L.mesh[m] - 1) / L.mesh[m];  // ceil(len / mesh size)
+      for (int64_t p = coord[m] * part; p < (coord[m] + 1) * part && p < len; ++p)
+        kept.push_back(cur[start + p]);
+    }
+    cur = kept;
+  }
+  return cur;
+}
+
+bool split_ok(const Layout& L, const int64_t* split) {
+  for (int m = 0; m < L.mesh_ndim; ++m) {
+    if (split[m] < 1) return false;
+    if (split[m] > 1 && L.placements[m] == kReplicate) return false;
+  }
+  return true;
 }
 
 /* Run fn(row_begin, row_end) over [0, rows) split into `threads` contiguous parts. */
@@ -388,6 +442,157 @@ int oracle_reshard(int ndim, const int64_t* shape, int64_t elem_size,
     });
   }
 
+  std::free(count);
+  if (own_x) std::free(X);
+  return status;
+}
+
+/*
+ * Global indices along tensor dim `dim` that `rank` holds, in local order
+ * (index_list).  split[m] is the split factor of mesh dim m (1 = Shard or
+ * Replicate).  Writes min(capacity, count) of them to out and the count to *n.
+ */
+int oracle_shard_indices(int ndim, const int64_t* shape, int mesh_ndim, const int64_t* mesh,
+                         const int32_t* placements, const int64_t* split, int64_t rank, int dim,
+                         int64_t* out, int64_t capacity, int64_t* n) {
+  Layout L{ndim, shape, mesh_ndim, mesh, placements};
+  if (!layout_ok(L) || !split_ok(L, split) || rank < 0 || rank >= num_ranks(L) || dim < 0 || dim >= ndim)
+    return ORACLE_BAD_LAYOUT;
+  const std::vector<int64_t> v = index_list(L, split, rank, dim);
+  for (int64_t i = 0; i < (int64_t)v.size() && i < capacity; ++i) out[i] = v[i];
+  *n = (int64_t)v.size();
+  return ORACLE_OK;
+}
+
+/*
+ * Gather-then-slice of one tensor whose layouts may use strided nesting,
+ * element by element over explicit index lists (index_list): X[idx(s, l)] =
+ * src_shard[s][l] for every source rank s and local multi-index l, then
+ * dst_shard[d][l] = X[idx(d, l)].  Arguments as oracle_reshard, plus the split
+ * factors of each layout's mesh dims.  Checks as oracle_reshard.
+ */
+int oracle_reshard_indexed(int ndim, const int64_t* shape, int64_t elem_size,
+                           int src_mesh_ndim, const int64_t* src_mesh, const int32_t* src_pl,
+                           const int64_t* src_split, const void* const* src_bufs,
+                           int dst_mesh_ndim, const int64_t* dst_mesh, const int32_t* dst_pl,
+                           const int64_t* dst_split, void* const* dst_bufs,
+                           void* global_out, int check, int threads) {
+  Layout S{ndim, shape, src_mesh_ndim, src_mesh, src_pl};
+  Layout D{ndim, shape, dst_mesh_ndim, dst_mesh, dst_pl};
+  if (!layout_ok(S) || !layout_ok(D) || !split_ok(S, src_split) || !split_ok(D, dst_split) || elem_size < 1)
+    return ORACLE_BAD_LAYOUT;
+  if (threads < 1) threads = 1;
+  int64_t numel = 1;
+  for (int k = 0; k < ndim; ++k) numel *= shape[k];
+  const size_t es = (size_t)elem_size;
+  int64_t gstride[kMaxDims];  // row-major strides of the global tensor, elements
+  int64_t st = 1;
+  for (int k = ndim - 1; k >= 0; --k) {
+    gstride[k] = st;
+    st *= shape[k];
+  }
+  int64_t copies = 1;  // replicas of every element among the sources
+  for (int m = 0; m < S.mesh_ndim; ++m)
+    if (S.placements[m] == kReplicate) copies = copies * S.mesh[m];
+  if (check && copies > 254) check = 0;
+
+  unsigned char* X = (unsigned char*)global_out;
+  bool own_x = false;
+  if (X == nullptr && numel > 0) {
+    X = (unsigned char*)std::malloc((size_t)numel * es);
+    if (!X) return ORACLE_NO_MEMORY;
+    own_x = true;
+  }
+  unsigned char* count = nullptr;
+  if (check && numel > 0) {
+    count = (unsigned char*)std::calloc((size_t)numel, 1);
+    if (!count) {
+      if (own_x) std::free(X);
+      return ORACLE_NO_MEMORY;
+    }
+  }
+  int status = ORACLE_OK;
+
+  // Global element offset of local row `row` (row-major over every dim but the
+  // last) of a shard with index lists idx.
+  auto row_base = [&](const std::vector<std::vector<int64_t>>& idx, int64_t row) {
+    int64_t off = 0;
+    for (int k = ndim - 2; k >= 0; --k) {
+      const int64_t len = (int64_t)idx[k].size();
+      off += idx[k][row % len] * gstride[k];
+      row /= len;
+    }
+    return off;
+  };
+
+  // 1. Gather.
+  for (int64_t s = 0; s < num_ranks(S) && status == ORACLE_OK; ++s) {
+    std::vector<std::vector<int64_t>> idx(ndim);
+    int64_t local = 1;
+    for (int k = 0; k < ndim; ++k) {
+      idx[k] = index_list(S, src_split, s, k);
+      local *= (int64_t)idx[k].size();
+    }
+    if (local == 0) continue;
+    if (src_bufs[s] == nullptr) {
+      status = ORACLE_NULL_BUFFER;
+      break;
+    }
+    const std::vector<int64_t>& last = idx[ndim - 1];
+    const int64_t run = (int64_t)last.size();
+    const int64_t rows = local / run;
+    const unsigned char* shard = (const unsigned char*)src_bufs[s];
+    std::atomic<int> mismatch{0};
+    parallel_rows(rows, threads, [&](int64_t a, int64_t b) {
+      for (int64_t row = a; row < b; ++row) {
+        const int64_t base = row_base(idx, row);
+        for (int64_t j = 0; j < run; ++j) {
+          const int64_t g = base + last[j];
+          const unsigned char* from = shard + (size_t)(row * run + j) * es;
+          if (check && count[g] != 0) {
+            if (std::memcmp(X + (size_t)g * es, from, es) != 0) mismatch.store(1);
+          } else {
+            std::memcpy(X + (size_t)g * es, from, es);
+          }
+          if (check) count[g] += 1;
+        }
+      }
+    });
+    if (mismatch.load()) status = ORACLE_REPLICA_MISMATCH;
+  }
+  if (status == ORACLE_OK && check) {
+    for (int64_t i = 0; i < numel; ++i)
+      if (count[i] != (unsigned char)copies) {
+        status = ORACLE_COVERAGE_MISMATCH;
+        break;
+      }
+  }
+
+  // 2. Slice.
+  for (int64_t d = 0; d < num_ranks(D) && status == ORACLE_OK; ++d) {
+    std::vector<std::vector<int64_t>> idx(ndim);
+    int64_t local = 1;
+    for (int k = 0; k < ndim; ++k) {
+      idx[k] = index_list(D, dst_split, d, k);
+      local *= (int64_t)idx[k].size();
+    }
+    if (local == 0) continue;
+    if (dst_bufs[d] == nullptr) {
+      status = ORACLE_NULL_BUFFER;
+      break;
+    }
+    const std::vector<int64_t>& last = idx[ndim - 1];
+    const int64_t run = (int64_t)last.size();
+    const int64_t rows = local / run;
+    unsigned char* shard = (unsigned char*)dst_bufs[d];
+    parallel_rows(rows, threads, [&](int64_t a, int64_t b) {
+      for (int64_t row = a; row < b; ++row) {
+        const int64_t base = row_base(idx, row);
+        for (int64_t j = 0; j < run; ++j)
+          std::memcpy(shard + (size_t)(row * run + j) * es, X + (size_t)(base + last[j]) * es, es);
+      }
+    });
+  }
   std::free(count);
   if (own_x) std::free(X);
   return status;

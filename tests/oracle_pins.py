@@ -23,6 +23,18 @@ a mismatch.  What pins what:
   f32 step either side); widening over all 65536 patterns of each 16-bit format.
 * ``pin_convert_closed``   -- float conversion on hand-derived values: ties to
   even, the overflow threshold, subnormals, signed zero, NaN convention.
+* ``pin_strided_vs_dtensor`` -- strided (right-to-left) index lists against
+  PyTorch DTensor's own split routines (``Shard._split_tensor``,
+  ``_StridedShard._split_tensor`` and ``local_shard_size_and_offset``) replayed
+  mesh dim by mesh dim on index tensors, and its documented 8-row example.
+* ``pin_strided_closed``   -- the owner of every index under one strided mesh
+  dim by a closed form; split factor 1 against the (pinned) box function; the
+  defining identity: [StridedShard(d, n1), Shard(d)] on mesh (n0, n1) gives rank
+  (c0, c1) what plain nesting gives rank (c1, c0) on mesh (n1, n0), for every
+  evenly divisible size.
+* ``pin_end_to_end_strided`` -- whole indexed reshard against gathering the
+  global tensor through DTensor's replayed split (no oracle index arithmetic
+  on that side), plus its replica / coverage / layout checks.
 """
 from __future__ import annotations
 
@@ -406,9 +418,149 @@ def pin_convert_closed(lib):
     assert got.tolist() == [0x7FC02000, 0xFFC00000 | (0x155 << 13)], [hex(v) for v in got]
 
 
+# ------------------------------------------------------ strided nesting
+
+def dtensor_split_local(shape, mesh, placements, split, rank):
+    """The global flat indices held by ``rank``, as its local tensor, from
+    PyTorch DTensor's own split routines replayed mesh dim by mesh dim on an
+    index tensor (what distributing a tensor does on each mesh dim)."""
+    from torch.distributed.tensor.placement_types import Shard, _StridedShard
+    c = coords_of(rank, mesh)
+    t = torch.arange(int(np.prod(shape)), dtype=torch.int64).reshape(shape)
+    for m, (p, f) in enumerate(zip(placements, split)):
+        if p == W.R:
+            continue
+        pl = Shard(p) if f == 1 else _StridedShard(p, split_factor=f)
+        shards, _ = pl._split_tensor(t, mesh[m], with_padding=False, contiguous=True)
+        t = shards[c[m]]
+    return t
+
+
+def oracle_split_local(lib, shape, mesh, placements, split, rank):
+    """The same local tensor from the oracle's per-dim index lists."""
+    idx = oracle.shard_indices(list(shape), list(mesh), list(placements), list(split), rank, lib=lib)
+    if any(len(i) == 0 for i in idx):
+        return torch.empty([len(i) for i in idx], dtype=torch.int64)
+    flat = np.ravel_multi_index(np.ix_(*[np.array(i, dtype=np.int64) for i in idx]), shape)
+    return torch.from_numpy(np.ascontiguousarray(flat))
+
+
+def strided_layouts(rng, count):
+    """Small random layouts whose shard placements carry split factors 1..4."""
+    out = []
+    for _ in range(count):
+        nd = rng.randint(1, 3)
+        shape = tuple(rng.randint(0, 13) for _ in range(nd))
+        md = rng.randint(1, 3)
+        mesh = tuple(rng.randint(1, 4) for _ in range(md))
+        pl = tuple(rng.choice([W.R] + list(range(nd))) for _ in range(md))
+        split = tuple(1 if p == W.R else rng.choice([1, 1, 2, 3, 4]) for p in pl)
+        out.append((shape, mesh, pl, split))
+    return out
+
+
+def pin_strided_vs_dtensor(lib, count=600, seed=17):
+    # DTensor's documented example: 8 rows on a 2x2 mesh, [_StridedShard(0, 2), Shard(0)]
+    rows = [oracle.shard_indices([8], [2, 2], [0, 0], [2, 1], r, lib=lib)[0] for r in range(4)]
+    assert rows == [[0, 1], [4, 5], [2, 3], [6, 7]], rows
+    rng = random.Random(seed)
+    cases = strided_layouts(rng, count)
+    cases += [((8, 6), (2, 2), (0, 0), (2, 1)), ((14336, 8), (2, 4), (0, 0), (4, 1)),
+              ((9, 10), (2, 3), (1, 1), (3, 1)), ((11,), (3, 2, 2), (0, 0, 0), (2, 3, 1)),
+              ((7, 5), (2, 2), (0, 1), (3, 2)), ((5,), (4,), (0,), (3,)), ((0, 3), (2,), (0,), (2,))]
+    for shape, mesh, pl, split in cases:
+        for r in range(nranks(mesh)):
+            want = dtensor_split_local(shape, mesh, pl, split, r)
+            got = oracle_split_local(lib, shape, mesh, pl, split, r)
+            assert list(got.shape) == list(want.shape) and torch.equal(got, want), (shape, mesh, pl, split, r)
+    # single placements against DTensor's offset routine
+    from torch.distributed.tensor.placement_types import _StridedShard
+    for n in range(0, 30):
+        for f in range(1, 6):
+            for k in range(1, 6):
+                for c in range(k):
+                    size, offs = _StridedShard.local_shard_size_and_offset(
+                        _StridedShard(0, split_factor=f), n, k, c, False)
+                    got = oracle.shard_indices([n], [k], [0], [f], c, lib=lib)[0]
+                    assert got == list(offs) and len(got) == size, (n, f, k, c, got, offs)
+
+
+def pin_strided_closed(lib):
+    # owner of index i under one strided mesh dim (n indices, f pieces, k parts):
+    # piece j = i // ceil(n / f); inside it, part (i - j ceil(n/f)) // ceil(len_j / k)
+    for n in range(0, 41):
+        for f in range(1, 7):
+            for k in range(1, 6):
+                held = [oracle.shard_indices([n], [k], [0], [f], c, lib=lib)[0] for c in range(k)]
+                owner = {}
+                for c, lst in enumerate(held):
+                    assert lst == sorted(lst), (n, f, k, c)
+                    for i in lst:
+                        assert i not in owner, (n, f, k, i)
+                        owner[i] = c
+                p = -(-n // f) if n else 0
+                for i in range(n):
+                    j = i // p
+                    ln = min(p, n - j * p)
+                    assert owner.get(i) == (i - j * p) // -(-ln // k), (n, f, k, i)
+    # split factor 1 everywhere: the box function's intervals
+    rng = random.Random(23)
+    for shape, mesh, pl in small_layouts(rng, 400):
+        for r in range(nranks(mesh)):
+            lo, hi = oracle.shard_box(shape, mesh, pl, r, lib=lib)
+            idx = oracle.shard_indices(list(shape), list(mesh), list(pl), [1] * len(mesh), r, lib=lib)
+            assert idx == [list(range(a, b)) if b > a else [] for a, b in zip(lo, hi)], (shape, mesh, pl, r)
+    # right-to-left identity, for sizes the two mesh dims divide evenly
+    for n0, n1 in [(2, 2), (2, 4), (4, 2), (3, 2), (2, 3), (1, 4), (4, 1)]:
+        for mult in (1, 2, 3):
+            for shape, d in (((n0 * n1 * mult, 3), 0), ((2, n0 * n1 * mult), 1)):
+                for c0 in range(n0):
+                    for c1 in range(n1):
+                        got = oracle.shard_indices(list(shape), [n0, n1], [d, d], [n1, 1], c0 * n1 + c1, lib=lib)
+                        lo, hi = oracle.shard_box(list(shape), [n1, n0], [d, d], c1 * n0 + c0, lib=lib)
+                        assert got == [list(range(a, b)) for a, b in zip(lo, hi)], (n0, n1, shape, c0, c1)
+
+
+def pin_end_to_end_strided(lib, count=250, seed=29):
+    rng = random.Random(seed)
+    for _ in range(count):
+        (shape, smesh, spl, ssp), = strided_layouts(rng, 1)
+        (_, dmesh, dpl, dsp), = strided_layouts(rng, 1)
+        dpl = tuple(p if p == W.R else p % len(shape) for p in dpl)
+        g = torch.arange(int(np.prod(shape)), dtype=torch.int32).reshape(shape)
+        srcs = [g.reshape(-1)[dtensor_split_local(shape, smesh, spl, ssp, s)].contiguous()
+                for s in range(nranks(smesh))]
+        want = [g.reshape(-1)[dtensor_split_local(shape, dmesh, dpl, dsp, d)].contiguous()
+                for d in range(nranks(dmesh))]
+        dsts = [torch.full_like(w, -7) for w in want]
+        oracle.reshard_indexed(list(shape), 4, list(smesh), list(spl), list(ssp),
+                               [s if s.numel() else None for s in srcs], list(dmesh), list(dpl), list(dsp),
+                               [d if d.numel() else None for d in dsts], lib=lib)
+        for d, (got, exp) in enumerate(zip(dsts, want)):
+            assert torch.equal(got, exp), (shape, smesh, spl, ssp, dmesh, dpl, dsp, d)
+    # replicas that disagree, and a split factor on a Replicate mesh dim
+    shape, smesh, spl, ssp = (12, 5), (2, 3), (W.R, 0), (1, 2)
+    g = torch.arange(60, dtype=torch.int32).reshape(shape)
+    srcs = [g.reshape(-1)[dtensor_split_local(shape, smesh, spl, ssp, s)].contiguous() for s in range(6)]
+    srcs[4] = srcs[4].clone()
+    srcs[4].view(-1)[1] += 1
+    dsts = [torch.empty(12, 5, dtype=torch.int32)]
+    try:
+        oracle.reshard_indexed(list(shape), 4, list(smesh), list(spl), list(ssp), srcs, [1], [W.R], [1], dsts,
+                               lib=lib)
+        raise AssertionError("replica mismatch not reported")
+    except oracle.OracleError as e:
+        assert e.code == oracle.REPLICA_MISMATCH, e
+    try:
+        oracle.shard_indices([4, 4], [2], [W.R], [2], 0, lib=lib)
+        raise AssertionError("split factor on Replicate accepted")
+    except oracle.OracleError as e:
+        assert e.code == oracle.BAD_LAYOUT
+
+
 ALL_PINS = (pin_convert_library, pin_convert_nan_payloads, pin_convert_closed,
             pin_worked_example, pin_box_vs_dtensor, pin_box_vs_chunk, pin_end_to_end_chunk,
-            pin_gather, pin_raw_bits)
+            pin_gather, pin_raw_bits, pin_strided_vs_dtensor, pin_strided_closed, pin_end_to_end_strided)
 
 
 def run_all(lib_path: str) -> int:

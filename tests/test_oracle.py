@@ -52,6 +52,33 @@ def test_pin_convert_closed(oracle_lib):
     P.pin_convert_closed(oracle_lib)
 
 
+def test_pin_strided_vs_dtensor(oracle_lib):
+    P.pin_strided_vs_dtensor(oracle_lib)
+
+
+def test_pin_strided_closed(oracle_lib):
+    P.pin_strided_closed(oracle_lib)
+
+
+def test_pin_end_to_end_strided(oracle_lib):
+    P.pin_end_to_end_strided(oracle_lib)
+
+
+def test_indexed_threads_give_same_bytes(oracle_lib):
+    shape, smesh, spl, ssp = (96, 40), (2, 4), (0, 0), (4, 1)
+    g = torch.randn(shape)
+    srcs = [g.reshape(-1)[P.dtensor_split_local(shape, smesh, spl, ssp, s)].contiguous() for s in range(8)]
+    outs = []
+    for threads in (1, 8):
+        dsts = [torch.empty(48, 40), torch.empty(48, 40)]
+        oracle.reshard_indexed(list(shape), 4, list(smesh), list(spl), list(ssp), srcs, [2], [0], [1], dsts,
+                               threads=threads, lib=oracle_lib)
+        outs.append(dsts)
+    for a, b in zip(*outs):
+        assert torch.equal(a, b)
+    assert torch.equal(torch.cat(outs[0]), g)
+
+
 def test_convert_threads_and_errors(oracle_lib):
     x = torch.randn(100_003, dtype=torch.float32)
     a = oracle.convert(x, "f32", "bf16", threads=1, lib=oracle_lib)
@@ -124,6 +151,18 @@ MUTANTS = {
                              "m = to.frac >= from.frac ? m << (to.frac - from.frac) : m & ((1u << to.frac) - 1);"),
     "nan_sign_dropped": ("return (sign << (to.bits - 1)) | (exp_all_ones(to) << to.frac) | m;",
                          "return (exp_all_ones(to) << to.frac) | m;"),
+    # strided nesting and the indexed gather-then-slice
+    "strided_factor_ignored": ("    const int64_t f = split[m];", "    const int64_t f = 1;"),
+    "strided_pieces_reversed": ("    for (int64_t j = 0; j < f; ++j) {\n      const int64_t start = j * piece;",
+                                "    for (int64_t jj = 0; jj < f; ++jj) {\n      const int64_t j = f - 1 - jj;\n"
+                                "      const int64_t start = j * piece;"),
+    "strided_parts_floor": ("const int64_t part = (len + L.mesh[m] - 1) / L.mesh[m];",
+                            "const int64_t part = len / L.mesh[m] > 0 ? len / L.mesh[m] : 1;"),
+    "strided_flat_nesting": ("        kept.push_back(cur[start + p]);", "        kept.push_back(start + p);"),
+    "indexed_row_order": ("      off += idx[k][row % len] * gstride[k];\n      row /= len;",
+                          "      off += idx[k][row / len % len] * gstride[k];\n      row %= len;"),
+    "indexed_no_replica_compare": ("if (std::memcmp(X + (size_t)g * es, from, es) != 0) mismatch.store(1);",
+                                   "if (false) mismatch.store(1);"),
 }
 
 
