@@ -87,8 +87,10 @@ def dtype_name(dt) -> str:
             "uint8": "u8"}.get(str(dt).replace("torch.", ""), str(dt).replace("torch.", ""))
 
 
-def layout_str(mesh, placements) -> str:
-    pl = ",".join("R" if p < 0 else f"S{p}" for p in placements)
+def layout_str(mesh, placements, split=None) -> str:
+    """(mesh)[placements]; a strided shard with split factor f prints as S<dim>/f."""
+    split = split or (1,) * len(mesh)
+    pl = ",".join("R" if p < 0 else f"S{p}" + (f"/{f}" if f > 1 else "") for p, f in zip(placements, split))
     return f"({','.join(str(m) for m in mesh)})[{pl}]"
 
 
@@ -114,8 +116,8 @@ def traffic_from_profile(workload: str):
 def build_plan(R, wl):
     srcs, dsts = [], []
     for t in wl.tensors:
-        srcs.append(R.reshard_layout_create(t.shape, R.dtype_code(t.dtype), t.src_mesh, t.src_placements))
-        dsts.append(R.reshard_layout_create(t.shape, R.dtype_code(t.out_dtype), t.dst_mesh, t.dst_placements))
+        srcs.append(R.layout_create(t.shape, R.dtype_code(t.dtype), t.src_mesh, t.src_placements, t.src_split))
+        dsts.append(R.layout_create(t.shape, R.dtype_code(t.out_dtype), t.dst_mesh, t.dst_placements, t.dst_split))
     plan = R.reshard_plan_create_batched(srcs, dsts)
     return plan, srcs, dsts
 
@@ -150,18 +152,20 @@ def alloc_set(torch, R, wl, lay_src, lay_dst, dev, seed):
     src_bufs, dst_bufs = [], []
     for t, spec in enumerate(wl.tensors):
         nd = len(spec.shape)
-        sboxes, dboxes = [], []
-        for r in range(R.reshard_layout_num_ranks(lay_src[t])):
-            off, ext = R.reshard_layout_shard_box(lay_src[t], r, nd)
-            sboxes.append((off, [o + e for o, e in zip(off, ext)]))
-        for r in range(R.reshard_layout_num_ranks(lay_dst[t])):
-            off, ext = R.reshard_layout_shard_box(lay_dst[t], r, nd)
-            dboxes.append((off, [o + e for o, e in zip(off, ext)]))
         g = W.make_global(spec, wl.values, seed, t, device=dev)
-        src_bufs += W.cut(g, sboxes)
+        if spec.strided:  # shards are runs of global indices per dim
+            lists = [[[i for a, b in R.reshard_layout_shard_runs(lay_src[t], r, k) for i in range(a, b)]
+                      for k in range(nd)] for r in range(R.reshard_layout_num_ranks(lay_src[t]))]
+            src_bufs += W.cut_indexed(g, lists)
+        else:
+            sboxes = []
+            for r in range(R.reshard_layout_num_ranks(lay_src[t])):
+                off, ext = R.reshard_layout_shard_box(lay_src[t], r, nd)
+                sboxes.append((off, [o + e for o, e in zip(off, ext)]))
+            src_bufs += W.cut(g, sboxes)
         del g
-        for lo, hi in dboxes:
-            shape = [max(0, h - l) for l, h in zip(lo, hi)]
+        for r in range(R.reshard_layout_num_ranks(lay_dst[t])):
+            shape = R.local_shape(lay_dst[t], r, nd)
             dst_bufs.append(torch.empty(shape, dtype=spec.out_dtype, device=dev) if all(shape) else None)
     sp = R.pointer_array([b.data_ptr() if b is not None else 0 for b in src_bufs])
     dp = R.pointer_array([b.data_ptr() if b is not None else 0 for b in dst_bufs])
@@ -361,15 +365,22 @@ def cpu_baseline(torch, R, wl, lay_src, lay_dst, gpu_set, reps: int, single_core
             srcs = [b.cpu().contiguous() if b is not None else None for b in src_bufs[s0:s1]]
             es = torch.empty((), dtype=spec.dtype).element_size()
             dsts = [torch.empty(b.shape, dtype=spec.dtype) if b is not None else None for b in dst_bufs[d0:d1]]
-            args = (list(spec.shape), es, list(spec.src_mesh), list(spec.src_placements),
-                    [x if x is not None and x.numel() else None for x in srcs], list(spec.dst_mesh),
-                    list(spec.dst_placements), [x if x is not None and x.numel() else None for x in dsts])
+            src_in = [x if x is not None and x.numel() else None for x in srcs]
+            dst_in = [x if x is not None and x.numel() else None for x in dsts]
+            if spec.strided:  # the oracle's index-list form
+                fn = oracle.reshard_indexed
+                args = (list(spec.shape), es, list(spec.src_mesh), list(spec.src_placements), list(spec.split("src")),
+                        src_in, list(spec.dst_mesh), list(spec.dst_placements), list(spec.split("dst")), dst_in)
+            else:
+                fn = oracle.reshard
+                args = (list(spec.shape), es, list(spec.src_mesh), list(spec.src_placements), src_in,
+                        list(spec.dst_mesh), list(spec.dst_placements), dst_in)
             t0 = time.perf_counter()
-            oracle.reshard(*args, threads=info["cores"])
+            fn(*args, threads=info["cores"])
             t_all += time.perf_counter() - t0
             if t < one_n:
                 t0 = time.perf_counter()
-                oracle.reshard(*args, threads=1)
+                fn(*args, threads=1)
                 t_one += time.perf_counter() - t0
                 if rep == 0:
                     algo_one += sum(x.numel() for x in srcs if x is not None) // max(1, _src_replicas(spec)) * es
@@ -624,8 +635,8 @@ def main() -> int:
             "workload": wl.name,
             "tensors": len(wl.tensors),
             "global_shape": list(spec0.shape) if len(wl.tensors) == 1 else None,
-            "src_layout": layout_str(spec0.src_mesh, spec0.src_placements),
-            "dst_layout": layout_str(spec0.dst_mesh, spec0.dst_placements),
+            "src_layout": layout_str(spec0.src_mesh, spec0.src_placements, spec0.src_split),
+            "dst_layout": layout_str(spec0.dst_mesh, spec0.dst_placements, spec0.dst_split),
             "bytes_read": st["bytes_read"],
             "bytes_written": st["bytes_written"],
             "pieces": st["n_pieces"],

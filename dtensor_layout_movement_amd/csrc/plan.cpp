@@ -83,7 +83,7 @@ void group_ranks(const Layout& L, int64_t tensor, std::vector<Group>* groups) {
           break;
         }
     }
-    if (found == SIZE_MAX) groups->push_back(Group{tensor, b, {r}});
+    if (found == SIZE_MAX) groups->push_back(Group{tensor, b, {r}, {}});
     else (*groups)[found].ranks.push_back(r);
   }
 }
@@ -355,12 +355,11 @@ void emit_pieces(HostPlan* P, int t, size_t pc0, size_t pc1) {
   const int conv = P->conv[t];
   for (size_t i = pc0; i < pc1; ++i) {
     const Piece& pc = P->pieces[i];
-    const Group& sgrp = P->src_groups[pc.src_group];
     const Group& dgrp = P->dst_groups[pc.dst_group];
     const uint32_t ref_begin = uint32_t(P->refs.size());
     for (int64_t r : dgrp.ranks) P->refs.push_back(uint32_t(P->dst_base[t] + r));
     describe_piece(P, uint32_t(i), uint32_t(P->src_base[t] + pc.src_rank), ref_begin,
-                   uint32_t(dgrp.ranks.size()), pc.box, sgrp.box, dgrp.box, nd, es_s, es_d, conv);
+                   uint32_t(dgrp.ranks.size()), pc.box, pc.sframe, pc.dframe, nd, es_s, es_d, conv);
   }
 }
 
@@ -643,6 +642,7 @@ void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1) {
   const size_t d0 = P->descs.size(), r0 = P->refs.size();
   emit_pieces(P, t, pc0, pc1);
   if (P->conv[t] != 0) return;  // converting rows always go element-group by element-group
+  if (P->src[t].strided || P->dst[t].strided) return;  // bands assume one box per rank
   bool narrow = false, chunked = false;
   for (size_t i = d0; i < P->descs.size(); ++i) {
     const reshard_descriptor_t& D = P->descs[i];
@@ -665,6 +665,190 @@ void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1) {
     P->descs.insert(P->descs.end(), saved.begin(), saved.end());
     P->refs.insert(P->refs.end(), saved_refs.begin(), saved_refs.end());
   }
+}
+
+// Groups the non-empty shards of a strided layout by equal runs along every
+// dim, in order of their lowest rank.
+void group_ranks_runs(const Layout& L, int64_t tensor, std::vector<Group>* groups) {
+  std::map<std::vector<int64_t>, size_t> index;
+  for (int64_t r = 0; r < L.nranks; ++r) {
+    Group g;
+    g.tensor = tensor;
+    std::vector<int64_t> key;
+    bool empty = false;
+    for (int k = 0; k < L.ndim; ++k) {
+      g.runs[k] = shard_runs(L, r, k);
+      if (g.runs[k].empty()) {
+        empty = true;
+        break;
+      }
+      g.box.lo[k] = g.runs[k].front().first;
+      g.box.hi[k] = g.runs[k].back().second;
+      key.push_back(int64_t(g.runs[k].size()));
+      for (const auto& [a, b] : g.runs[k]) {
+        key.push_back(a);
+        key.push_back(b);
+      }
+    }
+    if (empty) continue;
+    auto it = index.find(key);
+    if (it != index.end()) {
+      (*groups)[it->second].ranks.push_back(r);
+      continue;
+    }
+    index.emplace(std::move(key), groups->size());
+    g.ranks.push_back(r);
+    groups->push_back(std::move(g));
+  }
+}
+
+// Position, in a shard's local buffer along one dim, of the run starting at
+// global index lo (runs holds it).
+int64_t run_origin(const Runs& runs, int64_t lo) {
+  int64_t pos = 0;
+  for (const auto& [a, b] : runs) {
+    if (a == lo) return pos;
+    pos += b - a;
+  }
+  return -1;
+}
+
+int64_t runs_length(const Runs& runs) {
+  int64_t n = 0;
+  for (const auto& [a, b] : runs) n += b - a;
+  return n;
+}
+
+// Pieces and descriptors of one tensor whose source or destination layout is
+// strided.  Along each dim the runs of all source groups are either equal or
+// disjoint (a rank's runs depend only on its coordinates in the mesh dims that
+// split that dim), and together they cover the dim: they form a grid as the
+// boxes of a plain layout do.  Every run of a destination group is cut by the
+// grid; each cell is one piece, read from the least-loaded replica of the
+// source group that holds the cell and placed in both shard buffers by frames.
+reshard_status_t plan_runs_tensor(HostPlan* P, int t, std::vector<int64_t>& load, std::string* err) {
+  const Layout& S = P->src[t];
+  const Layout& D = P->dst[t];
+  const int nd = S.ndim;
+  const int64_t es = S.elem_size;
+  const size_t sg0 = P->src_groups.size();
+  group_ranks_runs(S, t, &P->src_groups);
+  const size_t sg1 = P->src_groups.size();
+  const size_t dg0 = P->dst_groups.size();
+  group_ranks_runs(D, t, &P->dst_groups);
+  const size_t dg1 = P->dst_groups.size();
+  for (size_t g = sg0; g < sg1; ++g)
+    for (int64_t r : P->src_groups[g].ranks) P->src_needed[P->src_base[t] + r] = 1;
+  for (size_t g = dg0; g < dg1; ++g)
+    for (int64_t r : P->dst_groups[g].ranks) P->dst_needed[P->dst_base[t] + r] = 1;
+  if (sg0 == sg1) return RESHARD_OK;
+
+  std::vector<Runs> iv(nd);  // per dim: every source run, sorted
+  for (int k = 0; k < nd; ++k) {
+    for (size_t g = sg0; g < sg1; ++g)
+      iv[k].insert(iv[k].end(), P->src_groups[g].runs[k].begin(), P->src_groups[g].runs[k].end());
+    std::sort(iv[k].begin(), iv[k].end());
+    iv[k].erase(std::unique(iv[k].begin(), iv[k].end()), iv[k].end());
+    for (size_t i = 0; i + 1 < iv[k].size(); ++i)
+      if (iv[k][i].second > iv[k][i + 1].first) {
+        *err = "internal: overlapping source runs";
+        return RESHARD_ERR_INVALID_ARGUMENT;
+      }
+  }
+  std::vector<int64_t> stride(nd, 1);
+  for (int k = nd - 2; k >= 0; --k) stride[k] = stride[k + 1] * int64_t(iv[k + 1].size());
+  std::unordered_map<int64_t, int64_t> cell_group;
+  for (size_t g = sg0; g < sg1; ++g) {
+    const Group& G = P->src_groups[g];
+    std::vector<size_t> j(nd, 0);
+    for (;;) {
+      int64_t cell = 0;
+      for (int k = 0; k < nd; ++k) cell += interval_index(iv[k], G.runs[k][j[k]].first) * stride[k];
+      cell_group[cell] = int64_t(g);
+      int k = nd - 1;
+      while (k >= 0 && j[k] + 1 == G.runs[k].size()) j[k--] = 0;
+      if (k < 0) break;
+      ++j[k];
+    }
+  }
+
+  const size_t pc0 = P->pieces.size();
+  for (size_t g = dg0; g < dg1; ++g) {
+    const Group& dgrp = P->dst_groups[g];
+    int64_t dext[kMaxDims];
+    for (int k = 0; k < nd; ++k) dext[k] = runs_length(dgrp.runs[k]);
+    std::vector<size_t> dj(nd, 0);
+    std::vector<int64_t> dorig(nd, 0);  // local position of run dj[k]
+    for (;;) {  // every destination sub-box: one run per dim
+      int64_t first[kMaxDims], last[kMaxDims], idx[kMaxDims];
+      for (int k = 0; k < nd; ++k) {
+        const auto& run = dgrp.runs[k][dj[k]];
+        const auto& v = iv[k];
+        auto lo_it = std::upper_bound(v.begin(), v.end(), std::make_pair(run.first, INT64_MAX));
+        first[k] = std::max<int64_t>(0, int64_t(lo_it - v.begin()) - 1);
+        last[k] = first[k];
+        while (last[k] + 1 < int64_t(v.size()) && v[last[k] + 1].first < run.second) ++last[k];
+        idx[k] = first[k];
+      }
+      for (;;) {  // every source cell overlapping it
+        int64_t cell = 0;
+        Box box;
+        bool empty = false;
+        for (int k = 0; k < nd; ++k) {
+          const auto& run = dgrp.runs[k][dj[k]];
+          cell += idx[k] * stride[k];
+          box.lo[k] = std::max(run.first, iv[k][idx[k]].first);
+          box.hi[k] = std::min(run.second, iv[k][idx[k]].second);
+          if (box.hi[k] <= box.lo[k]) empty = true;
+        }
+        if (!empty) {
+          auto it = cell_group.find(cell);
+          if (it == cell_group.end()) {
+            *err = "internal: source grid cell without a rank";
+            return RESHARD_ERR_INVALID_ARGUMENT;
+          }
+          const int64_t sg = it->second;
+          const Group& sgrp = P->src_groups[sg];
+          int64_t best = sgrp.ranks[0];
+          for (int64_t r : sgrp.ranks)
+            if (load[P->src_base[t] + r] < load[P->src_base[t] + best]) best = r;
+          Box sframe, dframe;
+          for (int k = 0; k < nd; ++k) {
+            const int64_t so = run_origin(sgrp.runs[k], iv[k][idx[k]].first);
+            sframe.lo[k] = iv[k][idx[k]].first - so;
+            sframe.hi[k] = sframe.lo[k] + runs_length(sgrp.runs[k]);
+            dframe.lo[k] = dgrp.runs[k][dj[k]].first - dorig[k];
+            dframe.hi[k] = dframe.lo[k] + dext[k];
+          }
+          const int64_t bytes = box_numel(nd, box) * es;
+          load[P->src_base[t] + best] += bytes;
+          P->pieces.push_back(Piece{t, best, sg, int64_t(g), box, bytes, sframe, dframe});
+          const int64_t fanout = int64_t(dgrp.ranks.size());
+          P->bytes_read += bytes;
+          P->bytes_written += box_numel(nd, box) * D.elem_size * fanout;
+          P->n_dst_writes += fanout;
+        }
+        int k = nd - 1;
+        while (k >= 0 && idx[k] == last[k]) {
+          idx[k] = first[k];
+          --k;
+        }
+        if (k < 0) break;
+        ++idx[k];
+      }
+      int k = nd - 1;
+      while (k >= 0 && dj[k] + 1 == dgrp.runs[k].size()) {
+        dj[k] = 0;
+        dorig[k] = 0;
+        --k;
+      }
+      if (k < 0) break;
+      dorig[k] += dgrp.runs[k][dj[k]].second - dgrp.runs[k][dj[k]].first;
+      ++dj[k];
+    }
+  }
+  emit_tensor(P, t, pc0, P->pieces.size());
+  return RESHARD_OK;
 }
 
 }  // namespace
@@ -694,7 +878,7 @@ void magic_u31(uint32_t d, uint32_t* m, uint32_t* s) {
 }
 
 bool make_layout(int ndim, const int64_t* shape, int dtype, int mesh_ndim, const int64_t* mesh,
-                 const int32_t* placements, Layout* out, std::string* err) {
+                 const int32_t* placements, Layout* out, std::string* err, const int64_t* split) {
   if (ndim < 1 || ndim > kMaxDims) {
     *err = "ndim must be in [1, " + std::to_string(kMaxDims) + "]";
     return false;
@@ -735,6 +919,16 @@ bool make_layout(int ndim, const int64_t* shape, int dtype, int mesh_ndim, const
     }
     L.mesh[m] = mesh[m];
     L.place[m] = placements[m];
+    L.split[m] = split ? split[m] : 1;
+    if (L.split[m] < 1 || L.split[m] > (int64_t(1) << 20)) {
+      *err = "split_factors[" + std::to_string(m) + "] must be in [1, 2^20]";
+      return false;
+    }
+    if (L.split[m] > 1 && placements[m] == RESHARD_REPLICATE) {
+      *err = "split_factors[" + std::to_string(m) + "] > 1 on a Replicate mesh dim";
+      return false;
+    }
+    if (L.split[m] > 1) L.strided = true;
     L.nranks *= mesh[m];
     if (L.nranks > (int64_t(1) << 24)) {
       *err = "mesh has more than 2^24 ranks";
@@ -763,6 +957,55 @@ void shard_box(const Layout& L, int64_t rank, Box* out) {
     out->lo[k] = std::min(hi, lo + coord[m] * chunk);
     out->hi[k] = std::min(hi, lo + (coord[m] + 1) * chunk);
   }
+}
+
+Runs shard_runs(const Layout& L, int64_t rank, int dim) {
+  int64_t coord[kMaxMeshDims];
+  for (int m = L.mesh_ndim - 1; m >= 0; --m) {
+    coord[m] = rank % L.mesh[m];
+    rank /= L.mesh[m];
+  }
+  Runs cur;
+  if (L.shape[dim] > 0) cur.emplace_back(0, L.shape[dim]);
+  int64_t n = L.shape[dim];  // length of cur
+  for (int m = 0; m < L.mesh_ndim; ++m) {
+    if (L.place[m] != dim) continue;
+    const int64_t f = L.split[m];
+    const int64_t piece = (n + f - 1) / f;
+    // local positions kept, in order: part coord[m] of each of the f pieces
+    Runs keep;
+    for (int64_t j = 0; j < f && j * piece < n; ++j) {
+      const int64_t start = j * piece, len = std::min(piece, n - start);
+      const int64_t part = (len + L.mesh[m] - 1) / L.mesh[m];
+      const int64_t a = std::min(len, coord[m] * part), b = std::min(len, (coord[m] + 1) * part);
+      if (a < b) keep.emplace_back(start + a, start + b);
+    }
+    // map the kept local positions through cur to global runs (both lists
+    // are increasing, so one forward walk over cur serves every kept range)
+    Runs next;
+    int64_t kept = 0;
+    size_t r = 0;
+    int64_t pos = 0;  // local position where cur[r] starts
+    for (const auto& [a, b] : keep) {
+      kept += b - a;
+      for (int64_t x = a; x < b;) {
+        const int64_t in_run = cur[r].second - cur[r].first;
+        if (pos + in_run <= x) {  // x lies past cur[r]
+          pos += in_run;
+          ++r;
+          continue;
+        }
+        const int64_t hi = std::min(b, pos + in_run);
+        const int64_t g0 = cur[r].first + (x - pos), g1 = cur[r].first + (hi - pos);
+        if (!next.empty() && next.back().second == g0) next.back().second = g1;
+        else next.emplace_back(g0, g1);
+        x = hi;
+      }
+    }
+    cur = std::move(next);
+    n = kept;
+  }
+  return cur;
 }
 
 bool box_empty(int ndim, const Box& b) {
@@ -827,6 +1070,11 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
     for (int k = 0; k < nd; ++k) numel *= S.shape[k];
     P->global_bytes += numel * es;
 
+    if (S.strided || D.strided) {
+      const reshard_status_t st = plan_runs_tensor(P, t, load, err);
+      if (st != RESHARD_OK) return st;
+      continue;
+    }
     const size_t sg0 = P->src_groups.size();
     group_ranks(S, t, &P->src_groups);
     const size_t sg1 = P->src_groups.size();
@@ -876,7 +1124,7 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
             if (load[P->src_base[t] + r] < load[P->src_base[t] + best]) best = r;
           const int64_t bytes = box_numel(nd, box) * es;
           load[P->src_base[t] + best] += bytes;
-          P->pieces.push_back(Piece{t, best, sg, int64_t(g), box, bytes});
+          P->pieces.push_back(Piece{t, best, sg, int64_t(g), box, bytes, sgrp.box, dgrp.box});
           const int64_t fanout = int64_t(dgrp.ranks.size());
           P->bytes_read += bytes;
           P->bytes_written += box_numel(nd, box) * D.elem_size * fanout;

@@ -13,6 +13,7 @@
 
 #include <cstdint>
 #include <string>
+#include <utility>
 #include <vector>
 
 #include "reshard.h"
@@ -30,6 +31,8 @@ struct Layout {
   int mesh_ndim = 0;
   int64_t mesh[kMaxMeshDims] = {};
   int32_t place[kMaxMeshDims] = {};
+  int64_t split[kMaxMeshDims] = {};  // split factor of each mesh dim (1 = plain Shard / Replicate)
+  bool strided = false;              // some split factor above 1
   int64_t nranks = 0;
 };
 
@@ -38,27 +41,47 @@ struct Box {
   int64_t hi[kMaxDims];
 };
 
+// Ordered runs [lo, hi) of global indices along one tensor dim: what a rank of
+// a strided layout holds, stored in this order (increasing, not touching).
+using Runs = std::vector<std::pair<int64_t, int64_t>>;
+
 // Conversion code (RESHARD_CONVERT_*) from src_dtype to dst_dtype: 0 when the
 // dtypes are equal, -1 when the pair is not supported.
 int conversion_of(int src_dtype, int dst_dtype);
 
 // Validates and fills a layout; returns false with a message on bad input.
+// split: one split factor per mesh dim, or NULL for all 1.
 bool make_layout(int ndim, const int64_t* shape, int dtype, int mesh_ndim, const int64_t* mesh,
-                 const int32_t* placements, Layout* out, std::string* err);
+                 const int32_t* placements, Layout* out, std::string* err, const int64_t* split = nullptr);
 
 // Box of `rank` (row-major mesh coordinates, nested ceil-chunk splitting).
+// Layouts without split factors only.
 void shard_box(const Layout& L, int64_t rank, Box* out);
+
+// Runs of global indices that `rank` holds along tensor dim `dim`, for any
+// layout.  A mesh dim with split factor f that shards `dim` cuts the rank's
+// current index list (what the mesh dims to its left left it, length n) into f
+// ceil-chunks, cuts each of those into mesh-size ceil-chunks, and keeps part
+// coord of each, in order (DTensor's right-to-left _StridedShard placement;
+// f = 1 is a plain Shard).
+Runs shard_runs(const Layout& L, int64_t rank, int dim);
 bool box_empty(int ndim, const Box& b);
 int64_t box_numel(int ndim, const Box& b);
 
-// A set of ranks of one tensor that hold the same non-empty box.
+// A set of ranks of one tensor that hold the same non-empty box (or, for a
+// strided layout, the same runs along every dim; box is then their bounding box).
 struct Group {
   int64_t tensor;
   Box box;
   std::vector<int64_t> ranks;  // ascending
+  Runs runs[kMaxDims];         // strided layouts only
 };
 
-// One overlap of a unique source box and a unique destination box.
+// One overlap of a unique source box and a unique destination box.  A frame
+// places the shard buffer in global coordinates: local index = global - lo,
+// buffer extents = hi - lo.  For a plain layout it is the group's box; for a
+// strided one it is shifted per run, so that the piece's run lands at its
+// position in the buffer.
 struct Piece {
   int64_t tensor;
   int64_t src_rank;   // replica chosen to read from
@@ -66,6 +89,7 @@ struct Piece {
   int64_t dst_group;  // index into HostPlan::dst_groups
   Box box;            // global coordinates
   int64_t bytes;
+  Box sframe, dframe;
 };
 
 // Tiling.  One workgroup of kTileThreads threads copies one tile of one

@@ -376,7 +376,39 @@ reshard_status_t reshard_layout_create(int ndim, const int64_t* global_shape, in
   return RESHARD_OK;
 }
 
+reshard_status_t reshard_layout_create_strided(int ndim, const int64_t* global_shape, int dtype,
+                                               int mesh_ndim, const int64_t* mesh_shape,
+                                               const int32_t* placements, const int64_t* split_factors,
+                                               reshard_layout_t* out) {
+  if (!out) return fail(RESHARD_ERR_INVALID_ARGUMENT, "out is NULL");
+  *out = nullptr;
+  if (!split_factors) return fail(RESHARD_ERR_INVALID_ARGUMENT, "split_factors is NULL");
+  rs::Layout L;
+  std::string err;
+  if (!rs::make_layout(ndim, global_shape, dtype, mesh_ndim, mesh_shape, placements, &L, &err, split_factors))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, err);
+  reshard_layout_s* h = new (std::nothrow) reshard_layout_s{L};
+  if (!h) return fail(RESHARD_ERR_OUT_OF_MEMORY, "layout allocation");
+  *out = h;
+  return RESHARD_OK;
+}
+
 void reshard_layout_destroy(reshard_layout_t layout) { delete layout; }
+
+reshard_status_t reshard_layout_shard_runs(reshard_layout_t layout, int64_t rank, int dim, int64_t capacity,
+                                           int64_t* runs, int64_t* n_runs) {
+  if (!layout || !n_runs || capacity < 0 || (capacity > 0 && !runs))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "bad argument");
+  if (rank < 0 || rank >= layout->L.nranks) return fail(RESHARD_ERR_INVALID_ARGUMENT, "rank out of range");
+  if (dim < 0 || dim >= layout->L.ndim) return fail(RESHARD_ERR_INVALID_ARGUMENT, "dim out of range");
+  const rs::Runs r = rs::shard_runs(layout->L, rank, dim);
+  *n_runs = int64_t(r.size());
+  for (int64_t i = 0; i < std::min<int64_t>(capacity, *n_runs); ++i) {
+    runs[2 * i] = r[size_t(i)].first;
+    runs[2 * i + 1] = r[size_t(i)].second;
+  }
+  return RESHARD_OK;
+}
 
 reshard_status_t reshard_layout_num_ranks(reshard_layout_t layout, int64_t* out) {
   if (!layout || !out) return fail(RESHARD_ERR_INVALID_ARGUMENT, "NULL argument");
@@ -389,6 +421,8 @@ reshard_status_t reshard_layout_shard_box(reshard_layout_t layout, int64_t rank,
   if (!layout || !offset || !extent) return fail(RESHARD_ERR_INVALID_ARGUMENT, "NULL argument");
   if (rank < 0 || rank >= layout->L.nranks)
     return fail(RESHARD_ERR_INVALID_ARGUMENT, "rank out of range");
+  if (layout->L.strided)
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "a strided layout's shard is not one box: use reshard_layout_shard_runs");
   rs::Box b;
   rs::shard_box(layout->L, rank, &b);
   for (int k = 0; k < layout->L.ndim; ++k) {
@@ -613,6 +647,8 @@ reshard_status_t reshard_plan_pieces(reshard_plan_t plan, int64_t capacity, resh
     for (int k = 0; k < nd; ++k) {
       o.lo[k] = pc.box.lo[k];
       o.hi[k] = pc.box.hi[k];
+      o.src_local[k] = pc.box.lo[k] - pc.sframe.lo[k];
+      o.dst_local[k] = pc.box.lo[k] - pc.dframe.lo[k];
     }
   }
   return RESHARD_OK;

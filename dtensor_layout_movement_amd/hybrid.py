@@ -25,7 +25,8 @@ class HybridPlan:
     """Plans for a list of tensors split by `use_reshard(spec)`.
 
     specs: objects with name, shape, dtype, src_mesh, src_placements, dst_mesh,
-    dst_placements (e.g. workloads.TensorSpec).  Tensors routed to the gather path
+    dst_placements and optionally src_split / dst_split (e.g.
+    workloads.TensorSpec).  Tensors routed to the gather path
     need one full-size buffer each (`global_shapes()`), owned by the caller.
     """
 
@@ -38,8 +39,10 @@ class HybridPlan:
         for t, spec in enumerate(self.specs):
             code = R.dtype_code(spec.dtype)
             out = R.dtype_code(getattr(spec, "out_dtype", spec.dtype))
-            src[t] = R.reshard_layout_create(spec.shape, code, spec.src_mesh, spec.src_placements)
-            dst[t] = R.reshard_layout_create(spec.shape, out, spec.dst_mesh, spec.dst_placements)
+            src[t] = R.layout_create(spec.shape, code, spec.src_mesh, spec.src_placements,
+                                     getattr(spec, "src_split", None))
+            dst[t] = R.layout_create(spec.shape, out, spec.dst_mesh, spec.dst_placements,
+                                     getattr(spec, "dst_split", None))
             self._layouts += [src[t], dst[t]]
             if t in self.gather:
                 glob[t] = R.reshard_layout_create(spec.shape, code, (1,), (R.REPLICATE,))

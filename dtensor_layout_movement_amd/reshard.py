@@ -49,6 +49,7 @@ CONVERT_F16_F32 = 4
 
 EXPORTED = (
     "reshard_dtype_size", "reshard_layout_create", "reshard_layout_destroy",
+    "reshard_layout_create_strided", "reshard_layout_shard_runs",
     "reshard_layout_num_ranks", "reshard_layout_shard_box", "reshard_plan_create",
     "reshard_plan_create_batched", "reshard_plan_upload", "reshard_execute", "reshard_execute_noalloc",
     "reshard_plan_stats", "reshard_plan_src_load", "reshard_plan_pieces", "reshard_plan_piece_fanout",
@@ -74,7 +75,8 @@ class Piece(ctypes.Structure):
     _fields_ = [("tensor", ctypes.c_int64), ("src_rank", ctypes.c_int64),
                 ("src_group", ctypes.c_int64), ("dst_group", ctypes.c_int64),
                 ("fanout", ctypes.c_int64), ("lo", ctypes.c_int64 * MAX_NDIM),
-                ("hi", ctypes.c_int64 * MAX_NDIM)]
+                ("hi", ctypes.c_int64 * MAX_NDIM), ("src_local", ctypes.c_int64 * MAX_NDIM),
+                ("dst_local", ctypes.c_int64 * MAX_NDIM)]
 
 
 class Descriptor(ctypes.Structure):
@@ -121,6 +123,9 @@ def _load() -> ctypes.CDLL:
         "reshard_dtype_size": (_I64, [ctypes.c_int]),
         "reshard_layout_create": (st, [ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, _I64P,
                                        ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(_VP)]),
+        "reshard_layout_create_strided": (st, [ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int, _I64P,
+                                               ctypes.POINTER(ctypes.c_int32), _I64P, ctypes.POINTER(_VP)]),
+        "reshard_layout_shard_runs": (st, [_VP, _I64, ctypes.c_int, _I64, _I64P, _I64P]),
         "reshard_layout_destroy": (None, [_VP]),
         "reshard_layout_num_ranks": (st, [_VP, _I64P]),
         "reshard_layout_shard_box": (st, [_VP, _I64, _I64P, _I64P]),
@@ -181,6 +186,40 @@ def reshard_layout_create(global_shape: Sequence[int], dtype: int, mesh_shape: S
     _check(_load().reshard_layout_create(len(global_shape), _i64s(global_shape), int(dtype),
                                          len(mesh_shape), _i64s(mesh_shape), pl, ctypes.byref(out)))
     return out.value
+
+
+def reshard_layout_create_strided(global_shape: Sequence[int], dtype: int, mesh_shape: Sequence[int],
+                                  placements: Sequence[int], split_factors: Sequence[int]) -> int:
+    out = _VP()
+    pl = (ctypes.c_int32 * max(1, len(placements)))(*[int(p) for p in placements])
+    _check(_load().reshard_layout_create_strided(len(global_shape), _i64s(global_shape), int(dtype),
+                                                 len(mesh_shape), _i64s(mesh_shape), pl, _i64s(split_factors),
+                                                 ctypes.byref(out)))
+    return out.value
+
+
+def reshard_layout_shard_runs(layout: int, rank: int, dim: int) -> list[tuple[int, int]]:
+    """The runs ``(lo, hi)`` of global indices ``rank`` holds along ``dim``."""
+    n = ctypes.c_int64()
+    _check(_load().reshard_layout_shard_runs(layout, int(rank), int(dim), 0, None, ctypes.byref(n)))
+    buf = (ctypes.c_int64 * max(2, 2 * n.value))()
+    _check(_load().reshard_layout_shard_runs(layout, int(rank), int(dim), n.value, buf, ctypes.byref(n)))
+    return [(buf[2 * i], buf[2 * i + 1]) for i in range(n.value)]
+
+
+def layout_create(global_shape: Sequence[int], dtype: int, mesh_shape: Sequence[int], placements: Sequence[int],
+                  split_factors: Sequence[int] | None = None) -> int:
+    """reshard_layout_create, or reshard_layout_create_strided when some split
+    factor is above 1 (None: all 1)."""
+    if split_factors is not None and any(int(f) != 1 for f in split_factors):
+        return reshard_layout_create_strided(global_shape, dtype, mesh_shape, placements, split_factors)
+    return reshard_layout_create(global_shape, dtype, mesh_shape, placements)
+
+
+def local_shape(layout: int, rank: int, ndim: int) -> list[int]:
+    """Shape of ``rank``'s local shard (any layout): per dim, the total length
+    of its runs."""
+    return [sum(b - a for a, b in reshard_layout_shard_runs(layout, rank, k)) for k in range(ndim)]
 
 
 def reshard_layout_destroy(layout: int) -> None:
@@ -271,7 +310,8 @@ def reshard_plan_pieces(plan: int) -> list[dict]:
     arr = (Piece * max(1, n.value))()
     _check(_load().reshard_plan_pieces(plan, n.value, arr, ctypes.byref(n)))
     return [{"tensor": p.tensor, "src_rank": p.src_rank, "src_group": p.src_group,
-             "dst_group": p.dst_group, "fanout": p.fanout, "lo": list(p.lo), "hi": list(p.hi)}
+             "dst_group": p.dst_group, "fanout": p.fanout, "lo": list(p.lo), "hi": list(p.hi),
+             "src_local": list(p.src_local), "dst_local": list(p.dst_local)}
             for p in arr[:n.value]]
 
 

@@ -24,21 +24,25 @@ from __future__ import annotations
 from . import reshard as R
 
 
-def stage1_layout(mesh, placements):
-    """(mesh, placements) of the stage-1 layout: the destination's non-Replicate
-    mesh dims in order, then its Replicate dims turned into Shard(0)."""
+def stage1_layout(mesh, placements, split=None):
+    """(mesh, placements, split factors) of the stage-1 layout: the
+    destination's non-Replicate mesh dims in order (with their split factors),
+    then its Replicate dims turned into Shard(0) (factor 1)."""
+    split = tuple(split) if split is not None else (1,) * len(mesh)
     non = [i for i, p in enumerate(placements) if p != R.REPLICATE]
     rep = [i for i, p in enumerate(placements) if p == R.REPLICATE]
     mesh1 = [mesh[i] for i in non] + [mesh[i] for i in rep]
     pl1 = [placements[i] for i in non] + [0] * len(rep)
-    return tuple(mesh1), tuple(pl1)
+    sp1 = [split[i] for i in non] + [1] * len(rep)
+    return tuple(mesh1), tuple(pl1), tuple(sp1)
 
 
 class TwoStagePlan:
     """Stage-1 and stage-2 plans for a list of tensors, `chunks` tensor chunks.
 
     specs: objects with shape, dtype, src_mesh, src_placements, dst_mesh,
-    dst_placements (e.g. workloads.TensorSpec).
+    dst_placements and optionally src_split / dst_split (e.g.
+    workloads.TensorSpec).
     """
 
     def __init__(self, specs, chunks: int = 1):
@@ -51,10 +55,10 @@ class TwoStagePlan:
         for spec in self.specs:
             code = R.dtype_code(spec.dtype)
             out = R.dtype_code(getattr(spec, "out_dtype", spec.dtype))  # a conversion happens in stage 1
-            m1, p1 = stage1_layout(spec.dst_mesh, spec.dst_placements)
-            s = R.reshard_layout_create(spec.shape, code, spec.src_mesh, spec.src_placements)
-            m = R.reshard_layout_create(spec.shape, out, m1, p1)
-            d = R.reshard_layout_create(spec.shape, out, spec.dst_mesh, spec.dst_placements)
+            m1, p1, f1 = stage1_layout(spec.dst_mesh, spec.dst_placements, getattr(spec, "dst_split", None))
+            s = R.layout_create(spec.shape, code, spec.src_mesh, spec.src_placements, getattr(spec, "src_split", None))
+            m = R.layout_create(spec.shape, out, m1, p1, f1)
+            d = R.layout_create(spec.shape, out, spec.dst_mesh, spec.dst_placements, getattr(spec, "dst_split", None))
             self._layouts += [s, m, d]
             self.src_l.append(s)
             self.mid_l.append(m)
@@ -70,7 +74,7 @@ class TwoStagePlan:
         out = []
         for t, spec in enumerate(self.specs):
             n = R.reshard_layout_num_ranks(self.mid_l[t])
-            out.append([R.reshard_layout_shard_box(self.mid_l[t], r, len(spec.shape))[1] for r in range(n)])
+            out.append([R.local_shape(self.mid_l[t], r, len(spec.shape)) for r in range(n)])
         return out
 
     def bytes_moved(self) -> int:

@@ -22,6 +22,8 @@ numbers, only an 8x8 example and multi-node refit latencies):
   ragged chunks -> seven row shards.
 * ``ffn_refit_32_layers`` -- 32 layers x (gate, up, down) moved by one fused
   launch: 4 pipeline stages x TP2 -> DP2 x TP4.
+* ``ffn_up_fsdp2_tp_14336x4096`` -- the up-projection trained under FSDP2 x TP
+  (right-to-left nesting, DTensor's _StridedShard) -> DP2 x TP2.
 
 Values: bf16 tensors are N(0, 0.02) drawn in fp32 and rounded to nearest-even;
 fp32 tensors are U[-1, 1); "raw" fills every byte uniformly at random (NaN
@@ -48,11 +50,24 @@ class TensorSpec:
     dst_mesh: tuple
     dst_placements: tuple
     dst_dtype: torch.dtype | None = None  # another float format: a converting reshard
+    src_split: tuple | None = None  # split factor per source mesh dim (right-to-left nesting)
+    dst_split: tuple | None = None  # the same for the destination; None: all 1
 
     @property
     def out_dtype(self) -> torch.dtype:
         """Element type of the destination shards."""
         return self.dst_dtype if self.dst_dtype is not None else self.dtype
+
+    @property
+    def strided(self) -> bool:
+        """Whether either layout nests right to left (a split factor above 1)."""
+        return any(f > 1 for f in (self.src_split or ()) + (self.dst_split or ()))
+
+    def split(self, side: str) -> tuple:
+        """Split factors of the "src" or "dst" layout, one per mesh dim."""
+        mesh = self.src_mesh if side == "src" else self.dst_mesh
+        f = self.src_split if side == "src" else self.dst_split
+        return tuple(f) if f is not None else (1,) * len(mesh)
 
 
 @dataclass(frozen=True)
@@ -88,6 +103,15 @@ def ffn_up(rows: int = 14336, cols: int = 4096) -> Workload:
     t = TensorSpec("up_proj", (rows, cols), torch.bfloat16, (4,), (0,), (2, 2), (R, 1))
     return Workload(f"ffn_up_{rows}x{cols}", (t,), "normal",
                     f"{rows}x{cols} bf16 N(0,0.02), (4,)[S0] -> (2,2)[R,S1]")
+
+
+def ffn_up_fsdp2_tp(rows: int = 14336, cols: int = 4096) -> Workload:
+    """The up-projection trained under FSDP2 (2) x TP (4): TP splits the rows
+    first and FSDP each TP slice, which DTensor writes as [_StridedShard(0,
+    split_factor=4), Shard(0)] on the (dp, tp) mesh -> DP2 x TP2 column split."""
+    t = TensorSpec("up_proj", (rows, cols), torch.bfloat16, (2, 4), (0, 0), (2, 2), (R, 1), src_split=(4, 1))
+    return Workload(f"ffn_up_fsdp2_tp_{rows}x{cols}", (t,), "normal",
+                    f"{rows}x{cols} bf16 N(0,0.02), (2,4)[S0 strided by 4, S0] -> (2,2)[R,S1]")
 
 
 def moe_experts(experts: int = 64, hidden: int = 2048, ffn: int = 7168) -> Workload:
@@ -225,6 +249,7 @@ WORKLOADS = {
     "narrow_columns_16b_tp8_4194304x8": narrow_columns_16b_tp8,
     "ffn_up_f32_to_bf16_14336x4096": ffn_up_f32_to_bf16,
     "dense_layer_refit_32_layers": dense_layer_refit,
+    "ffn_up_fsdp2_tp_14336x4096": ffn_up_fsdp2_tp,
 }
 
 
@@ -251,6 +276,22 @@ def make_global(spec: TensorSpec, values: str, seed: int, tensor_index: int = 0,
         raw = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g, device=device)
         return raw.view(spec.dtype).reshape(spec.shape)
     raise ValueError(f"unknown value kind {values!r}")
+
+
+def cut_indexed(global_tensor: torch.Tensor, index_lists: Sequence) -> list:
+    """Contiguous copies of the global tensor restricted, along every dim, to a
+    list of global indices (one list of per-dim lists per rank); None for an
+    empty shard."""
+    out = []
+    for lists in index_lists:
+        if any(len(ix) == 0 for ix in lists):
+            out.append(None)
+            continue
+        x = global_tensor
+        for k, ix in enumerate(lists):
+            x = x.index_select(k, torch.as_tensor(list(ix), dtype=torch.int64, device=x.device))
+        out.append(x.contiguous())
+    return out
 
 
 def cut(global_tensor: torch.Tensor, boxes: Sequence) -> list:

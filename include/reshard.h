@@ -28,7 +28,8 @@
  *     ranks may hold a short or an empty (zero-size) shard;
  *   - several mesh dims that shard the same tensor dim nest left to right;
  *   - each local shard is a contiguous row-major buffer whose shape is the
- *     extent of its box (reshard_layout_shard_box).
+ *     extent of its box (reshard_layout_shard_box);
+ *   - right-to-left (strided) nesting: reshard_layout_create_strided.
  * The copy is bytewise: bf16/fp32 NaN payloads, -0.0 and subnormals arrive
  * unchanged.  Source and destination dtypes match, or the pair is one of the
  * float conversions below.
@@ -124,6 +125,9 @@ typedef struct reshard_piece {
   int64_t fanout;                 /* destination ranks written (replicas of dst_group) */
   int64_t lo[RESHARD_MAX_NDIM];   /* box [lo, hi) of the overlap, global coordinates */
   int64_t hi[RESHARD_MAX_NDIM];
+  int64_t src_local[RESHARD_MAX_NDIM]; /* where the box starts in the source rank's buffer, local
+                                          coordinates (lo - the box's offset for a plain layout) */
+  int64_t dst_local[RESHARD_MAX_NDIM]; /* the same in every destination replica's buffer */
 } reshard_piece_t;
 
 /* Descriptor modes. */
@@ -247,12 +251,50 @@ reshard_status_t reshard_layout_create(int ndim, const int64_t* global_shape, in
                                        const int32_t* placements, reshard_layout_t* out);
 void reshard_layout_destroy(reshard_layout_t layout); /* NULL is a no-op */
 
+/*
+ * A layout with right-to-left ("strided") nesting.  The pages say only that
+ * the refit guide lists the supported layouts (news.bpdata.com write-up,
+ * "practical access and setup" section); the placement follows PyTorch
+ * DTensor's _StridedShard(k, split_factor), used by FSDP2 + TP when the TP
+ * mesh dim splits a tensor dim before the FSDP mesh dim does.
+ *   split_factors[mesh_ndim]  one factor f >= 1 per mesh dim; f > 1 only where
+ *                             placements[m] is a tensor dim (f = 1 is a plain
+ *                             Shard or Replicate: with all ones this is
+ *                             reshard_layout_create).
+ * At mesh dim m with factor f, a rank's current index list along dim k (what
+ * the mesh dims to its left left it, length n) is cut into f ceil-chunks
+ * (chunk = ceil(n / f), trailing ones short or empty); each of those is cut into
+ * mesh_shape[m] ceil-chunks, and coordinate c keeps part c of every one of the f
+ * chunks, in order.  Mesh dims still apply left to right.  Example: 8 rows on a
+ * 2x2 mesh with placements {0, 0} and split factors {2, 1} give ranks 0..3 rows
+ * {0,1}, {4,5}, {2,3}, {6,7}.  A rank's shard is then, along each dim, a list of
+ * runs of global indices (reshard_layout_shard_runs), and its local buffer is
+ * the contiguous row-major buffer over the product of those lists, runs in
+ * global order.  Other arguments, ownership and errors as reshard_layout_create.
+ */
+reshard_status_t reshard_layout_create_strided(int ndim, const int64_t* global_shape, int dtype,
+                                               int mesh_ndim, const int64_t* mesh_shape,
+                                               const int32_t* placements, const int64_t* split_factors,
+                                               reshard_layout_t* out);
+
 /* Number of ranks (product of the mesh shape). */
 reshard_status_t reshard_layout_num_ranks(reshard_layout_t layout, int64_t* out);
 
 /*
+ * Runs of global indices that `rank` holds along tensor dim `dim`, any layout:
+ * writes min(capacity, count) runs as (lo, hi) pairs to runs[2 * capacity] and
+ * the count to *n_runs (0: the shard is empty).  The runs are increasing and do
+ * not touch; the shard's local extent along `dim` is the sum of their lengths.
+ * A plain layout has one run per non-empty dim.  Errors:
+ * RESHARD_ERR_INVALID_ARGUMENT (NULL, rank or dim out of range).
+ */
+reshard_status_t reshard_layout_shard_runs(reshard_layout_t layout, int64_t rank, int dim, int64_t capacity,
+                                           int64_t* runs, int64_t* n_runs);
+
+/*
  * Box held by `rank`: offset[ndim] (global start) and extent[ndim] (local shape,
- * may contain zeros for an empty shard).  Errors: RESHARD_ERR_INVALID_ARGUMENT.
+ * may contain zeros for an empty shard).  Errors: RESHARD_ERR_INVALID_ARGUMENT,
+ * also for a layout with a split factor above 1 (its shards are not boxes).
  */
 reshard_status_t reshard_layout_shard_box(reshard_layout_t layout, int64_t rank,
                                           int64_t* offset, int64_t* extent);

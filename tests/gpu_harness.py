@@ -4,12 +4,13 @@ on both sides; destinations are prefilled, so a missed write, a stray write
 and an out-of-bounds write all show up."""
 from __future__ import annotations
 
+import numpy as np
 import torch
 
 import dtensor_layout_movement_amd as R
 from dtensor_layout_movement_amd import workloads as W
 from reshard_harness import (Plan, assert_boxes_agree, assert_descriptors_in_bounds, box_shape,
-                             oracle_boxes, oracle_dsts)
+                             oracle_boxes, oracle_cut, oracle_dsts, oracle_shapes)
 
 GUARD = 512
 CANARY = 0x5A
@@ -54,6 +55,11 @@ class GuardedShards:
         return bool((lo == CANARY).all().item()) and bool((hi == CANARY).all().item())
 
 
+def shape_nbytes(shapes, dtype):
+    es = torch.empty((), dtype=dtype).element_size()
+    return [int(np.prod(sh)) * es for sh in shapes]
+
+
 def shard_nbytes(boxes, dtype):
     es = torch.empty((), dtype=dtype).element_size()
     out = []
@@ -81,16 +87,14 @@ def run_parity(specs, values, seed, misalign=0, device="cuda", threads=8, execut
         assert_descriptors_in_bounds(plan)
         src_sets, dst_sets = [], []
         for t, spec in enumerate(plan.specs):
-            sboxes = oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements)
-            dboxes = oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements)
-            srcs = GuardedShards(shard_nbytes(sboxes, spec.dtype), dev, misalign)
+            srcs = GuardedShards(shape_nbytes(oracle_shapes(spec, "src"), spec.dtype), dev, misalign)
             g = make(t, spec, dev)
-            for i, piece in enumerate(W.cut(g, sboxes)):
+            for i, piece in enumerate(oracle_cut(spec, g)):
                 if piece is not None:
                     srcs.region(i).copy_(piece.reshape(-1).view(torch.uint8))
             del g
             src_sets.append(srcs)
-            dst_sets.append(GuardedShards(shard_nbytes(dboxes, spec.out_dtype), dev, misalign))
+            dst_sets.append(GuardedShards(shape_nbytes(oracle_shapes(spec, "dst"), spec.out_dtype), dev, misalign))
         src_ptrs = [p for s in src_sets for p in s.ptrs]
         dst_ptrs = [p for d in dst_sets for p in d.ptrs]
         print(f"[parity] {specs[0].name}{'+' if len(specs) > 1 else ''} values={values} seed={seed} "
@@ -100,7 +104,7 @@ def run_parity(specs, values, seed, misalign=0, device="cuda", threads=8, execut
         torch.cuda.synchronize()
         for t, spec in enumerate(plan.specs):
             g = make(t, spec, dev).cpu()
-            srcs_cpu = W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
+            srcs_cpu = oracle_cut(spec, g)
             del g
             want = oracle_dsts(spec, srcs_cpu, threads=threads)
             for i, w in enumerate(want):

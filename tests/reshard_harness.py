@@ -26,10 +26,8 @@ class Plan:
         self.specs = list(specs)
         self.src_layouts, self.dst_layouts = [], []
         for t in self.specs:
-            self.src_layouts.append(R.reshard_layout_create(t.shape, R.dtype_code(t.dtype), t.src_mesh,
-                                                            t.src_placements))
-            self.dst_layouts.append(R.reshard_layout_create(t.shape, R.dtype_code(t.out_dtype), t.dst_mesh,
-                                                            t.dst_placements))
+            self.src_layouts.append(make_layout(t, "src"))
+            self.dst_layouts.append(make_layout(t, "dst"))
         self.handle = R.reshard_plan_create_batched(self.src_layouts, self.dst_layouts)
 
     def src_boxes(self, t):
@@ -37,6 +35,12 @@ class Plan:
 
     def dst_boxes(self, t):
         return lib_boxes(self.dst_layouts[t], self.specs[t].shape)
+
+    def src_shapes(self, t):
+        return lib_shapes(self.src_layouts[t], self.specs[t].shape)
+
+    def dst_shapes(self, t):
+        return lib_shapes(self.dst_layouts[t], self.specs[t].shape)
 
     def stats(self):
         return R.reshard_plan_stats(self.handle)
@@ -56,6 +60,38 @@ class Plan:
         self.close()
 
 
+def make_layout(spec, side):
+    """The library layout of one side of a spec (strided when it has split factors)."""
+    if side == "src":
+        dt, mesh, pl = spec.dtype, spec.src_mesh, spec.src_placements
+    else:
+        dt, mesh, pl = spec.out_dtype, spec.dst_mesh, spec.dst_placements
+    split = spec.split(side)
+    if any(f > 1 for f in split):
+        return R.reshard_layout_create_strided(spec.shape, R.dtype_code(dt), mesh, pl, split)
+    return R.reshard_layout_create(spec.shape, R.dtype_code(dt), mesh, pl)
+
+
+def lib_runs(layout, shape):
+    """Per rank, per dim: the library's runs of global indices."""
+    return [[R.reshard_layout_shard_runs(layout, r, k) for k in range(len(shape))]
+            for r in range(R.reshard_layout_num_ranks(layout))]
+
+
+def lib_shapes(layout, shape):
+    """Local shard shapes (sum of run lengths per dim), any layout."""
+    return [[sum(b - a for a, b in runs) for runs in per_rank] for per_rank in lib_runs(layout, shape)]
+
+
+def oracle_index_lists(spec, side):
+    """Per rank, per dim: the oracle's global index lists."""
+    mesh = spec.src_mesh if side == "src" else spec.dst_mesh
+    pl = spec.src_placements if side == "src" else spec.dst_placements
+    n = int(np.prod(mesh))
+    return [oracle.shard_indices(list(spec.shape), list(mesh), list(pl), list(spec.split(side)), r)
+            for r in range(n)]
+
+
 def lib_boxes(layout, shape):
     n = R.reshard_layout_num_ranks(layout)
     out = []
@@ -73,8 +109,15 @@ def oracle_boxes(shape, mesh, placements):
 
 
 def assert_boxes_agree(plan: Plan):
-    """The library's boxes must equal the oracle's before any buffer is sized."""
+    """The library's boxes (runs, for a strided spec) must equal the oracle's
+    before any buffer is sized."""
     for t, spec in enumerate(plan.specs):
+        if spec.strided:
+            for side, lay in (("src", plan.src_layouts[t]), ("dst", plan.dst_layouts[t])):
+                got = [[[i for a, b in runs for i in range(a, b)] for runs in per_rank]
+                       for per_rank in lib_runs(lay, spec.shape)]
+                assert got == oracle_index_lists(spec, side), (spec, side)
+            continue
         assert plan.src_boxes(t) == oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements), spec
         assert plan.dst_boxes(t) == oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements), spec
 
@@ -90,48 +133,75 @@ FMT = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
 def oracle_dsts(spec, srcs, threads=1):
     """Destination shards by the oracle (gather-then-slice) from given sources;
     for a converting spec, each shard is then converted by the oracle."""
-    boxes = oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements)
-    dsts = [torch.empty(box_shape(b), dtype=spec.dtype) for b in boxes]
-    oracle.reshard(list(spec.shape), torch.empty((), dtype=spec.dtype).element_size(),
-                   list(spec.src_mesh), list(spec.src_placements),
-                   [s if s is not None and s.numel() else None for s in srcs],
-                   list(spec.dst_mesh), list(spec.dst_placements),
-                   [d if d.numel() else None for d in dsts], threads=threads)
+    es = torch.empty((), dtype=spec.dtype).element_size()
+    src_in = [s if s is not None and s.numel() else None for s in srcs]
+    if spec.strided:
+        dsts = [torch.empty([len(ix) for ix in lists], dtype=spec.dtype) for lists in oracle_index_lists(spec, "dst")]
+        oracle.reshard_indexed(list(spec.shape), es, list(spec.src_mesh), list(spec.src_placements),
+                               list(spec.split("src")), src_in, list(spec.dst_mesh), list(spec.dst_placements),
+                               list(spec.split("dst")), [d if d.numel() else None for d in dsts], threads=threads)
+    else:
+        boxes = oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements)
+        dsts = [torch.empty(box_shape(b), dtype=spec.dtype) for b in boxes]
+        oracle.reshard(list(spec.shape), es, list(spec.src_mesh), list(spec.src_placements), src_in,
+                       list(spec.dst_mesh), list(spec.dst_placements),
+                       [d if d.numel() else None for d in dsts], threads=threads)
     if spec.out_dtype != spec.dtype:
         dsts = [oracle.convert(d, FMT[spec.dtype], FMT[spec.out_dtype], threads=threads) for d in dsts]
     return dsts
 
 
+def oracle_shapes(spec, side):
+    """Local shard shapes of one side by the oracle (boxes, or index lists)."""
+    if spec.strided:
+        return [[len(ix) for ix in lists] for lists in oracle_index_lists(spec, side)]
+    mesh = spec.src_mesh if side == "src" else spec.dst_mesh
+    pl = spec.src_placements if side == "src" else spec.dst_placements
+    return [box_shape(b) for b in oracle_boxes(spec.shape, mesh, pl)]
+
+
+def oracle_cut(spec, g):
+    """Source shards of the global tensor g, cut by the oracle's boxes (index
+    lists, for a strided spec)."""
+    if spec.strided:
+        return W.cut_indexed(g, oracle_index_lists(spec, "src"))
+    return W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
+
+
 def sources_for(spec, values, seed, t=0):
-    """Seeded global tensor and its source shards cut with the oracle's boxes."""
+    """Seeded global tensor and its source shards cut with the oracle's boxes
+    (index lists, for a strided spec)."""
     g = W.make_global(spec, values, seed, t)
-    return g, W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
+    return g, oracle_cut(spec, g)
 
 
 def apply_pieces(plan: Plan, srcs_per_tensor, fill=None):
-    """Destination shards built by copying every planned piece on the host."""
+    """Destination shards built by copying every planned piece on the host, at
+    the local offsets the plan reports (for a plain layout those must equal the
+    piece's offset from its shard's box)."""
     out = []
     for t, spec in enumerate(plan.specs):
-        boxes = plan.dst_boxes(t)
-        out.append([torch.full(box_shape(b), 0 if fill is None else fill, dtype=spec.out_dtype)
-                    for b in boxes])
-    sboxes = [plan.src_boxes(t) for t in range(len(plan.specs))]
-    dboxes = [plan.dst_boxes(t) for t in range(len(plan.specs))]
+        out.append([torch.full(shape, 0 if fill is None else fill, dtype=spec.out_dtype)
+                    for shape in plan.dst_shapes(t)])
+    sboxes = [None if s.strided else plan.src_boxes(t) for t, s in enumerate(plan.specs)]
+    dboxes = [None if s.strided else plan.dst_boxes(t) for t, s in enumerate(plan.specs)]
     for i, pc in enumerate(R.reshard_plan_pieces(plan.handle)):
         t = pc["tensor"]
         nd = len(plan.specs[t].shape)
         lo, hi = pc["lo"][:nd], pc["hi"][:nd]
-        slo = sboxes[t][pc["src_rank"]][0]
+        ext = [h - l for l, h in zip(lo, hi)]
+        s_loc, d_loc = pc["src_local"][:nd], pc["dst_local"][:nd]
+        if sboxes[t] is not None:
+            assert s_loc == [l - o for l, o in zip(lo, sboxes[t][pc["src_rank"]][0])], pc
         src = srcs_per_tensor[t][pc["src_rank"]]
-        s_idx = tuple(slice(l - o, h - o) for l, h, o in zip(lo, hi, slo))
-        part = src[s_idx]
+        part = src[tuple(slice(a, a + e) for a, e in zip(s_loc, ext))]
         spec = plan.specs[t]
         if spec.out_dtype != spec.dtype:
             part = oracle.convert(part.contiguous(), FMT[spec.dtype], FMT[spec.out_dtype])
         for d in R.reshard_plan_piece_fanout(plan.handle, i):
-            dlo = dboxes[t][d][0]
-            d_idx = tuple(slice(l - o, h - o) for l, h, o in zip(lo, hi, dlo))
-            out[t][d][d_idx] = part
+            if dboxes[t] is not None:
+                assert d_loc == [l - o for l, o in zip(lo, dboxes[t][d][0])], pc
+            out[t][d][tuple(slice(a, a + e) for a, e in zip(d_loc, ext))] = part
     return out
 
 
@@ -313,8 +383,8 @@ def shard_bytes(plan: Plan):
     """Bytes of every shard, in the src / dst pointer-array order of execute."""
     sb, db = [], []
     for t, spec in enumerate(plan.specs):
-        sb += [int(np.prod(box_shape(b))) * spec.dtype.itemsize for b in plan.src_boxes(t)]
-        db += [int(np.prod(box_shape(b))) * spec.out_dtype.itemsize for b in plan.dst_boxes(t)]
+        sb += [int(np.prod(shape)) * spec.dtype.itemsize for shape in plan.src_shapes(t)]
+        db += [int(np.prod(shape)) * spec.out_dtype.itemsize for shape in plan.dst_shapes(t)]
     return sb, db
 
 

@@ -10,7 +10,7 @@ import oracle_pins as P
 from dtensor_layout_movement_amd import workloads as W
 from gpu_harness import GuardedShards, run_parity, shard_nbytes
 from reshard_harness import Plan, assert_boxes_agree, assert_descriptors_in_bounds, box_shape, oracle_boxes
-from test_planner import narrow_random_specs, random_specs, small_specs
+from test_planner import narrow_random_specs, random_specs, small_specs, strided_random_specs
 
 pytestmark = pytest.mark.gpu
 
@@ -50,7 +50,7 @@ SMALL_FULL = ["worked_example_8x8", "ffn_up_14336x4096", "moe_experts_64x2048x71
               "narrow_columns_4194304x8", "narrow_columns_tp8_2097152x16", "narrow_columns_64b_tp8_1048576x32",
               "narrow_columns_64b_tp4_1048576x32", "narrow_columns_32b_tp4_2097152x16",
               "narrow_columns_16b_tp8_4194304x8",
-              "ffn_up_f32_to_bf16_14336x4096"]
+              "ffn_up_f32_to_bf16_14336x4096", "ffn_up_fsdp2_tp_14336x4096"]
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -412,13 +412,16 @@ def test_two_stage_send_once_then_exchange(chunks):
     streams) reaches the oracle's bytes."""
     from dtensor_layout_movement_amd.two_stage import TwoStagePlan
     from reshard_harness import oracle_dsts
-    specs = list(W.ffn_refit(3, 64, 224).tensors) + [W.ffn_up(448, 320).tensors[0], W.uneven(301, 257).tensors[0]]
+    from reshard_harness import oracle_cut
+    strided = {s.name: s for s in small_specs()}
+    specs = list(W.ffn_refit(3, 64, 224).tensors) + [W.ffn_up(448, 320).tensors[0], W.uneven(301, 257).tensors[0],
+                                                      strided["strided_dst"], strided["strided_both"]]
     ts = TwoStagePlan(specs, chunks=chunks)
     try:
         srcs_d, dsts_d, stag_d, wants = [], [], [], []
         for t, spec in enumerate(specs):
             g = W.make_global(spec, "raw", 31, t)
-            srcs = W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
+            srcs = oracle_cut(spec, g)
             wants.append(oracle_dsts(spec, srcs))
             srcs_d.append([s.cuda() if s is not None else None for s in srcs])
             dsts_d.append([torch.full_like(w, 0, device="cuda") for w in wants[-1]])
@@ -474,6 +477,15 @@ def test_random_layouts_batched(batch):
     dims, nested / replicated / empty shards, several dtypes and conversions),
     six per fused launch."""
     specs = random_specs(100 + batch, 6)
+    run_parity(specs, "raw", batch)
+
+
+@pytest.mark.parametrize("batch", range(3))
+def test_random_strided_layouts_batched(batch):
+    """Seeded random layout pairs with right-to-left (strided) nesting on either
+    side, six per plan, together with three plain random pairs in the same
+    fused launch."""
+    specs = strided_random_specs(700 + batch, 6) + random_specs(800 + batch, 3)
     run_parity(specs, "raw", batch)
 
 

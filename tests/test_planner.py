@@ -17,7 +17,7 @@ import dtensor_layout_movement_amd as R
 import oracle_pins as P
 from dtensor_layout_movement_amd import workloads as W
 from reshard_harness import (Plan, apply_pieces, assert_boxes_agree, assert_descriptors_in_bounds,
-                             box_shape, magic_div,
+                             box_shape, lib_runs, magic_div,
                              oracle_dsts, run_descriptors, sources_for)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -134,7 +134,30 @@ def small_specs():
         T("conv_empty", (5, 3), torch.float32, (4,), (0,), (2,), (1,), torch.float16),
         T("conv_narrow", (4099, 8), torch.float32, (2,), (0,), (4,), (1,), torch.bfloat16),
     ]
-    return specs
+    return specs + strided_specs()
+
+
+def strided_specs():
+    """Right-to-left (strided) nesting on either side: FSDP2 x TP training
+    layouts, holdings of several runs per dim, empty shards, replicas, nesting
+    over three mesh dims, narrow runs and a converting case."""
+    S = W.TensorSpec
+    return [
+        S("strided_fsdp_tp", (96, 40), torch.bfloat16, (2, 4), (0, 0), (2, 2), (RR, 1), src_split=(4, 1)),
+        S("strided_runs", (50, 31), torch.float32, (2, 2), (0, 0), (3,), (1,), src_split=(3, 1)),
+        S("strided_dst", (64, 24), torch.bfloat16, (4,), (1,), (2, 2, 2), (RR, 1, 1), dst_split=(1, 2, 1)),
+        S("strided_both", (3, 40, 12), torch.float32, (2, 3), (1, 1), (2, 2), (1, 2), src_split=(3, 1),
+          dst_split=(2, 1)),
+        S("strided_empty", (5, 7), torch.int16, (4,), (0,), (2,), (1,), src_split=(4,)),
+        S("strided_three", (40, 6), torch.uint8, (2, 2, 2), (0, 0, 0), (2, 2), (1, 0), src_split=(2, 2, 1),
+          dst_split=(1, 3)),
+        S("strided_rep_src", (30, 20), torch.float64, (2, 3), (RR, 0), (2,), (1,), src_split=(1, 3)),
+        S("strided_narrow", (1031, 8), torch.bfloat16, (2,), (0,), (4,), (1,), dst_split=(2,)),
+        S("strided_same", (60, 16), torch.float32, (2, 3), (0, 0), (3, 2), (0, 0), src_split=(3, 1),
+          dst_split=(2, 1)),
+        S("strided_convert", (48, 36), torch.float32, (2, 2), (1, 1), (2, 2), (RR, 0), torch.bfloat16,
+          src_split=(2, 1)),
+    ]
 
 
 def values_for(spec):
@@ -153,8 +176,8 @@ def test_pieces_and_descriptors_match_oracle(spec):
         # byte-level walk of the device table
         sflat = [None if s is None else s.contiguous().view(torch.uint8).reshape(-1).numpy()
                  for s in srcs]
-        dflat = [np.full(int(np.prod(box_shape(b))) * spec.out_dtype.itemsize, 0xA5, dtype=np.uint8)
-                 for b in plan.dst_boxes(0)]
+        dflat = [np.full(int(np.prod(sh)) * spec.out_dtype.itemsize, 0xA5, dtype=np.uint8)
+                 for sh in plan.dst_shapes(0)]
         run_descriptors(plan, sflat, dflat)
         for d, (a, b) in enumerate(zip(dflat, want)):
             assert a.tobytes() == b.view(torch.uint8).numpy().tobytes(), d
@@ -206,6 +229,110 @@ def test_brute_force_random_layout_pairs():
             for a, b in zip(dflat, want):
                 assert a.tobytes() == b.view(torch.uint8).reshape(-1).numpy().tobytes(), spec
         n += 1
+
+
+def test_brute_force_random_strided_pairs():
+    """Random small layout pairs with split factors on either side (DTensor's
+    right-to-left placement): runs, pieces and the byte-level descriptor walk
+    against the oracle's index lists."""
+    rng = random.Random(5)
+    for n in range(220):
+        (shape, smesh, spl, ssp), = P.strided_layouts(rng, 1)
+        (_, dmesh, dpl, dsp), = P.strided_layouts(rng, 1)
+        dpl = tuple(p if p == RR else p % len(shape) for p in dpl)
+        dtype = rng.choice([torch.uint8, torch.bfloat16, torch.float32, torch.float64])
+        spec = T("sbf", shape, dtype, smesh, spl, dmesh, dpl, src_split=ssp, dst_split=dsp)
+        with Plan([spec]) as plan:
+            assert_boxes_agree(plan)
+            assert_descriptors_in_bounds(plan)
+            _, srcs = sources_for(spec, "raw", seed=n)
+            want = oracle_dsts(spec, srcs)
+            got = apply_pieces(plan, [srcs])[0]
+            for a, b in zip(got, want):
+                assert torch.equal(a.view(torch.uint8), b.view(torch.uint8)), spec
+            sflat = [None if s is None else s.view(torch.uint8).reshape(-1).numpy() for s in srcs]
+            dflat = [np.zeros(b.numel() * b.element_size(), dtype=np.uint8) for b in want]
+            run_descriptors(plan, sflat, dflat)
+            for a, b in zip(dflat, want):
+                assert a.tobytes() == b.view(torch.uint8).reshape(-1).numpy().tobytes(), spec
+            st = plan.stats()
+            assert st["bytes_read"] == int(np.prod(shape)) * dtype.itemsize
+
+
+def strided_random_specs(seed, count, max_numel=300_000):
+    """Seeded random layout pairs of moderate size with split factors 1-4 on
+    either side (1-3 dims, meshes of up to three dims, several dtypes)."""
+    rng = random.Random(seed)
+    caps = {1: 200_000, 2: 1500, 3: 120}
+    out = []
+    while len(out) < count:
+        nd = rng.randint(1, 3)
+        shape = tuple(rng.choice([rng.randint(1, 9), rng.randint(1, caps[nd])]) for _ in range(nd))
+        if int(np.prod(shape)) > max_numel:
+            continue
+        def layout():
+            md = rng.randint(1, 3)
+            mesh = tuple(rng.randint(1, 4) for _ in range(md))
+            pl = tuple(rng.choice([RR] + list(range(nd))) for _ in range(md))
+            return mesh, pl, tuple(1 if p == RR else rng.choice([1, 2, 3, 4]) for p in pl)
+        (sm, sp, ss), (dm, dp, ds) = layout(), layout()
+        dtype = rng.choice([torch.uint8, torch.bfloat16, torch.float32, torch.int16])
+        out.append(T(f"srand{seed}_{len(out)}", shape, dtype, sm, sp, dm, dp, src_split=ss, dst_split=ds))
+    return out
+
+
+def test_strided_layout_calls_and_errors():
+    # a split factor on a Replicate mesh dim, or below 1, is refused
+    with pytest.raises(R.ReshardError) as e:
+        R.reshard_layout_create_strided((8, 4), R.DTYPE_F32, (2, 2), (RR, 0), (2, 1))
+    assert e.value.status == R.ERR_INVALID_ARGUMENT
+    with pytest.raises(R.ReshardError):
+        R.reshard_layout_create_strided((8, 4), R.DTYPE_F32, (2,), (0,), (0,))
+    lay = R.reshard_layout_create_strided((8, 4), R.DTYPE_F32, (2, 2), (0, 0), (2, 1))
+    try:
+        # DTensor's documented example: rows {0,1}, {4,5}, {2,3}, {6,7}
+        assert [R.reshard_layout_shard_runs(lay, r, 0) for r in range(4)] == [[(0, 2)], [(4, 6)], [(2, 4)], [(6, 8)]]
+        assert R.reshard_layout_shard_runs(lay, 3, 1) == [(0, 4)]
+        with pytest.raises(R.ReshardError):  # not a box
+            R.reshard_layout_shard_box(lay, 0, 2)
+        with pytest.raises(R.ReshardError):
+            R.reshard_layout_shard_runs(lay, 4, 0)
+        with pytest.raises(R.ReshardError):
+            R.reshard_layout_shard_runs(lay, 0, 2)
+    finally:
+        R.reshard_layout_destroy(lay)
+    # several runs in one shard, and an empty one
+    lay = R.reshard_layout_create_strided((5,), R.DTYPE_U8, (4,), (0,), (4,))
+    try:
+        assert [R.reshard_layout_shard_runs(lay, r, 0) for r in range(4)] == [[(0, 1), (2, 3), (4, 5)],
+                                                                              [(1, 2), (3, 4)], [], []]
+    finally:
+        R.reshard_layout_destroy(lay)
+    # all factors 1: the plain layout, boxes and runs agree
+    lay = R.reshard_layout_create_strided((9, 7), R.DTYPE_F32, (2, 3), (1, 0), (1, 1))
+    try:
+        for r in range(6):
+            off, ext = R.reshard_layout_shard_box(lay, r, 2)
+            for k in range(2):
+                runs = R.reshard_layout_shard_runs(lay, r, k)
+                assert runs == ([(off[k], off[k] + ext[k])] if ext[k] else [])
+    finally:
+        R.reshard_layout_destroy(lay)
+
+
+def test_fsdp2_tp_layout_moves_as_plain_boxes():
+    """FSDP2 x TP right-to-left sharding of an FFN projection gives every rank
+    one run per dim, so the plan is the 16-byte item path of plain boxes."""
+    wl = W.ffn_up_fsdp2_tp()
+    with Plan(wl.tensors) as plan:
+        assert_boxes_agree(plan)
+        assert_descriptors_in_bounds(plan)
+        for r in range(8):
+            assert len(R.reshard_layout_shard_runs(plan.src_layouts[0], r, 0)) == 1
+        descs, _ = R.reshard_plan_descriptors(plan.handle)
+        assert all(D["mode"] == R.DESC_ITEMS and D["unit"] == 16 for D in descs)
+        st = plan.stats()
+        assert st["bytes_read"] == 14336 * 4096 * 2 and st["bytes_written"] == 2 * st["bytes_read"]
 
 
 def random_specs(seed, count, max_numel=400_000):
@@ -305,6 +432,20 @@ def test_random_moderate_layouts_descriptor_walk():
                 assert a.tobytes() == b.view(torch.uint8).reshape(-1).numpy().tobytes(), spec
 
 
+def assert_in_runs(runs, lo, hi, local):
+    """[lo, hi) lies inside one run of every dim, and local is its offset in the
+    shard's buffer (the run's position plus the offset inside the run)."""
+    for k, (a, b) in enumerate(zip(lo, hi)):
+        pos = 0
+        for ra, rb in runs[k]:
+            if ra <= a and b <= rb:
+                assert local[k] == pos + (a - ra), (k, runs[k], a, b, local)
+                break
+            pos += rb - ra
+        else:
+            raise AssertionError(f"dim {k}: [{a}, {b}) in no run of {runs[k]}")
+
+
 def full_workload_plans():
     return [mk() for mk in W.WORKLOADS.values()]
 
@@ -319,29 +460,30 @@ def test_invariants_full_size(wl):
         dst_bytes = 0
         for t, spec in enumerate(wl.tensors):
             es = spec.out_dtype.itemsize
-            for b in plan.dst_boxes(t):
-                dst_bytes += int(np.prod(box_shape(b))) * es
+            for sh in plan.dst_shapes(t):
+                dst_bytes += int(np.prod(sh)) * es
         # I2, I3: write bytes = destination bytes, read bytes = global bytes (no 2x inflation)
         assert st["global_bytes"] == wl.global_bytes
         assert st["bytes_read"] == wl.global_bytes
         assert st["bytes_written"] == dst_bytes
-        # I4: each piece lies in its source box and in every destination box it feeds;
-        # I1: per destination rank, the pieces tile its box exactly once
+        # I4: each piece lies in its source shard and in every destination shard it
+        # feeds (inside one run per dim, at the local offset the plan reports);
+        # I1: per destination rank, the pieces tile its shard exactly once
+        src_runs = [lib_runs(plan.src_layouts[t], s.shape) for t, s in enumerate(wl.tensors)]
+        dst_runs = [lib_runs(plan.dst_layouts[t], s.shape) for t, s in enumerate(wl.tensors)]
         covered = {}
         for i, pc in enumerate(pieces):
             t = pc["tensor"]
             nd = len(wl.tensors[t].shape)
             lo, hi = pc["lo"][:nd], pc["hi"][:nd]
-            slo, shi = plan.src_boxes(t)[pc["src_rank"]]
-            assert all(sl <= l and h <= sh for l, h, sl, sh in zip(lo, hi, slo, shi))
+            assert_in_runs(src_runs[t][pc["src_rank"]], lo, hi, pc["src_local"][:nd])
             vol = int(np.prod([h - l for l, h in zip(lo, hi)]))
             for d in R.reshard_plan_piece_fanout(plan.handle, i):
-                dlo, dhi = plan.dst_boxes(t)[d]
-                assert all(dl <= l and h <= dh for l, h, dl, dh in zip(lo, hi, dlo, dhi))
+                assert_in_runs(dst_runs[t][d], lo, hi, pc["dst_local"][:nd])
                 covered[(t, d)] = covered.get((t, d), 0) + vol
         for t, spec in enumerate(wl.tensors):
-            for d, b in enumerate(plan.dst_boxes(t)):
-                assert covered.get((t, d), 0) == int(np.prod(box_shape(b)))
+            for d, sh in enumerate(plan.dst_shapes(t)):
+                assert covered.get((t, d), 0) == int(np.prod(sh))
         # I6: the same layouts give a byte-identical table
         with Plan(wl.tensors) as again:
             assert R.reshard_plan_descriptors(plan.handle) == R.reshard_plan_descriptors(again.handle)
@@ -352,13 +494,12 @@ def test_pairwise_disjoint_pieces_small():
     written by exactly one piece."""
     for spec in small_specs():
         with Plan([spec]) as plan:
-            boxes = plan.dst_boxes(0)
-            counts = [np.zeros(box_shape(b), dtype=np.int32) for b in boxes]
+            counts = [np.zeros(sh, dtype=np.int32) for sh in plan.dst_shapes(0)]
             nd = len(spec.shape)
             for i, pc in enumerate(R.reshard_plan_pieces(plan.handle)):
                 for d in R.reshard_plan_piece_fanout(plan.handle, i):
-                    dlo = boxes[d][0]
-                    idx = tuple(slice(l - o, h - o) for l, h, o in zip(pc["lo"][:nd], pc["hi"][:nd], dlo))
+                    idx = tuple(slice(a, a + h - l) for a, l, h in zip(pc["dst_local"][:nd], pc["lo"][:nd],
+                                                                      pc["hi"][:nd]))
                     counts[d][idx] += 1
             for c in counts:
                 assert (c == 1).all(), spec.name
@@ -381,7 +522,7 @@ def test_piece_counts_of_workloads():
               "uneven_5000x3001": 42, "ffn_refit_32_layers": 384, "narrow_columns_4194304x8": 8, "ffn_up_f32_to_bf16_14336x4096": 8,
               "narrow_columns_tp8_2097152x16": 16, "narrow_columns_64b_tp8_1048576x32": 16, "narrow_columns_64b_tp4_1048576x32": 8,
               "narrow_columns_32b_tp4_2097152x16": 8, "narrow_columns_16b_tp8_4194304x8": 16,
-              "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1)}
+              "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1), "ffn_up_fsdp2_tp_14336x4096": 16}
     for wl in full_workload_plans():
         with Plan(wl.tensors) as plan:
             assert plan.stats()["n_pieces"] == counts[wl.name]
@@ -808,7 +949,7 @@ def test_two_stage_layout_slices_tile_each_box(wl):
     import oracle
     from dtensor_layout_movement_amd.two_stage import stage1_layout
     for spec in wl.tensors[:9]:
-        mesh1, pl1 = stage1_layout(spec.dst_mesh, spec.dst_placements)
+        mesh1, pl1, _ = stage1_layout(spec.dst_mesh, spec.dst_placements)
         n1 = int(np.prod(mesh1))
         # stage-1 rank r1 has the coordinates of the destination rank that owns its
         # slice, listed in stage-1 mesh order (non-Replicate dims, then Replicate)
@@ -833,6 +974,39 @@ def test_two_stage_layout_slices_tile_each_box(wl):
         for (dlo, dhi), vol in covered.items():
             assert vol == int(np.prod([max(0, h - l) for l, h in zip(dlo, dhi)]))
         assert sorted(rank_map) == list(range(int(np.prod(spec.dst_mesh))))
+
+
+def test_two_stage_strided_destination_slices_tile_each_shard():
+    """With split factors on the destination, the stage-1 layout keeps them on
+    its non-Replicate mesh dims: every stage-1 slice lies in the shard of the
+    destination rank that owns it, and a shard's replica slices tile it (index
+    sets from the oracle)."""
+    import itertools
+    import oracle
+    from dtensor_layout_movement_amd.two_stage import stage1_layout
+    for spec in strided_specs():
+        if spec.dst_split is None:
+            continue
+        mesh1, pl1, sp1 = stage1_layout(spec.dst_mesh, spec.dst_placements, spec.dst_split)
+        order = [i for i, p in enumerate(spec.dst_placements) if p != R.REPLICATE] + \
+                [i for i, p in enumerate(spec.dst_placements) if p == R.REPLICATE]
+        owned = {}
+        for r1 in range(int(np.prod(mesh1))):
+            c1 = np.unravel_index(r1, mesh1)
+            cd = [0] * len(spec.dst_mesh)
+            for j, i in enumerate(order):
+                cd[i] = int(c1[j])
+            d = int(np.ravel_multi_index(cd, spec.dst_mesh))
+            mid = oracle.shard_indices(list(spec.shape), list(mesh1), list(pl1), list(sp1), r1)
+            dst = oracle.shard_indices(list(spec.shape), list(spec.dst_mesh), list(spec.dst_placements),
+                                       list(spec.dst_split), d)
+            cells = set(itertools.product(*mid))
+            assert cells <= set(itertools.product(*dst)), spec.name
+            key = tuple(tuple(x) for x in dst)
+            assert not (owned.get(key, set()) & cells), spec.name  # slices of one shard are disjoint
+            owned[key] = owned.get(key, set()) | cells
+        for key, cells in owned.items():
+            assert cells == set(itertools.product(*key)), spec.name
 
 
 def test_hybrid_routing_bytes():
