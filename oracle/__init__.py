@@ -14,7 +14,8 @@ every destination shard out of it.  This module only marshals arguments.
 Placements are ints: ``-1`` is Replicate, ``k >= 0`` is Shard(k).  Layouts with
 right-to-left (strided) nesting add one split factor per mesh dim (1 = plain):
 ``shard_indices`` and ``reshard_indexed`` take them, on explicit per-dim index
-lists.
+lists.  A source mesh dim may also be Partial (``PARTIAL``, sum):
+``reshard_partial``.
 """
 from __future__ import annotations
 
@@ -70,8 +71,12 @@ def load(path: str = _LIB_PATH) -> ctypes.CDLL:
                                            ctypes.c_int, _I64P, _I32P, _I64P, ctypes.POINTER(ctypes.c_void_p),
                                            ctypes.c_int, _I64P, _I32P, _I64P, ctypes.POINTER(ctypes.c_void_p),
                                            ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+    lib.oracle_reshard_partial.argtypes = [ctypes.c_int, _I64P, ctypes.c_int, ctypes.c_int,
+                                           ctypes.c_int, _I64P, _I32P, ctypes.POINTER(ctypes.c_void_p),
+                                           ctypes.c_int, _I64P, _I32P, ctypes.POINTER(ctypes.c_void_p),
+                                           ctypes.c_int, ctypes.c_int]
     for f in (lib.oracle_num_ranks, lib.oracle_shard_box, lib.oracle_reshard, lib.oracle_convert,
-              lib.oracle_shard_indices, lib.oracle_reshard_indexed):
+              lib.oracle_shard_indices, lib.oracle_reshard_indexed, lib.oracle_reshard_partial):
         f.restype = ctypes.c_int
     if path == _LIB_PATH:
         _lib = lib
@@ -181,6 +186,25 @@ def reshard_indexed(shape, elem_size, src_mesh, src_pl, src_split, src_bufs, dst
 
 # Float formats of oracle_convert, by name.
 FORMATS = {"f32": 0, "bf16": 1, "f16": 2}
+
+# Placement code of a Partial (sum) mesh dim in a source layout.
+PARTIAL = -2
+
+
+def reshard_partial(shape, src_fmt: str, dst_fmt: str, src_mesh, src_pl, src_bufs, dst_mesh, dst_pl, dst_bufs,
+                    check: bool = True, threads: int = 1, lib=None) -> None:
+    """Reshard from a source layout with Partial mesh dims (placement ``PARTIAL``):
+    every destination element is the sum of the contributions, in contribution
+    order, in binary32, rounded once to ``dst_fmt`` ("f32", "bf16", "f16").
+    Buffers as for ``reshard``; the source shards hold ``src_fmt`` elements."""
+    lib = lib or load()
+    srcs = (ctypes.c_void_p * max(1, len(src_bufs)))(*[_addr(b) for b in src_bufs])
+    dsts = (ctypes.c_void_p * max(1, len(dst_bufs)))(*[_addr(b) for b in dst_bufs])
+    rc = lib.oracle_reshard_partial(len(shape), _i64(shape), FORMATS[src_fmt], FORMATS[dst_fmt],
+                                    len(src_mesh), _i64(src_mesh), _i32(src_pl), srcs,
+                                    len(dst_mesh), _i64(dst_mesh), _i32(dst_pl), dsts, int(check), int(threads))
+    if rc:
+        raise OracleError(rc)
 
 
 def convert(values, from_fmt: str, to_fmt: str, threads: int = 1, lib=None):

@@ -40,6 +40,9 @@
  * indices per tensor dim and move element by element; see the comment above
  * index_list.
  *
+ * Partial sources (oracle_reshard_partial) sum their partial tensors; see the
+ * comment above that function.
+ *
  * Built with g++ (plain C++17, std::thread); no HIP.
  */
 #include <atomic>
@@ -596,6 +599,148 @@ int oracle_reshard_indexed(int ndim, const int64_t* shape, int64_t elem_size,
   std::free(count);
   if (own_x) std::free(X);
   return status;
+}
+
+/*
+ * Reshard of one tensor whose source layout holds partial sums.  The write-ups
+ * say only that the refit guide lists the supported layouts (news.bpdata.com
+ * write-up, "practical access and setup" section); the reading taken is
+ * DTensor's Partial("sum") placement: along a source mesh dim marked Partial
+ * (code -2) every coordinate holds a full-size contribution of the same box, and
+ * the tensor is their elementwise sum.  Several Partial mesh dims number their
+ * contributions q = 0, 1, ... row-major over their coordinates.  The sum is
+ * taken in that order, in binary32: it starts from contribution 0 (widened
+ * exactly) and adds each next one with one binary32 rounding per addition
+ * (round to nearest, ties to even); the result is rounded once to the
+ * destination format (as oracle_convert does).  Destination layouts are plain
+ * (no Partial).  Formats as oracle_convert: 0 binary32, 1 bfloat16, 2 binary16.
+ *   src_bufs[s]  shard of source rank s, row-major over its box (boxes as for
+ *                a plain layout, Partial mesh dims splitting nothing)
+ * Checks: replicas of one contribution must hold equal bytes; every element is
+ * covered R_src times by every contribution.  Returns 0 or an OracleStatus.
+ */
+int oracle_reshard_partial(int ndim, const int64_t* shape, int src_fmt, int dst_fmt,
+                           int src_mesh_ndim, const int64_t* src_mesh, const int32_t* src_pl,
+                           const void* const* src_bufs,
+                           int dst_mesh_ndim, const int64_t* dst_mesh, const int32_t* dst_pl,
+                           void* const* dst_bufs, int check, int threads) {
+  constexpr int32_t kPartial = -2;
+  if (src_fmt < 0 || src_fmt > 2 || dst_fmt < 0 || dst_fmt > 2) return ORACLE_BAD_LAYOUT;
+  if (src_mesh_ndim < 1 || src_mesh_ndim > kMaxDims) return ORACLE_BAD_LAYOUT;
+  // the source's boxes: its layout with every Partial mesh dim read as Replicate
+  int32_t plain_pl[kMaxDims];
+  int64_t contributions = 1, copies = 1;
+  for (int m = 0; m < src_mesh_ndim; ++m) {
+    plain_pl[m] = src_pl[m] == kPartial ? kReplicate : src_pl[m];
+    if (src_pl[m] == kPartial) contributions *= src_mesh[m];
+    else if (src_pl[m] == kReplicate) copies *= src_mesh[m];
+  }
+  Layout S{ndim, shape, src_mesh_ndim, src_mesh, plain_pl};
+  Layout D{ndim, shape, dst_mesh_ndim, dst_mesh, dst_pl};
+  if (!layout_ok(S) || !layout_ok(D)) return ORACLE_BAD_LAYOUT;
+  if (check && copies > 254) check = 0;
+  if (threads < 1) threads = 1;
+  const Format& F = kFormats[src_fmt];
+  const Format& T = kFormats[dst_fmt];
+  const size_t es_s = size_t(F.bits / 8), es_d = size_t(T.bits / 8);
+  int64_t numel = 1;
+  for (int k = 0; k < ndim; ++k) numel *= shape[k];
+
+  // 1. Gather every contribution into its own binary32 copy of the tensor.
+  std::vector<std::vector<float>> X((size_t)contributions, std::vector<float>((size_t)numel));
+  std::vector<std::vector<unsigned char>> count;
+  if (check) count.assign((size_t)contributions, std::vector<unsigned char>((size_t)numel, 0));
+  int status = ORACLE_OK;
+  for (int64_t s = 0; s < num_ranks(S) && status == ORACLE_OK; ++s) {
+    // contribution index: the rank's coordinates on the Partial mesh dims, row-major
+    int64_t coord[kMaxDims], r = s, q = 0;
+    for (int m = src_mesh_ndim - 1; m >= 0; --m) {
+      coord[m] = r % src_mesh[m];
+      r /= src_mesh[m];
+    }
+    for (int m = 0; m < src_mesh_ndim; ++m)
+      if (src_pl[m] == kPartial) q = q * src_mesh[m] + coord[m];
+    int64_t lo[kMaxDims], hi[kMaxDims], ext[kMaxDims];
+    box_of(S, s, lo, hi);
+    if (box_empty(ndim, lo, hi)) continue;
+    if (src_bufs[s] == nullptr) {
+      status = ORACLE_NULL_BUFFER;
+      break;
+    }
+    int64_t rows = 1;
+    for (int k = 0; k < ndim; ++k) ext[k] = hi[k] - lo[k];
+    for (int k = 0; k < ndim - 1; ++k) rows *= ext[k];
+    const int64_t run = ext[ndim - 1];
+    const unsigned char* shard = (const unsigned char*)src_bufs[s];
+    float* Xq = X[(size_t)q].data();
+    unsigned char* cq = check ? count[(size_t)q].data() : nullptr;
+    std::atomic<int> mismatch{0};
+    parallel_rows(rows, threads, [&](int64_t a, int64_t b) {
+      for (int64_t row = a; row < b; ++row) {
+        const int64_t g = global_row_offset(ndim, shape, lo, ext, row);
+        for (int64_t j = 0; j < run; ++j) {
+          uint32_t bits = 0;
+          std::memcpy(&bits, shard + (size_t)(row * run + j) * es_s, es_s);
+          // widened exactly to binary32 (oracle_convert's rules; NaN stays NaN)
+          const uint32_t w = src_fmt == 0 ? bits : convert_one(F, kFormats[0], bits);
+          float v;
+          std::memcpy(&v, &w, 4);
+          if (cq && cq[g + j] != 0) {
+            if (std::memcmp(&Xq[g + j], &v, 4) != 0) mismatch.store(1);
+          } else {
+            Xq[g + j] = v;
+          }
+          if (cq) cq[g + j] += 1;
+        }
+      }
+    });
+    if (mismatch.load()) status = ORACLE_REPLICA_MISMATCH;
+  }
+  if (status == ORACLE_OK && check) {
+    for (int64_t q = 0; q < contributions && status == ORACLE_OK; ++q)
+      for (int64_t i = 0; i < numel; ++i)
+        if (count[(size_t)q][(size_t)i] != (unsigned char)copies) {
+          status = ORACLE_COVERAGE_MISMATCH;
+          break;
+        }
+  }
+  if (status != ORACLE_OK) return status;
+
+  // 2. Sum the contributions in order, in binary32.
+  std::vector<float> sum(X[0]);
+  for (int64_t q = 1; q < contributions; ++q) {
+    const std::vector<float>& Xq = X[(size_t)q];
+    for (int64_t i = 0; i < numel; ++i) {
+      volatile float t = sum[(size_t)i] + Xq[(size_t)i];  // one binary32 rounding
+      sum[(size_t)i] = t;
+    }
+  }
+
+  // 3. Slice each destination box out of the sum, rounded to the destination format.
+  for (int64_t d = 0; d < num_ranks(D); ++d) {
+    int64_t lo[kMaxDims], hi[kMaxDims], ext[kMaxDims];
+    box_of(D, d, lo, hi);
+    if (box_empty(ndim, lo, hi)) continue;
+    if (dst_bufs[d] == nullptr) return ORACLE_NULL_BUFFER;
+    int64_t rows = 1;
+    for (int k = 0; k < ndim; ++k) ext[k] = hi[k] - lo[k];
+    for (int k = 0; k < ndim - 1; ++k) rows *= ext[k];
+    const int64_t run = ext[ndim - 1];
+    unsigned char* shard = (unsigned char*)dst_bufs[d];
+    parallel_rows(rows, threads, [&](int64_t a, int64_t b) {
+      for (int64_t row = a; row < b; ++row) {
+        const int64_t g = global_row_offset(ndim, shape, lo, ext, row);
+        for (int64_t j = 0; j < run; ++j) {
+          const float v = sum[(size_t)(g + j)];
+          uint32_t f32;
+          std::memcpy(&f32, &v, 4);
+          const uint32_t out = dst_fmt == 0 ? f32 : convert_one(kFormats[0], T, f32);
+          std::memcpy(shard + (size_t)(row * run + j) * es_d, &out, es_d);
+        }
+      }
+    });
+  }
+  return ORACLE_OK;
 }
 
 /*

@@ -35,6 +35,12 @@ a mismatch.  What pins what:
 * ``pin_end_to_end_strided`` -- whole indexed reshard against gathering the
   global tensor through DTensor's replayed split (no oracle index arithmetic
   on that side), plus its replica / coverage / layout checks.
+* ``pin_partial_vs_numpy`` -- Partial (sum) sources against numpy's binary32
+  additions in contribution order and torch's / numpy's round-to-nearest-even
+  casts, on random layouts with Partial, Replicate and Shard mesh dims.
+* ``pin_partial_closed``   -- hand-derived sums where the order, the start
+  value, the single final rounding or the sign of zero decide the result;
+  exact integer sums; infinities; a replica mismatch.
 """
 from __future__ import annotations
 
@@ -558,9 +564,139 @@ def pin_end_to_end_strided(lib, count=250, seed=29):
         assert e.code == oracle.BAD_LAYOUT
 
 
+# ------------------------------------------------------ partial (sum)
+
+TORCH_FMT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
+
+
+def partial_index(rank, mesh, placements):
+    """Contribution number of a rank: its coordinates on the Partial mesh dims,
+    row-major."""
+    q = 0
+    for c, m, p in zip(coords_of(rank, mesh), mesh, placements):
+        if p == oracle.PARTIAL:
+            q = q * m + c
+    return q
+
+
+def partial_sources(contribs, shape, mesh, placements):
+    """Shard of every source rank: its contribution cut to its box (boxes by
+    nested torch.chunk, Partial dims splitting nothing)."""
+    plain = tuple(W.R if p == oracle.PARTIAL else p for p in placements)
+    out = []
+    for r in range(nranks(mesh)):
+        idx = chunk_indices(shape, mesh, plain, r)
+        if not all(len(i) for i in idx):
+            out.append(None)
+            continue
+        x = contribs[partial_index(r, mesh, placements)]
+        for k, ix in enumerate(idx):
+            x = x.index_select(k, torch.as_tensor(ix, dtype=torch.int64))
+        out.append(x.contiguous())
+    return out
+
+
+def expected_partial(contribs, dst_fmt):
+    """numpy binary32 additions in contribution order, then one cast (round to
+    nearest even) to the destination format."""
+    acc = contribs[0].float().numpy().astype(np.float32)
+    for c in contribs[1:]:
+        acc = np.add(acc, c.float().numpy().astype(np.float32), dtype=np.float32)
+    t = torch.from_numpy(acc)
+    if dst_fmt == "f16":
+        return torch.from_numpy(acc.astype(np.float16))
+    return t.to(TORCH_FMT[dst_fmt])
+
+
+def run_partial(lib, shape, src_fmt, dst_fmt, smesh, spl, dmesh, dpl, contribs, threads=1):
+    srcs = partial_sources(contribs, shape, smesh, spl)
+    dsts = []
+    for r in range(nranks(dmesh)):
+        idx = chunk_indices(shape, dmesh, dpl, r)
+        dsts.append(torch.empty([len(i) for i in idx], dtype=TORCH_FMT[dst_fmt]))
+    oracle.reshard_partial(list(shape), src_fmt, dst_fmt, list(smesh), list(spl), srcs, list(dmesh), list(dpl),
+                           [d if d.numel() else None for d in dsts], threads=threads, lib=lib)
+    return dsts
+
+
+def pin_partial_vs_numpy(lib, count=160, seed=31):
+    rng = random.Random(seed)
+    fmts = [("f32", "f32"), ("bf16", "bf16"), ("f16", "f16"), ("bf16", "f32"), ("f32", "bf16"), ("f32", "f16"),
+            ("f16", "f32")]
+    for n in range(count):
+        nd = rng.randint(1, 3)
+        shape = tuple(rng.randint(1, 9) for _ in range(nd))
+        md = rng.randint(1, 3)
+        smesh = tuple(rng.randint(1, 4) for _ in range(md))
+        spl = [rng.choice([W.R, oracle.PARTIAL] + list(range(nd))) for _ in range(md)]
+        spl[rng.randrange(md)] = oracle.PARTIAL
+        (_, dmesh, dpl), = small_layouts(rng, 1)
+        dpl = tuple(p if p == W.R else p % nd for p in dpl)
+        src_fmt, dst_fmt = rng.choice(fmts)
+        P = 1
+        for m, p in zip(smesh, spl):
+            if p == oracle.PARTIAL:
+                P *= m
+        g = torch.Generator().manual_seed(1000 + n)
+        contribs = [(torch.randn(shape, generator=g) * rng.choice([1e-3, 1.0, 300.0])).to(TORCH_FMT[src_fmt])
+                    for _ in range(P)]
+        got = run_partial(lib, shape, src_fmt, dst_fmt, smesh, spl, dmesh, dpl, contribs)
+        want = expected_partial(contribs, dst_fmt)
+        for r, d in enumerate(got):
+            idx = chunk_indices(shape, dmesh, dpl, r)
+            if d.numel() == 0:
+                continue
+            w = torch.from_numpy(np.ascontiguousarray(want.view(torch.int16 if dst_fmt != "f32" else torch.int32)
+                                                      .numpy()[np.ix_(*idx)]))
+            v = d.view(torch.int16 if dst_fmt != "f32" else torch.int32)
+            assert torch.equal(v, w), (shape, smesh, spl, dmesh, dpl, src_fmt, dst_fmt, r)
+
+
+def pin_partial_closed(lib):
+    def one(vals, src_fmt="f32", dst_fmt="f32"):
+        """Contributions vals[q] (scalars) over a (len(vals),)[Partial] mesh -> one rank."""
+        contribs = [torch.tensor([v], dtype=torch.float64).to(TORCH_FMT[src_fmt]) for v in vals]
+        d, = run_partial(lib, (1,), src_fmt, dst_fmt, (len(vals),), (oracle.PARTIAL,), (1,), (W.R,), contribs)
+        return d
+    # order: binary32 additions in contribution order (1e8 + 1 rounds back to 1e8)
+    assert one([1e8, 1.0, -1e8]).item() == 0.0
+    assert one([1e8, -1e8, 1.0]).item() == 1.0
+    assert one([1.0, 1e8, -1e8]).item() == 0.0
+    # the sum starts from contribution 0, not from +0: the sign of zero survives
+    assert torch.signbit(one([-0.0, -0.0])).item() and not torch.signbit(one([-0.0, 0.0])).item()
+    assert torch.signbit(one([-0.0])).item()
+    # one rounding to bf16 at the end, of the binary32 sum
+    assert one([1.0, 2.0 ** -8, 2.0 ** -8], "bf16", "bf16").float().item() == 1.0 + 2.0 ** -7
+    assert one([1.0, 2.0 ** -8], "bf16", "bf16").float().item() == 1.0        # tie to even
+    assert one([1.0, 3 * 2.0 ** -9], "bf16", "bf16").float().item() == 1.0 + 2.0 ** -7  # above the tie
+    assert one([1.0, 2.0 ** -24, 2.0 ** -24], "f32", "f32").item() == 1.0     # each addition rounds
+    # exact integer sums in every format
+    rng = random.Random(3)
+    for fmt in ("f32", "bf16", "f16"):
+        for _ in range(50):
+            vals = [rng.randint(-16, 16) for _ in range(rng.randint(1, 8))]
+            assert one(vals, fmt, fmt).float().item() == sum(vals), (fmt, vals)
+    # infinities
+    assert one([float("inf"), 1.0]).item() == float("inf")
+    assert np.isnan(one([float("inf"), float("-inf")]).item())
+    assert one([6e4, 6e4], "f32", "f16").float().item() == float("inf")  # 120000 overflows binary16
+    # replicas of one contribution that disagree are reported
+    contribs = [torch.ones(4, 3), torch.ones(4, 3)]
+    srcs = partial_sources(contribs, (4, 3), (2, 2), (oracle.PARTIAL, W.R))
+    srcs[1] = srcs[1].clone()
+    srcs[1][0, 0] = 2.0
+    try:
+        oracle.reshard_partial([4, 3], "f32", "f32", [2, 2], [oracle.PARTIAL, W.R], srcs, [1], [W.R],
+                               [torch.empty(4, 3)], lib=lib)
+        raise AssertionError("replica mismatch not reported")
+    except oracle.OracleError as e:
+        assert e.code == oracle.REPLICA_MISMATCH, e
+
+
 ALL_PINS = (pin_convert_library, pin_convert_nan_payloads, pin_convert_closed,
             pin_worked_example, pin_box_vs_dtensor, pin_box_vs_chunk, pin_end_to_end_chunk,
-            pin_gather, pin_raw_bits, pin_strided_vs_dtensor, pin_strided_closed, pin_end_to_end_strided)
+            pin_gather, pin_raw_bits, pin_strided_vs_dtensor, pin_strided_closed, pin_end_to_end_strided,
+            pin_partial_vs_numpy, pin_partial_closed)
 
 
 def run_all(lib_path: str) -> int:

@@ -64,6 +64,25 @@ def test_pin_end_to_end_strided(oracle_lib):
     P.pin_end_to_end_strided(oracle_lib)
 
 
+def test_pin_partial_vs_numpy(oracle_lib):
+    P.pin_partial_vs_numpy(oracle_lib)
+
+
+def test_pin_partial_closed(oracle_lib):
+    P.pin_partial_closed(oracle_lib)
+
+
+def test_partial_threads_give_same_bytes(oracle_lib):
+    g = torch.Generator().manual_seed(9)
+    contribs = [torch.randn(64, 48, generator=g).to(torch.bfloat16) for _ in range(4)]
+    a = P.run_partial(oracle_lib, (64, 48), "bf16", "bf16", (2, 2, 2), (0, oracle.PARTIAL, oracle.PARTIAL), (3,),
+                      (1,), contribs, threads=1)
+    b = P.run_partial(oracle_lib, (64, 48), "bf16", "bf16", (2, 2, 2), (0, oracle.PARTIAL, oracle.PARTIAL), (3,),
+                      (1,), contribs, threads=8)
+    for x, y in zip(a, b):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
 def test_indexed_threads_give_same_bytes(oracle_lib):
     shape, smesh, spl, ssp = (96, 40), (2, 4), (0, 0), (4, 1)
     g = torch.randn(shape)
@@ -162,6 +181,19 @@ MUTANTS = {
     "indexed_row_order": ("      off += idx[k][row % len] * gstride[k];\n      row /= len;",
                           "      off += idx[k][row / len % len] * gstride[k];\n      row %= len;"),
     "indexed_no_replica_compare": ("if (std::memcmp(X + (size_t)g * es, from, es) != 0) mismatch.store(1);",
+                                   "if (false) mismatch.store(1);"),
+    # partial (sum) sources
+    "partial_reverse_order": ("if (src_pl[m] == kPartial) q = q * src_mesh[m] + coord[m];",
+                              "if (src_pl[m] == kPartial) q = q * src_mesh[m] + (src_mesh[m] - 1 - coord[m]);"),
+    "partial_starts_from_zero": ("  std::vector<float> sum(X[0]);\n  for (int64_t q = 1; q < contributions; ++q) {",
+                                 "  std::vector<float> sum((size_t)numel, 0.0f);\n"
+                                 "  for (int64_t q = 0; q < contributions; ++q) {"),
+    "partial_drops_last": ("  for (int64_t q = 1; q < contributions; ++q) {",
+                           "  for (int64_t q = 1; q < contributions - 1; ++q) {"),
+    "partial_bf16_truncates": ("const uint32_t out = dst_fmt == 0 ? f32 : convert_one(kFormats[0], T, f32);",
+                               "const uint32_t out = dst_fmt == 0 ? f32 : (T.frac == 7 ? f32 >> 16 : "
+                               "convert_one(kFormats[0], T, f32));"),
+    "partial_no_replica_compare": ("if (std::memcmp(&Xq[g + j], &v, 4) != 0) mismatch.store(1);",
                                    "if (false) mismatch.store(1);"),
 }
 
