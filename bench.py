@@ -146,26 +146,35 @@ def plan_timing(R, wl, reps: int) -> dict:
             "upload_median": round(statistics.median(up), 2), "reps": reps}
 
 
+def source_shards(R, W, spec, layout, values: str, seed: int, t: int, dev) -> list:
+    """Seeded source shards of one tensor, one per rank (None when empty): boxes
+    of the global tensor, runs of it for a strided layout, or for a Partial
+    source each rank's box of its own contribution."""
+    nd = len(spec.shape)
+    ranks = range(R.reshard_layout_num_ranks(layout))
+
+    def box(r):
+        off, ext = R.reshard_layout_shard_box(layout, r, nd)
+        return off, [o + e for o, e in zip(off, ext)]
+    if spec.partial:
+        contribs = W.make_contributions(spec, values, seed, t, device=dev)
+        return [W.cut(contribs[W.contribution_of(spec, r)], [box(r)])[0] for r in ranks]
+    g = W.make_global(spec, values, seed, t, device=dev)
+    if spec.strided:
+        lists = [[[i for a, b in R.reshard_layout_shard_runs(layout, r, k) for i in range(a, b)] for k in range(nd)]
+                 for r in ranks]
+        return W.cut_indexed(g, lists)
+    return W.cut(g, [box(r) for r in ranks])
+
+
 def alloc_set(torch, R, wl, lay_src, lay_dst, dev, seed):
     """One set of source shards (seeded values) and destination shards."""
     from dtensor_layout_movement_amd import workloads as W
     src_bufs, dst_bufs = [], []
     for t, spec in enumerate(wl.tensors):
-        nd = len(spec.shape)
-        g = W.make_global(spec, wl.values, seed, t, device=dev)
-        if spec.strided:  # shards are runs of global indices per dim
-            lists = [[[i for a, b in R.reshard_layout_shard_runs(lay_src[t], r, k) for i in range(a, b)]
-                      for k in range(nd)] for r in range(R.reshard_layout_num_ranks(lay_src[t]))]
-            src_bufs += W.cut_indexed(g, lists)
-        else:
-            sboxes = []
-            for r in range(R.reshard_layout_num_ranks(lay_src[t])):
-                off, ext = R.reshard_layout_shard_box(lay_src[t], r, nd)
-                sboxes.append((off, [o + e for o, e in zip(off, ext)]))
-            src_bufs += W.cut(g, sboxes)
-        del g
+        src_bufs += source_shards(R, W, spec, lay_src[t], wl.values, seed, t, dev)
         for r in range(R.reshard_layout_num_ranks(lay_dst[t])):
-            shape = R.local_shape(lay_dst[t], r, nd)
+            shape = R.local_shape(lay_dst[t], r, len(spec.shape))
             dst_bufs.append(torch.empty(shape, dtype=spec.out_dtype, device=dev) if all(shape) else None)
     sp = R.pointer_array([b.data_ptr() if b is not None else 0 for b in src_bufs])
     dp = R.pointer_array([b.data_ptr() if b is not None else 0 for b in dst_bufs])
@@ -367,7 +376,15 @@ def cpu_baseline(torch, R, wl, lay_src, lay_dst, gpu_set, reps: int, single_core
             dsts = [torch.empty(b.shape, dtype=spec.dtype) if b is not None else None for b in dst_bufs[d0:d1]]
             src_in = [x if x is not None and x.numel() else None for x in srcs]
             dst_in = [x if x is not None and x.numel() else None for x in dsts]
-            if spec.strided:  # the oracle's index-list form
+            if spec.partial:  # the oracle's Partial sum, rounded to the destination dtype
+                fmt = {torch.float32: "f32", torch.bfloat16: "bf16", torch.float16: "f16"}
+                fn = oracle.reshard_partial
+                dsts = [torch.empty(b.shape, dtype=spec.out_dtype) if b is not None else None
+                        for b in dst_bufs[d0:d1]]
+                dst_in = [x if x is not None and x.numel() else None for x in dsts]
+                args = (list(spec.shape), fmt[spec.dtype], fmt[spec.out_dtype], list(spec.src_mesh),
+                        list(spec.src_placements), src_in, list(spec.dst_mesh), list(spec.dst_placements), dst_in)
+            elif spec.strided:  # the oracle's index-list form
                 fn = oracle.reshard_indexed
                 args = (list(spec.shape), es, list(spec.src_mesh), list(spec.src_placements), list(spec.split("src")),
                         src_in, list(spec.dst_mesh), list(spec.dst_placements), list(spec.split("dst")), dst_in)

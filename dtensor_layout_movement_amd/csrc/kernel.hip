@@ -1417,6 +1417,111 @@ __device__ __forceinline__ void convert_items(const reshard_descriptor_t& D, con
   }
 }
 
+// ------------------------------------------------------------ partial sums
+//
+// REDUCE mode (Partial sources): item f is up to 8 elements of a row; each
+// element is the binary32 sum, in list order, of the same element of every
+// contribution (source slots refs[src_ptr ...], all at the same offsets),
+// rounded once to the destination format.  The sum starts from contribution 0
+// widened exactly, so that a -0.0 survives, and each addition is one v_add_f32
+// (round to nearest even, denormals kept).  Formats: 0 binary32, 1 bfloat16,
+// 2 binary16.
+
+template <int kFmt>
+__device__ __forceinline__ float widen_elem(uint32_t x) {
+  uint32_t u;
+  if constexpr (kFmt == 0) u = x;
+  else if constexpr (kFmt == 1) u = bf16_to_f32(x);
+  else u = f16_to_f32(x);
+  return __uint_as_float(u);
+}
+
+template <int kFmt>
+__device__ __forceinline__ uint32_t narrow_elem(float v) {
+  const uint32_t u = __float_as_uint(v);
+  if constexpr (kFmt == 0) return u;
+  else if constexpr (kFmt == 1) return f32_to_bf16(u);
+  else return f32_to_f16(u);
+}
+
+// The n <= 8 elements at s as binary32 (the rest 0): 16-byte loads when vec
+// (n == 8 and s 16-byte aligned), else element by element.
+template <int kFmt>
+__device__ __forceinline__ void load_elems(uintptr_t s, uint32_t n, bool vec, float x[8]) {
+  if (vec) {
+    if constexpr (kFmt == 0) {
+      const u32x4 a = __builtin_nontemporal_load(as_global<const u32x4>(s));
+      const u32x4 b = __builtin_nontemporal_load(as_global<const u32x4>(s + 16));
+      x[0] = widen_elem<0>(a.x); x[1] = widen_elem<0>(a.y); x[2] = widen_elem<0>(a.z); x[3] = widen_elem<0>(a.w);
+      x[4] = widen_elem<0>(b.x); x[5] = widen_elem<0>(b.y); x[6] = widen_elem<0>(b.z); x[7] = widen_elem<0>(b.w);
+    } else {
+      const u32x4 a = __builtin_nontemporal_load(as_global<const u32x4>(s));
+      const uint32_t w[4] = {a.x, a.y, a.z, a.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        x[2 * k] = widen_elem<kFmt>(w[k] & 0xffffu);
+        x[2 * k + 1] = widen_elem<kFmt>(w[k] >> 16);
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (uint32_t k = 0; k < 8; ++k) {
+    if (k < n) {
+      if constexpr (kFmt == 0) x[k] = widen_elem<0>(*as_global<const u32_u>(s + 4 * k));
+      else x[k] = widen_elem<kFmt>(*as_global<const u16_u>(s + 2 * k));
+    } else {
+      x[k] = 0.0f;
+    }
+  }
+}
+
+template <int kSrc, int kDst, class Sh>
+__device__ __forceinline__ void reduce_items(const reshard_descriptor_t& D, const uint32_t* __restrict__ refs,
+                                             const Sh& sh, uint32_t lo, uint32_t hi, bool aligned) {
+  static_assert(rs::kItemsPerThread == 1, "a REDUCE tile holds one item per thread");
+  constexpr uint32_t kEs = kSrc == 0 ? 4 : 2, kEd = kDst == 0 ? 4 : 2;
+  const uint32_t f = lo + threadIdx.x;
+  if (f >= hi) return;
+  const ItemPos o = item_pos(D, f);
+  const uint32_t e0 = o.col * rs::kConvertElems;
+  const uint32_t n = min(rs::kConvertElems, D.run_bytes - e0);
+  const uint64_t soff = o.src + uint64_t(e0) * kEs, doff = o.dst + uint64_t(e0) * kEd;
+  const uint32_t parts = D.unit & 0xfffu;
+  const bool vec = aligned && n == rs::kConvertElems && ((soff | doff) & 15) == 0;
+  float acc[8];
+  load_elems<kSrc>(sh.ptr(refs[D.src_ptr]) + soff, n, vec, acc);
+#pragma unroll 2
+  for (uint32_t p = 1; p < parts; ++p) {
+    float x[8];
+    load_elems<kSrc>(sh.ptr(refs[D.src_ptr + p]) + soff, n, vec, x);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[k] = acc[k] + x[k];
+  }
+  uint32_t y[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) y[k] = narrow_elem<kDst>(acc[k]);
+  for (uint32_t r = 0; r < D.fanout; ++r) {
+    const uintptr_t d = sh.dst(r) + doff;
+    if (vec) {
+      if constexpr (kEd == 4) {
+        __builtin_nontemporal_store(u32x4{y[0], y[1], y[2], y[3]}, as_global<u32x4>(d));
+        __builtin_nontemporal_store(u32x4{y[4], y[5], y[6], y[7]}, as_global<u32x4>(d + 16));
+      } else {
+        const u32x4 v{y[0] | (y[1] << 16), y[2] | (y[3] << 16), y[4] | (y[5] << 16), y[6] | (y[7] << 16)};
+        __builtin_nontemporal_store(v, as_global<u32x4>(d));
+      }
+      continue;
+    }
+#pragma unroll
+    for (uint32_t k = 0; k < 8; ++k) {
+      if (k >= n) break;
+      if constexpr (kEd == 4) *as_global<u32_u>(d + 4 * k) = y[k];
+      else *as_global<u16_u>(d + 2 * k) = uint16_t(y[k]);
+    }
+  }
+}
+
 // ------------------------------------------------------------ gather rows
 //
 // A RESHARD_DESC_GATHER_ROWS tile writes kGatherTileBytes consecutive bytes of
@@ -1560,6 +1665,7 @@ enum KernelKind : int {
   kKindOctets = 9,   // every descriptor a 16-byte window band of eight 2-byte column
                      // runs (window_octets): no LDS
   kKindGatherRows = 10,  // every descriptor RESHARD_DESC_GATHER_ROWS (gather_rows)
+  kKindReduce = 11,      // every descriptor RESHARD_DESC_REDUCE (reduce_items)
   kKindAligned = 16, // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
@@ -1624,6 +1730,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
                                   kKind == kKindBands16 || kKind == kKindRuns32 || kKind == kKindOctets
                             ? uint32_t(RESHARD_DESC_WINDOW)
                         : kKind == kKindGatherRows ? uint32_t(RESHARD_DESC_GATHER_ROWS)
+                        : kKind == kKindReduce ? uint32_t(RESHARD_DESC_REDUCE)
                                                : unit_mode >> 16;
   if constexpr (kKind == kKindQuadRows) {
     const Shards<kKarg> wsh{table, &karg, refs};
@@ -1653,6 +1760,24 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   if constexpr (kKind == kKindGatherRows) {
     const Shards<kKarg> gsh{table, &karg, refs};
     gather_rows(D, segs, refs, gsh, t - tile_begin[lo]);
+    return;
+  }
+  if constexpr (kKind == kKindReduce) {
+    (void)mode;
+    const uint32_t items = D.extent[0] * D.extent[1] * D.extent[2] * D.row_items;
+    const uint32_t first = (t - tile_begin[lo]) * rs::kTileItems;
+    const uint32_t last = min(first + rs::kTileItems, items);
+    const Shards<kKarg> rsh{table, &karg, refs + D.dst_ref_begin};
+    const bool aligned = (flags & kAllAligned16) != 0;
+    switch (unit >> 12) {  // source format | destination format << 2
+      case 0 | (0 << 2): reduce_items<0, 0>(D, refs, rsh, first, last, aligned); break;
+      case 0 | (1 << 2): reduce_items<0, 1>(D, refs, rsh, first, last, aligned); break;
+      case 0 | (2 << 2): reduce_items<0, 2>(D, refs, rsh, first, last, aligned); break;
+      case 1 | (1 << 2): reduce_items<1, 1>(D, refs, rsh, first, last, aligned); break;
+      case 1 | (0 << 2): reduce_items<1, 0>(D, refs, rsh, first, last, aligned); break;
+      case 2 | (2 << 2): reduce_items<2, 2>(D, refs, rsh, first, last, aligned); break;
+      default: reduce_items<2, 0>(D, refs, rsh, first, last, aligned); break;
+    }
     return;
   }
   if constexpr (kKind == kKindOctets) {
@@ -1772,6 +1897,8 @@ hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_des
       return RS_LAUNCH(kKindOctets);
     case kKindGatherRows:
       return RS_LAUNCH(kKindGatherRows);
+    case kKindReduce:
+      return RS_LAUNCH(kKindReduce);
     default:
       return RS_LAUNCH(kKindAll);
   }
@@ -1859,7 +1986,7 @@ int kernel_kind_gather_rows() { return kKindGatherRows; }
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
   bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, bands16 = true, runs32 = true;
-  bool octets = true, gather = true;
+  bool octets = true, gather = true, reduce = true;
   bool window = false;
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
@@ -1873,9 +2000,11 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
     if (!runs32_band(D, segs)) runs32 = false;
     if (!octets_band(D, segs)) octets = false;
     if (D.mode != RESHARD_DESC_GATHER_ROWS) gather = false;
+    if (D.mode != RESHARD_DESC_REDUCE) reduce = false;
     if (D.mode == RESHARD_DESC_WINDOW) window = true;
   }
   if (gather && !descs.empty()) return kKindGatherRows;
+  if (reduce && !descs.empty()) return kKindReduce;
   return items16 ? kKindItems16 : chunks ? kKindChunks : octets ? kKindOctets : quad_rows ? kKindQuadRows
          : runs ? kKindRuns
          : runs64 ? kKindRuns64 : bands16 ? kKindBands16 : runs32 ? kKindRuns32 : window ? kKindAll : kKindCopy;

@@ -133,6 +133,49 @@ SourceGrid make_grid(int ndim, const std::vector<Group>& groups, size_t g_begin,
   return G;
 }
 
+// Calls fn(box, source group) for every cell of the source grid that
+// overlaps dbox (the overlap as box), in row-major cell order.
+template <class Fn>
+reshard_status_t for_each_cell(const SourceGrid& grid, const Box& dbox, int nd, std::string* err, Fn fn) {
+  // per dim, the range of source intervals that overlap the destination box
+  int64_t first[kMaxDims], last[kMaxDims], idx[kMaxDims];
+  for (int k = 0; k < nd; ++k) {
+    const auto& v = grid.iv[k];
+    auto lo_it = std::upper_bound(v.begin(), v.end(), std::make_pair(dbox.lo[k], INT64_MAX));
+    first[k] = std::max<int64_t>(0, int64_t(lo_it - v.begin()) - 1);
+    last[k] = first[k];
+    while (last[k] + 1 < int64_t(v.size()) && v[last[k] + 1].first < dbox.hi[k]) ++last[k];
+    idx[k] = first[k];
+  }
+  for (;;) {  // every cell in the product of those ranges
+    int64_t cell = 0;
+    Box box;
+    bool empty = false;
+    for (int k = 0; k < nd; ++k) {
+      cell += idx[k] * grid.cell_stride[k];
+      box.lo[k] = std::max(dbox.lo[k], grid.iv[k][idx[k]].first);
+      box.hi[k] = std::min(dbox.hi[k], grid.iv[k][idx[k]].second);
+      if (box.hi[k] <= box.lo[k]) empty = true;
+    }
+    if (!empty) {
+      const int64_t sg = grid.group_of(cell);
+      if (sg < 0) {
+        *err = "internal: source grid cell without a rank";
+        return RESHARD_ERR_INVALID_ARGUMENT;
+      }
+      fn(box, sg);
+    }
+    int k = nd - 1;
+    while (k >= 0 && idx[k] == last[k]) {
+      idx[k] = first[k];
+      --k;
+    }
+    if (k < 0) break;
+    ++idx[k];
+  }
+  return RESHARD_OK;
+}
+
 struct Dim {
   int64_t e;   // extent
   int64_t ss;  // source stride, bytes
@@ -232,24 +275,26 @@ void emit(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_begin, uin
   P->descs.push_back(D);
 }
 
-// RESHARD_DESC_CONVERT descriptors for rows of `run` elements (outer dims
-// inner -> outer, byte strides of each side), split like emit() does.
+// RESHARD_DESC_CONVERT (or RESHARD_DESC_REDUCE) descriptors for rows of `run`
+// elements (outer dims inner -> outer, byte strides of each side), split like
+// emit() does; `unit` is the descriptor's conversion (or contributions and
+// formats) field.
 void emit_convert(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_begin, uint32_t fanout,
-                  int64_t src_off, int64_t dst_off, int64_t run, Dims outer, int conv, int64_t es_s,
-                  int64_t es_d) {
+                  int64_t src_off, int64_t dst_off, int64_t run, Dims outer, uint32_t unit, int64_t es_s,
+                  int64_t es_d, uint16_t mode = RESHARD_DESC_CONVERT) {
   if (outer.size() > 3) {
     Dim top = outer.back();
     outer.pop_back();
     for (int64_t i = 0; i < top.e; ++i)
       emit_convert(P, piece, src_ptr, ref_begin, fanout, src_off + i * top.ss, dst_off + i * top.sd,
-                   run, outer, conv, es_s, es_d);
+                   run, outer, unit, es_s, es_d, mode);
     return;
   }
   const int64_t max_run = kMaxRunBytes / 4;  // elements: every row stays under kMaxRunBytes per side
   if (run > max_run) {
     for (int64_t c = 0; c < run; c += max_run)
       emit_convert(P, piece, src_ptr, ref_begin, fanout, src_off + c * es_s, dst_off + c * es_d,
-                   std::min<int64_t>(max_run, run - c), outer, conv, es_s, es_d);
+                   std::min<int64_t>(max_run, run - c), outer, unit, es_s, es_d, mode);
     return;
   }
   const uint64_t row_items = uint64_t(run + kConvertElems - 1) / kConvertElems;
@@ -262,9 +307,9 @@ void emit_convert(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_be
       const int64_t h = outer[k].e / 2;
       a[k].e = h;
       b[k].e = outer[k].e - h;
-      emit_convert(P, piece, src_ptr, ref_begin, fanout, src_off, dst_off, run, a, conv, es_s, es_d);
+      emit_convert(P, piece, src_ptr, ref_begin, fanout, src_off, dst_off, run, a, unit, es_s, es_d, mode);
       emit_convert(P, piece, src_ptr, ref_begin, fanout, src_off + h * outer[k].ss,
-                   dst_off + h * outer[k].sd, run, b, conv, es_s, es_d);
+                   dst_off + h * outer[k].sd, run, b, unit, es_s, es_d, mode);
       return;
     }
   }
@@ -284,8 +329,8 @@ void emit_convert(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_be
   }
   D.run_bytes = uint32_t(run);
   D.row_items = uint32_t(row_items);
-  D.unit = uint16_t(conv);
-  D.mode = RESHARD_DESC_CONVERT;
+  D.unit = uint16_t(unit);
+  D.mode = mode;
   D.src_ptr = src_ptr;
   D.dst_ref_begin = ref_begin;
   D.fanout = fanout;
@@ -303,7 +348,7 @@ void emit_convert(HostPlan* P, uint32_t piece, uint32_t src_ptr, uint32_t ref_be
 // converting reshard, conv != 0).
 void describe_piece(HostPlan* P, uint32_t piece_idx, uint32_t src_ptr, uint32_t ref_begin,
                     uint32_t fanout, const Box& piece, const Box& sbox, const Box& dbox, int ndim,
-                    int64_t es_s, int64_t es_d, int conv) {
+                    int64_t es_s, int64_t es_d, int conv, uint32_t reduce_unit = 0) {
   int64_t s_stride[kMaxDims], d_stride[kMaxDims];  // elements
   int64_t ss = 1, sd = 1;
   for (int k = ndim - 1; k >= 0; --k) {
@@ -341,11 +386,19 @@ void describe_piece(HostPlan* P, uint32_t piece_idx, uint32_t src_ptr, uint32_t 
     outer[j].ss *= es_s;
     outer[j].sd *= es_d;
   }
-  if (conv == 0)
+  if (reduce_unit != 0)
+    emit_convert(P, piece_idx, src_ptr, ref_begin, fanout, src_off * es_s, dst_off * es_d, run, outer,
+                 reduce_unit, es_s, es_d, RESHARD_DESC_REDUCE);
+  else if (conv == 0)
     emit(P, piece_idx, src_ptr, ref_begin, fanout, src_off * es_s, dst_off * es_d, run * es_s, outer);
   else
     emit_convert(P, piece_idx, src_ptr, ref_begin, fanout, src_off * es_s, dst_off * es_d, run, outer,
-                 conv, es_s, es_d);
+                 uint32_t(conv), es_s, es_d);
+}
+
+// Float format code of a REDUCE descriptor: 0 binary32, 1 bfloat16, 2 binary16.
+uint32_t float_format(int dtype) {
+  return dtype == RESHARD_DTYPE_BF16 ? 1u : dtype == RESHARD_DTYPE_F16 ? 2u : 0u;
 }
 
 // Copy descriptors of every piece of one tensor, in piece order.
@@ -358,6 +411,15 @@ void emit_pieces(HostPlan* P, int t, size_t pc0, size_t pc1) {
     const Group& dgrp = P->dst_groups[pc.dst_group];
     const uint32_t ref_begin = uint32_t(P->refs.size());
     for (int64_t r : dgrp.ranks) P->refs.push_back(uint32_t(P->dst_base[t] + r));
+    if (!pc.src_ranks.empty()) {  // Partial: the contributions' source slots follow the fan-out
+      const uint32_t list = uint32_t(P->refs.size());
+      for (int64_t r : pc.src_ranks) P->refs.push_back(uint32_t(P->src_base[t] + r));
+      const uint32_t unit = uint32_t(pc.src_ranks.size()) | (float_format(P->src[t].dtype) << 12) |
+                            (float_format(P->dst[t].dtype) << 14);
+      describe_piece(P, uint32_t(i), list, ref_begin, uint32_t(dgrp.ranks.size()), pc.box, pc.sframe,
+                     pc.dframe, nd, es_s, es_d, conv, unit);
+      continue;
+    }
     describe_piece(P, uint32_t(i), uint32_t(P->src_base[t] + pc.src_rank), ref_begin,
                    uint32_t(dgrp.ranks.size()), pc.box, pc.sframe, pc.dframe, nd, es_s, es_d, conv);
   }
@@ -643,6 +705,7 @@ void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1) {
   emit_pieces(P, t, pc0, pc1);
   if (P->conv[t] != 0) return;  // converting rows always go element-group by element-group
   if (P->src[t].strided || P->dst[t].strided) return;  // bands assume one box per rank
+  if (P->src[t].partial) return;                         // sums go element group by element group
   bool narrow = false, chunked = false;
   for (size_t i = d0; i < P->descs.size(); ++i) {
     const reshard_descriptor_t& D = P->descs[i];
@@ -913,8 +976,9 @@ bool make_layout(int ndim, const int64_t* shape, int dtype, int mesh_ndim, const
       *err = "mesh_shape[" + std::to_string(m) + "] must be in [1, 2^20]";
       return false;
     }
-    if (placements[m] != RESHARD_REPLICATE && (placements[m] < 0 || placements[m] >= ndim)) {
-      *err = "placements[" + std::to_string(m) + "] must be RESHARD_REPLICATE or a tensor dim";
+    if (placements[m] != RESHARD_REPLICATE && placements[m] != RESHARD_PARTIAL &&
+        (placements[m] < 0 || placements[m] >= ndim)) {
+      *err = "placements[" + std::to_string(m) + "] must be RESHARD_REPLICATE, RESHARD_PARTIAL or a tensor dim";
       return false;
     }
     L.mesh[m] = mesh[m];
@@ -924,11 +988,15 @@ bool make_layout(int ndim, const int64_t* shape, int dtype, int mesh_ndim, const
       *err = "split_factors[" + std::to_string(m) + "] must be in [1, 2^20]";
       return false;
     }
-    if (L.split[m] > 1 && placements[m] == RESHARD_REPLICATE) {
-      *err = "split_factors[" + std::to_string(m) + "] > 1 on a Replicate mesh dim";
+    if (L.split[m] > 1 && placements[m] < 0) {
+      *err = "split_factors[" + std::to_string(m) + "] > 1 on a Replicate or Partial mesh dim";
       return false;
     }
     if (L.split[m] > 1) L.strided = true;
+    if (placements[m] == RESHARD_PARTIAL) {
+      L.partial = true;
+      L.n_partial *= mesh[m];
+    }
     L.nranks *= mesh[m];
     if (L.nranks > (int64_t(1) << 24)) {
       *err = "mesh has more than 2^24 ranks";
@@ -950,13 +1018,25 @@ void shard_box(const Layout& L, int64_t rank, Box* out) {
     out->hi[k] = L.shape[k];
   }
   for (int m = 0; m < L.mesh_ndim; ++m) {
-    if (L.place[m] == RESHARD_REPLICATE) continue;
+    if (L.place[m] < 0) continue;  // Replicate or Partial: no split
     const int k = L.place[m];
     const int64_t lo = out->lo[k], hi = out->hi[k];
     const int64_t chunk = (hi - lo + L.mesh[m] - 1) / L.mesh[m];
     out->lo[k] = std::min(hi, lo + coord[m] * chunk);
     out->hi[k] = std::min(hi, lo + (coord[m] + 1) * chunk);
   }
+}
+
+int64_t partial_index(const Layout& L, int64_t rank) {
+  int64_t coord[kMaxMeshDims];
+  for (int m = L.mesh_ndim - 1; m >= 0; --m) {
+    coord[m] = rank % L.mesh[m];
+    rank /= L.mesh[m];
+  }
+  int64_t q = 0;
+  for (int m = 0; m < L.mesh_ndim; ++m)
+    if (L.place[m] == RESHARD_PARTIAL) q = q * L.mesh[m] + coord[m];
+  return q;
 }
 
 Runs shard_runs(const Layout& L, int64_t rank, int dim) {
@@ -1045,6 +1125,19 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
              " to dtype " + std::to_string(D.dtype);
       return RESHARD_ERR_LAYOUT_MISMATCH;
     }
+    if (D.partial) {
+      *err = "tensor " + std::to_string(t) + ": a destination layout cannot be Partial";
+      return RESHARD_ERR_LAYOUT_MISMATCH;
+    }
+    if (S.partial) {
+      const bool fp = S.dtype == RESHARD_DTYPE_F32 || S.dtype == RESHARD_DTYPE_BF16 || S.dtype == RESHARD_DTYPE_F16;
+      if (!fp || S.strided || D.strided || S.n_partial > kMaxPartials) {
+        *err = "tensor " + std::to_string(t) +
+               ": a Partial source needs F32, BF16 or F16 elements, no split factors on either side and at most " +
+               std::to_string(kMaxPartials) + " contributions";
+        return RESHARD_ERR_LAYOUT_MISMATCH;
+      }
+    }
     P->conv.push_back(conv);
     P->src.push_back(S);
     P->dst.push_back(D);
@@ -1088,56 +1181,44 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
     if (sg0 == sg1) continue;  // empty tensor
 
     SourceGrid grid = make_grid(nd, P->src_groups, sg0, sg1);
+    if (S.partial)  // every contribution of a box in the same group, split by contribution
+      for (size_t g = sg0; g < sg1; ++g) {
+        Group& G = P->src_groups[g];
+        G.parts.assign(size_t(S.n_partial), {});
+        for (int64_t r : G.ranks) G.parts[size_t(partial_index(S, r))].push_back(r);
+      }
     const size_t pc0 = P->pieces.size();
     for (size_t g = dg0; g < dg1; ++g) {
       const Group& dgrp = P->dst_groups[g];
-      // per dim, the range of source intervals that overlap this destination box
-      int64_t first[kMaxDims], last[kMaxDims], idx[kMaxDims];
-      for (int k = 0; k < nd; ++k) {
-        const auto& v = grid.iv[k];
-        auto lo_it = std::upper_bound(v.begin(), v.end(), std::make_pair(dgrp.box.lo[k], INT64_MAX));
-        first[k] = std::max<int64_t>(0, int64_t(lo_it - v.begin()) - 1);
-        last[k] = first[k];
-        while (last[k] + 1 < int64_t(v.size()) && v[last[k] + 1].first < dgrp.box.hi[k]) ++last[k];
-        idx[k] = first[k];
-      }
-      for (;;) {  // every cell in the product of those ranges
-        int64_t cell = 0;
-        Box box;
-        bool empty = false;
-        for (int k = 0; k < nd; ++k) {
-          cell += idx[k] * grid.cell_stride[k];
-          box.lo[k] = std::max(dgrp.box.lo[k], grid.iv[k][idx[k]].first);
-          box.hi[k] = std::min(dgrp.box.hi[k], grid.iv[k][idx[k]].second);
-          if (box.hi[k] <= box.lo[k]) empty = true;
-        }
-        if (!empty) {
-          const int64_t sg = grid.group_of(cell);
-          if (sg < 0) {
-            *err = "internal: source grid cell without a rank";
-            return RESHARD_ERR_INVALID_ARGUMENT;
-          }
-          const Group& sgrp = P->src_groups[sg];
-          // least-loaded replica of this source box; ties go to the lowest rank
-          int64_t best = sgrp.ranks[0];
-          for (int64_t r : sgrp.ranks)
+      const reshard_status_t st = for_each_cell(grid, dgrp.box, nd, err, [&](const Box& box, int64_t sg) {
+        const Group& sgrp = P->src_groups[sg];
+        // least-loaded replica of this source box; ties go to the lowest rank
+        auto least_loaded = [&](const std::vector<int64_t>& ranks) {
+          int64_t best = ranks[0];
+          for (int64_t r : ranks)
             if (load[P->src_base[t] + r] < load[P->src_base[t] + best]) best = r;
-          const int64_t bytes = box_numel(nd, box) * es;
-          load[P->src_base[t] + best] += bytes;
-          P->pieces.push_back(Piece{t, best, sg, int64_t(g), box, bytes, sgrp.box, dgrp.box});
-          const int64_t fanout = int64_t(dgrp.ranks.size());
-          P->bytes_read += bytes;
-          P->bytes_written += box_numel(nd, box) * D.elem_size * fanout;
-          P->n_dst_writes += fanout;
+          return best;
+        };
+        const int64_t bytes = box_numel(nd, box) * es;
+        Piece pc{t, 0, sg, int64_t(g), box, bytes, sgrp.box, dgrp.box, {}};
+        if (S.partial) {  // one replica of every contribution, in contribution order
+          for (const auto& part : sgrp.parts) {
+            const int64_t r = least_loaded(part);
+            load[P->src_base[t] + r] += bytes;
+            pc.src_ranks.push_back(r);
+          }
+          pc.src_rank = pc.src_ranks[0];
+        } else {
+          pc.src_rank = least_loaded(sgrp.ranks);
+          load[P->src_base[t] + pc.src_rank] += bytes;
         }
-        int k = nd - 1;
-        while (k >= 0 && idx[k] == last[k]) {
-          idx[k] = first[k];
-          --k;
-        }
-        if (k < 0) break;
-        ++idx[k];
-      }
+        const int64_t fanout = int64_t(dgrp.ranks.size());
+        P->bytes_read += bytes * S.n_partial;
+        P->bytes_written += box_numel(nd, box) * D.elem_size * fanout;
+        P->n_dst_writes += fanout;
+        P->pieces.push_back(std::move(pc));
+      });
+      if (st != RESHARD_OK) return st;
     }
     emit_tensor(P, t, pc0, P->pieces.size());
   }

@@ -33,8 +33,17 @@ struct Layout {
   int32_t place[kMaxMeshDims] = {};
   int64_t split[kMaxMeshDims] = {};  // split factor of each mesh dim (1 = plain Shard / Replicate)
   bool strided = false;              // some split factor above 1
+  int64_t n_partial = 1;             // contributions: product of the Partial mesh dims' sizes
+  bool partial = false;              // some mesh dim is Partial (sum)
   int64_t nranks = 0;
 };
+
+// Contribution number of `rank` under a layout with Partial mesh dims: its
+// coordinates on those dims, row-major (0 for a layout without them).
+int64_t partial_index(const Layout& L, int64_t rank);
+
+// Contributions one REDUCE descriptor can sum (12 bits of its unit field).
+constexpr int64_t kMaxPartials = 4095;
 
 struct Box {
   int64_t lo[kMaxDims];
@@ -75,6 +84,7 @@ struct Group {
   Box box;
   std::vector<int64_t> ranks;  // ascending
   Runs runs[kMaxDims];         // strided layouts only
+  std::vector<std::vector<int64_t>> parts;  // Partial layouts only: ranks by contribution
 };
 
 // One overlap of a unique source box and a unique destination box.  A frame
@@ -90,6 +100,7 @@ struct Piece {
   Box box;            // global coordinates
   int64_t bytes;
   Box sframe, dframe;
+  std::vector<int64_t> src_ranks;  // Partial sources: the rank read for each contribution
 };
 
 // Tiling.  One workgroup of kTileThreads threads copies one tile of one

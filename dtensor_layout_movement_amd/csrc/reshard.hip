@@ -94,7 +94,8 @@ struct Group {
 
 // The launches of one execute.  Only the general build (rs::kKindAll) runs
 // item, chunk and convert descriptors together with window bands, or bands of
-// several kinds together (gather-rows bands run in their own build only), and
+// several kinds together (gather-rows bands and Partial sums run in their own
+// builds only), and
 // it stages bands through LDS and holds more registers, so
 // a plan that mixes them would run everything slower.  Instead the descriptors
 // that are not bands share one launch (the item, chunk or copy build already
@@ -106,7 +107,8 @@ std::vector<Group> launch_groups(const rs::HostPlan& H) {
   std::vector<Group> bands;   // bands by kind, in order of first appearance
   std::vector<reshard_descriptor_t> one(1);
   for (uint32_t i = 0; i < uint32_t(H.descs.size()); ++i) {
-    if (H.descs[i].mode != RESHARD_DESC_WINDOW && H.descs[i].mode != RESHARD_DESC_GATHER_ROWS) {
+    if (H.descs[i].mode != RESHARD_DESC_WINDOW && H.descs[i].mode != RESHARD_DESC_GATHER_ROWS &&
+        H.descs[i].mode != RESHARD_DESC_REDUCE) {
       rows.add(i, H);
       continue;
     }
@@ -186,8 +188,14 @@ void build_image_locked(reshard_plan_s* p) {
     t += rs::tile_groups(g.tiles);
     launches.push_back(L);
   }
+  // the fan-out list in absolute slots of the pointer array (sources first,
+  // then destinations); a REDUCE descriptor's list of contributions holds
+  // source slots, which are absolute already
   uint32_t* r = reinterpret_cast<uint32_t*>(img.data() + refs_off);
   for (size_t i = 0; i < H.refs.size(); ++i) r[i] = uint32_t(H.n_src_ptrs) + H.refs[i];
+  for (const reshard_descriptor_t& D : H.descs)
+    if (D.mode == RESHARD_DESC_REDUCE)
+      for (uint32_t q = 0; q < (D.unit & 0xfffu); ++q) r[D.src_ptr + q] = H.refs[D.src_ptr + q];
   // window segments as planned: a source segment indexes the source pointers,
   // which come first in the pointer array; a destination segment indexes the
   // fan-out list, whose entries were made absolute above
@@ -651,6 +659,32 @@ reshard_status_t reshard_plan_pieces(reshard_plan_t plan, int64_t capacity, resh
       o.dst_local[k] = pc.box.lo[k] - pc.dframe.lo[k];
     }
   }
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_plan_device_refs(reshard_plan_t plan, int64_t capacity, uint32_t* refs, int64_t* n_refs) {
+  if (!plan || !n_refs || capacity < 0 || (capacity > 0 && !refs))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "bad argument");
+  std::lock_guard<std::mutex> lock(plan->mu);
+  build_image_locked(plan);
+  *n_refs = int64_t(plan->host.refs.size());
+  const uint32_t* r = reinterpret_cast<const uint32_t*>(plan->image.data() + plan->refs_off);
+  for (int64_t i = 0; i < std::min<int64_t>(capacity, *n_refs); ++i) refs[i] = r[i];
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_plan_piece_sources(reshard_plan_t plan, int64_t index, int64_t capacity,
+                                            int64_t* ranks, int64_t* n_total) {
+  if (!plan || !n_total || capacity < 0 || (capacity > 0 && !ranks))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "bad argument");
+  const rs::HostPlan& H = plan->host;
+  if (index < 0 || index >= int64_t(H.pieces.size()))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "piece index out of range");
+  const rs::Piece& pc = H.pieces[index];
+  const std::vector<int64_t> one{pc.src_rank};
+  const std::vector<int64_t>& rk = pc.src_ranks.empty() ? one : pc.src_ranks;
+  *n_total = int64_t(rk.size());
+  for (int64_t i = 0; i < std::min<int64_t>(capacity, *n_total); ++i) ranks[i] = rk[i];
   return RESHARD_OK;
 }
 

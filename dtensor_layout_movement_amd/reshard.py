@@ -20,6 +20,7 @@ from typing import Sequence
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libreshard.so")
 
 REPLICATE = -1
+PARTIAL = -2  # Partial (sum): source layouts only
 MAX_NDIM = 8
 
 OK = 0
@@ -40,6 +41,7 @@ DESC_DST_CHUNKS = 1  # rows cut into destination-aligned 16-byte chunks
 DESC_WINDOW = 2      # a band of rows staged through an LDS window
 DESC_CONVERT = 3     # rows of elements converted to another float format (run in elements)
 DESC_GATHER_ROWS = 4  # whole destination rows gathered from wide source column segments
+DESC_REDUCE = 5      # rows of elements summed over Partial contributions (run in elements)
 
 # conversions: the `unit` of a DESC_CONVERT descriptor
 CONVERT_F32_BF16 = 1
@@ -52,7 +54,9 @@ EXPORTED = (
     "reshard_layout_create_strided", "reshard_layout_shard_runs",
     "reshard_layout_num_ranks", "reshard_layout_shard_box", "reshard_plan_create",
     "reshard_plan_create_batched", "reshard_plan_upload", "reshard_execute", "reshard_execute_noalloc",
-    "reshard_plan_stats", "reshard_plan_src_load", "reshard_plan_pieces", "reshard_plan_piece_fanout",
+    "reshard_plan_stats", "reshard_plan_src_load", "reshard_plan_pieces", "reshard_plan_piece_sources",
+    "reshard_plan_device_refs",
+    "reshard_plan_piece_fanout",
     "reshard_plan_descriptors", "reshard_plan_segments", "reshard_plan_destroy",
     "reshard_last_error",
 )
@@ -139,6 +143,8 @@ def _load() -> ctypes.CDLL:
         "reshard_plan_src_load": (st, [_VP, _I64, _I64P, _I64P]),
         "reshard_plan_pieces": (st, [_VP, _I64, ctypes.POINTER(Piece), _I64P]),
         "reshard_plan_piece_fanout": (st, [_VP, _I64, _I64, _I64P, _I64P]),
+        "reshard_plan_piece_sources": (st, [_VP, _I64, _I64, _I64P, _I64P]),
+        "reshard_plan_device_refs": (st, [_VP, _I64, ctypes.POINTER(ctypes.c_uint32), _I64P]),
         "reshard_plan_descriptors": (st, [_VP, _I64, ctypes.POINTER(Descriptor), _I64P, _I64,
                                           ctypes.POINTER(ctypes.c_uint32), _I64P]),
         "reshard_plan_segments": (st, [_VP, _I64, ctypes.POINTER(Segment), _I64P]),
@@ -313,6 +319,25 @@ def reshard_plan_pieces(plan: int) -> list[dict]:
              "dst_group": p.dst_group, "fanout": p.fanout, "lo": list(p.lo), "hi": list(p.hi),
              "src_local": list(p.src_local), "dst_local": list(p.dst_local)}
             for p in arr[:n.value]]
+
+
+def reshard_plan_device_refs(plan: int) -> list[int]:
+    """The fan-out list as the kernel reads it from the device table: absolute
+    slots of the pointer array (sources, then destinations)."""
+    n = ctypes.c_int64()
+    _check(_load().reshard_plan_device_refs(plan, 0, None, ctypes.byref(n)))
+    arr = (ctypes.c_uint32 * max(1, n.value))()
+    _check(_load().reshard_plan_device_refs(plan, n.value, arr, ctypes.byref(n)))
+    return list(arr[:n.value])
+
+
+def reshard_plan_piece_sources(plan: int, index: int) -> list[int]:
+    """Source ranks piece ``index`` reads, in contribution order."""
+    n = ctypes.c_int64()
+    _check(_load().reshard_plan_piece_sources(plan, int(index), 0, None, ctypes.byref(n)))
+    arr = (ctypes.c_int64 * max(1, n.value))()
+    _check(_load().reshard_plan_piece_sources(plan, int(index), n.value, arr, ctypes.byref(n)))
+    return list(arr[:n.value])
 
 
 def reshard_plan_piece_fanout(plan: int, index: int) -> list[int]:

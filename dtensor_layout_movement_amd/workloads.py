@@ -24,6 +24,9 @@ numbers, only an 8x8 example and multi-node refit latencies):
   launch: 4 pipeline stages x TP2 -> DP2 x TP4.
 * ``ffn_up_fsdp2_tp_14336x4096`` -- the up-projection trained under FSDP2 x TP
   (right-to-left nesting, DTensor's _StridedShard) -> DP2 x TP2.
+* ``ffn_up_partial_14336x4096`` -- the up-projection held as two Partial (sum)
+  contributions, rows split over 4 -> DP2 x TP2; contribution q of tensor t
+  under seed s draws from generator seed 1000 s + t + 7919 (q + 1).
 
 Values: bf16 tensors are N(0, 0.02) drawn in fp32 and rounded to nearest-even;
 fp32 tensors are U[-1, 1); "raw" fills every byte uniformly at random (NaN
@@ -38,6 +41,7 @@ from typing import Sequence
 import torch
 
 R = -1  # Replicate placement code (Shard(k) is k)
+P = -2  # Partial (sum) placement code, source layouts only
 
 
 @dataclass(frozen=True)
@@ -57,6 +61,16 @@ class TensorSpec:
     def out_dtype(self) -> torch.dtype:
         """Element type of the destination shards."""
         return self.dst_dtype if self.dst_dtype is not None else self.dtype
+
+    @property
+    def partial(self) -> int:
+        """Contributions of a Partial (sum) source: the product of the sizes of
+        its Partial mesh dims (0 for a source without any)."""
+        n = 0
+        for m, p in zip(self.src_mesh, self.src_placements):
+            if p == P:
+                n = (n or 1) * m
+        return n
 
     @property
     def strided(self) -> bool:
@@ -112,6 +126,14 @@ def ffn_up_fsdp2_tp(rows: int = 14336, cols: int = 4096) -> Workload:
     t = TensorSpec("up_proj", (rows, cols), torch.bfloat16, (2, 4), (0, 0), (2, 2), (R, 1), src_split=(4, 1))
     return Workload(f"ffn_up_fsdp2_tp_{rows}x{cols}", (t,), "normal",
                     f"{rows}x{cols} bf16 N(0,0.02), (2,4)[S0 strided by 4, S0] -> (2,2)[R,S1]")
+
+
+def ffn_up_partial(rows: int = 14336, cols: int = 4096) -> Workload:
+    """The up-projection held as two partial sums (a Partial mesh dim of 2, rows
+    split over 4) -> DP2 x TP2 column split of the summed weight."""
+    t = TensorSpec("up_proj", (rows, cols), torch.bfloat16, (2, 4), (P, 0), (2, 2), (R, 1))
+    return Workload(f"ffn_up_partial_{rows}x{cols}", (t,), "normal",
+                    f"{rows}x{cols} bf16 N(0,0.02) x 2 contributions, (2,4)[P,S0] -> (2,2)[R,S1]")
 
 
 def moe_experts(experts: int = 64, hidden: int = 2048, ffn: int = 7168) -> Workload:
@@ -250,6 +272,7 @@ WORKLOADS = {
     "ffn_up_f32_to_bf16_14336x4096": ffn_up_f32_to_bf16,
     "dense_layer_refit_32_layers": dense_layer_refit,
     "ffn_up_fsdp2_tp_14336x4096": ffn_up_fsdp2_tp,
+    "ffn_up_partial_14336x4096": ffn_up_partial,
 }
 
 
@@ -276,6 +299,27 @@ def make_global(spec: TensorSpec, values: str, seed: int, tensor_index: int = 0,
         raw = torch.randint(0, 256, (nbytes,), dtype=torch.uint8, generator=g, device=device)
         return raw.view(spec.dtype).reshape(spec.shape)
     raise ValueError(f"unknown value kind {values!r}")
+
+
+def contribution_of(spec: TensorSpec, rank: int) -> int:
+    """The contribution a source rank of a Partial spec holds: its coordinates
+    on the Partial mesh dims, row-major (ranks are row-major over the mesh)."""
+    coords = []
+    for m in reversed(spec.src_mesh):
+        coords.append(rank % m)
+        rank //= m
+    q = 0
+    for c, m, p in zip(reversed(coords), spec.src_mesh, spec.src_placements):
+        if p == P:
+            q = q * m + c
+    return q
+
+
+def make_contributions(spec: TensorSpec, values: str, seed: int, tensor_index: int = 0, device="cpu") -> list:
+    """The seeded contributions of a Partial source, one global-shaped tensor
+    each (contribution q draws from tensor index tensor_index + 7919 (q + 1))."""
+    return [make_global(spec, values, seed, tensor_index + 7919 * (q + 1), device=device)
+            for q in range(spec.partial)]
 
 
 def cut_indexed(global_tensor: torch.Tensor, index_lists: Sequence) -> list:

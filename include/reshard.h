@@ -29,7 +29,20 @@
  *   - several mesh dims that shard the same tensor dim nest left to right;
  *   - each local shard is a contiguous row-major buffer whose shape is the
  *     extent of its box (reshard_layout_shard_box);
- *   - right-to-left (strided) nesting: reshard_layout_create_strided.
+ *   - right-to-left (strided) nesting: reshard_layout_create_strided;
+ *   - Partial (sum) sources: a source mesh dim with placement RESHARD_PARTIAL
+ *     splits nothing; each of its coordinates holds a full-size contribution
+ *     of the same box, and the tensor is their elementwise sum (DTensor's
+ *     Partial("sum")).  With several Partial mesh dims the contributions are
+ *     numbered q = 0, 1, ... row-major over their coordinates.  The sum is taken
+ *     in binary32 in ascending q: it starts from contribution 0, widened
+ *     exactly, adds each next one with one rounding to nearest even, and is
+ *     rounded once more to the destination dtype.  Sources are F32, BF16 or F16;
+ *     the destination dtype is the source's or one of its conversions below.
+ *     A destination with Partial, or Partial with split factors, is refused
+ *     (RESHARD_ERR_LAYOUT_MISMATCH).  The pages say only that the refit guide
+ *     lists the supported layouts (news.bpdata.com write-up, "practical access
+ *     and setup" section).
  * The copy is bytewise: bf16/fp32 NaN payloads, -0.0 and subnormals arrive
  * unchanged.  Source and destination dtypes match, or the pair is one of the
  * float conversions below.
@@ -60,6 +73,7 @@ extern "C" {
 #define RESHARD_MAX_NDIM 8       /* tensor dims supported */
 #define RESHARD_MAX_MESH_NDIM 8  /* mesh dims supported */
 #define RESHARD_REPLICATE (-1)   /* placement code for Replicate */
+#define RESHARD_PARTIAL (-2)     /* placement code for Partial (sum), source layouts only */
 
 typedef enum reshard_status {
   RESHARD_OK = 0,
@@ -99,7 +113,8 @@ typedef struct reshard_plan_stats {
   int64_t n_pieces;       /* source box x unique destination box overlaps */
   int64_t n_dst_writes;   /* sum over pieces of their destination fan-out */
   int64_t global_bytes;   /* sum over tensors of the global tensor's bytes in the source dtype (G) */
-  int64_t bytes_read;     /* bytes the kernel reads  (= G: each element once) */
+  int64_t bytes_read;     /* bytes the kernel reads  (= G: each element once; times the
+                             number of contributions for a Partial source) */
   int64_t bytes_written;  /* bytes the kernel writes (= sum of destination shard bytes, in the
                              destination dtype) */
   int64_t n_descriptors;  /* device copy descriptors after dim merging / splitting */
@@ -136,6 +151,7 @@ typedef struct reshard_piece {
 #define RESHARD_DESC_WINDOW 2     /* a band of rows staged through LDS (see below) */
 #define RESHARD_DESC_CONVERT 3    /* rows of elements converted to another float format */
 #define RESHARD_DESC_GATHER_ROWS 4 /* whole destination rows gathered from column segments */
+#define RESHARD_DESC_REDUCE 5     /* rows of elements summed over Partial contributions */
 
 /* Conversions (the `unit` field of a RESHARD_DESC_CONVERT descriptor). */
 #define RESHARD_CONVERT_F32_BF16 1
@@ -201,6 +217,15 @@ typedef struct reshard_piece {
  *                            [c*8, min(c*8+8, run)) of the row; row_items =
  *                            ceil(run / 8).  Offsets and strides are in bytes of
  *                            each side's own dtype.
+ *   RESHARD_DESC_REDUCE      rows and items as RESHARD_DESC_CONVERT, each element
+ *                            the binary32 sum, in list order, of the same element
+ *                            of n contributions (Partial sources), rounded to the
+ *                            destination format.  The contributions' source
+ *                            pointer slots are refs[src_ptr .. src_ptr + n) of
+ *                            the fan-out list (all at the same offsets); `unit`
+ *                            holds n in bits 0-11, the source format in bits
+ *                            12-13 and the destination format in bits 14-15
+ *                            (0 binary32, 1 bfloat16, 2 binary16).
  */
 typedef struct reshard_descriptor {
   int64_t src_offset;       /* byte offset of the row origin in the source shard */
@@ -420,14 +445,35 @@ reshard_status_t reshard_plan_src_load(reshard_plan_t plan, int64_t capacity, in
 reshard_status_t reshard_plan_pieces(reshard_plan_t plan, int64_t capacity,
                                      reshard_piece_t* out, int64_t* n_total);
 
+/*
+ * Inspection: the fan-out list as the kernel reads it from the device table,
+ * host-side (builds the table image if needed; no device call).  Entries are
+ * absolute slots of the pointer array the kernel indexes (src_ptrs first,
+ * then dst_ptrs): n_src_ptrs + the reshard_plan_descriptors entry for a
+ * destination, the entry itself for a REDUCE descriptor's contributions.
+ * Writes min(capacity, count) entries and the count.  Errors:
+ * RESHARD_ERR_INVALID_ARGUMENT.
+ */
+reshard_status_t reshard_plan_device_refs(reshard_plan_t plan, int64_t capacity, uint32_t* refs,
+                                          int64_t* n_refs);
+
+/* Source ranks (within the piece's tensor) that piece `index` reads, in
+ * contribution order: one for a plain source, one per contribution for a
+ * Partial source (the first is the piece's src_rank).  Writes min(capacity,
+ * count) ranks and the count.  Errors: RESHARD_ERR_INVALID_ARGUMENT. */
+reshard_status_t reshard_plan_piece_sources(reshard_plan_t plan, int64_t index, int64_t capacity,
+                                            int64_t* ranks, int64_t* n_total);
+
 /* Destination ranks (within the piece's tensor) that piece `index` is written to. */
 reshard_status_t reshard_plan_piece_fanout(reshard_plan_t plan, int64_t index, int64_t capacity,
                                            int64_t* ranks, int64_t* n_total);
 
 /*
  * Inspection: copy the descriptor table (up to `capacity` entries) and the
- * fan-out reference list (indices into the destination pointer array; up to
- * `ref_capacity` entries).  Totals go to *n_desc and *n_refs.
+ * fan-out reference list (indices into the destination pointer array, except
+ * a REDUCE descriptor's list of contributions at src_ptr, which indexes the
+ * source pointer array; up to `ref_capacity` entries).  Totals go to *n_desc
+ * and *n_refs.
  */
 reshard_status_t reshard_plan_descriptors(reshard_plan_t plan, int64_t capacity,
                                           reshard_descriptor_t* out, int64_t* n_desc,

@@ -134,7 +134,8 @@ def layout_cases():
     for make in W.WORKLOADS.values():
         wl = make()
         for t in wl.tensors[:3]:
-            cases.append((t.shape, t.src_mesh, t.src_placements))
+            # boxes only: a Partial mesh dim splits nothing (like Replicate)
+            cases.append((t.shape, t.src_mesh, tuple(W.R if p == W.P else p for p in t.src_placements)))
             cases.append((t.shape, t.dst_mesh, t.dst_placements))
     cases += [
         ((5, 3), (4,), (0,)), ((1, 7), (4, 2), (0, 1)), ((9, 4), (2, 3), (0, 0)),

@@ -102,10 +102,15 @@ def lib_boxes(layout, shape):
 
 
 def oracle_boxes(shape, mesh, placements):
+    """The oracle's boxes (a Partial mesh dim splits nothing, like Replicate)."""
     n = 1
     for m in mesh:
         n *= m
-    return [oracle.shard_box(list(shape), list(mesh), list(placements), r) for r in range(n)]
+    plain = [W.R if p == W.P else p for p in placements]
+    return [oracle.shard_box(list(shape), list(mesh), plain, r) for r in range(n)]
+
+
+
 
 
 def assert_boxes_agree(plan: Plan):
@@ -135,6 +140,13 @@ def oracle_dsts(spec, srcs, threads=1):
     for a converting spec, each shard is then converted by the oracle."""
     es = torch.empty((), dtype=spec.dtype).element_size()
     src_in = [s if s is not None and s.numel() else None for s in srcs]
+    if spec.partial:  # the sum, rounded to the destination dtype by the oracle itself
+        boxes = oracle_boxes(spec.shape, spec.dst_mesh, spec.dst_placements)
+        dsts = [torch.empty(box_shape(b), dtype=spec.out_dtype) for b in boxes]
+        oracle.reshard_partial(list(spec.shape), FMT[spec.dtype], FMT[spec.out_dtype], list(spec.src_mesh),
+                               list(spec.src_placements), src_in, list(spec.dst_mesh), list(spec.dst_placements),
+                               [d if d.numel() else None for d in dsts], threads=threads)
+        return dsts
     if spec.strided:
         dsts = [torch.empty([len(ix) for ix in lists], dtype=spec.dtype) for lists in oracle_index_lists(spec, "dst")]
         oracle.reshard_indexed(list(spec.shape), es, list(spec.src_mesh), list(spec.src_placements),
@@ -162,16 +174,27 @@ def oracle_shapes(spec, side):
 
 def oracle_cut(spec, g):
     """Source shards of the global tensor g, cut by the oracle's boxes (index
-    lists, for a strided spec)."""
+    lists, for a strided spec).  For a Partial spec g is the list of
+    contributions and each rank gets its own contribution's box."""
+    if spec.partial:
+        boxes = oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements)
+        return [W.cut(g[W.contribution_of(spec, r)], [b])[0] for r, b in enumerate(boxes)]
     if spec.strided:
         return W.cut_indexed(g, oracle_index_lists(spec, "src"))
     return W.cut(g, oracle_boxes(spec.shape, spec.src_mesh, spec.src_placements))
 
 
+def make_inputs(spec, values, seed, t=0, device="cpu"):
+    """The seeded global tensor, or for a Partial spec its contributions."""
+    if spec.partial:
+        return W.make_contributions(spec, values, seed, t, device=device)
+    return W.make_global(spec, values, seed, t, device=device)
+
+
 def sources_for(spec, values, seed, t=0):
     """Seeded global tensor and its source shards cut with the oracle's boxes
     (index lists, for a strided spec)."""
-    g = W.make_global(spec, values, seed, t)
+    g = make_inputs(spec, values, seed, t)
     return g, oracle_cut(spec, g)
 
 
@@ -193,11 +216,24 @@ def apply_pieces(plan: Plan, srcs_per_tensor, fill=None):
         s_loc, d_loc = pc["src_local"][:nd], pc["dst_local"][:nd]
         if sboxes[t] is not None:
             assert s_loc == [l - o for l, o in zip(lo, sboxes[t][pc["src_rank"]][0])], pc
-        src = srcs_per_tensor[t][pc["src_rank"]]
-        part = src[tuple(slice(a, a + e) for a, e in zip(s_loc, ext))]
         spec = plan.specs[t]
-        if spec.out_dtype != spec.dtype:
-            part = oracle.convert(part.contiguous(), FMT[spec.dtype], FMT[spec.out_dtype])
+        sel = tuple(slice(a, a + e) for a, e in zip(s_loc, ext))
+        if spec.partial:  # binary32 sum over the contributions, in order, then one rounding
+            ranks = R.reshard_plan_piece_sources(plan.handle, i)
+            assert len(ranks) == spec.partial and ranks[0] == pc["src_rank"]
+            assert [W.contribution_of(spec, r) for r in ranks] == list(range(len(ranks)))
+            acc = None
+            for r in ranks:
+                x = srcs_per_tensor[t][r][sel].contiguous()
+                x = x.numpy() if spec.dtype == torch.float32 else oracle.convert(x, FMT[spec.dtype], "f32").numpy()
+                acc = x.astype(np.float32) if acc is None else np.add(acc, x, dtype=np.float32)
+            part = torch.from_numpy(np.ascontiguousarray(acc))
+            if spec.out_dtype != torch.float32:
+                part = oracle.convert(part, "f32", FMT[spec.out_dtype])
+        else:
+            part = srcs_per_tensor[t][pc["src_rank"]][sel]
+            if spec.out_dtype != spec.dtype:
+                part = oracle.convert(part.contiguous(), FMT[spec.dtype], FMT[spec.out_dtype])
         for d in R.reshard_plan_piece_fanout(plan.handle, i):
             if dboxes[t] is not None:
                 assert d_loc == [l - o for l, o in zip(lo, dboxes[t][d][0])], pc
@@ -217,12 +253,17 @@ def _ranges(starts, lengths):
 
 def run_descriptors(plan: Plan, srcs_flat, dsts_flat):
     """Execute the descriptor table on host byte arrays exactly as the kernel
-    addresses memory (shard bases taken as 16-byte aligned).  srcs_flat /
+    addresses memory (shard bases taken as 16-byte aligned) and resolves its
+    shard pointers from the device table's fan-out list.  srcs_flat /
     dsts_flat: uint8 numpy arrays (or None), in the pointer-array order of
     reshard_execute.  For DST_CHUNKS descriptors it also checks that the chunks
     of every row tile the row exactly."""
-    descs, refs = R.reshard_plan_descriptors(plan.handle)
+    descs, _ = R.reshard_plan_descriptors(plan.handle)
     segs = R.reshard_plan_segments(plan.handle)
+    # pointers resolve as in the kernel: one array of sources then destinations,
+    # indexed by source slots and by the device table's fan-out list (absolute)
+    refs = R.reshard_plan_device_refs(plan.handle)
+    srcs_flat = dsts_flat = list(srcs_flat) + list(dsts_flat)
     for D in descs:
         if D["mode"] == R.DESC_WINDOW:
             _run_window(D, segs, refs, srcs_flat, dsts_flat)
@@ -232,6 +273,9 @@ def run_descriptors(plan: Plan, srcs_flat, dsts_flat):
             continue
         if D["mode"] == R.DESC_CONVERT:
             _run_convert(D, refs, srcs_flat, dsts_flat)
+            continue
+        if D["mode"] == R.DESC_REDUCE:
+            _run_reduce(D, refs, srcs_flat, dsts_flat)
             continue
         e0, e1, e2 = D["extent"]
         i0, i1, i2 = np.meshgrid(np.arange(e0), np.arange(e1), np.arange(e2), indexing="ij")
@@ -286,6 +330,46 @@ def _run_convert(D, refs, srcs_flat, dsts_flat):
     vals = np.stack([src[s_byte + b] for b in range(es)], axis=1).reshape(-1)
     conv = oracle.convert(torch.from_numpy(vals.copy()).view(_TORCH[fs]), fs, fd)
     out = conv.view(torch.uint8).numpy().reshape(-1, ed)
+    for r in range(D["fanout"]):
+        dst = dsts_flat[refs[D["dst_ref_begin"] + r]]
+        for b in range(ed):
+            dst[d_byte + b] = out[:, b]
+
+
+_FORMATS = ("f32", "bf16", "f16")
+
+
+def _run_reduce(D, refs, srcs_flat, dsts_flat):
+    """A REDUCE descriptor element by element: items of 8 elements tile each row
+    of `run` elements; each element is the binary32 sum of the contributions
+    refs[src_ptr ...] in list order (numpy float32 additions), rounded to the
+    destination format by the oracle."""
+    unit = D["unit"]
+    parts, fs, fd = unit & 0xFFF, _FORMATS[(unit >> 12) & 3], _FORMATS[(unit >> 14) & 3]
+    es, ed = (4 if fs == "f32" else 2), (4 if fd == "f32" else 2)
+    run, n = D["run_bytes"], D["row_items"]
+    assert n == (run + 7) // 8 and parts >= 1
+    e0, e1, e2 = D["extent"]
+    i0, i1, i2 = np.meshgrid(np.arange(e0), np.arange(e1), np.arange(e2), indexing="ij")
+    so = (D["src_offset"] + i0 * D["src_stride"][0] + i1 * D["src_stride"][1]
+          + i2 * D["src_stride"][2]).reshape(-1)
+    do = (D["dst_offset"] + i0 * D["dst_stride"][0] + i1 * D["dst_stride"][1]
+          + i2 * D["dst_stride"][2]).reshape(-1)
+    el = np.arange(n * 8, dtype=np.int64)
+    el = el[el < run]
+    s_byte = (so[:, None] + el[None, :] * es).reshape(-1)
+    d_byte = (do[:, None] + el[None, :] * ed).reshape(-1)
+    acc = None
+    for p in range(parts):
+        src = srcs_flat[refs[D["src_ptr"] + p]]
+        vals = np.stack([src[s_byte + b] for b in range(es)], axis=1).reshape(-1)
+        x = torch.from_numpy(vals.copy()).view(_TORCH[fs])
+        x = (x if fs == "f32" else oracle.convert(x, fs, "f32")).numpy()
+        acc = x.copy() if acc is None else np.add(acc, x, dtype=np.float32)
+    out = torch.from_numpy(acc)
+    if fd != "f32":
+        out = oracle.convert(out, "f32", fd)
+    out = out.view(torch.uint8).numpy().reshape(-1, ed)
     for r in range(D["fanout"]):
         dst = dsts_flat[refs[D["dst_ref_begin"] + r]]
         for b in range(ed):
@@ -394,6 +478,16 @@ def assert_descriptors_in_bounds(plan: Plan):
     sb, db = shard_bytes(plan)
     descs, refs = R.reshard_plan_descriptors(plan.handle)
     segs = R.reshard_plan_segments(plan.handle)
+    # the device table's fan-out list: absolute slots, destinations after the
+    # sources, a REDUCE descriptor's contributions among the sources
+    drefs = R.reshard_plan_device_refs(plan.handle)
+    n_src = len(sb)
+    reduce_slots = {D["src_ptr"] + q for D in descs if D["mode"] == R.DESC_REDUCE for q in range(D["unit"] & 0xFFF)}
+    for i, (a, b) in enumerate(zip(drefs, refs)):
+        if i in reduce_slots:
+            assert a == b < n_src, (i, a, b)
+        else:
+            assert a == n_src + b < n_src + len(db), (i, a, b)
     for D in descs:
         ext = D["extent"]
         if D["mode"] == R.DESC_GATHER_ROWS:
@@ -439,11 +533,19 @@ def assert_descriptors_in_bounds(plan: Plan):
         if D["mode"] == R.DESC_CONVERT:
             _, _, es, ed = CONVERSIONS[D["unit"]]
             s_span, d_span = D["run_bytes"] * es, D["run_bytes"] * ed
+        src_slots = [D["src_ptr"]]
+        if D["mode"] == R.DESC_REDUCE:  # every contribution's slot, all at the same offsets
+            unit = D["unit"]
+            es, ed = (4 if (unit >> 12) & 3 == 0 else 2), (4 if (unit >> 14) & 3 == 0 else 2)
+            s_span, d_span = D["run_bytes"] * es, D["run_bytes"] * ed
+            src_slots = [refs[D["src_ptr"] + p] for p in range(unit & 0xFFF)]
+            assert len(src_slots) >= 1
         s_last = D["src_offset"] + sum((e - 1) * st for e, st in zip(ext, D["src_stride"])) + s_span
         d_last = D["dst_offset"] + sum((e - 1) * st for e, st in zip(ext, D["dst_stride"])) + d_span
         assert D["src_offset"] >= 0 and D["dst_offset"] >= 0
         assert all(st >= 0 for st in D["src_stride"] + D["dst_stride"])
-        assert s_last <= sb[D["src_ptr"]], D
+        for slot in src_slots:
+            assert s_last <= sb[slot], D
         for r in range(D["fanout"]):
             assert d_last <= db[refs[D["dst_ref_begin"] + r]], D
 

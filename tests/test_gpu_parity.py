@@ -50,7 +50,7 @@ SMALL_FULL = ["worked_example_8x8", "ffn_up_14336x4096", "moe_experts_64x2048x71
               "narrow_columns_4194304x8", "narrow_columns_tp8_2097152x16", "narrow_columns_64b_tp8_1048576x32",
               "narrow_columns_64b_tp4_1048576x32", "narrow_columns_32b_tp4_2097152x16",
               "narrow_columns_16b_tp8_4194304x8",
-              "ffn_up_f32_to_bf16_14336x4096", "ffn_up_fsdp2_tp_14336x4096"]
+              "ffn_up_f32_to_bf16_14336x4096", "ffn_up_fsdp2_tp_14336x4096", "ffn_up_partial_14336x4096"]
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])
@@ -99,7 +99,16 @@ def test_replan_after_rank_loss():
 
 @pytest.mark.parametrize("spec", small_specs(), ids=lambda s: s.name)
 def test_small_layouts(spec):
-    run_parity([spec], "raw", 3)
+    run_parity([spec], "normal" if spec.partial else "raw", 3)
+
+
+@pytest.mark.parametrize("name", ["partial_tp2", "partial_rep", "partial_two_dims", "partial_f32_f16"])
+def test_partial_sums_of_raw_bits(name):
+    """Partial sums over random bytes: infinities, NaN payloads, subnormals and
+    signed zeros in every contribution.  Every element that is not NaN matches
+    the oracle bit for bit; NaN positions match."""
+    spec = {s.name: s for s in small_specs()}[name]
+    run_parity([spec], "raw", 5)
 
 
 @pytest.mark.parametrize("misalign", [1, 2, 4, 8, "mixed"])

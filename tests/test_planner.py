@@ -134,7 +134,27 @@ def small_specs():
         T("conv_empty", (5, 3), torch.float32, (4,), (0,), (2,), (1,), torch.float16),
         T("conv_narrow", (4099, 8), torch.float32, (2,), (0,), (4,), (1,), torch.bfloat16),
     ]
-    return specs + strided_specs()
+    return specs + strided_specs() + partial_specs()
+
+
+def partial_specs():
+    """Partial (sum) sources: contributions over one or two mesh dims, replicas
+    of a contribution, row and column splits, empty shards, conversions, a
+    single contribution and ragged rows."""
+    S = W.TensorSpec
+    PP = W.P
+    return [
+        S("partial_tp2", (96, 40), torch.bfloat16, (2, 2), (PP, 0), (2, 2), (RR, 1)),
+        S("partial_f32", (50, 31), torch.float32, (3,), (PP,), (2,), (0,)),
+        S("partial_rep", (40, 24), torch.float32, (2, 2, 2), (RR, PP, 1), (4,), (0,), torch.bfloat16),
+        S("partial_two_dims", (33, 17), torch.float16, (2, 3), (PP, PP), (2,), (1,)),
+        S("partial_bf16_f32", (64, 48), torch.bfloat16, (4,), (PP,), (2, 2), (0, 1), torch.float32),
+        S("partial_f32_f16", (31, 9), torch.float32, (2, 2), (PP, 0), (3,), (RR,), torch.float16),
+        S("partial_empty", (5, 3), torch.float32, (2, 4), (PP, 0), (2,), (0,)),
+        S("partial_nested", (3, 40, 12), torch.bfloat16, (2, 2, 2), (1, PP, 1), (2, 2), (2, RR)),
+        S("partial_single", (20, 8), torch.float32, (1,), (PP,), (2,), (0,)),
+        S("partial_ragged", (7, 13), torch.bfloat16, (3, 2), (PP, 1), (2,), (0,)),
+    ]
 
 
 def strided_specs():
@@ -161,7 +181,10 @@ def strided_specs():
 
 
 def values_for(spec):
-    return "raw"
+    """Random bytes, except for Partial sums: there a NaN's payload is the
+    adder's to choose, so their bit-exact tests use normal values (NaN-ness is
+    tested on its own)."""
+    return "normal" if spec.partial else "raw"
 
 
 @pytest.mark.parametrize("spec", small_specs(), ids=lambda s: s.name)
@@ -464,7 +487,9 @@ def test_invariants_full_size(wl):
                 dst_bytes += int(np.prod(sh)) * es
         # I2, I3: write bytes = destination bytes, read bytes = global bytes (no 2x inflation)
         assert st["global_bytes"] == wl.global_bytes
-        assert st["bytes_read"] == wl.global_bytes
+        # a Partial source is read once per contribution
+        assert st["bytes_read"] == sum(int(np.prod(s.shape)) * s.dtype.itemsize * max(1, s.partial)
+                                       for s in wl.tensors)
         assert st["bytes_written"] == dst_bytes
         # I4: each piece lies in its source shard and in every destination shard it
         # feeds (inside one run per dim, at the local offset the plan reports);
@@ -522,7 +547,8 @@ def test_piece_counts_of_workloads():
               "uneven_5000x3001": 42, "ffn_refit_32_layers": 384, "narrow_columns_4194304x8": 8, "ffn_up_f32_to_bf16_14336x4096": 8,
               "narrow_columns_tp8_2097152x16": 16, "narrow_columns_64b_tp8_1048576x32": 16, "narrow_columns_64b_tp4_1048576x32": 8,
               "narrow_columns_32b_tp4_2097152x16": 8, "narrow_columns_16b_tp8_4194304x8": 16,
-              "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1), "ffn_up_fsdp2_tp_14336x4096": 16}
+              "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1), "ffn_up_fsdp2_tp_14336x4096": 16,
+              "ffn_up_partial_14336x4096": 8}
     for wl in full_workload_plans():
         with Plan(wl.tensors) as plan:
             assert plan.stats()["n_pieces"] == counts[wl.name]
@@ -861,6 +887,33 @@ def test_errors():
         R.reshard_layout_destroy(h)
     R.reshard_plan_destroy(None)
     R.reshard_layout_destroy(None)
+
+
+def test_partial_errors():
+    """Partial only on a source, only for float elements, never with split factors."""
+    src = R.reshard_layout_create((8, 4), R.DTYPE_F32, (2, 2), (R.PARTIAL, 0))
+    dst = R.reshard_layout_create((8, 4), R.DTYPE_F32, (2,), (1,))
+    isrc = R.reshard_layout_create((8, 4), R.DTYPE_I32, (2, 2), (R.PARTIAL, 0))
+    idst = R.reshard_layout_create((8, 4), R.DTYPE_I32, (2,), (1,))
+    sdst = R.reshard_layout_create_strided((8, 4), R.DTYPE_F32, (2,), (0,), (2,))
+    try:
+        for a, b in ((dst, src), (isrc, idst), (src, sdst)):
+            with pytest.raises(R.ReshardError) as e:
+                R.reshard_plan_create(a, b)
+            assert e.value.status == R.ERR_LAYOUT_MISMATCH
+        with pytest.raises(R.ReshardError) as e:  # no split factor on a Partial dim
+            R.reshard_layout_create_strided((8, 4), R.DTYPE_F32, (2,), (R.PARTIAL,), (2,))
+        assert e.value.status == R.ERR_INVALID_ARGUMENT
+        plan = R.reshard_plan_create(src, dst)
+        st = R.reshard_plan_stats(plan)
+        assert st["bytes_read"] == 2 * 8 * 4 * 4 and st["bytes_written"] == 8 * 4 * 4
+        descs, refs = R.reshard_plan_descriptors(plan)
+        assert all(D["mode"] == R.DESC_REDUCE and D["unit"] & 0xFFF == 2 for D in descs)
+        assert R.reshard_plan_piece_sources(plan, 0) == [0, 2]  # contribution 0, then 1
+        R.reshard_plan_destroy(plan)
+    finally:
+        for h in (src, dst, isrc, idst, sdst):
+            R.reshard_layout_destroy(h)
 
 
 def test_dtype_sizes():
