@@ -461,6 +461,73 @@ __device__ __forceinline__ void window_tile(const reshard_descriptor_t& D, const
   }
 }
 
+// Dword bands: a WINDOW band more than 16 bytes wide whose segments all hold
+// their rows back to back (row stride = width) at dword granularity (column,
+// width and offset multiples of 4 bytes).  Every side is then a contiguous
+// stream of dwords, and one lane moves one dword: a segment's stream dword j is
+// row j / w, dword j % w of the segment (w its width in dwords).  The window
+// keeps rows at an odd pitch of dwords, so lanes that touch one column of
+// consecutive rows, or consecutive dwords of one row, hit distinct LDS banks;
+// its rows per tile are the LDS window's, and kDwordWindowWords bounds the
+// window (checked on the host).
+constexpr uint32_t kDwordWindowWords = 4608;  // 18 KiB
+constexpr int kDwordBatch = 4;                 // dwords per lane with loads in flight together
+
+// n / w for n < 2^16 and 1 <= w < 2^16, with m = 2^32 / w rounded up (w > 1).
+__device__ __forceinline__ uint32_t div_small(uint32_t n, uint32_t w, uint32_t m) {
+  return w == 1 ? n : __umulhi(n, m);
+}
+
+template <class Sh>
+__device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
+                                              const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile,
+                                              uint32_t* lds) {
+  const uint32_t rows = D.extent[0], per_tile = D.extent[1];
+  const uint32_t r0 = tile * per_tile;
+  const uint32_t hr = min(per_tile, rows - r0);
+  const uint32_t pitch = (D.run_bytes / 4) | 1u;  // odd
+  const reshard_segment_t* src_segs = segs + D.src_ptr;
+  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+
+  // phase 1: source streams -> window
+  for (uint32_t s = 0; s < D.dst_ref_begin; ++s) {
+    const reshard_segment_t S = src_segs[s];
+    const uint32_t w = S.width / 4, c = S.col / 4, n = hr * w;
+    const uint32_t m = w > 1 ? 0xffffffffu / w + 1u : 0u;
+    const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+    for (uint32_t base = threadIdx.x; base < n; base += kBlock * kDwordBatch) {
+      uint32_t v[kDwordBatch];
+#pragma unroll
+      for (int k = 0; k < kDwordBatch; ++k) {
+        const uint32_t j = base + uint32_t(k) * kBlock;
+        if (j < n) v[k] = __builtin_nontemporal_load(as_global<const u32_u>(g + 4 * uint64_t(j)));
+      }
+#pragma unroll
+      for (int k = 0; k < kDwordBatch; ++k) {
+        const uint32_t j = base + uint32_t(k) * kBlock;
+        if (j >= n) break;
+        const uint32_t r = div_small(j, w, m);
+        lds[r * pitch + c + (j - r * w)] = v[k];
+      }
+    }
+  }
+  __syncthreads();
+
+  // phase 2: window -> destination streams, every replica
+  for (uint32_t s = 0; s < D.fanout; ++s) {
+    const reshard_segment_t S = dst_segs[s];
+    const uint32_t w = S.width / 4, c = S.col / 4, n = hr * w;
+    const uint32_t m = w > 1 ? 0xffffffffu / w + 1u : 0u;
+    const uint64_t row_off = uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+    for (uint32_t j = threadIdx.x; j < n; j += kBlock) {
+      const uint32_t r = div_small(j, w, m);
+      const uint32_t v = lds[r * pitch + c + (j - r * w)];
+      for (uint32_t f = 0; f < S.fanout; ++f)
+        __builtin_nontemporal_store(v, as_global<u32_u>(sh.ptr(refs[S.ptr + f]) + row_off + 4 * uint64_t(j)));
+    }
+  }
+}
+
 // n <= 16 bytes from global address a into bytes [0, n) of the result (any
 // alignment: gfx950 global accesses need none).  Streaming (non-temporal).
 __device__ __forceinline__ u32x4 load_bytes(uintptr_t a, uint32_t n) {
@@ -1666,6 +1733,7 @@ enum KernelKind : int {
                      // runs (window_octets): no LDS
   kKindGatherRows = 10,  // every descriptor RESHARD_DESC_GATHER_ROWS (gather_rows)
   kKindReduce = 11,      // every descriptor RESHARD_DESC_REDUCE (reduce_items)
+  kKindDwords = 12,      // every descriptor a dword band (window_dwords): LDS, no byte paths
   kKindAligned = 16, // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
@@ -1727,7 +1795,8 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
                         : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
                         : kKind == kKindQuadRows || kKind == kKindRuns || kKind == kKindRuns64 ||
-                                  kKind == kKindBands16 || kKind == kKindRuns32 || kKind == kKindOctets
+                                  kKind == kKindBands16 || kKind == kKindRuns32 || kKind == kKindOctets ||
+                                  kKind == kKindDwords
                             ? uint32_t(RESHARD_DESC_WINDOW)
                         : kKind == kKindGatherRows ? uint32_t(RESHARD_DESC_GATHER_ROWS)
                         : kKind == kKindReduce ? uint32_t(RESHARD_DESC_REDUCE)
@@ -1760,6 +1829,12 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   if constexpr (kKind == kKindGatherRows) {
     const Shards<kKarg> gsh{table, &karg, refs};
     gather_rows(D, segs, refs, gsh, t - tile_begin[lo]);
+    return;
+  }
+  if constexpr (kKind == kKindDwords) {
+    __shared__ uint32_t dword_window[kDwordWindowWords];
+    const Shards<kKarg> wsh{table, &karg, refs};
+    window_dwords(D, segs, refs, wsh, t - tile_begin[lo], dword_window);
     return;
   }
   if constexpr (kKind == kKindReduce) {
@@ -1899,6 +1974,8 @@ hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_des
       return RS_LAUNCH(kKindGatherRows);
     case kKindReduce:
       return RS_LAUNCH(kKindReduce);
+    case kKindDwords:
+      return RS_LAUNCH(kKindDwords);
     default:
       return RS_LAUNCH(kKindAll);
   }
@@ -1979,6 +2056,21 @@ bool runs64_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
   return (src_runs && full_side(T, D.fanout, w)) || (dst_runs && full_side(S, D.dst_ref_begin, w));
 }
 
+// Whether a descriptor is a band window_dwords moves: a WINDOW band more than
+// 16 bytes (and at most 256) wide, every segment packed at dword granularity,
+// and the window's rows at the odd dword pitch within kDwordWindowWords.
+bool dwords_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
+  const uint32_t w = D.run_bytes;
+  if (D.mode != RESHARD_DESC_WINDOW || w <= uint32_t(rs::kRowModeBytes) || w > 256 || w % 4) return false;
+  if (uint64_t(D.extent[1]) * ((w / 4) | 1u) > kDwordWindowWords) return false;
+  const reshard_segment_t* S = segs.data() + D.src_ptr;
+  for (uint32_t i = 0; i < D.dst_ref_begin + D.fanout; ++i) {
+    const reshard_segment_t& x = S[i];
+    if (x.width % 4 || x.col % 4 || x.offset % 4 || uint64_t(x.row_stride) != x.width) return false;
+  }
+  return true;
+}
+
 }  // namespace
 
 int kernel_kind_gather_rows() { return kKindGatherRows; }
@@ -1986,7 +2078,7 @@ int kernel_kind_gather_rows() { return kKindGatherRows; }
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
   bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, bands16 = true, runs32 = true;
-  bool octets = true, gather = true, reduce = true;
+  bool octets = true, gather = true, reduce = true, dwords = true;
   bool window = false;
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
@@ -2001,13 +2093,15 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
     if (!octets_band(D, segs)) octets = false;
     if (D.mode != RESHARD_DESC_GATHER_ROWS) gather = false;
     if (D.mode != RESHARD_DESC_REDUCE) reduce = false;
+    if (!dwords_band(D, segs)) dwords = false;
     if (D.mode == RESHARD_DESC_WINDOW) window = true;
   }
   if (gather && !descs.empty()) return kKindGatherRows;
   if (reduce && !descs.empty()) return kKindReduce;
   return items16 ? kKindItems16 : chunks ? kKindChunks : octets ? kKindOctets : quad_rows ? kKindQuadRows
          : runs ? kKindRuns
-         : runs64 ? kKindRuns64 : bands16 ? kKindBands16 : runs32 ? kKindRuns32 : window ? kKindAll : kKindCopy;
+         : runs64 ? kKindRuns64 : bands16 ? kKindBands16 : runs32 ? kKindRuns32 : dwords ? kKindDwords
+         : window ? kKindAll : kKindCopy;
 }
 
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,

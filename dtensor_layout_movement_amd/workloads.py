@@ -257,6 +257,32 @@ def narrow_columns_16b_tp8(rows: int = 1 << 22) -> Workload:
                     f"{rows}x8 bf16 N(0,0.02), (2,)[S0] -> (8,)[S1]: single columns of 16-byte rows")
 
 
+def narrow_columns_8b_tp2(rows: int = 1 << 23) -> Workload:
+    """4 bf16 columns (8-byte rows), rows split over two sources, columns over
+    two destinations: every destination row is a 2-element (4-byte) half of an
+    8-byte source row."""
+    t = TensorSpec("narrow4", (rows, 4), torch.bfloat16, (2,), (0,), (2,), (1,))
+    return Workload(f"narrow_columns_8b_tp2_{rows}x4", (t,), "normal",
+                    f"{rows}x4 bf16 N(0,0.02), (2,)[S0] -> (2,)[S1]: 4-byte halves of 8-byte rows")
+
+
+def narrow_columns_64b_tp16(rows: int = 1 << 20) -> Workload:
+    """32 bf16 columns (64-byte rows), rows split over two sources, columns over
+    sixteen destinations: every destination row is a 2-element (4-byte) slice
+    of a 64-byte source row."""
+    t = TensorSpec("narrow32s", (rows, 32), torch.bfloat16, (2,), (0,), (16,), (1,))
+    return Workload(f"narrow_columns_64b_tp16_{rows}x32", (t,), "normal",
+                    f"{rows}x32 bf16 N(0,0.02), (2,)[S0] -> (16,)[S1]: 4-byte slices of 64-byte rows")
+
+
+def narrow_columns_ragged_tp4(rows: int = 2396745) -> Workload:
+    """14 bf16 columns (28-byte rows) over four destinations: ceil-split column
+    shards of 4, 4, 4 and 2 elements (8-, 8-, 8- and 4-byte runs)."""
+    t = TensorSpec("narrow14", (rows, 14), torch.bfloat16, (2,), (0,), (4,), (1,))
+    return Workload(f"narrow_columns_ragged_tp4_{rows}x14", (t,), "normal",
+                    f"{rows}x14 bf16 N(0,0.02), (2,)[S0] -> (4,)[S1]: ragged 8/8/8/4-byte column shards")
+
+
 WORKLOADS = {
     "worked_example_8x8": worked_example_8x8,
     "ffn_up_14336x4096": ffn_up,
@@ -273,6 +299,9 @@ WORKLOADS = {
     "dense_layer_refit_32_layers": dense_layer_refit,
     "ffn_up_fsdp2_tp_14336x4096": ffn_up_fsdp2_tp,
     "ffn_up_partial_14336x4096": ffn_up_partial,
+    "narrow_columns_8b_tp2_8388608x4": narrow_columns_8b_tp2,
+    "narrow_columns_64b_tp16_1048576x32": narrow_columns_64b_tp16,
+    "narrow_columns_ragged_tp4_2396745x14": narrow_columns_ragged_tp4,
 }
 
 

@@ -46,11 +46,11 @@ def kernel_meta(tmp_path_factory):
 
 def test_every_variant_is_compiled(kernel_meta):
     names = [n for n in kernel_meta if "reshard_copy_kernel" in n]
-    # two pointer placements x thirteen variants (16-byte items, destination
+    # two pointer placements x fourteen variants (16-byte items, destination
     # chunks, aligned destination chunks, copy modes, quad row bands, 2-byte-run
     # bands, 4-byte-run bands, 8-byte-run bands in 64- and 32-byte rows, 16-byte
-    # chunk bands, gather-rows bands, Partial sums, all modes)
-    assert len(names) == 26, sorted(kernel_meta)
+    # chunk bands, gather-rows bands, Partial sums, dword bands, all modes)
+    assert len(names) == 28, sorted(kernel_meta)
 
 
 def test_no_scratch(kernel_meta):
@@ -58,11 +58,13 @@ def test_no_scratch(kernel_meta):
         assert meta["private"] == 0, (name, meta)
 
 
-def test_lds_only_in_the_window_variant(kernel_meta):
-    """Only the all-modes variant (LDS windows) allocates LDS: a private array
-    the compiler moved to LDS (an index it could not resolve) shows up here."""
+def test_lds_only_in_the_window_variants(kernel_meta):
+    """Only the all-modes variant (LDS windows) and the dword-band variant
+    allocate LDS: a private array the compiler moved to LDS (an index it could
+    not resolve) shows up here."""
     for name, meta in kernel_meta.items():
-        want = 16384 if re.search(r"reshard_copy_kernelILb[01]ELi3E", name) else 0
+        want = 16384 if re.search(r"reshard_copy_kernelILb[01]ELi3E", name) else \
+            18432 if re.search(r"reshard_copy_kernelILb[01]ELi12E", name) else 0
         assert meta["lds"] == want, (name, meta)
 
 

@@ -548,7 +548,8 @@ def test_piece_counts_of_workloads():
               "narrow_columns_tp8_2097152x16": 16, "narrow_columns_64b_tp8_1048576x32": 16, "narrow_columns_64b_tp4_1048576x32": 8,
               "narrow_columns_32b_tp4_2097152x16": 8, "narrow_columns_16b_tp8_4194304x8": 16,
               "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1), "ffn_up_fsdp2_tp_14336x4096": 16,
-              "ffn_up_partial_14336x4096": 8}
+              "ffn_up_partial_14336x4096": 8, "narrow_columns_8b_tp2_8388608x4": 4,
+              "narrow_columns_64b_tp16_1048576x32": 32, "narrow_columns_ragged_tp4_2396745x14": 8}
     for wl in full_workload_plans():
         with Plan(wl.tensors) as plan:
             assert plan.stats()["n_pieces"] == counts[wl.name]
