@@ -478,6 +478,13 @@ __device__ __forceinline__ uint32_t div_small(uint32_t n, uint32_t w, uint32_t m
   return w == 1 ? n : __umulhi(n, m);
 }
 
+// Whether four consecutive stream dwords of a segment (from a multiple of 4)
+// stay consecutive in the window: the segment is a whole number of 16 bytes
+// wide, or it is the whole row and the pitch adds no padding (odd width).
+__device__ __forceinline__ bool dword_quads(uint32_t w, uint32_t c, uint32_t pitch) {
+  return (w & 3u) == 0 || (c == 0 && w == pitch);
+}
+
 template <class Sh>
 __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
                                               const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile,
@@ -489,13 +496,34 @@ __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, con
   const reshard_segment_t* src_segs = segs + D.src_ptr;
   const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
 
-  // phase 1: source streams -> window
+  // phase 1: source streams -> window; 16-byte accesses where four stream
+  // dwords stay together in the window, single dwords otherwise
   for (uint32_t s = 0; s < D.dst_ref_begin; ++s) {
     const reshard_segment_t S = src_segs[s];
     const uint32_t w = S.width / 4, c = S.col / 4, n = hr * w;
     const uint32_t m = w > 1 ? 0xffffffffu / w + 1u : 0u;
     const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
-    for (uint32_t base = threadIdx.x; base < n; base += kBlock * kDwordBatch) {
+    uint32_t done = 0;  // stream dwords moved as quads
+    if (dword_quads(w, c, pitch)) {
+      const uint32_t nq = n / 4;
+      for (uint32_t base = threadIdx.x; base < nq; base += kBlock * kDwordBatch) {
+        u32x4 v[kDwordBatch];
+#pragma unroll
+        for (int k = 0; k < kDwordBatch; ++k) {
+          const uint32_t q = base + uint32_t(k) * kBlock;
+          if (q < nq) v[k] = load_16_unaligned(g + 16 * uint64_t(q));
+        }
+#pragma unroll
+        for (int k = 0; k < kDwordBatch; ++k) {
+          const uint32_t q = base + uint32_t(k) * kBlock;
+          if (q >= nq) break;
+          const uint32_t j = 4 * q, r = div_small(j, w, m);
+          *reinterpret_cast<u32x4_u1*>(lds + r * pitch + c + (j - r * w)) = v[k];
+        }
+      }
+      done = 4 * nq;
+    }
+    for (uint32_t base = done + threadIdx.x; base < n; base += kBlock * kDwordBatch) {
       uint32_t v[kDwordBatch];
 #pragma unroll
       for (int k = 0; k < kDwordBatch; ++k) {
@@ -519,7 +547,18 @@ __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, con
     const uint32_t w = S.width / 4, c = S.col / 4, n = hr * w;
     const uint32_t m = w > 1 ? 0xffffffffu / w + 1u : 0u;
     const uint64_t row_off = uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
-    for (uint32_t j = threadIdx.x; j < n; j += kBlock) {
+    uint32_t done = 0;
+    if (dword_quads(w, c, pitch)) {
+      const uint32_t nq = n / 4;
+      for (uint32_t q = threadIdx.x; q < nq; q += kBlock) {
+        const uint32_t j = 4 * q, r = div_small(j, w, m);
+        const u32x4 v = *reinterpret_cast<const u32x4_u1*>(lds + r * pitch + c + (j - r * w));
+        for (uint32_t f = 0; f < S.fanout; ++f)
+          __builtin_nontemporal_store(v, as_global<u32x4_u1>(sh.ptr(refs[S.ptr + f]) + row_off + 16 * uint64_t(q)));
+      }
+      done = 4 * nq;
+    }
+    for (uint32_t j = done + threadIdx.x; j < n; j += kBlock) {
       const uint32_t r = div_small(j, w, m);
       const uint32_t v = lds[r * pitch + c + (j - r * w)];
       for (uint32_t f = 0; f < S.fanout; ++f)
