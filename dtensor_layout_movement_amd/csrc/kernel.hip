@@ -485,6 +485,12 @@ __device__ __forceinline__ bool dword_quads(uint32_t w, uint32_t c, uint32_t pit
   return (w & 3u) == 0 || (c == 0 && w == pitch);
 }
 
+__device__ __forceinline__ uint64_t readlane64(uint64_t v, uint32_t lane) {
+  const uint32_t lo = __builtin_amdgcn_readlane(uint32_t(v), lane);
+  const uint32_t hi = __builtin_amdgcn_readlane(uint32_t(v >> 32), lane);
+  return uint64_t(lo) | (uint64_t(hi) << 32);
+}
+
 template <class Sh>
 __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
                                               const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile,
@@ -493,16 +499,40 @@ __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, con
   const uint32_t r0 = tile * per_tile;
   const uint32_t hr = min(per_tile, rows - r0);
   const uint32_t pitch = (D.run_bytes / 4) | 1u;  // odd
+  const uint32_t ns = D.dst_ref_begin, nd = D.fanout;  // at most 64 each
   const reshard_segment_t* src_segs = segs + D.src_ptr;
-  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
+  const reshard_segment_t* dst_segs = src_segs + ns;
+  // Every wave reads the segments once, lane s holding source segment s and
+  // destination segment s (with its first replica's address), so that the
+  // per-segment loops below take their fields from registers instead of
+  // waiting on two dependent scalar loads per segment.
+  const uint32_t lane = threadIdx.x & 63u;
+  uint32_t s_wc = 0, d_wc = 0, d_ref = 0, d_fan = 0;  // width | col << 16 (dwords)
+  uint32_t s_m = 0, d_m = 0;                           // division constants of the widths
+  uint64_t s_addr = 0, d_off = 0, d_addr = 0;
+  if (lane < ns) {
+    const reshard_segment_t S = src_segs[lane];
+    s_wc = (S.width / 4) | ((S.col / 4) << 16);
+    s_m = S.width > 4 ? 0xffffffffu / (S.width / 4) + 1u : 0u;
+    s_addr = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+  }
+  if (lane < nd) {
+    const reshard_segment_t S = dst_segs[lane];
+    d_wc = (S.width / 4) | ((S.col / 4) << 16);
+    d_m = S.width > 4 ? 0xffffffffu / (S.width / 4) + 1u : 0u;
+    d_off = uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+    d_ref = S.ptr;
+    d_fan = S.fanout;
+    d_addr = sh.ptr(refs[S.ptr]) + d_off;
+  }
 
   // phase 1: source streams -> window; 16-byte accesses where four stream
   // dwords stay together in the window, single dwords otherwise
-  for (uint32_t s = 0; s < D.dst_ref_begin; ++s) {
-    const reshard_segment_t S = src_segs[s];
-    const uint32_t w = S.width / 4, c = S.col / 4, n = hr * w;
-    const uint32_t m = w > 1 ? 0xffffffffu / w + 1u : 0u;
-    const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+  for (uint32_t s = 0; s < ns; ++s) {
+    const uint32_t wc = __builtin_amdgcn_readlane(s_wc, s);
+    const uint32_t w = wc & 0xffffu, c = wc >> 16, n = hr * w;
+    const uint32_t m = __builtin_amdgcn_readlane(s_m, s);
+    const uintptr_t g = readlane64(s_addr, s);
     uint32_t done = 0;  // stream dwords moved as quads
     if (dword_quads(w, c, pitch)) {
       const uint32_t nq = n / 4;
@@ -542,27 +572,33 @@ __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, con
   __syncthreads();
 
   // phase 2: window -> destination streams, every replica
-  for (uint32_t s = 0; s < D.fanout; ++s) {
-    const reshard_segment_t S = dst_segs[s];
-    const uint32_t w = S.width / 4, c = S.col / 4, n = hr * w;
-    const uint32_t m = w > 1 ? 0xffffffffu / w + 1u : 0u;
-    const uint64_t row_off = uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
+#pragma unroll 2
+  for (uint32_t s = 0; s < nd; ++s) {
+    const uint32_t wc = __builtin_amdgcn_readlane(d_wc, s);
+    const uint32_t w = wc & 0xffffu, c = wc >> 16, n = hr * w;
+    const uint32_t m = __builtin_amdgcn_readlane(d_m, s);
+    const uintptr_t g0 = readlane64(d_addr, s);
+    const uint32_t fan = __builtin_amdgcn_readlane(d_fan, s);
+    const uint32_t ref = __builtin_amdgcn_readlane(d_ref, s);
+    const uint64_t off = readlane64(d_off, s);
     uint32_t done = 0;
     if (dword_quads(w, c, pitch)) {
       const uint32_t nq = n / 4;
       for (uint32_t q = threadIdx.x; q < nq; q += kBlock) {
         const uint32_t j = 4 * q, r = div_small(j, w, m);
         const u32x4 v = *reinterpret_cast<const u32x4_u1*>(lds + r * pitch + c + (j - r * w));
-        for (uint32_t f = 0; f < S.fanout; ++f)
-          __builtin_nontemporal_store(v, as_global<u32x4_u1>(sh.ptr(refs[S.ptr + f]) + row_off + 16 * uint64_t(q)));
+        __builtin_nontemporal_store(v, as_global<u32x4_u1>(g0 + 16 * uint64_t(q)));
+        for (uint32_t f = 1; f < fan; ++f)
+          __builtin_nontemporal_store(v, as_global<u32x4_u1>(sh.ptr(refs[ref + f]) + off + 16 * uint64_t(q)));
       }
       done = 4 * nq;
     }
     for (uint32_t j = done + threadIdx.x; j < n; j += kBlock) {
       const uint32_t r = div_small(j, w, m);
       const uint32_t v = lds[r * pitch + c + (j - r * w)];
-      for (uint32_t f = 0; f < S.fanout; ++f)
-        __builtin_nontemporal_store(v, as_global<u32_u>(sh.ptr(refs[S.ptr + f]) + row_off + 4 * uint64_t(j)));
+      __builtin_nontemporal_store(v, as_global<u32_u>(g0 + 4 * uint64_t(j)));
+      for (uint32_t f = 1; f < fan; ++f)
+        __builtin_nontemporal_store(v, as_global<u32_u>(sh.ptr(refs[ref + f]) + off + 4 * uint64_t(j)));
     }
   }
 }
@@ -2102,6 +2138,7 @@ bool dwords_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
   const uint32_t w = D.run_bytes;
   if (D.mode != RESHARD_DESC_WINDOW || w <= uint32_t(rs::kRowModeBytes) || w > 256 || w % 4) return false;
   if (uint64_t(D.extent[1]) * ((w / 4) | 1u) > kDwordWindowWords) return false;
+  if (D.dst_ref_begin > 64 || D.fanout > 64) return false;  // one segment per lane
   const reshard_segment_t* S = segs.data() + D.src_ptr;
   for (uint32_t i = 0; i < D.dst_ref_begin + D.fanout; ++i) {
     const reshard_segment_t& x = S[i];
