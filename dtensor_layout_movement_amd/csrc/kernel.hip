@@ -506,25 +506,20 @@ __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, con
   // destination segment s (with its first replica's address), so that the
   // per-segment loops below take their fields from registers instead of
   // waiting on two dependent scalar loads per segment.
+  // (lanes past the last segment read segment 0 again: every load is issued
+  // unconditionally, so that the two segment loads, then the source pointer
+  // and the fan-out entry, then the destination pointer go out together)
   const uint32_t lane = threadIdx.x & 63u;
-  uint32_t s_wc = 0, d_wc = 0, d_ref = 0, d_fan = 0;  // width | col << 16 (dwords)
-  uint32_t s_m = 0, d_m = 0;                           // division constants of the widths
-  uint64_t s_addr = 0, d_off = 0, d_addr = 0;
-  if (lane < ns) {
-    const reshard_segment_t S = src_segs[lane];
-    s_wc = (S.width / 4) | ((S.col / 4) << 16);
-    s_m = S.width > 4 ? 0xffffffffu / (S.width / 4) + 1u : 0u;
-    s_addr = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
-  }
-  if (lane < nd) {
-    const reshard_segment_t S = dst_segs[lane];
-    d_wc = (S.width / 4) | ((S.col / 4) << 16);
-    d_m = S.width > 4 ? 0xffffffffu / (S.width / 4) + 1u : 0u;
-    d_off = uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.row_stride);
-    d_ref = S.ptr;
-    d_fan = S.fanout;
-    d_addr = sh.ptr(refs[S.ptr]) + d_off;
-  }
+  const reshard_segment_t SS = src_segs[lane < ns ? lane : 0u];
+  const uint64_t s_addr = sh.ptr(SS.ptr) + uint64_t(SS.offset) + uint64_t(r0) * uint64_t(SS.row_stride);
+  const reshard_segment_t SD = dst_segs[lane < nd ? lane : 0u];
+  const uint64_t d_off = uint64_t(SD.offset) + uint64_t(r0) * uint64_t(SD.row_stride);
+  const uint32_t d_ref = SD.ptr, d_fan = SD.fanout;
+  const uint64_t d_addr = sh.ptr(refs[SD.ptr]) + d_off;
+  const uint32_t s_wc = (SS.width / 4) | ((SS.col / 4) << 16);  // width | col << 16 (dwords)
+  const uint32_t d_wc = (SD.width / 4) | ((SD.col / 4) << 16);
+  // division constants of the widths (a width of one dword wraps to 0, unused)
+  const uint32_t s_m = 0xffffffffu / (SS.width / 4) + 1u, d_m = 0xffffffffu / (SD.width / 4) + 1u;
 
   // phase 1: source streams -> window; 16-byte accesses where four stream
   // dwords stay together in the window, single dwords otherwise
