@@ -227,6 +227,7 @@ __device__ __forceinline__ void copy_chunks(const reshard_descriptor_t& D, const
 // runs still move in 16-byte global accesses.
 
 typedef uint32_t u32x4_u1 __attribute__((ext_vector_type(4), aligned(1)));
+typedef uint32_t u32x2_u1 __attribute__((ext_vector_type(2), aligned(1)));
 
 __device__ __forceinline__ u32x4 shift_left_bytes(u32x4 v, uint32_t s) {  // s in [0, 15]
   if (s == 0) return v;
@@ -491,6 +492,47 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, uint32_t lane) {
   return uint64_t(lo) | (uint64_t(hi) << 32);
 }
 
+// Phase 1 of a dword band for one source stream: loads into the window.
+__device__ __forceinline__ void dword_stream_in(uintptr_t g, uint32_t w, uint32_t c, uint32_t m, uint32_t hr,
+                                                uint32_t pitch, uint32_t* lds) {
+  const uint32_t n = hr * w;
+  uint32_t done = 0;  // stream dwords moved as quads
+  if (dword_quads(w, c, pitch)) {
+    const uint32_t nq = n / 4;
+    for (uint32_t base = threadIdx.x; base < nq; base += kBlock * kDwordBatch) {
+      u32x4 v[kDwordBatch];
+#pragma unroll
+      for (int k = 0; k < kDwordBatch; ++k) {
+        const uint32_t q = base + uint32_t(k) * kBlock;
+        if (q < nq) v[k] = load_16_unaligned(g + 16 * uint64_t(q));
+      }
+#pragma unroll
+      for (int k = 0; k < kDwordBatch; ++k) {
+        const uint32_t q = base + uint32_t(k) * kBlock;
+        if (q >= nq) break;
+        const uint32_t j = 4 * q, r = div_small(j, w, m);
+        *reinterpret_cast<u32x4_u1*>(lds + r * pitch + c + (j - r * w)) = v[k];
+      }
+    }
+    done = 4 * nq;
+  }
+  for (uint32_t base = done + threadIdx.x; base < n; base += kBlock * kDwordBatch) {
+    uint32_t v[kDwordBatch];
+#pragma unroll
+    for (int k = 0; k < kDwordBatch; ++k) {
+      const uint32_t j = base + uint32_t(k) * kBlock;
+      if (j < n) v[k] = __builtin_nontemporal_load(as_global<const u32_u>(g + 4 * uint64_t(j)));
+    }
+#pragma unroll
+    for (int k = 0; k < kDwordBatch; ++k) {
+      const uint32_t j = base + uint32_t(k) * kBlock;
+      if (j >= n) break;
+      const uint32_t r = div_small(j, w, m);
+      lds[r * pitch + c + (j - r * w)] = v[k];
+    }
+  }
+}
+
 template <class Sh>
 __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
                                               const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile,
@@ -502,78 +544,68 @@ __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, con
   const uint32_t ns = D.dst_ref_begin, nd = D.fanout;  // at most 64 each
   const reshard_segment_t* src_segs = segs + D.src_ptr;
   const reshard_segment_t* dst_segs = src_segs + ns;
-  // Every wave reads the segments once, lane s holding source segment s and
-  // destination segment s (with its first replica's address), so that the
-  // per-segment loops below take their fields from registers instead of
-  // waiting on two dependent scalar loads per segment.
-  // (lanes past the last segment read segment 0 again: every load is issued
-  // unconditionally, so that the two segment loads, then the source pointer
-  // and the fan-out entry, then the destination pointer go out together)
+  // Every wave reads the destination segments once, lane s holding segment s
+  // and its first replica's address (its slot sits in the segment's row_stride
+  // in the device table), so that the loop of phase 2 takes them from
+  // registers.  The loads go out first; phase 1 does not wait for them.
+  // (Lanes past the last segment read segment 0 again.)
   const uint32_t lane = threadIdx.x & 63u;
-  const reshard_segment_t SS = src_segs[lane < ns ? lane : 0u];
-  const uint64_t s_addr = sh.ptr(SS.ptr) + uint64_t(SS.offset) + uint64_t(r0) * uint64_t(SS.row_stride);
   const reshard_segment_t SD = dst_segs[lane < nd ? lane : 0u];
-  const uint64_t d_off = uint64_t(SD.offset) + uint64_t(r0) * uint64_t(SD.row_stride);
-  const uint32_t d_ref = SD.ptr, d_fan = SD.fanout;
-  const uint64_t d_addr = sh.ptr(refs[SD.ptr]) + d_off;
-  const uint32_t s_wc = (SS.width / 4) | ((SS.col / 4) << 16);  // width | col << 16 (dwords)
-  const uint32_t d_wc = (SD.width / 4) | ((SD.col / 4) << 16);
-  // division constants of the widths (a width of one dword wraps to 0, unused)
-  const uint32_t s_m = 0xffffffffu / (SS.width / 4) + 1u, d_m = 0xffffffffu / (SD.width / 4) + 1u;
 
   // phase 1: source streams -> window; 16-byte accesses where four stream
-  // dwords stay together in the window, single dwords otherwise
-  for (uint32_t s = 0; s < ns; ++s) {
-    const uint32_t wc = __builtin_amdgcn_readlane(s_wc, s);
-    const uint32_t w = wc & 0xffffu, c = wc >> 16, n = hr * w;
-    const uint32_t m = __builtin_amdgcn_readlane(s_m, s);
-    const uintptr_t g = readlane64(s_addr, s);
-    uint32_t done = 0;  // stream dwords moved as quads
-    if (dword_quads(w, c, pitch)) {
-      const uint32_t nq = n / 4;
-      for (uint32_t base = threadIdx.x; base < nq; base += kBlock * kDwordBatch) {
-        u32x4 v[kDwordBatch];
-#pragma unroll
-        for (int k = 0; k < kDwordBatch; ++k) {
-          const uint32_t q = base + uint32_t(k) * kBlock;
-          if (q < nq) v[k] = load_16_unaligned(g + 16 * uint64_t(q));
-        }
-#pragma unroll
-        for (int k = 0; k < kDwordBatch; ++k) {
-          const uint32_t q = base + uint32_t(k) * kBlock;
-          if (q >= nq) break;
-          const uint32_t j = 4 * q, r = div_small(j, w, m);
-          *reinterpret_cast<u32x4_u1*>(lds + r * pitch + c + (j - r * w)) = v[k];
-        }
-      }
-      done = 4 * nq;
-    }
-    for (uint32_t base = done + threadIdx.x; base < n; base += kBlock * kDwordBatch) {
-      uint32_t v[kDwordBatch];
-#pragma unroll
-      for (int k = 0; k < kDwordBatch; ++k) {
-        const uint32_t j = base + uint32_t(k) * kBlock;
-        if (j < n) v[k] = __builtin_nontemporal_load(as_global<const u32_u>(g + 4 * uint64_t(j)));
-      }
-#pragma unroll
-      for (int k = 0; k < kDwordBatch; ++k) {
-        const uint32_t j = base + uint32_t(k) * kBlock;
-        if (j >= n) break;
-        const uint32_t r = div_small(j, w, m);
-        lds[r * pitch + c + (j - r * w)] = v[k];
-      }
+  // dwords stay together in the window, single dwords otherwise.  One source
+  // segment comes through the scalar cache; several, one per lane as above.
+  if (ns == 1) {
+    const reshard_segment_t S = src_segs[0];
+    const uint32_t w = S.width / 4;
+    dword_stream_in(sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.width), w, S.col / 4,
+                    w > 1 ? 0xffffffffu / w + 1u : 0u, hr, pitch, lds);
+  } else {
+    const reshard_segment_t SS = src_segs[lane < ns ? lane : 0u];
+    const uint32_t s_wc = (SS.width / 4) | ((SS.col / 4) << 16);  // width | col << 16 (dwords)
+    const uint32_t s_m = 0xffffffffu / (SS.width / 4) + 1u;       // a width of one wraps to 0, unused
+    const uint64_t s_addr = sh.ptr(SS.ptr) + uint64_t(SS.offset) + uint64_t(r0) * uint64_t(SS.width);
+    for (uint32_t s = 0; s < ns; ++s) {
+      const uint32_t wc = __builtin_amdgcn_readlane(s_wc, s);
+      dword_stream_in(readlane64(s_addr, s), wc & 0xffffu, wc >> 16, __builtin_amdgcn_readlane(s_m, s), hr, pitch,
+                      lds);
     }
   }
+  const uint32_t d_wc = (SD.width / 4) | ((SD.col / 4) << 16);
+  const uint32_t d_m = 0xffffffffu / (SD.width / 4) + 1u;
+  const uint64_t d_off = uint64_t(SD.offset) + uint64_t(r0) * uint64_t(SD.width);
+  const uint32_t d_ref = SD.ptr, d_fan = SD.fanout;
+  const uint64_t d_addr = sh.ptr(uint32_t(SD.row_stride)) + d_off;
   __syncthreads();
 
-  // phase 2: window -> destination streams, every replica
-#pragma unroll 2
+  // phase 2: window -> destination streams, every replica.  A segment at most
+  // four dwords wide goes row by row, one row a lane: one LDS read of the
+  // row's dwords and one store of them (the lanes' stores are consecutive in
+  // the stream); wider ones in stream order like phase 1.
   for (uint32_t s = 0; s < nd; ++s) {
     const uint32_t wc = __builtin_amdgcn_readlane(d_wc, s);
     const uint32_t w = wc & 0xffffu, c = wc >> 16, n = hr * w;
-    const uint32_t m = __builtin_amdgcn_readlane(d_m, s);
     const uintptr_t g0 = readlane64(d_addr, s);
     const uint32_t fan = __builtin_amdgcn_readlane(d_fan, s);
+    if (w <= 4 && fan == 1) {
+      for (uint32_t r = threadIdx.x; r < hr; r += kBlock) {
+        const uint32_t* src = lds + r * pitch + c;
+        const uintptr_t d = g0 + uint64_t(r) * (4 * w);
+        switch (w) {
+          case 1: __builtin_nontemporal_store(src[0], as_global<u32_u>(d)); break;
+          case 2: __builtin_nontemporal_store(*reinterpret_cast<const u32x2_u1*>(src), as_global<u32x2_u1>(d)); break;
+          case 3: {
+            const u32x2_u1 a = *reinterpret_cast<const u32x2_u1*>(src);
+            __builtin_nontemporal_store(a, as_global<u32x2_u1>(d));
+            __builtin_nontemporal_store(src[2], as_global<u32_u>(d + 8));
+            break;
+          }
+          default: __builtin_nontemporal_store(*reinterpret_cast<const u32x4_u1*>(src), as_global<u32x4_u1>(d));
+        }
+      }
+      continue;
+    }
+    const uint32_t m = __builtin_amdgcn_readlane(d_m, s);
     const uint32_t ref = __builtin_amdgcn_readlane(d_ref, s);
     const uint64_t off = readlane64(d_off, s);
     uint32_t done = 0;
@@ -2145,6 +2177,7 @@ bool dwords_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
 }  // namespace
 
 int kernel_kind_gather_rows() { return kKindGatherRows; }
+int kernel_kind_dwords() { return kKindDwords; }
 
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {

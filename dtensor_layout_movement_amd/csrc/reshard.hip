@@ -201,6 +201,18 @@ void build_image_locked(reshard_plan_s* p) {
   // fan-out list, whose entries were made absolute above
   reshard_segment_t* sg = reinterpret_cast<reshard_segment_t*>(img.data() + segs_off);
   for (size_t i = 0; i < H.segs.size(); ++i) sg[i] = H.segs[i];
+  // dword bands: each destination segment carries its first replica's slot
+  // (the kernel then reaches the pointer in one load instead of two)
+  for (const Group& g : groups) {
+    if (g.kind != rs::kernel_kind_dwords()) continue;
+    for (const uint32_t i : g.descs) {
+      const reshard_descriptor_t& D = H.descs[i];
+      for (uint32_t k = 0; k < D.fanout; ++k) {
+        reshard_segment_t& x = sg[D.src_ptr + D.dst_ref_begin + k];
+        x.row_stride = int64_t(uint32_t(H.n_src_ptrs) + H.refs[x.ptr]);
+      }
+    }
+  }
   p->image = std::move(img);
   p->launches = std::move(launches);
   p->refs_off = refs_off;
@@ -670,6 +682,18 @@ reshard_status_t reshard_plan_device_refs(reshard_plan_t plan, int64_t capacity,
   *n_refs = int64_t(plan->host.refs.size());
   const uint32_t* r = reinterpret_cast<const uint32_t*>(plan->image.data() + plan->refs_off);
   for (int64_t i = 0; i < std::min<int64_t>(capacity, *n_refs); ++i) refs[i] = r[i];
+  return RESHARD_OK;
+}
+
+reshard_status_t reshard_plan_device_segments(reshard_plan_t plan, int64_t capacity, reshard_segment_t* out,
+                                              int64_t* n_total) {
+  if (!plan || !n_total || capacity < 0 || (capacity > 0 && !out))
+    return fail(RESHARD_ERR_INVALID_ARGUMENT, "bad argument");
+  std::lock_guard<std::mutex> lock(plan->mu);
+  build_image_locked(plan);
+  *n_total = int64_t(plan->host.segs.size());
+  const reshard_segment_t* sg = reinterpret_cast<const reshard_segment_t*>(plan->image.data() + plan->segs_off);
+  for (int64_t i = 0; i < std::min<int64_t>(capacity, *n_total); ++i) out[i] = sg[i];
   return RESHARD_OK;
 }
 

@@ -55,7 +55,7 @@ EXPORTED = (
     "reshard_layout_num_ranks", "reshard_layout_shard_box", "reshard_plan_create",
     "reshard_plan_create_batched", "reshard_plan_upload", "reshard_execute", "reshard_execute_noalloc",
     "reshard_plan_stats", "reshard_plan_src_load", "reshard_plan_pieces", "reshard_plan_piece_sources",
-    "reshard_plan_device_refs",
+    "reshard_plan_device_refs", "reshard_plan_device_segments",
     "reshard_plan_piece_fanout",
     "reshard_plan_descriptors", "reshard_plan_segments", "reshard_plan_destroy",
     "reshard_last_error",
@@ -145,6 +145,7 @@ def _load() -> ctypes.CDLL:
         "reshard_plan_piece_fanout": (st, [_VP, _I64, _I64, _I64P, _I64P]),
         "reshard_plan_piece_sources": (st, [_VP, _I64, _I64, _I64P, _I64P]),
         "reshard_plan_device_refs": (st, [_VP, _I64, ctypes.POINTER(ctypes.c_uint32), _I64P]),
+        "reshard_plan_device_segments": (st, [_VP, _I64, ctypes.POINTER(Segment), _I64P]),
         "reshard_plan_descriptors": (st, [_VP, _I64, ctypes.POINTER(Descriptor), _I64P, _I64,
                                           ctypes.POINTER(ctypes.c_uint32), _I64P]),
         "reshard_plan_segments": (st, [_VP, _I64, ctypes.POINTER(Segment), _I64P]),
@@ -329,6 +330,15 @@ def reshard_plan_device_refs(plan: int) -> list[int]:
     arr = (ctypes.c_uint32 * max(1, n.value))()
     _check(_load().reshard_plan_device_refs(plan, n.value, arr, ctypes.byref(n)))
     return list(arr[:n.value])
+
+
+def reshard_plan_device_segments(plan: int) -> list[dict]:
+    """The segment table as the kernel reads it (see the C header)."""
+    n = ctypes.c_int64()
+    _check(_load().reshard_plan_device_segments(plan, 0, None, ctypes.byref(n)))
+    arr = (Segment * max(1, n.value))()
+    _check(_load().reshard_plan_device_segments(plan, n.value, arr, ctypes.byref(n)))
+    return [{name: getattr(x, name) for name, _ in Segment._fields_} for x in arr[:n.value]]
 
 
 def reshard_plan_piece_sources(plan: int, index: int) -> list[int]:

@@ -457,6 +457,18 @@ reshard_status_t reshard_plan_pieces(reshard_plan_t plan, int64_t capacity,
 reshard_status_t reshard_plan_device_refs(reshard_plan_t plan, int64_t capacity, uint32_t* refs,
                                           int64_t* n_refs);
 
+/*
+ * Inspection: the segment table as the kernel reads it from the device table,
+ * host-side (no device call).  It equals reshard_plan_segments except in the
+ * destination segments of the bands that the dword-band kernel build moves
+ * (packed bands at dword granularity: every segment's row stride is its width):
+ * there row_stride holds the absolute pointer slot of the segment's first
+ * replica instead.  Writes min(capacity, count) segments and the count.
+ * Errors: RESHARD_ERR_INVALID_ARGUMENT.
+ */
+reshard_status_t reshard_plan_device_segments(reshard_plan_t plan, int64_t capacity, reshard_segment_t* out,
+                                              int64_t* n_total);
+
 /* Source ranks (within the piece's tensor) that piece `index` reads, in
  * contribution order: one for a plain source, one per contribution for a
  * Partial source (the first is the piece's src_rank).  Writes min(capacity,

@@ -890,6 +890,41 @@ def test_errors():
     R.reshard_layout_destroy(None)
 
 
+def test_device_segments_of_dword_bands():
+    """The device table's segments equal the planned ones, except that each
+    destination segment of a packed dword band carries its first replica's
+    absolute pointer slot in row_stride (all of a band's segments, or none)."""
+    specs = [W.narrow_columns_64b_tp16(4096).tensors[0], W.narrow_columns_ragged_tp4(3001).tensors[0],
+             W.narrow_columns(2048).tensors[0], W.uneven(301, 257).tensors[0]]
+    specs += [s for s in small_specs() if s.name in ("wide_window", "narrow_scatter_rep", "strips_fanout")]
+    rewritten_bands = 0
+    for spec in specs:
+        with Plan([spec]) as plan:
+            st = plan.stats()
+            host = R.reshard_plan_segments(plan.handle)
+            dev = R.reshard_plan_device_segments(plan.handle)
+            _, refs = R.reshard_plan_descriptors(plan.handle)
+            descs, _ = R.reshard_plan_descriptors(plan.handle)
+            assert len(host) == len(dev)
+            for D in descs:
+                if D["mode"] != R.DESC_WINDOW:
+                    continue
+                first = D["src_ptr"]
+                for k in range(D["dst_ref_begin"]):  # sources: unchanged
+                    assert dev[first + k] == host[first + k]
+                dst = range(first + D["dst_ref_begin"], first + D["dst_ref_begin"] + D["fanout"])
+                # (a slot may equal the width by chance: one changed segment marks the band)
+                if any(dev[i] != host[i] for i in dst):
+                    rewritten_bands += 1
+                    for i in dst:
+                        h, d = host[i], dev[i]
+                        assert h["row_stride"] == h["width"] and h["width"] % 4 == 0
+                        assert d["row_stride"] == st["n_src_ptrs"] + refs[h["ptr"]]
+                        assert {k: v for k, v in d.items() if k != "row_stride"} == \
+                            {k: v for k, v in h.items() if k != "row_stride"}
+    assert rewritten_bands >= 2
+
+
 def test_partial_errors():
     """Partial only on a source, only for float elements, never with split factors."""
     src = R.reshard_layout_create((8, 4), R.DTYPE_F32, (2, 2), (R.PARTIAL, 0))
