@@ -587,6 +587,42 @@ __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, con
     const uint32_t w = wc & 0xffffu, c = wc >> 16, n = hr * w;
     const uintptr_t g0 = readlane64(d_addr, s);
     const uint32_t fan = __builtin_amdgcn_readlane(d_fan, s);
+    // four one-dword segments side by side (columns c .. c + 3, one replica
+    // each): one LDS read of the four dwords a row, four stores
+    if (w == 1 && fan == 1 && s + 3 < nd) {
+      const uint32_t wc3 = __builtin_amdgcn_readlane(d_wc, s + 3);
+      const uint32_t f1 = __builtin_amdgcn_readlane(d_fan, s + 1), f2 = __builtin_amdgcn_readlane(d_fan, s + 2),
+                     f3 = __builtin_amdgcn_readlane(d_fan, s + 3);
+      if (wc3 == (1u | ((c + 3) << 16)) && __builtin_amdgcn_readlane(d_wc, s + 1) == (1u | ((c + 1) << 16)) &&
+          __builtin_amdgcn_readlane(d_wc, s + 2) == (1u | ((c + 2) << 16)) && (f1 & f2 & f3) == 1) {
+        const uintptr_t g1 = readlane64(d_addr, s + 1), g2 = readlane64(d_addr, s + 2),
+                        g3 = readlane64(d_addr, s + 3);
+        for (uint32_t r = threadIdx.x; r < hr; r += kBlock) {
+          const u32x4 v = *reinterpret_cast<const u32x4_u1*>(lds + r * pitch + c);
+          const uint64_t o = 4 * uint64_t(r);
+          __builtin_nontemporal_store(v.x, as_global<u32_u>(g0 + o));
+          __builtin_nontemporal_store(v.y, as_global<u32_u>(g1 + o));
+          __builtin_nontemporal_store(v.z, as_global<u32_u>(g2 + o));
+          __builtin_nontemporal_store(v.w, as_global<u32_u>(g3 + o));
+        }
+        s += 3;
+        continue;
+      }
+    }
+    // two two-dword segments side by side (8-byte runs): one LDS read of the
+    // four dwords a row, two stores
+    if (w == 2 && fan == 1 && s + 1 < nd && __builtin_amdgcn_readlane(d_wc, s + 1) == (2u | ((c + 2) << 16)) &&
+        __builtin_amdgcn_readlane(d_fan, s + 1) == 1) {
+      const uintptr_t g1 = readlane64(d_addr, s + 1);
+      for (uint32_t r = threadIdx.x; r < hr; r += kBlock) {
+        const u32x4 v = *reinterpret_cast<const u32x4_u1*>(lds + r * pitch + c);
+        const uint64_t o = 8 * uint64_t(r);
+        __builtin_nontemporal_store(u32x2_u1{v.x, v.y}, as_global<u32x2_u1>(g0 + o));
+        __builtin_nontemporal_store(u32x2_u1{v.z, v.w}, as_global<u32x2_u1>(g1 + o));
+      }
+      s += 1;
+      continue;
+    }
     if (w <= 4 && fan == 1) {
       for (uint32_t r = threadIdx.x; r < hr; r += kBlock) {
         const uint32_t* src = lds + r * pitch + c;
