@@ -883,34 +883,6 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
   else return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x1F | (X << 10)));
 }
 
-// One butterfly stage of an 8 x 8 transpose of 32-bit words across each group
-// of eight consecutive lanes: word i of lane L and word i ^ X of lane L ^ X
-// trade places wherever bit X of L and of i differ.  The words travel by value
-// and every index is a compile-time constant (recursion over I): through a
-// reference, the select between the pair's two words is folded into a select
-// between their addresses, and the array then stays in memory (scratch or LDS).
-template <int X, int I = 0>
-__device__ __forceinline__ u32x8 transpose_stage(u32x8 m) {
-  if constexpr (I < 8) {
-    if constexpr ((I & X) == 0) {  // I is the low word of the pair (I, I ^ X)
-      const bool hi = (threadIdx.x & uint32_t(X)) != 0;
-      const uint32_t lo = m[I], up = m[I ^ X];
-      const uint32_t got = lane_xor<X>(hi ? lo : up);
-      m[I] = hi ? got : lo;
-      m[I ^ X] = hi ? up : got;
-    }
-    return transpose_stage<X, I + 1>(m);
-  } else {
-    return m;
-  }
-}
-
-// With row i of an 8 x 8 matrix in lane i of the group, lane j ends with
-// column j, after three butterfly stages.
-__device__ __forceinline__ u32x8 lanes_transpose8(u32x8 m) {
-  return transpose_stage<4>(transpose_stage<2>(transpose_stage<1>(m)));
-}
-
 // Whether segments [0, n) of a band are K packed rw-byte column runs in column
 // order (run s at column rw * s) with one fan-out, or one packed run of the
 // whole row of w bytes.  Host-side checks: in a plan that runs a band kernel
@@ -925,460 +897,6 @@ inline bool runs_side(const reshard_segment_t* S, uint32_t n, uint32_t k, uint32
 }
 inline bool full_side(const reshard_segment_t* S, uint32_t n, uint32_t w) {
   return n == 1 && S[0].width == w && uint64_t(S[0].row_stride) == w;
-}
-
-// A 32-byte window band whose one side is eight packed 4-byte column runs
-// (bf16 pairs or fp32 columns, one per shard) and whose other side is one packed
-// run of whole rows or eight runs too.  No LDS: the tile's 512 rows are split so
-// that every 16-byte access of a wave is contiguous on both sides.
-//  - whole-row side: slice q (0..3) of lane L is bytes [16 L, 16 L + 16) of the
-//    tile's q-th 4 KiB, i.e. half L & 1 of row L / 2 + 128 q;
-//  - run side: lane j of group G (eight lanes) holds rows 4G..4G+3 (+128 q) of
-//    the run at column 4j, 16 contiguous bytes.
-// Slices q = 2p (set A) and 2p + 1 (set B) travel together: the halves layout
-// (words 0-3: set A half h of row 4G + r, words 4-7: the same of set B, in lane
-// 8G + 2r + h) turns into whole rows with one exchange between lanes 1 apart
-// (lane 2r: row r of set A, lane 2r + 1: row r of set B), and then into the run
-// layout by the 8x8 transpose (word 2r: set A row r, word 2r + 1: set B row r,
-// of column j).  The reverse takes the same steps backwards.
-// The exchange between lanes 1 apart of words 0-3 (odd lanes) against words
-// 4-7 (even lanes), used both ways.  Value selects only (see transpose_stage).
-template <int I = 0>
-__device__ __forceinline__ u32x8 swap_halves(u32x8 m) {
-  if constexpr (I < 4) {
-    const bool h = (threadIdx.x & 1u) != 0;
-    const uint32_t a = m[I], b = m[4 + I];
-    const uint32_t got = lane_xor<1>(h ? a : b);
-    m[I] = h ? got : a;
-    m[4 + I] = h ? b : got;
-    return swap_halves<I + 1>(m);
-  } else {
-    return m;
-  }
-}
-// halves layout -> whole rows (lane 2r: set A row r = [own A half 0, the
-// neighbour's A half 1]; lane 2r + 1: set B row r = [the neighbour's B half 0,
-// own B half 1]) -> run layout
-__device__ __forceinline__ u32x8 halves_to_runs(u32x8 m) { return lanes_transpose8(swap_halves(m)); }
-__device__ __forceinline__ u32x8 runs_to_halves(u32x8 m) { return swap_halves(lanes_transpose8(m)); }
-
-// The run at column 4 * (lane & 7) of a run side (segment lane & 7: the runs
-// are in column order), replica f, at tile row 0.  Each lane resolves its own
-// run, so the three dependent lookups (segment, fan-out list, pointer) are
-// paid once, not once per segment.
-template <bool dst, class Sh>
-__device__ __forceinline__ uintptr_t run_base(const reshard_segment_t* __restrict__ S,
-                                              const uint32_t* __restrict__ refs, const Sh& sh, uint32_t r0,
-                                              uint32_t f) {
-  const reshard_segment_t& seg = S[threadIdx.x & 7u];
-  const uint32_t i = dst ? refs[seg.ptr + f] : seg.ptr;
-  return sh.ptr(i) + uint64_t(seg.offset) + uint64_t(r0) * 4u;
-}
-
-// Slices 2P and 2P + 1 of a window_runs8 tile (P a template argument, so that
-// no word index is left to run time).
-template <int P, bool src_runs>
-__device__ __forceinline__ u32x8 runs8_load(uintptr_t g, uint32_t hr) {
-  const uint32_t lane = threadIdx.x;
-  u32x8 m;
-#pragma unroll
-  for (int set = 0; set < 2; ++set) {
-    if constexpr (src_runs) {  // lane j of group G: rows 4G..4G+3 of the run at column 4j
-      const uint32_t r = 4u * (lane >> 3) + 128u * uint32_t(2 * P + set);
-      uint32_t w[4] = {0, 0, 0, 0};
-      if (r + 4 <= hr) {
-        const u32x4 x = load_16_unaligned(g + uint64_t(r) * 4u);
-        w[0] = x.x; w[1] = x.y; w[2] = x.z; w[3] = x.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r + i < hr) w[i] = __builtin_nontemporal_load(as_global<const u32_u>(g + uint64_t(r + i) * 4u));
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) m[2 * i + set] = w[i];
-    } else {  // half lane & 1 of row lane / 2 of whole 32-byte rows
-      const uint32_t r = (lane >> 1) + 128u * uint32_t(2 * P + set);
-      u32x4 x = u32x4{0, 0, 0, 0};
-      if (r < hr) x = load_16_unaligned(g + uint64_t(r) * 32u);
-      m[4 * set] = x.x; m[4 * set + 1] = x.y; m[4 * set + 2] = x.z; m[4 * set + 3] = x.w;
-    }
-  }
-  return m;
-}
-
-template <int P, bool dst_runs>
-__device__ __forceinline__ void runs8_store(u32x8 m, uintptr_t g, uint32_t hr) {
-  const uint32_t lane = threadIdx.x;
-#pragma unroll
-  for (int set = 0; set < 2; ++set) {
-    if constexpr (dst_runs) {
-      const uint32_t r = 4u * (lane >> 3) + 128u * uint32_t(2 * P + set);
-      const uint32_t w[4] = {m[set], m[2 + set], m[4 + set], m[6 + set]};
-      if (r + 4 <= hr) {
-        store_bytes(g + uint64_t(r) * 4u, u32x4{w[0], w[1], w[2], w[3]}, 16);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (r + i < hr) __builtin_nontemporal_store(w[i], as_global<u32_u>(g + uint64_t(r + i) * 4u));
-      }
-    } else {
-      const uint32_t r = (lane >> 1) + 128u * uint32_t(2 * P + set);
-      if (r < hr)
-        store_bytes(g + uint64_t(r) * 32u, u32x4{m[4 * set], m[4 * set + 1], m[4 * set + 2], m[4 * set + 3]}, 16);
-    }
-  }
-}
-
-// One body per pair of sides, so that each is straight-line code with no
-// values merged across the two layouts.
-template <bool src_runs, bool dst_runs, class Sh>
-__device__ __forceinline__ void window_runs8_sides(const reshard_descriptor_t& D,
-                                                   const reshard_segment_t* __restrict__ src_segs,
-                                                   const reshard_segment_t* __restrict__ dst_segs,
-                                                   const uint32_t* __restrict__ refs, const Sh& sh,
-                                                   uint32_t r0, uint32_t hr) {
-  const uint32_t h = threadIdx.x & 1u;
-  uintptr_t gs;
-  if constexpr (src_runs)
-    gs = run_base<false>(src_segs, refs, sh, r0, 0);
-  else
-    gs = sh.ptr(src_segs[0].ptr) + uint64_t(src_segs[0].offset) + uint64_t(r0) * 32u + 16u * h;
-  u32x8 m0 = runs8_load<0, src_runs>(gs, hr);
-  u32x8 m1 = runs8_load<1, src_runs>(gs, hr);
-  if constexpr (src_runs && !dst_runs) {
-    m0 = runs_to_halves(m0);
-    m1 = runs_to_halves(m1);
-  } else if constexpr (!src_runs && dst_runs) {
-    m0 = halves_to_runs(m0);
-    m1 = halves_to_runs(m1);
-  }
-  for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {  // one fan-out on a run side
-    uintptr_t gd;
-    if constexpr (dst_runs)
-      gd = run_base<true>(dst_segs, refs, sh, r0, f);
-    else
-      gd = sh.ptr(refs[dst_segs[0].ptr + f]) + uint64_t(dst_segs[0].offset) + uint64_t(r0) * 32u + 16u * h;
-    runs8_store<0, dst_runs>(m0, gd, hr);
-    runs8_store<1, dst_runs>(m1, gd, hr);
-  }
-}
-
-template <class Sh>
-__device__ __forceinline__ void window_runs8(const reshard_descriptor_t& D,
-                                             const reshard_segment_t* __restrict__ segs,
-                                             const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
-  const uint32_t rows = D.extent[0], per_tile = D.extent[1];  // 512 rows per tile
-  const uint32_t r0 = tile * per_tile;
-  const uint32_t hr = min(per_tile, rows - r0);
-  const reshard_segment_t* src_segs = segs + D.src_ptr;
-  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
-  const bool src_runs = D.dst_ref_begin == 8;  // else one segment of whole rows
-  const bool dst_runs = D.fanout == 8;
-  if (src_runs && dst_runs)
-    window_runs8_sides<true, true>(D, src_segs, dst_segs, refs, sh, r0, hr);
-  else if (src_runs)
-    window_runs8_sides<true, false>(D, src_segs, dst_segs, refs, sh, r0, hr);
-  else
-    window_runs8_sides<false, true>(D, src_segs, dst_segs, refs, sh, r0, hr);
-}
-
-// A 64-byte window band whose one side is eight packed 8-byte column runs (four
-// bf16 or two fp32 columns per shard over eight shards) and whose other side is
-// one packed run of whole rows.  No LDS: a tile is 256 rows, 64 per wave, and
-// every 16-byte access of a wave is contiguous on both sides.
-//  - whole-row side: slice q (0..3) of lane L = 4a + b is quarter b of row
-//    16 q + a of the wave's 64 (one 1 KiB piece per slice);
-//  - run side: lane L = 8G + j holds run j at rows 16 m + 2G and 16 m + 2G + 1
-//    of the wave's 64 for m = 0..3 (16 bytes per m; the eight lanes that hold
-//    run j cover its rows 16 m .. 16 m + 15 in one access).
-// Between the two: a 4 x 4 transpose of 16-byte quarters across each quad
-// (lane 4a + b then holds all of row 16 b + a), then an 8 x 8 transpose of
-// 8-byte elements across each group of eight lanes: lane offset o = 4e + m
-// holds row 16 m + 2G + e, so after it lane j holds run j at those eight rows
-// in the order o, and the 16-byte piece m is elements m and 4 + m.
-//
-// Stage X of the 8 x 8 transpose on 8-byte elements (words 2k and 2k + 1 of
-// element k): element k of lane o and element k ^ X of lane o ^ X trade places
-// wherever bit X of o and of k differ.  Values and constant indices only.
-template <int X, int K = 0>
-__device__ __forceinline__ u32x16 transpose_stage64(u32x16 m) {
-  if constexpr (K < 8) {
-    if constexpr ((K & X) == 0) {
-      const bool hi = (threadIdx.x & uint32_t(X)) != 0;
-      constexpr int A = 2 * K, B = 2 * (K ^ X);
-      const uint32_t lo0 = m[A], lo1 = m[A + 1], up0 = m[B], up1 = m[B + 1];
-      const uint32_t got0 = lane_xor<X>(hi ? lo0 : up0), got1 = lane_xor<X>(hi ? lo1 : up1);
-      m[A] = hi ? got0 : lo0;
-      m[A + 1] = hi ? got1 : lo1;
-      m[B] = hi ? up0 : got0;
-      m[B + 1] = hi ? up1 : got1;
-    }
-    return transpose_stage64<X, K + 1>(m);
-  } else {
-    return m;
-  }
-}
-__device__ __forceinline__ u32x16 lanes_transpose8x64(u32x16 m) {
-  return transpose_stage64<4>(transpose_stage64<2>(transpose_stage64<1>(m)));
-}
-// Quarter q of the row is words 4q..4q+3: word i of every quarter goes through
-// one 4 x 4 word transpose of the quad.
-template <int I = 0>
-__device__ __forceinline__ u32x16 quarters_transpose(u32x16 m) {
-  if constexpr (I < 4) {
-    const u32x4 v = quad_transpose(u32x4{m[I], m[4 + I], m[8 + I], m[12 + I]});
-    m[I] = v.x;
-    m[4 + I] = v.y;
-    m[8 + I] = v.z;
-    m[12 + I] = v.w;
-    return quarters_transpose<I + 1>(m);
-  } else {
-    return m;
-  }
-}
-
-template <bool src_runs, class Sh>
-__device__ __forceinline__ void window_runs64_sides(const reshard_segment_t* __restrict__ src_segs,
-                                                    const reshard_segment_t* __restrict__ dst_segs,
-                                                    const uint32_t* __restrict__ refs, const Sh& sh,
-                                                    uint32_t r0, uint32_t hr) {
-  const uint32_t lane = threadIdx.x & 63u, w0 = (threadIdx.x >> 6) * 64u;  // the wave's first tile row
-  const uint32_t a = lane >> 2, b = lane & 3u, G = lane >> 3;
-  u32x16 m;
-  // replica 0's run address (rows in) is looked up next to the data loads
-  const reshard_segment_t& dseg = dst_segs[lane & 7u];
-  const uintptr_t gd0 = src_runs ? 0 : sh.ptr(refs[dseg.ptr]) + uint64_t(dseg.offset) + uint64_t(r0) * 8u;
-  if constexpr (!src_runs) {  // whole rows in: slice q of lane 4a + b is quarter b of row 16q + a
-    const uintptr_t g = sh.ptr(src_segs[0].ptr) + uint64_t(src_segs[0].offset) + uint64_t(r0) * 64u + 16u * b;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t r = w0 + 16u * uint32_t(q) + a;
-      const u32x4 x = load_16_unaligned(g + uint64_t(min(r, hr - 1)) * 64u);  // past hr: never stored
-      m[4 * q] = x.x; m[4 * q + 1] = x.y; m[4 * q + 2] = x.z; m[4 * q + 3] = x.w;
-    }
-    m = lanes_transpose8x64(quarters_transpose(m));
-  } else {  // run lane & 7 in: rows 16m + 2G, 16m + 2G + 1 of the wave's 64, for m = 0..3
-    const reshard_segment_t& seg = src_segs[lane & 7u];
-    const uintptr_t g = sh.ptr(seg.ptr) + uint64_t(seg.offset) + uint64_t(r0) * 8u;
-#pragma unroll
-    for (int mm = 0; mm < 4; ++mm) {
-      const uint32_t r = w0 + 16u * uint32_t(mm) + 2u * G;
-      u32x4 x = u32x4{0, 0, 0, 0};
-      if (r + 2 <= hr) {
-        x = load_16_unaligned(g + uint64_t(r) * 8u);
-      } else if (r < hr) {
-        const uint64_t y = __builtin_nontemporal_load(as_global<const u64_u>(g + uint64_t(r) * 8u));
-        x = u32x4{uint32_t(y), uint32_t(y >> 32), 0, 0};
-      }
-      m[2 * mm] = x.x; m[2 * mm + 1] = x.y; m[8 + 2 * mm] = x.z; m[8 + 2 * mm + 1] = x.w;
-    }
-    m = quarters_transpose(lanes_transpose8x64(m));
-  }
-  for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {
-    if constexpr (!src_runs) {  // run lane & 7 out
-      const uintptr_t g = f == 0 ? gd0 : sh.ptr(refs[dseg.ptr + f]) + uint64_t(dseg.offset) + uint64_t(r0) * 8u;
-#pragma unroll
-      for (int mm = 0; mm < 4; ++mm) {
-        const uint32_t r = w0 + 16u * uint32_t(mm) + 2u * G;
-        const u32x4 x = u32x4{m[2 * mm], m[2 * mm + 1], m[8 + 2 * mm], m[8 + 2 * mm + 1]};
-        if (r + 2 <= hr) store_bytes(g + uint64_t(r) * 8u, x, 16);
-        else if (r < hr) store_bytes(g + uint64_t(r) * 8u, x, 8);
-      }
-    } else {  // whole rows out
-      const uintptr_t g =
-          sh.ptr(refs[dst_segs[0].ptr + f]) + uint64_t(dst_segs[0].offset) + uint64_t(r0) * 64u + 16u * b;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t r = w0 + 16u * uint32_t(q) + a;
-        if (r < hr) store_bytes(g + uint64_t(r) * 64u, u32x4{m[4 * q], m[4 * q + 1], m[4 * q + 2], m[4 * q + 3]}, 16);
-      }
-    }
-  }
-}
-
-template <class Sh>
-__device__ __forceinline__ void window_runs64(const reshard_descriptor_t& D,
-                                              const reshard_segment_t* __restrict__ segs,
-                                              const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
-  const uint32_t rows = D.extent[0], per_tile = D.extent[1];  // 256 rows per tile
-  const uint32_t r0 = tile * per_tile;
-  const uint32_t hr = min(per_tile, rows - r0);
-  const reshard_segment_t* src_segs = segs + D.src_ptr;
-  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
-  if (D.dst_ref_begin == 8)  // else one segment of whole rows (and eight runs out)
-    window_runs64_sides<true>(src_segs, dst_segs, refs, sh, r0, hr);
-  else
-    window_runs64_sides<false>(src_segs, dst_segs, refs, sh, r0, hr);
-}
-
-// A window band 32 to 256 bytes wide (a multiple of 16) whose sides are each n
-// packed segments of one width, a multiple of 16 bytes (whole rows, or the
-// equal column shards of a split), in column order: every 16-byte chunk of a
-// row lies in one segment on each side, so the band moves as 16-byte chunks
-// with no LDS and no exchange.  With cpr chunks per row, lane L < rps * cpr
-// (rps = 256 / cpr rows per step, rounded down) takes chunk column L % cpr of
-// row k * rps + L / cpr at step k: a wave's accesses are contiguous in every
-// packed segment, and each lane resolves its two segment addresses once.  A
-// tile is kWindowBytes / w rows: four steps, five when cpr is not a power of
-// two.
-template <class Sh>
-__device__ __forceinline__ void window_chunks16(const reshard_descriptor_t& D,
-                                                const reshard_segment_t* __restrict__ segs,
-                                                const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
-  const uint32_t w = D.run_bytes, rows = D.extent[0], per_tile = D.extent[1];
-  const uint32_t r0 = tile * per_tile;
-  const uint32_t hr = min(per_tile, rows - r0);
-  const reshard_segment_t* src_segs = segs + D.src_ptr;
-  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
-  const uint32_t cpr = w >> 4, rps = uint32_t(kBlock) / cpr;
-  const uint32_t c = threadIdx.x % cpr, q = threadIdx.x / cpr;  // q >= rps: an idle lane
-  const uint32_t ws = w / D.dst_ref_begin, wd = w / D.fanout;  // segment widths
-  const reshard_segment_t& ss = src_segs[16u * c / ws];
-  const reshard_segment_t& sd = dst_segs[16u * c / wd];
-  const uintptr_t gs = sh.ptr(ss.ptr) + uint64_t(ss.offset) + (16u * c - ss.col) + uint64_t(r0) * ws;
-  u32x4 v[5];
-#pragma unroll
-  for (int k = 0; k < 4; ++k)  // unconditional: rows past the tile re-read its last row, never stored
-    v[k] = load_16_unaligned(gs + uint64_t(min(uint32_t(k) * rps + q, hr - 1)) * ws);
-  v[4] = u32x4{0, 0, 0, 0};
-  if (4u * rps < hr)  // uniform: a fifth step (chunks per row not a power of two)
-    v[4] = load_16_unaligned(gs + uint64_t(min(4u * rps + q, hr - 1)) * ws);
-  for (uint32_t f = 0; f < sd.fanout; ++f) {
-    const uintptr_t gd = sh.ptr(refs[sd.ptr + f]) + uint64_t(sd.offset) + (16u * c - sd.col) + uint64_t(r0) * wd;
-#pragma unroll
-    for (int k = 0; k < 5; ++k) {
-      const uint32_t r = uint32_t(k) * rps + q;
-      if (q < rps && r < hr) store_bytes(gd + uint64_t(r) * wd, v[k], 16);
-    }
-  }
-}
-
-// A 32-byte window band whose one side is four packed 8-byte column runs (four
-// bf16 or two fp32 columns per shard over four shards) and whose other side is
-// one packed run of whole rows.  No LDS: a tile is 512 rows, 128 per wave, and
-// every 16-byte access of a wave is contiguous on both sides.
-//  - whole-row side: slice q (0..3) of lane L = 2a + b is half b of row
-//    32 q + a of the wave's 128 (one 1 KiB piece per slice);
-//  - run side: lane L = 4g + j holds run j at rows 64 p + 2g, + 1 (piece A) and
-//    64 p + 32 + 2g, + 1 (piece B) for p = 0, 1; the sixteen lanes that hold
-//    run j cover its rows 64 p .. 64 p + 31 (or + 32 .. + 63) in one access.
-// Between the two: slices 2p and 2p + 1 (words 8p .. 8p + 7) become whole rows
-// by one exchange between lanes 1 apart (lane 2a + b: row 64 p + 32 b + a), then
-// a 4 x 4 transpose of 8-byte elements across each quad (lane offset o = 2e + b
-// holds row 64 p + 32 b + 2g + e) leaves lane j with run j at those rows, so
-// piece A is elements 0 and 2, piece B elements 1 and 3.
-template <int P, int I = 0>
-__device__ __forceinline__ u32x16 swap_halves16(u32x16 m) {
-  if constexpr (I < 4) {
-    const bool h = (threadIdx.x & 1u) != 0;
-    constexpr int A = 8 * P + I, B = 8 * P + 4 + I;
-    const uint32_t a = m[A], b = m[B];
-    const uint32_t got = lane_xor<1>(h ? a : b);
-    m[A] = h ? got : a;
-    m[B] = h ? b : got;
-    return swap_halves16<P, I + 1>(m);
-  } else {
-    return m;
-  }
-}
-// Stage X (1 or 2) of the 4 x 4 transpose of 8-byte elements k = 0..3 at words
-// 8P + 2k, 8P + 2k + 1 across the quad.
-template <int P, int X, int K = 0>
-__device__ __forceinline__ u32x16 quad_stage64(u32x16 m) {
-  if constexpr (K < 4) {
-    if constexpr ((K & X) == 0) {
-      const bool hi = (threadIdx.x & uint32_t(X)) != 0;
-      constexpr int A = 8 * P + 2 * K, B = 8 * P + 2 * (K ^ X);
-      const uint32_t lo0 = m[A], lo1 = m[A + 1], up0 = m[B], up1 = m[B + 1];
-      const uint32_t got0 = lane_xor<X>(hi ? lo0 : up0), got1 = lane_xor<X>(hi ? lo1 : up1);
-      m[A] = hi ? got0 : lo0;
-      m[A + 1] = hi ? got1 : lo1;
-      m[B] = hi ? up0 : got0;
-      m[B + 1] = hi ? up1 : got1;
-    }
-    return quad_stage64<P, X, K + 1>(m);
-  } else {
-    return m;
-  }
-}
-template <int P>
-__device__ __forceinline__ u32x16 quad_transpose64(u32x16 m) {
-  return quad_stage64<P, 2>(quad_stage64<P, 1>(m));
-}
-
-template <bool src_runs, class Sh>
-__device__ __forceinline__ void window_runs32_sides(const reshard_segment_t* __restrict__ src_segs,
-                                                    const reshard_segment_t* __restrict__ dst_segs,
-                                                    const uint32_t* __restrict__ refs, const Sh& sh,
-                                                    uint32_t r0, uint32_t hr) {
-  const uint32_t lane = threadIdx.x & 63u, w0 = (threadIdx.x >> 6) * 128u;  // the wave's first tile row
-  const uint32_t a = lane >> 1, b = lane & 1u, g = lane >> 2;
-  u32x16 m;
-  if constexpr (!src_runs) {  // whole rows in: slice q of lane 2a + b is half b of row 32q + a
-    const uintptr_t gr = sh.ptr(src_segs[0].ptr) + uint64_t(src_segs[0].offset) + uint64_t(r0) * 32u + 16u * b;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t r = w0 + 32u * uint32_t(q) + a;
-      const u32x4 x = load_16_unaligned(gr + uint64_t(min(r, hr - 1)) * 32u);  // past hr: never stored
-      m[4 * q] = x.x; m[4 * q + 1] = x.y; m[4 * q + 2] = x.z; m[4 * q + 3] = x.w;
-    }
-    m = quad_transpose64<1>(quad_transpose64<0>(swap_halves16<1>(swap_halves16<0>(m))));
-  } else {  // run lane & 3 in: pieces A and B of sets p = 0, 1
-    const reshard_segment_t& seg = src_segs[lane & 3u];
-    const uintptr_t gr = sh.ptr(seg.ptr) + uint64_t(seg.offset) + uint64_t(r0) * 8u;
-#pragma unroll
-    for (int pc = 0; pc < 4; ++pc) {  // pc = 2p + piece
-      const uint32_t r = w0 + 64u * uint32_t(pc >> 1) + 32u * uint32_t(pc & 1) + 2u * g;
-      u32x4 x = u32x4{0, 0, 0, 0};
-      if (r + 2 <= hr) {
-        x = load_16_unaligned(gr + uint64_t(r) * 8u);
-      } else if (r < hr) {
-        const uint64_t y = __builtin_nontemporal_load(as_global<const u64_u>(gr + uint64_t(r) * 8u));
-        x = u32x4{uint32_t(y), uint32_t(y >> 32), 0, 0};
-      }
-      // piece A: elements 0 and 2; piece B: elements 1 and 3 (of set p)
-      const int e0 = 8 * (pc >> 1) + 2 * (pc & 1), e1 = e0 + 4;
-      m[e0] = x.x; m[e0 + 1] = x.y; m[e1] = x.z; m[e1 + 1] = x.w;
-    }
-    m = swap_halves16<1>(swap_halves16<0>(quad_transpose64<1>(quad_transpose64<0>(m))));
-  }
-  for (uint32_t f = 0; f < dst_segs[0].fanout; ++f) {
-    if constexpr (!src_runs) {  // run lane & 3 out
-      const reshard_segment_t& seg = dst_segs[lane & 3u];
-      const uintptr_t gr = sh.ptr(refs[seg.ptr + f]) + uint64_t(seg.offset) + uint64_t(r0) * 8u;
-#pragma unroll
-      for (int pc = 0; pc < 4; ++pc) {
-        const uint32_t r = w0 + 64u * uint32_t(pc >> 1) + 32u * uint32_t(pc & 1) + 2u * g;
-        const int e0 = 8 * (pc >> 1) + 2 * (pc & 1), e1 = e0 + 4;
-        const u32x4 x = u32x4{m[e0], m[e0 + 1], m[e1], m[e1 + 1]};
-        if (r + 2 <= hr) store_bytes(gr + uint64_t(r) * 8u, x, 16);
-        else if (r < hr) store_bytes(gr + uint64_t(r) * 8u, x, 8);
-      }
-    } else {  // whole rows out
-      const uintptr_t gr =
-          sh.ptr(refs[dst_segs[0].ptr + f]) + uint64_t(dst_segs[0].offset) + uint64_t(r0) * 32u + 16u * b;
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint32_t r = w0 + 32u * uint32_t(q) + a;
-        if (r < hr) store_bytes(gr + uint64_t(r) * 32u, u32x4{m[4 * q], m[4 * q + 1], m[4 * q + 2], m[4 * q + 3]}, 16);
-      }
-    }
-  }
-}
-
-template <class Sh>
-__device__ __forceinline__ void window_runs32(const reshard_descriptor_t& D,
-                                              const reshard_segment_t* __restrict__ segs,
-                                              const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile) {
-  const uint32_t rows = D.extent[0], per_tile = D.extent[1];  // 512 rows per tile
-  const uint32_t r0 = tile * per_tile;
-  const uint32_t hr = min(per_tile, rows - r0);
-  const reshard_segment_t* src_segs = segs + D.src_ptr;
-  const reshard_segment_t* dst_segs = src_segs + D.dst_ref_begin;
-  if (D.dst_ref_begin == 4)  // else one segment of whole rows (and four runs out)
-    window_runs32_sides<true>(src_segs, dst_segs, refs, sh, r0, hr);
-  else
-    window_runs32_sides<false>(src_segs, dst_segs, refs, sh, r0, hr);
 }
 
 // A 16-byte window band whose one side is eight packed 2-byte column runs (one
@@ -1859,14 +1377,6 @@ enum KernelKind : int {
   kKindAll = 3,      // any mode, LDS window included
   kKindQuadRows = 4, // every descriptor a 16-byte row-mode band with the quad exchange
                      // (kQuadRowsPerLane rows per lane): no LDS, fewer registers
-  kKindRuns = 5,     // every descriptor a 32-byte window band of 4-byte column runs
-                     // (window_runs8): no LDS
-  kKindRuns64 = 6,   // every descriptor a 64-byte window band of 8-byte column runs
-                     // (window_runs64): no LDS
-  kKindBands16 = 7,  // every descriptor a window band of 16-byte-aligned packed
-                     // segments (window_chunks16): no LDS
-  kKindRuns32 = 8,   // every descriptor a 32-byte window band of four 8-byte column
-                     // runs (window_runs32): no LDS
   kKindOctets = 9,   // every descriptor a 16-byte window band of eight 2-byte column
                      // runs (window_octets): no LDS
   kKindGatherRows = 10,  // every descriptor RESHARD_DESC_GATHER_ROWS (gather_rows)
@@ -1932,9 +1442,7 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t unit = kKind == kKindItems16 ? 16u : unit_mode & 0xffffu;
   const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
                         : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
-                        : kKind == kKindQuadRows || kKind == kKindRuns || kKind == kKindRuns64 ||
-                                  kKind == kKindBands16 || kKind == kKindRuns32 || kKind == kKindOctets ||
-                                  kKind == kKindDwords
+                        : kKind == kKindQuadRows || kKind == kKindOctets || kKind == kKindDwords
                             ? uint32_t(RESHARD_DESC_WINDOW)
                         : kKind == kKindGatherRows ? uint32_t(RESHARD_DESC_GATHER_ROWS)
                         : kKind == kKindReduce ? uint32_t(RESHARD_DESC_REDUCE)
@@ -1942,26 +1450,6 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   if constexpr (kKind == kKindQuadRows) {
     const Shards<kKarg> wsh{table, &karg, refs};
     window_rows<int(rs::kQuadRowsPerLane)>(D, segs, refs, wsh, t - tile_begin[lo]);
-    return;
-  }
-  if constexpr (kKind == kKindRuns) {
-    const Shards<kKarg> wsh{table, &karg, refs};
-    window_runs8(D, segs, refs, wsh, t - tile_begin[lo]);
-    return;
-  }
-  if constexpr (kKind == kKindRuns64) {
-    const Shards<kKarg> wsh{table, &karg, refs};
-    window_runs64(D, segs, refs, wsh, t - tile_begin[lo]);
-    return;
-  }
-  if constexpr (kKind == kKindBands16) {
-    const Shards<kKarg> wsh{table, &karg, refs};
-    window_chunks16(D, segs, refs, wsh, t - tile_begin[lo]);
-    return;
-  }
-  if constexpr (kKind == kKindRuns32) {
-    const Shards<kKarg> wsh{table, &karg, refs};
-    window_runs32(D, segs, refs, wsh, t - tile_begin[lo]);
     return;
   }
   if constexpr (kKind == kKindGatherRows) {
@@ -2098,14 +1586,6 @@ hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_des
       return RS_LAUNCH(kKindCopy);
     case kKindQuadRows:
       return RS_LAUNCH(kKindQuadRows);
-    case kKindRuns:
-      return RS_LAUNCH(kKindRuns);
-    case kKindRuns64:
-      return RS_LAUNCH(kKindRuns64);
-    case kKindBands16:
-      return RS_LAUNCH(kKindBands16);
-    case kKindRuns32:
-      return RS_LAUNCH(kKindRuns32);
     case kKindOctets:
       return RS_LAUNCH(kKindOctets);
     case kKindGatherRows:
@@ -2124,39 +1604,6 @@ hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_des
 
 namespace {
 
-// Whether a descriptor is a band window_runs8 moves: 32 bytes wide, tiles of
-// the window's rows, one side eight packed 4-byte runs, the other eight runs or
-// one packed run of whole rows (the same tests the kernel makes).  (Sixteen
-// lanes for 64-byte bands would need 71 VGPRs: one wave per SIMD fewer.)
-bool runs_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
-  const uint32_t w = D.run_bytes;
-  if (D.mode != RESHARD_DESC_WINDOW || w != 32 || D.extent[1] != kWindowBytes / w) return false;
-  const reshard_segment_t* S = segs.data() + D.src_ptr;
-  const reshard_segment_t* T = S + D.dst_ref_begin;
-  const bool src_runs = runs_side(S, D.dst_ref_begin, 8, 4), dst_runs = runs_side(T, D.fanout, 8, 4);
-  return (src_runs || full_side(S, D.dst_ref_begin, w)) && (dst_runs || full_side(T, D.fanout, w)) &&
-         (src_runs || dst_runs);
-}
-
-// Whether a descriptor is a band window_chunks16 moves: 32 to 256 bytes wide (a
-// multiple of 16), tiles of kWindowBytes / w rows, each side n packed segments
-// of one width, a multiple of 16, in column order, with one fan-out.
-bool chunks16_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
-  const uint32_t w = D.run_bytes;
-  if (D.mode != RESHARD_DESC_WINDOW || w < 32 || w > 256 || w % 16 != 0 || D.extent[1] != kWindowBytes / w)
-    return false;
-  auto side = [&](const reshard_segment_t* S, uint32_t n) {
-    if (n == 0 || w % n != 0 || (w / n) % 16 != 0) return false;
-    for (uint32_t s = 0; s < n; ++s)
-      if (S[s].width != w / n || uint64_t(S[s].row_stride) != w / n || S[s].col != s * (w / n) ||
-          S[s].fanout != S[0].fanout)
-        return false;
-    return true;
-  };
-  const reshard_segment_t* S = segs.data() + D.src_ptr;
-  return side(S, D.dst_ref_begin) && side(S + D.dst_ref_begin, D.fanout);
-}
-
 // Whether a descriptor is a band window_octets moves: 16 bytes wide, tiles of
 // kQuadRowsPerLane * kBlock rows, one side eight 2-byte runs in column order,
 // the other one packed run of whole rows.
@@ -2167,30 +1614,6 @@ bool octets_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
   const reshard_segment_t* S = segs.data() + D.src_ptr;
   const reshard_segment_t* T = S + D.dst_ref_begin;
   const bool src_runs = runs_side(S, D.dst_ref_begin, 8, 2), dst_runs = runs_side(T, D.fanout, 8, 2);
-  return (src_runs && full_side(T, D.fanout, w)) || (dst_runs && full_side(S, D.dst_ref_begin, w));
-}
-
-// Whether a descriptor is a band window_runs32 moves: 32 bytes wide, tiles of
-// kWindowBytes / 32 rows, one side four 8-byte runs in column order, the other
-// one packed run of whole rows.
-bool runs32_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
-  const uint32_t w = D.run_bytes;
-  if (D.mode != RESHARD_DESC_WINDOW || w != 32 || D.extent[1] != kWindowBytes / w) return false;
-  const reshard_segment_t* S = segs.data() + D.src_ptr;
-  const reshard_segment_t* T = S + D.dst_ref_begin;
-  const bool src_runs = runs_side(S, D.dst_ref_begin, 4, 8), dst_runs = runs_side(T, D.fanout, 4, 8);
-  return (src_runs && full_side(T, D.fanout, w)) || (dst_runs && full_side(S, D.dst_ref_begin, w));
-}
-
-// Whether a descriptor is a band window_runs64 moves: 64 bytes wide, tiles of
-// kWindowBytes / 64 rows, one side eight 8-byte runs in column order, the
-// other one packed run of whole rows.
-bool runs64_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
-  const uint32_t w = D.run_bytes;
-  if (D.mode != RESHARD_DESC_WINDOW || w != 64 || D.extent[1] != kWindowBytes / w) return false;
-  const reshard_segment_t* S = segs.data() + D.src_ptr;
-  const reshard_segment_t* T = S + D.dst_ref_begin;
-  const bool src_runs = runs_side(S, D.dst_ref_begin, 8, 8), dst_runs = runs_side(T, D.fanout, 8, 8);
   return (src_runs && full_side(T, D.fanout, w)) || (dst_runs && full_side(S, D.dst_ref_begin, w));
 }
 
@@ -2217,8 +1640,7 @@ int kernel_kind_dwords() { return kKindDwords; }
 
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
-  bool items16 = true, chunks = true, quad_rows = true, runs = true, runs64 = true, bands16 = true, runs32 = true;
-  bool octets = true, gather = true, reduce = true, dwords = true;
+  bool items16 = true, chunks = true, quad_rows = true, octets = true, gather = true, reduce = true, dwords = true;
   bool window = false;
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
@@ -2226,10 +1648,6 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
     if (D.mode != RESHARD_DESC_WINDOW || D.run_bytes > uint32_t(rs::kRowModeBytes) ||
         D.extent[1] != rs::kQuadRowsPerLane * uint32_t(kBlock))
       quad_rows = false;
-    if (!runs_band(D, segs)) runs = false;
-    if (!runs64_band(D, segs)) runs64 = false;
-    if (!chunks16_band(D, segs)) bands16 = false;
-    if (!runs32_band(D, segs)) runs32 = false;
     if (!octets_band(D, segs)) octets = false;
     if (D.mode != RESHARD_DESC_GATHER_ROWS) gather = false;
     if (D.mode != RESHARD_DESC_REDUCE) reduce = false;
@@ -2239,9 +1657,7 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
   if (gather && !descs.empty()) return kKindGatherRows;
   if (reduce && !descs.empty()) return kKindReduce;
   return items16 ? kKindItems16 : chunks ? kKindChunks : octets ? kKindOctets : quad_rows ? kKindQuadRows
-         : runs ? kKindRuns
-         : runs64 ? kKindRuns64 : bands16 ? kKindBands16 : runs32 ? kKindRuns32 : dwords ? kKindDwords
-         : window ? kKindAll : kKindCopy;
+         : dwords ? kKindDwords : window ? kKindAll : kKindCopy;
 }
 
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,

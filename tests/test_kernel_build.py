@@ -46,11 +46,10 @@ def kernel_meta(tmp_path_factory):
 
 def test_every_variant_is_compiled(kernel_meta):
     names = [n for n in kernel_meta if "reshard_copy_kernel" in n]
-    # two pointer placements x fourteen variants (16-byte items, destination
-    # chunks, aligned destination chunks, copy modes, quad row bands, 2-byte-run
-    # bands, 4-byte-run bands, 8-byte-run bands in 64- and 32-byte rows, 16-byte
-    # chunk bands, gather-rows bands, Partial sums, dword bands, all modes)
-    assert len(names) == 28, sorted(kernel_meta)
+    # two pointer placements x ten variants (16-byte items, destination chunks,
+    # aligned destination chunks, copy modes, quad row bands, 2-byte-run bands,
+    # gather-rows bands, Partial sums, dword bands, all modes)
+    assert len(names) == 20, sorted(kernel_meta)
 
 
 def test_no_scratch(kernel_meta):
