@@ -553,6 +553,42 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
     b.d.extent[2] = 1;
     b.d.piece = uint32_t(pc0);
     if (rb - ra > int64_t(kMaxItems)) return false;
+    // Tiles of a band end where its segments' lines end only if the band starts
+    // on the line grid: otherwise two tiles (often on different XCDs) write
+    // parts of each line a tile boundary cuts.  Take the head rows up to the
+    // row that puts the most segment starts on the grid (a destination counts
+    // twice: a line written in part costs more than one read twice) into a
+    // band of their own, when at least one full tile follows.
+    const int64_t tile = b.d.extent[1];
+    int64_t head = 0;
+    bool tiles_keep_grid = true;
+    for (const auto* side : {&b.src, &b.dst})
+      for (const auto& x : *side) tiles_keep_grid &= (tile * x.row_stride) % kLineBytes == 0;
+    if (tiles_keep_grid) {
+      auto score = [&](int64_t h) {
+        int64_t n = 0;
+        for (const auto& x : b.src) n += (x.offset + h * x.row_stride) % kLineBytes == 0;
+        for (const auto& x : b.dst) n += 2 * ((x.offset + h * x.row_stride) % kLineBytes == 0);
+        return n;
+      };
+      int64_t best = score(0);
+      for (int64_t h = 1; h < kLineBytes && h + tile <= rb - ra; ++h)
+        if (score(h) > best) best = score(h), head = h;
+    }
+    if (head > 0) {
+      Pending rest = b;
+      b.d.extent[0] = uint32_t(head);
+      rest.d.extent[0] = uint32_t(rb - ra - head);
+      for (auto* side : {&rest.src, &rest.dst})
+        for (auto& x : *side) x.offset += head * x.row_stride;
+      int64_t rest_bits = width;
+      for (const auto& x : rest.src) rest_bits |= x.offset | x.row_stride | x.col | x.width;
+      for (const auto& x : rest.dst) rest_bits |= x.offset | x.row_stride | x.col | x.width;
+      rest.d.unit = uint16_t(unit_for(rest_bits));
+      bands.push_back(std::move(b));
+      bands.push_back(std::move(rest));
+      continue;
+    }
     bands.push_back(std::move(b));
   }
   for (Pending& b : bands) {

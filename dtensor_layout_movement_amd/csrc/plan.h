@@ -130,6 +130,10 @@ constexpr int64_t kWindowMaxRun = 128;
 constexpr int64_t kRowModeBytes = 16;
 constexpr uint32_t kRowsPerLane = 4;
 constexpr uint32_t kQuadRowsPerLane = 2;
+// Cache line of the L2: a band whose tiles would start off the line grid in
+// its segments gives up to kLineBytes / row_stride rows to a head band of its
+// own, so that the tiles after it start on the grid (destination lines first).
+constexpr int64_t kLineBytes = 128;
 
 // Whether the segments of one side of a 16-byte band are four packed 4-byte
 // column runs with one fan-out (the kernel's quad exchange applies).
