@@ -31,11 +31,11 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
 // The kernel variant that moves RESHARD_DESC_GATHER_ROWS bands.
 int kernel_kind_gather_rows();
 
-// The kernel variant that moves dword bands (packed WINDOW bands at dword
-// granularity).  In the device table, a destination segment of a band in a
-// launch of this variant holds, in row_stride, the absolute pointer slot of
-// its first replica (the band is packed: its row stride is its width).
-int kernel_kind_dwords();
+// Whether a kernel variant is one that moves narrow bands (packed WINDOW bands
+// more than 16 bytes wide).  In the device table, a destination segment of a
+// band in a launch of such a variant holds, in row_stride, the absolute pointer
+// slot of its first replica (the band is packed: its row stride is its width).
+bool kernel_kind_narrow(int kind);
 
 // Workgroups of one launch at most: a dispatch counts its work-items in 32
 // bits.  A multiple of kXcds, so that every launch starts on XCD 0's turn.

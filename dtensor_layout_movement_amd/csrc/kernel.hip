@@ -462,17 +462,79 @@ __device__ __forceinline__ void window_tile(const reshard_descriptor_t& D, const
   }
 }
 
-// Dword bands: a WINDOW band more than 16 bytes wide whose segments all hold
-// their rows back to back (row stride = width) at dword granularity (column,
-// width and offset multiples of 4 bytes).  Every side is then a contiguous
-// stream of dwords, and one lane moves one dword: a segment's stream dword j is
-// row j / w, dword j % w of the segment (w its width in dwords).  The window
-// keeps rows at an odd pitch of dwords, so lanes that touch one column of
-// consecutive rows, or consecutive dwords of one row, hit distinct LDS banks;
-// its rows per tile are the LDS window's, and kDwordWindowWords bounds the
-// window (checked on the host).
-constexpr uint32_t kDwordWindowWords = 4608;  // 18 KiB
-constexpr int kDwordBatch = 4;                 // dwords per lane with loads in flight together
+// n <= 16 bytes from global address a into bytes [0, n) of the result (any
+// alignment: gfx950 global accesses need none).  Streaming (non-temporal).
+__device__ __forceinline__ u32x4 load_bytes(uintptr_t a, uint32_t n) {
+  if (n == 16) return load_16_unaligned(a);
+  uint64_t lo = 0, hi = 0;
+  uint32_t at = 0;
+  if (n & 8) {
+    lo = __builtin_nontemporal_load(as_global<const u64_u>(a));
+    at = 8;
+  }
+  if (n & 4) {
+    const uint64_t x = __builtin_nontemporal_load(as_global<const u32_u>(a + at));
+    if (at < 8) lo |= x << (8 * at); else hi |= x;
+    at += 4;
+  }
+  if (n & 2) {
+    const uint64_t x = *as_global<const u16_u>(a + at);
+    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
+    at += 2;
+  }
+  if (n & 1) {
+    const uint64_t x = *as_global<const uint8_t>(a + at);
+    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
+  }
+  return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
+}
+
+// Bytes [0, n) of v (n <= 16) to global address d, streaming stores for the
+// whole-word widths, at most four stores otherwise.
+__device__ __forceinline__ void store_bytes(uintptr_t d, u32x4 v, uint32_t n) {
+  if (n == 16) __builtin_nontemporal_store(v, as_global<u32x4_u>(d));
+  else if (n == 8) __builtin_nontemporal_store((uint64_t(v.y) << 32) | v.x, as_global<u64_u>(d));
+  else if (n == 4) __builtin_nontemporal_store(v.x, as_global<u32_u>(d));
+  else store_head_bytes(d, v, n);
+}
+
+// Narrow bands: a WINDOW band more than 16 bytes wide whose segments all hold
+// their rows back to back in their shards (row stride = width).  Every side is
+// then a contiguous stream of bytes: stream byte j of a segment w bytes wide is
+// row j / w, byte j % w of the segment.  The window keeps rows at a pitch of P
+// bytes: an odd number of dwords when the band width W is a multiple of 4 (lanes
+// that touch one column of consecutive rows, or consecutive dwords of one row,
+// then hit distinct LDS banks), W otherwise (a segment of whole rows is then the
+// window itself).  Its rows per tile are the LDS window's, and
+// kNarrowWindowBytes bounds the window (checked on the host).  Each segment
+// moves in one of four ways:
+//   dwords  P, column and width multiples of 4: a lane moves one dword of the
+//           stream, or four where they stay together in the window;
+//   whole   the whole row, P = W: 16-byte pieces of the stream are 16-byte
+//           pieces of the window;
+//   rows    at most 16 bytes wide: a lane moves one row;
+//   pieces  wider: a lane moves a 16-byte piece of the stream, which meets at
+//           most two rows.
+constexpr uint32_t kNarrowWindowBytes = 18432;
+constexpr uint32_t kNarrowWindowWords = kNarrowWindowBytes / 4;
+constexpr int kNarrowBatch = 4;  // dword pieces per lane with loads in flight together
+constexpr int kBytesBatch = 2;   // other pieces
+constexpr uint32_t kSegDwords = 0, kSegWhole = 1, kSegRows = 2, kSegPieces = 3;
+
+__host__ __device__ __forceinline__ uint32_t narrow_pitch(uint32_t W) { return W % 4 ? W : 4 * ((W / 4) | 1u); }
+
+__host__ __device__ __forceinline__ uint32_t narrow_class(uint32_t wb, uint32_t cb, uint32_t P, uint32_t W) {
+  if (P % 4 == 0 && wb % 4 == 0 && cb % 4 == 0) return kSegDwords;
+  if (cb == 0 && wb == W && P == W) return kSegWhole;
+  return wb <= 16 ? kSegRows : kSegPieces;
+}
+
+// 2^32 / d rounded up, for div_small by d (its unit: dwords for a dword segment,
+// bytes otherwise); 0 for d = 1.
+__device__ __forceinline__ uint32_t narrow_magic(uint32_t wb, uint32_t cb, uint32_t P, uint32_t W) {
+  const uint32_t d = narrow_class(wb, cb, P, W) == kSegDwords ? wb / 4 : wb;
+  return d > 1 ? 0xffffffffu / d + 1u : 0u;
+}
 
 // n / w for n < 2^16 and 1 <= w < 2^16, with m = 2^32 / w rounded up (w > 1).
 __device__ __forceinline__ uint32_t div_small(uint32_t n, uint32_t w, uint32_t m) {
@@ -492,22 +554,154 @@ __device__ __forceinline__ uint64_t readlane64(uint64_t v, uint32_t lane) {
   return uint64_t(lo) | (uint64_t(hi) << 32);
 }
 
-// Phase 1 of a dword band for one source stream: loads into the window.
+// Lane `lane`'s value of v (a per-lane value; lane may differ between lanes).
+__device__ __forceinline__ uint32_t lane_value(uint32_t v, uint32_t lane) {
+  return uint32_t(__builtin_amdgcn_ds_bpermute(int(lane * 4), int(v)));
+}
+__device__ __forceinline__ uint64_t lane_value64(uint64_t v, uint32_t lane) {
+  return uint64_t(lane_value(uint32_t(v), lane)) | (uint64_t(lane_value(uint32_t(v >> 32), lane)) << 32);
+}
+
+// v rotated toward higher bytes by s (0 <= s < 16): byte i of the result is
+// byte (i - s) mod 16 of v.  Four selects a stage, s may differ between lanes.
+__device__ __forceinline__ u32x4 rotate_bytes(u32x4 v, uint32_t s) {
+  u32x4 t = u32x4{(v.x << 8) | (v.w >> 24), (v.y << 8) | (v.x >> 24), (v.z << 8) | (v.y >> 24),
+                  (v.w << 8) | (v.z >> 24)};
+  v = (s & 1) ? t : v;
+  t = u32x4{(v.x << 16) | (v.w >> 16), (v.y << 16) | (v.x >> 16), (v.z << 16) | (v.y >> 16), (v.w << 16) | (v.z >> 16)};
+  v = (s & 2) ? t : v;
+  t = u32x4{v.w, v.x, v.y, v.z};
+  v = (s & 4) ? t : v;
+  t = u32x4{v.z, v.w, v.x, v.y};
+  return (s & 8) ? t : v;
+}
+
+// A run of m thin segments (kWb = 1 or 2 bytes wide, columns cb0, cb0 + kWb,
+// ..., the same fan-out) of one side of a narrow band, for one tile of hr rows.
+// A lane moves 8 consecutive rows of one segment, 8 kWb contiguous bytes of
+// its stream, in one global access; the (segment, piece) pairs of the run are
+// spread over the whole workgroup, and a lane finds its segment's address in
+// the lane holding that segment (lane_addr: segment s in lane s).  The rows'
+// LDS accesses go in an order rotated per lane so that the lanes of one access
+// touch distinct banks (at 32 or 64 banks of 4 bytes and an odd dword pitch);
+// the piece's bytes are rotated to match.  Rows past the last whole piece go
+// one row a lane.  kIn: source side (stream -> window), else destination side
+// (window -> stream, to every replica).
+template <uint32_t kWb, bool kIn, class Sh>
+__device__ __forceinline__ void thin_run(uint32_t s0, uint32_t m, uint32_t cb0, uint32_t fan, uint64_t lane_addr,
+                                         uint64_t lane_off, uint32_t lane_ref, const uint32_t* __restrict__ refs,
+                                         const Sh& sh, uint32_t hr, uint32_t P, uint8_t* lds) {
+  constexpr uint32_t k = 8, kBytes = 8 * kWb;  // rows and bytes per piece
+  const uint32_t nq = hr / k, tail = hr - nq * k;
+  const uint32_t lane = threadIdx.x & 63u;
+  const uint32_t wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x - lane);  // the wave's first thread
+  const uint32_t rot = ((lane >> 2) ^ (lane >> 5)) & (k - 1);
+  const uint32_t mq = nq > 1 ? 0xffffffffu / nq + 1u : 0u;
+  // The trip counts are the same for every lane of a wave, and a lane past the
+  // last item repeats it: every lane takes part in the lane lookups, whose
+  // source lane must be active.
+  const uint32_t items = m * nq;
+  for (uint32_t base = wave0; base < items; base += kBlock) {
+    const uint32_t i = base + lane, ic = min(i, items - 1);
+    const uint32_t seg = nq == 1 ? ic : div_small(ic, nq, mq), q = ic - seg * nq;
+    const uint64_t g = lane_value64(lane_addr, s0 + seg) + kBytes * uint64_t(q);
+    const uint64_t o = !kIn && fan > 1 ? lane_value64(lane_off, s0 + seg) + kBytes * uint64_t(q) : 0u;
+    const uint32_t ref = !kIn && fan > 1 ? lane_value(lane_ref, s0 + seg) : 0u;
+    if (i >= items) continue;
+    uint8_t* p = lds + q * k * P + cb0 + seg * kWb;
+    if constexpr (kIn) {
+      // slot j of the rotated piece is row (j + rot) mod 8
+      uint32_t w[4];
+      if constexpr (kWb == 2) {
+        const u32x4 v = rotate_bytes(load_16_unaligned(g), (16 - 2 * rot) & 15u);
+        w[0] = v.x, w[1] = v.y, w[2] = v.z, w[3] = v.w;
+      } else {
+        const uint64_t x = __builtin_nontemporal_load(as_global<const u64_u>(g));
+        const uint64_t y = rot ? (x >> (8 * rot)) | (x << (64 - 8 * rot)) : x;
+        w[0] = uint32_t(y), w[1] = uint32_t(y >> 32);
+      }
+#pragma unroll
+      for (uint32_t j = 0; j < k; ++j) {
+        uint8_t* at = p + ((j + rot) & (k - 1)) * P;
+        if constexpr (kWb == 2) *reinterpret_cast<u16_u*>(at) = uint16_t(w[j / 2] >> (16 * (j % 2)));
+        else *at = uint8_t(w[j / 4] >> (8 * (j % 4)));
+      }
+    } else {
+      uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+      for (uint32_t j = 0; j < k; ++j) {
+        const uint8_t* at = p + ((j + rot) & (k - 1)) * P;
+        if constexpr (kWb == 2) w[j / 2] |= uint32_t(*reinterpret_cast<const u16_u*>(at)) << (16 * (j % 2));
+        else w[j / 4] |= uint32_t(*at) << (8 * (j % 4));
+      }
+      if constexpr (kWb == 2) {
+        const u32x4 v = rotate_bytes(u32x4{w[0], w[1], w[2], w[3]}, 2 * rot);
+        __builtin_nontemporal_store(v, as_global<u32x4_u>(g));
+        for (uint32_t f = 1; f < fan; ++f) __builtin_nontemporal_store(v, as_global<u32x4_u>(sh.ptr(refs[ref + f]) + o));
+      } else {
+        const uint64_t x = uint64_t(w[0]) | (uint64_t(w[1]) << 32);
+        const uint64_t v = rot ? (x << (8 * rot)) | (x >> (64 - 8 * rot)) : x;
+        __builtin_nontemporal_store(v, as_global<u64_u>(g));
+        for (uint32_t f = 1; f < fan; ++f) __builtin_nontemporal_store(v, as_global<u64_u>(sh.ptr(refs[ref + f]) + o));
+      }
+    }
+  }
+  if (tail == 0) return;
+  const uint32_t mt = tail > 1 ? 0xffffffffu / tail + 1u : 0u;
+  const uint32_t tail_items = m * tail;
+  for (uint32_t base = wave0; base < tail_items; base += kBlock) {  // as above
+    const uint32_t i = base + lane, ic = min(i, tail_items - 1);
+    const uint32_t seg = div_small(ic, tail, mt), r = nq * k + (ic - seg * tail);
+    const uint64_t o = uint64_t(r) * kWb;
+    const uint64_t g = lane_value64(lane_addr, s0 + seg) + o;
+    const uint64_t off = kIn ? 0u : lane_value64(lane_off, s0 + seg) + o;
+    const uint32_t ref = kIn ? 0u : lane_value(lane_ref, s0 + seg);
+    if (i >= tail_items) continue;
+    uint8_t* p = lds + r * P + cb0 + seg * kWb;
+    if constexpr (kIn) {
+      if constexpr (kWb == 2) *reinterpret_cast<u16_u*>(p) = *as_global<const u16_u>(g);
+      else *p = *as_global<const uint8_t>(g);
+    } else {
+      const uint32_t x = kWb == 2 ? uint32_t(*reinterpret_cast<const u16_u*>(p)) : uint32_t(*p);
+      for (uint32_t f = 0; f < fan; ++f) {
+        const uintptr_t d = f == 0 ? g : sh.ptr(refs[ref + f]) + off;
+        if constexpr (kWb == 2) *as_global<u16_u>(d) = uint16_t(x);
+        else *as_global<uint8_t>(d) = uint8_t(x);
+      }
+    }
+  }
+}
+
+// The end of the run of thin segments that starts at segment s of one side
+// (lane t of wc / fan holding segment t's width | column << 16 and fan-out):
+// the following segments of the same width, the next columns, the same fan-out.
+__device__ __forceinline__ uint32_t thin_run_end(uint32_t s, uint32_t n, uint32_t wc, uint32_t fan) {
+  const uint32_t w0 = __builtin_amdgcn_readlane(wc, s);
+  const uint32_t wb = w0 & 0xffffu, f0 = __builtin_amdgcn_readlane(fan, s);
+  uint32_t e = s + 1;
+  while (e < n && __builtin_amdgcn_readlane(wc, e) == w0 + ((e - s) * wb << 16) &&
+         __builtin_amdgcn_readlane(fan, e) == f0)
+    ++e;
+  return e;
+}
+
+// Phase 1 of a narrow band for one dword source stream: loads into the window
+// (w, c and pitch in dwords).
 __device__ __forceinline__ void dword_stream_in(uintptr_t g, uint32_t w, uint32_t c, uint32_t m, uint32_t hr,
                                                 uint32_t pitch, uint32_t* lds) {
   const uint32_t n = hr * w;
   uint32_t done = 0;  // stream dwords moved as quads
   if (dword_quads(w, c, pitch)) {
     const uint32_t nq = n / 4;
-    for (uint32_t base = threadIdx.x; base < nq; base += kBlock * kDwordBatch) {
-      u32x4 v[kDwordBatch];
+    for (uint32_t base = threadIdx.x; base < nq; base += kBlock * kNarrowBatch) {
+      u32x4 v[kNarrowBatch];
 #pragma unroll
-      for (int k = 0; k < kDwordBatch; ++k) {
+      for (int k = 0; k < kNarrowBatch; ++k) {
         const uint32_t q = base + uint32_t(k) * kBlock;
         if (q < nq) v[k] = load_16_unaligned(g + 16 * uint64_t(q));
       }
 #pragma unroll
-      for (int k = 0; k < kDwordBatch; ++k) {
+      for (int k = 0; k < kNarrowBatch; ++k) {
         const uint32_t q = base + uint32_t(k) * kBlock;
         if (q >= nq) break;
         const uint32_t j = 4 * q, r = div_small(j, w, m);
@@ -516,15 +710,15 @@ __device__ __forceinline__ void dword_stream_in(uintptr_t g, uint32_t w, uint32_
     }
     done = 4 * nq;
   }
-  for (uint32_t base = done + threadIdx.x; base < n; base += kBlock * kDwordBatch) {
-    uint32_t v[kDwordBatch];
+  for (uint32_t base = done + threadIdx.x; base < n; base += kBlock * kNarrowBatch) {
+    uint32_t v[kNarrowBatch];
 #pragma unroll
-    for (int k = 0; k < kDwordBatch; ++k) {
+    for (int k = 0; k < kNarrowBatch; ++k) {
       const uint32_t j = base + uint32_t(k) * kBlock;
       if (j < n) v[k] = __builtin_nontemporal_load(as_global<const u32_u>(g + 4 * uint64_t(j)));
     }
 #pragma unroll
-    for (int k = 0; k < kDwordBatch; ++k) {
+    for (int k = 0; k < kNarrowBatch; ++k) {
       const uint32_t j = base + uint32_t(k) * kBlock;
       if (j >= n) break;
       const uint32_t r = div_small(j, w, m);
@@ -533,14 +727,101 @@ __device__ __forceinline__ void dword_stream_in(uintptr_t g, uint32_t w, uint32_
   }
 }
 
+// Phase 1 of a narrow band for one source stream of any other class (wb, cb
+// and P in bytes).
+__device__ __forceinline__ void bytes_stream_in(uintptr_t g, uint32_t wb, uint32_t cb, uint32_t m, uint32_t cls,
+                                                uint32_t hr, uint32_t P, uint8_t* lds) {
+  if (cls == kSegRows) {
+    for (uint32_t base = threadIdx.x; base < hr; base += kBlock * kBytesBatch) {
+      u32x4 v[kBytesBatch];
+#pragma unroll
+      for (int k = 0; k < kBytesBatch; ++k) {
+        const uint32_t r = base + uint32_t(k) * kBlock;
+        if (r < hr) v[k] = load_bytes(g + uint64_t(r) * wb, wb);
+      }
+#pragma unroll
+      for (int k = 0; k < kBytesBatch; ++k) {
+        const uint32_t r = base + uint32_t(k) * kBlock;
+        if (r >= hr) break;
+        lds_put(lds + r * P + cb, v[k], wb);
+      }
+    }
+    return;
+  }
+  const uint32_t nb = hr * wb;
+  for (uint32_t base = threadIdx.x; 16 * base < nb; base += kBlock * kBytesBatch) {
+    u32x4 v[kBytesBatch];
+#pragma unroll
+    for (int k = 0; k < kBytesBatch; ++k) {
+      const uint32_t j = 16 * (base + uint32_t(k) * kBlock);
+      if (j < nb) v[k] = load_bytes(g + j, min(16u, nb - j));
+    }
+#pragma unroll
+    for (int k = 0; k < kBytesBatch; ++k) {
+      const uint32_t j = 16 * (base + uint32_t(k) * kBlock);
+      if (j >= nb) break;
+      const uint32_t len = min(16u, nb - j);
+      if (cls == kSegWhole) {
+        lds_put(lds + j, v[k], len);
+        continue;
+      }
+      const uint32_t r = div_small(j, wb, m), col = j - r * wb;
+      const uint32_t l1 = min(len, wb - col);
+      lds_put(lds + r * P + cb + col, v[k], l1);
+      if (len > l1) lds_put(lds + (r + 1) * P + cb, shift_right_bytes(v[k], l1), len - l1);
+    }
+  }
+}
+
+// Phase 2 of a narrow band for one destination stream that is not a dword
+// stream: to g0 (first replica) and, at the same offset `off`, to the other
+// replicas of fan-out list refs[ref ..].
 template <class Sh>
-__device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
+__device__ __forceinline__ void bytes_stream_out(uintptr_t g0, uint64_t off, uint32_t ref, uint32_t fan,
+                                                 const uint32_t* __restrict__ refs, const Sh& sh, uint32_t wb,
+                                                 uint32_t cb, uint32_t m, uint32_t cls, uint32_t hr, uint32_t P,
+                                                 const uint8_t* lds) {
+  if (cls == kSegRows) {
+    for (uint32_t r = threadIdx.x; r < hr; r += kBlock) {
+      const u32x4 v = lds_get(lds + r * P + cb, wb);
+      const uint64_t o = uint64_t(r) * wb;
+      store_bytes(g0 + o, v, wb);
+      for (uint32_t f = 1; f < fan; ++f) store_bytes(sh.ptr(refs[ref + f]) + off + o, v, wb);
+    }
+    return;
+  }
+  const uint32_t nb = hr * wb;
+  for (uint32_t j = 16 * threadIdx.x; j < nb; j += 16 * kBlock) {
+    const uint32_t len = min(16u, nb - j);
+    u32x4 v;
+    if (cls == kSegWhole) {
+      v = lds_get(lds + j, len);
+    } else {
+      const uint32_t r = div_small(j, wb, m), col = j - r * wb;
+      const uint32_t l1 = min(len, wb - col);
+      v = lds_get(lds + r * P + cb + col, l1);
+      if (len > l1) {
+        const u32x4 x = shift_left_bytes(lds_get(lds + (r + 1) * P + cb, len - l1), l1);
+        v = u32x4{v.x | x.x, v.y | x.y, v.z | x.z, v.w | x.w};
+      }
+    }
+    store_bytes(g0 + j, v, len);
+    for (uint32_t f = 1; f < fan; ++f) store_bytes(sh.ptr(refs[ref + f]) + off + j, v, len);
+  }
+}
+
+// kBytes: the build for bands with segments of every class; without it, every
+// segment of every band is a dword segment (checked on the host), and only the
+// dword paths are compiled.
+template <bool kBytes, class Sh>
+__device__ __forceinline__ void window_narrow(const reshard_descriptor_t& D, const reshard_segment_t* __restrict__ segs,
                                               const uint32_t* __restrict__ refs, const Sh& sh, uint32_t tile,
                                               uint32_t* lds) {
   const uint32_t rows = D.extent[0], per_tile = D.extent[1];
   const uint32_t r0 = tile * per_tile;
   const uint32_t hr = min(per_tile, rows - r0);
-  const uint32_t pitch = (D.run_bytes / 4) | 1u;  // odd
+  const uint32_t W = D.run_bytes, P = narrow_pitch(W), pitch = P / 4;  // pitch: dwords, for dword segments
+  uint8_t* lds8 = reinterpret_cast<uint8_t*>(lds);
   const uint32_t ns = D.dst_ref_begin, nd = D.fanout;  // at most 64 each
   const reshard_segment_t* src_segs = segs + D.src_ptr;
   const reshard_segment_t* dst_segs = src_segs + ns;
@@ -552,49 +833,72 @@ __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, con
   const uint32_t lane = threadIdx.x & 63u;
   const reshard_segment_t SD = dst_segs[lane < nd ? lane : 0u];
 
-  // phase 1: source streams -> window; 16-byte accesses where four stream
-  // dwords stay together in the window, single dwords otherwise.  One source
-  // segment comes through the scalar cache; several, one per lane as above.
+  // phase 1: source streams -> window.  One source segment comes through the
+  // scalar cache; several, one per lane as above.
   if (ns == 1) {
     const reshard_segment_t S = src_segs[0];
-    const uint32_t w = S.width / 4;
-    dword_stream_in(sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.width), w, S.col / 4,
-                    w > 1 ? 0xffffffffu / w + 1u : 0u, hr, pitch, lds);
+    const uintptr_t g = sh.ptr(S.ptr) + uint64_t(S.offset) + uint64_t(r0) * uint64_t(S.width);
+    const uint32_t cls = narrow_class(S.width, S.col, P, W), m = narrow_magic(S.width, S.col, P, W);
+    if (!kBytes || cls == kSegDwords) dword_stream_in(g, S.width / 4, S.col / 4, m, hr, pitch, lds);
+    else bytes_stream_in(g, S.width, S.col, m, cls, hr, P, lds8);
   } else {
     const reshard_segment_t SS = src_segs[lane < ns ? lane : 0u];
-    const uint32_t s_wc = (SS.width / 4) | ((SS.col / 4) << 16);  // width | col << 16 (dwords)
-    const uint32_t s_m = 0xffffffffu / (SS.width / 4) + 1u;       // a width of one wraps to 0, unused
+    const uint32_t s_wc = SS.width | (SS.col << 16);  // width | col << 16 (bytes)
+    const uint32_t s_m = narrow_magic(SS.width, SS.col, P, W);
     const uint64_t s_addr = sh.ptr(SS.ptr) + uint64_t(SS.offset) + uint64_t(r0) * uint64_t(SS.width);
     for (uint32_t s = 0; s < ns; ++s) {
       const uint32_t wc = __builtin_amdgcn_readlane(s_wc, s);
-      dword_stream_in(readlane64(s_addr, s), wc & 0xffffu, wc >> 16, __builtin_amdgcn_readlane(s_m, s), hr, pitch,
-                      lds);
+      const uint32_t wb = wc & 0xffffu, cb = wc >> 16, cls = narrow_class(wb, cb, P, W);
+      if (kBytes && wb <= 2) {  // thin: a run of them together
+        const uint32_t e = thin_run_end(s, ns, s_wc, 0u);
+        if (wb == 2) thin_run<2, true>(s, e - s, cb, 1u, s_addr, 0u, 0u, refs, sh, hr, P, lds8);
+        else thin_run<1, true>(s, e - s, cb, 1u, s_addr, 0u, 0u, refs, sh, hr, P, lds8);
+        s = e - 1;
+        continue;
+      }
+      const uint32_t m = __builtin_amdgcn_readlane(s_m, s);
+      if (!kBytes || cls == kSegDwords) dword_stream_in(readlane64(s_addr, s), wb / 4, cb / 4, m, hr, pitch, lds);
+      else bytes_stream_in(readlane64(s_addr, s), wb, cb, m, cls, hr, P, lds8);
     }
   }
-  const uint32_t d_wc = (SD.width / 4) | ((SD.col / 4) << 16);
-  const uint32_t d_m = 0xffffffffu / (SD.width / 4) + 1u;
+  const uint32_t d_wc = SD.width | (SD.col << 16);  // bytes
+  const uint32_t d_m = narrow_magic(SD.width, SD.col, P, W);
   const uint64_t d_off = uint64_t(SD.offset) + uint64_t(r0) * uint64_t(SD.width);
   const uint32_t d_ref = SD.ptr, d_fan = SD.fanout;
   const uint64_t d_addr = sh.ptr(uint32_t(SD.row_stride)) + d_off;
   __syncthreads();
 
-  // phase 2: window -> destination streams, every replica.  A segment at most
-  // four dwords wide goes row by row, one row a lane: one LDS read of the
+  // phase 2: window -> destination streams, every replica.  A dword segment at
+  // most four dwords wide goes row by row, one row a lane: one LDS read of the
   // row's dwords and one store of them (the lanes' stores are consecutive in
   // the stream); wider ones in stream order like phase 1.
   for (uint32_t s = 0; s < nd; ++s) {
     const uint32_t wc = __builtin_amdgcn_readlane(d_wc, s);
-    const uint32_t w = wc & 0xffffu, c = wc >> 16, n = hr * w;
+    const uint32_t wb = wc & 0xffffu, cb = wc >> 16;
     const uintptr_t g0 = readlane64(d_addr, s);
     const uint32_t fan = __builtin_amdgcn_readlane(d_fan, s);
+    const uint32_t cls = narrow_class(wb, cb, P, W);
+    if (kBytes && wb <= 2) {  // thin: a run of them together
+      const uint32_t e = thin_run_end(s, nd, d_wc, d_fan);
+      if (wb == 2) thin_run<2, false>(s, e - s, cb, fan, d_addr, d_off, d_ref, refs, sh, hr, P, lds8);
+      else thin_run<1, false>(s, e - s, cb, fan, d_addr, d_off, d_ref, refs, sh, hr, P, lds8);
+      s = e - 1;
+      continue;
+    }
+    if (kBytes && cls != kSegDwords) {
+      bytes_stream_out(g0, readlane64(d_off, s), __builtin_amdgcn_readlane(d_ref, s), fan, refs, sh, wb, cb,
+                       __builtin_amdgcn_readlane(d_m, s), cls, hr, P, lds8);
+      continue;
+    }
+    const uint32_t w = wb / 4, c = cb / 4, n = hr * w;
     // four one-dword segments side by side (columns c .. c + 3, one replica
     // each): one LDS read of the four dwords a row, four stores
     if (w == 1 && fan == 1 && s + 3 < nd) {
       const uint32_t wc3 = __builtin_amdgcn_readlane(d_wc, s + 3);
       const uint32_t f1 = __builtin_amdgcn_readlane(d_fan, s + 1), f2 = __builtin_amdgcn_readlane(d_fan, s + 2),
                      f3 = __builtin_amdgcn_readlane(d_fan, s + 3);
-      if (wc3 == (1u | ((c + 3) << 16)) && __builtin_amdgcn_readlane(d_wc, s + 1) == (1u | ((c + 1) << 16)) &&
-          __builtin_amdgcn_readlane(d_wc, s + 2) == (1u | ((c + 2) << 16)) && (f1 & f2 & f3) == 1) {
+      if (wc3 == (4u | ((cb + 12) << 16)) && __builtin_amdgcn_readlane(d_wc, s + 1) == (4u | ((cb + 4) << 16)) &&
+          __builtin_amdgcn_readlane(d_wc, s + 2) == (4u | ((cb + 8) << 16)) && (f1 & f2 & f3) == 1) {
         const uintptr_t g1 = readlane64(d_addr, s + 1), g2 = readlane64(d_addr, s + 2),
                         g3 = readlane64(d_addr, s + 3);
         for (uint32_t r = threadIdx.x; r < hr; r += kBlock) {
@@ -611,7 +915,7 @@ __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, con
     }
     // two two-dword segments side by side (8-byte runs): one LDS read of the
     // four dwords a row, two stores
-    if (w == 2 && fan == 1 && s + 1 < nd && __builtin_amdgcn_readlane(d_wc, s + 1) == (2u | ((c + 2) << 16)) &&
+    if (w == 2 && fan == 1 && s + 1 < nd && __builtin_amdgcn_readlane(d_wc, s + 1) == (8u | ((cb + 8) << 16)) &&
         __builtin_amdgcn_readlane(d_fan, s + 1) == 1) {
       const uintptr_t g1 = readlane64(d_addr, s + 1);
       for (uint32_t r = threadIdx.x; r < hr; r += kBlock) {
@@ -664,42 +968,6 @@ __device__ __forceinline__ void window_dwords(const reshard_descriptor_t& D, con
         __builtin_nontemporal_store(v, as_global<u32_u>(sh.ptr(refs[ref + f]) + off + 4 * uint64_t(j)));
     }
   }
-}
-
-// n <= 16 bytes from global address a into bytes [0, n) of the result (any
-// alignment: gfx950 global accesses need none).  Streaming (non-temporal).
-__device__ __forceinline__ u32x4 load_bytes(uintptr_t a, uint32_t n) {
-  if (n == 16) return load_16_unaligned(a);
-  uint64_t lo = 0, hi = 0;
-  uint32_t at = 0;
-  if (n & 8) {
-    lo = __builtin_nontemporal_load(as_global<const u64_u>(a));
-    at = 8;
-  }
-  if (n & 4) {
-    const uint64_t x = __builtin_nontemporal_load(as_global<const u32_u>(a + at));
-    if (at < 8) lo |= x << (8 * at); else hi |= x;
-    at += 4;
-  }
-  if (n & 2) {
-    const uint64_t x = *as_global<const u16_u>(a + at);
-    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
-    at += 2;
-  }
-  if (n & 1) {
-    const uint64_t x = *as_global<const uint8_t>(a + at);
-    if (at < 8) lo |= x << (8 * at); else hi |= x << (8 * (at - 8));
-  }
-  return u32x4{uint32_t(lo), uint32_t(lo >> 32), uint32_t(hi), uint32_t(hi >> 32)};
-}
-
-// Bytes [0, n) of v (n <= 16) to global address d, streaming stores for the
-// whole-word widths, at most four stores otherwise.
-__device__ __forceinline__ void store_bytes(uintptr_t d, u32x4 v, uint32_t n) {
-  if (n == 16) __builtin_nontemporal_store(v, as_global<u32x4_u>(d));
-  else if (n == 8) __builtin_nontemporal_store((uint64_t(v.y) << 32) | v.x, as_global<u64_u>(d));
-  else if (n == 4) __builtin_nontemporal_store(v.x, as_global<u32_u>(d));
-  else store_head_bytes(d, v, n);
 }
 
 // 4x4 transpose of 32-bit words across the four lanes of each quad: with row i
@@ -1381,7 +1649,8 @@ enum KernelKind : int {
                      // runs (window_octets): no LDS
   kKindGatherRows = 10,  // every descriptor RESHARD_DESC_GATHER_ROWS (gather_rows)
   kKindReduce = 11,      // every descriptor RESHARD_DESC_REDUCE (reduce_items)
-  kKindDwords = 12,      // every descriptor a dword band (window_dwords): LDS, no byte paths
+  kKindNarrow = 12,      // every descriptor a narrow band of dword segments (window_narrow): LDS
+  kKindNarrowBytes = 13, // every descriptor a narrow band (window_narrow, every segment class): LDS
   kKindAligned = 16, // added to kKindChunks when every shard pointer is 16-byte
                      // aligned: no bytewise fallback is compiled in
 };
@@ -1442,7 +1711,8 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
   const uint32_t unit = kKind == kKindItems16 ? 16u : unit_mode & 0xffffu;
   const uint32_t mode = kKind == kKindItems16 ? uint32_t(RESHARD_DESC_ITEMS)
                         : kKind == kKindChunks ? uint32_t(RESHARD_DESC_DST_CHUNKS)
-                        : kKind == kKindQuadRows || kKind == kKindOctets || kKind == kKindDwords
+                        : kKind == kKindQuadRows || kKind == kKindOctets || kKind == kKindNarrow ||
+                                  kKind == kKindNarrowBytes
                             ? uint32_t(RESHARD_DESC_WINDOW)
                         : kKind == kKindGatherRows ? uint32_t(RESHARD_DESC_GATHER_ROWS)
                         : kKind == kKindReduce ? uint32_t(RESHARD_DESC_REDUCE)
@@ -1457,10 +1727,10 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     gather_rows(D, segs, refs, gsh, t - tile_begin[lo]);
     return;
   }
-  if constexpr (kKind == kKindDwords) {
-    __shared__ uint32_t dword_window[kDwordWindowWords];
+  if constexpr (kKind == kKindNarrow || kKind == kKindNarrowBytes) {
+    __shared__ uint32_t narrow_window[kNarrowWindowWords];
     const Shards<kKarg> wsh{table, &karg, refs};
-    window_dwords(D, segs, refs, wsh, t - tile_begin[lo], dword_window);
+    window_narrow<kKind == kKindNarrowBytes>(D, segs, refs, wsh, t - tile_begin[lo], narrow_window);
     return;
   }
   if constexpr (kKind == kKindReduce) {
@@ -1592,8 +1862,10 @@ hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_des
       return RS_LAUNCH(kKindGatherRows);
     case kKindReduce:
       return RS_LAUNCH(kKindReduce);
-    case kKindDwords:
-      return RS_LAUNCH(kKindDwords);
+    case kKindNarrow:
+      return RS_LAUNCH(kKindNarrow);
+    case kKindNarrowBytes:
+      return RS_LAUNCH(kKindNarrowBytes);
     default:
       return RS_LAUNCH(kKindAll);
   }
@@ -1617,31 +1889,36 @@ bool octets_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
   return (src_runs && full_side(T, D.fanout, w)) || (dst_runs && full_side(S, D.dst_ref_begin, w));
 }
 
-// Whether a descriptor is a band window_dwords moves: a WINDOW band more than
-// 16 bytes (and at most 256) wide, every segment packed at dword granularity,
-// and the window's rows at the odd dword pitch within kDwordWindowWords.
-bool dwords_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
+// Whether a descriptor is a band window_narrow moves (a WINDOW band more than
+// 16 bytes wide whose segments are all packed, row stride = width, at most 64 a
+// side, with its rows per tile within kNarrowWindowBytes at the band's pitch):
+// 0 no, 1 with dword segments only, 2 with segments of other classes too.
+int narrow_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
   const uint32_t w = D.run_bytes;
-  if (D.mode != RESHARD_DESC_WINDOW || w <= uint32_t(rs::kRowModeBytes) || w > 256 || w % 4) return false;
-  if (uint64_t(D.extent[1]) * ((w / 4) | 1u) > kDwordWindowWords) return false;
-  if (D.dst_ref_begin > 64 || D.fanout > 64) return false;  // one segment per lane
+  if (D.mode != RESHARD_DESC_WINDOW || w <= uint32_t(rs::kRowModeBytes) || w > rs::kWindowBytes) return 0;
+  const uint32_t P = narrow_pitch(w);
+  if (uint64_t(D.extent[1]) * P > kNarrowWindowBytes) return 0;
+  if (D.dst_ref_begin > 64 || D.fanout > 64) return 0;  // one segment per lane
   const reshard_segment_t* S = segs.data() + D.src_ptr;
+  int kind = 1;
   for (uint32_t i = 0; i < D.dst_ref_begin + D.fanout; ++i) {
     const reshard_segment_t& x = S[i];
-    if (x.width % 4 || x.col % 4 || x.offset % 4 || uint64_t(x.row_stride) != x.width) return false;
+    if (x.width == 0 || uint64_t(x.row_stride) != x.width || uint64_t(x.col) + x.width > w) return 0;
+    if (narrow_class(x.width, x.col, P, w) != kSegDwords) kind = 2;
   }
-  return true;
+  return kind;
 }
 
 }  // namespace
 
 int kernel_kind_gather_rows() { return kKindGatherRows; }
-int kernel_kind_dwords() { return kKindDwords; }
+bool kernel_kind_narrow(int kind) { return kind == kKindNarrow || kind == kKindNarrowBytes; }
 
 // The kernel variant of a plan's descriptors.
 int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vector<reshard_segment_t>& segs) {
-  bool items16 = true, chunks = true, quad_rows = true, octets = true, gather = true, reduce = true, dwords = true;
+  bool items16 = true, chunks = true, quad_rows = true, octets = true, gather = true, reduce = true;
   bool window = false;
+  int narrow = 1;  // the narrow build that moves every descriptor (0: none)
   for (const reshard_descriptor_t& D : descs) {
     if (D.mode != RESHARD_DESC_ITEMS || D.unit != 16) items16 = false;
     if (D.mode != RESHARD_DESC_DST_CHUNKS) chunks = false;
@@ -1651,13 +1928,14 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
     if (!octets_band(D, segs)) octets = false;
     if (D.mode != RESHARD_DESC_GATHER_ROWS) gather = false;
     if (D.mode != RESHARD_DESC_REDUCE) reduce = false;
-    if (!dwords_band(D, segs)) dwords = false;
+    const int n = narrow_band(D, segs);
+    narrow = n == 0 || narrow == 0 ? 0 : std::max(narrow, n);
     if (D.mode == RESHARD_DESC_WINDOW) window = true;
   }
   if (gather && !descs.empty()) return kKindGatherRows;
   if (reduce && !descs.empty()) return kKindReduce;
   return items16 ? kKindItems16 : chunks ? kKindChunks : octets ? kKindOctets : quad_rows ? kKindQuadRows
-         : dwords ? kKindDwords : window ? kKindAll : kKindCopy;
+         : narrow == 1 ? kKindNarrow : narrow == 2 ? kKindNarrowBytes : window ? kKindAll : kKindCopy;
 }
 
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,

@@ -204,7 +204,7 @@ void build_image_locked(reshard_plan_s* p) {
   // dword bands: each destination segment carries its first replica's slot
   // (the kernel then reaches the pointer in one load instead of two)
   for (const Group& g : groups) {
-    if (g.kind != rs::kernel_kind_dwords()) continue;
+    if (!rs::kernel_kind_narrow(g.kind)) continue;
     for (const uint32_t i : g.descs) {
       const reshard_descriptor_t& D = H.descs[i];
       for (uint32_t k = 0; k < D.fanout; ++k) {

@@ -376,10 +376,228 @@ def _run_reduce(D, refs, srcs_flat, dsts_flat):
             dst[d_byte + b] = out[:, b]
 
 
+NARROW_WINDOW_BYTES = 18432
+
+
+def narrow_pitch(W):
+    """Window row pitch (bytes) of a narrow band: an odd number of dwords when the
+    band width W is a multiple of 4, else W."""
+    return W if W % 4 else 4 * ((W // 4) | 1)
+
+
+def narrow_class(wb, cb, P, W):
+    """How the narrow-band kernel moves a segment of width wb at column cb."""
+    if P % 4 == 0 and wb % 4 == 0 and cb % 4 == 0:
+        return "dwords"
+    if cb == 0 and wb == W and P == W:
+        return "whole"
+    return "rows" if wb <= 16 else "pieces"
+
+
+def is_narrow_band(D, segs):
+    """The host check that sends a WINDOW band to the narrow-band kernel."""
+    W = D["run_bytes"]
+    if D["mode"] != R.DESC_WINDOW or W <= 16 or W > 16384:
+        return False
+    if D["extent"][1] * narrow_pitch(W) > NARROW_WINDOW_BYTES or D["dst_ref_begin"] > 64 or D["fanout"] > 64:
+        return False
+    side = segs[D["src_ptr"]:D["src_ptr"] + D["dst_ref_begin"] + D["fanout"]]
+    return all(sg["width"] > 0 and sg["row_stride"] == sg["width"] and sg["col"] + sg["width"] <= W for sg in side)
+
+
+def _div_small(n, w):
+    """The kernel's n / w (n < 2^16, 1 <= w < 2^16) by a multiply with 2^32 / w
+    rounded up; n may be an array."""
+    assert 1 <= w < 1 << 16 and np.all(np.asarray(n) < 1 << 16)
+    if w == 1:
+        return n
+    return (np.asarray(n, dtype=np.uint64) * np.uint64(0xFFFFFFFF // w + 1) >> np.uint64(32)).astype(np.int64)
+
+
+def narrow_segment_moves(sg, P, W, hr, phase):
+    """The narrow-band kernel's addressing of one segment for one tile of hr
+    rows, replayed: arrays (stream byte, window byte, bytes) of the pieces its
+    lanes move, in phase 1 (source stream into the window) or phase 2 (window
+    into the destination stream).  Every piece stays inside the segment's
+    columns of one window row."""
+    wb, cb = sg["width"], sg["col"]
+    cls = narrow_class(wb, cb, P, W)
+    if cls == "dwords":
+        w, c, pitch, n = wb // 4, cb // 4, P // 4, hr * wb // 4
+        row_lane = phase == 2 and w <= 4 and sg["fanout"] == 1  # one row a lane (also the batched reads)
+        if row_lane:
+            r = np.arange(hr, dtype=np.int64)
+            lo, win, ln = 4 * w * r, 4 * (r * pitch + c), np.full(hr, 4 * w)
+        else:
+            quads = (w & 3) == 0 or (c == 0 and w == pitch)
+            nq = n // 4 if quads else 0
+            j = np.concatenate([4 * np.arange(nq, dtype=np.int64), np.arange(4 * nq, n, dtype=np.int64)])
+            r = _div_small(j, w)
+            lo, win = 4 * j, 4 * (r * pitch + c + (j - r * w))
+            ln = np.where(np.arange(len(j)) < nq, 16, 4)
+            # a quad stays together in the window
+            jq = j[:nq]
+            rq = _div_small(jq + 3, w)
+            assert np.all(rq * pitch + c + (jq + 3 - rq * w) == win[:nq] // 4 + 3)
+    elif cls == "whole":
+        lo = 16 * np.arange(-(-hr * wb // 16), dtype=np.int64)
+        win, ln = lo.copy(), np.minimum(16, hr * wb - lo)
+    elif cls == "rows":
+        r = np.arange(hr, dtype=np.int64)
+        lo, win, ln = r * wb, r * P + cb, np.full(hr, wb)
+    else:
+        j = 16 * np.arange(-(-hr * wb // 16), dtype=np.int64)
+        ln = np.minimum(16, hr * wb - j)
+        r = _div_small(j, wb)
+        col = j - r * wb
+        l1 = np.minimum(ln, wb - col)
+        two = ln > l1
+        lo = np.concatenate([j, j[two] + l1[two]])
+        win = np.concatenate([r * P + cb + col, (r[two] + 1) * P + cb])
+        ln = np.concatenate([l1, ln[two] - l1[two]])
+    lo, win, ln = (np.asarray(x, dtype=np.int64) for x in (lo, win, ln))
+    assert np.all(ln >= 1) and np.all(lo >= 0) and np.all(lo + ln <= hr * wb)
+    if cb == 0 and wb == W == P:  # whole rows with no padding: the stream is the window
+        assert np.all(win == lo)
+    else:
+        row = win // P
+        assert np.all(row < hr) and np.all(win % P >= cb) and np.all(win % P + ln <= cb + wb)
+        assert np.all((win - row * P - cb) == lo - row * wb)  # the same row and column on both sides
+    return lo, win, ln
+
+
+_M32 = 0xFFFFFFFF
+
+
+def _rotate_bytes(v, s):
+    """The kernel's rotate_bytes on four 32-bit words: byte i of the result is
+    byte (i - s) mod 16 of v, built the way the kernel builds it."""
+    if s & 1:
+        v = [((v[0] << 8) | (v[3] >> 24)) & _M32, ((v[1] << 8) | (v[0] >> 24)) & _M32,
+             ((v[2] << 8) | (v[1] >> 24)) & _M32, ((v[3] << 8) | (v[2] >> 24)) & _M32]
+    if s & 2:
+        v = [((v[0] << 16) | (v[3] >> 16)) & _M32, ((v[1] << 16) | (v[0] >> 16)) & _M32,
+             ((v[2] << 16) | (v[1] >> 16)) & _M32, ((v[3] << 16) | (v[2] >> 16)) & _M32]
+    if s & 4:
+        v = [v[3], v[0], v[1], v[2]]
+    if s & 8:
+        v = [v[2], v[3], v[0], v[1]]
+    return v
+
+
+def thin_runs(side, fan_matters):
+    """The kernel's runs of thin segments (1 or 2 bytes wide) of one side: lists
+    of consecutive segment indices with one width, consecutive columns and (on
+    the destination side) one fan-out; every other segment stands alone."""
+    out, s = [], 0
+    while s < len(side):
+        e = s + 1
+        if side[s]["width"] <= 2:
+            while (e < len(side) and side[e]["width"] == side[s]["width"]
+                   and side[e]["col"] == side[s]["col"] + (e - s) * side[s]["width"]
+                   and (not fan_matters or side[e]["fanout"] == side[s]["fanout"])):
+                e += 1
+        out.append(list(range(s, e)))
+        s = e
+    return out
+
+
+def _thin_run_bytes(run, side, P, hr, r0, window, flat, refs, is_src):
+    """A run of thin segments through the kernel's thin path, byte for byte: a
+    lane (item i, lane i mod 64) moves 8 rows of one segment in a rotated
+    order, rows past the last whole piece one a lane."""
+    wb = side[run[0]]["width"]
+    nq, tail = hr // 8, hr % 8
+    for i in range(len(run) * nq):
+        seg, q = divmod(i, nq)
+        sg = side[run[seg]]
+        lane = i % 64
+        rot = ((lane >> 2) ^ (lane >> 5)) & 7
+        g = sg["offset"] + r0 * wb + 8 * wb * q                 # stream piece in the shard
+        p = q * 8 * P + side[run[0]]["col"] + seg * wb          # window byte of row 8q
+        assert p - q * 8 * P == sg["col"]
+        at = [p + ((j + rot) & 7) * P for j in range(8)]         # slot j -> row (j + rot) mod 8
+        if is_src:
+            data = flat[sg["ptr"]][g:g + 8 * wb]
+            if wb == 2:
+                w = [int(x) for x in data.view(np.uint32)]
+                w = _rotate_bytes(w, (16 - 2 * rot) & 15)
+                slots = np.array(w, dtype=np.uint32).view(np.uint8)
+            else:
+                x = int(data.view(np.uint64)[0])
+                y = ((x >> (8 * rot)) | (x << (64 - 8 * rot))) & (2 ** 64 - 1) if rot else x
+                slots = np.array([y], dtype=np.uint64).view(np.uint8)
+            for j in range(8):
+                window[at[j]:at[j] + wb] = slots[j * wb:(j + 1) * wb]
+        else:
+            slots = np.concatenate([window[a:a + wb] for a in at])
+            if wb == 2:
+                w = [int(x) for x in slots.view(np.uint32)]
+                v = np.array(_rotate_bytes(w, 2 * rot), dtype=np.uint32).view(np.uint8)
+            else:
+                x = int(slots.view(np.uint64)[0])
+                y = ((x << (8 * rot)) | (x >> (64 - 8 * rot))) & (2 ** 64 - 1) if rot else x
+                v = np.array([y], dtype=np.uint64).view(np.uint8)
+            for k in range(sg["fanout"]):
+                flat[refs[sg["ptr"] + k]][g:g + 8 * wb] = v
+    for i in range(len(run) * tail):
+        seg, t = divmod(i, tail)
+        sg = side[run[seg]]
+        r = 8 * nq + t
+        g, a = sg["offset"] + (r0 + r) * wb, r * P + sg["col"]
+        if is_src:
+            window[a:a + wb] = flat[sg["ptr"]][g:g + wb]
+        else:
+            for k in range(sg["fanout"]):
+                flat[refs[sg["ptr"] + k]][g:g + wb] = window[a:a + wb]
+
+
+def _run_narrow(D, segs, refs, srcs_flat, dsts_flat):
+    """A narrow band tile by tile, as the narrow-band kernel addresses it; checks
+    that phase 1 writes every window byte of the tile's rows once and phase 2
+    writes every destination stream byte once."""
+    rows, per_tile, W = D["extent"][0], D["extent"][1], D["run_bytes"]
+    P = narrow_pitch(W)
+    assert per_tile * P <= NARROW_WINDOW_BYTES
+    srcs = segs[D["src_ptr"]:D["src_ptr"] + D["dst_ref_begin"]]
+    dsts = segs[D["src_ptr"] + D["dst_ref_begin"]:D["src_ptr"] + D["dst_ref_begin"] + D["fanout"]]
+    for tile in range(-(-rows // per_tile)):
+        r0 = tile * per_tile
+        hr = min(per_tile, rows - r0)
+        window = np.zeros(per_tile * P, dtype=np.uint8)
+        written = np.zeros(per_tile * P, dtype=np.int32)
+        # a single source segment is read through the scalar path, never as a run
+        for run in thin_runs(srcs, False) if len(srcs) > 1 else [[0]]:
+            for s_i in run:
+                lo, win, ln = narrow_segment_moves(srcs[s_i], P, W, hr, 1)
+                written[_ranges(win, ln)] += 1
+            if srcs[run[0]]["width"] <= 2:
+                _thin_run_bytes(run, srcs, P, hr, r0, window, srcs_flat, refs, True)
+                continue
+            sg = srcs[run[0]]
+            lo, win, ln = narrow_segment_moves(sg, P, W, hr, 1)
+            si, wi = _ranges(lo, ln), _ranges(win, ln)
+            assert len(np.unique(si)) == len(si) == hr * sg["width"]
+            window[wi] = srcs_flat[sg["ptr"]][sg["offset"] + r0 * sg["width"] + si]
+        used = (np.arange(hr)[:, None] * P + np.arange(W)[None, :]).reshape(-1)
+        assert np.all(written[used] == 1) and written.sum() == hr * W
+        for run in thin_runs(dsts, True):
+            if dsts[run[0]]["width"] <= 2:
+                _thin_run_bytes(run, dsts, P, hr, r0, window, dsts_flat, refs, False)
+                continue
+            sg = dsts[run[0]]
+            lo, win, ln = narrow_segment_moves(sg, P, W, hr, 2)
+            di, wi = _ranges(lo, ln), _ranges(win, ln)
+            assert len(np.unique(di)) == len(di) == hr * sg["width"]
+            for k in range(sg["fanout"]):
+                dsts_flat[refs[sg["ptr"] + k]][sg["offset"] + r0 * sg["width"] + di] = window[wi]
+
+
 def _run_window(D, segs, refs, srcs_flat, dsts_flat):
     """A window band row by row: sources into a window row, window row out to
     every destination replica.  Also checks that the sources and the
-    destinations each tile the window row exactly."""
+    destinations each tile the window row exactly.  Narrow bands go through
+    the narrow-band kernel's addressing (_run_narrow) after the same check."""
     rows, width = D["extent"][0], D["run_bytes"]
     window = np.zeros((rows, width), dtype=np.uint8)
     srcs = segs[D["src_ptr"]:D["src_ptr"] + D["dst_ref_begin"]]
@@ -389,6 +607,9 @@ def _run_window(D, segs, refs, srcs_flat, dsts_flat):
         for sg in side:
             cover[sg["col"]:sg["col"] + sg["width"]] += 1
         assert (cover == 1).all()
+    if is_narrow_band(D, segs):
+        _run_narrow(D, segs, refs, srcs_flat, dsts_flat)
+        return
     r = np.arange(rows, dtype=np.int64)[:, None]
     for sg in srcs:
         assert sg["fanout"] == 0

@@ -127,15 +127,17 @@ def test_misaligned_shard_pointers(misalign):
                                                 "runs32_gather", "octets_gather", "octets_scatter_rep", "bands16_96",
                                                 "bands16_80_rep", "pairs_gather", "pairs_rep", "narrow_8byte_rows",
                                                 "gather_uneven", "gather_fanout", "gather_rep_src",
-                                                "gather_row_cuts")]
+                                                "gather_row_cuts", "bytes_r2_in32", "bytes_r2_rep",
+                                                "bytes_ragged13", "bytes_ragged13_gather", "bytes_u8_odd_rows",
+                                                "bytes_pieces18", "bytes_pieces18_gather", "bytes_w512")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 
 
 @pytest.mark.parametrize("name", ["narrow_scatter_rep", "runs_scatter", "runs64_scatter", "runs32_scatter",
-                                  "bands16_scatter", "octets_gather"])
+                                  "bands16_scatter", "octets_gather", "bytes_r2_rep", "bytes_ragged13_gather"])
 def test_band_builds_with_pointer_table(name):
-    """Narrow band layouts (quad rows, dword bands, 2-byte column runs) with
+    """Narrow band layouts (quad rows, narrow bands, 2-byte column runs) with
     their shard pointers in the device table (a batch of copies of one narrow
     layout, more pointers than the kernel arguments hold), so every pointer
     lookup goes through the table."""
@@ -567,7 +569,7 @@ def test_graph_capture_refused_for_pointer_table_plans():
 
 def _mixed_kind_specs():
     """A batch that mixes descriptor kinds: 16-byte items of a 32 MiB projection,
-    dword bands of 64 MiB of 8-byte column slices, destination chunks, a small
+    narrow bands of 64 MiB of 8-byte column slices, destination chunks, a small
     band of 2-byte column runs and gather-rows bands (8002-byte rows from three
     column strips)."""
     small = {s.name: s for s in small_specs()}
@@ -578,7 +580,7 @@ def _mixed_kind_specs():
 
 def test_mixed_kinds_one_launch_per_group():
     """The descriptors that are not bands share one launch, and each band kind
-    (dword bands, 2-byte column runs, gather rows) runs in a launch of its
+    (narrow bands, 2-byte column runs, gather rows) runs in a launch of its
     own build; bit-exact.  Items with chunks, or one band kind alone, stay one
     launch."""
     specs = _mixed_kind_specs()
@@ -645,12 +647,12 @@ def test_random_mixed_launch_groups(seed):
     """Three narrow band workloads of 4096 tiles each, drawn at random, batched
     with seeded random layouts and small narrow ones in shuffled order: the plan
     runs as several launch groups (one per band build drawn, quad rows, 2-byte
-    column runs or dword bands), and every destination is bit-exact."""
+    column runs or narrow bands), and every destination is bit-exact."""
     import random
     rng = random.Random(seed)
-    bands = [(W.narrow_columns(1 << 21), "quad"), (W.narrow_columns_tp8(1 << 21), "dwords"),
-             (W.narrow_columns_64b_tp8(1 << 20), "dwords"), (W.narrow_columns_64b_tp4(1 << 20), "dwords"),
-             (W.narrow_columns_32b_tp4(1 << 21), "dwords"), (W.narrow_columns_16b_tp8(1 << 21), "octets")]
+    bands = [(W.narrow_columns(1 << 21), "quad"), (W.narrow_columns_tp8(1 << 21), "narrow"),
+             (W.narrow_columns_64b_tp8(1 << 20), "narrow"), (W.narrow_columns_64b_tp4(1 << 20), "narrow"),
+             (W.narrow_columns_32b_tp4(1 << 21), "narrow"), (W.narrow_columns_16b_tp8(1 << 21), "octets")]
     drawn = rng.sample(bands, 3)
     specs = [w.tensors[0] for w, _ in drawn] + random_specs(400 + seed, 4) + narrow_random_specs(500 + seed, 3)
     rng.shuffle(specs)

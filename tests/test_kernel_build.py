@@ -46,10 +46,11 @@ def kernel_meta(tmp_path_factory):
 
 def test_every_variant_is_compiled(kernel_meta):
     names = [n for n in kernel_meta if "reshard_copy_kernel" in n]
-    # two pointer placements x ten variants (16-byte items, destination chunks,
-    # aligned destination chunks, copy modes, quad row bands, 2-byte-run bands,
-    # gather-rows bands, Partial sums, dword bands, all modes)
-    assert len(names) == 20, sorted(kernel_meta)
+    # two pointer placements x eleven variants (16-byte items, destination
+    # chunks, aligned destination chunks, copy modes, quad row bands, 2-byte-run
+    # bands, gather-rows bands, Partial sums, narrow bands of dword segments,
+    # narrow bands of any segments, all modes)
+    assert len(names) == 22, sorted(kernel_meta)
 
 
 def test_no_scratch(kernel_meta):
@@ -58,12 +59,12 @@ def test_no_scratch(kernel_meta):
 
 
 def test_lds_only_in_the_window_variants(kernel_meta):
-    """Only the all-modes variant (LDS windows) and the dword-band variant
+    """Only the all-modes variant (LDS windows) and the narrow-band variants
     allocate LDS: a private array the compiler moved to LDS (an index it could
     not resolve) shows up here."""
     for name, meta in kernel_meta.items():
         want = 16384 if re.search(r"reshard_copy_kernelILb[01]ELi3E", name) else \
-            18432 if re.search(r"reshard_copy_kernelILb[01]ELi12E", name) else 0
+            18432 if re.search(r"reshard_copy_kernelILb[01]ELi1[23]E", name) else 0
         assert meta["lds"] == want, (name, meta)
 
 

@@ -93,6 +93,25 @@ def small_specs():
         T("octets_gather", (1041, 8), torch.bfloat16, (8,), (1,), (3,), (0,)),
         T("octets_scatter_rep", (523, 8), torch.float16, (3,), (0,), (2, 8), (RR, 1)),
         T("octets_tiny", (5, 8), torch.bfloat16, (1,), (0,), (8,), (1,)),
+        # narrow bands at 2- and 1-byte granularity and past 256 bytes: single
+        # bf16 columns of 32- and 64-byte rows (scatter, gather, replicas),
+        # ragged 8/8/8/2-byte shards of 26-byte rows (a pitch of one row), 6-,
+        # 5- and 1-byte shards, odd row widths, 18-byte shards whose 16-byte
+        # pieces straddle rows, 512-byte rows of 64-byte shards, a tiny band
+        T("bytes_r2_in32", (1037, 16), torch.bfloat16, (2,), (0,), (16,), (1,)),
+        T("bytes_r2_in64_gather", (1043, 32), torch.bfloat16, (32,), (1,), (3,), (0,)),
+        T("bytes_r2_rep", (523, 16), torch.float16, (3,), (0,), (2, 16), (RR, 1)),
+        T("bytes_ragged13", (2053, 13), torch.bfloat16, (2,), (0,), (4,), (1,)),
+        T("bytes_ragged13_gather", (2053, 13), torch.bfloat16, (4,), (1,), (3,), (0,)),
+        T("bytes_r6_in24", (1031, 12), torch.bfloat16, (3,), (0,), (4,), (1,)),
+        T("bytes_u8_r5", (1029, 40), torch.uint8, (2,), (0,), (8,), (1,)),
+        T("bytes_u8_r1", (1033, 24), torch.uint8, (2,), (0,), (24,), (1,)),
+        T("bytes_u8_odd_rows", (1031, 19), torch.uint8, (3,), (0,), (2,), (1,)),
+        T("bytes_pieces18", (1039, 18), torch.bfloat16, (2,), (0,), (2,), (1,)),
+        T("bytes_pieces18_gather", (1039, 18), torch.bfloat16, (2,), (1,), (3,), (0,)),
+        T("bytes_w512", (301, 256), torch.bfloat16, (2,), (0,), (8,), (1,)),
+        T("bytes_w512_gather", (301, 256), torch.bfloat16, (8,), (1,), (2,), (0,)),
+        T("bytes_tiny", (3, 13), torch.bfloat16, (1,), (0,), (4,), (1,)),
         # 8-byte rows cut into two 4-byte column runs (register row mode)
         T("pairs_gather", (1029, 4), torch.bfloat16, (2,), (1,), (3,), (0,)),
         T("pairs_rep", (517, 2), torch.float32, (3,), (0,), (2, 2), (RR, 1)),
