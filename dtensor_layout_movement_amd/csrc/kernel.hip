@@ -515,13 +515,12 @@ __device__ __forceinline__ void store_bytes(uintptr_t d, u32x4 v, uint32_t n) {
 //   rows    at most 16 bytes wide: a lane moves one row;
 //   pieces  wider: a lane moves a 16-byte piece of the stream, which meets at
 //           most two rows.
-constexpr uint32_t kNarrowWindowBytes = 18432;
+using rs::kNarrowWindowBytes;
+using rs::narrow_pitch;
 constexpr uint32_t kNarrowWindowWords = kNarrowWindowBytes / 4;
 constexpr int kNarrowBatch = 4;  // dword pieces per lane with loads in flight together
 constexpr int kBytesBatch = 2;   // other pieces
 constexpr uint32_t kSegDwords = 0, kSegWhole = 1, kSegRows = 2, kSegPieces = 3;
-
-__host__ __device__ __forceinline__ uint32_t narrow_pitch(uint32_t W) { return W % 4 ? W : 4 * ((W / 4) | 1u); }
 
 __host__ __device__ __forceinline__ uint32_t narrow_class(uint32_t wb, uint32_t cb, uint32_t P, uint32_t W) {
   if (P % 4 == 0 && wb % 4 == 0 && cb % 4 == 0) return kSegDwords;
@@ -1895,17 +1894,22 @@ bool octets_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
 // 0 no, 1 with dword segments only, 2 with segments of other classes too.
 int narrow_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
   const uint32_t w = D.run_bytes;
-  if (D.mode != RESHARD_DESC_WINDOW || w <= uint32_t(rs::kRowModeBytes) || w > rs::kWindowBytes) return 0;
+  if (D.mode != RESHARD_DESC_WINDOW || w == 0 || w > rs::kWindowBytes) return 0;
   const uint32_t P = narrow_pitch(w);
   if (uint64_t(D.extent[1]) * P > kNarrowWindowBytes) return 0;
   if (D.dst_ref_begin > 64 || D.fanout > 64) return 0;  // one segment per lane
   const reshard_segment_t* S = segs.data() + D.src_ptr;
   int kind = 1;
+  bool thin = false;
   for (uint32_t i = 0; i < D.dst_ref_begin + D.fanout; ++i) {
     const reshard_segment_t& x = S[i];
     if (x.width == 0 || uint64_t(x.row_stride) != x.width || uint64_t(x.col) + x.width > w) return 0;
     if (narrow_class(x.width, x.col, P, w) != kSegDwords) kind = 2;
+    thin |= x.width <= 2;
   }
+  // a row-mode band (at most 16 bytes wide) only with segments of one or two
+  // bytes, and not a band of the octet exchange
+  if (w <= uint32_t(rs::kRowModeBytes) && (!thin || octets_band(D, segs))) return 0;
   return kind;
 }
 
@@ -1934,8 +1938,8 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
   }
   if (gather && !descs.empty()) return kKindGatherRows;
   if (reduce && !descs.empty()) return kKindReduce;
-  return items16 ? kKindItems16 : chunks ? kKindChunks : octets ? kKindOctets : quad_rows ? kKindQuadRows
-         : narrow == 1 ? kKindNarrow : narrow == 2 ? kKindNarrowBytes : window ? kKindAll : kKindCopy;
+  return items16 ? kKindItems16 : chunks ? kKindChunks : octets ? kKindOctets : narrow == 1 ? kKindNarrow
+         : narrow == 2 ? kKindNarrowBytes : quad_rows ? kKindQuadRows : window ? kKindAll : kKindCopy;
 }
 
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,

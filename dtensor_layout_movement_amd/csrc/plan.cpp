@@ -548,8 +548,14 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
     b.d.extent[0] = uint32_t(rb - ra);
     const bool quad = width == kRowModeBytes && (quad_side(b.src) || quad_side(b.dst) || octet_side(b.src) ||
                                                  octet_side(b.dst));
-    b.d.extent[1] = uint32_t(width > kRowModeBytes ? window_rows
-                             : int64_t(kTileThreads) * (quad ? kQuadRowsPerLane : kRowsPerLane));
+    bool thin = false;  // a segment of one or two bytes
+    for (const auto* side : {&b.src, &b.dst})
+      for (const auto& x : *side) thin |= x.width <= 2;
+    int64_t rows_per_tile = width > kRowModeBytes ? window_rows
+                            : int64_t(kTileThreads) * (quad ? kQuadRowsPerLane : kRowsPerLane);
+    if (width <= kRowModeBytes && thin && !quad)
+      while (rows_per_tile * narrow_pitch(uint32_t(width)) > int64_t(kNarrowWindowBytes)) rows_per_tile /= 2;
+    b.d.extent[1] = uint32_t(rows_per_tile);
     b.d.extent[2] = 1;
     b.d.piece = uint32_t(pc0);
     if (rb - ra > int64_t(kMaxItems)) return false;

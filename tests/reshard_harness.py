@@ -394,15 +394,37 @@ def narrow_class(wb, cb, P, W):
     return "rows" if wb <= 16 else "pieces"
 
 
+def _octets_band(D, srcs, dsts):
+    """A 16-byte band of the octet exchange: eight packed 2-byte column runs on
+    one side, one packed run of whole rows on the other."""
+    def runs(S):
+        return len(S) == 8 and all(x["width"] == 2 and x["row_stride"] == 2 and x["col"] == 2 * i
+                                   and x["fanout"] == S[0]["fanout"] for i, x in enumerate(S))
+
+    def full(S):
+        return len(S) == 1 and S[0]["width"] == 16 and S[0]["row_stride"] == 16
+    return (D["run_bytes"] == 16 and D["extent"][1] == 512
+            and ((runs(srcs) and full(dsts)) or (runs(dsts) and full(srcs))))
+
+
 def is_narrow_band(D, segs):
-    """The host check that sends a WINDOW band to the narrow-band kernel."""
+    """The host check that sends a WINDOW band to the narrow-band kernel: packed
+    segments, at most 64 a side, the window within its LDS; a band of at most 16
+    bytes only with a segment of one or two bytes and not of the octet
+    exchange."""
     W = D["run_bytes"]
-    if D["mode"] != R.DESC_WINDOW or W <= 16 or W > 16384:
+    if D["mode"] != R.DESC_WINDOW or W == 0 or W > 16384:
         return False
     if D["extent"][1] * narrow_pitch(W) > NARROW_WINDOW_BYTES or D["dst_ref_begin"] > 64 or D["fanout"] > 64:
         return False
-    side = segs[D["src_ptr"]:D["src_ptr"] + D["dst_ref_begin"] + D["fanout"]]
-    return all(sg["width"] > 0 and sg["row_stride"] == sg["width"] and sg["col"] + sg["width"] <= W for sg in side)
+    srcs = segs[D["src_ptr"]:D["src_ptr"] + D["dst_ref_begin"]]
+    dsts = segs[D["src_ptr"] + D["dst_ref_begin"]:D["src_ptr"] + D["dst_ref_begin"] + D["fanout"]]
+    if not all(sg["width"] > 0 and sg["row_stride"] == sg["width"] and sg["col"] + sg["width"] <= W
+               for sg in srcs + dsts):
+        return False
+    if W <= 16 and (all(sg["width"] > 2 for sg in srcs + dsts) or _octets_band(D, srcs, dsts)):
+        return False
+    return True
 
 
 def _div_small(n, w):

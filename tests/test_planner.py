@@ -112,6 +112,15 @@ def small_specs():
         T("bytes_w512", (301, 256), torch.bfloat16, (2,), (0,), (8,), (1,)),
         T("bytes_w512_gather", (301, 256), torch.bfloat16, (8,), (1,), (2,), (0,)),
         T("bytes_tiny", (3, 13), torch.bfloat16, (1,), (0,), (4,), (1,)),
+        # rows of at most 16 bytes with 1- or 2-byte shards (narrow bands too):
+        # sixteen u8 columns, four bf16 columns, a gather of u8 columns, f16
+        # pairs with replicas, three bf16 columns (a pitch of one row), tiny
+        T("thin_u8_16", (1037, 16), torch.uint8, (2,), (0,), (16,), (1,)),
+        T("thin_bf16_8", (2053, 4), torch.bfloat16, (3,), (0,), (4,), (1,)),
+        T("thin_u8_gather", (1031, 8), torch.uint8, (8,), (1,), (3,), (0,)),
+        T("thin_f16_rep", (1029, 2), torch.float16, (2,), (0,), (2, 2), (RR, 1)),
+        T("thin_bf16_6", (2049, 3), torch.bfloat16, (2,), (0,), (3,), (1,)),
+        T("thin_tiny", (5, 16), torch.uint8, (1,), (0,), (16,), (1,)),
         # 8-byte rows cut into two 4-byte column runs (register row mode)
         T("pairs_gather", (1029, 4), torch.bfloat16, (2,), (1,), (3,), (0,)),
         T("pairs_rep", (517, 2), torch.float32, (3,), (0,), (2, 2), (RR, 1)),
