@@ -283,6 +283,14 @@ def narrow_columns_ragged_tp4(rows: int = 2396745) -> Workload:
                     f"{rows}x14 bf16 N(0,0.02), (2,)[S0] -> (4,)[S1]: ragged 8/8/8/4-byte column shards")
 
 
+def narrow_columns_2b_tp16(rows: int = 1 << 21) -> Workload:
+    """16 bf16 columns (32-byte rows, a rank-16 low-rank factor) over sixteen
+    destinations: every destination row is a single 2-byte column."""
+    t = TensorSpec("narrow16t", (rows, 16), torch.bfloat16, (2,), (0,), (16,), (1,))
+    return Workload(f"narrow_columns_2b_tp16_{rows}x16", (t,), "normal",
+                    f"{rows}x16 bf16 N(0,0.02), (2,)[S0] -> (16,)[S1]: single bf16 columns of 32-byte rows")
+
+
 WORKLOADS = {
     "worked_example_8x8": worked_example_8x8,
     "ffn_up_14336x4096": ffn_up,
@@ -302,6 +310,7 @@ WORKLOADS = {
     "narrow_columns_8b_tp2_8388608x4": narrow_columns_8b_tp2,
     "narrow_columns_64b_tp16_1048576x32": narrow_columns_64b_tp16,
     "narrow_columns_ragged_tp4_2396745x14": narrow_columns_ragged_tp4,
+    "narrow_columns_2b_tp16_2097152x16": narrow_columns_2b_tp16,
 }
 
 

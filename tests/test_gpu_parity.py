@@ -52,7 +52,7 @@ SMALL_FULL = ["worked_example_8x8", "ffn_up_14336x4096", "moe_experts_64x2048x71
               "narrow_columns_16b_tp8_4194304x8",
               "ffn_up_f32_to_bf16_14336x4096", "ffn_up_fsdp2_tp_14336x4096", "ffn_up_partial_14336x4096",
               "narrow_columns_8b_tp2_8388608x4", "narrow_columns_64b_tp16_1048576x32",
-              "narrow_columns_ragged_tp4_2396745x14"]
+              "narrow_columns_ragged_tp4_2396745x14", "narrow_columns_2b_tp16_2097152x16"]
 
 
 @pytest.mark.parametrize("seed", [0, 1, 2])

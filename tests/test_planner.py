@@ -17,7 +17,7 @@ import dtensor_layout_movement_amd as R
 import oracle_pins as P
 from dtensor_layout_movement_amd import workloads as W
 from reshard_harness import (Plan, apply_pieces, assert_boxes_agree, assert_descriptors_in_bounds,
-                             box_shape, lib_runs, magic_div,
+                             box_shape, is_narrow_band, lib_runs, magic_div,
                              oracle_dsts, run_descriptors, sources_for)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -577,7 +577,8 @@ def test_piece_counts_of_workloads():
               "narrow_columns_32b_tp4_2097152x16": 8, "narrow_columns_16b_tp8_4194304x8": 16,
               "dense_layer_refit_32_layers": 32 * (7 * 4 + 2 * 1), "ffn_up_fsdp2_tp_14336x4096": 16,
               "ffn_up_partial_14336x4096": 8, "narrow_columns_8b_tp2_8388608x4": 4,
-              "narrow_columns_64b_tp16_1048576x32": 32, "narrow_columns_ragged_tp4_2396745x14": 8}
+              "narrow_columns_64b_tp16_1048576x32": 32, "narrow_columns_ragged_tp4_2396745x14": 8,
+              "narrow_columns_2b_tp16_2097152x16": 32}
     for wl in full_workload_plans():
         with Plan(wl.tensors) as plan:
             assert plan.stats()["n_pieces"] == counts[wl.name]
@@ -918,13 +919,15 @@ def test_errors():
     R.reshard_layout_destroy(None)
 
 
-def test_device_segments_of_dword_bands():
+def test_device_segments_of_narrow_bands():
     """The device table's segments equal the planned ones, except that each
-    destination segment of a packed dword band carries its first replica's
-    absolute pointer slot in row_stride (all of a band's segments, or none)."""
+    destination segment of a narrow band carries its first replica's absolute
+    pointer slot in row_stride (all of a band's segments, or none)."""
     specs = [W.narrow_columns_64b_tp16(4096).tensors[0], W.narrow_columns_ragged_tp4(3001).tensors[0],
-             W.narrow_columns(2048).tensors[0], W.uneven(301, 257).tensors[0]]
-    specs += [s for s in small_specs() if s.name in ("wide_window", "narrow_scatter_rep", "strips_fanout")]
+             W.narrow_columns(2048).tensors[0], W.uneven(301, 257).tensors[0],
+             W.narrow_columns_2b_tp16(4096).tensors[0]]
+    specs += [s for s in small_specs() if s.name in ("wide_window", "narrow_scatter_rep", "strips_fanout",
+                                                     "bytes_r2_rep", "thin_u8_16")]
     rewritten_bands = 0
     for spec in specs:
         with Plan([spec]) as plan:
@@ -941,16 +944,17 @@ def test_device_segments_of_dword_bands():
                 for k in range(D["dst_ref_begin"]):  # sources: unchanged
                     assert dev[first + k] == host[first + k]
                 dst = range(first + D["dst_ref_begin"], first + D["dst_ref_begin"] + D["fanout"])
-                # (a slot may equal the width by chance: one changed segment marks the band)
-                if any(dev[i] != host[i] for i in dst):
+                if is_narrow_band(D, host):
                     rewritten_bands += 1
                     for i in dst:
                         h, d = host[i], dev[i]
-                        assert h["row_stride"] == h["width"] and h["width"] % 4 == 0
+                        assert h["row_stride"] == h["width"]
                         assert d["row_stride"] == st["n_src_ptrs"] + refs[h["ptr"]]
                         assert {k: v for k, v in d.items() if k != "row_stride"} == \
                             {k: v for k, v in h.items() if k != "row_stride"}
-    assert rewritten_bands >= 2
+                else:
+                    assert all(dev[i] == host[i] for i in dst)
+    assert rewritten_bands >= 6
 
 
 def test_partial_errors():
