@@ -201,7 +201,7 @@ void build_image_locked(reshard_plan_s* p) {
   // fan-out list, whose entries were made absolute above
   reshard_segment_t* sg = reinterpret_cast<reshard_segment_t*>(img.data() + segs_off);
   for (size_t i = 0; i < H.segs.size(); ++i) sg[i] = H.segs[i];
-  // dword bands: each destination segment carries its first replica's slot
+  // narrow bands: each destination segment carries its first replica's slot
   // (the kernel then reaches the pointer in one load instead of two)
   for (const Group& g : groups) {
     if (!rs::kernel_kind_narrow(g.kind)) continue;

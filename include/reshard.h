@@ -181,16 +181,20 @@ typedef struct reshard_piece {
  *                            read into the window) followed by `fanout` destination
  *                            segments (written from it), each side in column
  *                            order; offsets and strides are ignored.  Used for
- *                            narrow or misaligned pieces.  A band at most 16
- *                            bytes wide skips LDS: one lane per row assembles
- *                            the row in registers, `extent[1]` = 1024 rows per
- *                            tile (512 when one side is four packed 4-byte
- *                            column runs, which the four lanes of a quad
- *                            exchange).  Some band shapes skip LDS in a kernel
- *                            build of their own (whole rows against packed
- *                            column runs of 2, 4 or 8 bytes, or against
- *                            16-byte-aligned column slices: lanes exchange
- *                            values in registers); each such band kind runs in
+ *                            narrow or misaligned pieces.  A band whose
+ *                            segments are all packed (row stride = width) moves
+ *                            in a narrow-band kernel build, each segment's rows
+ *                            as one contiguous stream on the global side, with
+ *                            `extent[1]` rows per tile within an 18 KiB window.
+ *                            Other bands at most 16 bytes wide skip LDS: one
+ *                            lane per row assembles the row in registers,
+ *                            `extent[1]` = 1024 rows per tile (512 when one
+ *                            side is four packed 4-byte column runs, which the
+ *                            four lanes of a quad exchange, or eight packed
+ *                            2-byte runs, which eight lanes exchange; a band
+ *                            of at most 16 bytes with a 1- or 2-byte segment
+ *                            takes the largest power of two up to 1024 whose
+ *                            narrow-band window fits).  Each band kind runs in
  *                            a launch of its own, whatever the rest of the plan
  *                            holds (n_launches counts them).
  *   RESHARD_DESC_GATHER_ROWS `extent[0]` whole rows of `run_bytes` bytes, packed in
@@ -460,10 +464,9 @@ reshard_status_t reshard_plan_device_refs(reshard_plan_t plan, int64_t capacity,
 /*
  * Inspection: the segment table as the kernel reads it from the device table,
  * host-side (no device call).  It equals reshard_plan_segments except in the
- * destination segments of the bands that the dword-band kernel build moves
- * (packed bands at dword granularity: every segment's row stride is its width):
- * there row_stride holds the absolute pointer slot of the segment's first
- * replica instead.  Writes min(capacity, count) segments and the count.
+ * destination segments of the bands that the narrow-band kernel builds move
+ * (packed bands: every segment's row stride is its width): there row_stride
+ * holds the absolute pointer slot of the segment's first replica instead.  Writes min(capacity, count) segments and the count.
  * Errors: RESHARD_ERR_INVALID_ARGUMENT.
  */
 reshard_status_t reshard_plan_device_segments(reshard_plan_t plan, int64_t capacity, reshard_segment_t* out,
