@@ -1907,9 +1907,19 @@ int narrow_band(const reshard_descriptor_t& D, const std::vector<reshard_segment
     if (narrow_class(x.width, x.col, P, w) != kSegDwords) kind = 2;
     thin |= x.width <= 2;
   }
-  // a row-mode band (at most 16 bytes wide) only with segments of one or two
-  // bytes, and not a band of the octet exchange
-  if (w <= uint32_t(rs::kRowModeBytes) && (!thin || octets_band(D, segs))) return 0;
+  // A band of at most 16 bytes (the row mode's) only with a 1- or 2-byte
+  // segment, or with dword segments only and rows of an odd number of dwords
+  // (12 bytes: the window's rows then sit back to back and whole rows move as
+  // 16-byte pieces); and not a 16-byte band with four 4-byte or eight 2-byte
+  // column runs on one side (the quad and octet exchanges).  The row mode
+  // measured faster on 8- and 16-byte rows of dword segments.
+  if (w <= uint32_t(rs::kRowModeBytes)) {
+    const reshard_segment_t* T = S + D.dst_ref_begin;
+    if (w == uint32_t(rs::kRowModeBytes) && (runs_side(S, D.dst_ref_begin, 4, 4) || runs_side(T, D.fanout, 4, 4) ||
+                                             runs_side(S, D.dst_ref_begin, 8, 2) || runs_side(T, D.fanout, 8, 2)))
+      return 0;
+    if (!thin && (kind != 1 || P != w)) return 0;
+  }
   return kind;
 }
 

@@ -133,8 +133,9 @@ constexpr uint32_t kQuadRowsPerLane = 2;
 // LDS window of a narrow band (a packed window band that the narrow-band
 // kernel moves), and its row pitch for a band W bytes wide: an odd number of
 // dwords when W is a multiple of 4, else W.  A band of at most kRowModeBytes
-// with segments of one or two bytes goes there too; its rows per tile are the
-// largest power of two up to kTileThreads * kRowsPerLane whose window fits.
+// with segments of one or two bytes goes there too (its rows per tile are the
+// largest power of two up to kTileThreads * kRowsPerLane whose window fits), and
+// so does one of 12-byte rows of dword segments.
 constexpr uint32_t kNarrowWindowBytes = 18432;
 constexpr uint32_t narrow_pitch(uint32_t W) { return W % 4 ? W : 4 * ((W / 4) | 1u); }
 // Cache line of the L2: a band whose tiles would start off the line grid in

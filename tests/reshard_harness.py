@@ -394,24 +394,20 @@ def narrow_class(wb, cb, P, W):
     return "rows" if wb <= 16 else "pieces"
 
 
-def _octets_band(D, srcs, dsts):
-    """A 16-byte band of the octet exchange: eight packed 2-byte column runs on
-    one side, one packed run of whole rows on the other."""
-    def runs(S):
-        return len(S) == 8 and all(x["width"] == 2 and x["row_stride"] == 2 and x["col"] == 2 * i
+def _exchange_band(D, srcs, dsts):
+    """A 16-byte band with four packed 4-byte or eight packed 2-byte column runs
+    on one side (the quad and octet exchanges of the row mode)."""
+    def runs(S, k, rw):
+        return len(S) == k and all(x["width"] == rw and x["row_stride"] == rw and x["col"] == rw * i
                                    and x["fanout"] == S[0]["fanout"] for i, x in enumerate(S))
-
-    def full(S):
-        return len(S) == 1 and S[0]["width"] == 16 and S[0]["row_stride"] == 16
-    return (D["run_bytes"] == 16 and D["extent"][1] == 512
-            and ((runs(srcs) and full(dsts)) or (runs(dsts) and full(srcs))))
+    return D["run_bytes"] == 16 and any(runs(S, k, rw) for S in (srcs, dsts) for k, rw in ((4, 4), (8, 2)))
 
 
 def is_narrow_band(D, segs):
     """The host check that sends a WINDOW band to the narrow-band kernel: packed
     segments, at most 64 a side, the window within its LDS; a band of at most 16
-    bytes only with a segment of one or two bytes and not of the octet
-    exchange."""
+    bytes only with a segment of one or two bytes, or of 12-byte rows of dword
+    segments, and not one of the quad or octet exchanges."""
     W = D["run_bytes"]
     if D["mode"] != R.DESC_WINDOW or W == 0 or W > 16384:
         return False
@@ -422,8 +418,12 @@ def is_narrow_band(D, segs):
     if not all(sg["width"] > 0 and sg["row_stride"] == sg["width"] and sg["col"] + sg["width"] <= W
                for sg in srcs + dsts):
         return False
-    if W <= 16 and (all(sg["width"] > 2 for sg in srcs + dsts) or _octets_band(D, srcs, dsts)):
-        return False
+    if W <= 16:
+        P = narrow_pitch(W)
+        thin = any(sg["width"] <= 2 for sg in srcs + dsts)
+        dwords = all(narrow_class(sg["width"], sg["col"], P, W) == "dwords" for sg in srcs + dsts)
+        if _exchange_band(D, srcs, dsts) or not (thin or (dwords and P == W)):
+            return False
     return True
 
 

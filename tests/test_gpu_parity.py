@@ -130,7 +130,8 @@ def test_misaligned_shard_pointers(misalign):
                                                 "gather_row_cuts", "bytes_r2_in32", "bytes_r2_rep",
                                                 "bytes_ragged13", "bytes_ragged13_gather", "bytes_u8_odd_rows",
                                                 "bytes_pieces18", "bytes_pieces18_gather", "bytes_w512",
-                                                "thin_u8_16", "thin_u8_gather", "thin_f16_rep", "thin_bf16_6")]
+                                                "thin_u8_16", "thin_u8_gather", "thin_f16_rep", "thin_bf16_6",
+                                                "rows12_f32", "rows12_gather", "rows12_rep")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 

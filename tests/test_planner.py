@@ -121,6 +121,11 @@ def small_specs():
         T("thin_f16_rep", (1029, 2), torch.float16, (2,), (0,), (2, 2), (RR, 1)),
         T("thin_bf16_6", (2049, 3), torch.bfloat16, (2,), (0,), (3,), (1,)),
         T("thin_tiny", (5, 16), torch.uint8, (1,), (0,), (16,), (1,)),
+        # 12-byte rows of 4-byte shards (narrow bands with rows back to back):
+        # scatter, gather, replicas
+        T("rows12_f32", (2053, 3), torch.float32, (2,), (0,), (3,), (1,)),
+        T("rows12_gather", (1031, 6), torch.bfloat16, (3,), (1,), (2,), (0,)),
+        T("rows12_rep", (517, 3), torch.float32, (3,), (0,), (2, 3), (RR, 1)),
         # 8-byte rows cut into two 4-byte column runs (register row mode)
         T("pairs_gather", (1029, 4), torch.bfloat16, (2,), (1,), (3,), (0,)),
         T("pairs_rep", (517, 2), torch.float32, (3,), (0,), (2, 2), (RR, 1)),
