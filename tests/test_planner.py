@@ -419,23 +419,26 @@ def random_specs(seed, count, max_numel=400_000):
 
 
 def narrow_random_specs(seed, count):
-    """Seeded random 2-d layouts whose rows are at most 256 bytes and whose column
-    splits give runs of 1 to 128 bytes: the register row mode, the quad and
-    8-lane exchanges, the 16-byte chunk bands and the LDS windows, with ragged row counts (partial groups of
-    four and eight rows, short last tiles), row splits on either side, replicas
-    on either side and every element size."""
+    """Seeded random 2-d layouts whose rows are at most 512 bytes (odd widths
+    included) and whose column splits, even or ragged, give shards of 1 to 256
+    bytes: the register row mode, the quad and octet exchanges, the narrow
+    bands of every segment class (thin runs of up to 32 segments among them)
+    and the LDS windows, with ragged row counts (partial groups of four and
+    eight rows, short last tiles), row splits on either side, replicas on either
+    side and every element size."""
     rng = random.Random(seed)
     out = []
     while len(out) < count:
         dtype = rng.choice([torch.uint8, torch.bfloat16, torch.float32, torch.float64])
         es = torch.tensor([], dtype=dtype).element_size()
-        width = rng.choice([b for b in (4, 8, 16, 32, 48, 64, 96, 128, 256) if b >= es])
+        width = rng.choice([b for b in (4, 5, 6, 8, 10, 12, 13, 16, 19, 24, 26, 32, 48, 64, 96, 128, 256, 512)
+                            if b >= es and b % es == 0])
         cols = width // es
         rows = rng.choice([rng.randint(1, 40), rng.randint(500, 1100), rng.randint(2000, 5000)])
         # runs the register exchanges move: four or eight 4-byte runs, eight 8-byte runs
         runs4 = 8 if width == 64 else width // 4 if width in (16, 32) and es <= 4 else 0
         def layout():
-            k = rng.choice([c for c in (1, 2, 4, 8) if c <= cols])
+            k = rng.choice([c for c in (1, 2, 3, 4, 8, 16, 32) if c <= cols])
             if runs4 and rng.random() < 0.5:
                 k = runs4
             r = rng.choice([1, 2, 3])
