@@ -512,7 +512,11 @@ __device__ __forceinline__ void store_bytes(uintptr_t d, u32x4 v, uint32_t n) {
 //           stream, or four where they stay together in the window;
 //   whole   the whole row, P = W: 16-byte pieces of the stream are 16-byte
 //           pieces of the window;
-//   rows    at most 16 bytes wide: a lane moves one row;
+//   rows    4, 8 or 16 bytes wide (or 1 or 2: thin_run): a lane moves one row;
+//   bytes   another width below 16: on the source side a lane moves a
+//           16-byte piece of the stream byte by byte (one global access
+//           instead of two or more a row); on the destination side, one row
+//           a lane as for rows;
 //   pieces  wider: a lane moves a 16-byte piece of the stream, which meets at
 //           most two rows.
 using rs::kNarrowWindowBytes;
@@ -520,12 +524,13 @@ using rs::narrow_pitch;
 constexpr uint32_t kNarrowWindowWords = kNarrowWindowBytes / 4;
 constexpr int kNarrowBatch = 4;  // dword pieces per lane with loads in flight together
 constexpr int kBytesBatch = 2;   // other pieces
-constexpr uint32_t kSegDwords = 0, kSegWhole = 1, kSegRows = 2, kSegPieces = 3;
+constexpr uint32_t kSegDwords = 0, kSegWhole = 1, kSegRows = 2, kSegPieces = 3, kSegBytes = 4;
 
 __host__ __device__ __forceinline__ uint32_t narrow_class(uint32_t wb, uint32_t cb, uint32_t P, uint32_t W) {
   if (P % 4 == 0 && wb % 4 == 0 && cb % 4 == 0) return kSegDwords;
   if (cb == 0 && wb == W && P == W) return kSegWhole;
-  return wb <= 16 ? kSegRows : kSegPieces;
+  if (wb > 16) return kSegPieces;
+  return wb <= 2 || wb == 4 || wb == 8 || wb == 16 ? kSegRows : kSegBytes;
 }
 
 // 2^32 / d rounded up, for div_small by d (its unit: dwords for a dword segment,
@@ -730,6 +735,33 @@ __device__ __forceinline__ void dword_stream_in(uintptr_t g, uint32_t w, uint32_
 // and P in bytes).
 __device__ __forceinline__ void bytes_stream_in(uintptr_t g, uint32_t wb, uint32_t cb, uint32_t m, uint32_t cls,
                                                 uint32_t hr, uint32_t P, uint8_t* lds) {
+  if (cls == kSegBytes) {
+    const uint32_t nb = hr * wb;
+    for (uint32_t base = threadIdx.x; 16 * base < nb; base += kBlock * kBytesBatch) {
+      u32x4 v[kBytesBatch];
+#pragma unroll
+      for (int k = 0; k < kBytesBatch; ++k) {
+        const uint32_t j = 16 * (base + uint32_t(k) * kBlock);
+        if (j < nb) v[k] = load_bytes(g + j, min(16u, nb - j));
+      }
+#pragma unroll
+      for (int k = 0; k < kBytesBatch; ++k) {
+        const uint32_t j = 16 * (base + uint32_t(k) * kBlock);
+        if (j >= nb) break;
+        const uint32_t len = min(16u, nb - j);
+        uint32_t r = div_small(j, wb, m), col = j - r * wb;
+        uint8_t* a = lds + r * P + cb + col;
+        const uint32_t w[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (uint32_t b = 0; b < 16; ++b) {  // stream byte j + b: the next column, or the next row's first
+          if (b < len) *a = uint8_t(w[b / 4] >> (8 * (b % 4)));
+          ++col, ++a;
+          if (col == wb) col = 0, a += P - wb;
+        }
+      }
+    }
+    return;
+  }
   if (cls == kSegRows) {
     for (uint32_t base = threadIdx.x; base < hr; base += kBlock * kBytesBatch) {
       u32x4 v[kBytesBatch];
@@ -780,7 +812,7 @@ __device__ __forceinline__ void bytes_stream_out(uintptr_t g0, uint64_t off, uin
                                                  const uint32_t* __restrict__ refs, const Sh& sh, uint32_t wb,
                                                  uint32_t cb, uint32_t m, uint32_t cls, uint32_t hr, uint32_t P,
                                                  const uint8_t* lds) {
-  if (cls == kSegRows) {
+  if (cls == kSegRows || cls == kSegBytes) {  // one row a lane (byte by byte measured no faster here)
     for (uint32_t r = threadIdx.x; r < hr; r += kBlock) {
       const u32x4 v = lds_get(lds + r * P + cb, wb);
       const uint64_t o = uint64_t(r) * wb;

@@ -391,7 +391,9 @@ def narrow_class(wb, cb, P, W):
         return "dwords"
     if cb == 0 and wb == W and P == W:
         return "whole"
-    return "rows" if wb <= 16 else "pieces"
+    if wb > 16:
+        return "pieces"
+    return "rows" if wb in (1, 2, 4, 8, 16) else "bytes"
 
 
 def _exchange_band(D, srcs, dsts):
@@ -467,6 +469,19 @@ def narrow_segment_moves(sg, P, W, hr, phase):
     elif cls == "rows":
         r = np.arange(hr, dtype=np.int64)
         lo, win, ln = r * wb, r * P + cb, np.full(hr, wb)
+    elif cls == "bytes" and phase == 2:  # one row a lane, as for rows
+        r = np.arange(hr, dtype=np.int64)
+        lo, win, ln = r * wb, r * P + cb, np.full(hr, wb)
+    elif cls == "bytes":  # 16-byte pieces byte by byte: row and column of the first, then stepping
+        j0 = 16 * np.arange(-(-hr * wb // 16), dtype=np.int64)
+        r0 = _div_small(j0, wb)
+        b = np.arange(16, dtype=np.int64)
+        lo = (j0[:, None] + b[None, :]).reshape(-1)
+        step = (j0 - r0 * wb)[:, None] + b[None, :]
+        win = ((r0[:, None] + step // wb) * P + cb + step % wb).reshape(-1)
+        keep = lo < hr * wb
+        lo, win = lo[keep], win[keep]
+        ln = np.ones(len(lo), dtype=np.int64)
     else:
         j = 16 * np.arange(-(-hr * wb // 16), dtype=np.int64)
         ln = np.minimum(16, hr * wb - j)

@@ -131,7 +131,8 @@ def test_misaligned_shard_pointers(misalign):
                                                 "bytes_ragged13", "bytes_ragged13_gather", "bytes_u8_odd_rows",
                                                 "bytes_pieces18", "bytes_pieces18_gather", "bytes_w512",
                                                 "thin_u8_16", "thin_u8_gather", "thin_f16_rep", "thin_bf16_6",
-                                                "rows12_f32", "rows12_gather", "rows12_rep")]
+                                                "rows12_f32", "rows12_gather", "rows12_rep", "bytes_r6_gather",
+                                                "bytes_u8_r7_rep")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 

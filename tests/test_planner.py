@@ -126,6 +126,11 @@ def small_specs():
         T("rows12_f32", (2053, 3), torch.float32, (2,), (0,), (3,), (1,)),
         T("rows12_gather", (1031, 6), torch.bfloat16, (3,), (1,), (2,), (0,)),
         T("rows12_rep", (517, 3), torch.float32, (3,), (0,), (2, 3), (RR, 1)),
+        # shards of 3 to 15 bytes moved byte by byte in 16-byte pieces: gathers
+        # of 6-byte and 5-byte shards, 7-byte shards with replicas
+        T("bytes_r6_gather", (1031, 12), torch.bfloat16, (4,), (1,), (3,), (0,)),
+        T("bytes_u8_r5_gather", (1029, 20), torch.uint8, (4,), (1,), (2,), (0,)),
+        T("bytes_u8_r7_rep", (523, 28), torch.uint8, (2,), (0,), (2, 4), (RR, 1)),
         # 8-byte rows cut into two 4-byte column runs (register row mode)
         T("pairs_gather", (1029, 4), torch.bfloat16, (2,), (1,), (3,), (0,)),
         T("pairs_rep", (517, 2), torch.float32, (3,), (0,), (2, 2), (RR, 1)),
