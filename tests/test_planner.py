@@ -121,6 +121,10 @@ def small_specs():
         T("thin_f16_rep", (1029, 2), torch.float16, (2,), (0,), (2, 2), (RR, 1)),
         T("thin_bf16_6", (2049, 3), torch.bfloat16, (2,), (0,), (3,), (1,)),
         T("thin_tiny", (5, 16), torch.uint8, (1,), (0,), (16,), (1,)),
+        # 2-byte shards of 19-byte rows (an odd pitch: 2-byte window accesses at
+        # odd addresses), scatter and gather
+        T("thin_u8_odd_pitch", (1033, 19), torch.uint8, (2,), (0,), (10,), (1,)),
+        T("thin_u8_odd_gather", (1033, 19), torch.uint8, (10,), (1,), (2,), (0,)),
         # 12-byte rows of 4-byte shards (narrow bands with rows back to back):
         # scatter, gather, replicas
         T("rows12_f32", (2053, 3), torch.float32, (2,), (0,), (3,), (1,)),
