@@ -498,8 +498,10 @@ __device__ __forceinline__ void store_bytes(uintptr_t d, u32x4 v, uint32_t n) {
   else store_head_bytes(d, v, n);
 }
 
-// Narrow bands: a WINDOW band more than 16 bytes wide whose segments all hold
-// their rows back to back in their shards (row stride = width).  Every side is
+// Narrow bands: a WINDOW band whose segments all hold their rows back to back
+// in their shards (row stride = width), more than 16 bytes wide, or at most 16
+// with a segment of one or two bytes, or of 12-byte rows of dword segments
+// (narrow_band on the host has the details).  Every side is
 // then a contiguous stream of bytes: stream byte j of a segment w bytes wide is
 // row j / w, byte j % w of the segment.  The window keeps rows at a pitch of P
 // bytes: an odd number of dwords when the band width W is a multiple of 4 (lanes
@@ -507,7 +509,7 @@ __device__ __forceinline__ void store_bytes(uintptr_t d, u32x4 v, uint32_t n) {
 // then hit distinct LDS banks), W otherwise (a segment of whole rows is then the
 // window itself).  Its rows per tile are the LDS window's, and
 // kNarrowWindowBytes bounds the window (checked on the host).  Each segment
-// moves in one of four ways:
+// moves in one of five ways:
 //   dwords  P, column and width multiples of 4: a lane moves one dword of the
 //           stream, or four where they stay together in the window;
 //   whole   the whole row, P = W: 16-byte pieces of the stream are 16-byte
@@ -1920,10 +1922,11 @@ bool octets_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
   return (src_runs && full_side(T, D.fanout, w)) || (dst_runs && full_side(S, D.dst_ref_begin, w));
 }
 
-// Whether a descriptor is a band window_narrow moves (a WINDOW band more than
-// 16 bytes wide whose segments are all packed, row stride = width, at most 64 a
-// side, with its rows per tile within kNarrowWindowBytes at the band's pitch):
-// 0 no, 1 with dword segments only, 2 with segments of other classes too.
+// Whether a descriptor is a band window_narrow moves (a WINDOW band whose
+// segments are all packed, row stride = width, at most 64 a side, with its rows
+// per tile within kNarrowWindowBytes at the band's pitch; a band of at most 16
+// bytes only as below): 0 no, 1 with dword segments only, 2 with segments of
+// other classes too.
 int narrow_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
   const uint32_t w = D.run_bytes;
   if (D.mode != RESHARD_DESC_WINDOW || w == 0 || w > rs::kWindowBytes) return 0;
