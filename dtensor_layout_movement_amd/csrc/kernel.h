@@ -52,10 +52,12 @@ struct TileStride {
 // Variant `kind` over workgroups [0, n_wg) on `stream`, as one launch, or as
 // several back-to-back launches of at most kMaxLaunchBlocks workgroups each
 // when n_wg is larger.  Shard pointers come from `karg` when `table` is NULL,
-// else from the device table.  Returns the first launch error.
+// else from the device table.  The narrow-band variants take `lds_bytes` of
+// dynamic LDS for their window (the largest of the launch's bands).
+// Returns the first launch error.
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,
                        uint32_t n_desc, const uint32_t* tile_begin, const uint32_t* refs,
                        const reshard_segment_t* segs, const void* const* table, const KargPtrs& karg,
-                       uint32_t n_tiles, uint32_t per_xcd, uint32_t flags, TileStride stride);
+                       uint32_t n_tiles, uint32_t per_xcd, uint32_t flags, TileStride stride, uint32_t lds_bytes);
 
 }  // namespace rs

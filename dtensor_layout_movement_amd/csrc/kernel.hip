@@ -526,14 +526,8 @@ using rs::narrow_pitch;
 constexpr uint32_t kNarrowWindowWords = kNarrowWindowBytes / 4;
 constexpr int kNarrowBatch = 4;  // dword pieces per lane with loads in flight together
 constexpr int kBytesBatch = 2;   // other pieces
-constexpr uint32_t kSegDwords = 0, kSegWhole = 1, kSegRows = 2, kSegPieces = 3, kSegBytes = 4;
-
-__host__ __device__ __forceinline__ uint32_t narrow_class(uint32_t wb, uint32_t cb, uint32_t P, uint32_t W) {
-  if (P % 4 == 0 && wb % 4 == 0 && cb % 4 == 0) return kSegDwords;
-  if (cb == 0 && wb == W && P == W) return kSegWhole;
-  if (wb > 16) return kSegPieces;
-  return wb <= 2 || wb == 4 || wb == 8 || wb == 16 ? kSegRows : kSegBytes;
-}
+// (the segment classes kSeg* and narrow_class sit with the planner, which
+// checks and sizes the bands)
 
 // 2^32 / d rounded up, for div_small by d (its unit: dwords for a dword segment,
 // bytes otherwise); 0 for d = 1.
@@ -1184,18 +1178,11 @@ __device__ __forceinline__ uint32_t lane_xor(uint32_t v) {
   else return uint32_t(__builtin_amdgcn_ds_swizzle(int(v), 0x1F | (X << 10)));
 }
 
-// Whether segments [0, n) of a band are K packed rw-byte column runs in column
-// order (run s at column rw * s) with one fan-out, or one packed run of the
-// whole row of w bytes.  Host-side checks: in a plan that runs a band kernel
-// every descriptor passed them, so on the device a side's segment count tells
-// the two apart (K segments: runs, one: whole rows).
-inline bool runs_side(const reshard_segment_t* S, uint32_t n, uint32_t k, uint32_t rw) {
-  if (n != k) return false;
-  for (uint32_t s = 0; s < n; ++s)
-    if (S[s].width != rw || uint64_t(S[s].row_stride) != rw || S[s].col != rw * s || S[s].fanout != S[0].fanout)
-      return false;
-  return true;
-}
+// Whether segments [0, n) of a band side are one packed run of the whole row
+// of w bytes (runs_side, with the planner, tells K packed column runs).
+// Host-side checks: in a plan that runs a band kernel every descriptor passed
+// them, so on the device a side's segment count tells the two apart (K
+// segments: runs, one: whole rows).
 inline bool full_side(const reshard_segment_t* S, uint32_t n, uint32_t w) {
   return n == 1 && S[0].width == w && uint64_t(S[0].row_stride) == w;
 }
@@ -1761,7 +1748,8 @@ __global__ __launch_bounds__(kBlock) void reshard_copy_kernel(
     return;
   }
   if constexpr (kKind == kKindNarrow || kKind == kKindNarrowBytes) {
-    __shared__ uint32_t narrow_window[kNarrowWindowWords];
+    // the window: dynamic LDS, as large as the launch's largest band needs
+    extern __shared__ __attribute__((aligned(16))) uint32_t narrow_window[];
     const Shards<kKarg> wsh{table, &karg, refs};
     window_narrow<kKind == kKindNarrowBytes>(D, segs, refs, wsh, t - tile_begin[lo], narrow_window);
     return;
@@ -1860,10 +1848,10 @@ template <bool kKarg, int kVariant>
 hipError_t launch_kind(uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
                        const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
                        const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
-                       uint32_t flags, TileStride stride) {
+                       uint32_t flags, TileStride stride, uint32_t lds_bytes) {
   for (uint32_t base = 0; base < n_wg; base += kMaxLaunchBlocks) {
     const uint32_t grid = n_wg - base < kMaxLaunchBlocks ? n_wg - base : kMaxLaunchBlocks;
-    hipLaunchKernelGGL((reshard_copy_kernel<kKarg, kVariant>), dim3(grid), dim3(kBlock), 0, stream, descs,
+    hipLaunchKernelGGL((reshard_copy_kernel<kKarg, kVariant>), dim3(grid), dim3(kBlock), lds_bytes, stream, descs,
                        n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags, base, stride);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -1875,11 +1863,11 @@ template <bool kKarg>
 hipError_t launch(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs, uint32_t n_desc,
                   const uint32_t* tile_begin, const uint32_t* refs, const reshard_segment_t* segs,
                   const void* const* table, const KargPtrs& karg, uint32_t n_tiles, uint32_t per_xcd,
-                  uint32_t flags, TileStride stride) {
+                  uint32_t flags, TileStride stride, uint32_t lds_bytes) {
   const bool aligned = (flags & kAllAligned16) != 0;
 #define RS_LAUNCH(V) \
   launch_kind<kKarg, V>(n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd, flags, \
-                        stride)
+                        stride, (V) == kKindNarrow || (V) == kKindNarrowBytes ? lds_bytes : 0u)
   switch (kind) {
     case kKindItems16:  // (an aligned-only build of this one measured slower on long copies)
       return RS_LAUNCH(kKindItems16);
@@ -1922,40 +1910,12 @@ bool octets_band(const reshard_descriptor_t& D, const std::vector<reshard_segmen
   return (src_runs && full_side(T, D.fanout, w)) || (dst_runs && full_side(S, D.dst_ref_begin, w));
 }
 
-// Whether a descriptor is a band window_narrow moves (a WINDOW band whose
-// segments are all packed, row stride = width, at most 64 a side, with its rows
-// per tile within kNarrowWindowBytes at the band's pitch; a band of at most 16
-// bytes only as below): 0 no, 1 with dword segments only, 2 with segments of
-// other classes too.
+// Whether a descriptor is a band window_narrow moves (rs::narrow_band on its
+// segments): 0 no, 1 with dword segments only, 2 with segments of other classes.
 int narrow_band(const reshard_descriptor_t& D, const std::vector<reshard_segment_t>& segs) {
-  const uint32_t w = D.run_bytes;
-  if (D.mode != RESHARD_DESC_WINDOW || w == 0 || w > rs::kWindowBytes) return 0;
-  const uint32_t P = narrow_pitch(w);
-  if (uint64_t(D.extent[1]) * P > kNarrowWindowBytes) return 0;
-  if (D.dst_ref_begin > 64 || D.fanout > 64) return 0;  // one segment per lane
+  if (D.mode != RESHARD_DESC_WINDOW) return 0;
   const reshard_segment_t* S = segs.data() + D.src_ptr;
-  int kind = 1;
-  bool thin = false;
-  for (uint32_t i = 0; i < D.dst_ref_begin + D.fanout; ++i) {
-    const reshard_segment_t& x = S[i];
-    if (x.width == 0 || uint64_t(x.row_stride) != x.width || uint64_t(x.col) + x.width > w) return 0;
-    if (narrow_class(x.width, x.col, P, w) != kSegDwords) kind = 2;
-    thin |= x.width <= 2;
-  }
-  // A band of at most 16 bytes (the row mode's) only with a 1- or 2-byte
-  // segment, or with dword segments only and rows of an odd number of dwords
-  // (12 bytes: the window's rows then sit back to back and whole rows move as
-  // 16-byte pieces); and not a 16-byte band with four 4-byte or eight 2-byte
-  // column runs on one side (the quad and octet exchanges).  The row mode
-  // measured faster on 8- and 16-byte rows of dword segments.
-  if (w <= uint32_t(rs::kRowModeBytes)) {
-    const reshard_segment_t* T = S + D.dst_ref_begin;
-    if (w == uint32_t(rs::kRowModeBytes) && (runs_side(S, D.dst_ref_begin, 4, 4) || runs_side(T, D.fanout, 4, 4) ||
-                                             runs_side(S, D.dst_ref_begin, 8, 2) || runs_side(T, D.fanout, 8, 2)))
-      return 0;
-    if (!thin && (kind != 1 || P != w)) return 0;
-  }
-  return kind;
+  return rs::narrow_band(D.run_bytes, D.extent[1], S, D.dst_ref_begin, S + D.dst_ref_begin, D.fanout);
 }
 
 }  // namespace
@@ -1990,12 +1950,12 @@ int kernel_kind(const std::vector<reshard_descriptor_t>& descs, const std::vecto
 hipError_t launch_copy(int kind, uint32_t n_wg, hipStream_t stream, const reshard_descriptor_t* descs,
                        uint32_t n_desc, const uint32_t* tile_begin, const uint32_t* refs,
                        const reshard_segment_t* segs, const void* const* table, const KargPtrs& karg,
-                       uint32_t n_tiles, uint32_t per_xcd, uint32_t flags, TileStride stride) {
+                       uint32_t n_tiles, uint32_t per_xcd, uint32_t flags, TileStride stride, uint32_t lds_bytes) {
   if (table)
     return launch<false>(kind, n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles,
-                         per_xcd, flags, stride);
+                         per_xcd, flags, stride, lds_bytes);
   return launch<true>(kind, n_wg, stream, descs, n_desc, tile_begin, refs, segs, table, karg, n_tiles, per_xcd,
-                      flags, stride);
+                      flags, stride, lds_bytes);
 }
 
 }  // namespace rs

@@ -3,10 +3,12 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <limits>
 #include <chrono>
 #include <cstring>
 #include <map>
 #include <unordered_map>
+#include <utility>
 
 namespace rs {
 
@@ -555,6 +557,15 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
                             : int64_t(kTileThreads) * (quad ? kQuadRowsPerLane : kRowsPerLane);
     if (width <= kRowModeBytes && thin && !quad)
       while (rows_per_tile * narrow_pitch(uint32_t(width)) > int64_t(kNarrowWindowBytes)) rows_per_tile /= 2;
+    // a narrow band with small destination pieces or short tiles: twice the rows
+    if (narrow_band(uint32_t(width), uint64_t(rows_per_tile), b.src.data(), uint32_t(b.src.size()), b.dst.data(),
+                    uint32_t(b.dst.size()))) {
+      int64_t smallest = std::numeric_limits<int64_t>::max();
+      for (const auto& x : b.dst) smallest = std::min<int64_t>(smallest, rows_per_tile * int64_t(x.width));
+      if ((smallest < kNarrowSmallPiece || rows_per_tile < kNarrowShortTile) &&
+          2 * rows_per_tile * narrow_pitch(uint32_t(width)) <= int64_t(kNarrowBigWindowBytes))
+        rows_per_tile *= 2;
+    }
     b.d.extent[1] = uint32_t(rows_per_tile);
     b.d.extent[2] = 1;
     b.d.piece = uint32_t(pc0);
@@ -1079,6 +1090,30 @@ int64_t partial_index(const Layout& L, int64_t rank) {
   for (int m = 0; m < L.mesh_ndim; ++m)
     if (L.place[m] == RESHARD_PARTIAL) q = q * L.mesh[m] + coord[m];
   return q;
+}
+
+int narrow_band(uint32_t W, uint64_t rows_per_tile, const reshard_segment_t* src, uint32_t ns,
+                const reshard_segment_t* dst, uint32_t nd) {
+  if (W == 0 || W > kWindowBytes || ns > 64 || nd > 64) return 0;  // one segment per lane
+  const uint32_t P = narrow_pitch(W);
+  if (rows_per_tile * P > kNarrowBigWindowBytes) return 0;
+  int kind = 1;
+  bool thin = false;
+  for (const auto& side : {std::make_pair(src, ns), std::make_pair(dst, nd)})
+    for (uint32_t i = 0; i < side.second; ++i) {
+      const reshard_segment_t& x = side.first[i];
+      if (x.width == 0 || uint64_t(x.row_stride) != x.width || uint64_t(x.col) + x.width > W) return 0;
+      if (narrow_class(x.width, x.col, P, W) != kSegDwords) kind = 2;
+      thin |= x.width <= 2;
+    }
+  // the row mode measured faster on 8- and 16-byte rows of dword segments
+  if (W <= uint32_t(kRowModeBytes)) {
+    if (W == uint32_t(kRowModeBytes) &&
+        (runs_side(src, ns, 4, 4) || runs_side(dst, nd, 4, 4) || runs_side(src, ns, 8, 2) || runs_side(dst, nd, 8, 2)))
+      return 0;
+    if (!thin && (kind != 1 || P != W)) return 0;
+  }
+  return kind;
 }
 
 Runs shard_runs(const Layout& L, int64_t rank, int dim) {

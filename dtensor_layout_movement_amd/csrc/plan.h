@@ -138,6 +138,46 @@ constexpr uint32_t kQuadRowsPerLane = 2;
 // so does one of 12-byte rows of dword segments.
 constexpr uint32_t kNarrowWindowBytes = 18432;
 constexpr uint32_t narrow_pitch(uint32_t W) { return W % 4 ? W : 4 * ((W / 4) | 1u); }
+// A narrow band whose destination pieces per tile would be small (under
+// kNarrowSmallPiece bytes in some destination segment) or whose tiles would be
+// short (under kNarrowShortTile rows) takes twice the rows, in a window of up
+// to kNarrowBigWindowBytes; such bands run in launches of their own, with half
+// as many workgroups per CU.
+constexpr uint32_t kNarrowBigWindowBytes = 2 * kNarrowWindowBytes;
+constexpr int64_t kNarrowSmallPiece = 1024;
+constexpr int64_t kNarrowShortTile = 64;
+
+// How the narrow-band kernel moves a segment wb bytes wide at window column cb
+// of a band W bytes wide at pitch P (see the kernel).
+enum NarrowClass : uint32_t { kSegDwords = 0, kSegWhole = 1, kSegRows = 2, kSegPieces = 3, kSegBytes = 4 };
+constexpr uint32_t narrow_class(uint32_t wb, uint32_t cb, uint32_t P, uint32_t W) {
+  return P % 4 == 0 && wb % 4 == 0 && cb % 4 == 0 ? kSegDwords
+         : cb == 0 && wb == W && P == W          ? kSegWhole
+         : wb > 16                               ? kSegPieces
+         : wb <= 2 || wb == 4 || wb == 8 || wb == 16 ? kSegRows
+                                                     : kSegBytes;
+}
+
+// Whether segments [0, n) of a band side are k packed rw-byte column runs in
+// column order (run s at column rw * s) with one fan-out.
+inline bool runs_side(const reshard_segment_t* S, uint32_t n, uint32_t k, uint32_t rw) {
+  if (n != k) return false;
+  for (uint32_t s = 0; s < n; ++s)
+    if (S[s].width != rw || uint64_t(S[s].row_stride) != rw || S[s].col != rw * s || S[s].fanout != S[0].fanout)
+      return false;
+  return true;
+}
+
+// Whether a WINDOW band (run_bytes W wide, `rows_per_tile` rows a tile, source
+// segments src[0, ns), destination segments dst[0, nd)) is one the narrow-band
+// kernel builds move: 0 no, 1 with dword segments only, 2 with segments of
+// other classes too.  Every segment packed (row stride = width), at most 64 a
+// side, the window (rows_per_tile rows at the band's pitch) within
+// kNarrowBigWindowBytes; a band of at most kRowModeBytes only with a segment of
+// one or two bytes, or of 12-byte rows of dword segments, and not one with four
+// 4-byte or eight 2-byte column runs on a side (the row mode's exchanges).
+int narrow_band(uint32_t W, uint64_t rows_per_tile, const reshard_segment_t* src, uint32_t ns,
+                const reshard_segment_t* dst, uint32_t nd);
 // Cache line of the L2: a band whose tiles would start off the line grid in
 // its segments gives up to kLineBytes / row_stride rows to a head band of its
 // own, so that the tiles after it start on the grid (destination lines first).

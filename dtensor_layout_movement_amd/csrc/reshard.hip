@@ -53,6 +53,7 @@ struct reshard_plan_s {
     uint32_t per_xcd = 0;  // blocks per XCD, a multiple of rs::kXcdGroup (0: one block per tile)
     uint32_t n_wg = 0;     // grid: rs::kXcds * per_xcd blocks (surplus ones exit), else n_tiles
     rs::TileStride stride; // gather-rows launches whose bands all span stride.tiles tiles
+    uint32_t lds_bytes = 0;  // narrow-band launches: the window of their largest band (dynamic LDS)
     size_t desc_off = 0;   // the group's descriptors in the image
     size_t tb_off = 0;     // its first tile of each, from 0; n_desc + 1 entries
   };
@@ -83,6 +84,7 @@ namespace {
 // Descriptors that run in one launch, in plan order, and their tiles.
 struct Group {
   int kind = 0;
+  bool big = false;  // narrow bands whose window exceeds rs::kNarrowWindowBytes
   std::vector<uint32_t> descs;
   uint64_t tiles = 0;
 
@@ -100,8 +102,13 @@ struct Group {
 // a plan that mixes them would run everything slower.  Instead the descriptors
 // that are not bands share one launch (the item, chunk or copy build already
 // covers any mix of them), and each band kind runs in a launch of its own
-// build; bands that no special build moves share the general one.  A plan with
-// only one of these groups runs its descriptors in plan order.
+// build; bands that no special build moves share the general one.  Narrow
+// bands with the larger window (rs::kNarrowBigWindowBytes) run apart from those
+// with the usual one, since the window sets how many workgroups share a CU.  A
+// plan with only one of these groups runs its descriptors in plan order.
+// LDS bytes of a narrow band's window: its rows per tile at its pitch.
+uint32_t narrow_window_bytes(const reshard_descriptor_t& D) { return D.extent[1] * rs::narrow_pitch(D.run_bytes); }
+
 std::vector<Group> launch_groups(const rs::HostPlan& H) {
   Group rows;                 // descriptors that are not bands
   std::vector<Group> bands;   // bands by kind, in order of first appearance
@@ -114,8 +121,9 @@ std::vector<Group> launch_groups(const rs::HostPlan& H) {
     }
     one[0] = H.descs[i];
     const int kind = rs::kernel_kind(one, H.segs);
-    auto g = std::find_if(bands.begin(), bands.end(), [&](const Group& x) { return x.kind == kind; });
-    if (g == bands.end()) g = bands.insert(bands.end(), Group{kind, {}, 0});
+    const bool big = rs::kernel_kind_narrow(kind) && narrow_window_bytes(H.descs[i]) > rs::kNarrowWindowBytes;
+    auto g = std::find_if(bands.begin(), bands.end(), [&](const Group& x) { return x.kind == kind && x.big == big; });
+    if (g == bands.end()) g = bands.insert(bands.end(), Group{kind, big, {}, 0});
     g->add(i, H);
   }
   std::vector<Group> out;
@@ -154,6 +162,8 @@ void build_image_locked(reshard_plan_s* p) {
     L.kind = g.kind;
     L.n_desc = uint32_t(g.descs.size());
     L.n_tiles = uint32_t(g.tiles);
+    if (rs::kernel_kind_narrow(g.kind))
+      for (const uint32_t i : g.descs) L.lds_bytes = std::max(L.lds_bytes, narrow_window_bytes(H.descs[i]));
     // Gather-rows bands of (nearly) one size take a common tile stride, so that
     // a workgroup finds its band by a division instead of a table load: the
     // shorter bands leave their last tiles idle (at most 1/16 more tiles).
@@ -282,7 +292,7 @@ hipError_t launch_groups_at(const reshard_plan_s* p, const uint8_t* base, const 
     const hipError_t e =
         rs::launch_copy(L.kind, L.n_wg, stream, reinterpret_cast<const reshard_descriptor_t*>(base + L.desc_off),
                         L.n_desc, reinterpret_cast<const uint32_t*>(base + L.tb_off), refs, segs, table, karg,
-                        L.n_tiles, L.per_xcd, flags, L.stride);
+                        L.n_tiles, L.per_xcd, flags, L.stride, L.lds_bytes);
     if (e != hipSuccess) return e;
   }
   return hipSuccess;

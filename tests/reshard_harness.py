@@ -377,6 +377,7 @@ def _run_reduce(D, refs, srcs_flat, dsts_flat):
 
 
 NARROW_WINDOW_BYTES = 18432
+NARROW_BIG_WINDOW_BYTES = 36864  # bands with small destination pieces or short tiles: twice the rows
 
 
 def narrow_pitch(W):
@@ -413,7 +414,7 @@ def is_narrow_band(D, segs):
     W = D["run_bytes"]
     if D["mode"] != R.DESC_WINDOW or W == 0 or W > 16384:
         return False
-    if D["extent"][1] * narrow_pitch(W) > NARROW_WINDOW_BYTES or D["dst_ref_begin"] > 64 or D["fanout"] > 64:
+    if D["extent"][1] * narrow_pitch(W) > NARROW_BIG_WINDOW_BYTES or D["dst_ref_begin"] > 64 or D["fanout"] > 64:
         return False
     srcs = segs[D["src_ptr"]:D["src_ptr"] + D["dst_ref_begin"]]
     dsts = segs[D["src_ptr"] + D["dst_ref_begin"]:D["src_ptr"] + D["dst_ref_begin"] + D["fanout"]]
@@ -595,7 +596,7 @@ def _run_narrow(D, segs, refs, srcs_flat, dsts_flat):
     writes every destination stream byte once."""
     rows, per_tile, W = D["extent"][0], D["extent"][1], D["run_bytes"]
     P = narrow_pitch(W)
-    assert per_tile * P <= NARROW_WINDOW_BYTES
+    assert per_tile * P <= NARROW_BIG_WINDOW_BYTES
     srcs = segs[D["src_ptr"]:D["src_ptr"] + D["dst_ref_begin"]]
     dsts = segs[D["src_ptr"] + D["dst_ref_begin"]:D["src_ptr"] + D["dst_ref_begin"] + D["fanout"]]
     for tile in range(-(-rows // per_tile)):
@@ -774,7 +775,10 @@ def assert_descriptors_in_bounds(plan: Plan):
         if D["mode"] == R.DESC_WINDOW:
             rows, per_tile, pitch, width = ext[0], ext[1], D["row_items"], D["run_bytes"]
             assert rows >= 1 and per_tile >= 1 and pitch % 16 == 0 and pitch >= width
-            assert per_tile * pitch <= 16384 or (width <= 16 and per_tile % 256 == 0)  # LDS window, or row mode
+            # the all-modes LDS window, or the row mode, or a narrow band's window (twice
+            # the rows for small destination pieces)
+            assert (per_tile * pitch <= 16384 or (width <= 16 and per_tile % 256 == 0)
+                    or (is_narrow_band(D, segs) and per_tile * narrow_pitch(width) <= NARROW_BIG_WINDOW_BYTES))
             first = D["src_ptr"]
             for i, sg in enumerate(segs[first:first + D["dst_ref_begin"] + D["fanout"]]):
                 assert sg["col"] + sg["width"] <= width and sg["offset"] >= 0 and sg["row_stride"] >= 0

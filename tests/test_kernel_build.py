@@ -59,12 +59,12 @@ def test_no_scratch(kernel_meta):
 
 
 def test_lds_only_in_the_window_variants(kernel_meta):
-    """Only the all-modes variant (LDS windows) and the narrow-band variants
-    allocate LDS: a private array the compiler moved to LDS (an index it could
-    not resolve) shows up here."""
+    """Only the all-modes variant allocates LDS statically (its 16 KiB window;
+    the narrow-band variants take theirs as dynamic LDS at launch): a private
+    array the compiler moved to LDS (an index it could not resolve) shows up
+    here."""
     for name, meta in kernel_meta.items():
-        want = 16384 if re.search(r"reshard_copy_kernelILb[01]ELi3E", name) else \
-            18432 if re.search(r"reshard_copy_kernelILb[01]ELi1[23]E", name) else 0
+        want = 16384 if re.search(r"reshard_copy_kernelILb[01]ELi3E", name) else 0
         assert meta["lds"] == want, (name, meta)
 
 
