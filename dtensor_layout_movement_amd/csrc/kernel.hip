@@ -507,8 +507,9 @@ __device__ __forceinline__ void store_bytes(uintptr_t d, u32x4 v, uint32_t n) {
 // bytes: an odd number of dwords when the band width W is a multiple of 4 (lanes
 // that touch one column of consecutive rows, or consecutive dwords of one row,
 // then hit distinct LDS banks), W otherwise (a segment of whole rows is then the
-// window itself).  Its rows per tile are the LDS window's, and
-// kNarrowWindowBytes bounds the window (checked on the host).  Each segment
+// window itself).  The window is dynamic LDS, sized at launch for the launch's
+// largest band: kNarrowWindowBytes, or kNarrowBigWindowBytes for bands with
+// small destination pieces (checked on the host).  Each segment
 // moves in one of five ways:
 //   dwords  P, column and width multiples of 4: a lane moves one dword of the
 //           stream, or four where they stay together in the window;

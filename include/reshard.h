@@ -185,7 +185,10 @@ typedef struct reshard_piece {
  *                            segments are all packed (row stride = width) moves
  *                            in a narrow-band kernel build, each segment's rows
  *                            as one contiguous stream on the global side, with
- *                            `extent[1]` rows per tile within an 18 KiB window.
+ *                            `extent[1]` rows per tile within an 18 KiB window
+ *                            (36 KiB when a destination segment would get less
+ *                            than 1 KiB a tile or a tile fewer than 64 rows:
+ *                            then twice the rows, in a launch of its own).
  *                            Other bands at most 16 bytes wide skip LDS: one
  *                            lane per row assembles the row in registers,
  *                            `extent[1]` = 1024 rows per tile (512 when one
