@@ -104,6 +104,19 @@ def test_noalloc_refuses_a_plan_beyond_the_scratch_array():
         assert int(buf[4096 * n_t:].sum().item()) == 0  # nothing was written
 
 
+def test_noalloc_narrow_band_windows():
+    """Narrow bands in launches of both window sizes (dynamic LDS sized per
+    launch): 4-byte shards of 64-byte rows (the usual window) with single u8
+    columns of 16-byte rows (twice the rows), then a smaller plan of 2-byte
+    shards of 64-byte rows (twice the rows)."""
+    mix = [W.narrow_columns_64b_tp16(2048).tensors[0],
+           T("u8_cols", (4099, 16), torch.uint8, (2,), (0,), (16,), (1,))]
+    st = run_both(mix, 5)
+    assert st["n_launches"] >= 2
+    small = [T("bf16_cols", (1031, 32), torch.bfloat16, (2,), (0,), (32,), (1,))]
+    run_both(small, 6)
+
+
 def test_noalloc_then_execute_same_plan_repeatedly():
     """The two entry points alternate on one plan and one stream; every result
     is compared with the oracle."""
