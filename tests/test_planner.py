@@ -17,7 +17,7 @@ import dtensor_layout_movement_amd as R
 import oracle_pins as P
 from dtensor_layout_movement_amd import workloads as W
 from reshard_harness import (Plan, apply_pieces, assert_boxes_agree, assert_descriptors_in_bounds,
-                             box_shape, is_narrow_band, lib_runs, magic_div,
+                             box_shape, is_narrow_band, lib_runs, magic_div, narrow_pitch,
                              oracle_dsts, run_descriptors, sources_for)
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
@@ -808,6 +808,28 @@ def test_descriptor_modes():
         assert modes([small[name]]) == {(R.DESC_DST_CHUNKS, 4 if small[name].dtype == torch.float32 else 2)}, name
     # a 4-byte piece in 16804-byte rows: too wide for a window, so per piece
     assert {m for m, _ in modes([small["narrow_wide_rows"]])} == {R.DESC_DST_CHUNKS, R.DESC_ITEMS}
+
+
+def test_narrow_band_window_per_band():
+    """Narrow bands take twice the rows per tile (a window of up to 36 KiB)
+    when a destination segment would get less than 1 KiB a tile or a tile
+    fewer than 64 rows, and keep the usual rows otherwise; every band stays a
+    narrow band."""
+    cases = [
+        (T("u8_16", (4099, 16), torch.uint8, (2,), (0,), (16,), (1,)), 1024),     # 1-byte columns, 512 -> 1024
+        (T("bf16_64", (1031, 32), torch.bfloat16, (2,), (0,), (32,), (1,)), 512),  # 2-byte columns, 256 -> 512
+        (T("rows512", (301, 256), torch.bfloat16, (2,), (0,), (8,), (1,)), 64),   # 32-row tiles -> 64
+        (T("bf16_32", (2053, 16), torch.bfloat16, (2,), (0,), (16,), (1,)), 512),  # 1 KiB pieces: as planned
+        (W.narrow_columns_64b_tp16(2048).tensors[0], 256),                         # 4-byte columns, 1 KiB pieces
+        (W.narrow_columns_tp8(4096).tensors[0], 512),
+    ]
+    for spec, rows in cases:
+        with Plan([spec]) as plan:
+            descs, _ = R.reshard_plan_descriptors(plan.handle)
+            segs = R.reshard_plan_segments(plan.handle)
+        assert {d["extent"][1] for d in descs} == {rows}, spec.name
+        assert all(is_narrow_band(d, segs) for d in descs), spec.name
+        assert all(d["extent"][1] * narrow_pitch(d["run_bytes"]) <= 36864 for d in descs), spec.name
 
 
 def test_row_mode_tile_rows():
