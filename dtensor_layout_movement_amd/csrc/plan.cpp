@@ -454,7 +454,7 @@ bool view_2d(const HostPlan& P, int t, size_t pc0, size_t pc1, View2d* v) {
 // box starts or ends; each band lists the pieces that cover it as source
 // segments (merged where one shard continues across pieces) and the
 // destination boxes that cover it as destination segments.
-bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
+bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v, std::vector<int64_t>& load) {
   const int nd = P->src[t].ndim;
   const int64_t es = P->src[t].elem_size;
   const int64_t width = v.cols * es;
@@ -463,10 +463,28 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
   const int64_t window_rows = int64_t(kWindowBytes) / pitch;  // rows per tile of an LDS window
   auto rlo = [&](const Box& b) { return b.lo[0] * v.row_mult; };
   auto rhi = [&](const Box& b) { return b.hi[0] * v.row_mult; };
+  // A replicated source box is read in k row parts, part j from its j-th
+  // replica: a band then reads whole source rows from one replica (its
+  // segments of that box merge into one packed run), and the replicas share
+  // the reads evenly.
+  auto part_cut = [&](const Group& g, int64_t j) {
+    const int64_t k = int64_t(g.ranks.size());
+    return rlo(g.box) + (rhi(g.box) - rlo(g.box)) * j / k;
+  };
+  auto replica = [&](const Group& g, int64_t row) {
+    int64_t j = int64_t(g.ranks.size()) - 1;
+    while (j > 0 && part_cut(g, j) > row) --j;
+    return g.ranks[size_t(j)];
+  };
   std::vector<int64_t> cuts;
   for (size_t i = pc0; i < pc1; ++i) {
     cuts.push_back(rlo(P->pieces[i].box));
     cuts.push_back(rhi(P->pieces[i].box));
+    const Group& sg = P->src_groups[P->pieces[i].src_group];
+    for (int64_t j = 1; j < int64_t(sg.ranks.size()); ++j) {
+      const int64_t cut = part_cut(sg, j);
+      if (cut > rlo(P->pieces[i].box) && cut < rhi(P->pieces[i].box)) cuts.push_back(cut);
+    }
   }
   std::sort(cuts.begin(), cuts.end());
   cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
@@ -491,7 +509,7 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
       s.row_stride = s_cols * es;
       s.col = uint32_t(pc.box.lo[nd - 1] * es);
       s.width = uint32_t((pc.box.hi[nd - 1] - pc.box.lo[nd - 1]) * es);
-      s.ptr = uint32_t(P->src_base[t] + pc.src_rank);
+      s.ptr = uint32_t(P->src_base[t] + replica(P->src_groups[pc.src_group], ra));
       s.fanout = 0;
       b.src.push_back(s);
       if (std::find(dst_seen.begin(), dst_seen.end(), pc.dst_group) == dst_seen.end()) {
@@ -621,6 +639,10 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v) {
     }
     P->descs.push_back(b.d);
   }
+  // source reads by the bands in place of the pieces' own replica choice
+  for (size_t i = pc0; i < pc1; ++i) load[size_t(P->src_base[t] + P->pieces[i].src_rank)] -= P->pieces[i].bytes;
+  for (const Pending& b : bands)
+    for (const auto& s : b.src) load[s.ptr] += int64_t(b.d.extent[0]) * s.width;
   return true;
 }
 
@@ -642,10 +664,28 @@ bool emit_gather_rows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& 
     const Box& db = P->dst_groups[P->pieces[i].dst_group].box;
     if (db.lo[nd - 1] != 0 || db.hi[nd - 1] != v.cols) return false;  // destination rows must be whole
   }
+  // A replicated source box is read in k row parts, part j from its j-th
+  // replica: a band then reads whole source rows from one replica (its
+  // segments of that box merge into one packed run), and the replicas share
+  // the reads evenly.
+  auto part_cut = [&](const Group& g, int64_t j) {
+    const int64_t k = int64_t(g.ranks.size());
+    return rlo(g.box) + (rhi(g.box) - rlo(g.box)) * j / k;
+  };
+  auto replica = [&](const Group& g, int64_t row) {
+    int64_t j = int64_t(g.ranks.size()) - 1;
+    while (j > 0 && part_cut(g, j) > row) --j;
+    return g.ranks[size_t(j)];
+  };
   std::vector<int64_t> cuts;
   for (size_t i = pc0; i < pc1; ++i) {
     cuts.push_back(rlo(P->pieces[i].box));
     cuts.push_back(rhi(P->pieces[i].box));
+    const Group& sg = P->src_groups[P->pieces[i].src_group];
+    for (int64_t j = 1; j < int64_t(sg.ranks.size()); ++j) {
+      const int64_t cut = part_cut(sg, j);
+      if (cut > rlo(P->pieces[i].box) && cut < rhi(P->pieces[i].box)) cuts.push_back(cut);
+    }
   }
   std::sort(cuts.begin(), cuts.end());
   cuts.erase(std::unique(cuts.begin(), cuts.end()), cuts.end());
@@ -752,7 +792,7 @@ bool emit_gather_rows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& 
 // rows are assembled from wide source column strips that meet off the 16-byte
 // grid (the per-piece path would write the lines where strips meet in part,
 // from two workgroups); per-piece descriptors otherwise.
-void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1) {
+void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1, std::vector<int64_t>& load) {
   if (pc0 == pc1) return;
   const size_t d0 = P->descs.size(), r0 = P->refs.size();
   emit_pieces(P, t, pc0, pc1);
@@ -773,7 +813,7 @@ void emit_tensor(HostPlan* P, int t, size_t pc0, size_t pc1) {
   std::vector<uint32_t> saved_refs(P->refs.begin() + r0, P->refs.end());
   P->descs.resize(d0);
   P->refs.resize(r0);
-  const bool done = narrow ? emit_windows(P, t, pc0, pc1, v) : emit_gather_rows(P, t, pc0, pc1, v);
+  const bool done = narrow ? emit_windows(P, t, pc0, pc1, v, load) : emit_gather_rows(P, t, pc0, pc1, v);
   if (!done) {  // keep the per-piece descriptors
     P->descs.resize(d0);
     P->refs.resize(r0);
@@ -963,7 +1003,7 @@ reshard_status_t plan_runs_tensor(HostPlan* P, int t, std::vector<int64_t>& load
       ++dj[k];
     }
   }
-  emit_tensor(P, t, pc0, P->pieces.size());
+  emit_tensor(P, t, pc0, P->pieces.size(), load);
   return RESHARD_OK;
 }
 
@@ -1297,7 +1337,7 @@ reshard_status_t build_plan(int n, const Layout* const* src, const Layout* const
       });
       if (st != RESHARD_OK) return st;
     }
-    emit_tensor(P, t, pc0, P->pieces.size());
+    emit_tensor(P, t, pc0, P->pieces.size(), load);
   }
   // tiles: each descriptor gets desc_tiles() consecutive tiles
   P->tile_begin.assign(1, 0);

@@ -135,6 +135,9 @@ def small_specs():
         T("bytes_r6_gather", (1031, 12), torch.bfloat16, (4,), (1,), (3,), (0,)),
         T("bytes_u8_r5_gather", (1029, 20), torch.uint8, (4,), (1,), (2,), (0,)),
         T("bytes_u8_r7_rep", (523, 28), torch.uint8, (2,), (0,), (2, 4), (RR, 1)),
+        # replicated sources: each replica reads its own part of the rows
+        T("rep_src_u8", (515, 40), torch.uint8, (3,), (RR,), (5,), (1,)),
+        T("rep_src_bf16_rows", (1027, 24), torch.bfloat16, (2, 3), (RR, 0), (4,), (1,)),
         # 8-byte rows cut into two 4-byte column runs (register row mode)
         T("pairs_gather", (1029, 4), torch.bfloat16, (2,), (1,), (3,), (0,)),
         T("pairs_rep", (517, 2), torch.float32, (3,), (0,), (2, 2), (RR, 1)),
@@ -642,6 +645,33 @@ def test_source_load_per_slot():
         assert load[7] == load[8] == 64 * 64 * 2 // 2
         for i, pc in enumerate(R.reshard_plan_pieces(plan.handle)):
             assert load[[0, 4, 7][pc["tensor"]] + pc["src_rank"]] > 0
+
+
+def test_replicated_source_bands():
+    """A replicated source box is read in row parts, one per replica: every
+    band takes each box's rows from one replica, so a narrow band's sources stay
+    packed (one segment per box and band) and take the narrow path, and the
+    replicas of a box read equal shares to within a row."""
+    cases = {"rep_src": [(0, 2), (1, 3)], "rep_src_u8": [(0, 1, 2)],
+             "rep_src_bf16_rows": [(0, 3), (1, 4), (2, 5)], "narrow_gather_rep": [(j, 4 + j) for j in range(4)]}
+    specs = {s.name: s for s in small_specs()}
+    for name, boxes in cases.items():
+        spec = specs[name]
+        width = spec.shape[-1] * torch.empty((), dtype=spec.dtype).element_size()
+        with Plan([spec]) as plan:
+            descs, _ = R.reshard_plan_descriptors(plan.handle)
+            segs = R.reshard_plan_segments(plan.handle)
+            load = R.reshard_plan_src_load(plan.handle)
+        bands = [D for D in descs if D["mode"] == R.DESC_WINDOW]
+        assert bands, name
+        for D in bands:
+            src = segs[D["src_ptr"]:D["src_ptr"] + D["dst_ref_begin"]]
+            assert len({s["ptr"] for s in src}) == len(src), name  # one replica per box and band
+            if width > 16:
+                assert is_narrow_band(D, segs), name
+        for box in boxes:
+            shares = [load[r] for r in box]
+            assert max(shares) - min(shares) <= width and min(shares) > 0, (name, shares)
 
 
 def rank_loss_sequence(rows=448, cols=320):
