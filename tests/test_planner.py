@@ -93,6 +93,11 @@ def small_specs():
         T("octets_gather", (1041, 8), torch.bfloat16, (8,), (1,), (3,), (0,)),
         T("octets_scatter_rep", (523, 8), torch.float16, (3,), (0,), (2, 8), (RR, 1)),
         T("octets_tiny", (5, 8), torch.bfloat16, (1,), (0,), (8,), (1,)),
+        # single bf16 or fp16 columns of 32-byte rows over sixteen shards
+        # gathered (thin runs on the source side), with destination replicas, tiny
+        T("thin32_gather", (1041, 16), torch.float16, (16,), (1,), (3,), (0,)),
+        T("thin32_gather_rep", (1029, 16), torch.bfloat16, (16,), (1,), (2, 3), (RR, 0)),
+        T("thin32_tiny", (5, 16), torch.bfloat16, (1,), (0,), (16,), (1,)),
         # narrow bands at 2- and 1-byte granularity and past 256 bytes: single
         # bf16 columns of 32- and 64-byte rows (scatter, gather, replicas),
         # ragged 8/8/8/2-byte shards of 26-byte rows (a pitch of one row), 6-,
@@ -850,6 +855,7 @@ def test_narrow_band_window_per_band():
         (T("bf16_64", (1031, 32), torch.bfloat16, (2,), (0,), (32,), (1,)), 512),  # 2-byte columns, 256 -> 512
         (T("rows512", (301, 256), torch.bfloat16, (2,), (0,), (8,), (1,)), 64),   # 32-row tiles -> 64
         (T("bf16_32", (2053, 16), torch.bfloat16, (2,), (0,), (16,), (1,)), 512),  # 1 KiB pieces: as planned
+        (T("bf16_24", (2053, 12), torch.bfloat16, (2,), (0,), (12,), (1,)), 512),
         (W.narrow_columns_64b_tp16(2048).tensors[0], 256),                         # 4-byte columns, 1 KiB pieces
         (W.narrow_columns_tp8(4096).tensors[0], 512),
     ]
@@ -874,7 +880,8 @@ def test_row_mode_tile_rows():
             "runs_f32_cols": 512, "runs64_scatter": 256, "runs64_gather": 256, "runs64_scatter_rep": 256,
             "bands16_scatter": 256, "bands16_gather": 128, "bands16_rep": 128, "bands16_256": 64,
             "runs32_scatter": 512, "runs32_gather": 512, "runs32_scatter_rep": 512,
-            "octets_gather": 512, "octets_scatter_rep": 512, "bands16_96": 170, "bands16_48_gather": 341,
+            "octets_gather": 512, "octets_scatter_rep": 512, "thin32_gather": 512, "thin32_gather_rep": 512,
+            "bytes_r2_in32": 512, "bytes_r2_rep": 512, "bands16_96": 170, "bands16_48_gather": 341,
             "bands16_80_rep": 204}
     for name, rows in want.items():
         with Plan([small[name]]) as plan:
