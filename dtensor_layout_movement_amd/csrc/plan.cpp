@@ -3,7 +3,6 @@
 #include "plan.h"
 
 #include <algorithm>
-#include <limits>
 #include <chrono>
 #include <cstring>
 #include <map>
@@ -578,9 +577,12 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v, s
     // a narrow band with small destination pieces or short tiles: twice the rows
     if (narrow_band(uint32_t(width), uint64_t(rows_per_tile), b.src.data(), uint32_t(b.src.size()), b.dst.data(),
                     uint32_t(b.dst.size()))) {
-      int64_t smallest = std::numeric_limits<int64_t>::max();
-      for (const auto& x : b.dst) smallest = std::min<int64_t>(smallest, rows_per_tile * int64_t(x.width));
-      if ((smallest < kNarrowSmallPiece || rows_per_tile < kNarrowShortTile) &&
+      bool small = rows_per_tile < kNarrowShortTile;
+      for (const auto& x : b.dst) {
+        const int64_t piece = rows_per_tile * int64_t(x.width);
+        small |= piece < kNarrowSmallPiece || (x.width <= 2 && piece == kNarrowSmallPiece);
+      }
+      if (small &&
           2 * rows_per_tile * narrow_pitch(uint32_t(width)) <= int64_t(kNarrowBigWindowBytes))
         rows_per_tile *= 2;
     }

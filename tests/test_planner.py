@@ -847,15 +847,17 @@ def test_descriptor_modes():
 
 def test_narrow_band_window_per_band():
     """Narrow bands take twice the rows per tile (a window of up to 36 KiB)
-    when a destination segment would get less than 1 KiB a tile or a tile
-    fewer than 64 rows, and keep the usual rows otherwise; every band stays a
-    narrow band."""
+    when a destination segment would get less than 1 KiB a tile (at most 1 KiB
+    for a segment of one or two bytes) or a tile fewer than 64 rows, and keep
+    the usual rows otherwise; every band stays a narrow band."""
     cases = [
         (T("u8_16", (4099, 16), torch.uint8, (2,), (0,), (16,), (1,)), 1024),     # 1-byte columns, 512 -> 1024
         (T("bf16_64", (1031, 32), torch.bfloat16, (2,), (0,), (32,), (1,)), 512),  # 2-byte columns, 256 -> 512
         (T("rows512", (301, 256), torch.bfloat16, (2,), (0,), (8,), (1,)), 64),   # 32-row tiles -> 64
-        (T("bf16_32", (2053, 16), torch.bfloat16, (2,), (0,), (16,), (1,)), 512),  # 1 KiB pieces: as planned
-        (T("bf16_24", (2053, 12), torch.bfloat16, (2,), (0,), (12,), (1,)), 512),
+        (T("bf16_32", (2053, 16), torch.bfloat16, (2,), (0,), (16,), (1,)), 1024),  # 1 KiB of a 2-byte column: 512 -> 1024
+        (T("bf16_24", (2053, 12), torch.bfloat16, (2,), (0,), (12,), (1,)), 1024),
+        (T("u8_8", (4099, 8), torch.uint8, (2,), (0,), (8,), (1,)), 2048),        # 1 KiB of a 1-byte column: 1024 -> 2048
+        (T("bf16_8", (4099, 4), torch.bfloat16, (2,), (0,), (4,), (1,)), 1024),   # 2 KiB of a 2-byte column: as planned
         (W.narrow_columns_64b_tp16(2048).tensors[0], 256),                         # 4-byte columns, 1 KiB pieces
         (W.narrow_columns_tp8(4096).tensors[0], 512),
     ]
@@ -881,7 +883,7 @@ def test_row_mode_tile_rows():
             "bands16_scatter": 256, "bands16_gather": 128, "bands16_rep": 128, "bands16_256": 64,
             "runs32_scatter": 512, "runs32_gather": 512, "runs32_scatter_rep": 512,
             "octets_gather": 512, "octets_scatter_rep": 512, "thin32_gather": 512, "thin32_gather_rep": 512,
-            "bytes_r2_in32": 512, "bytes_r2_rep": 512, "bands16_96": 170, "bands16_48_gather": 341,
+            "bytes_r2_in32": 1024, "bytes_r2_rep": 1024, "bands16_96": 170, "bands16_48_gather": 341,
             "bands16_80_rep": 204}
     for name, rows in want.items():
         with Plan([small[name]]) as plan:
