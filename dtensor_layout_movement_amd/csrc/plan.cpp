@@ -580,7 +580,7 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v, s
       bool small = rows_per_tile < kNarrowShortTile;
       for (const auto& x : b.dst) {
         const int64_t piece = rows_per_tile * int64_t(x.width);
-        small |= piece < kNarrowSmallPiece || (x.width <= 2 && piece == kNarrowSmallPiece);
+        small |= piece < kNarrowSmallPiece || x.width <= 2;
       }
       if (small &&
           2 * rows_per_tile * narrow_pitch(uint32_t(width)) <= int64_t(kNarrowBigWindowBytes))

@@ -139,8 +139,9 @@ constexpr uint32_t kQuadRowsPerLane = 2;
 constexpr uint32_t kNarrowWindowBytes = 18432;
 constexpr uint32_t narrow_pitch(uint32_t W) { return W % 4 ? W : 4 * ((W / 4) | 1u); }
 // A narrow band whose destination pieces per tile would be small (under
-// kNarrowSmallPiece bytes in some destination segment, or at most that in one
-// of one or two bytes, whose lanes move eight rows each) or whose tiles would be
+// kNarrowSmallPiece bytes in some destination segment), that has a destination
+// segment of one or two bytes (whose lanes move eight rows each), or whose
+// tiles would be
 // short (under kNarrowShortTile rows) takes twice the rows, in a window of up
 // to kNarrowBigWindowBytes; such bands run in launches of their own, with half
 // as many workgroups per CU.

@@ -847,9 +847,9 @@ def test_descriptor_modes():
 
 def test_narrow_band_window_per_band():
     """Narrow bands take twice the rows per tile (a window of up to 36 KiB)
-    when a destination segment would get less than 1 KiB a tile (at most 1 KiB
-    for a segment of one or two bytes) or a tile fewer than 64 rows, and keep
-    the usual rows otherwise; every band stays a narrow band."""
+    when a destination segment would get less than 1 KiB a tile or is one or
+    two bytes wide, or a tile fewer than 64 rows, and keep the usual rows
+    otherwise; every band but the row-mode one stays a narrow band."""
     cases = [
         (T("u8_16", (4099, 16), torch.uint8, (2,), (0,), (16,), (1,)), 1024),     # 1-byte columns, 512 -> 1024
         (T("bf16_64", (1031, 32), torch.bfloat16, (2,), (0,), (32,), (1,)), 512),  # 2-byte columns, 256 -> 512
@@ -857,7 +857,8 @@ def test_narrow_band_window_per_band():
         (T("bf16_32", (2053, 16), torch.bfloat16, (2,), (0,), (16,), (1,)), 1024),  # 1 KiB of a 2-byte column: 512 -> 1024
         (T("bf16_24", (2053, 12), torch.bfloat16, (2,), (0,), (12,), (1,)), 1024),
         (T("u8_8", (4099, 8), torch.uint8, (2,), (0,), (8,), (1,)), 2048),        # 1 KiB of a 1-byte column: 1024 -> 2048
-        (T("bf16_8", (4099, 4), torch.bfloat16, (2,), (0,), (4,), (1,)), 1024),   # 2 KiB of a 2-byte column: as planned
+        (T("bf16_8", (4099, 4), torch.bfloat16, (2,), (0,), (4,), (1,)), 2048),   # 2 KiB of a 2-byte column: 1024 -> 2048
+        (T("f32_8", (4099, 2), torch.float32, (2,), (0,), (2,), (1,)), 1024),     # 4-byte columns of 8-byte rows: row mode
         (W.narrow_columns_64b_tp16(2048).tensors[0], 256),                         # 4-byte columns, 1 KiB pieces
         (W.narrow_columns_tp8(4096).tensors[0], 512),
     ]
@@ -866,7 +867,7 @@ def test_narrow_band_window_per_band():
             descs, _ = R.reshard_plan_descriptors(plan.handle)
             segs = R.reshard_plan_segments(plan.handle)
         assert {d["extent"][1] for d in descs} == {rows}, spec.name
-        assert all(is_narrow_band(d, segs) for d in descs), spec.name
+        assert all(is_narrow_band(d, segs) == (spec.name != "f32_8") for d in descs), spec.name
         assert all(d["extent"][1] * narrow_pitch(d["run_bytes"]) <= 36864 for d in descs), spec.name
 
 
