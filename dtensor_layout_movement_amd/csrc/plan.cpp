@@ -567,12 +567,14 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v, s
     b.d.extent[0] = uint32_t(rb - ra);
     const bool quad = width == kRowModeBytes && (quad_side(b.src) || quad_side(b.dst) || octet_side(b.src) ||
                                                  octet_side(b.dst));
-    bool thin = false;  // a segment of one or two bytes
+    bool bytewise = false;  // a segment of one or two bytes, or of another width the narrow kernel moves bytewise
     for (const auto* side : {&b.src, &b.dst})
-      for (const auto& x : *side) thin |= x.width <= 2;
+      for (const auto& x : *side)
+        bytewise |= x.width <= 2 || (narrow_class(x.width, x.col, narrow_pitch(uint32_t(width)), uint32_t(width)) ==
+                                         kSegBytes && (side == &b.src || x.width > 4));
     int64_t rows_per_tile = width > kRowModeBytes ? window_rows
                             : int64_t(kTileThreads) * (quad ? kQuadRowsPerLane : kRowsPerLane);
-    if (width <= kRowModeBytes && thin && !quad)
+    if (width <= kRowModeBytes && bytewise && !quad)
       while (rows_per_tile * narrow_pitch(uint32_t(width)) > int64_t(kNarrowWindowBytes)) rows_per_tile /= 2;
     // a narrow band with small destination pieces or short tiles: twice the rows
     if (narrow_band(uint32_t(width), uint64_t(rows_per_tile), b.src.data(), uint32_t(b.src.size()), b.dst.data(),
@@ -1140,20 +1142,23 @@ int narrow_band(uint32_t W, uint64_t rows_per_tile, const reshard_segment_t* src
   const uint32_t P = narrow_pitch(W);
   if (rows_per_tile * P > kNarrowBigWindowBytes) return 0;
   int kind = 1;
-  bool thin = false;
+  bool thin = false, bytes = false;  // bytes: a source segment of the bytes class, or a destination one over 4 bytes
   for (const auto& side : {std::make_pair(src, ns), std::make_pair(dst, nd)})
     for (uint32_t i = 0; i < side.second; ++i) {
       const reshard_segment_t& x = side.first[i];
       if (x.width == 0 || uint64_t(x.row_stride) != x.width || uint64_t(x.col) + x.width > W) return 0;
-      if (narrow_class(x.width, x.col, P, W) != kSegDwords) kind = 2;
+      const uint32_t cls = narrow_class(x.width, x.col, P, W);
+      if (cls != kSegDwords) kind = 2;
       thin |= x.width <= 2;
+      bytes |= cls == kSegBytes && (side.first == src || x.width > 4);
     }
-  // the row mode measured faster on 8- and 16-byte rows of dword segments
+  // the row mode measured faster on 8- and 16-byte rows of dword segments, and
+  // on rows scattered into 3-byte shards
   if (W <= uint32_t(kRowModeBytes)) {
     if (W == uint32_t(kRowModeBytes) &&
         (runs_side(src, ns, 4, 4) || runs_side(dst, nd, 4, 4) || runs_side(src, ns, 8, 2) || runs_side(dst, nd, 8, 2)))
       return 0;
-    if (!thin && (kind != 1 || P != W)) return 0;
+    if (!thin && !bytes && (kind != 1 || P != W)) return 0;
   }
   return kind;
 }

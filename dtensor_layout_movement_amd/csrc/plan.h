@@ -176,7 +176,8 @@ inline bool runs_side(const reshard_segment_t* S, uint32_t n, uint32_t k, uint32
 // other classes too.  Every segment packed (row stride = width), at most 64 a
 // side, the window (rows_per_tile rows at the band's pitch) within
 // kNarrowBigWindowBytes; a band of at most kRowModeBytes only with a segment of
-// one or two bytes, or of 12-byte rows of dword segments, and not one with four
+// one or two bytes, a source segment of the bytes class or a destination one
+// over 4 bytes, or of 12-byte rows of dword segments, and not one with four
 // 4-byte or eight 2-byte column runs on a side (the row mode's exchanges).
 int narrow_band(uint32_t W, uint64_t rows_per_tile, const reshard_segment_t* src, uint32_t ns,
                 const reshard_segment_t* dst, uint32_t nd);

@@ -409,7 +409,8 @@ def _exchange_band(D, srcs, dsts):
 def is_narrow_band(D, segs):
     """The host check that sends a WINDOW band to the narrow-band kernel: packed
     segments, at most 64 a side, the window within its LDS; a band of at most 16
-    bytes only with a segment of one or two bytes, or of 12-byte rows of dword
+    bytes only with a segment of one or two bytes, a source segment of the bytes
+    class or a destination one over 4 bytes, or of 12-byte rows of dword
     segments, and not one of the quad or octet exchanges."""
     W = D["run_bytes"]
     if D["mode"] != R.DESC_WINDOW or W == 0 or W > 16384:
@@ -424,8 +425,10 @@ def is_narrow_band(D, segs):
     if W <= 16:
         P = narrow_pitch(W)
         thin = any(sg["width"] <= 2 for sg in srcs + dsts)
+        bytewise = any(narrow_class(sg["width"], sg["col"], P, W) == "bytes" and (i < len(srcs) or sg["width"] > 4)
+                       for i, sg in enumerate(srcs + dsts))
         dwords = all(narrow_class(sg["width"], sg["col"], P, W) == "dwords" for sg in srcs + dsts)
-        if _exchange_band(D, srcs, dsts) or not (thin or (dwords and P == W)):
+        if _exchange_band(D, srcs, dsts) or not (thin or bytewise or (dwords and P == W)):
             return False
     return True
 

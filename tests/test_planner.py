@@ -140,6 +140,11 @@ def small_specs():
         T("bytes_r6_gather", (1031, 12), torch.bfloat16, (4,), (1,), (3,), (0,)),
         T("bytes_u8_r5_gather", (1029, 20), torch.uint8, (4,), (1,), (2,), (0,)),
         T("bytes_u8_r7_rep", (523, 28), torch.uint8, (2,), (0,), (2, 4), (RR, 1)),
+        # rows of at most 16 bytes gathered from 3-byte shards or scattered into
+        # 5- to 7-byte ones (narrow bands, not the row mode)
+        T("bytes_u8_r3_gather", (1029, 12), torch.uint8, (4,), (1,), (3,), (0,)),
+        T("bytes_r6_in12", (1033, 6), torch.bfloat16, (3,), (0,), (2,), (1,)),
+        T("bytes_u8_r5_rep", (517, 15), torch.uint8, (2,), (0,), (2, 3), (RR, 1)),
         # replicated sources: each replica reads its own part of the rows
         T("rep_src_u8", (515, 40), torch.uint8, (3,), (RR,), (5,), (1,)),
         T("rep_src_bf16_rows", (1027, 24), torch.bfloat16, (2, 3), (RR, 0), (4,), (1,)),
