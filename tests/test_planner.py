@@ -447,7 +447,8 @@ def narrow_random_specs(seed, count):
     bands of every segment class (thin runs of up to 32 segments among them)
     and the LDS windows, with ragged row counts (partial groups of four and
     eight rows, short last tiles), row splits on either side, replicas on either
-    side and every element size."""
+    side (of column shards, of row shards, of the whole tensor) and every
+    element size."""
     rng = random.Random(seed)
     out = []
     while len(out) < count:
@@ -464,14 +465,18 @@ def narrow_random_specs(seed, count):
             if runs4 and rng.random() < 0.5:
                 k = runs4
             r = rng.choice([1, 2, 3])
-            kind = rng.randint(0, 3)
+            kind = rng.randint(0, 5)
             if kind == 0:
                 return (k,), (1,)
             if kind == 1:
                 return (r,), (0,)
             if kind == 2:
                 return (r, k), (0, 1)
-            return (2, k), (RR, 1)
+            if kind == 3:
+                return (2, k), (RR, 1)
+            if kind == 4:  # replicated row shards (a source reads them in row parts, one per replica)
+                return (rng.choice([2, 3]), r), (RR, 0)
+            return (rng.choice([2, 3]),), (RR,)
         (sm, sp), (dm, dp) = layout(), layout()
         if runs4 and rng.random() < 0.4:  # whole rows on one side, 4-byte runs on the other
             rows_side = ((rng.choice([1, 2, 3]),), (0,))
