@@ -134,7 +134,10 @@ typedef struct reshard_plan_stats {
 /* One planned overlap, in global coordinates (inspection API). */
 typedef struct reshard_piece {
   int64_t tensor;                 /* tensor index inside the plan */
-  int64_t src_rank;               /* source rank read (after replica choice) */
+  int64_t src_rank;               /* source rank the replica choice picks for it (a tensor
+                                     moved as window bands reads a replicated box in row
+                                     parts, one per replica, instead: reshard_plan_src_load
+                                     counts what is read) */
   int64_t src_group;              /* index of the unique source box it belongs to */
   int64_t dst_group;              /* index of the unique destination box it feeds */
   int64_t fanout;                 /* destination ranks written (replicas of dst_group) */
@@ -342,7 +345,8 @@ reshard_status_t reshard_layout_shard_box(reshard_layout_t layout, int64_t rank,
  * each of two row shards).  Host-only: intersects every source box with every
  * unique destination box, picks one source replica per overlap (least-loaded
  * first: replicated weights can be read at any of their holders, news.bpdata.com,
- * "the approach" section), merges contiguous dims and builds the descriptor
+ * "the approach" section; in a tensor moved as window bands each replica of a
+ * box reads a near-equal part of its rows), merges contiguous dims and builds the descriptor
  * table.  The layouts may be destroyed afterwards.  The device table is
  * uploaded by reshard_plan_upload or by the first reshard_execute.
  * Errors: RESHARD_ERR_INVALID_ARGUMENT, RESHARD_ERR_LAYOUT_MISMATCH,
