@@ -710,6 +710,32 @@ __device__ __forceinline__ void dword_stream_in(uintptr_t g, uint32_t w, uint32_
       }
     }
     done = 4 * nq;
+  } else {  // 16-byte loads too, their four dwords placed one by one (a row may end inside)
+    const uint32_t nq = n / 4;
+    for (uint32_t base = threadIdx.x; base < nq; base += kBlock * kNarrowBatch) {
+      u32x4 v[kNarrowBatch];
+#pragma unroll
+      for (int k = 0; k < kNarrowBatch; ++k) {
+        const uint32_t q = base + uint32_t(k) * kBlock;
+        if (q < nq) v[k] = load_16_unaligned(g + 16 * uint64_t(q));
+      }
+#pragma unroll
+      for (int k = 0; k < kNarrowBatch; ++k) {
+        const uint32_t q = base + uint32_t(k) * kBlock;
+        if (q >= nq) break;
+        const uint32_t j = 4 * q, r = div_small(j, w, m);
+        uint32_t col = j - r * w;
+        uint32_t* a = lds + r * pitch + c + col;
+        const uint32_t x[4] = {v[k].x, v[k].y, v[k].z, v[k].w};
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {  // stream dword j + b: the next column, or the next row's first
+          *a = x[b];
+          ++a;
+          if (++col == w) col = 0, a += pitch - w;
+        }
+      }
+    }
+    done = 4 * nq;
   }
   for (uint32_t base = done + threadIdx.x; base < n; base += kBlock * kNarrowBatch) {
     uint32_t v[kNarrowBatch];
@@ -982,6 +1008,25 @@ __device__ __forceinline__ void window_narrow(const reshard_descriptor_t& D, con
       for (uint32_t q = threadIdx.x; q < nq; q += kBlock) {
         const uint32_t j = 4 * q, r = div_small(j, w, m);
         const u32x4 v = *reinterpret_cast<const u32x4_u1*>(lds + r * pitch + c + (j - r * w));
+        __builtin_nontemporal_store(v, as_global<u32x4_u1>(g0 + 16 * uint64_t(q)));
+        for (uint32_t f = 1; f < fan; ++f)
+          __builtin_nontemporal_store(v, as_global<u32x4_u1>(sh.ptr(refs[ref + f]) + off + 16 * uint64_t(q)));
+      }
+      done = 4 * nq;
+    } else {  // 16-byte stores too, their four dwords read one by one (a row may end inside)
+      const uint32_t nq = n / 4;
+      for (uint32_t q = threadIdx.x; q < nq; q += kBlock) {
+        const uint32_t j = 4 * q, r = div_small(j, w, m);
+        uint32_t col = j - r * w;
+        const uint32_t* a = lds + r * pitch + c + col;
+        uint32_t x[4];
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+          x[b] = *a;
+          ++a;
+          if (++col == w) col = 0, a += pitch - w;
+        }
+        const u32x4 v = u32x4{x[0], x[1], x[2], x[3]};
         __builtin_nontemporal_store(v, as_global<u32x4_u1>(g0 + 16 * uint64_t(q)));
         for (uint32_t f = 1; f < fan; ++f)
           __builtin_nontemporal_store(v, as_global<u32x4_u1>(sh.ptr(refs[ref + f]) + off + 16 * uint64_t(q)));

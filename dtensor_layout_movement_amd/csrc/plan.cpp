@@ -567,7 +567,9 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v, s
     b.d.extent[0] = uint32_t(rb - ra);
     const bool quad = width == kRowModeBytes && (quad_side(b.src) || quad_side(b.dst) || octet_side(b.src) ||
                                                  octet_side(b.dst));
-    bool bytewise = false;  // a segment of one or two bytes, or of another width the narrow kernel moves bytewise
+    // a segment of one or two bytes, a source segment of the bytes class or a
+    // destination one over 4 bytes: a band the narrow kernel takes from the row mode
+    bool bytewise = false;
     for (const auto* side : {&b.src, &b.dst})
       for (const auto& x : *side)
         bytewise |= x.width <= 2 || (narrow_class(x.width, x.col, narrow_pitch(uint32_t(width)), uint32_t(width)) ==
@@ -576,7 +578,8 @@ bool emit_windows(HostPlan* P, int t, size_t pc0, size_t pc1, const View2d& v, s
                             : int64_t(kTileThreads) * (quad ? kQuadRowsPerLane : kRowsPerLane);
     if (width <= kRowModeBytes && bytewise && !quad)
       while (rows_per_tile * narrow_pitch(uint32_t(width)) > int64_t(kNarrowWindowBytes)) rows_per_tile /= 2;
-    // a narrow band with small destination pieces or short tiles: twice the rows
+    // a narrow band with small destination pieces, a thin destination segment or
+    // short tiles: twice the rows
     if (narrow_band(uint32_t(width), uint64_t(rows_per_tile), b.src.data(), uint32_t(b.src.size()), b.dst.data(),
                     uint32_t(b.dst.size()))) {
       bool small = rows_per_tile < kNarrowShortTile;

@@ -457,6 +457,9 @@ def narrow_segment_moves(sg, P, W, hr, phase):
             r = np.arange(hr, dtype=np.int64)
             lo, win, ln = 4 * w * r, 4 * (r * pitch + c), np.full(hr, 4 * w)
         else:
+            # quads stay together in the window; otherwise the kernel still moves
+            # 16 bytes of the stream a lane but places its four dwords one by one
+            # (the same dword moves as below, by stream offset)
             quads = (w & 3) == 0 or (c == 0 and w == pitch)
             nq = n // 4 if quads else 0
             j = np.concatenate([4 * np.arange(nq, dtype=np.int64), np.arange(4 * nq, n, dtype=np.int64)])

@@ -140,6 +140,12 @@ def small_specs():
         T("bytes_r6_gather", (1031, 12), torch.bfloat16, (4,), (1,), (3,), (0,)),
         T("bytes_u8_r5_gather", (1029, 20), torch.uint8, (4,), (1,), (2,), (0,)),
         T("bytes_u8_r7_rep", (523, 28), torch.uint8, (2,), (0,), (2, 4), (RR, 1)),
+        # rows of 24 and 40 bytes (a window pitch one dword wider): 16-byte
+        # stream pieces whose dwords fall in two window rows, scattered,
+        # scattered to replicas and gathered
+        T("dwords24_scatter", (1031, 6), torch.float32, (2,), (0,), (3,), (1,)),
+        T("dwords40_rep", (1029, 10), torch.float32, (3,), (0,), (2, 5), (RR, 1)),
+        T("dwords24_gather", (1033, 6), torch.float32, (3,), (1,), (2,), (0,)),
         # rows of at most 16 bytes gathered from 3-byte shards or scattered into
         # 5- to 7-byte ones (narrow bands, not the row mode)
         T("bytes_u8_r3_gather", (1029, 12), torch.uint8, (4,), (1,), (3,), (0,)),
