@@ -836,7 +836,26 @@ __device__ __forceinline__ void bytes_stream_out(uintptr_t g0, uint64_t off, uin
                                                  uint32_t cb, uint32_t m, uint32_t cls, uint32_t hr, uint32_t P,
                                                  const uint8_t* lds) {
   if (cls == kSegRows || cls == kSegBytes) {  // one row a lane (byte by byte measured no faster here)
-    for (uint32_t r = threadIdx.x; r < hr; r += kBlock) {
+    uint32_t first = 0;  // rows moved 16 stream bytes a lane
+    if (wb == 4 || wb == 8) {  // 16 / wb rows a lane: one window access a row, one 16-byte store
+      const uint32_t k = 16 / wb, nq = hr / k;
+      for (uint32_t q = threadIdx.x; q < nq; q += kBlock) {
+        const uint8_t* a = lds + q * k * P + cb;
+        u32x4 v;
+        if (wb == 8) {
+          const u32x2_u1 x = *reinterpret_cast<const u32x2_u1*>(a), y = *reinterpret_cast<const u32x2_u1*>(a + P);
+          v = u32x4{x.x, x.y, y.x, y.y};
+        } else {
+          v = u32x4{*reinterpret_cast<const u32_u*>(a), *reinterpret_cast<const u32_u*>(a + P),
+                    *reinterpret_cast<const u32_u*>(a + 2 * P), *reinterpret_cast<const u32_u*>(a + 3 * P)};
+        }
+        const uint64_t o = 16 * uint64_t(q);
+        __builtin_nontemporal_store(v, as_global<u32x4_u1>(g0 + o));
+        for (uint32_t f = 1; f < fan; ++f) __builtin_nontemporal_store(v, as_global<u32x4_u1>(sh.ptr(refs[ref + f]) + off + o));
+      }
+      first = nq * k;
+    }
+    for (uint32_t r = first + threadIdx.x; r < hr; r += kBlock) {
       const u32x4 v = lds_get(lds + r * P + cb, wb);
       const uint64_t o = uint64_t(r) * wb;
       store_bytes(g0 + o, v, wb);

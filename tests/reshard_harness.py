@@ -473,7 +473,7 @@ def narrow_segment_moves(sg, P, W, hr, phase):
     elif cls == "whole":
         lo = 16 * np.arange(-(-hr * wb // 16), dtype=np.int64)
         win, ln = lo.copy(), np.minimum(16, hr * wb - lo)
-    elif cls == "rows":
+    elif cls == "rows":  # phase 2 moves 4- and 8-byte rows 16 stream bytes a lane, one window access a row
         r = np.arange(hr, dtype=np.int64)
         lo, win, ln = r * wb, r * P + cb, np.full(hr, wb)
     elif cls == "bytes" and phase == 2:  # one row a lane, as for rows

@@ -146,6 +146,10 @@ def small_specs():
         T("dwords24_scatter", (1031, 6), torch.float32, (2,), (0,), (3,), (1,)),
         T("dwords40_rep", (1029, 10), torch.float32, (3,), (0,), (2, 5), (RR, 1)),
         T("dwords24_gather", (1033, 6), torch.float32, (3,), (1,), (2,), (0,)),
+        # 4-byte shards at an odd window pitch (10-byte rows): 16 stream bytes
+        # a lane cover four rows, scattered and gathered
+        T("rows4_w10", (1031, 5), torch.bfloat16, (2,), (0,), (3,), (1,)),
+        T("rows4_w10_gather", (1029, 5), torch.bfloat16, (3,), (1,), (2,), (0,)),
         # rows of at most 16 bytes gathered from 3-byte shards or scattered into
         # 5- to 7-byte ones (narrow bands, not the row mode)
         T("bytes_u8_r3_gather", (1029, 12), torch.uint8, (4,), (1,), (3,), (0,)),
