@@ -104,6 +104,26 @@ def test_small_layouts(spec):
     run_parity([spec], "normal" if spec.partial else "raw", 3)
 
 
+def _narrow_shapes_at_scale():
+    """Narrow layouts of a million rows and more that take the narrow-band paths
+    the small cases cover only in a few tiles: 24- and 40-byte rows into 8-byte
+    shards (16-byte stream pieces split over window rows), 10-byte rows into
+    4/4/2-byte shards (4-byte rows 16 stream bytes a lane), 12-byte rows gathered
+    from 3-byte shards (a band of at most 16 bytes on the narrow path), and
+    32-byte rows read from replicated row shards in row parts."""
+    return [T("f32_in24", ((1 << 20) + 3, 6), torch.float32, (2,), (0,), (3,), (1,)),
+            T("bf16_in40", ((1 << 19) + 7, 20), torch.bfloat16, (2,), (0,), (5,), (1,)),
+            T("bf16_in10", ((1 << 20) + 5, 5), torch.bfloat16, (2,), (0,), (3,), (1,)),
+            T("u8_r3_gather", ((1 << 20) + 1, 12), torch.uint8, (4,), (1,), (2,), (0,)),
+            T("rep_rows_in32", ((1 << 20) + 9, 16), torch.bfloat16, (2, 3), (RR, 0), (16,), (1,))]
+
+
+@pytest.mark.parametrize("spec", _narrow_shapes_at_scale(), ids=lambda s: s.name)
+def test_narrow_shapes_at_scale(spec):
+    """Bit-exact against the oracle, every destination byte."""
+    run_parity([spec], "raw", 7)
+
+
 @pytest.mark.parametrize("name", ["partial_tp2", "partial_rep", "partial_two_dims", "partial_f32_f16"])
 def test_partial_sums_of_raw_bits(name):
     """Partial sums over random bytes: infinities, NaN payloads, subnormals and
@@ -132,7 +152,10 @@ def test_misaligned_shard_pointers(misalign):
                                                 "bytes_pieces18", "bytes_pieces18_gather", "bytes_w512",
                                                 "thin_u8_16", "thin_u8_gather", "thin_f16_rep", "thin_bf16_6",
                                                 "rows12_f32", "rows12_gather", "rows12_rep", "bytes_r6_gather",
-                                                "bytes_u8_r7_rep")]
+                                                "bytes_u8_r7_rep", "dwords24_scatter", "dwords40_rep",
+                                                "dwords24_gather", "rows4_w10", "rows4_w10_gather",
+                                                "bytes_u8_r3_gather", "bytes_r6_in12", "rep_src_u8",
+                                                "rep_src_bf16_rows", "thin32_gather_rep")]
     for spec in specs:
         run_parity([spec], "raw", 4, misalign=misalign)
 
