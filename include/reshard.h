@@ -184,23 +184,28 @@ typedef struct reshard_piece {
  *                            read into the window) followed by `fanout` destination
  *                            segments (written from it), each side in column
  *                            order; offsets and strides are ignored.  Used for
- *                            narrow or misaligned pieces.  A band whose
- *                            segments are all packed (row stride = width) moves
- *                            in a narrow-band kernel build, each segment's rows
- *                            as one contiguous stream on the global side, with
- *                            `extent[1]` rows per tile within an 18 KiB window
- *                            (36 KiB when a destination segment would get less
- *                            than 1 KiB a tile or a tile fewer than 64 rows:
- *                            then twice the rows, in a launch of its own).
+ *                            narrow or misaligned pieces.  A band more than 16
+ *                            bytes wide whose segments are all packed (row
+ *                            stride = width) moves in a narrow-band kernel
+ *                            build, each segment's rows as one contiguous
+ *                            stream on the global side, with `extent[1]` rows
+ *                            per tile within an 18 KiB window (36 KiB when a
+ *                            destination segment would get less than 1 KiB a
+ *                            tile or is one or two bytes wide, or a tile would
+ *                            have fewer than 64 rows: then twice the rows, in a
+ *                            launch of its own).  So do packed bands of at most
+ *                            16 bytes with a 1- or 2-byte segment, a source
+ *                            segment that is not dword-granular, or such a
+ *                            destination segment over 4 bytes.
  *                            Other bands at most 16 bytes wide skip LDS: one
  *                            lane per row assembles the row in registers,
  *                            `extent[1]` = 1024 rows per tile (512 when one
  *                            side is four packed 4-byte column runs, which the
  *                            four lanes of a quad exchange, or eight packed
  *                            2-byte runs, which eight lanes exchange; a band
- *                            of at most 16 bytes with a 1- or 2-byte segment
- *                            takes the largest power of two up to 1024 whose
- *                            narrow-band window fits).  Each band kind runs in
+ *                            of at most 16 bytes on the narrow-band build takes
+ *                            the largest power of two up to 1024 whose window
+ *                            fits, doubled as above).  Each band kind runs in
  *                            a launch of its own, whatever the rest of the plan
  *                            holds (n_launches counts them).
  *   RESHARD_DESC_GATHER_ROWS `extent[0]` whole rows of `run_bytes` bytes, packed in
