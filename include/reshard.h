@@ -195,8 +195,9 @@ typedef struct reshard_piece {
  *                            have fewer than 64 rows: then twice the rows, in a
  *                            launch of its own).  So do packed bands of at most
  *                            16 bytes with a 1- or 2-byte segment, a source
- *                            segment that is not dword-granular, or such a
- *                            destination segment over 4 bytes.
+ *                            segment of 3 to 15 bytes (not 4 or 8) that is not
+ *                            dword-granular, or such a destination segment of 5
+ *                            bytes or more.
  *                            Other bands at most 16 bytes wide skip LDS: one
  *                            lane per row assembles the row in registers,
  *                            `extent[1]` = 1024 rows per tile (512 when one
